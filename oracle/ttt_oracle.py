@@ -1,0 +1,313 @@
+"""fp64 CPU oracle of the chunk-wise test-time-training (TTT) inner loop.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link
+this module: only the tests, the smoke check and the CPU-baseline leg of the
+benchmark use it, to check the HIP library against plain definitions.
+
+It is a plain, slow, readable restatement of the method in float64 numpy, with
+hand-derived backpropagation, written from these pages:
+
+  [E2E] "[논문리뷰] End-to-End Test-Time Training for Long Context"
+        (review on kimjy99.github.io)
+        - Method: prefill conditions on x_0..x_T, x_0 is BOS.
+        - section 1, eq. (1): l_t(W) = CE(f(x_{t-1}; W), x_t).
+        - section 1, eq. (2): per-token update W_t = W_{t-1} - eta * grad l_t(W_{t-1}).
+        - section 2, eq. (3)/(4): test loss L(W_0; X) and the static L_naive(W_0; X).
+        - section 3, eq. (5): mini-batch update
+              W_i = W_{i-1} - eta * (1/b) * sum_{t in chunk i} grad l_t(W_{i-1}).
+        - section 3, eq. (6): L(W_0; X) = (1/T) sum_i sum_{t in chunk i} l_t(W_{i-1}).
+        - section 3.1: only the MLP layers are updated; embedding and normalisation
+          layers stay frozen.
+  [IPT] "[논문리뷰] In-Place Test-Time Training" (blog.secrett2633.cloud)
+        - section 1 (Key Terms): the MLP block's final projection is the fast
+          weight; the sequence is split into chunks updated one after another.
+  [SGF] "Self-Generated Feedback Destabilizes Test-Time Training" (summary on
+        onedev.kr), "how it works": one *clipped* gradient step per 1024-token
+        chunk on the last three layers' feed-forward modules.
+
+Readings where the pages leave a step open (each is also listed in the design
+notes of the repository):
+  * f = embedding -> L residual MLP blocks -> LM head; no biases, no final norm,
+    untied input embedding E_in and output head E_out (both frozen).
+  * "rms" blocks are pre-norm: n = h * (mean_j h_j^2 + eps)^(-1/2), no gain.
+  * GELU is the exact erf form; its derivative is Phi(u) + u * phi(u).
+  * SwiGLU block (In-Place shape): a = SiLU(n Wg) * (n Wu); Wg, Wu frozen, W2 fast.
+  * clipping: global L2 norm g over all fast tensors of the chunk-mean gradient,
+    scale s = min(1, c/g); c <= 0 disables it; g = 0 gives s = 1.
+  * a chunk whose g is not finite takes no step (the update is skipped).
+  * argmax ties resolve to the lowest index.
+
+Arrays: E_in, E_out [V, d]; W1, Wg, Wu [d, m]; W2 [m, d]; all row-major, rows of
+activations are tokens.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+from scipy.special import erf
+
+SQRT2 = math.sqrt(2.0)
+INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+@dataclasses.dataclass(frozen=True)
+class Model:
+    vocab: int
+    d_model: int
+    d_hidden: int
+    n_blocks: int
+    mlp: str = "gelu"        # "gelu" | "swiglu_w2"
+    norm: str = "none"       # "none" | "rms"
+    eps: float = 1e-6
+    chunk: int = 1           # b
+    lr: float = 0.0          # eta
+    clip: float = 0.0        # c; <= 0 disables clipping
+
+    @classmethod
+    def from_workload(cls, w, **kw) -> "Model":
+        base = dict(vocab=w.vocab, d_model=w.d_model, d_hidden=w.d_hidden,
+                    n_blocks=w.n_blocks, mlp=w.mlp, norm=w.norm, eps=w.eps,
+                    chunk=w.chunk, lr=w.lr, clip=w.clip)
+        base.update(kw)
+        return cls(**base)
+
+    def fast_names(self) -> List[str]:
+        # [E2E] section 3.1 updates the whole MLP; [IPT] section 1 only its final projection.
+        return ["W1", "W2"] if self.mlp == "gelu" else ["W2"]
+
+    def fast_keys(self) -> List[str]:
+        return [f"{n}.{l}" for l in range(self.n_blocks) for n in self.fast_names()]
+
+
+def as_f64(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    return {k: np.asarray(v, dtype=np.float64) for k, v in weights.items()}
+
+
+# ------------------------------------------------------------- elementwise maps
+def gelu(u):
+    """Exact GELU: u * Phi(u), Phi the standard normal CDF."""
+    return 0.5 * u * (1.0 + erf(u / SQRT2))
+
+
+def gelu_prime(u):
+    """d/du [u Phi(u)] = Phi(u) + u phi(u)."""
+    return 0.5 * (1.0 + erf(u / SQRT2)) + u * INV_SQRT_2PI * np.exp(-0.5 * u * u)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    return x * sigmoid(x)
+
+
+def silu_prime(x):
+    s = sigmoid(x)
+    return s * (1.0 + x * (1.0 - s))
+
+
+def logsumexp_rows(z: np.ndarray) -> np.ndarray:
+    """log sum_v exp(z[t, v]) per row, shifted by the row max for stability."""
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+# ------------------------------------------------------------- model f(x; W)
+def forward(model: Model, P: Dict[str, np.ndarray], x_prev: np.ndarray):
+    """Hidden state h^L for each conditioning token x_{t-1}, plus a cache for backprop.
+
+    [E2E] section 1: f reads only x_{t-1} in the MLP-only model. The stack is
+    h^0 = E_in[x_{t-1}]; h^l = h^{l-1} + MLP_l(norm(h^{l-1})).
+    """
+    h = P["E_in"][x_prev]
+    cache = []
+    for l in range(model.n_blocks):
+        h_in = h
+        if model.norm == "rms":
+            r = 1.0 / np.sqrt(np.mean(h_in * h_in, axis=1) + model.eps)
+            n = h_in * r[:, None]
+        else:
+            r = None
+            n = h_in
+        if model.mlp == "gelu":
+            u = n @ P[f"W1.{l}"]
+            a = gelu(u)
+            c = dict(n=n, r=r, u=u, a=a)
+        else:
+            g = n @ P[f"Wg.{l}"]
+            v = n @ P[f"Wu.{l}"]
+            a = silu(g) * v
+            c = dict(n=n, r=r, g=g, v=v, a=a)
+        h = h_in + a @ P[f"W2.{l}"]
+        cache.append(c)
+    return h, cache
+
+
+def logits(model: Model, P, x_prev):
+    h, cache = forward(model, P, x_prev)
+    return h @ P["E_out"].T, h, cache
+
+
+def ce_stats(z: np.ndarray, x_tgt: np.ndarray):
+    """Per row: loss = logsumexp(z_t) - z_t[x_t], lse, argmax (first maximum), top-2 gap."""
+    lse = logsumexp_rows(z)
+    rows = np.arange(z.shape[0])
+    loss = lse - z[rows, x_tgt]
+    am = np.argmax(z, axis=1)  # numpy returns the first maximum
+    if z.shape[1] > 1:
+        part = np.partition(z, -2, axis=1)
+        margin = part[:, -1] - part[:, -2]
+    else:
+        margin = np.full(z.shape[0], np.inf)
+    return loss, lse, am.astype(np.int64), margin
+
+
+def token_losses(model: Model, P, x_prev, x_tgt):
+    """[E2E] eq. (1): l_t = CE(f(x_{t-1}; W), x_t) = logsumexp(z_t) - z_t[x_t].
+
+    Also returns argmax_t (lowest index on ties) and the top-2 logit margin.
+    """
+    z, _, _ = logits(model, P, x_prev)
+    loss, _, am, margin = ce_stats(z, x_tgt)
+    return loss, am, margin
+
+
+def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt):
+    """Mean chunk loss (1/b) sum_t l_t(W) and its gradient w.r.t. every fast tensor.
+
+    This is the quantity differentiated in [E2E] eq. (5). Backprop by hand:
+      dz = (softmax(z) - onehot(x_t)) / b,  dh = dz E_out
+      per block, top to bottom:
+        G_W2 = a^T dh ;  da = dh W2^T
+        gelu:   du = da * gelu'(u) ; G_W1 = n^T du ; dn = du W1^T
+        swiglu: dg = da * v * silu'(g) ; dv = da * silu(g) ; dn = dg Wg^T + dv Wu^T
+        rms:    dh <- dh + r * (dn - n * mean_j(dn_j n_j))
+        none:   dh <- dh + dn
+      (the embedding is frozen, so the lowest block stops after its weight grads)
+    """
+    b = x_prev.shape[0]
+    z, h, cache = logits(model, P, x_prev)
+    losses, lse, am, margin = ce_stats(z, x_tgt)
+    rows = np.arange(b)
+    p = np.exp(z - lse[:, None])
+    dz = p
+    dz[rows, x_tgt] -= 1.0
+    dz /= b
+    dh = dz @ P["E_out"]
+    grads = {}
+    for l in reversed(range(model.n_blocks)):
+        c = cache[l]
+        W2 = P[f"W2.{l}"]
+        grads[f"W2.{l}"] = c["a"].T @ dh
+        if model.mlp == "gelu":
+            da = dh @ W2.T
+            du = da * gelu_prime(c["u"])
+            grads[f"W1.{l}"] = c["n"].T @ du
+            if l == 0:
+                break
+            dn = du @ P[f"W1.{l}"].T
+        else:
+            if l == 0:
+                break
+            da = dh @ W2.T
+            dg = da * c["v"] * silu_prime(c["g"])
+            dv = da * silu(c["g"])
+            dn = dg @ P[f"Wg.{l}"].T + dv @ P[f"Wu.{l}"].T
+        if model.norm == "rms":
+            n = c["n"]
+            dh = dh + c["r"][:, None] * (dn - n * np.mean(dn * n, axis=1)[:, None])
+        else:
+            dh = dh + dn
+    return float(losses.mean()), dict(losses=losses, argmax=am, margin=margin), grads
+
+
+def clip_scale(g: float, c: float) -> float:
+    """[SGF] "one clipped gradient step": s = min(1, c/g); c <= 0 means no clipping."""
+    if c <= 0.0 or g <= c:
+        return 1.0
+    return c / g
+
+
+# ------------------------------------------------------------- the inner loop
+@dataclasses.dataclass
+class TTTResult:
+    losses: np.ndarray          # l_t(W_{i-1}) for t = 1..T  ([E2E] eq. 6 summands)
+    argmax: np.ndarray          # argmax of the logits that scored l_t
+    margin: np.ndarray          # top-2 logit gap of those logits
+    grad_norm: np.ndarray       # g_i per chunk
+    scale: np.ndarray           # s_i per chunk
+    skipped: np.ndarray         # chunk took no step (non-finite g)
+    delta: Dict[str, np.ndarray]   # D = W_{T/b} - W_0 per fast tensor
+    weights: Dict[str, np.ndarray]  # W_{T/b} = W_0 + D
+
+    @property
+    def mean_loss(self) -> float:
+        return float(self.losses.mean())
+
+
+def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
+            n_chunks: Optional[int] = None) -> TTTResult:
+    """Sequential chunk loop of [E2E] eq. (5)/(6) with the clipped step of [SGF].
+
+    tokens = x_0..x_T with T a multiple of b. Chunk i scores and differentiates
+    tokens t = (i-1)b+1 .. ib at W_{i-1} (the weights before its own step), then
+    steps W_i = W_{i-1} - eta * s_i * G_i. The fast state is kept as W_0 + D so
+    that the accumulated update D is exact.
+    """
+    P0 = as_f64(P0)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    b = model.chunk
+    T = tokens.shape[0] - 1
+    if T % b != 0:
+        raise ValueError("T must be a multiple of the chunk size")
+    nc = T // b if n_chunks is None else n_chunks
+    keys = model.fast_keys()
+    D = {k: np.zeros_like(P0[k]) for k in keys}
+    losses, argm, marg = [], [], []
+    gn, sc, sk = [], [], []
+    for i in range(nc):
+        P = dict(P0)
+        for k in keys:
+            P[k] = P0[k] + D[k]
+        x_prev = tokens[i * b: i * b + b]
+        x_tgt = tokens[i * b + 1: i * b + b + 1]
+        _, st, G = chunk_loss_and_grads(model, P, x_prev, x_tgt)
+        losses.append(st["losses"])
+        argm.append(st["argmax"])
+        marg.append(st["margin"])
+        g = math.sqrt(sum(float(np.sum(G[k] * G[k])) for k in keys))
+        if not math.isfinite(g):
+            gn.append(g)
+            sc.append(0.0)
+            sk.append(True)
+            continue
+        s = clip_scale(g, model.clip)
+        for k in keys:
+            D[k] = D[k] - model.lr * s * G[k]
+        gn.append(g)
+        sc.append(s)
+        sk.append(False)
+    Wf = {k: P0[k] + D[k] for k in keys}
+    return TTTResult(np.concatenate(losses) if losses else np.zeros(0),
+                     np.concatenate(argm) if argm else np.zeros(0, np.int64),
+                     np.concatenate(marg) if marg else np.zeros(0),
+                     np.asarray(gn), np.asarray(sc), np.asarray(sk, dtype=bool),
+                     D, Wf)
+
+
+def static_losses(model: Model, P0, tokens, n_tokens: Optional[int] = None) -> np.ndarray:
+    """l_t(W_0) for every t: the summands of L_naive, [E2E] eq. (4)."""
+    P0 = as_f64(P0)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    T = tokens.shape[0] - 1 if n_tokens is None else n_tokens
+    out = []
+    step = 4096
+    for s in range(0, T, step):
+        e = min(T, s + step)
+        l, _, _ = token_losses(model, P0, tokens[s:e], tokens[s + 1:e + 1])
+        out.append(l)
+    return np.concatenate(out)

@@ -1,0 +1,363 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Pages cited (by title and section/equation):
+  [E2E] "End-to-End Test-Time Training for Long Context" review (kimjy99.github.io)
+  [SGF] "Self-Generated Feedback Destabilizes Test-Time Training" summary (onedev.kr)
+The pages print no worked numeric example of the inner loop, so each pin is a
+closed form, an identity the equations imply, a library special case, finite
+differences, or an independently written second implementation (torch fp64
+autograd on the CPU). None of these tests calls the HIP library.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import oracle.ttt_oracle as O
+import ttt_workloads as W
+
+
+def tiny_model(mlp="gelu", norm="none", L=2, b=3, lr=0.3, clip=0.0, V=11, d=6, m=10):
+    return O.Model(vocab=V, d_model=d, d_hidden=m, n_blocks=L, mlp=mlp, norm=norm,
+                   eps=1e-6, chunk=b, lr=lr, clip=clip)
+
+
+def tiny_params(model, seed=0, std=0.5):
+    rng = np.random.default_rng(seed)
+    P = {"E_in": rng.normal(0, std, (model.vocab, model.d_model)),
+         "E_out": rng.normal(0, std, (model.vocab, model.d_model))}
+    for l in range(model.n_blocks):
+        if model.mlp == "gelu":
+            P[f"W1.{l}"] = rng.normal(0, std, (model.d_model, model.d_hidden))
+        else:
+            P[f"Wg.{l}"] = rng.normal(0, std, (model.d_model, model.d_hidden))
+            P[f"Wu.{l}"] = rng.normal(0, std, (model.d_model, model.d_hidden))
+        P[f"W2.{l}"] = rng.normal(0, std, (model.d_hidden, model.d_model))
+    return P
+
+
+def tiny_tokens(model, n, seed=1):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, model.vocab, n + 1)
+    x[0] = 0
+    return x
+
+
+COMBOS = [("gelu", "none"), ("gelu", "rms"), ("swiglu_w2", "none"), ("swiglu_w2", "rms")]
+
+
+# ------------------------------------------------------------------ P1 finite differences
+def fd_check(model, P, x_prev, x_tgt, h=1e-5):
+    _, _, G = O.chunk_loss_and_grads(model, P, x_prev, x_tgt)
+    worst = 0.0
+    for k in model.fast_keys():
+        fd = np.zeros_like(P[k])
+        for idx in np.ndindex(P[k].shape):
+            Pp = dict(P); Pp[k] = P[k].copy(); Pp[k][idx] += h
+            Pm = dict(P); Pm[k] = P[k].copy(); Pm[k][idx] -= h
+            lp, _, _ = O.chunk_loss_and_grads(model, Pp, x_prev, x_tgt)
+            lm, _, _ = O.chunk_loss_and_grads(model, Pm, x_prev, x_tgt)
+            fd[idx] = (lp - lm) / (2 * h)
+        rel = np.linalg.norm(fd - G[k]) / max(np.linalg.norm(G[k]), 1e-30)
+        worst = max(worst, rel)
+    return worst
+
+
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+def test_p1_finite_differences(mlp, norm):
+    """Backprop of eq. (1) through every block type matches central differences."""
+    model = tiny_model(mlp, norm, L=2, b=3)
+    P = tiny_params(model, seed=3)
+    x = tiny_tokens(model, 3, seed=4)
+    assert fd_check(model, P, x[:-1], x[1:]) < 1e-6
+
+
+# ------------------------------------------------------------------ P2 b = 1 is eq. (2)
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+def test_p2_chunk_one_is_per_token_rule(mlp, norm):
+    """[E2E] eq. (5) with b = 1 is the online rule of eq. (2): W_t = W_{t-1} - eta grad l_t(W_{t-1})."""
+    model = tiny_model(mlp, norm, L=2, b=1, lr=0.2)
+    P = tiny_params(model, seed=5)
+    x = tiny_tokens(model, 9, seed=6)
+    res = O.run_ttt(model, P, x)
+    # independent loop: explicit sequence of single-token steps
+    Wc = {k: P[k].copy() for k in model.fast_keys()}
+    losses = []
+    for t in range(1, len(x)):
+        Pt = dict(P); Pt.update(Wc)
+        lt, _, G = O.chunk_loss_and_grads(model, Pt, x[t - 1:t], x[t:t + 1])
+        losses.append(lt)
+        for k in Wc:
+            Wc[k] = Wc[k] - model.lr * G[k]
+    np.testing.assert_allclose(res.losses, losses, rtol=1e-12, atol=0)
+    for k in Wc:
+        np.testing.assert_allclose(res.weights[k], Wc[k], rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------------ P3 eta = 0 is L_naive
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+def test_p3_zero_lr_is_naive_loss(mlp, norm):
+    """[E2E] eq. (6) at eta = 0 equals eq. (4): every l_t is scored at W_0, and W never moves."""
+    model = tiny_model(mlp, norm, L=2, b=4, lr=0.0)
+    P = tiny_params(model, seed=7)
+    x = tiny_tokens(model, 12, seed=8)
+    res = O.run_ttt(model, P, x)
+    naive = O.static_losses(model, P, x)
+    assert abs(res.mean_loss - naive.mean()) <= 1e-15 * abs(naive.mean()) + 1e-15
+    for k in model.fast_keys():
+        assert np.array_equal(res.weights[k], P[k])
+        assert not res.delta[k].any()
+
+
+# ------------------------------------------------------------------ P4 chunk gradient is a mean
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+def test_p4_chunk_gradient_is_mean_of_token_gradients(mlp, norm):
+    """[E2E] eq. (5): the chunk step uses (1/b) sum_t grad l_t at the same W."""
+    b = 5
+    model = tiny_model(mlp, norm, L=2, b=b)
+    one = tiny_model(mlp, norm, L=2, b=1)
+    P = tiny_params(model, seed=9)
+    x = tiny_tokens(model, b, seed=10)
+    _, _, G = O.chunk_loss_and_grads(model, P, x[:-1], x[1:])
+    for k in model.fast_keys():
+        acc = np.zeros_like(P[k])
+        for t in range(b):
+            _, _, Gt = O.chunk_loss_and_grads(one, P, x[t:t + 1], x[t + 1:t + 2])
+            acc += Gt[k]
+        np.testing.assert_allclose(G[k], acc / b, rtol=1e-12, atol=1e-17)
+
+
+# ------------------------------------------------------------------ P5 TTT helps on Markov data
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_p5_markov_ttt_beats_static(seed):
+    """[E2E] section 2 (toy figure): on bigram-structured data TTT lowers the test loss
+    below the static-weight loss L_naive. Checked on the toy workload in fp64."""
+    w = W.preset("toy")
+    x = W.token_stream(w, seed)
+    P = W.init_weights(w, seed)
+    model = O.Model.from_workload(w)
+    res = O.run_ttt(model, P, x)
+    naive = O.static_losses(model, P, x)
+    assert res.mean_loss < naive.mean()
+
+
+# ------------------------------------------------------------------ P6 closed form E_out = 0
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+def test_p6_zero_head_gives_log_vocab(mlp, norm):
+    """With E_out = 0 every logit is 0: l_t = ln V exactly, the gradient is 0, W stays put."""
+    model = tiny_model(mlp, norm, L=2, b=2, lr=0.5)
+    P = tiny_params(model, seed=11)
+    P["E_out"] = np.zeros_like(P["E_out"])
+    x = tiny_tokens(model, 6, seed=12)
+    res = O.run_ttt(model, P, x)
+    assert np.all(res.losses == math.log(model.vocab))
+    assert np.all(res.grad_norm == 0.0)
+    for k in model.fast_keys():
+        assert np.array_equal(res.weights[k], P[k])
+
+
+# ------------------------------------------------------------------ P7 W2 = 0 wiring
+def test_p7_zero_down_projection_kills_w1_gradient():
+    """One GELU block with W2 = 0: dA = dH W2^T = 0, so G_W1 = 0 exactly, while G_W2 != 0."""
+    model = tiny_model("gelu", "rms", L=1, b=4)
+    P = tiny_params(model, seed=13)
+    P["W2.0"] = np.zeros_like(P["W2.0"])
+    x = tiny_tokens(model, 4, seed=14)
+    _, _, G = O.chunk_loss_and_grads(model, P, x[:-1], x[1:])
+    assert not G["W1.0"].any()
+    assert np.abs(G["W2.0"]).max() > 1e-3
+
+
+# ------------------------------------------------------------------ P8 clip identity
+@pytest.mark.parametrize("clip", [0.0, 0.05, 1e3])
+def test_p8_clipped_step_length(clip):
+    """[SGF] clipped step: ||W_i - W_{i-1}||_F over all fast tensors = eta * min(g_i, c)."""
+    model = tiny_model("gelu", "rms", L=2, b=2, lr=0.3, clip=clip)
+    P = tiny_params(model, seed=15)
+    x = tiny_tokens(model, 8, seed=16)
+    prev = {k: P[k].copy() for k in model.fast_keys()}
+    for i in range(4):
+        res = O.run_ttt(model, P, x, n_chunks=i + 1)
+        step = math.sqrt(sum(np.sum((res.weights[k] - prev[k]) ** 2) for k in prev))
+        g = res.grad_norm[i]
+        expect = model.lr * (g if clip <= 0 else min(g, clip))
+        assert abs(step - expect) <= 1e-12 * expect
+        if 0 < clip < g:
+            assert res.scale[i] < 1.0
+        prev = {k: res.weights[k].copy() for k in prev}
+
+
+# ------------------------------------------------------------------ P9 logsumexp special case
+def test_p9_logsumexp_matches_library():
+    rng = np.random.default_rng(17)
+    for z in [rng.normal(0, 3, (7, 50)), rng.normal(0, 1, (3, 1000)) * 1e4,
+              np.array([[1e4, -1e4, 0.0], [-1e4, -1e4, -1e4]])]:
+        np.testing.assert_allclose(O.logsumexp_rows(z), scipy.special.logsumexp(z, axis=1),
+                                   rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------------ P10 second implementation
+def torch_ttt(model, P0, tokens):
+    """Independent implementation of eq. (5)/(6) + clipped step with torch fp64 autograd."""
+    t = lambda a: torch.tensor(a, dtype=torch.float64)
+    E_in, E_out = t(P0["E_in"]), t(P0["E_out"])
+    frozen = {k: t(v) for k, v in P0.items() if k.startswith(("Wg", "Wu"))}
+    fast = {k: t(P0[k]) for k in model.fast_keys()}
+    x = torch.tensor(np.asarray(tokens), dtype=torch.long)
+    b = model.chunk
+    losses, gnorms = [], []
+    for i in range((len(tokens) - 1) // b):
+        params = {k: v.clone().requires_grad_(True) for k, v in fast.items()}
+        ctx, tgt = x[i * b:(i + 1) * b], x[i * b + 1:(i + 1) * b + 1]
+        h = E_in[ctx]
+        for l in range(model.n_blocks):
+            n = h
+            if model.norm == "rms":
+                n = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + model.eps)
+            if model.mlp == "gelu":
+                a = torch.nn.functional.gelu(n @ params[f"W1.{l}"], approximate="none")
+            else:
+                a = torch.nn.functional.silu(n @ frozen[f"Wg.{l}"]) * (n @ frozen[f"Wu.{l}"])
+            h = h + a @ params[f"W2.{l}"]
+        z = h @ E_out.T
+        per_tok = torch.nn.functional.cross_entropy(z, tgt, reduction="none")
+        grads = torch.autograd.grad(per_tok.mean(), list(params.values()))
+        g = math.sqrt(sum(float((gr * gr).sum()) for gr in grads))
+        s = 1.0 if (model.clip <= 0 or g <= model.clip) else model.clip / g
+        for (k, _), gr in zip(params.items(), grads):
+            fast[k] = fast[k] - model.lr * s * gr
+        losses.append(per_tok.detach().numpy())
+        gnorms.append(g)
+    return np.concatenate(losses), np.array(gnorms), {k: v.numpy() for k, v in fast.items()}
+
+
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+@pytest.mark.parametrize("clip", [0.0, 0.1])
+def test_p10_torch_autograd_second_opinion(mlp, norm, clip):
+    model = tiny_model(mlp, norm, L=3, b=3, lr=0.4, clip=clip)
+    P = tiny_params(model, seed=18)
+    x = tiny_tokens(model, 12, seed=19)
+    res = O.run_ttt(model, P, x)
+    tl, tg, tw = torch_ttt(model, P, x)
+    np.testing.assert_allclose(res.losses, tl, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(res.grad_norm, tg, rtol=1e-12)
+    for k in model.fast_keys():
+        np.testing.assert_allclose(res.weights[k], tw[k], rtol=1e-12, atol=1e-14)
+        # the update itself (the part the stated weight gate cannot see)
+        np.testing.assert_allclose(res.delta[k], tw[k] - P[k], rtol=1e-9, atol=1e-15)
+
+
+def test_p10_realistic_shape_one_chunk():
+    """Same second opinion at a real width (single-block shape, narrowed vocab, 1 chunk)."""
+    w = W.preset("single", vocab=512, chunk=64, n_tokens=64)
+    model = O.Model.from_workload(w)
+    P = W.init_weights(w, 0)
+    x = W.token_stream(w, 0)
+    res = O.run_ttt(model, P, x)
+    tl, tg, tw = torch_ttt(model, P, x)
+    np.testing.assert_allclose(res.losses, tl, rtol=1e-12)
+    for k in model.fast_keys():
+        np.testing.assert_allclose(res.delta[k], tw[k] - P[k], rtol=1e-9, atol=1e-16)
+
+
+# ------------------------------------------------------------------ closed-form bigram example
+def test_closed_form_two_token_bigram():
+    """Hand-derived example: V=2, d=m=1, one GELU block, b=1, no norm.
+
+    E_in = [[1], [1]], E_out = [[1], [-1]], W1 = [[0]], W2 = [[w]], x = (0, 0, 1).
+    t=1: h = 1 + gelu(0) w = 1, z = (1, -1), target 0:
+         l_1 = ln(1 + e^-2); p_1 = 1/(1+e^2); dh = -2 p_1;
+         G_W1 = n * (dh * w * gelu'(0)) = -w p_1 (gelu'(0) = 1/2), G_W2 = gelu(0) dh = 0.
+         W1 <- eta * w * p_1.
+    t=2: u = eta w p_1, h = 1 + gelu(u) w, z = (h, -h), target 1: l_2 = ln(1 + e^{2h}).
+    """
+    w2, eta = 0.5, 0.7
+    model = O.Model(vocab=2, d_model=1, d_hidden=1, n_blocks=1, mlp="gelu", norm="none",
+                    chunk=1, lr=eta, clip=0.0)
+    P = {"E_in": np.array([[1.0], [1.0]]), "E_out": np.array([[1.0], [-1.0]]),
+         "W1.0": np.array([[0.0]]), "W2.0": np.array([[w2]])}
+    res = O.run_ttt(model, P, np.array([0, 0, 1]))
+    p1 = 1.0 / (1.0 + math.e ** 2)
+    l1 = math.log1p(math.exp(-2.0))
+    u = eta * w2 * p1
+    gelu_u = 0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0)))
+    h = 1.0 + gelu_u * w2
+    l2 = math.log1p(math.exp(2.0 * h))
+    assert res.losses[0] == pytest.approx(l1, rel=1e-15)
+    assert res.losses[1] == pytest.approx(l2, rel=1e-14)
+    assert res.grad_norm[0] == pytest.approx(w2 * p1, rel=1e-15)
+    g2 = res.grad_norm[1]
+    assert g2 > 0
+    # W2 got no gradient in step 1 (a = gelu(0) = 0)
+    _, _, G = O.chunk_loss_and_grads(model, P, np.array([0]), np.array([0]))
+    assert G["W2.0"][0, 0] == 0.0
+    assert G["W1.0"][0, 0] == pytest.approx(-w2 * p1, rel=1e-15)
+
+
+# ------------------------------------------------------------------ the pins catch planted mistakes
+def test_pins_catch_wrong_gelu_derivative(monkeypatch):
+    """Planting a dropped term in the oracle's GELU' (on the CPU) must fail the FD pin."""
+    monkeypatch.setattr(O, "gelu_prime", lambda u: 0.5 * (1.0 + scipy.special.erf(u / O.SQRT2)))
+    model = tiny_model("gelu", "none", L=1, b=3)
+    P = tiny_params(model, seed=3)
+    x = tiny_tokens(model, 3, seed=4)
+    assert fd_check(model, P, x[:-1], x[1:]) > 1e-3
+
+
+def test_pins_catch_wrong_silu_derivative(monkeypatch):
+    monkeypatch.setattr(O, "silu_prime", lambda g: O.sigmoid(g))
+    model = tiny_model("swiglu_w2", "rms", L=2, b=3)
+    P = tiny_params(model, seed=3)
+    x = tiny_tokens(model, 3, seed=4)
+    assert fd_check(model, P, x[:-1], x[1:]) > 1e-3
+
+
+def test_pins_catch_unclipped_step(monkeypatch):
+    monkeypatch.setattr(O, "clip_scale", lambda g, c: 1.0)
+    model = tiny_model("gelu", "rms", L=2, b=2, lr=0.3, clip=0.05)
+    P = tiny_params(model, seed=15)
+    x = tiny_tokens(model, 4, seed=16)
+    res = O.run_ttt(model, P, x, n_chunks=1)
+    step = math.sqrt(sum(np.sum(res.delta[k] ** 2) for k in model.fast_keys()))
+    assert abs(step - model.lr * min(res.grad_norm[0], model.clip)) > 1e-3
+
+
+def test_pins_catch_off_by_one_target():
+    """Scoring x_{t-1} instead of x_t (an index slip) breaks the closed form."""
+    model = O.Model(vocab=2, d_model=1, d_hidden=1, n_blocks=1, chunk=1, lr=0.0)
+    P = {"E_in": np.array([[1.0], [1.0]]), "E_out": np.array([[1.0], [-1.0]]),
+         "W1.0": np.array([[0.0]]), "W2.0": np.array([[0.5]])}
+    good, _, _ = O.token_losses(model, P, np.array([0]), np.array([1]))
+    slip, _, _ = O.token_losses(model, P, np.array([0]), np.array([0]))
+    assert good[0] == pytest.approx(math.log1p(math.exp(2.0)), rel=1e-15)
+    assert abs(slip[0] - good[0]) > 1.0
+
+
+# ------------------------------------------------------------------ non-finite chunk is skipped
+def test_nonfinite_gradient_skips_update():
+    model = tiny_model("gelu", "none", L=1, b=2, lr=0.3)
+    P = tiny_params(model, seed=20)
+    P["E_in"] = P["E_in"].copy()
+    P["E_in"][3, 0] = np.nan
+    x = np.array([0, 3, 1, 2, 4])  # chunk 1 reads E_in[3] (NaN), chunk 2 does not
+    res = O.run_ttt(model, P, x)
+    assert res.skipped.tolist() == [True, False]
+    assert np.isfinite(res.delta["W1.0"]).all()
+    assert res.delta["W1.0"].any()
+
+
+# ------------------------------------------------------------------ input generator sanity
+def test_workload_streams_are_seeded_and_in_range():
+    w = W.preset("single", n_tokens=4096)
+    a, b = W.token_stream(w, 3), W.token_stream(w, 3)
+    assert np.array_equal(a, b) and a[0] == W.BOS
+    assert a.min() >= 0 and a.max() < w.vocab
+    c = W.token_stream(w, 4)
+    assert not np.array_equal(a, c)
+    P = W.init_weights(w.replace(vocab=512), 0)
+    for k, v in P.items():
+        assert np.array_equal(W.round_to_bf16(v), v)  # bf16-exact
+        assert 0.018 < v.std() < 0.022
