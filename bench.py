@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Throughput of the chunk-wise TTT inner loop on one MI355X.
+
+One step = one full prefill of the workload's token stream through the HIP library: for
+each chunk of b tokens, forward through the fast blocks, next-token CE through the frozen
+LM head, backward to the fast weights, global-norm clip and SGD step; chunks in sequence.
+Steps continue the same context (the fast state keeps learning), so no reset sits inside
+the timed region.
+
+Prints one JSON line on stdout; diagnostics go to stderr.
+  python bench.py [--steps K] [--warmup W] [--workload s760m] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15     # MI355X dense bf16 MFMA, flop/s
+PEAK_FP32 = 157.3e12   # MI355X fp32 matrix, flop/s
+PEAK_HBM = 8.0e12      # MI355X HBM3E, byte/s
+METRIC = "TTT inner-loop tokens/s (fwd+bwd+update) at 1 GPU; % of bf16 MFMA peak"
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_flops_per_token(w) -> float:
+    """Algorithmic flops per token: what the method must compute, no recompute.
+
+    GELU blocks: forward 4dm per block; backward 8dm per block above the lowest (dA, G2,
+    G1, dHn) and 6dm for the lowest (no dHn). SwiGLU with only W2 fast: forward 6dm,
+    backward 2dm (G2). LM head: 2Vd logits + 2Vd for dY.
+    """
+    d, m, L, V = w.d_model, w.d_hidden, w.n_blocks, w.vocab
+    if w.mlp == "gelu":
+        blocks = 4 * d * m * L + (8 * d * m * (L - 1) + 6 * d * m if L > 0 else 0)
+    else:
+        blocks = 8 * d * m * L
+    return float(blocks + 4 * V * d)
+
+
+def kind_flops_per_chunk(w, kind: str) -> float:
+    """Flops one chunk's launches of a GEMM kind perform (each counted once, no padding)."""
+    b, d, m, V, L = w.chunk, w.d_model, w.d_hidden, w.vocab, w.n_blocks
+    g = w.mlp == "gelu"
+    table = {
+        "ce_fwd": 2.0 * b * V * d,
+        "ce_prob": 2.0 * b * V * d,
+        "ce_dy": 2.0 * b * V * d,
+        "up": (2.0 if g else 4.0) * b * d * m * L,
+        "down": 2.0 * b * d * m * L,
+        "du": 2.0 * b * d * m * L if g else 0.0,
+        "dw": (4.0 if g else 2.0) * b * d * m * L,
+        "dhn": 2.0 * b * d * m * max(L - 1, 0) if g else 0.0,
+    }
+    return table.get(kind, 0.0)
+
+
+def cpu_baseline(w, P, x, n_chunks: int):
+    """The fp64 oracle, as it stands, on the first n_chunks chunks of the same stream."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    model = O.Model.from_workload(w)
+    t0 = time.perf_counter()
+    O.run_ttt(model, P, x[:n_chunks * w.chunk + 1], n_chunks=n_chunks)
+    dt = time.perf_counter() - t0
+    return {"value": n_chunks * w.chunk / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_chunks} chunks ({n_chunks * w.chunk} tokens) of the same stream, fp64 numpy, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="s760m")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-chunks", type=int, default=2)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        eprint("bench.py measures one GPU only: the inner loop of one token stream runs on a single "
+               "MI355X here and this build has no multi-GPU path; run with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import ttt_workloads as W
+    import test_long_context_chunk_amd as ttt
+
+    w = W.preset(args.workload)
+    T = w.n_tokens
+    eprint(f"[bench] workload {w.name}: V={w.vocab} d={w.d_model} m={w.d_hidden} L={w.n_blocks} "
+           f"mlp={w.mlp} norm={w.norm} T={T} b={w.chunk} {w.precision}")
+    x = W.token_stream(w, args.seed)
+    P = W.init_weights(w, args.seed)
+    dev = {k: ttt.to_device(v, w.precision) for k, v in P.items()}
+    total_steps = args.warmup + args.steps + 2
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * total_steps)
+    del dev
+    tok = torch.from_numpy(x.astype(np.int32)).cuda()
+    torch.cuda.synchronize()
+
+    # untimed: one step with every kernel kind traced -> breakdown and the dominant kind
+    ctx.profile(ttt._binding.KERNEL_KINDS)
+    ctx.prefill(tok)
+    prof = ctx.profile_read()
+    ctx.profile([])
+    tot = sum(v[0] for v in prof.values())
+    eprint("[bench] per-kind time of one traced step (events around every launch):")
+    for k, (ms, n) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
+        f = kind_flops_per_chunk(w, k) * w.n_chunks
+        rate = f / (ms * 1e-3) / 1e12 if f > 0 and ms > 0 else 0.0
+        eprint(f"  {k:10s} {ms:9.3f} ms {100 * ms / tot:5.1f}%  {n:5d} launches  {rate:8.1f} TFLOP/s")
+    gemm_kinds = {k: v for k, v in prof.items() if kind_flops_per_chunk(w, k) > 0}
+    dom = max(gemm_kinds, key=lambda k: gemm_kinds[k][0])
+
+    for _ in range(args.warmup):
+        ctx.prefill(tok)
+    torch.cuda.synchronize()
+
+    # timed: exactly `steps` steps; only the dominant kind is bracketed by events
+    ctx.profile([dom])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ctx.prefill(tok)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dprof = ctx.profile_read()
+    ctx.profile([])
+    status = ctx.sync()
+    if status != 0:
+        eprint(f"[bench] library reported status {status}")
+        sys.exit(1)
+    losses = ctx.token_losses(T * (total_steps - args.steps - 2 + 1), 8).cpu().numpy()
+    if not np.all(np.isfinite(losses)):
+        eprint("[bench] non-finite losses")
+        sys.exit(1)
+
+    tokens_per_s = args.steps * T / elapsed
+    fpt = alg_flops_per_token(w)
+    frac_peak = tokens_per_s * fpt / PEAK_BF16
+    dom_ms, dom_n = dprof.get(dom, (0.0, 0))
+    launches_per_chunk = max(1, dom_n // (args.steps * w.n_chunks))
+    per_launch = kind_flops_per_chunk(w, dom) / launches_per_chunk
+    avg_s = dom_ms * 1e-3 / max(dom_n, 1)
+    achieved = per_launch / avg_s / 1e12 if avg_s > 0 else 0.0
+    peak = (PEAK_BF16 if w.precision == "bf16" else PEAK_FP32) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.precision,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.n_blocks} x {'pre-RMSNorm ' if w.norm == 'rms' else ''}"
+                        f"{'GELU' if w.mlp == 'gelu' else 'SwiGLU(W2 fast)'} block, d={w.d_model}, "
+                        f"m={w.d_hidden}, V={w.vocab}",
+            "tokens_per_step": T, "chunk": w.chunk, "lr": w.lr, "clip": w.clip,
+            "stream": f"Zipf(1.1) + sparse Markov, seed {args.seed}",
+        },
+        "frac_of_bf16_peak": frac_peak,
+        "alg_flops_per_token": fpt,
+        "roofline": {
+            "bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": None,
+            "alg_flops_per_launch": per_launch, "avg_launch_us": avg_s * 1e6, "launches": dom_n,
+        },
+    }
+    if not args.no_cpu_baseline:
+        eprint(f"[bench] timing the fp64 oracle on {args.cpu_chunks} chunks ...")
+        out["cpu_baseline"] = cpu_baseline(w, P, x, args.cpu_chunks)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

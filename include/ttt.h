@@ -1,0 +1,195 @@
+/*
+ * ttt.h — C ABI of the chunk-wise test-time-training (TTT) inner loop on MI355X (gfx950).
+ *
+ * What the library computes (pages: "End-to-End Test-Time Training for Long Context",
+ * review on kimjy99.github.io = [E2E]; "In-Place Test-Time Training", review on
+ * blog.secrett2633.cloud = [IPT]; "Self-Generated Feedback Destabilizes Test-Time
+ * Training", summary on onedev.kr = [SGF]):
+ *
+ *   f(x; W) = LMhead( block_L( ... block_1( E_in[x] ) ) )       (no final norm, untied head)
+ *   block_l(h) = h + MLP_l(norm(h)),  norm = none | RMSNorm without gain (eps from the config)
+ *   MLP = GELU(n W1) W2 with W1, W2 fast                         ([E2E] section 3.1)
+ *       | (SiLU(n Wg) * (n Wu)) W2 with Wg, Wu frozen, W2 fast   ([IPT] section 1)
+ *   l_t(W) = CE(f(x_{t-1}; W), x_t)                              ([E2E] eq. 1)
+ *   for chunk i = 1..T/b, in sequence, tokens of a chunk in parallel ([E2E] eq. 5):
+ *       G_i = (1/b) sum_{t in chunk i} grad l_t(W_{i-1})
+ *       g_i = ||G_i||_2 over all fast tensors; s_i = min(1, clip/g_i) (clip <= 0: s_i = 1)
+ *                                                                ([SGF] one clipped step per chunk)
+ *       W_i = W_{i-1} - lr * s_i * G_i
+ *   the loss recorded for token t is l_t(W_{i-1}), its chunk's weights before the step
+ *                                                                ([E2E] eq. 6)
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are HIP device pointers unless stated otherwise; row-major.
+ *   - Tokens are int32 ids in [0, vocab).
+ *   - Every function returns a ttt_status and never throws or aborts.
+ *   - A context is bound to one HIP stream (given at creation) and is not thread-safe.
+ *     Separate contexts are independent.
+ *   - Conditions the device detects (an id out of range, a non-finite gradient norm)
+ *     are recorded in a sticky device flag and returned by the next synchronising call
+ *     (ttt_sync, ttt_token_losses, ttt_token_argmax, ttt_chunk_stats, ttt_fast_weights).
+ *     After that, ttt_prefill_chunks returns TTT_ESTATE until ttt_reset or ttt_destroy.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef struct ttt_ctx ttt_ctx;
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_EINVAL = -1,     /* bad argument or configuration; nothing was enqueued            */
+  TTT_ENOMEM = -2,     /* device allocation failed                                         */
+  TTT_EDEVICE = -3,    /* no usable HIP device, or a HIP runtime call failed               */
+  TTT_ERANGE = -4,     /* a token id outside [0, vocab) was seen (it was read as id 0)     */
+  TTT_ENONFINITE = -5, /* a chunk's gradient norm was not finite; that chunk took no step  */
+  TTT_ESTATE = -6      /* the context holds a sticky error; reset or destroy it            */
+} ttt_status;
+
+enum { TTT_MLP_GELU = 0, TTT_MLP_SWIGLU_W2 = 1 };
+enum { TTT_NORM_NONE = 0, TTT_NORM_RMS = 1 };
+/* TTT_FP32: fp32 GEMM operands and fp32 fast weights.
+ * TTT_BF16: bf16 GEMM operands (weights and activations rounded to nearest even),
+ *           fp32 accumulation, fp32 residual stream, losses and gradients; the fast
+ *           state is kept as W0 + D with D the fp32 accumulated update, and the GEMMs
+ *           read bf16(W0 + D). */
+enum { TTT_FP32 = 0, TTT_BF16 = 1 };
+
+typedef struct {
+  int32_t abi_version;  /* must be TTT_ABI_VERSION                                        */
+  int32_t vocab;        /* V >= 2, multiple of 8                                          */
+  int32_t d_model;      /* d >= 8, multiple of 8                                          */
+  int32_t d_hidden;     /* m >= 8, multiple of 8                                          */
+  int32_t n_blocks;     /* L >= 0; 0 = LM head on the embeddings (no fast weights).
+                           TTT_MLP_SWIGLU_W2 supports L = 1 only.                         */
+  int32_t mlp;          /* TTT_MLP_*                                                       */
+  int32_t norm;         /* TTT_NORM_*                                                      */
+  int32_t precision;    /* TTT_FP32 | TTT_BF16                                             */
+  int32_t chunk;        /* b >= 1 tokens per TTT step                                      */
+  int32_t reserved;     /* must be 0                                                       */
+  int64_t max_tokens;   /* capacity of the per-token loss / argmax record (multiple of b) */
+  float lr;             /* eta >= 0                                                        */
+  float clip;           /* c; <= 0 disables clipping                                       */
+  float rms_eps;        /* epsilon of RMSNorm (ignored for TTT_NORM_NONE)                  */
+  float reserved_f;     /* must be 0                                                       */
+} ttt_config;
+
+/* Initial weights. Element type is bf16 (raw 16-bit patterns) for TTT_BF16, fp32 for
+ * TTT_FP32. Shapes, row-major:
+ *   embed    [V x d]  input embedding E_in (frozen)
+ *   lm_head  [V x d]  output head E_out (frozen; logits z = h E_out^T)
+ *   w1[l]    [d x m]  GELU: fast W1 of block l.  SWIGLU: frozen gate Wg.
+ *   w_up[l]  [d x m]  SWIGLU only: frozen up projection Wu; NULL array for GELU.
+ *   w2[l]    [m x d]  fast down projection W2 of block l.
+ * The arrays w1, w_up, w2 are HOST arrays of n_blocks device pointers. */
+typedef struct {
+  const void* embed;
+  const void* lm_head;
+  const void* const* w1;
+  const void* const* w_up;
+  const void* const* w2;
+} ttt_weights;
+
+/* Create a context: validates the configuration, allocates all device memory the
+ * chunk loop needs, and copies every weight into library-owned memory (the caller may
+ * free its tensors when this returns). Synchronous. `stream` is a hipStream_t (NULL =
+ * the default stream) on which every later call of this context is enqueued.
+ * Errors: TTT_EINVAL (config), TTT_ENOMEM, TTT_EDEVICE. On error *out is NULL. */
+ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out);
+
+/* Run the inner loop over n_tokens new tokens ([E2E] Method: prefill; section 3 eq. 5).
+ * tokens: device int32 [n_tokens + 1]; tokens[0] conditions the first prediction (BOS on
+ *         the first call, else the previous call's last token); tokens[1..n_tokens] are
+ *         scored and trained on. Borrowed until the stream passes this call.
+ * n_tokens must be a positive multiple of the chunk size and fit in the remaining
+ * capacity (max_tokens - tokens already consumed). Enqueued; returns immediately.
+ * Errors (nothing enqueued): TTT_EINVAL, TTT_ESTATE. */
+ttt_status ttt_prefill_chunks(ttt_ctx* ctx, const int32_t* tokens, int64_t n_tokens);
+
+/* Copy the recorded losses l_t(W_{i-1}) of tokens [offset, offset + n) (counted from the
+ * first token of the first prefill since creation or reset) into dst (device fp32 [n]).
+ * Synchronises the context's stream; returns a pending sticky error if there is one
+ * (the copy is still made). Errors: TTT_EINVAL (range), TTT_ERANGE, TTT_ENONFINITE. */
+ttt_status ttt_token_losses(ttt_ctx* ctx, float* dst, int64_t offset, int64_t n);
+
+/* Same for the argmax of each scored token's logits (lowest index on ties); dst int32 [n]. */
+ttt_status ttt_token_argmax(ttt_ctx* ctx, int32_t* dst, int64_t offset, int64_t n);
+
+/* Per-chunk clip statistics: dst device fp32 [n x 2] = (g_i, s_i) for chunks
+ * [offset, offset + n); s_i = 0 marks a chunk that took no step. Synchronises. */
+ttt_status ttt_chunk_stats(ttt_ctx* ctx, float* dst, int64_t offset, int64_t n);
+
+/* Export a fast tensor as fp32 into dst (device, same shape/layout as its initial
+ * weight: W1 [d x m], W2 [m x d]). which: 1 = W1 (GELU only), 2 = W2.
+ * kind: 0 = current W = W0 + D;  1 = accumulated update D = W - W0. Synchronises.
+ * Errors: TTT_EINVAL (block/which/kind). */
+ttt_status ttt_fast_weights(ttt_ctx* ctx, int32_t block, int32_t which, int32_t kind, float* dst);
+
+/* Restore W = W0, forget recorded losses, and clear a sticky error. Enqueued. */
+ttt_status ttt_reset(ttt_ctx* ctx);
+
+/* Wait for the context's stream; return a pending sticky error if there is one. */
+ttt_status ttt_sync(ttt_ctx* ctx);
+
+/* Number of tokens consumed since creation or reset (host-side counter). */
+int64_t ttt_tokens_consumed(const ttt_ctx* ctx);
+
+/* Free all device memory of the context (synchronises first). NULL is allowed. */
+ttt_status ttt_destroy(ttt_ctx* ctx);
+
+/* Kernel kinds of the chunk loop, for event-based timing. */
+typedef enum {
+  TTT_K_GATHER = 0,    /* embedding gather                                   */
+  TTT_K_NORM = 1,      /* block pre-norm                                     */
+  TTT_K_TRANSPOSE = 2, /* transposed copies of activations / gradients       */
+  TTT_K_UP = 3,        /* up-projection GEMM + activation epilogue           */
+  TTT_K_DOWN = 4,      /* down-projection GEMM (split-K partials)            */
+  TTT_K_RESIDUAL = 5,  /* residual add of the down-projection partials       */
+  TTT_K_CE_FWD = 6,    /* LM-head GEMM + online-softmax partials             */
+  TTT_K_CE_MERGE = 7,  /* per-token merge of the vocab-tile partials         */
+  TTT_K_CE_PROB = 8,   /* logits recompute -> dlogits, per vocab super-tile  */
+  TTT_K_CE_DY = 9,     /* dlogits x E_out GEMM (split over the vocab)        */
+  TTT_K_DY_SUM = 10,   /* sum of the dY partials                             */
+  TTT_K_DU = 11,       /* dY W2^T GEMM + GELU' epilogue                      */
+  TTT_K_DW = 12,       /* weight-gradient GEMMs (+ sum of squares per tile)  */
+  TTT_K_DHN = 13,      /* dU W1^T GEMM (split-K partials)                    */
+  TTT_K_NORM_BWD = 14, /* norm backward into the residual gradient           */
+  TTT_K_GRADNORM = 15, /* global gradient norm and clip scale                */
+  TTT_K_UPDATE = 16,   /* clipped SGD step of one fast tensor                */
+  TTT_K_COUNT = 17
+} ttt_kernel_kind;
+
+/* Tracing: when bit k of `mask` is set, every later launch of kind k by this context is
+ * bracketed by a pair of HIP events recorded on the context stream. mask = 0 turns it off.
+ * Events cost a few microseconds of stream time each; leave the mask at 0 for timing runs
+ * that do not need per-kernel figures. */
+ttt_status ttt_profile_enable(ttt_ctx* ctx, uint32_t mask);
+
+/* Synchronise, then add the bracketed durations recorded since the last read into
+ * total_ms[TTT_K_COUNT] and launches[TTT_K_COUNT] (host arrays, overwritten), and forget them. */
+ttt_status ttt_profile_read(ttt_ctx* ctx, double* total_ms, int64_t* launches);
+
+/* Static English description of a status code. */
+const char* ttt_status_string(ttt_status s);
+
+/* Test hook: the library's own tiled MFMA GEMM, C = X Y^T in fp32, with X [M x K] (row
+ * stride ldx elements) and Y [N x K] (row stride ldy), both bf16 (precision = TTT_BF16)
+ * or fp32 (TTT_FP32), C [M x N] fp32 (row stride ldc). K must be a multiple of 8 (bf16)
+ * or 4 (fp32); rows and K-offsets must keep 16-byte alignment. Enqueued on `stream`.
+ * It exposes the kernel the inner loop uses so that its tiling can be tested on ragged
+ * shapes; it is not a second code path. Errors: TTT_EINVAL. */
+ttt_status ttt_test_gemm(int32_t precision, const void* X, int64_t ldx, const void* Y, int64_t ldy,
+                         float* C, int64_t ldc, int32_t M, int32_t N, int32_t K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H_ */

@@ -176,7 +176,7 @@ def token_losses(model: Model, P, x_prev, x_tgt):
     return loss, am, margin
 
 
-def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt):
+def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None):
     """Mean chunk loss (1/b) sum_t l_t(W) and its gradient w.r.t. every fast tensor.
 
     This is the quantity differentiated in [E2E] eq. (5). Backprop by hand:
@@ -191,6 +191,8 @@ def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt):
     """
     b = x_prev.shape[0]
     z, h, cache = logits(model, P, x_prev)
+    if logit_probe is not None:
+        logit_probe(z)
     losses, lse, am, margin = ce_stats(z, x_tgt)
     rows = np.arange(b)
     p = np.exp(z - lse[:, None])
@@ -250,13 +252,14 @@ class TTTResult:
 
 
 def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
-            n_chunks: Optional[int] = None) -> TTTResult:
+            n_chunks: Optional[int] = None, logit_probe=None) -> TTTResult:
     """Sequential chunk loop of [E2E] eq. (5)/(6) with the clipped step of [SGF].
 
     tokens = x_0..x_T with T a multiple of b. Chunk i scores and differentiates
     tokens t = (i-1)b+1 .. ib at W_{i-1} (the weights before its own step), then
     steps W_i = W_{i-1} - eta * s_i * G_i. The fast state is kept as W_0 + D so
-    that the accumulated update D is exact.
+    that the accumulated update D is exact. logit_probe(i, z), when given, sees chunk
+    i's logits (for checks that need logits the result does not keep).
     """
     P0 = as_f64(P0)
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -275,7 +278,8 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
             P[k] = P0[k] + D[k]
         x_prev = tokens[i * b: i * b + b]
         x_tgt = tokens[i * b + 1: i * b + b + 1]
-        _, st, G = chunk_loss_and_grads(model, P, x_prev, x_tgt)
+        _, st, G = chunk_loss_and_grads(model, P, x_prev, x_tgt, logit_probe=(
+            None if logit_probe is None else (lambda z, i=i: logit_probe(i, z))))
         losses.append(st["losses"])
         argm.append(st["argmax"])
         marg.append(st["margin"])

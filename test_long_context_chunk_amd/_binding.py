@@ -1,0 +1,249 @@
+"""ctypes binding of the HIP library declared in include/ttt.h.
+
+Argument marshalling only: torch tensors are used for device memory and streams, their
+pointers are handed to the library, and every step of the inner loop runs in the
+library's HIP kernels. There is no fallback: if the library is missing or fails to load,
+constructing a context raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+from .build import lib_path
+
+c_int32, c_int64, c_float, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+ABI_VERSION = 1
+STATUS = {0: "TTT_OK", -1: "TTT_EINVAL", -2: "TTT_ENOMEM", -3: "TTT_EDEVICE",
+          -4: "TTT_ERANGE", -5: "TTT_ENONFINITE", -6: "TTT_ESTATE"}
+MLP = {"gelu": 0, "swiglu_w2": 1}
+NORM = {"none": 0, "rms": 1}
+PRECISION = {"fp32": 0, "bf16": 1}
+# ttt_kernel_kind order of include/ttt.h
+KERNEL_KINDS = ["gather", "norm", "transpose", "up", "down", "residual", "ce_fwd", "ce_merge", "ce_prob",
+                "ce_dy", "dy_sum", "du", "dw", "dhn", "norm_bwd", "gradnorm", "update"]
+
+# Functions declared in include/ttt.h, with their ctypes signatures.
+SIGNATURES = {
+    "ttt_create": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
+    "ttt_prefill_chunks": (c_int32, [c_void_p, c_void_p, c_int64]),
+    "ttt_token_losses": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
+    "ttt_token_argmax": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
+    "ttt_chunk_stats": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
+    "ttt_fast_weights": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p]),
+    "ttt_reset": (c_int32, [c_void_p]),
+    "ttt_sync": (c_int32, [c_void_p]),
+    "ttt_tokens_consumed": (c_int64, [c_void_p]),
+    "ttt_destroy": (c_int32, [c_void_p]),
+    "ttt_status_string": (ctypes.c_char_p, [c_int32]),
+    "ttt_profile_enable": (c_int32, [c_void_p, ctypes.c_uint32]),
+    "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
+    "ttt_test_gemm": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                c_int32, c_int32, c_int32, c_void_p]),
+}
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("abi_version", c_int32), ("vocab", c_int32), ("d_model", c_int32),
+                ("d_hidden", c_int32), ("n_blocks", c_int32), ("mlp", c_int32), ("norm", c_int32),
+                ("precision", c_int32), ("chunk", c_int32), ("reserved", c_int32),
+                ("max_tokens", c_int64), ("lr", c_float), ("clip", c_float),
+                ("rms_eps", c_float), ("reserved_f", c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("lm_head", c_void_p), ("w1", ctypes.POINTER(c_void_p)),
+                ("w_up", ctypes.POINTER(c_void_p)), ("w2", ctypes.POINTER(c_void_p))]
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_string(status)})")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (after torch, so that both share one HIP runtime)."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or lib_path()
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP library {p} is not built: run `python -m test_long_context_chunk_amd.build`")
+    import torch  # noqa: F401  (loads torch's libamdhip64 first; ours binds to the same soname)
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def _status_string(s: int) -> str:
+    try:
+        return load_library().ttt_status_string(s).decode()
+    except Exception:
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise TTTError(status, what)
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def to_device(a, precision: str, device="cuda"):
+    """numpy float32 array -> contiguous device tensor in the GEMM precision (bf16 bits or fp32)."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    t = torch.from_numpy(a)
+    if precision == "bf16":
+        # values are bf16-exact already; the cast keeps them bit for bit
+        t = t.to(torch.bfloat16)
+    return t.to(device).contiguous()
+
+
+class TTT:
+    """One context of the library: private fast weights, bound to one HIP stream."""
+
+    def __init__(self, *, vocab: int, d_model: int, d_hidden: int, n_blocks: int, mlp: str,
+                 norm: str, precision: str, chunk: int, max_tokens: int, lr: float, clip: float,
+                 rms_eps: float = 1e-6, weights: Dict[str, "object"], stream=None):
+        import torch
+        self._lib = load_library()
+        self.vocab, self.d_model, self.d_hidden, self.n_blocks = vocab, d_model, d_hidden, n_blocks
+        self.mlp, self.norm, self.precision, self.chunk = mlp, norm, precision, chunk
+        self.max_tokens = max_tokens
+        self._stream = stream if stream is not None else torch.cuda.current_stream()
+        dt = torch.bfloat16 if precision == "bf16" else torch.float32
+        for k, t in weights.items():
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"weight {k} must be a contiguous {dt} device tensor")
+        cfg = Config(ABI_VERSION, vocab, d_model, d_hidden, n_blocks, MLP[mlp], NORM[norm],
+                     PRECISION[precision], chunk, 0, max_tokens, lr, clip, rms_eps, 0.0)
+        L = n_blocks
+        first = "W1" if mlp == "gelu" else "Wg"
+        w1 = (c_void_p * max(L, 1))(*[_ptr(weights[f"{first}.{l}"]) for l in range(L)])
+        w2 = (c_void_p * max(L, 1))(*[_ptr(weights[f"W2.{l}"]) for l in range(L)])
+        wup = (c_void_p * max(L, 1))(*[_ptr(weights[f"Wu.{l}"]) for l in range(L)]) if mlp == "swiglu_w2" else None
+        w = Weights(_ptr(weights["E_in"]), _ptr(weights["E_out"]),
+                    ctypes.cast(w1, ctypes.POINTER(c_void_p)),
+                    ctypes.cast(wup, ctypes.POINTER(c_void_p)) if wup is not None else None,
+                    ctypes.cast(w2, ctypes.POINTER(c_void_p)))
+        ctx = c_void_p()
+        _check(self._lib.ttt_create(ctypes.byref(cfg), ctypes.byref(w),
+                                    c_void_p(_stream_handle(self._stream)), ctypes.byref(ctx)), "ttt_create")
+        self._ctx = ctx
+
+    @classmethod
+    def from_workload(cls, w, weights: Dict[str, "object"], max_tokens: Optional[int] = None, stream=None, **kw):
+        """Create from a workload description (any object with the preset fields)."""
+        args = dict(vocab=w.vocab, d_model=w.d_model, d_hidden=w.d_hidden, n_blocks=w.n_blocks,
+                    mlp=w.mlp, norm=w.norm, precision=w.precision, chunk=w.chunk,
+                    max_tokens=max_tokens or w.n_tokens, lr=w.lr, clip=w.clip, rms_eps=w.eps)
+        args.update(kw)
+        return cls(weights=weights, stream=stream, **args)
+
+    # ------------------------------------------------------------------ calls
+    def prefill(self, tokens) -> None:
+        """tokens: device int32 [n + 1]; runs n / chunk TTT steps (enqueued)."""
+        import torch
+        if tokens.dtype != torch.int32 or not tokens.is_cuda or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 device tensor")
+        n = tokens.numel() - 1
+        _check(self._lib.ttt_prefill_chunks(self._ctx, c_void_p(_ptr(tokens)), n), "ttt_prefill_chunks")
+
+    def token_losses(self, offset: int = 0, n: Optional[int] = None):
+        import torch
+        n = self.consumed() - offset if n is None else n
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+        _check(self._lib.ttt_token_losses(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_losses")
+        return out
+
+    def token_argmax(self, offset: int = 0, n: Optional[int] = None):
+        import torch
+        n = self.consumed() - offset if n is None else n
+        out = torch.empty(n, dtype=torch.int32, device="cuda")
+        _check(self._lib.ttt_token_argmax(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_argmax")
+        return out
+
+    def chunk_stats(self, offset: int = 0, n: Optional[int] = None):
+        import torch
+        n = self.consumed() // self.chunk - offset if n is None else n
+        out = torch.empty((n, 2), dtype=torch.float32, device="cuda")
+        _check(self._lib.ttt_chunk_stats(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_chunk_stats")
+        return out
+
+    def fast_weight(self, block: int, which: str, kind: str = "W"):
+        """which: "W1" | "W2"; kind: "W" (current) | "delta" (W - W0). fp32 device tensor."""
+        import torch
+        shape = (self.d_model, self.d_hidden) if which == "W1" else (self.d_hidden, self.d_model)
+        out = torch.empty(shape, dtype=torch.float32, device="cuda")
+        _check(self._lib.ttt_fast_weights(self._ctx, block, 1 if which == "W1" else 2,
+                                          0 if kind == "W" else 1, c_void_p(_ptr(out))), "ttt_fast_weights")
+        return out
+
+    def profile(self, kinds) -> None:
+        """Bracket launches of the given kernel kinds (names of KERNEL_KINDS) with HIP events."""
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS.index(k)
+        _check(self._lib.ttt_profile_enable(self._ctx, mask), "ttt_profile_enable")
+
+    def profile_read(self) -> Dict[str, tuple]:
+        """{kind: (total_ms, launches)} for the bracketed launches since the last read."""
+        tot = (ctypes.c_double * len(KERNEL_KINDS))()
+        cnt = (c_int64 * len(KERNEL_KINDS))()
+        _check(self._lib.ttt_profile_read(self._ctx, ctypes.cast(tot, c_void_p), ctypes.cast(cnt, c_void_p)),
+               "ttt_profile_read")
+        return {k: (tot[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS) if cnt[i] > 0}
+
+    def reset(self) -> None:
+        _check(self._lib.ttt_reset(self._ctx), "ttt_reset")
+
+    def sync(self) -> int:
+        return self._lib.ttt_sync(self._ctx)
+
+    def consumed(self) -> int:
+        return int(self._lib.ttt_tokens_consumed(self._ctx))
+
+    def close(self) -> None:
+        if getattr(self, "_ctx", None):
+            self._lib.ttt_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gemm_test_hook(X, Y, precision: str, stream=None):
+    """C = X Y^T through the library's GEMM tile engine (test hook)."""
+    import torch
+    lib = load_library()
+    M, K = X.shape
+    N = Y.shape[0]
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    _check(lib.ttt_test_gemm(PRECISION[precision], c_void_p(_ptr(X)), X.stride(0), c_void_p(_ptr(Y)),
+                             Y.stride(0), c_void_p(_ptr(C)), N, M, N, K,
+                             c_void_p(_stream_handle(stream))), "ttt_test_gemm")
+    return C

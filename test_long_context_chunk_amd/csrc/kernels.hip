@@ -1,0 +1,327 @@
+// Row-wise and elementwise kernels of the TTT inner loop (everything that is not a GEMM).
+#include "launchers.h"
+#include "gemm.h"
+
+namespace {
+
+constexpr int NT = 256;  // threads per block for the row/elementwise kernels
+
+// Block-wide sum in a fixed order (wave butterflies, then waves 0..3 in order).
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// a1: H[t, :] = E_in[x_{t-1}, :] for the b tokens of the chunk ([E2E] eq. 1: f reads
+// x_{t-1}). Ids outside [0, V) raise the sticky range bit and are read as id 0, so no
+// access leaves the table. Also records the clamped conditioning and target ids.
+template <class T>
+__global__ void __launch_bounds__(NT) k_gather(const int* __restrict__ tokens, int V, int d,
+                                               const T* __restrict__ E, float* __restrict__ H,
+                                               T* __restrict__ Yb, int* __restrict__ tok_prev,
+                                               int* __restrict__ tok_tgt, int* __restrict__ err) {
+  const int t = blockIdx.x;
+  int xp = tokens[t], xt = tokens[t + 1];
+  const bool bad = (xp < 0 || xp >= V || xt < 0 || xt >= V);
+  if (xp < 0 || xp >= V) xp = 0;
+  if (xt < 0 || xt >= V) xt = 0;
+  if (threadIdx.x == 0) {
+    tok_prev[t] = xp;
+    tok_tgt[t] = xt;
+    if (bad) atomicOr(err, ERRBIT_RANGE);
+  }
+  const T* src = E + (int64_t)xp * d;
+  float* h = H + (int64_t)t * d;
+  for (int c = threadIdx.x; c < d; c += NT) {
+    const T v = src[c];
+    h[c] = to_f<T>(v);
+    if (Yb) Yb[(int64_t)t * d + c] = v;
+  }
+}
+
+// a2: pre-norm of a block. rms: n = h * (mean h^2 + eps)^(-1/2) (no gain); none: n = h.
+template <class T>
+__global__ void __launch_bounds__(NT) k_rmsnorm(const float* __restrict__ H, int d, float eps, int rms,
+                                                T* __restrict__ Hn, float* __restrict__ r) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const float* h = H + (int64_t)t * d;
+  float rr = 1.0f;
+  if (rms) {
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < d; c += NT) ss += h[c] * h[c];
+    ss = block_sum_256(ss, red);
+    rr = 1.0f / sqrtf(ss / (float)d + eps);
+  }
+  if (threadIdx.x == 0) r[t] = rr;
+  T* o = Hn + (int64_t)t * d;
+  for (int c = threadIdx.x; c < d; c += NT) o[c] = from_f<T>(h[c] * rr);
+}
+
+// dst[c, r] = src[r, c] for r < R, c < C through a 64 x 64 LDS tile.
+template <class T>
+__global__ void __launch_bounds__(NT) k_transpose(const T* __restrict__ src, int64_t lds, int R, int C,
+                                                  T* __restrict__ dst, int64_t ldd) {
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int r = r0 + k, c = c0 + tx;
+    if (r < R && c < C) tile[k][tx] = src[(int64_t)r * lds + c];
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int c = c0 + k, r = r0 + tx;
+    if (c < C && r < R) dst[(int64_t)c * ldd + r] = tile[tx][k];
+  }
+}
+
+// a4 residual: H <- H + sum_s part[s] (split-K partials of A W2, summed in split order);
+// optionally also the GEMM-precision copy of the new H.
+template <class T>
+__global__ void __launch_bounds__(NT) k_residual(float* __restrict__ H, const float* __restrict__ part, int S,
+                                                 int64_t pstride, int64_t n, T* __restrict__ Yb) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    float acc = part[i];
+    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * pstride + i];
+    const float v = H[i] + acc;
+    H[i] = v;
+    if (Yb) Yb[i] = from_f<T>(v);
+  }
+}
+
+// out = sum_s part[s] (fixed order), plus its GEMM-precision copy.
+template <class T>
+__global__ void __launch_bounds__(NT) k_sum_partials(const float* __restrict__ part, int S, int64_t pstride,
+                                                     int64_t n, float* __restrict__ out, T* __restrict__ outb) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    float acc = part[i];
+    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * pstride + i];
+    out[i] = acc;
+    outb[i] = from_f<T>(acc);
+  }
+}
+
+// a5 merge: combine the per-vocab-tile (max, sum exp, argmax) partials of each row in
+// tile order: lse = M + ln S, l_t = lse - z_t[x_t] ([E2E] eq. 1), argmax (lowest index).
+__global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax, const float* __restrict__ psum,
+                                                 const int* __restrict__ pidx, int ntiles, int b,
+                                                 const float* __restrict__ tgt_logit, float* __restrict__ lse,
+                                                 float* __restrict__ loss, int* __restrict__ amax) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  if (row >= b) return;
+  float mx = -INFINITY, sm = 0.f;
+  int ix = 0x7fffffff;
+  for (int j = lane; j < ntiles; j += 64) {
+    const int64_t o = (int64_t)j * b + row;
+    ce_combine(mx, sm, ix, pmax[o], psum[o], pidx[o]);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float omx = __shfl_xor(mx, off, TTT_WAVE);
+    const float osm = __shfl_xor(sm, off, TTT_WAVE);
+    const int oix = __shfl_xor(ix, off, TTT_WAVE);
+    ce_combine(mx, sm, ix, omx, osm, oix);
+  }
+  if (lane == 0) {
+    const float l = mx + logf(sm);
+    lse[row] = l;
+    loss[row] = l - tgt_logit[row];
+    amax[row] = ix;
+  }
+}
+
+// a7 norm backward (pre-norm block, through the frozen norm into the residual stream):
+//   dn = sum_s part[s] (= dU W1^T);  rms: dH += r (dn - n mean_j(dn_j n_j));  none: dH += dn.
+template <class T>
+__global__ void __launch_bounds__(NT) k_norm_bwd(const float* __restrict__ part, int S, int64_t pstride,
+                                                 const T* __restrict__ Hn, const float* __restrict__ r, int d,
+                                                 int rms, float* __restrict__ dH, T* __restrict__ dHb) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int64_t base = (int64_t)t * d;
+  float mean = 0.f, rr = 1.f;
+  if (rms) {
+    float dot = 0.f;
+    for (int c = threadIdx.x; c < d; c += NT) {
+      float dn = part[base + c];
+      for (int s = 1; s < S; ++s) dn += part[(int64_t)s * pstride + base + c];
+      dot += dn * to_f<T>(Hn[base + c]);
+    }
+    dot = block_sum_256(dot, red);
+    mean = dot / (float)d;
+    rr = r[t];
+  }
+  for (int c = threadIdx.x; c < d; c += NT) {
+    float dn = part[base + c];
+    for (int s = 1; s < S; ++s) dn += part[(int64_t)s * pstride + base + c];
+    const float g = rms ? rr * (dn - to_f<T>(Hn[base + c]) * mean) : dn;
+    const float v = dH[base + c] + g;
+    dH[base + c] = v;
+    dHb[base + c] = from_f<T>(v);
+  }
+}
+
+// a8: g = sqrt(sum of the per-tile sums of squares of every fast gradient), in fp64 and a
+// fixed order; s = min(1, clip / g) (clip <= 0: 1); a non-finite g skips the step.
+__global__ void __launch_bounds__(NT) k_gradnorm(const float* __restrict__ slot, int nslot, float clip,
+                                                 float* __restrict__ sc, float* __restrict__ stat,
+                                                 int* __restrict__ err) {
+  __shared__ double red[4];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nslot; i += NT) acc += (double)slot[i];
+  acc = wave_sum_d(acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double g = sqrt((red[0] + red[1]) + (red[2] + red[3]));
+    const bool finite = isfinite(g);
+    double s = 1.0;
+    if (!finite) s = 0.0;
+    else if (clip > 0.f && g > (double)clip) s = (double)clip / g;
+    sc[0] = (float)s;
+    sc[1] = finite ? 0.f : 1.f;
+    stat[0] = (float)g;
+    stat[1] = (float)s;
+    if (!finite) atomicOr(err, ERRBIT_NONFINITE);
+  }
+}
+
+// a9: in-place clipped SGD step of one fast tensor [R x C]:
+//   D <- D - lr * s * G;  W = W0 + D rounded to the GEMM precision, stored in both
+//   orientations (row-major W for one GEMM, W^T for the other).
+template <class T>
+__global__ void __launch_bounds__(NT) k_update(const float* __restrict__ G, float* __restrict__ D,
+                                               const T* __restrict__ W0, T* __restrict__ Wop,
+                                               T* __restrict__ WopT, int R, int C, float lr,
+                                               const float* __restrict__ sc) {
+  if (sc[1] != 0.f) return;  // non-finite gradient norm: no step for this chunk
+  const float step = lr * sc[0];
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int r = r0 + k, c = c0 + tx;
+    if (r < R && c < C) {
+      const int64_t i = (int64_t)r * C + c;
+      const float dn = D[i] - step * G[i];
+      D[i] = dn;
+      const T w = from_f<T>(to_f<T>(W0[i]) + dn);
+      Wop[i] = w;
+      tile[k][tx] = w;
+    }
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int c = c0 + k, r = r0 + tx;
+    if (c < C && r < R) WopT[(int64_t)c * R + r] = tile[tx][k];
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(NT) k_export(const float* __restrict__ D, const T* __restrict__ W0, int64_t n,
+                                               int kind, float* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
+    dst[i] = kind ? D[i] : to_f<T>(W0[i]) + D[i];
+}
+
+__global__ void __launch_bounds__(NT) k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) p[i] = v;
+}
+
+inline int grid_for(int64_t n) {
+  int64_t g = (n + NT - 1) / NT;
+  if (g > 4096) g = 4096;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+#define DISPATCH_T(prec, ...)                 \
+  do {                                        \
+    if ((prec) == PREC_BF16) {                \
+      using T = bf16_t;                       \
+      __VA_ARGS__;                            \
+    } else {                                  \
+      using T = float;                        \
+      __VA_ARGS__;                            \
+    }                                         \
+  } while (0)
+
+hipError_t run_gather(hipStream_t st, int prec, const int* tokens, int b, int V, int d, const void* E, float* H,
+                      void* Yb, int* tok_prev, int* tok_tgt, int* err) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_gather<T>, dim3(b), dim3(NT), 0, st, tokens, V, d, (const T*)E, H, (T*)Yb,
+                                      tok_prev, tok_tgt, err));
+  return hipGetLastError();
+}
+
+hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_rmsnorm<T>, dim3(b), dim3(NT), 0, st, H, d, eps, rms, (T*)Hn, r));
+  return hipGetLastError();
+}
+
+hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds, int R, int C, void* dst, int64_t ldd) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  dim3 grid((C + 63) / 64, (R + 63) / 64);
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_transpose<T>, grid, dim3(NT), 0, st, (const T*)src, lds, R, C, (T*)dst, ldd));
+  return hipGetLastError();
+}
+
+hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, int S, int64_t pstride, int64_t n,
+                        void* Yb) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_residual<T>, dim3(grid_for(n)), dim3(NT), 0, st, H, part, S, pstride, n,
+                                      (T*)Yb));
+  return hipGetLastError();
+}
+
+hipError_t run_sum_partials(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int64_t n,
+                            float* out, void* outb) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_sum_partials<T>, dim3(grid_for(n)), dim3(NT), 0, st, part, S, pstride, n,
+                                      out, (T*)outb));
+  return hipGetLastError();
+}
+
+hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int ntiles, int b,
+                        const float* tgt_logit, float* lse, float* loss, int* amax) {
+  hipLaunchKernelGGL(k_ce_merge, dim3((b + 3) / 4), dim3(NT), 0, st, pmax, psum, pidx, ntiles, b, tgt_logit, lse,
+                     loss, amax);
+  return hipGetLastError();
+}
+
+hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int64_t pstride, const void* Hn,
+                        const float* r, int b, int d, int rms, float* dH, void* dHb) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_norm_bwd<T>, dim3(b), dim3(NT), 0, st, part, S, pstride, (const T*)Hn, r, d,
+                                      rms, dH, (T*)dHb));
+  return hipGetLastError();
+}
+
+hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat, int* err) {
+  hipLaunchKernelGGL(k_gradnorm, dim3(1), dim3(NT), 0, st, slot, nslot, clip, sc, stat, err);
+  return hipGetLastError();
+}
+
+hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WopT, int R,
+                      int C, float lr, const float* sc) {
+  dim3 grid((C + 63) / 64, (R + 63) / 64);
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, G, D, (const T*)W0, (T*)Wop, (T*)WopT, R,
+                                      C, lr, sc));
+  return hipGetLastError();
+}
+
+hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_export<T>, dim3(grid_for(n)), dim3(NT), 0, st, D, (const T*)W0, n, kind, dst));
+  return hipGetLastError();
+}
+
+hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n)), dim3(NT), 0, st, (uint32_t*)p, n, v);
+  return hipGetLastError();
+}

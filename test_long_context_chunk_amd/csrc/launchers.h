@@ -1,0 +1,59 @@
+// Host-side launchers of the TTT inner-loop kernels. Every launcher enqueues on `st` and
+// returns the launch status; `prec` is PREC_FP32 or PREC_BF16 and selects the element type
+// of the GEMM-operand buffers (void* below). fp32 buffers are typed float*.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum { PREC_FP32 = 0, PREC_BF16 = 1 };
+
+// ---- row / elementwise kernels (kernels.hip)
+hipError_t run_gather(hipStream_t st, int prec, const int* tokens, int b, int V, int d, const void* E, float* H,
+                      void* Yb, int* tok_prev, int* tok_tgt, int* err);
+hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r);
+hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds, int R, int C, void* dst, int64_t ldd);
+hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, int S, int64_t pstride, int64_t n,
+                        void* Yb);
+hipError_t run_sum_partials(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int64_t n,
+                            float* out, void* outb);
+hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int ntiles, int b,
+                        const float* tgt_logit, float* lse, float* loss, int* amax);
+hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int64_t pstride, const void* Hn,
+                        const float* r, int b, int d, int rms, float* dH, void* dHb);
+hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat, int* err);
+hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WopT, int R,
+                      int C, float lr, const float* sc);
+hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst);
+hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
+
+// ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
+// Tile rows of the CE partial buffers: one (max, sum, argmax) triple per row and per
+// GEMM_CE_BN-wide vocab tile.
+constexpr int GEMM_CE_BN = 128;
+
+// Plain fp32 output; split-K partial slab s lands at C + s * split_stride; accumulate adds
+// to the existing values instead of overwriting them.
+hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                    int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate);
+// GELU up-projection epilogue: A = GELU(U) [M x lda], A^T [N x ldat], GELU'(U) [M x lda].
+hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                     int K, void* A, void* AT, void* GP, int64_t lda, int64_t ldat);
+// SwiGLU up epilogue: A = SiLU(UG) * (X Y^T), A [M x lda], A^T [N x ldat].
+hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                       int K, const float* UG, void* A, void* AT, int64_t lda, int64_t ldat);
+// GELU backward epilogue: dU = (X Y^T) * GP, dU [M x ld], dU^T [N x ldt].
+hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                   int K, const void* GP, void* DU, void* DUT, int64_t ld, int64_t ldt);
+// Weight-gradient epilogue: G [M x ldg] fp32 and one sum of squares per output tile in
+// slot[tile]; returns the number of slots via *nslots when non-null.
+hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                     int K, float* G, int64_t ldg, float* slot);
+int gemm_grad_slots(int M, int N);
+// LM head + online-softmax partials over the full vocabulary (N = V).
+hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
+                           int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit);
+// Recomputed logits of one vocab super-tile -> dlogits P = (softmax - onehot) / b.
+hipError_t gemm_ce_prob(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
+                        int N, int K, const int* tgt, const float* lse, void* P, int64_t ldp, int col_base,
+                        float inv_b);

@@ -1,0 +1,529 @@
+// Host side of the C ABI declared in include/ttt.h: configuration checks, the device
+// memory plan, weight ingestion, and the chunk loop that enqueues the kernels.
+#include <new>
+#include <vector>
+
+#include "common.h"
+#include "launchers.h"
+#include "ttt.h"
+
+namespace {
+
+constexpr int SPLIT_MAX = 8;       // split-K slabs for the small-M, long-K GEMMs
+constexpr int VOCAB_SUPER = 16384;  // vocab columns of dlogits recomputed per CE-backward pass
+constexpr int PAD = 64;             // token dimension of transposed activations is padded to this
+
+struct FastTensor {
+  int rows = 0, cols = 0;  // natural layout [rows x cols] (W1 [d x m], W2 [m x d])
+  void* W0 = nullptr;      // initial weights (GEMM precision)
+  float* D = nullptr;      // accumulated update, fp32
+  void* Wop = nullptr;     // bf16/fp32 copy of W0 + D, [rows x cols]
+  void* WopT = nullptr;    // the same, transposed [cols x rows]
+  float* G = nullptr;      // chunk gradient, fp32 [rows x cols]
+  int slot0 = 0;           // first grad-norm slot
+};
+
+struct Block {
+  FastTensor w1, w2;        // w1 unused for SwiGLU
+  void* WgT = nullptr;      // SwiGLU frozen gate, [m x d]
+  void* WuT = nullptr;      // SwiGLU frozen up, [m x d]
+  void* Hn = nullptr;       // normed block input [b x d]
+  void* HnT = nullptr;      // its transpose [d x bp]
+  float* r = nullptr;       // RMSNorm scale per token [b]
+  void* AT = nullptr;       // activation transpose [m x bp]
+  void* GP = nullptr;       // GELU'(U) [b x m]
+};
+
+}  // namespace
+
+struct ttt_ctx {
+  ttt_config cfg{};
+  hipStream_t st = nullptr;
+  int prec = 0, es = 4;
+  int b = 0, bp = 0, V = 0, d = 0, m = 0, L = 0;
+  int vs = 0;  // vocab super-tile width
+  std::vector<void*> allocs;
+
+  void *E_in = nullptr, *E_out = nullptr, *E_outT = nullptr;
+  std::vector<Block> blocks;
+  std::vector<FastTensor*> fast;
+
+  float* H = nullptr;
+  void* Yb = nullptr;
+  int *tok_prev = nullptr, *tok_tgt = nullptr;
+  float *pmax = nullptr, *psum = nullptr, *tgt_logit = nullptr, *lse = nullptr;
+  int* pidx = nullptr;
+  int ce_tiles = 0;
+  void* P = nullptr;
+  float* part = nullptr;
+  float* dH = nullptr;
+  void *dHb = nullptr, *dHT = nullptr, *A = nullptr, *dU = nullptr, *dUT = nullptr;
+  float* UG = nullptr;
+  float* slots = nullptr;
+  int nslots = 0;
+  float* sc = nullptr;
+  float* losses = nullptr;
+  int* amax = nullptr;
+  float* stats = nullptr;
+  int* err = nullptr;
+  int64_t max_chunks = 0;
+
+  int64_t pos = 0;
+  ttt_status sticky = TTT_OK;
+
+  // tracing: event pairs around launches of the kinds set in prof_mask
+  uint32_t prof_mask = 0;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<int> ev_kind;
+};
+
+namespace {
+
+struct HipFail {
+  ttt_status s;
+};
+
+inline void check(hipError_t e) {
+  if (e == hipErrorOutOfMemory) throw HipFail{TTT_ENOMEM};
+  if (e != hipSuccess) throw HipFail{TTT_EDEVICE};
+}
+
+template <class P>
+P* dalloc(ttt_ctx* c, int64_t bytes) {
+  void* p = nullptr;
+  if (bytes <= 0) bytes = 16;
+  check(hipMalloc(&p, (size_t)bytes));
+  c->allocs.push_back(p);
+  return (P*)p;
+}
+
+void free_all(ttt_ctx* c) {
+  for (void* p : c->allocs) (void)hipFree(p);
+  c->allocs.clear();
+}
+
+inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Split-K factor for a 128 x 128-tiled GEMM with a small output and a long K: enough
+// workgroups to cover the chip twice, at least 4 K-iterations per split.
+int choose_splits(int M, int N, int K, int es) {
+  const int tiles = cdiv(M, 128) * cdiv(N, 128);
+  const int kiters = cdiv(K, 128 / es);
+  int s = cdiv(512, tiles);
+  if (s > kiters / 4) s = kiters / 4;
+  if (s > SPLIT_MAX) s = SPLIT_MAX;
+  if (s < 1) s = 1;
+  return s;
+}
+
+ttt_status validate(const ttt_config* c, const ttt_weights* w) {
+  if (!c || !w) return TTT_EINVAL;
+  if (c->abi_version != TTT_ABI_VERSION || c->reserved != 0 || c->reserved_f != 0.f) return TTT_EINVAL;
+  if (c->vocab < 2 || c->vocab % 8 || c->d_model < 8 || c->d_model % 8 || c->d_hidden < 8 || c->d_hidden % 8)
+    return TTT_EINVAL;
+  if (c->n_blocks < 0 || c->n_blocks > 64) return TTT_EINVAL;
+  if (c->mlp != TTT_MLP_GELU && c->mlp != TTT_MLP_SWIGLU_W2) return TTT_EINVAL;
+  if (c->mlp == TTT_MLP_SWIGLU_W2 && c->n_blocks != 1) return TTT_EINVAL;
+  if (c->norm != TTT_NORM_NONE && c->norm != TTT_NORM_RMS) return TTT_EINVAL;
+  if (c->precision != TTT_FP32 && c->precision != TTT_BF16) return TTT_EINVAL;
+  if (c->chunk < 1 || c->chunk > (1 << 20)) return TTT_EINVAL;
+  if (c->max_tokens < c->chunk || c->max_tokens % c->chunk) return TTT_EINVAL;
+  if (!(c->lr >= 0.f) || !(c->rms_eps >= 0.f) || c->clip != c->clip) return TTT_EINVAL;
+  if (c->norm == TTT_NORM_RMS && !(c->rms_eps > 0.f)) return TTT_EINVAL;
+  if ((int64_t)c->vocab * c->d_model > (int64_t)1 << 31) return TTT_EINVAL;
+  if (!w->embed || !w->lm_head) return TTT_EINVAL;
+  if (c->n_blocks > 0) {
+    if (!w->w1 || !w->w2) return TTT_EINVAL;
+    if (c->mlp == TTT_MLP_SWIGLU_W2 && !w->w_up) return TTT_EINVAL;
+    for (int l = 0; l < c->n_blocks; ++l) {
+      if (!w->w1[l] || !w->w2[l]) return TTT_EINVAL;
+      if (c->mlp == TTT_MLP_SWIGLU_W2 && !w->w_up[l]) return TTT_EINVAL;
+    }
+  }
+  return TTT_OK;
+}
+
+void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
+  const int64_t n = (int64_t)rows * cols;
+  f.rows = rows;
+  f.cols = cols;
+  f.W0 = dalloc<char>(c, n * c->es);
+  f.D = dalloc<float>(c, n * 4);
+  f.Wop = dalloc<char>(c, n * c->es);
+  f.WopT = dalloc<char>(c, n * c->es);
+  f.G = dalloc<float>(c, n * 4);
+  check(hipMemcpyAsync(f.W0, src, n * c->es, hipMemcpyDeviceToDevice, c->st));
+  f.slot0 = c->nslots;
+  c->nslots += gemm_grad_slots(rows, cols);
+  c->fast.push_back(&f);
+}
+
+void reset_fast(ttt_ctx* c, FastTensor& f) {
+  const int64_t n = (int64_t)f.rows * f.cols;
+  check(run_fill_u32(c->st, f.D, n, 0u));
+  check(hipMemcpyAsync(f.Wop, f.W0, n * c->es, hipMemcpyDeviceToDevice, c->st));
+  check(run_transpose(c->st, c->prec, f.W0, f.cols, f.rows, f.cols, f.WopT, f.rows));
+}
+
+void build(ttt_ctx* c, const ttt_weights* w) {
+  const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L, es = c->es;
+  const int64_t Vd = (int64_t)V * d;
+  c->E_in = dalloc<char>(c, Vd * es);
+  c->E_out = dalloc<char>(c, Vd * es);
+  c->E_outT = dalloc<char>(c, Vd * es);
+  check(hipMemcpyAsync(c->E_in, w->embed, Vd * es, hipMemcpyDeviceToDevice, c->st));
+  check(hipMemcpyAsync(c->E_out, w->lm_head, Vd * es, hipMemcpyDeviceToDevice, c->st));
+  check(run_transpose(c->st, c->prec, c->E_out, d, V, d, c->E_outT, V));
+
+  c->blocks.resize(L);
+  for (int l = 0; l < L; ++l) {
+    Block& B = c->blocks[l];
+    if (c->cfg.mlp == TTT_MLP_GELU) {
+      init_fast(c, B.w1, d, m, w->w1[l]);
+      B.GP = dalloc<char>(c, (int64_t)b * m * es);
+      B.HnT = dalloc<char>(c, (int64_t)d * bp * es);
+      check(hipMemsetAsync(B.HnT, 0, (int64_t)d * bp * es, c->st));
+    } else {
+      B.WgT = dalloc<char>(c, (int64_t)m * d * es);
+      B.WuT = dalloc<char>(c, (int64_t)m * d * es);
+      check(run_transpose(c->st, c->prec, w->w1[l], m, d, m, B.WgT, d));
+      check(run_transpose(c->st, c->prec, w->w_up[l], m, d, m, B.WuT, d));
+    }
+    init_fast(c, B.w2, m, d, w->w2[l]);
+    B.Hn = dalloc<char>(c, (int64_t)b * d * es);
+    B.r = dalloc<float>(c, (int64_t)b * 4);
+    B.AT = dalloc<char>(c, (int64_t)m * bp * es);
+    check(hipMemsetAsync(B.AT, 0, (int64_t)m * bp * es, c->st));
+  }
+  for (FastTensor* f : c->fast) reset_fast(c, *f);
+
+  c->H = dalloc<float>(c, (int64_t)b * d * 4);
+  c->Yb = dalloc<char>(c, (int64_t)b * d * es);
+  c->tok_prev = dalloc<int>(c, (int64_t)b * 4);
+  c->tok_tgt = dalloc<int>(c, (int64_t)b * 4);
+  c->ce_tiles = cdiv(V, GEMM_CE_BN);
+  c->pmax = dalloc<float>(c, (int64_t)c->ce_tiles * b * 4);
+  c->psum = dalloc<float>(c, (int64_t)c->ce_tiles * b * 4);
+  c->pidx = dalloc<int>(c, (int64_t)c->ce_tiles * b * 4);
+  c->tgt_logit = dalloc<float>(c, (int64_t)b * 4);
+  c->lse = dalloc<float>(c, (int64_t)b * 4);
+  c->vs = V < VOCAB_SUPER ? V : VOCAB_SUPER;
+  c->P = dalloc<char>(c, (int64_t)b * c->vs * es);
+  c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * b * d * 4);
+  c->dH = dalloc<float>(c, (int64_t)b * d * 4);
+  c->dHb = dalloc<char>(c, (int64_t)b * d * es);
+  c->dHT = dalloc<char>(c, (int64_t)d * bp * es);
+  check(hipMemsetAsync(c->dHT, 0, (int64_t)d * bp * es, c->st));
+  c->A = dalloc<char>(c, (int64_t)b * m * es);
+  c->dU = dalloc<char>(c, (int64_t)b * m * es);
+  c->dUT = dalloc<char>(c, (int64_t)m * bp * es);
+  check(hipMemsetAsync(c->dUT, 0, (int64_t)m * bp * es, c->st));
+  if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)b * m * 4);
+  c->slots = dalloc<float>(c, (int64_t)(c->nslots > 0 ? c->nslots : 1) * 4);
+  c->sc = dalloc<float>(c, 4 * 4);
+  c->losses = dalloc<float>(c, c->cfg.max_tokens * 4);
+  c->amax = dalloc<int>(c, c->cfg.max_tokens * 4);
+  c->max_chunks = c->cfg.max_tokens / b;
+  c->stats = dalloc<float>(c, c->max_chunks * 2 * 4);
+  c->err = dalloc<int>(c, 4);
+  check(hipMemsetAsync(c->err, 0, 4, c->st));
+  check(hipMemsetAsync(c->losses, 0, c->cfg.max_tokens * 4, c->st));
+  check(hipMemsetAsync(c->amax, 0, c->cfg.max_tokens * 4, c->st));
+  check(hipMemsetAsync(c->stats, 0, c->max_chunks * 2 * 4, c->st));
+}
+
+void prof_mark(ttt_ctx* c) {
+  if (c->ev_used == c->ev_pool.size()) {
+    hipEvent_t e;
+    check(hipEventCreate(&e));
+    c->ev_pool.push_back(e);
+  }
+  check(hipEventRecord(c->ev_pool[c->ev_used++], c->st));
+}
+
+// Enqueue one launch; bracket it with events when its kind is traced.
+#define RUN(kind, expr)                         \
+  do {                                          \
+    const bool traced_ = (c->prof_mask >> (kind)) & 1u; \
+    if (traced_) prof_mark(c);                  \
+    check(expr);                                \
+    if (traced_) {                              \
+      prof_mark(c);                             \
+      c->ev_kind.push_back(kind);               \
+    }                                           \
+  } while (0)
+
+// One chunk of [E2E] eq. (5): forward at W_{i-1}, record l_t(W_{i-1}) (eq. 6), backward
+// to every fast tensor, global-norm clip ([SGF]), SGD step.
+void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
+  hipStream_t st = c->st;
+  const int prec = c->prec, es = c->es;
+  const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L;
+  const int rms = c->cfg.norm == TTT_NORM_RMS;
+  const bool gelu = c->cfg.mlp == TTT_MLP_GELU;
+  const int64_t bd = (int64_t)b * d;
+
+  // a1 gather
+  RUN(TTT_K_GATHER, run_gather(st, prec, tok, b, V, d, c->E_in, c->H, L == 0 ? c->Yb : nullptr, c->tok_prev,
+                               c->tok_tgt, c->err));
+
+  // a2-a4 forward through the blocks
+  for (int l = 0; l < L; ++l) {
+    Block& B = c->blocks[l];
+    RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r));
+    if (gelu) {
+      RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
+      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, B.w1.WopT, d, b, m, d, c->A, B.AT, B.GP, m, bp));
+    } else {
+      RUN(TTT_K_UP, gemm_f32(st, prec, B.Hn, d, B.WgT, d, b, m, d, 1, c->UG, m, 0, 0));
+      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, b, m, d, c->UG, c->A, B.AT, m, bp));
+    }
+    const int S = choose_splits(b, d, m, es);
+    RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, B.w2.WopT, m, b, d, m, S, c->part, d, bd, 0));
+    RUN(TTT_K_RESIDUAL, run_residual(st, prec, c->H, c->part, S, bd, bd, l == L - 1 ? c->Yb : nullptr));
+  }
+
+  // a5 LM head + CE forward (vocab-tiled online softmax, no b x V buffer)
+  RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, b, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
+                                    c->tgt_logit));
+  RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_tiles, b, c->tgt_logit, c->lse,
+                                   c->losses + tokpos, c->amax + tokpos));
+
+  const int64_t chunk_idx = tokpos / b;
+  if (L > 0) {
+    // a6 CE backward: dlogits recomputed per vocab super-tile, dY = sum over tiles of P E_out
+    const int S2 = choose_splits(b, d, c->vs, es);
+    const float inv_b = 1.0f / (float)b;
+    for (int v0 = 0, s = 0; v0 < V; v0 += c->vs, ++s) {
+      const int vn = (V - v0) < c->vs ? (V - v0) : c->vs;
+      RUN(TTT_K_CE_PROB, gemm_ce_prob(st, prec, c->Yb, d, (const char*)c->E_out + (int64_t)v0 * d * es, d, b, vn, d,
+                                      c->tok_tgt, c->lse, c->P, c->vs, v0, inv_b));
+      RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, c->vs, (const char*)c->E_outT + (int64_t)v0 * es, V, b, d, vn, S2,
+                                c->part, d, bd, s > 0));
+    }
+    RUN(TTT_K_DY_SUM, run_sum_partials(st, prec, c->part, S2, bd, bd, c->dH, c->dHb));
+    RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+
+    // a7 block backward, top to bottom
+    for (int l = L - 1; l >= 0; --l) {
+      Block& B = c->blocks[l];
+      RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
+      if (!gelu) continue;  // SwiGLU: only W2 is fast and the block is the lowest one
+      RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT, m, bp));
+      RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
+      if (l > 0) {
+        const int S = choose_splits(b, d, m, es);
+        RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
+        RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb));
+        RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+      }
+    }
+  }
+
+  // a8 global grad norm and clip scale; a9 update
+  RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx, c->err));
+  for (FastTensor* f : c->fast)
+    RUN(TTT_K_UPDATE, run_update(st, prec, f->G, f->D, f->W0, f->Wop, f->WopT, f->rows, f->cols, c->cfg.lr, c->sc));
+}
+
+ttt_status read_sticky(ttt_ctx* c) {
+  int e = 0;
+  check(hipMemcpyAsync(&e, c->err, 4, hipMemcpyDeviceToHost, c->st));
+  check(hipStreamSynchronize(c->st));
+  if (c->sticky == TTT_OK) {
+    if (e & ERRBIT_RANGE) c->sticky = TTT_ERANGE;
+    else if (e & ERRBIT_NONFINITE) c->sticky = TTT_ENONFINITE;
+  }
+  return c->sticky;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out) {
+  if (!out) return TTT_EINVAL;
+  *out = nullptr;
+  ttt_status v = validate(cfg, w);
+  if (v != TTT_OK) return v;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return TTT_EDEVICE;
+  ttt_ctx* c = new (std::nothrow) ttt_ctx();
+  if (!c) return TTT_ENOMEM;
+  c->cfg = *cfg;
+  c->st = (hipStream_t)stream;
+  c->prec = cfg->precision == TTT_BF16 ? PREC_BF16 : PREC_FP32;
+  c->es = c->prec == PREC_BF16 ? 2 : 4;
+  c->b = cfg->chunk;
+  c->bp = (cfg->chunk + PAD - 1) / PAD * PAD;
+  c->V = cfg->vocab;
+  c->d = cfg->d_model;
+  c->m = cfg->d_hidden;
+  c->L = cfg->n_blocks;
+  try {
+    build(c, w);
+    check(hipStreamSynchronize(c->st));
+  } catch (const HipFail& f) {
+    (void)hipStreamSynchronize(c->st);
+    free_all(c);
+    delete c;
+    return f.s;
+  } catch (const std::bad_alloc&) {
+    (void)hipStreamSynchronize(c->st);
+    free_all(c);
+    delete c;
+    return TTT_ENOMEM;
+  }
+  *out = c;
+  return TTT_OK;
+}
+
+ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_tokens) {
+  if (!c || !tokens) return TTT_EINVAL;
+  if (c->sticky != TTT_OK) return TTT_ESTATE;
+  if (n_tokens <= 0 || n_tokens % c->b) return TTT_EINVAL;
+  if (c->pos + n_tokens > c->cfg.max_tokens) return TTT_EINVAL;
+  try {
+    for (int64_t i = 0; i < n_tokens; i += c->b) run_chunk(c, tokens + i, c->pos + i);
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  c->pos += n_tokens;
+  return TTT_OK;
+}
+
+ttt_status ttt_sync(ttt_ctx* c) {
+  if (!c) return TTT_EINVAL;
+  try {
+    return read_sticky(c);
+  } catch (const HipFail& f) {
+    return f.s;
+  }
+}
+
+static ttt_status copy_record(ttt_ctx* c, void* dst, const void* src, int64_t offset, int64_t n, int64_t limit,
+                              int64_t elem) {
+  if (!c || (!dst && n > 0) || offset < 0 || n < 0 || offset + n > limit) return TTT_EINVAL;
+  try {
+    if (n > 0)
+      check(hipMemcpyAsync(dst, (const char*)src + offset * elem, n * elem, hipMemcpyDeviceToDevice, c->st));
+    return read_sticky(c);
+  } catch (const HipFail& f) {
+    return f.s;
+  }
+}
+
+ttt_status ttt_token_losses(ttt_ctx* c, float* dst, int64_t offset, int64_t n) {
+  if (!c) return TTT_EINVAL;
+  return copy_record(c, dst, c->losses, offset, n, c->pos, 4);
+}
+
+ttt_status ttt_token_argmax(ttt_ctx* c, int32_t* dst, int64_t offset, int64_t n) {
+  if (!c) return TTT_EINVAL;
+  return copy_record(c, dst, c->amax, offset, n, c->pos, 4);
+}
+
+ttt_status ttt_chunk_stats(ttt_ctx* c, float* dst, int64_t offset, int64_t n) {
+  if (!c) return TTT_EINVAL;
+  if (!dst && n > 0) return TTT_EINVAL;
+  if (offset < 0 || n < 0 || offset + n > c->pos / c->b) return TTT_EINVAL;
+  try {
+    if (n > 0) check(hipMemcpyAsync(dst, c->stats + 2 * offset, n * 8, hipMemcpyDeviceToDevice, c->st));
+    return read_sticky(c);
+  } catch (const HipFail& f) {
+    return f.s;
+  }
+}
+
+ttt_status ttt_fast_weights(ttt_ctx* c, int32_t block, int32_t which, int32_t kind, float* dst) {
+  if (!c || !dst || block < 0 || block >= c->L || (kind != 0 && kind != 1)) return TTT_EINVAL;
+  if (which != 1 && which != 2) return TTT_EINVAL;
+  if (which == 1 && c->cfg.mlp != TTT_MLP_GELU) return TTT_EINVAL;
+  FastTensor& f = which == 1 ? c->blocks[block].w1 : c->blocks[block].w2;
+  try {
+    check(run_export(c->st, c->prec, f.D, f.W0, (int64_t)f.rows * f.cols, kind, dst));
+    return read_sticky(c);
+  } catch (const HipFail& e) {
+    return e.s;
+  }
+}
+
+ttt_status ttt_reset(ttt_ctx* c) {
+  if (!c) return TTT_EINVAL;
+  try {
+    for (FastTensor* f : c->fast) reset_fast(c, *f);
+    check(run_fill_u32(c->st, c->err, 1, 0u));
+  } catch (const HipFail& f) {
+    return f.s;
+  }
+  c->pos = 0;
+  c->sticky = TTT_OK;
+  return TTT_OK;
+}
+
+int64_t ttt_tokens_consumed(const ttt_ctx* c) { return c ? c->pos : -1; }
+
+ttt_status ttt_profile_enable(ttt_ctx* c, uint32_t mask) {
+  if (!c || (mask >> TTT_K_COUNT) != 0) return TTT_EINVAL;
+  c->prof_mask = mask;
+  return TTT_OK;
+}
+
+ttt_status ttt_profile_read(ttt_ctx* c, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return TTT_EINVAL;
+  for (int k = 0; k < TTT_K_COUNT; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  try {
+    check(hipStreamSynchronize(c->st));
+    for (size_t p = 0; p < c->ev_kind.size(); ++p) {
+      float ms = 0.f;
+      check(hipEventElapsedTime(&ms, c->ev_pool[2 * p], c->ev_pool[2 * p + 1]));
+      total_ms[c->ev_kind[p]] += ms;
+      launches[c->ev_kind[p]] += 1;
+    }
+  } catch (const HipFail& f) {
+    return f.s;
+  }
+  c->ev_used = 0;
+  c->ev_kind.clear();
+  return TTT_OK;
+}
+
+ttt_status ttt_destroy(ttt_ctx* c) {
+  if (!c) return TTT_OK;
+  (void)hipStreamSynchronize(c->st);
+  for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+  free_all(c);
+  delete c;
+  return TTT_OK;
+}
+
+const char* ttt_status_string(ttt_status s) {
+  switch (s) {
+    case TTT_OK: return "ok";
+    case TTT_EINVAL: return "invalid argument or configuration";
+    case TTT_ENOMEM: return "device out of memory";
+    case TTT_EDEVICE: return "HIP device or runtime error";
+    case TTT_ERANGE: return "token id out of range";
+    case TTT_ENONFINITE: return "non-finite gradient norm (update skipped)";
+    case TTT_ESTATE: return "context holds a sticky error";
+  }
+  return "unknown status";
+}
+
+ttt_status ttt_test_gemm(int32_t precision, const void* X, int64_t ldx, const void* Y, int64_t ldy, float* C,
+                         int64_t ldc, int32_t M, int32_t N, int32_t K, void* stream) {
+  if (precision != TTT_FP32 && precision != TTT_BF16) return TTT_EINVAL;
+  if (!X || !Y || !C || M < 0 || N < 0 || K < 0) return TTT_EINVAL;
+  const int kc = precision == TTT_BF16 ? 8 : 4;
+  if (K % kc || ldx % kc || ldy % kc || ldx < K || ldy < K || ldc < N) return TTT_EINVAL;
+  const int prec = precision == TTT_BF16 ? PREC_BF16 : PREC_FP32;
+  hipError_t e = gemm_f32((hipStream_t)stream, prec, X, ldx, Y, ldy, M, N, K, 1, C, ldc, 0, 0);
+  return e == hipSuccess ? TTT_OK : TTT_EDEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+"""The C-ABI library loads and exports every function include/ttt.h declares (no GPU needed).
+
+Only host-side paths are exercised here: symbol lookup, the status strings, and argument
+validation that ttt_create / ttt_test_gemm perform before touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import test_long_context_chunk_amd as ttt
+from test_long_context_chunk_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ttt_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ttt.lib_path()):
+        pytest.fail("the HIP library is not built (run python -m test_long_context_chunk_amd.build)")
+    return ttt.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["ttt_create", "ttt_prefill_chunks", "ttt_token_losses", "ttt_fast_weights", "ttt_destroy"]:
+        assert must in names
+    assert set(names) == set(B.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in B.STATUS:
+        s = lib.ttt_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.ttt_status_string(123) == b"unknown status"
+
+
+def test_config_struct_layout_matches_header():
+    # int32 x 10, int64, float x 4 -> 40 + 8 + 16 bytes
+    assert ctypes.sizeof(B.Config) == 64
+    assert B.Config.max_tokens.offset == 40
+    assert ctypes.sizeof(B.Weights) == 5 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def _cfg(**kw):
+    base = dict(abi_version=B.ABI_VERSION, vocab=256, d_model=64, d_hidden=256, n_blocks=1, mlp=0,
+                norm=0, precision=0, chunk=1, reserved=0, max_tokens=128, lr=0.1, clip=0.0,
+                rms_eps=1e-6, reserved_f=0.0)
+    base.update(kw)
+    return B.Config(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(abi_version=99), dict(vocab=1), dict(vocab=250), dict(d_model=60), dict(d_hidden=12),
+    dict(n_blocks=-1), dict(mlp=7), dict(norm=3), dict(precision=5), dict(chunk=0),
+    dict(max_tokens=0), dict(max_tokens=130, chunk=4), dict(lr=-1.0), dict(reserved=1),
+    dict(mlp=1, n_blocks=2), dict(norm=1, rms_eps=0.0), dict(clip=float("nan")),
+])
+def test_create_rejects_bad_config_before_touching_a_device(lib, bad):
+    cfg = _cfg(**bad)
+    dummy = (ctypes.c_void_p * 1)(1)
+    w = B.Weights(1, 1, ctypes.cast(dummy, ctypes.POINTER(ctypes.c_void_p)), None,
+                  ctypes.cast(dummy, ctypes.POINTER(ctypes.c_void_p)))
+    out = ctypes.c_void_p(12345)
+    assert lib.ttt_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out)) == -1
+    assert out.value is None
+
+
+def test_create_rejects_missing_weights(lib):
+    cfg = _cfg()
+    w = B.Weights(None, None, None, None, None)
+    out = ctypes.c_void_p()
+    assert lib.ttt_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out)) == -1
+
+
+def test_null_context_calls_are_rejected(lib):
+    assert lib.ttt_prefill_chunks(None, None, 8) == -1
+    assert lib.ttt_token_losses(None, None, 0, 0) == -1
+    assert lib.ttt_sync(None) == -1
+    assert lib.ttt_destroy(None) == 0
+    assert lib.ttt_tokens_consumed(None) == -1
+
+
+def test_gemm_hook_validates_shapes(lib):
+    # K not a multiple of the 16-byte operand chunk
+    assert lib.ttt_test_gemm(1, 1, 8, 1, 8, 1, 8, 4, 4, 6, None) == -1
+    assert lib.ttt_test_gemm(0, 1, 8, 1, 8, 1, 8, 4, 4, 6, None) == -1
+    assert lib.ttt_test_gemm(7, 1, 8, 1, 8, 1, 8, 4, 4, 8, None) == -1
