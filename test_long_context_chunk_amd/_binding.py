@@ -98,6 +98,16 @@ def _check(status: int, what: str):
         raise TTTError(status, what)
 
 
+# Sticky conditions found on the device (id out of range, non-finite gradient norm): the
+# record copies still complete, so getters return their data and sync() reports the status.
+_STICKY = (-4, -5)
+
+
+def _check_copy(status: int, what: str):
+    if status != 0 and status not in _STICKY:
+        raise TTTError(status, what)
+
+
 def _ptr(t) -> int:
     return t.data_ptr()
 
@@ -174,21 +184,21 @@ class TTT:
         import torch
         n = self.consumed() - offset if n is None else n
         out = torch.empty(n, dtype=torch.float32, device="cuda")
-        _check(self._lib.ttt_token_losses(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_losses")
+        _check_copy(self._lib.ttt_token_losses(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_losses")
         return out
 
     def token_argmax(self, offset: int = 0, n: Optional[int] = None):
         import torch
         n = self.consumed() - offset if n is None else n
         out = torch.empty(n, dtype=torch.int32, device="cuda")
-        _check(self._lib.ttt_token_argmax(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_argmax")
+        _check_copy(self._lib.ttt_token_argmax(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_argmax")
         return out
 
     def chunk_stats(self, offset: int = 0, n: Optional[int] = None):
         import torch
         n = self.consumed() // self.chunk - offset if n is None else n
         out = torch.empty((n, 2), dtype=torch.float32, device="cuda")
-        _check(self._lib.ttt_chunk_stats(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_chunk_stats")
+        _check_copy(self._lib.ttt_chunk_stats(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_chunk_stats")
         return out
 
     def fast_weight(self, block: int, which: str, kind: str = "W"):
@@ -196,8 +206,8 @@ class TTT:
         import torch
         shape = (self.d_model, self.d_hidden) if which == "W1" else (self.d_hidden, self.d_model)
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
-        _check(self._lib.ttt_fast_weights(self._ctx, block, 1 if which == "W1" else 2,
-                                          0 if kind == "W" else 1, c_void_p(_ptr(out))), "ttt_fast_weights")
+        _check_copy(self._lib.ttt_fast_weights(self._ctx, block, 1 if which == "W1" else 2,
+                                               0 if kind == "W" else 1, c_void_p(_ptr(out))), "ttt_fast_weights")
         return out
 
     def profile(self, kinds) -> None:

@@ -23,13 +23,18 @@
 
 #include "common.h"
 
+// A GEMM may carry a second K-segment: C = X Y^T + X2 Y2^T (same M, N). The kernel walks
+// the concatenated K range, so the two products share accumulators, tiles and splits.
 struct GemmArgs {
   const void* X;
   const void* Y;
-  int64_t ldx, ldy;  // row strides in elements
-  int M, N, K;
+  const void* X2;
+  const void* Y2;
+  int64_t ldx, ldy, ldx2, ldy2;  // row strides in elements
+  int M, N, K, K2;
   int tiles_m, tiles_n;
-  int kiters;  // K-iterations of 128 bytes
+  int kit_a;   // K-iterations (of 128 bytes) of the first segment
+  int kiters;  // K-iterations of both segments
   int kps;     // K-iterations per split
 };
 
@@ -76,21 +81,27 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g, Epi epi) {
   const int lrow = tid >> 3, lch = tid & 7;
   const char* __restrict__ Xp = (const char*)g.X;
   const char* __restrict__ Yp = (const char*)g.Y;
+  const char* __restrict__ X2p = (const char*)g.X2;
+  const char* __restrict__ Y2p = (const char*)g.Y2;
   uint4 ra[BM / 32], rb[BN / 32];
 
   auto gload = [&](int kit) {
-    const int kk = kit * KE + lch * KC;
-    const bool kok = kk < g.K;
+    const bool seg2 = kit >= g.kit_a;
+    const int kk = (seg2 ? kit - g.kit_a : kit) * KE + lch * KC;
+    const bool kok = kk < (seg2 ? g.K2 : g.K);
+    const char* xb = seg2 ? X2p : Xp;
+    const char* yb = seg2 ? Y2p : Yp;
+    const int64_t lx = seg2 ? g.ldx2 : g.ldx, ly = seg2 ? g.ldy2 : g.ldy;
 #pragma unroll
     for (int p = 0; p < BM / 32; ++p) {
       const int r = m0 + p * 32 + lrow;
-      ra[p] = (kok && r < g.M) ? *(const uint4*)(Xp + ((int64_t)r * g.ldx + kk) * (int64_t)sizeof(T))
+      ra[p] = (kok && r < g.M) ? *(const uint4*)(xb + ((int64_t)r * lx + kk) * (int64_t)sizeof(T))
                                : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < BN / 32; ++p) {
       const int r = n0 + p * 32 + lrow;
-      rb[p] = (kok && r < g.N) ? *(const uint4*)(Yp + ((int64_t)r * g.ldy + kk) * (int64_t)sizeof(T))
+      rb[p] = (kok && r < g.N) ? *(const uint4*)(yb + ((int64_t)r * ly + kk) * (int64_t)sizeof(T))
                                : make_uint4(0, 0, 0, 0);
     }
   };
@@ -174,8 +185,9 @@ __device__ __forceinline__ void store4_t<bf16_t>(bf16_t* dst, float v0, float v1
     u.y = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
     *(uint2*)dst = u;
   } else {
-    const float v[4] = {v0, v1, v2, v3};
-    for (int e = 0; e < nvalid; ++e) dst[e] = f2bf(v[e]);
+    if (nvalid > 0) dst[0] = f2bf(v0);
+    if (nvalid > 1) dst[1] = f2bf(v1);
+    if (nvalid > 2) dst[2] = f2bf(v2);
   }
 }
 template <>
@@ -183,8 +195,9 @@ __device__ __forceinline__ void store4_t<float>(float* dst, float v0, float v1, 
   if (nvalid >= 4) {
     *(float4*)dst = make_float4(v0, v1, v2, v3);
   } else {
-    const float v[4] = {v0, v1, v2, v3};
-    for (int e = 0; e < nvalid; ++e) dst[e] = v[e];
+    if (nvalid > 0) dst[0] = v0;
+    if (nvalid > 1) dst[1] = v1;
+    if (nvalid > 2) dst[2] = v2;
   }
 }
 
@@ -195,7 +208,7 @@ struct EpiStoreF32 {
   int64_t split_stride;
   int accumulate;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float* Cs = C + (int64_t)p.split * split_stride;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -214,16 +227,45 @@ struct EpiStoreF32 {
   }
 };
 
+// Per-row sum over the tile's columns of a per-element value v[i][e] (already summed over
+// the wave's j blocks by the caller): 16-lane butterfly, then the two column-half waves are
+// combined through LDS and written to out[tn * ldo + row]. Fixed order, so deterministic.
+// Uses 2 * BM floats of LDS; all threads of the block must call it.
+template <int FM>
+__device__ __forceinline__ void row_partial_store(const EpiPos& p, float (&v)[FM][4], float* out, int64_t ldo) {
+  constexpr int WTM = 16 * FM;
+  float* l1 = (float*)p.smem;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[i][e] = xor16_sum(v[i][e]);
+      if (p.wn == 1 && (p.lane & 15) == 0) l1[p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e] = v[i][e];
+    }
+  __syncthreads();
+  if (p.wn == 0 && (p.lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = epi_row(p, i, e);
+        if (row < p.M) out[(int64_t)p.tn * ldo + row] = v[i][e] + l1[p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e];
+      }
+  }
+}
+
 // Up-projection of a GELU block: U = Hn W1 -> A = GELU(U) (row-major and transposed) and
-// GELU'(U) for the backward pass.
+// GELU'(U) for the backward pass. RES (optional) keeps A - rn(A), the rounding residual of
+// the stored operand, for the first-order loss compensation.
 template <class T>
 struct EpiGelu {
   T* A;     // [M x lda]
   T* AT;    // [N x ldat]
   T* GP;    // [M x lda]
+  T* RES;   // [M x lda] or null
   int64_t lda, ldat;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r0 = epi_row(p, i, 0);
@@ -239,8 +281,11 @@ struct EpiGelu {
           const float u = acc[i][j][e];
           a[e] = gelu_f(u);
           if (e < nv) {
-            A[(int64_t)(r0 + e) * lda + col] = from_f<T>(a[e]);
-            GP[(int64_t)(r0 + e) * lda + col] = from_f<T>(gelu_prime_f(u));
+            const int64_t o = (int64_t)(r0 + e) * lda + col;
+            const T q = from_f<T>(a[e]);
+            A[o] = q;
+            GP[o] = from_f<T>(gelu_prime_f(u));
+            if (RES) RES[o] = from_f<T>(a[e] - to_f<T>(q));
           }
         }
         store4_t<T>(AT + (int64_t)col * ldat + r0, a[0], a[1], a[2], a[3], nv);
@@ -249,15 +294,18 @@ struct EpiGelu {
   }
 };
 
-// Up-projection of a SwiGLU block (gate result already in UG): A = SiLU(UG) * (Hn Wu).
+// Up-projection of a SwiGLU block (gate result already in UG): V = Hn Wu is kept (fp32) for
+// the backward pass, A = SiLU(UG) * V is stored row-major and transposed, RES as above.
 template <class T>
 struct EpiSwiglu {
   const float* UG;  // [M x lda] fp32 gate pre-activation
+  float* VU;        // [M x lda] fp32 up-projection (may be null)
   T* A;
   T* AT;
+  T* RES;           // may be null
   int64_t lda, ldat;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r0 = epi_row(p, i, 0);
@@ -271,8 +319,12 @@ struct EpiSwiglu {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (e < nv) {
-            a[e] = silu_f(UG[(int64_t)(r0 + e) * lda + col]) * acc[i][j][e];
-            A[(int64_t)(r0 + e) * lda + col] = from_f<T>(a[e]);
+            const int64_t o = (int64_t)(r0 + e) * lda + col;
+            a[e] = silu_f(UG[o]) * acc[i][j][e];
+            const T q = from_f<T>(a[e]);
+            A[o] = q;
+            if (VU) VU[o] = acc[i][j][e];
+            if (RES) RES[o] = from_f<T>(a[e] - to_f<T>(q));
           }
         }
         store4_t<T>(AT + (int64_t)col * ldat + r0, a[0], a[1], a[2], a[3], nv);
@@ -281,17 +333,24 @@ struct EpiSwiglu {
   }
 };
 
-// Backward through GELU: dU = (dY W2^T) * GELU'(U), row-major and transposed.
+// Backward through GELU: dA = dY W2^T (the accumulator); dU = dA * GELU'(U), row-major and
+// transposed. With RES, also the per-token partial dot <dA_t, A_t - rn(A_t)> of this tile's
+// columns into cdot[tn * M + row].
 template <class T>
 struct EpiDU {
-  const T* GP;  // [M x ld]
-  T* DU;        // [M x ld]
-  T* DUT;       // [N x ldt]
+  const T* GP;   // [M x ld]
+  T* DU;         // [M x ld]
+  T* DUT;        // [N x ldt]
+  const T* RES;  // [M x ld] or null
+  float* cdot;   // [tiles_n x M] or null
   int64_t ld, ldt;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    float dots[FM][4];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dots[i][e] = 0.f;
       const int r0 = epi_row(p, i, 0);
       const int nv = min(4, p.M - r0);
       if (nv <= 0) continue;
@@ -303,13 +362,55 @@ struct EpiDU {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (e < nv) {
-            v[e] = acc[i][j][e] * to_f<T>(GP[(int64_t)(r0 + e) * ld + col]);
-            DU[(int64_t)(r0 + e) * ld + col] = from_f<T>(v[e]);
+            const int64_t o = (int64_t)(r0 + e) * ld + col;
+            v[e] = acc[i][j][e] * to_f<T>(GP[o]);
+            DU[o] = from_f<T>(v[e]);
+            if (RES) dots[i][e] += acc[i][j][e] * to_f<T>(RES[o]);
           }
         }
         store4_t<T>(DUT + (int64_t)col * ldt + r0, v[0], v[1], v[2], v[3], nv);
       }
     }
+    if (cdot) row_partial_store<FM>(p, dots, cdot, p.M);
+  }
+};
+
+// Backward into a SwiGLU block whose gate/up are frozen (only needed to carry the loss
+// compensation below the block): dA = dY W2^T (accumulator); dG = dA * V * SiLU'(UG),
+// dV = dA * SiLU(UG); plus the per-token partial dot <dA_t, RES_t> as in EpiDU.
+template <class T>
+struct EpiSwigluBwd {
+  const float* UG;
+  const float* VU;
+  T* DG;
+  T* DV;
+  const T* RES;
+  float* cdot;
+  int64_t ld;
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    float dots[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dots[i][e] = 0.f;
+        const int row = epi_row(p, i, e);
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = epi_col(p, j);
+          if (col >= p.N) continue;
+          const int64_t o = (int64_t)row * ld + col;
+          const float da = acc[i][j][e];
+          const float g = UG[o];
+          const float sg = 1.0f / (1.0f + expf(-g));
+          DG[o] = from_f<T>(da * VU[o] * sg * (1.0f + g * (1.0f - sg)));
+          DV[o] = from_f<T>(da * g * sg);
+          dots[i][e] += da * to_f<T>(RES[o]);
+        }
+      }
+    row_partial_store<FM>(p, dots, cdot, p.M);
   }
 };
 
@@ -319,7 +420,7 @@ struct EpiGrad {
   int64_t ldg;
   float* slot;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -364,7 +465,7 @@ struct EpiCEPartial {
   float* tgt_logit;  // [M]
   int ldp;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     constexpr int WTM = 16 * FM, BM = 2 * WTM;
     float* lmax = (float*)p.smem;
     float* lsum = lmax + BM;
@@ -443,7 +544,7 @@ struct EpiCEProb {
   int col_base;  // vocab id of column 0
   float inv_b;
   template <int FM, int FN>
-  __device__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -464,9 +565,18 @@ struct EpiCEProb {
 };
 
 // ------------------------------------------------------------------------- launcher
+// Second K-segment of a GEMM (absent when K2 == 0).
+struct Seg2 {
+  const void* X = nullptr;
+  int64_t ldx = 0;
+  const void* Y = nullptr;
+  int64_t ldy = 0;
+  int K = 0;
+};
+
 template <class T, int BM, int BN, class Epi>
 inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
-                              int N, int K, int splits, const Epi& epi) {
+                              int N, int K, int splits, const Epi& epi, const Seg2& s2 = Seg2()) {
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int KE = 128 / (int)sizeof(T);
   GemmArgs g;
@@ -474,12 +584,18 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
   g.Y = Y;
   g.ldx = ldx;
   g.ldy = ldy;
+  g.X2 = s2.X;
+  g.Y2 = s2.Y;
+  g.ldx2 = s2.ldx;
+  g.ldy2 = s2.ldy;
   g.M = M;
   g.N = N;
   g.K = K;
+  g.K2 = s2.K;
   g.tiles_m = (M + BM - 1) / BM;
   g.tiles_n = (N + BN - 1) / BN;
-  g.kiters = (K + KE - 1) / KE;
+  g.kit_a = (K + KE - 1) / KE;
+  g.kiters = g.kit_a + (s2.K + KE - 1) / KE;
   if (splits < 1) splits = 1;
   g.kps = (g.kiters + splits - 1) / splits;
   dim3 grid(g.tiles_m * g.tiles_n, splits);

@@ -17,35 +17,59 @@ constexpr int BM = 128, BN = 128;
     }                          \
   } while (0)
 
+namespace {
+inline Seg2 seg(const GemmSeg2& s) {
+  Seg2 r;
+  r.X = s.X;
+  r.ldx = s.ldx;
+  r.Y = s.Y;
+  r.ldy = s.ldy;
+  r.K = s.K;
+  return r;
+}
+}  // namespace
+
 hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                    int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate) {
+                    int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate,
+                    const GemmSeg2& s2) {
   EpiStoreF32 e{C, ldc, split_stride, accumulate};
-  DISPATCH_T(prec, return (launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, splits, e)));
+  DISPATCH_T(prec, return (launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, splits, e, seg(s2))));
 }
 
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, void* A, void* AT, void* GP, int64_t lda, int64_t ldat) {
+                     int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat, const GemmSeg2& s2) {
   DISPATCH_T(prec, {
-    EpiGelu<T> e{(T*)A, (T*)AT, (T*)GP, lda, ldat};
-    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    EpiGelu<T> e{(T*)A, (T*)AT, (T*)GP, (T*)RES, lda, ldat};
+    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
   });
 }
 
 hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                       int K, const float* UG, void* A, void* AT, int64_t lda, int64_t ldat) {
+                       int K, const float* UG, float* VU, void* A, void* AT, void* RES, int64_t lda, int64_t ldat) {
   DISPATCH_T(prec, {
-    EpiSwiglu<T> e{UG, (T*)A, (T*)AT, lda, ldat};
+    EpiSwiglu<T> e{UG, VU, (T*)A, (T*)AT, (T*)RES, lda, ldat};
     return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }
 
 hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                   int K, const void* GP, void* DU, void* DUT, int64_t ld, int64_t ldt) {
+                   int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt) {
   DISPATCH_T(prec, {
-    EpiDU<T> e{(const T*)GP, (T*)DU, (T*)DUT, ld, ldt};
+    EpiDU<T> e{(const T*)GP, (T*)DU, (T*)DUT, (const T*)RES, cdot, ld, ldt};
     return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }
+
+hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
+                           int N, int K, const float* UG, const float* VU, void* DG, void* DV, const void* RES,
+                           float* cdot, int64_t ld) {
+  DISPATCH_T(prec, {
+    EpiSwigluBwd<T> e{UG, VU, (T*)DG, (T*)DV, (const T*)RES, cdot, ld};
+    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+  });
+}
+
+int gemm_col_tiles(int N) { return (N + BN - 1) / BN; }
 
 int gemm_grad_slots(int M, int N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 

@@ -44,9 +44,10 @@ __global__ void __launch_bounds__(NT) k_gather(const int* __restrict__ tokens, i
 }
 
 // a2: pre-norm of a block. rms: n = h * (mean h^2 + eps)^(-1/2) (no gain); none: n = h.
+// With RES, also the rounding residual n - rn(n) of the stored GEMM operand.
 template <class T>
 __global__ void __launch_bounds__(NT) k_rmsnorm(const float* __restrict__ H, int d, float eps, int rms,
-                                                T* __restrict__ Hn, float* __restrict__ r) {
+                                                T* __restrict__ Hn, float* __restrict__ r, T* __restrict__ RES) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const float* h = H + (int64_t)t * d;
@@ -59,7 +60,12 @@ __global__ void __launch_bounds__(NT) k_rmsnorm(const float* __restrict__ H, int
   }
   if (threadIdx.x == 0) r[t] = rr;
   T* o = Hn + (int64_t)t * d;
-  for (int c = threadIdx.x; c < d; c += NT) o[c] = from_f<T>(h[c] * rr);
+  for (int c = threadIdx.x; c < d; c += NT) {
+    const float n = h[c] * rr;
+    const T q = from_f<T>(n);
+    o[c] = q;
+    if (RES) RES[(int64_t)t * d + c] = from_f<T>(n - to_f<T>(q));
+  }
 }
 
 // dst[c, r] = src[r, c] for r < R, c < C through a 64 x 64 LDS tile.
@@ -94,16 +100,40 @@ __global__ void __launch_bounds__(NT) k_residual(float* __restrict__ H, const fl
   }
 }
 
-// out = sum_s part[s] (fixed order), plus its GEMM-precision copy.
+// a6 finish, one block per token row: dY = sum_s part[s] (fixed order) into dH and its
+// GEMM-precision copy. With Hres (the fp32 hidden state whose rounded copy Yb fed the LM
+// head), also cdot[t] = <dY_t, H_t - rn(H_t)> for the first-order loss compensation.
 template <class T>
-__global__ void __launch_bounds__(NT) k_sum_partials(const float* __restrict__ part, int S, int64_t pstride,
-                                                     int64_t n, float* __restrict__ out, T* __restrict__ outb) {
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
-    float acc = part[i];
-    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * pstride + i];
-    out[i] = acc;
-    outb[i] = from_f<T>(acc);
+__global__ void __launch_bounds__(NT) k_dy_finish(const float* __restrict__ part, int S, int64_t pstride, int d,
+                                                  float* __restrict__ dH, T* __restrict__ dHb,
+                                                  const float* __restrict__ Hres, const T* __restrict__ Yb,
+                                                  float* __restrict__ cdot) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int64_t base = (int64_t)t * d;
+  float dot = 0.f;
+  for (int c = threadIdx.x; c < d; c += NT) {
+    float acc = part[base + c];
+    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * pstride + base + c];
+    dH[base + c] = acc;
+    dHb[base + c] = from_f<T>(acc);
+    if (cdot) dot += acc * (Hres[base + c] - to_f<T>(Yb[base + c]));
   }
+  if (cdot) {
+    dot = block_sum_256(dot, red);
+    if (threadIdx.x == 0) cdot[t] = dot;
+  }
+}
+
+// Add the first-order rounding compensation to the recorded losses:
+//   l_t += scale * sum_s cpart[s * b + t]   (slots in a fixed order).
+__global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ cpart, int nslot, int b, float scale,
+                                                     float* __restrict__ loss) {
+  const int t = blockIdx.x * NT + threadIdx.x;
+  if (t >= b) return;
+  float acc = 0.f;
+  for (int s = 0; s < nslot; ++s) acc += cpart[(int64_t)s * b + t];
+  loss[t] += scale * acc;
 }
 
 // a5 merge: combine the per-vocab-tile (max, sum exp, argmax) partials of each row in
@@ -138,25 +168,36 @@ __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax,
 
 // a7 norm backward (pre-norm block, through the frozen norm into the residual stream):
 //   dn = sum_s part[s] (= dU W1^T);  rms: dH += r (dn - n mean_j(dn_j n_j));  none: dH += dn.
+// With RES, also cdot[t] = <dn_t, RES_t> (first-order loss compensation of the rounded n);
+// update_dh = 0 computes only that dot (the lowest block, whose input gradient is not needed).
 template <class T>
 __global__ void __launch_bounds__(NT) k_norm_bwd(const float* __restrict__ part, int S, int64_t pstride,
                                                  const T* __restrict__ Hn, const float* __restrict__ r, int d,
-                                                 int rms, float* __restrict__ dH, T* __restrict__ dHb) {
+                                                 int rms, float* __restrict__ dH, T* __restrict__ dHb,
+                                                 const T* __restrict__ RES, float* __restrict__ cdot, int update_dh) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t base = (int64_t)t * d;
   float mean = 0.f, rr = 1.f;
-  if (rms) {
-    float dot = 0.f;
+  if (rms || cdot) {
+    float dot = 0.f, cd = 0.f;
     for (int c = threadIdx.x; c < d; c += NT) {
       float dn = part[base + c];
       for (int s = 1; s < S; ++s) dn += part[(int64_t)s * pstride + base + c];
       dot += dn * to_f<T>(Hn[base + c]);
+      if (cdot) cd += dn * to_f<T>(RES[base + c]);
     }
-    dot = block_sum_256(dot, red);
-    mean = dot / (float)d;
-    rr = r[t];
+    if (rms) {
+      dot = block_sum_256(dot, red);
+      mean = dot / (float)d;
+      rr = r[t];
+    }
+    if (cdot) {
+      cd = block_sum_256(cd, red);
+      if (threadIdx.x == 0) cdot[t] = cd;
+    }
   }
+  if (!update_dh) return;
   for (int c = threadIdx.x; c < d; c += NT) {
     float dn = part[base + c];
     for (int s = 1; s < S; ++s) dn += part[(int64_t)s * pstride + base + c];
@@ -194,13 +235,14 @@ __global__ void __launch_bounds__(NT) k_gradnorm(const float* __restrict__ slot,
 }
 
 // a9: in-place clipped SGD step of one fast tensor [R x C]:
-//   D <- D - lr * s * G;  W = W0 + D rounded to the GEMM precision, stored in both
-//   orientations (row-major W for one GEMM, W^T for the other).
+//   D <- D - lr * s * G;  Wop = rn(W0 + D) row-major (the backward GEMMs' operand);
+//   WtT = transposed copy of rn(D) when delta_t (bf16: the forward GEMMs add X rn(D)^T to
+//   X W0^T, so updates far below W0's rounding step still reach them), else of rn(W0 + D).
 template <class T>
 __global__ void __launch_bounds__(NT) k_update(const float* __restrict__ G, float* __restrict__ D,
                                                const T* __restrict__ W0, T* __restrict__ Wop,
-                                               T* __restrict__ WopT, int R, int C, float lr,
-                                               const float* __restrict__ sc) {
+                                               T* __restrict__ WtT, int R, int C, float lr,
+                                               const float* __restrict__ sc, int delta_t) {
   if (sc[1] != 0.f) return;  // non-finite gradient norm: no step for this chunk
   const float step = lr * sc[0];
   __shared__ T tile[64][65];
@@ -214,13 +256,13 @@ __global__ void __launch_bounds__(NT) k_update(const float* __restrict__ G, floa
       D[i] = dn;
       const T w = from_f<T>(to_f<T>(W0[i]) + dn);
       Wop[i] = w;
-      tile[k][tx] = w;
+      tile[k][tx] = delta_t ? from_f<T>(dn) : w;
     }
   }
   __syncthreads();
   for (int k = ty; k < 64; k += 4) {
     const int c = c0 + k, r = r0 + tx;
-    if (c < C && r < R) WopT[(int64_t)c * R + r] = tile[tx][k];
+    if (c < C && r < R) WtT[(int64_t)c * R + r] = tile[tx][k];
   }
 }
 
@@ -262,8 +304,9 @@ hipError_t run_gather(hipStream_t st, int prec, const int* tokens, int b, int V,
   return hipGetLastError();
 }
 
-hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r) {
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_rmsnorm<T>, dim3(b), dim3(NT), 0, st, H, d, eps, rms, (T*)Hn, r));
+hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r,
+                       void* RES) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_rmsnorm<T>, dim3(b), dim3(NT), 0, st, H, d, eps, rms, (T*)Hn, r, (T*)RES));
   return hipGetLastError();
 }
 
@@ -281,10 +324,15 @@ hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, i
   return hipGetLastError();
 }
 
-hipError_t run_sum_partials(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int64_t n,
-                            float* out, void* outb) {
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_sum_partials<T>, dim3(grid_for(n)), dim3(NT), 0, st, part, S, pstride, n,
-                                      out, (T*)outb));
+hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int b, int d,
+                         float* dH, void* dHb, const float* Hres, const void* Yb, float* cdot) {
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_dy_finish<T>, dim3(b), dim3(NT), 0, st, part, S, pstride, d, dH, (T*)dHb, Hres,
+                                      (const T*)Yb, cdot));
+  return hipGetLastError();
+}
+
+hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss) {
+  hipLaunchKernelGGL(k_loss_correct, dim3((b + NT - 1) / NT), dim3(NT), 0, st, cpart, nslot, b, scale, loss);
   return hipGetLastError();
 }
 
@@ -296,9 +344,10 @@ hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, co
 }
 
 hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int64_t pstride, const void* Hn,
-                        const float* r, int b, int d, int rms, float* dH, void* dHb) {
+                        const float* r, int b, int d, int rms, float* dH, void* dHb, const void* RES, float* cdot,
+                        int update_dh) {
   DISPATCH_T(prec, hipLaunchKernelGGL(k_norm_bwd<T>, dim3(b), dim3(NT), 0, st, part, S, pstride, (const T*)Hn, r, d,
-                                      rms, dH, (T*)dHb));
+                                      rms, dH, (T*)dHb, (const T*)RES, cdot, update_dh));
   return hipGetLastError();
 }
 
@@ -307,11 +356,11 @@ hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip
   return hipGetLastError();
 }
 
-hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WopT, int R,
-                      int C, float lr, const float* sc) {
+hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WtT, int R,
+                      int C, float lr, const float* sc, int delta_t) {
   dim3 grid((C + 63) / 64, (R + 63) / 64);
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, G, D, (const T*)W0, (T*)Wop, (T*)WopT, R,
-                                      C, lr, sc));
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, G, D, (const T*)W0, (T*)Wop, (T*)WtT, R,
+                                      C, lr, sc, delta_t));
   return hipGetLastError();
 }
 

@@ -11,19 +11,22 @@ enum { PREC_FP32 = 0, PREC_BF16 = 1 };
 // ---- row / elementwise kernels (kernels.hip)
 hipError_t run_gather(hipStream_t st, int prec, const int* tokens, int b, int V, int d, const void* E, float* H,
                       void* Yb, int* tok_prev, int* tok_tgt, int* err);
-hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r);
+hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r,
+                       void* RES);
 hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds, int R, int C, void* dst, int64_t ldd);
 hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, int S, int64_t pstride, int64_t n,
                         void* Yb);
-hipError_t run_sum_partials(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int64_t n,
-                            float* out, void* outb);
+hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int b, int d,
+                         float* dH, void* dHb, const float* Hres, const void* Yb, float* cdot);
+hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss);
 hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int ntiles, int b,
                         const float* tgt_logit, float* lse, float* loss, int* amax);
 hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int64_t pstride, const void* Hn,
-                        const float* r, int b, int d, int rms, float* dH, void* dHb);
+                        const float* r, int b, int d, int rms, float* dH, void* dHb, const void* RES, float* cdot,
+                        int update_dh);
 hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat, int* err);
-hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WopT, int R,
-                      int C, float lr, const float* sc);
+hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WtT, int R,
+                      int C, float lr, const float* sc, int delta_t);
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst);
 hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
 
@@ -32,21 +35,41 @@ hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
 // GEMM_CE_BN-wide vocab tile.
 constexpr int GEMM_CE_BN = 128;
 
+// Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).
+struct GemmSeg2 {
+  const void* X = nullptr;
+  int64_t ldx = 0;
+  const void* Y = nullptr;
+  int64_t ldy = 0;
+  int K = 0;
+};
+
 // Plain fp32 output; split-K partial slab s lands at C + s * split_stride; accumulate adds
 // to the existing values instead of overwriting them.
 hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                    int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate);
-// GELU up-projection epilogue: A = GELU(U) [M x lda], A^T [N x ldat], GELU'(U) [M x lda].
+                    int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate,
+                    const GemmSeg2& s2 = GemmSeg2());
+// GELU up-projection epilogue: A = GELU(U) [M x lda], A^T [N x ldat], GELU'(U) [M x lda],
+// and (RES non-null) the rounding residual A - rn(A) [M x lda].
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, void* A, void* AT, void* GP, int64_t lda, int64_t ldat);
-// SwiGLU up epilogue: A = SiLU(UG) * (X Y^T), A [M x lda], A^T [N x ldat].
+                     int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat,
+                     const GemmSeg2& s2 = GemmSeg2());
+// SwiGLU up epilogue: V = X Y^T kept in VU (fp32, may be null), A = SiLU(UG) * V stored as
+// A [M x lda] and A^T [N x ldat], RES as above.
 hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                       int K, const float* UG, void* A, void* AT, int64_t lda, int64_t ldat);
-// GELU backward epilogue: dU = (X Y^T) * GP, dU [M x ld], dU^T [N x ldt].
+                       int K, const float* UG, float* VU, void* A, void* AT, void* RES, int64_t lda, int64_t ldat);
+// GELU backward epilogue: dU = (X Y^T) * GP, dU [M x ld], dU^T [N x ldt]; with RES, per-token
+// partial dots <X Y^T, RES> of each column tile into cdot [tiles x M].
 hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                   int K, const void* GP, void* DU, void* DUT, int64_t ld, int64_t ldt);
+                   int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt);
+// SwiGLU backward through frozen gate/up: dA = X Y^T; dG, dV [M x ld]; partial dots with RES.
+hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
+                           int N, int K, const float* UG, const float* VU, void* DG, void* DV, const void* RES,
+                           float* cdot, int64_t ld);
+// Number of 128-wide column tiles of an N-column GEMM output (partial-dot slots per row).
+int gemm_col_tiles(int N);
 // Weight-gradient epilogue: G [M x ldg] fp32 and one sum of squares per output tile in
-// slot[tile]; returns the number of slots via *nslots when non-null.
+// slot[tile].
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, float* G, int64_t ldg, float* slot);
 int gemm_grad_slots(int M, int N);

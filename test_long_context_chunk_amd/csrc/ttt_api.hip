@@ -13,12 +13,18 @@ constexpr int SPLIT_MAX = 8;       // split-K slabs for the small-M, long-K GEMM
 constexpr int VOCAB_SUPER = 16384;  // vocab columns of dlogits recomputed per CE-backward pass
 constexpr int PAD = 64;             // token dimension of transposed activations is padded to this
 
+// One fast tensor, natural layout [rows x cols] (W1 [d x m], W2 [m x d]). The forward GEMMs
+// read it transposed, the backward GEMMs row-major:
+//   fp32: forward X (W0 + D)^T via WtT; backward X (W0 + D) via Wop.
+//   bf16: forward X W0^T + X rn(D)^T via W0T and WtT (two K-segments, so updates far below
+//         the rounding step of W0 still reach the forward pass); backward X rn(W0 + D) via Wop.
 struct FastTensor {
-  int rows = 0, cols = 0;  // natural layout [rows x cols] (W1 [d x m], W2 [m x d])
-  void* W0 = nullptr;      // initial weights (GEMM precision)
-  float* D = nullptr;      // accumulated update, fp32
-  void* Wop = nullptr;     // bf16/fp32 copy of W0 + D, [rows x cols]
-  void* WopT = nullptr;    // the same, transposed [cols x rows]
+  int rows = 0, cols = 0;
+  void* W0 = nullptr;      // initial weights (GEMM precision) [rows x cols]
+  void* W0T = nullptr;     // bf16 only: W0^T [cols x rows]
+  float* D = nullptr;      // accumulated update, fp32 [rows x cols]
+  void* Wop = nullptr;     // rn(W0 + D) [rows x cols]
+  void* WtT = nullptr;     // bf16: rn(D)^T, fp32: (W0 + D)^T  [cols x rows]
   float* G = nullptr;      // chunk gradient, fp32 [rows x cols]
   int slot0 = 0;           // first grad-norm slot
 };
@@ -27,11 +33,17 @@ struct Block {
   FastTensor w1, w2;        // w1 unused for SwiGLU
   void* WgT = nullptr;      // SwiGLU frozen gate, [m x d]
   void* WuT = nullptr;      // SwiGLU frozen up, [m x d]
+  void* Wg = nullptr;       // SwiGLU frozen gate/up, natural [d x m] (loss compensation only)
+  void* Wu = nullptr;
   void* Hn = nullptr;       // normed block input [b x d]
   void* HnT = nullptr;      // its transpose [d x bp]
   float* r = nullptr;       // RMSNorm scale per token [b]
   void* AT = nullptr;       // activation transpose [m x bp]
   void* GP = nullptr;       // GELU'(U) [b x m]
+  void* ResN = nullptr;     // bf16 only: n - rn(n) [b x d]
+  void* ResA = nullptr;     // bf16 only: A - rn(A) [b x m]
+  float* VU = nullptr;      // SwiGLU + bf16: up projection n Wu [b x m] fp32
+  int cslot = 0;            // first loss-compensation slot of this block
 };
 
 }  // namespace
@@ -59,6 +71,10 @@ struct ttt_ctx {
   float* dH = nullptr;
   void *dHb = nullptr, *dHT = nullptr, *A = nullptr, *dU = nullptr, *dUT = nullptr;
   float* UG = nullptr;
+  void *DG = nullptr, *DV = nullptr;  // SwiGLU + bf16: gradients at the gate / up outputs
+  bool foc = false;                   // first-order loss compensation (bf16 with blocks)
+  float* cpart = nullptr;             // compensation slots [ncslot x b]
+  int ncslot = 0;
   float* slots = nullptr;
   int nslots = 0;
   float* sc = nullptr;
@@ -151,9 +167,13 @@ void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
   f.W0 = dalloc<char>(c, n * c->es);
   f.D = dalloc<float>(c, n * 4);
   f.Wop = dalloc<char>(c, n * c->es);
-  f.WopT = dalloc<char>(c, n * c->es);
+  f.WtT = dalloc<char>(c, n * c->es);
   f.G = dalloc<float>(c, n * 4);
   check(hipMemcpyAsync(f.W0, src, n * c->es, hipMemcpyDeviceToDevice, c->st));
+  if (c->prec == PREC_BF16) {
+    f.W0T = dalloc<char>(c, n * c->es);
+    check(run_transpose(c->st, c->prec, f.W0, cols, rows, cols, f.W0T, rows));
+  }
   f.slot0 = c->nslots;
   c->nslots += gemm_grad_slots(rows, cols);
   c->fast.push_back(&f);
@@ -163,7 +183,10 @@ void reset_fast(ttt_ctx* c, FastTensor& f) {
   const int64_t n = (int64_t)f.rows * f.cols;
   check(run_fill_u32(c->st, f.D, n, 0u));
   check(hipMemcpyAsync(f.Wop, f.W0, n * c->es, hipMemcpyDeviceToDevice, c->st));
-  check(run_transpose(c->st, c->prec, f.W0, f.cols, f.rows, f.cols, f.WopT, f.rows));
+  if (c->prec == PREC_BF16)
+    check(run_fill_u32(c->st, f.WtT, n * c->es / 4, 0u));  // rn(D)^T with D = 0
+  else
+    check(run_transpose(c->st, c->prec, f.W0, f.cols, f.rows, f.cols, f.WtT, f.rows));
 }
 
 void build(ttt_ctx* c, const ttt_weights* w) {
@@ -176,6 +199,9 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   check(hipMemcpyAsync(c->E_out, w->lm_head, Vd * es, hipMemcpyDeviceToDevice, c->st));
   check(run_transpose(c->st, c->prec, c->E_out, d, V, d, c->E_outT, V));
 
+  c->foc = c->prec == PREC_BF16 && L > 0;
+  const int tnm = gemm_col_tiles(m);
+  c->ncslot = 1;  // slot 0: the LM-head input Y
   c->blocks.resize(L);
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
@@ -189,12 +215,25 @@ void build(ttt_ctx* c, const ttt_weights* w) {
       B.WuT = dalloc<char>(c, (int64_t)m * d * es);
       check(run_transpose(c->st, c->prec, w->w1[l], m, d, m, B.WgT, d));
       check(run_transpose(c->st, c->prec, w->w_up[l], m, d, m, B.WuT, d));
+      if (c->foc) {
+        B.Wg = dalloc<char>(c, (int64_t)m * d * es);
+        B.Wu = dalloc<char>(c, (int64_t)m * d * es);
+        check(hipMemcpyAsync(B.Wg, w->w1[l], (int64_t)m * d * es, hipMemcpyDeviceToDevice, c->st));
+        check(hipMemcpyAsync(B.Wu, w->w_up[l], (int64_t)m * d * es, hipMemcpyDeviceToDevice, c->st));
+        B.VU = dalloc<float>(c, (int64_t)b * m * 4);
+      }
     }
     init_fast(c, B.w2, m, d, w->w2[l]);
     B.Hn = dalloc<char>(c, (int64_t)b * d * es);
     B.r = dalloc<float>(c, (int64_t)b * 4);
     B.AT = dalloc<char>(c, (int64_t)m * bp * es);
     check(hipMemsetAsync(B.AT, 0, (int64_t)m * bp * es, c->st));
+    if (c->foc) {
+      B.ResN = dalloc<char>(c, (int64_t)b * d * es);
+      B.ResA = dalloc<char>(c, (int64_t)b * m * es);
+      B.cslot = c->ncslot;
+      c->ncslot += tnm + 1;  // tnm partial dots for A, one for n
+    }
   }
   for (FastTensor* f : c->fast) reset_fast(c, *f);
 
@@ -220,6 +259,14 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->dUT = dalloc<char>(c, (int64_t)m * bp * es);
   check(hipMemsetAsync(c->dUT, 0, (int64_t)m * bp * es, c->st));
   if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)b * m * 4);
+  if (c->foc && c->cfg.mlp == TTT_MLP_SWIGLU_W2) {
+    c->DG = dalloc<char>(c, (int64_t)b * m * es);
+    c->DV = dalloc<char>(c, (int64_t)b * m * es);
+  }
+  if (c->foc) {
+    c->cpart = dalloc<float>(c, (int64_t)c->ncslot * b * 4);
+    check(hipMemsetAsync(c->cpart, 0, (int64_t)c->ncslot * b * 4, c->st));
+  }
   c->slots = dalloc<float>(c, (int64_t)(c->nslots > 0 ? c->nslots : 1) * 4);
   c->sc = dalloc<float>(c, 4 * 4);
   c->losses = dalloc<float>(c, c->cfg.max_tokens * 4);
@@ -256,13 +303,22 @@ void prof_mark(ttt_ctx* c) {
 
 // One chunk of [E2E] eq. (5): forward at W_{i-1}, record l_t(W_{i-1}) (eq. 6), backward
 // to every fast tensor, global-norm clip ([SGF]), SGD step.
+//
+// bf16 only, first-order loss compensation: the forward rounds three kinds of GEMM operands
+// to bf16 (block inputs n, activations A, the LM-head input Y). Each recorded loss is
+// corrected by b * sum <dL/dX_t, X_t - rn(X_t)> over those operands, with dL/dX the
+// chunk-mean-loss gradients the backward pass computes anyway, so l_t matches the loss of
+// the unrounded forward to first order in the rounding error.
 void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   hipStream_t st = c->st;
   const int prec = c->prec, es = c->es;
   const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L;
   const int rms = c->cfg.norm == TTT_NORM_RMS;
   const bool gelu = c->cfg.mlp == TTT_MLP_GELU;
+  const bool bf = prec == PREC_BF16;
+  const bool foc = c->foc;
   const int64_t bd = (int64_t)b * d;
+  const int tnm = gemm_col_tiles(m);
 
   // a1 gather
   RUN(TTT_K_GATHER, run_gather(st, prec, tok, b, V, d, c->E_in, c->H, L == 0 ? c->Yb : nullptr, c->tok_prev,
@@ -271,16 +327,22 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   // a2-a4 forward through the blocks
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
-    RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r));
+    RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
     if (gelu) {
       RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
-      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, B.w1.WopT, d, b, m, d, c->A, B.AT, B.GP, m, bp));
+      GemmSeg2 s2;
+      if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
+      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
+                              foc ? B.ResA : nullptr, m, bp, s2));
     } else {
       RUN(TTT_K_UP, gemm_f32(st, prec, B.Hn, d, B.WgT, d, b, m, d, 1, c->UG, m, 0, 0));
-      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, b, m, d, c->UG, c->A, B.AT, m, bp));
+      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, b, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
+                                foc ? B.ResA : nullptr, m, bp));
     }
-    const int S = choose_splits(b, d, m, es);
-    RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, B.w2.WopT, m, b, d, m, S, c->part, d, bd, 0));
+    const int S = choose_splits(b, d, bf ? 2 * m : m, es);
+    GemmSeg2 s2;
+    if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
+    RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, bd, 0, s2));
     RUN(TTT_K_RESIDUAL, run_residual(st, prec, c->H, c->part, S, bd, bd, l == L - 1 ? c->Yb : nullptr));
   }
 
@@ -302,29 +364,51 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
       RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, c->vs, (const char*)c->E_outT + (int64_t)v0 * es, V, b, d, vn, S2,
                                 c->part, d, bd, s > 0));
     }
-    RUN(TTT_K_DY_SUM, run_sum_partials(st, prec, c->part, S2, bd, bd, c->dH, c->dHb));
+    RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, bd, b, d, c->dH, c->dHb, c->H, c->Yb,
+                                    foc ? c->cpart : nullptr));
     RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
 
     // a7 block backward, top to bottom
     for (int l = L - 1; l >= 0; --l) {
       Block& B = c->blocks[l];
+      float* cA = foc ? c->cpart + (int64_t)B.cslot * b : nullptr;        // tnm slots
+      float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * b : nullptr;  // one slot
       RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
-      if (!gelu) continue;  // SwiGLU: only W2 is fast and the block is the lowest one
-      RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT, m, bp));
-      RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
-      if (l > 0) {
-        const int S = choose_splits(b, d, m, es);
-        RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
-        RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb));
-        RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+      if (gelu) {
+        RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
+                              foc ? B.ResA : nullptr, cA, m, bp));
+        RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
+        // the block input gradient is needed below this block, and for the compensation of
+        // a rounded n (the lowest block's n = E_in[x] is exact when there is no norm)
+        if (l > 0 || (foc && rms)) {
+          const int S = choose_splits(b, d, m, es);
+          RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
+          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb,
+                                           foc ? B.ResN : nullptr, cN, l > 0));
+          if (l > 0) RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+        }
+      } else if (foc) {
+        // SwiGLU (one block, W2 only fast): dA, then dn = dG Wg^T + dV Wu^T, only to carry
+        // the loss compensation of A and n.
+        RUN(TTT_K_DU, gemm_swiglu_bwd(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, c->UG, B.VU, c->DG, c->DV, B.ResA,
+                                      cA, m));
+        if (rms) {
+          const int S = choose_splits(b, d, 2 * m, es);
+          GemmSeg2 s2{c->DV, m, B.Wu, m, m};
+          RUN(TTT_K_DHN, gemm_f32(st, prec, c->DG, m, B.Wg, m, b, d, m, S, c->part, d, bd, 0, s2));
+          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb, B.ResN, cN,
+                                           0));
+        }
       }
     }
+    if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, b, (float)b, c->losses + tokpos));
   }
 
   // a8 global grad norm and clip scale; a9 update
   RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx, c->err));
   for (FastTensor* f : c->fast)
-    RUN(TTT_K_UPDATE, run_update(st, prec, f->G, f->D, f->W0, f->Wop, f->WopT, f->rows, f->cols, c->cfg.lr, c->sc));
+    RUN(TTT_K_UPDATE, run_update(st, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols, c->cfg.lr, c->sc,
+                                 bf ? 1 : 0));
 }
 
 ttt_status read_sticky(ttt_ctx* c) {
