@@ -55,6 +55,10 @@ __device__ __forceinline__ float gelu_prime_f(float u) {
 }
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
+// exp(x) through the hardware base-2 exponential (a few ulp; used where the result is
+// summed into softmax normalisers or dlogits, never for a value that is stored as is).
+__device__ __forceinline__ float exp_fast(float x) { return __expf(x); }
+
 // Butterfly over the 16 lanes that share (lane / 16): every lane ends with the same
 // bitwise result because each step combines two partials of the same lane set.
 __device__ __forceinline__ float xor16_sum(float v) {

@@ -41,17 +41,24 @@ struct GemmArgs {
 struct EpiPos {
   int row0, col0;  // global coordinates of this wave's sub-tile
   int lane, wave, wm, wn;
+  int wgm, wgn;      // wave grid of the workgroup (rows x columns of waves)
+  int bm, bn;        // tile rows and columns
+  int tid, nthr;     // thread index and count of the workgroup
+  int smem_bytes;    // LDS the epilogue may use
   int tm, tn, tile;  // tile coordinates; tile = tn * tiles_m + tm (a stable slot id)
   int split;
   int M, N;
-  char* smem;  // the kernel's LDS, free for the epilogue
+  char* smem;  // the kernel's LDS, free for the epilogue (at least 16 KB)
 };
 
 __device__ __forceinline__ int epi_row(const EpiPos& p, int i, int e) { return p.row0 + 16 * i + 4 * (p.lane >> 4) + e; }
 __device__ __forceinline__ int epi_col(const EpiPos& p, int j) { return p.col0 + 16 * j + (p.lane & 15); }
 
+// Register-staged variant (any K that is a multiple of the 16-byte chunk): global loads go
+// through VGPRs into two LDS stages, with zero fill outside the operands.
 template <class T, int BM, int BN, class Epi>
-__global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g, Epi epi) {
+__global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
+  constexpr int WGM_ = 2, WGN_ = 2;
   constexpr int ROWB = 128;
   constexpr int KE = ROWB / (int)sizeof(T);
   constexpr int KC = 16 / (int)sizeof(T);
@@ -162,6 +169,13 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g, Epi epi) {
   pos.wave = wave;
   pos.wm = wm;
   pos.wn = wn;
+  pos.wgm = 2;
+  pos.wgn = 2;
+  pos.bm = BM;
+  pos.bn = BN;
+  pos.tid = tid;
+  pos.nthr = 256;
+  pos.smem_bytes = 2 * STAGE;
   pos.tm = tm;
   pos.tn = tn;
   pos.tile = tile;
@@ -169,7 +183,137 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g, Epi epi) {
   pos.M = g.M;
   pos.N = g.N;
   pos.smem = smem;
-  epi.template apply<FM, FN>(pos, acc);
+  epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
+}
+
+// Direct-to-LDS variant (K of both segments a multiple of the 128-byte slice): every wave
+// streams whole 8-row blocks of the tile with global_load_lds_dwordx4 (64 lanes x 16 B =
+// one 1 KB block), choosing each lane's source chunk so that the block lands in the same
+// XOR-swizzled layout the MFMA operand reads expect. No VGPR staging, no zero fill: rows
+// past M or N re-read the last valid row and only feed outputs the epilogue never stores.
+// Two LDS stages: the next slice is requested right after the barrier that retires the
+// stage it overwrites.
+template <class T, int BM, int BN, int WGM, int WGN, class Epi>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Epi epi) {
+  constexpr int WGM_ = WGM, WGN_ = WGN;
+  constexpr int NW = WGM * WGN;
+  constexpr int ROWB = 128;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int PW = (BM + BN) / 8 / NW;  // 8-row blocks per wave
+  static_assert(((BM + BN) / 8) % NW == 0 && (BM / 8) % PW == 0, "each wave streams blocks of one operand");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  const int nblk = gridDim.x * gridDim.y;
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int xcd = lin & 7;
+  const int id = xcd * per + min(xcd, rem) + (lin >> 3);
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int split = id / ntiles;
+  const int tile = id - split * ntiles;
+  const int tm = tile % g.tiles_m, tn = tile / g.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kit0 = split * g.kps;
+  const int kit1 = min(g.kiters, kit0 + g.kps);
+
+  // this wave's blocks all belong to X (first BM rows) or all to Y; per-row source
+  // pointers of both K-segments are formed once, outside the K loop
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool xside = wave_s * PW * 8 < BM;
+  const int rbase = xside ? m0 + wave_s * PW * 8 : n0 + wave_s * PW * 8 - BM;
+  const int rlim = (xside ? g.M : g.N) - 1;
+  const int rsub = lane >> 3;
+  const int cbyte = (((lane & 7) ^ rsub) << 4);
+  const char* const b1 = (const char*)(xside ? g.X : g.Y);
+  const char* const b2 = (const char*)(xside ? g.X2 : g.Y2);
+  const int64_t l1 = (xside ? g.ldx : g.ldy) * (int64_t)sizeof(T);
+  const int64_t l2 = (xside ? g.ldx2 : g.ldy2) * (int64_t)sizeof(T);
+  const bool has2 = g.kiters > g.kit_a;
+  const char* p1[PW];
+  const char* p2[PW];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    const int r = min(rbase + q * 8 + rsub, rlim);
+    p1[q] = b1 + (int64_t)r * l1 + cbyte;
+    p2[q] = has2 ? b2 + (int64_t)r * l2 + cbyte : p1[q];
+  }
+  char* const sdst = smem + (wave_s * PW) * 1024;
+  const int kit_a = g.kit_a;
+
+  auto issue = [&](int kit, int stage) {
+    const bool seg2 = kit >= kit_a;
+    const int64_t kb = (int64_t)(seg2 ? kit - kit_a : kit) * ROWB;
+    char* const d = sdst + stage * STAGE;
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)((seg2 ? p2[q] : p1[q]) + kb),
+                                       (__attribute__((address_space(3))) void*)(d + q * 1024), 16, 0, 0);
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (kit0 < kit1) issue(kit0, 0);
+  for (int it = kit0; it < kit1; ++it) {
+    const int cur = (it - kit0) & 1;
+    // own requests for this stage are done, then everyone's (and the other stage is free)
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
+    if (it + 1 < kit1) issue(it + 1, cur ^ 1);
+    const char* sa = smem + cur * STAGE;
+    const char* sb = sa + BM * ROWB;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const int ch = kg * 4 + (lane >> 4);
+      uint4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 16 + (lane & 15);
+        af[i] = *(const uint4*)(sa + r * ROWB + ((ch ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 16 + (lane & 15);
+        bfr[j] = *(const uint4*)(sb + r * ROWB + ((ch ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma_chunk(acc[i][j], af[i], bfr[j], T());
+    }
+  }
+  __syncthreads();  // the epilogue may reuse the LDS
+
+  EpiPos pos;
+  pos.row0 = m0 + wm * WTM;
+  pos.col0 = n0 + wn * WTN;
+  pos.lane = lane;
+  pos.wave = wave;
+  pos.wm = wm;
+  pos.wn = wn;
+  pos.wgm = WGM;
+  pos.wgn = WGN;
+  pos.bm = BM;
+  pos.bn = BN;
+  pos.tid = tid;
+  pos.nthr = NW * 64;
+  pos.smem_bytes = 2 * STAGE;
+  pos.tm = tm;
+  pos.tn = tn;
+  pos.tile = tile;
+  pos.split = split;
+  pos.M = g.M;
+  pos.N = g.N;
+  pos.smem = smem;
+  epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
 }
 
 // ------------------------------------------------------------------------- epilogues
@@ -201,13 +345,214 @@ __device__ __forceinline__ void store4_t<float>(float* dst, float v0, float v1, 
   }
 }
 
+// ---- LDS staging of bf16 tiles, so that global traffic is 16-byte and row-contiguous.
+// A lane's 4 vertically adjacent values (rows r0..r0+3 of one column) travel packed in two
+// dwords: lo half = row r0 (or r0+2), hi half = row r0+1 (or r0+3).
+template <int FM, int FN>
+using Packed = uint32_t[FM][FN][2];
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Copy the LDS tile (R rows of L elements, row stride ldl) to dst rows [g0, g0 + R) and
+// columns [c0, c0 + L), clipped to rows < gr_lim and columns < gc_lim.
+__device__ __forceinline__ void lds_to_global_bf16(const EpiPos& p, const bf16_t* lds, int ldl, int R, int L,
+                                                   bf16_t* dst, int64_t ld, int g0, int c0, int gr_lim, int gc_lim) {
+  const int cpr = L / 8;
+  const bool vec_ok = (ld % 8) == 0;
+  for (int idx = p.tid; idx < R * cpr; idx += p.nthr) {
+    const int r = idx / cpr, c = (idx - r * cpr) * 8;
+    const int gr = g0 + r, gc = c0 + c;
+    if (gr >= gr_lim || gc >= gc_lim) continue;
+    const bf16_t* s = lds + r * ldl + c;
+    bf16_t* d = dst + (int64_t)gr * ld + gc;
+    if (vec_ok && gc + 8 <= gc_lim) {
+      *(uint4*)d = *(const uint4*)s;
+    } else {
+      for (int k = 0; k < 8 && gc + k < gc_lim; ++k) d[k] = s[k];
+    }
+  }
+}
+
+// Row-major store of the tile's values into dst [M x ld]. Returns false (nothing written)
+// when the tile does not fit the LDS; the caller then stores directly.
+// Compile-time tile geometry of an epilogue: BM x BN tile, LDS of the two K stages.
+template <int FM, int FN, int WGM, int WGN>
+struct TileGeo {
+  static constexpr int WTM = 16 * FM, WTN = 16 * FN;
+  static constexpr int BM = WGM * WTM, BN = WGN * WTN;
+  static constexpr int SMEM = 2 * (BM + BN) * 128;
+  static constexpr bool ROWS_PAD = BM * (BN + 8) * 2 <= SMEM;
+  static constexpr int LDR = ROWS_PAD ? BN + 8 : BN;         // row-major staging stride
+  static constexpr bool ROWS_FIT = BM * LDR * 2 <= SMEM;
+  static constexpr int LDC = BM + 8;                          // transposed staging stride
+  static constexpr bool COLS_FIT = BN * LDC * 2 <= SMEM;
+};
+
+template <int FM, int FN, int WGM, int WGN>
+__device__ __forceinline__ bool stage_rows_bf16(const EpiPos& p, const Packed<FM, FN>& v, bf16_t* dst, int64_t ld) {
+  using G = TileGeo<FM, FN, WGM, WGN>;
+  if constexpr (!G::ROWS_FIT) return false;
+  constexpr int ldl = G::LDR, WTM = G::WTM, WTN = G::WTN;
+  bf16_t* lds = (bf16_t*)p.smem;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rl = p.wm * WTM + 16 * i + 4 * (p.lane >> 4);
+      const int cl = p.wn * WTN + 16 * j + (p.lane & 15);
+      lds[(rl + 0) * ldl + cl] = (bf16_t)(v[i][j][0] & 0xffff);
+      lds[(rl + 1) * ldl + cl] = (bf16_t)(v[i][j][0] >> 16);
+      lds[(rl + 2) * ldl + cl] = (bf16_t)(v[i][j][1] & 0xffff);
+      lds[(rl + 3) * ldl + cl] = (bf16_t)(v[i][j][1] >> 16);
+    }
+  __syncthreads();
+  lds_to_global_bf16(p, lds, ldl, G::BM, G::BN, dst, ld, p.row0 - p.wm * WTM, p.col0 - p.wn * WTN, p.M, p.N);
+  return true;
+}
+
+// Transposed store: dstT [N x ldt] receives the tile's columns as rows.
+template <int FM, int FN, int WGM, int WGN>
+__device__ __forceinline__ bool stage_cols_bf16(const EpiPos& p, const Packed<FM, FN>& v, bf16_t* dstT, int64_t ldt) {
+  using G = TileGeo<FM, FN, WGM, WGN>;
+  if constexpr (!G::COLS_FIT) return false;
+  constexpr int ldl = G::LDC, WTM = G::WTM, WTN = G::WTN;
+  bf16_t* lds = (bf16_t*)p.smem;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rl = p.wm * WTM + 16 * i + 4 * (p.lane >> 4);
+      const int cl = p.wn * WTN + 16 * j + (p.lane & 15);
+      *(uint2*)(lds + cl * ldl + rl) = make_uint2(v[i][j][0], v[i][j][1]);
+    }
+  __syncthreads();
+  lds_to_global_bf16(p, lds, ldl, G::BN, G::BM, dstT, ldt, p.col0 - p.wn * WTN, p.row0 - p.wm * WTM, p.N, p.M);
+  return true;
+}
+
+// Load the tile region [rows of the tile] x [columns of the tile] of a row-major bf16
+// matrix into LDS (row stride bn + 8; values outside M x N read as 0). Returns false when
+// it does not fit; afterwards lane values are read with staged_at().
+template <int FM, int FN, int WGM, int WGN>
+__device__ __forceinline__ bool stage_load_bf16(const EpiPos& p, const bf16_t* src, int64_t ld) {
+  using G = TileGeo<FM, FN, WGM, WGN>;
+  if constexpr (!(G::ROWS_PAD && G::ROWS_FIT)) return false;
+  constexpr int ldl = G::BN + 8;
+  bf16_t* lds = (bf16_t*)p.smem;
+  const int g0 = p.row0 - p.wm * G::WTM, c0 = p.col0 - p.wn * G::WTN;
+  constexpr int cpr = G::BN / 8;
+  const bool vec_ok = (ld % 8) == 0;
+  __syncthreads();
+  for (int idx = p.tid; idx < G::BM * cpr; idx += WGM * WGN * 64) {
+    const int r = idx / cpr, c = (idx - r * cpr) * 8;
+    const int gr = g0 + r, gc = c0 + c;
+    bf16_t* dl = lds + r * ldl + c;
+    const bf16_t* s = src + (int64_t)gr * ld + gc;
+    if (gr < p.M && vec_ok && gc + 8 <= p.N) {
+      *(uint4*)dl = *(const uint4*)s;
+    } else {
+      for (int k = 0; k < 8; ++k) dl[k] = (gr < p.M && gc + k < p.N) ? s[k] : (bf16_t)0;
+    }
+  }
+  __syncthreads();
+  return true;
+}
+template <int FM, int FN, int WGM, int WGN>
+__device__ __forceinline__ float staged_at(const EpiPos& p, int rl, int cl) {
+  return bf2f(((const bf16_t*)p.smem)[rl * (TileGeo<FM, FN, WGM, WGN>::BN + 8) + cl]);
+}
+
+// ---- fp32 accumulator tile in LDS, processed by rolled loops (small register footprint,
+// row-contiguous global traffic). Needs BM * BN * 4 bytes of LDS (the 128 x 128 tiles).
+template <int FM, int FN, int WGM, int WGN>
+struct AccTile {
+  using G = TileGeo<FM, FN, WGM, WGN>;
+  static constexpr bool FITS = G::BM * G::BN * 4 <= G::SMEM;
+  static constexpr int NT = WGM * WGN * 64;
+};
+
+// Write the accumulators into LDS as a row-major [BM][BN] fp32 tile.
+template <int FM, int FN, int WGM, int WGN>
+__device__ __forceinline__ void acc_to_lds(const EpiPos& p, const f32x4_t (&acc)[FM][FN]) {
+  using G = TileGeo<FM, FN, WGM, WGN>;
+  float* U = (float*)p.smem;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rl = p.wm * G::WTM + 16 * i + 4 * (p.lane >> 4);
+      const int cl = p.wn * G::WTN + 16 * j + (p.lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) U[(rl + e) * G::BN + cl] = acc[i][j][e];
+    }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
+}
+// Store 4 consecutive values of a row (8 bytes when aligned and whole).
+__device__ __forceinline__ void store_row4_bf16(bf16_t* d, float a, float b, float c, float e, int nvalid) {
+  if (nvalid >= 4) {
+    *(uint2*)d = pack4_bf16(a, b, c, e);
+  } else {
+    if (nvalid > 0) d[0] = f2bf(a);
+    if (nvalid > 1) d[1] = f2bf(b);
+    if (nvalid > 2) d[2] = f2bf(c);
+  }
+}
+__device__ __forceinline__ float4 load_row4_bf16(const bf16_t* s, int nvalid) {
+  if (nvalid >= 4) {
+    const uint2 u = *(const uint2*)s;
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+  }
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (nvalid > 0) v[0] = bf2f(s[0]);
+  if (nvalid > 1) v[1] = bf2f(s[1]);
+  if (nvalid > 2) v[2] = bf2f(s[2]);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Transposed store of the LDS fp32 tile: dstT row (n0 + c) gets tile column c, 8 rows per
+// thread (16-byte stores); lanes walk consecutive columns (bank-conflict-free LDS reads).
+template <int FM, int FN, int WGM, int WGN>
+__device__ __forceinline__ void lds_cols_to_global_bf16(const EpiPos& p, bf16_t* dstT, int64_t ldt) {
+  using G = TileGeo<FM, FN, WGM, WGN>;
+  const float* U = (const float*)p.smem;
+  const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+  const bool vec_ok = (ldt % 8) == 0;
+#pragma unroll 1
+  for (int idx = p.tid; idx < G::BN * (G::BM / 8); idx += AccTile<FM, FN, WGM, WGN>::NT) {
+    const int c = idx % G::BN, r = (idx / G::BN) * 8;
+    const int gc = n0 + c, gr = m0 + r;
+    if (gc >= p.N || gr >= p.M) continue;
+    bf16_t* d = dstT + (int64_t)gc * ldt + gr;
+    if (vec_ok && gr + 8 <= p.M) {
+      uint4 v;
+      v.x = pack_bf2(U[(r + 0) * G::BN + c], U[(r + 1) * G::BN + c]);
+      v.y = pack_bf2(U[(r + 2) * G::BN + c], U[(r + 3) * G::BN + c]);
+      v.z = pack_bf2(U[(r + 4) * G::BN + c], U[(r + 5) * G::BN + c]);
+      v.w = pack_bf2(U[(r + 6) * G::BN + c], U[(r + 7) * G::BN + c]);
+      *(uint4*)d = v;
+    } else {
+      for (int k = 0; k < 8 && gr + k < p.M; ++k) d[k] = f2bf(U[(r + k) * G::BN + c]);
+    }
+  }
+}
+
 // Plain fp32 store, optionally accumulating, with one output slab per split.
 struct EpiStoreF32 {
   float* C;
   int64_t ldc;
   int64_t split_stride;
   int accumulate;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float* Cs = C + (int64_t)p.split * split_stride;
 #pragma unroll
@@ -228,19 +573,20 @@ struct EpiStoreF32 {
 };
 
 // Per-row sum over the tile's columns of a per-element value v[i][e] (already summed over
-// the wave's j blocks by the caller): 16-lane butterfly, then the two column-half waves are
-// combined through LDS and written to out[tn * ldo + row]. Fixed order, so deterministic.
-// Uses 2 * BM floats of LDS; all threads of the block must call it.
+// the wave's j blocks by the caller): 16-lane butterfly, then the column waves' partials
+// are combined through LDS in column order and written to out[tn * ldo + row]. Fixed
+// order, so deterministic. Uses wgn * bm floats of LDS; all threads must call it.
 template <int FM>
 __device__ __forceinline__ void row_partial_store(const EpiPos& p, float (&v)[FM][4], float* out, int64_t ldo) {
   constexpr int WTM = 16 * FM;
   float* l1 = (float*)p.smem;
+  __syncthreads();  // the LDS may still be read by a preceding staged copy
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[i][e] = xor16_sum(v[i][e]);
-      if (p.wn == 1 && (p.lane & 15) == 0) l1[p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e] = v[i][e];
+      if ((p.lane & 15) == 0) l1[p.wn * p.bm + p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e] = v[i][e];
     }
   __syncthreads();
   if (p.wn == 0 && (p.lane & 15) == 0) {
@@ -249,7 +595,10 @@ __device__ __forceinline__ void row_partial_store(const EpiPos& p, float (&v)[FM
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = epi_row(p, i, e);
-        if (row < p.M) out[(int64_t)p.tn * ldo + row] = v[i][e] + l1[p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e];
+        const int lr = p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
+        float sum = l1[lr];
+        for (int c = 1; c < p.wgn; ++c) sum += l1[c * p.bm + lr];
+        if (row < p.M) out[(int64_t)p.tn * ldo + row] = sum;
       }
   }
 }
@@ -264,8 +613,42 @@ struct EpiGelu {
   T* GP;    // [M x lda]
   T* RES;   // [M x lda] or null
   int64_t lda, ldat;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    if constexpr (sizeof(T) == 2 && AccTile<FM, FN, WGM, WGN>::FITS) {
+      using G = TileGeo<FM, FN, WGM, WGN>;
+      acc_to_lds<FM, FN, WGM, WGN>(p, acc);
+      float* U = (float*)p.smem;
+      const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+      // rows: A, GELU'(U), residual; A written back in place for the transposed pass
+#pragma unroll 1
+      for (int idx = p.tid; idx < G::BM * (G::BN / 4); idx += AccTile<FM, FN, WGM, WGN>::NT) {
+        const int r = idx / (G::BN / 4), c = (idx % (G::BN / 4)) * 4;
+        const int gr = m0 + r, gc = n0 + c;
+        float4* up = (float4*)(U + r * G::BN + c);
+        const float4 u = *up;
+        const float uu[4] = {u.x, u.y, u.z, u.w};
+        float a[4], gp[4], rs[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float phi = 0.5f * (1.0f + erff(uu[q] * 0.70710678118654752f));
+          a[q] = uu[q] * phi;
+          gp[q] = phi + uu[q] * 0.39894228040143268f * expf(-0.5f * uu[q] * uu[q]);
+          rs[q] = a[q] - bf2f(f2bf(a[q]));
+        }
+        *up = make_float4(a[0], a[1], a[2], a[3]);
+        if (gr < p.M && gc < p.N) {
+          const int nv = min(4, p.N - gc);
+          const int64_t o = (int64_t)gr * lda + gc;
+          store_row4_bf16((bf16_t*)A + o, a[0], a[1], a[2], a[3], nv);
+          store_row4_bf16((bf16_t*)GP + o, gp[0], gp[1], gp[2], gp[3], nv);
+          if (RES) store_row4_bf16((bf16_t*)RES + o, rs[0], rs[1], rs[2], rs[3], nv);
+        }
+      }
+      __syncthreads();
+      lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)AT, ldat);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r0 = epi_row(p, i, 0);
@@ -304,7 +687,7 @@ struct EpiSwiglu {
   T* AT;
   T* RES;           // may be null
   int64_t lda, ldat;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -344,13 +727,53 @@ struct EpiDU {
   const T* RES;  // [M x ld] or null
   float* cdot;   // [tiles_n x M] or null
   int64_t ld, ldt;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float dots[FM][4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dots[i][e] = 0.f;
+    if constexpr (sizeof(T) == 2 && AccTile<FM, FN, WGM, WGN>::FITS && TileGeo<FM, FN, WGM, WGN>::BN == 128) {
+      // rows are covered by 32 consecutive threads (4 columns each): their partial dots
+      // combine with a 32-lane butterfly in a fixed order
+      using G = TileGeo<FM, FN, WGM, WGN>;
+      acc_to_lds<FM, FN, WGM, WGN>(p, acc);
+      float* U = (float*)p.smem;
+      const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+#pragma unroll 1
+      for (int base = 0; base < G::BM * 32; base += AccTile<FM, FN, WGM, WGN>::NT) {
+        const int idx = base + p.tid;
+        const int r = idx >> 5, c = (idx & 31) * 4;
+        const int gr = m0 + r, gc = n0 + c;
+        float4* up = (float4*)(U + r * G::BN + c);
+        const float4 da = *up;
+        float4 du = make_float4(0.f, 0.f, 0.f, 0.f);
+        float dot = 0.f;
+        if (gr < p.M && gc < p.N) {
+          const int nv = min(4, p.N - gc);
+          const int64_t o = (int64_t)gr * ld + gc;
+          const float4 g = load_row4_bf16((const bf16_t*)GP + o, nv);
+          du = make_float4(da.x * g.x, da.y * g.y, da.z * g.z, da.w * g.w);
+          store_row4_bf16((bf16_t*)DU + o, du.x, du.y, du.z, du.w, nv);
+          if (RES) {
+            const float4 rr = load_row4_bf16((const bf16_t*)RES + o, nv);
+            dot = (da.x * rr.x + da.y * rr.y) + (da.z * rr.z + da.w * rr.w);
+          }
+        }
+        *up = du;
+        if (cdot) {
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) dot += __shfl_xor(dot, off, TTT_WAVE);
+          if ((p.lane & 31) == 0 && gr < p.M) cdot[(int64_t)p.tn * p.M + gr] = dot;
+        }
+      }
+      __syncthreads();
+      lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
       const int r0 = epi_row(p, i, 0);
       const int nv = min(4, p.M - r0);
       if (nv <= 0) continue;
@@ -387,7 +810,7 @@ struct EpiSwigluBwd {
   const T* RES;
   float* cdot;
   int64_t ld;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float dots[FM][4];
 #pragma unroll
@@ -414,12 +837,15 @@ struct EpiSwigluBwd {
   }
 };
 
-// Weight gradient: store G (fp32) and this tile's sum of squares into slot[tile].
+// Weight gradient: store G in the GEMM operand precision (bf16 tiles through LDS, 16-byte
+// row stores; fp32 directly) and this tile's sum of squares of the fp32 accumulators into
+// slot[tile] (the clip norm never sees the rounding of the stored G).
+template <class T>
 struct EpiGrad {
-  float* G;
+  T* G;
   int64_t ldg;
   float* slot;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float ss = 0.f;
 #pragma unroll
@@ -430,10 +856,8 @@ struct EpiGrad {
         if (row >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = epi_col(p, j);
-          if (col >= p.N) continue;
+          if (epi_col(p, j) >= p.N) continue;
           const float v = acc[i][j][e];
-          G[(int64_t)row * ldg + col] = v;
           ss += v * v;
         }
       }
@@ -441,7 +865,35 @@ struct EpiGrad {
     float* red = (float*)p.smem;
     if (p.lane == 0) red[p.wave] = ss;
     __syncthreads();
-    if (p.wave == 0 && p.lane == 0) slot[p.tile] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (p.wave == 0 && p.lane == 0) {
+      float t = red[0];
+      for (int w = 1; w < p.wgm * p.wgn; ++w) t += red[w];
+      slot[p.tile] = t;
+    }
+    if constexpr (sizeof(T) == 2 && TileGeo<FM, FN, WGM, WGN>::ROWS_FIT) {
+      Packed<FM, FN> pg;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          pg[i][j][0] = pack_bf2(acc[i][j][0], acc[i][j][1]);
+          pg[i][j][1] = pack_bf2(acc[i][j][2], acc[i][j][3]);
+        }
+      stage_rows_bf16<FM, FN, WGM, WGN>(p, pg, (bf16_t*)G, ldg);  // begins with a barrier
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = epi_row(p, i, e);
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = epi_col(p, j);
+          if (col < p.N) G[(int64_t)row * ldg + col] = from_f<T>(acc[i][j][e]);
+        }
+      }
   }
 };
 
@@ -464,14 +916,13 @@ struct EpiCEPartial {
   int* pidx;
   float* tgt_logit;  // [M]
   int ldp;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
-    constexpr int WTM = 16 * FM, BM = 2 * WTM;
+    constexpr int WTM = 16 * FM;
+    // LDS: [wgn][bm] of (max, sum, argmax) per column wave
     float* lmax = (float*)p.smem;
-    float* lsum = lmax + BM;
-    int* lidx = (int*)(lsum + BM);
-    float rm[FM][4], rs[FM][4];
-    int ri[FM][4];
+    float* lsum = lmax + p.wgn * p.bm;
+    int* lidx = (int*)(lsum + p.wgn * p.bm);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -489,24 +940,23 @@ struct EpiCEPartial {
             if (col == tg) tgt_logit[row] = v;
           }
         }
+        // row max and first argmax over the 16 lanes of the row, then one exp per element
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float omx = __shfl_xor(mx, off, TTT_WAVE);
+          const int oix = __shfl_xor(ix, off, TTT_WAVE);
+          if (omx > mx || (omx == mx && oix < ix)) ix = oix;
+          mx = fmaxf(mx, omx);
+        }
         float sm = 0.f;
         if (mx != -INFINITY) {
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            if (epi_col(p, j) < p.N) sm += expf(acc[i][j][e] - mx);
+            if (epi_col(p, j) < p.N) sm += exp_fast(acc[i][j][e] - mx);
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float omx = __shfl_xor(mx, off, TTT_WAVE);
-          const float osm = __shfl_xor(sm, off, TTT_WAVE);
-          const int oix = __shfl_xor(ix, off, TTT_WAVE);
-          ce_combine(mx, sm, ix, omx, osm, oix);
-        }
-        rm[i][e] = mx;
-        rs[i][e] = sm;
-        ri[i][e] = ix;
-        const int lr = p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
-        if (p.wn == 1 && (p.lane & 15) == 0) {
+        sm = xor16_sum(sm);
+        const int lr = p.wn * p.bm + p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
+        if ((p.lane & 15) == 0) {
           lmax[lr] = mx;
           lsum[lr] = sm;
           lidx[lr] = ix;
@@ -521,9 +971,9 @@ struct EpiCEPartial {
           const int row = epi_row(p, i, e);
           if (row >= p.M) continue;
           const int lr = p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
-          float mx = rm[i][e], sm = rs[i][e];
-          int ix = ri[i][e];
-          ce_combine(mx, sm, ix, lmax[lr], lsum[lr], lidx[lr]);
+          float mx = lmax[lr], sm = lsum[lr];
+          int ix = lidx[lr];
+          for (int c = 1; c < p.wgn; ++c) ce_combine(mx, sm, ix, lmax[c * p.bm + lr], lsum[c * p.bm + lr], lidx[c * p.bm + lr]);
           const int64_t o = (int64_t)p.tn * ldp + row;
           pmax[o] = mx;
           psum[o] = sm;
@@ -543,8 +993,35 @@ struct EpiCEProb {
   int64_t ldp;
   int col_base;  // vocab id of column 0
   float inv_b;
-  template <int FM, int FN>
+  template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    if constexpr (sizeof(T) == 2 && TileGeo<FM, FN, WGM, WGN>::ROWS_FIT) {
+      {
+        Packed<FM, FN> pp;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float ls[4];
+          int tg[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = min(epi_row(p, i, e), p.M - 1);
+            ls[e] = lse[row];
+            tg[e] = tgt[row] - col_base;
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = epi_col(p, j);
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (exp_fast(acc[i][j][e] - ls[e]) - (col == tg[e] ? 1.f : 0.f)) * inv_b;
+            pp[i][j][0] = pack_bf2(v[0], v[1]);
+            pp[i][j][1] = pack_bf2(v[2], v[3]);
+          }
+        }
+        stage_rows_bf16<FM, FN, WGM, WGN>(p, pp, (bf16_t*)P, ldp);
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -557,7 +1034,7 @@ struct EpiCEProb {
         for (int j = 0; j < FN; ++j) {
           const int col = epi_col(p, j);
           if (col >= p.N) continue;
-          const float v = (expf(acc[i][j][e] - ls) - (col == tg ? 1.f : 0.f)) * inv_b;
+          const float v = (exp_fast(acc[i][j][e] - ls) - (col == tg ? 1.f : 0.f)) * inv_b;
           P[(int64_t)row * ldp + col] = from_f<T>(v);
         }
       }
@@ -574,11 +1051,42 @@ struct Seg2 {
   int K = 0;
 };
 
-template <class T, int BM, int BN, class Epi>
-inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
-                              int N, int K, int splits, const Epi& epi, const Seg2& s2 = Seg2()) {
+template <class T, int BM, int BN, int WGM, int WGN, class Epi>
+inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, const Epi& epi) {
+  constexpr size_t lds = 2 * (size_t)(BM + BN) * 128;
+  auto kern = gemm_dma_kernel<T, BM, BN, WGM, WGN, Epi>;
+  static bool lds_attr = false;  // per instantiation
+  if (!lds_attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_attr = true;
+  }
+  dim3 grid(g.tiles_m * g.tiles_n, splits);
+  hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, g, epi);
+  return hipGetLastError();
+}
+
+// Tile plan of a GEMM launch (shared with the host code that sizes per-tile buffers).
+struct TilePlan {
+  int bm, bn;
+  bool dma;
+};
+inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
+  const int ke = 128 / es;
+  TilePlan t{128, 128, (K % ke == 0) && (K2 % ke == 0)};
+  if (t.dma && splits <= 1 && ((M + 255) / 256) * ((N + 255) / 256) >= 256) t.bm = t.bn = 256;
+  return t;
+}
+
+// C = X Y^T (+ X2 Y2^T) with a fused epilogue. K-slices of 128 bytes go through LDS by
+// direct loads when both K extents are whole slices, else through registers. Wide outputs
+// (at least one 256 x 256 tile per CU) use 256 x 256 tiles with 8 waves; the rest 128 x 128.
+template <class T, class Epi>
+inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                              int K, int splits, const Epi& epi, const Seg2& s2 = Seg2()) {
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int KE = 128 / (int)sizeof(T);
+  if (splits < 1) splits = 1;
   GemmArgs g;
   g.X = X;
   g.Y = Y;
@@ -592,13 +1100,25 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
   g.N = N;
   g.K = K;
   g.K2 = s2.K;
-  g.tiles_m = (M + BM - 1) / BM;
-  g.tiles_n = (N + BN - 1) / BN;
   g.kit_a = (K + KE - 1) / KE;
   g.kiters = g.kit_a + (s2.K + KE - 1) / KE;
-  if (splits < 1) splits = 1;
+  const TilePlan plan = gemm_plan(M, N, K, s2.K, (int)sizeof(T), splits);
+  if (plan.dma) {
+    if (plan.bm == 256) {
+      g.tiles_m = (M + 255) / 256;
+      g.tiles_n = (N + 255) / 256;
+      g.kps = g.kiters;
+      return launch_dma<T, 256, 256, 2, 4>(st, g, 1, epi);
+    }
+    g.tiles_m = (M + 127) / 128;
+    g.tiles_n = (N + 127) / 128;
+    g.kps = (g.kiters + splits - 1) / splits;
+    return launch_dma<T, 128, 128, 2, 2>(st, g, splits, epi);
+  }
+  g.tiles_m = (M + 127) / 128;
+  g.tiles_n = (N + 127) / 128;
   g.kps = (g.kiters + splits - 1) / splits;
   dim3 grid(g.tiles_m * g.tiles_n, splits);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, Epi>), grid, dim3(256), 0, st, g, epi);
+  hipLaunchKernelGGL((gemm_reg_kernel<T, 128, 128, Epi>), grid, dim3(256), 0, st, g, epi);
   return hipGetLastError();
 }

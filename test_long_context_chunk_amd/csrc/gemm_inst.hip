@@ -2,9 +2,6 @@
 #include "launchers.h"
 #include "gemm.h"
 
-namespace {
-constexpr int BM = 128, BN = 128;
-}
 
 #define DISPATCH_T(prec, ...)  \
   do {                         \
@@ -33,14 +30,14 @@ hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const 
                     int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate,
                     const GemmSeg2& s2) {
   EpiStoreF32 e{C, ldc, split_stride, accumulate};
-  DISPATCH_T(prec, return (launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, splits, e, seg(s2))));
+  DISPATCH_T(prec, return (launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, splits, e, seg(s2))));
 }
 
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat, const GemmSeg2& s2) {
   DISPATCH_T(prec, {
     EpiGelu<T> e{(T*)A, (T*)AT, (T*)GP, (T*)RES, lda, ldat};
-    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
   });
 }
 
@@ -48,7 +45,7 @@ hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, con
                        int K, const float* UG, float* VU, void* A, void* AT, void* RES, int64_t lda, int64_t ldat) {
   DISPATCH_T(prec, {
     EpiSwiglu<T> e{UG, VU, (T*)A, (T*)AT, (T*)RES, lda, ldat};
-    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }
 
@@ -56,7 +53,7 @@ hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const v
                    int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt) {
   DISPATCH_T(prec, {
     EpiDU<T> e{(const T*)GP, (T*)DU, (T*)DUT, (const T*)RES, cdot, ld, ldt};
-    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }
 
@@ -65,25 +62,28 @@ hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx,
                            float* cdot, int64_t ld) {
   DISPATCH_T(prec, {
     EpiSwigluBwd<T> e{UG, VU, (T*)DG, (T*)DV, (const T*)RES, cdot, ld};
-    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }
 
-int gemm_col_tiles(int N) { return (N + BN - 1) / BN; }
-
-int gemm_grad_slots(int M, int N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n) {
+  const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits);
+  *tile_m = t.bm;
+  *tile_n = t.bn;
+}
 
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, float* G, int64_t ldg, float* slot) {
-  EpiGrad e{G, ldg, slot};
-  DISPATCH_T(prec, return (launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e)));
+                     int K, void* G, int64_t ldg, float* slot) {
+  DISPATCH_T(prec, {
+    EpiGrad<T> e{(T*)G, ldg, slot};
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+  });
 }
 
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit) {
-  static_assert(BN == GEMM_CE_BN, "CE partial tiles must match the merge");
   EpiCEPartial e{tgt, pmax, psum, pidx, tgt_logit, M};
-  DISPATCH_T(prec, return (launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e)));
+  DISPATCH_T(prec, return (launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e)));
 }
 
 hipError_t gemm_ce_prob(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
@@ -91,6 +91,6 @@ hipError_t gemm_ce_prob(hipStream_t st, int prec, const void* X, int64_t ldx, co
                         float inv_b) {
   DISPATCH_T(prec, {
     EpiCEProb<T> e{tgt, lse, (T*)P, ldp, col_base, inv_b};
-    return launch_gemm<T, BM, BN>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }

@@ -126,14 +126,24 @@ __global__ void __launch_bounds__(NT) k_dy_finish(const float* __restrict__ part
 }
 
 // Add the first-order rounding compensation to the recorded losses:
-//   l_t += scale * sum_s cpart[s * b + t]   (slots in a fixed order).
+//   l_t += scale * sum_s cpart[s * b + t]   (fixed order).
+// 16 tokens per block; the 16 threads of a token sum interleaved slots, then combine in a
+// fixed butterfly order.
 __global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ cpart, int nslot, int b, float scale,
                                                      float* __restrict__ loss) {
-  const int t = blockIdx.x * NT + threadIdx.x;
-  if (t >= b) return;
+  const int t = blockIdx.x * 16 + (threadIdx.x & 15);
+  const int part = threadIdx.x >> 4;  // 0..15
   float acc = 0.f;
-  for (int s = 0; s < nslot; ++s) acc += cpart[(int64_t)s * b + t];
-  loss[t] += scale * acc;
+  if (t < b)
+    for (int s = part; s < nslot; s += 16) acc += cpart[(int64_t)s * b + t];
+  // lanes t, t+16, t+32, t+48 of a wave hold the same token: sum across lane groups, then waves
+  acc += __shfl_xor(acc, 16, TTT_WAVE);
+  acc += __shfl_xor(acc, 32, TTT_WAVE);
+  __shared__ float red[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane < 16) red[wave][lane] = acc;
+  __syncthreads();
+  if (threadIdx.x < 16 && t < b) loss[t] += scale * ((red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]));
 }
 
 // a5 merge: combine the per-vocab-tile (max, sum exp, argmax) partials of each row in
@@ -238,31 +248,82 @@ __global__ void __launch_bounds__(NT) k_gradnorm(const float* __restrict__ slot,
 //   D <- D - lr * s * G;  Wop = rn(W0 + D) row-major (the backward GEMMs' operand);
 //   WtT = transposed copy of rn(D) when delta_t (bf16: the forward GEMMs add X rn(D)^T to
 //   X W0^T, so updates far below W0's rounding step still reach them), else of rn(W0 + D).
+// A block owns a 64 x 64 tile: each thread updates 4 consecutive columns of 4 rows with
+// vector accesses, and the transposed copy leaves through LDS as 16-byte row pieces.
 template <class T>
-__global__ void __launch_bounds__(NT) k_update(const float* __restrict__ G, float* __restrict__ D,
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) { return *(const float4*)p; }
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+template <class T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  *(uint2*)p = make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
+}
+
+template <class T>
+__global__ void __launch_bounds__(NT) k_update(const T* __restrict__ G, float* __restrict__ D,
                                                const T* __restrict__ W0, T* __restrict__ Wop,
                                                T* __restrict__ WtT, int R, int C, float lr,
                                                const float* __restrict__ sc, int delta_t) {
   if (sc[1] != 0.f) return;  // non-finite gradient norm: no step for this chunk
   const float step = lr * sc[0];
-  __shared__ T tile[64][65];
+  __shared__ T tile[64][64 + 16 / sizeof(T)];  // [col][row] of the transposed output
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int r = r0 + k, c = c0 + tx;
-    if (r < R && c < C) {
-      const int64_t i = (int64_t)r * C + c;
-      const float dn = D[i] - step * G[i];
-      D[i] = dn;
-      const T w = from_f<T>(to_f<T>(W0[i]) + dn);
-      Wop[i] = w;
-      tile[k][tx] = delta_t ? from_f<T>(dn) : w;
+  const int cq = (threadIdx.x & 15) * 4, rq = threadIdx.x >> 4;  // 16 column quads x 16 rows
+  const bool vec = (C % 4) == 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rl = rq + 16 * k, r = r0 + rl, c = c0 + cq;
+    if (r >= R || c >= C) continue;
+    const int64_t i = (int64_t)r * C + c;
+    float w[4];
+    if (vec) {
+      const float4 g = load4<T>(G + i), d = load4<float>(D + i), w0 = load4<T>(W0 + i);
+      const float dn[4] = {d.x - step * g.x, d.y - step * g.y, d.z - step * g.z, d.w - step * g.w};
+      *(float4*)(D + i) = make_float4(dn[0], dn[1], dn[2], dn[3]);
+      const float wv[4] = {w0.x + dn[0], w0.y + dn[1], w0.z + dn[2], w0.w + dn[3]};
+      store4<T>(Wop + i, wv[0], wv[1], wv[2], wv[3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = delta_t ? dn[q] : wv[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = 0.f;
+        if (c + q >= C) continue;
+        const float dn = D[i + q] - step * to_f<T>(G[i + q]);
+        D[i + q] = dn;
+        const float wv = to_f<T>(W0[i + q]) + dn;
+        Wop[i + q] = from_f<T>(wv);
+        w[q] = delta_t ? dn : wv;
+      }
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[cq + q][rl] = from_f<T>(w[q]);
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int c = c0 + k, r = r0 + tx;
-    if (c < C && r < R) WtT[(int64_t)c * R + r] = tile[tx][k];
+  // transposed rows: WtT[c][r0 .. r0 + 63], 16-byte pieces
+  constexpr int PER = 16 / sizeof(T);  // elements per piece
+  for (int idx = threadIdx.x; idx < 64 * (64 / PER); idx += NT) {
+    const int cl = idx / (64 / PER), rl = (idx % (64 / PER)) * PER;
+    const int c = c0 + cl, r = r0 + rl;
+    if (c >= C || r >= R) continue;
+    T* dst = WtT + (int64_t)c * R + r;
+    if ((R % PER) == 0 && r + PER <= R) {
+      *(uint4*)dst = *(const uint4*)&tile[cl][rl];
+    } else {
+      for (int q = 0; q < PER && r + q < R; ++q) dst[q] = tile[cl][rl + q];
+    }
   }
 }
 
@@ -332,7 +393,7 @@ hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int
 }
 
 hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss) {
-  hipLaunchKernelGGL(k_loss_correct, dim3((b + NT - 1) / NT), dim3(NT), 0, st, cpart, nslot, b, scale, loss);
+  hipLaunchKernelGGL(k_loss_correct, dim3((b + 15) / 16), dim3(NT), 0, st, cpart, nslot, b, scale, loss);
   return hipGetLastError();
 }
 
@@ -356,11 +417,11 @@ hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip
   return hipGetLastError();
 }
 
-hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WtT, int R,
+hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const void* W0, void* Wop, void* WtT, int R,
                       int C, float lr, const float* sc, int delta_t) {
   dim3 grid((C + 63) / 64, (R + 63) / 64);
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, G, D, (const T*)W0, (T*)Wop, (T*)WtT, R,
-                                      C, lr, sc, delta_t));
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, (const T*)G, D, (const T*)W0, (T*)Wop,
+                                      (T*)WtT, R, C, lr, sc, delta_t));
   return hipGetLastError();
 }
 

@@ -25,16 +25,12 @@ hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int6
                         const float* r, int b, int d, int rms, float* dH, void* dHb, const void* RES, float* cdot,
                         int update_dh);
 hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat, int* err);
-hipError_t run_update(hipStream_t st, int prec, const float* G, float* D, const void* W0, void* Wop, void* WtT, int R,
+hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const void* W0, void* Wop, void* WtT, int R,
                       int C, float lr, const float* sc, int delta_t);
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst);
 hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
 
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
-// Tile rows of the CE partial buffers: one (max, sum, argmax) triple per row and per
-// GEMM_CE_BN-wide vocab tile.
-constexpr int GEMM_CE_BN = 128;
-
 // Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).
 struct GemmSeg2 {
   const void* X = nullptr;
@@ -66,13 +62,13 @@ hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const v
 hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const float* UG, const float* VU, void* DG, void* DV, const void* RES,
                            float* cdot, int64_t ld);
-// Number of 128-wide column tiles of an N-column GEMM output (partial-dot slots per row).
-int gemm_col_tiles(int N);
-// Weight-gradient epilogue: G [M x ldg] fp32 and one sum of squares per output tile in
-// slot[tile].
+// Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits):
+// per-tile buffers (CE partials, sums of squares, partial dots) are sized from it.
+void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n);
+// Weight-gradient epilogue: G [M x ldg] in the GEMM precision and one sum of squares of the
+// fp32 accumulators per output tile in slot[tile].
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, float* G, int64_t ldg, float* slot);
-int gemm_grad_slots(int M, int N);
+                     int K, void* G, int64_t ldg, float* slot);
 // LM head + online-softmax partials over the full vocabulary (N = V).
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit);

@@ -25,7 +25,7 @@ struct FastTensor {
   float* D = nullptr;      // accumulated update, fp32 [rows x cols]
   void* Wop = nullptr;     // rn(W0 + D) [rows x cols]
   void* WtT = nullptr;     // bf16: rn(D)^T, fp32: (W0 + D)^T  [cols x rows]
-  float* G = nullptr;      // chunk gradient, fp32 [rows x cols]
+  void* G = nullptr;       // chunk gradient in the GEMM precision [rows x cols]
   int slot0 = 0;           // first grad-norm slot
 };
 
@@ -65,7 +65,8 @@ struct ttt_ctx {
   int *tok_prev = nullptr, *tok_tgt = nullptr;
   float *pmax = nullptr, *psum = nullptr, *tgt_logit = nullptr, *lse = nullptr;
   int* pidx = nullptr;
-  int ce_tiles = 0;
+  int ce_tiles = 0;   // vocab tiles of the LM-head GEMM (one CE partial per tile and row)
+  int dot_tiles = 0;  // column tiles of the dA GEMM (one partial dot per tile and row)
   void* P = nullptr;
   float* part = nullptr;
   float* dH = nullptr;
@@ -168,14 +169,16 @@ void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
   f.D = dalloc<float>(c, n * 4);
   f.Wop = dalloc<char>(c, n * c->es);
   f.WtT = dalloc<char>(c, n * c->es);
-  f.G = dalloc<float>(c, n * 4);
+  f.G = dalloc<char>(c, n * c->es);
   check(hipMemcpyAsync(f.W0, src, n * c->es, hipMemcpyDeviceToDevice, c->st));
   if (c->prec == PREC_BF16) {
     f.W0T = dalloc<char>(c, n * c->es);
     check(run_transpose(c->st, c->prec, f.W0, cols, rows, cols, f.W0T, rows));
   }
   f.slot0 = c->nslots;
-  c->nslots += gemm_grad_slots(rows, cols);
+  int tm = 0, tn = 0;
+  gemm_tile_shape(c->prec, rows, cols, c->bp, 0, 1, &tm, &tn);
+  c->nslots += cdiv(rows, tm) * cdiv(cols, tn);
   c->fast.push_back(&f);
 }
 
@@ -200,7 +203,10 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   check(run_transpose(c->st, c->prec, c->E_out, d, V, d, c->E_outT, V));
 
   c->foc = c->prec == PREC_BF16 && L > 0;
-  const int tnm = gemm_col_tiles(m);
+  int tmm = 0, tnm_w = 0;
+  gemm_tile_shape(c->prec, b, m, d, 0, 1, &tmm, &tnm_w);  // the dA GEMM (M = b, N = m, K = d)
+  const int tnm = cdiv(m, tnm_w);
+  c->dot_tiles = tnm;
   c->ncslot = 1;  // slot 0: the LM-head input Y
   c->blocks.resize(L);
   for (int l = 0; l < L; ++l) {
@@ -241,7 +247,11 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->Yb = dalloc<char>(c, (int64_t)b * d * es);
   c->tok_prev = dalloc<int>(c, (int64_t)b * 4);
   c->tok_tgt = dalloc<int>(c, (int64_t)b * 4);
-  c->ce_tiles = cdiv(V, GEMM_CE_BN);
+  {
+    int tm = 0, tn = 0;
+    gemm_tile_shape(c->prec, b, V, d, 0, 1, &tm, &tn);  // the LM-head GEMM
+    c->ce_tiles = cdiv(V, tn);
+  }
   c->pmax = dalloc<float>(c, (int64_t)c->ce_tiles * b * 4);
   c->psum = dalloc<float>(c, (int64_t)c->ce_tiles * b * 4);
   c->pidx = dalloc<int>(c, (int64_t)c->ce_tiles * b * 4);
@@ -268,6 +278,7 @@ void build(ttt_ctx* c, const ttt_weights* w) {
     check(hipMemsetAsync(c->cpart, 0, (int64_t)c->ncslot * b * 4, c->st));
   }
   c->slots = dalloc<float>(c, (int64_t)(c->nslots > 0 ? c->nslots : 1) * 4);
+  check(hipMemsetAsync(c->slots, 0, (int64_t)(c->nslots > 0 ? c->nslots : 1) * 4, c->st));
   c->sc = dalloc<float>(c, 4 * 4);
   c->losses = dalloc<float>(c, c->cfg.max_tokens * 4);
   c->amax = dalloc<int>(c, c->cfg.max_tokens * 4);
@@ -318,7 +329,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   const bool bf = prec == PREC_BF16;
   const bool foc = c->foc;
   const int64_t bd = (int64_t)b * d;
-  const int tnm = gemm_col_tiles(m);
+  const int tnm = c->dot_tiles;
 
   // a1 gather
   RUN(TTT_K_GATHER, run_gather(st, prec, tok, b, V, d, c->E_in, c->H, L == 0 ? c->Yb : nullptr, c->tok_prev,
