@@ -193,6 +193,46 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
 // past M or N re-read the last valid row and only feed outputs the epilogue never stores.
 // Two LDS stages: the next slice is requested right after the barrier that retires the
 // stage it overwrites.
+//
+// One K-iteration: request the next slice into stage `nxt` and multiply the slice held in
+// stage `cur`. The two stage pointers are restrict-qualified: they never overlap, and
+// saying so lets the compiler read `cur` while the direct loads into `nxt` are still in
+// flight (without it, every LDS read would first wait for those loads to land).
+template <class T, int BM, int BN, int WGM, int WGN, int PW>
+__device__ __forceinline__ void dma_iteration(const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
+                                              const char* const (&src)[PW], int64_t kb, int wm, int wn, int lane,
+                                              f32x4_t (&acc)[BM / WGM / 16][BN / WGN / 16]) {
+  constexpr int ROWB = 128;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  if (issue) {
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + kb),
+                                       (__attribute__((address_space(3))) void*)(nxt + q * 1024), 16, 0, 0);
+  }
+  const char* sb = cur + BM * ROWB;
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg) {
+    const int ch = kg * 4 + (lane >> 4);
+    uint4 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + (lane & 15);
+      af[i] = *(const uint4*)(cur + r * ROWB + ((ch ^ (r & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * 16 + (lane & 15);
+      bfr[j] = *(const uint4*)(sb + r * ROWB + ((ch ^ (r & 7)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_chunk(acc[i][j], af[i], bfr[j], T());
+  }
+}
+
 template <class T, int BM, int BN, int WGM, int WGN, class Epi>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Epi epi) {
   constexpr int WGM_ = WGM, WGN_ = WGN;
@@ -267,28 +307,14 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
     // own requests for this stage are done, then everyone's (and the other stage is free)
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
-    if (it + 1 < kit1) issue(it + 1, cur ^ 1);
-    const char* sa = smem + cur * STAGE;
-    const char* sb = sa + BM * ROWB;
+    const int nit = it + 1;
+    const bool seg2 = nit >= kit_a;
+    const int64_t kb = (int64_t)(seg2 ? nit - kit_a : nit) * ROWB;
+    const char* src[PW];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      const int ch = kg * 4 + (lane >> 4);
-      uint4 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 16 + (lane & 15);
-        af[i] = *(const uint4*)(sa + r * ROWB + ((ch ^ (r & 7)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 16 + (lane & 15);
-        bfr[j] = *(const uint4*)(sb + r * ROWB + ((ch ^ (r & 7)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma_chunk(acc[i][j], af[i], bfr[j], T());
-    }
+    for (int q = 0; q < PW; ++q) src[q] = seg2 ? p2[q] : p1[q];
+    dma_iteration<T, BM, BN, WGM, WGN, PW>(smem + cur * STAGE, sdst + (cur ^ 1) * STAGE, nit < kit1, src, kb, wm, wn,
+                                           lane, acc);
   }
   __syncthreads();  // the epilogue may reuse the LDS
 
