@@ -15,12 +15,13 @@ enum : int { ERRBIT_RANGE = 1, ERRBIT_NONFINITE = 2 };
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// float -> bfloat16, round to nearest even (the hardware conversion; NaN stays a NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two bfloat16 in one dword (low half = a), one conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <class T> __device__ __forceinline__ float to_f(T v);
@@ -48,10 +49,35 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const uint4& a, const u
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-// Exact-erf GELU and its derivative Phi(u) + u phi(u), via the device math library.
-__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+// GELU(u) = u Phi(u) and its derivative GELU'(u) = Phi(u) + u phi(u), Phi the standard
+// normal CDF, phi its density. erf comes from the rational approximation of Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 on [0, inf)):
+//   erfc(x) ~= t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),  t = 1 / (1 + p x).
+// With x = |u| / sqrt(2) the same exp(-x^2) = exp(-u^2 / 2) also gives phi(u), and
+// Phi(u) = 1 - erfc(x) / 2 for u >= 0, erfc(x) / 2 for u < 0 (no cancellation on that side).
+__device__ __forceinline__ void gelu_pair(float u, float& g, float& gp) {
+  // coefficients halved so that q = erfc(x) / 2 directly
+  constexpr float P = 0.3275911f;
+  constexpr float A1 = 0.5f * 0.254829592f, A2 = 0.5f * -0.284496736f, A3 = 0.5f * 1.421413741f,
+                  A4 = 0.5f * -1.453152027f, A5 = 0.5f * 1.061405429f;
+  const float x = fabsf(u) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(P, x, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, A5, A4), A3), A2), A1);
+  const float e = __builtin_amdgcn_exp2f(-0.5f * 1.4426950408889634f * u * u);  // exp(-u^2/2)
+  const float q = poly * e;
+  const float Phi = u >= 0.f ? 1.0f - q : q;
+  g = u * Phi;
+  gp = fmaf(u, 0.39894228040143268f * e, Phi);
+}
+__device__ __forceinline__ float gelu_f(float u) {
+  float g, gp;
+  gelu_pair(u, g, gp);
+  return g;
+}
 __device__ __forceinline__ float gelu_prime_f(float u) {
-  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * 0.39894228040143268f * expf(-0.5f * u * u);
+  float g, gp;
+  gelu_pair(u, g, gp);
+  return gp;
 }
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 

@@ -377,9 +377,7 @@ __device__ __forceinline__ void store4_t<float>(float* dst, float v0, float v1, 
 template <int FM, int FN>
 using Packed = uint32_t[FM][FN][2];
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // Copy the LDS tile (R rows of L elements, row stride ldl) to dst rows [g0, g0 + R) and
 // columns [c0, c0 + L), clipped to rows < gr_lim and columns < gc_lim.
@@ -520,7 +518,7 @@ __device__ __forceinline__ void acc_to_lds(const EpiPos& p, const f32x4_t (&acc)
 }
 
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-  return make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 // Store 4 consecutive values of a row (8 bytes when aligned and whole).
 __device__ __forceinline__ void store_row4_bf16(bf16_t* d, float a, float b, float c, float e, int nvalid) {
@@ -543,6 +541,17 @@ __device__ __forceinline__ float4 load_row4_bf16(const bf16_t* s, int nvalid) {
   if (nvalid > 1) v[1] = bf2f(s[1]);
   if (nvalid > 2) v[2] = bf2f(s[2]);
   return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Store 8 consecutive values of a row: one 16-byte store when whole and aligned.
+__device__ __forceinline__ void store_row8_bf16(bf16_t* d, const float (&v)[8], int nvalid, bool aligned) {
+  if (nvalid >= 8 && aligned) {
+    *(uint4*)d = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7]));
+  } else {
+    store_row4_bf16(d, v[0], v[1], v[2], v[3], nvalid);
+    if (nvalid > 4) store_row4_bf16(d + 4, v[4], v[5], v[6], v[7], nvalid - 4);
+  }
 }
 
 // Transposed store of the LDS fp32 tile: dstT row (n0 + c) gets tile column c, 8 rows per
@@ -646,29 +655,29 @@ struct EpiGelu {
       acc_to_lds<FM, FN, WGM, WGN>(p, acc);
       float* U = (float*)p.smem;
       const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
-      // rows: A, GELU'(U), residual; A written back in place for the transposed pass
+      const bool aligned = (lda & 7) == 0;
+      // rows of 8: A, GELU'(U), rounding residual; A written back in place for the transposed pass
 #pragma unroll 1
-      for (int idx = p.tid; idx < G::BM * (G::BN / 4); idx += AccTile<FM, FN, WGM, WGN>::NT) {
-        const int r = idx / (G::BN / 4), c = (idx % (G::BN / 4)) * 4;
+      for (int idx = p.tid; idx < G::BM * (G::BN / 8); idx += AccTile<FM, FN, WGM, WGN>::NT) {
+        const int r = idx / (G::BN / 8), c = (idx % (G::BN / 8)) * 8;
         const int gr = m0 + r, gc = n0 + c;
         float4* up = (float4*)(U + r * G::BN + c);
-        const float4 u = *up;
-        const float uu[4] = {u.x, u.y, u.z, u.w};
-        float a[4], gp[4], rs[4];
+        const float4 u0 = up[0], u1 = up[1];
+        const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float a[8], gp[8], rs[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float phi = 0.5f * (1.0f + erff(uu[q] * 0.70710678118654752f));
-          a[q] = uu[q] * phi;
-          gp[q] = phi + uu[q] * 0.39894228040143268f * expf(-0.5f * uu[q] * uu[q]);
+        for (int q = 0; q < 8; ++q) {
+          gelu_pair(uu[q], a[q], gp[q]);
           rs[q] = a[q] - bf2f(f2bf(a[q]));
         }
-        *up = make_float4(a[0], a[1], a[2], a[3]);
+        up[0] = make_float4(a[0], a[1], a[2], a[3]);
+        up[1] = make_float4(a[4], a[5], a[6], a[7]);
         if (gr < p.M && gc < p.N) {
-          const int nv = min(4, p.N - gc);
+          const int nv = min(8, p.N - gc);
           const int64_t o = (int64_t)gr * lda + gc;
-          store_row4_bf16((bf16_t*)A + o, a[0], a[1], a[2], a[3], nv);
-          store_row4_bf16((bf16_t*)GP + o, gp[0], gp[1], gp[2], gp[3], nv);
-          if (RES) store_row4_bf16((bf16_t*)RES + o, rs[0], rs[1], rs[2], rs[3], nv);
+          store_row8_bf16((bf16_t*)A + o, a, nv, aligned);
+          store_row8_bf16((bf16_t*)GP + o, gp, nv, aligned);
+          if (RES) store_row8_bf16((bf16_t*)RES + o, rs, nv, aligned);
         }
       }
       __syncthreads();
@@ -687,13 +696,13 @@ struct EpiGelu {
         float a[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float u = acc[i][j][e];
-          a[e] = gelu_f(u);
+          float gp;
+          gelu_pair(acc[i][j][e], a[e], gp);
           if (e < nv) {
             const int64_t o = (int64_t)(r0 + e) * lda + col;
             const T q = from_f<T>(a[e]);
             A[o] = q;
-            GP[o] = from_f<T>(gelu_prime_f(u));
+            GP[o] = from_f<T>(gp);
             if (RES) RES[o] = from_f<T>(a[e] - to_f<T>(q));
           }
         }
@@ -945,27 +954,36 @@ struct EpiCEPartial {
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     constexpr int WTM = 16 * FM;
+    constexpr float L2E = 1.4426950408889634f;
     // LDS: [wgn][bm] of (max, sum, argmax) per column wave
     float* lmax = (float*)p.smem;
     float* lsum = lmax + p.wgn * p.bm;
     int* lidx = (int*)(lsum + p.wgn * p.bm);
+    const int lc = p.col0 + (p.lane & 15);  // this lane's columns: lc + 16 j
+    const bool full = p.col0 + 16 * FN <= p.N;  // wave-uniform: every column of the wave exists
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = epi_row(p, i, e);
         const int tg = row < p.M ? tgt[row] : -1;
+        // this lane's values (missing columns as -inf), max and first argmax
+        float v[FN];
         float mx = -INFINITY;
-        int ix = 0x7fffffff;
+        int jx = 0;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = epi_col(p, j);
-          if (col < p.N) {
-            const float v = acc[i][j][e];
-            if (v > mx) { mx = v; ix = col; }
-            if (col == tg) tgt_logit[row] = v;
-          }
+          v[j] = (full || lc + 16 * j < p.N) ? acc[i][j][e] : -INFINITY;
+          jx = v[j] > mx ? j : jx;
+          mx = fmaxf(mx, v[j]);
         }
+        int ix = mx == -INFINITY ? 0x7fffffff : lc + 16 * jx;
+        // the target logit, if one of this lane's columns is the target
+        const int jt = tg - lc;
+        const bool hit = jt >= 0 && jt < 16 * FN && (jt & 15) == 0;
+        float tv = v[0];
+#pragma unroll
+        for (int j = 1; j < FN; ++j) tv = (jt >> 4) == j ? v[j] : tv;
         // row max and first argmax over the 16 lanes of the row, then one exp per element
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) {
@@ -974,13 +992,12 @@ struct EpiCEPartial {
           if (omx > mx || (omx == mx && oix < ix)) ix = oix;
           mx = fmaxf(mx, omx);
         }
+        const float nm = mx == -INFINITY ? 0.f : -mx * L2E;
         float sm = 0.f;
-        if (mx != -INFINITY) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            if (epi_col(p, j) < p.N) sm += exp_fast(acc[i][j][e] - mx);
-        }
+        for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f(fmaf(v[j], L2E, nm));
         sm = xor16_sum(sm);
+        if (hit) tgt_logit[row] = tv;
         const int lr = p.wn * p.bm + p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
         if ((p.lane & 15) == 0) {
           lmax[lr] = mx;
