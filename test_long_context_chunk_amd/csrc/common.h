@@ -85,13 +85,39 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x));
 // summed into softmax normalisers or dlogits, never for a value that is stored as is).
 __device__ __forceinline__ float exp_fast(float x) { return __expf(x); }
 
-// Butterfly over the 16 lanes that share (lane / 16): every lane ends with the same
-// bitwise result because each step combines two partials of the same lane set.
-__device__ __forceinline__ float xor16_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, TTT_WAVE);
+// Value of lane ((lane - n) mod 16) of this lane's 16-lane row (a DPP row rotation, fused
+// into the consuming VALU instruction: no LDS traffic, no wait).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ int row_ror_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x120 + N, 0xf, 0xf, false);
+}
+// Sum over the 16 lanes of a row, by rotations of 8, 4, 2, 1: after the step of size s every
+// lane holds the combination of a set that repeats with period s, and each step adds two
+// equal-valued partials in either order, so all 16 lanes end with the same bitwise result.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
   return v;
 }
+// Row-wide max and the lowest index attaining it (index ties resolved to the smallest).
+__device__ __forceinline__ void row16_max_argmax(float& mx, int& ix) {
+#define TTT_ROW_STEP(N)                                                     \
+  {                                                                         \
+    const float om = row_ror<N>(mx);                                        \
+    const int oi = row_ror_i<N>(ix);                                        \
+    ix = (om > mx || (om == mx && oi < ix)) ? oi : ix;                      \
+    mx = fmaxf(mx, om);                                                     \
+  }
+  TTT_ROW_STEP(8) TTT_ROW_STEP(4) TTT_ROW_STEP(2) TTT_ROW_STEP(1)
+#undef TTT_ROW_STEP
+}
+__device__ __forceinline__ float xor16_sum(float v) { return row16_sum(v); }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 1; off < TTT_WAVE; off <<= 1) v += __shfl_xor(v, off, TTT_WAVE);

@@ -776,6 +776,54 @@ struct EpiDU {
       acc_to_lds<FM, FN, WGM, WGN>(p, acc);
       float* U = (float*)p.smem;
       const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+      constexpr int NT = AccTile<FM, FN, WGM, WGN>::NT;
+      constexpr int TPR = G::BN / 8, RPP = NT / TPR, NP = G::BM / RPP;  // rows of 8 per thread
+      if (m0 + G::BM <= p.M && n0 + G::BN <= p.N && (ld & 7) == 0 && (NT % TPR) == 0 && (G::BM % RPP) == 0) {
+        // interior tile: every GP / RES row piece is requested before any is used
+        const int c = (p.tid % TPR) * 8;
+        uint4 gq[NP], rq[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const int64_t o = (int64_t)(m0 + k * RPP + p.tid / TPR) * ld + n0 + c;
+          gq[k] = *(const uint4*)((const bf16_t*)GP + o);
+          rq[k] = RES ? *(const uint4*)((const bf16_t*)RES + o) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const int r = k * RPP + p.tid / TPR;
+          float4* up = (float4*)(U + r * G::BN + c);
+          const float4 a0 = up[0], a1 = up[1];
+          const float da[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const uint32_t gw[4] = {gq[k].x, gq[k].y, gq[k].z, gq[k].w};
+          const uint32_t rw[4] = {rq[k].x, rq[k].y, rq[k].z, rq[k].w};
+          float du[8];
+          float dot = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            du[2 * q] = da[2 * q] * __uint_as_float(gw[q] << 16);
+            du[2 * q + 1] = da[2 * q + 1] * __uint_as_float(gw[q] & 0xffff0000u);
+            dot = fmaf(da[2 * q], __uint_as_float(rw[q] << 16), dot);
+            dot = fmaf(da[2 * q + 1], __uint_as_float(rw[q] & 0xffff0000u), dot);
+          }
+          *(uint4*)((bf16_t*)DU + (int64_t)(m0 + r) * ld + n0 + c) =
+              make_uint4(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]), pack_bf16x2(du[4], du[5]),
+                         pack_bf16x2(du[6], du[7]));
+          up[0] = make_float4(du[0], du[1], du[2], du[3]);
+          up[1] = make_float4(du[4], du[5], du[6], du[7]);
+          if (cdot) {
+            if constexpr (TPR == 16) {
+              dot = row16_sum(dot);
+            } else {
+#pragma unroll
+              for (int off = 1; off < TPR; off <<= 1) dot += __shfl_xor(dot, off, TTT_WAVE);
+            }
+            if ((p.tid % TPR) == 0) cdot[(int64_t)p.tn * p.M + m0 + r] = dot;
+          }
+        }
+        __syncthreads();
+        lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
+        return;
+      }
 #pragma unroll 1
       for (int base = 0; base < G::BM * 32; base += AccTile<FM, FN, WGM, WGN>::NT) {
         const int idx = base + p.tid;
@@ -937,8 +985,8 @@ struct EpiGrad {
 // lane whose column is the row's target.
 __device__ __forceinline__ void ce_combine(float& mx, float& sm, int& ix, float omx, float osm, int oix) {
   const float nm = fmaxf(mx, omx);
-  const float a = (mx == -INFINITY) ? 0.f : sm * expf(mx - nm);
-  const float b = (omx == -INFINITY) ? 0.f : osm * expf(omx - nm);
+  const float a = (mx == -INFINITY) ? 0.f : sm * __builtin_amdgcn_exp2f((mx - nm) * 1.4426950408889634f);
+  const float b = (omx == -INFINITY) ? 0.f : osm * __builtin_amdgcn_exp2f((omx - nm) * 1.4426950408889634f);
   if (omx > mx || (omx == mx && oix < ix)) ix = oix;
   mx = nm;
   sm = a + b;
@@ -961,12 +1009,18 @@ struct EpiCEPartial {
     int* lidx = (int*)(lsum + p.wgn * p.bm);
     const int lc = p.col0 + (p.lane & 15);  // this lane's columns: lc + 16 j
     const bool full = p.col0 + 16 * FN <= p.N;  // wave-uniform: every column of the wave exists
+    // all target ids first: independent loads in flight together
+    int tgs[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tgs[i][e] = tgt[min(epi_row(p, i, e), p.M - 1)];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = epi_row(p, i, e);
-        const int tg = row < p.M ? tgt[row] : -1;
+        const int tg = row < p.M ? tgs[i][e] : -1;
         // this lane's values (missing columns as -inf), max and first argmax
         float v[FN];
         float mx = -INFINITY;
@@ -985,18 +1039,12 @@ struct EpiCEPartial {
 #pragma unroll
         for (int j = 1; j < FN; ++j) tv = (jt >> 4) == j ? v[j] : tv;
         // row max and first argmax over the 16 lanes of the row, then one exp per element
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float omx = __shfl_xor(mx, off, TTT_WAVE);
-          const int oix = __shfl_xor(ix, off, TTT_WAVE);
-          if (omx > mx || (omx == mx && oix < ix)) ix = oix;
-          mx = fmaxf(mx, omx);
-        }
+        row16_max_argmax(mx, ix);
         const float nm = mx == -INFINITY ? 0.f : -mx * L2E;
         float sm = 0.f;
 #pragma unroll
         for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f(fmaf(v[j], L2E, nm));
-        sm = xor16_sum(sm);
+        sm = row16_sum(sm);
         if (hit) tgt_logit[row] = tv;
         const int lr = p.wn * p.bm + p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
         if ((p.lane & 15) == 0) {
@@ -1006,22 +1054,18 @@ struct EpiCEPartial {
         }
       }
     __syncthreads();
-    if (p.wn == 0 && (p.lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = epi_row(p, i, e);
-          if (row >= p.M) continue;
-          const int lr = p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
-          float mx = lmax[lr], sm = lsum[lr];
-          int ix = lidx[lr];
-          for (int c = 1; c < p.wgn; ++c) ce_combine(mx, sm, ix, lmax[c * p.bm + lr], lsum[c * p.bm + lr], lidx[c * p.bm + lr]);
-          const int64_t o = (int64_t)p.tn * ldp + row;
-          pmax[o] = mx;
-          psum[o] = sm;
-          pidx[o] = ix;
-        }
+    // one thread per tile row merges the column waves' partials
+    const int m0 = p.row0 - p.wm * WTM;
+    for (int t = p.tid; t < p.bm; t += p.nthr) {
+      const int row = m0 + t;
+      if (row >= p.M) continue;
+      float mx = lmax[t], sm = lsum[t];
+      int ix = lidx[t];
+      for (int c = 1; c < p.wgn; ++c) ce_combine(mx, sm, ix, lmax[c * p.bm + t], lsum[c * p.bm + t], lidx[c * p.bm + t]);
+      const int64_t o = (int64_t)p.tn * ldp + row;
+      pmax[o] = mx;
+      psum[o] = sm;
+      pidx[o] = ix;
     }
   }
 };
@@ -1040,23 +1084,28 @@ struct EpiCEProb {
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     if constexpr (sizeof(T) == 2 && TileGeo<FM, FN, WGM, WGN>::ROWS_FIT) {
       {
+        constexpr float L2E = 1.4426950408889634f;
         Packed<FM, FN> pp;
+        // every row's lse and target first: independent loads in flight together
+        float nls[FM][4];
+        int tg[FM][4];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          float ls[4];
-          int tg[4];
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = min(epi_row(p, i, e), p.M - 1);
-            ls[e] = lse[row];
-            tg[e] = tgt[row] - col_base;
+            nls[i][e] = -L2E * lse[row];
+            tg[i][e] = tgt[row] - col_base;
           }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int col = epi_col(p, j);
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (exp_fast(acc[i][j][e] - ls[e]) - (col == tg[e] ? 1.f : 0.f)) * inv_b;
+            for (int e = 0; e < 4; ++e)
+              v[e] = (__builtin_amdgcn_exp2f(fmaf(acc[i][j][e], L2E, nls[i][e])) - (col == tg[i][e] ? 1.f : 0.f)) * inv_b;
             pp[i][j][0] = pack_bf2(v[0], v[1]);
             pp[i][j][1] = pack_bf2(v[2], v[3]);
           }
