@@ -29,6 +29,8 @@ hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const v
                       int C, float lr, const float* sc, int delta_t);
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst);
 hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
+// Cache hint: read one dword per 128-byte line of [p, p + bytes) (sink is never written).
+hipError_t run_prefetch(hipStream_t st, const void* p, int64_t bytes, uint32_t* sink);
 
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
 // Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).

@@ -88,6 +88,13 @@ struct ttt_ctx {
   int64_t pos = 0;
   ttt_status sticky = TTT_OK;
 
+  // cache hints: reads of the next GEMM's weights run on a second stream (default
+  // priority), ordered after the launches enqueued so far; the main stream never waits
+  // for them
+  hipStream_t pf = nullptr;
+  hipEvent_t ev_pf = nullptr;
+  uint32_t* sink = nullptr;
+
   // tracing: event pairs around launches of the kinds set in prof_mask
   uint32_t prof_mask = 0;
   std::vector<hipEvent_t> ev_pool;
@@ -122,16 +129,31 @@ void free_all(ttt_ctx* c) {
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Split-K factor for a 128 x 128-tiled GEMM with a small output and a long K: enough
-// workgroups to cover the chip twice, at least 4 K-iterations per split.
+// Split-K slabs for a narrow output: as many as still fit in one round of the 512
+// workgroup slots (two 128 x 128 tiles per CU), so no slab waits for a second round.
 int choose_splits(int M, int N, int K, int es) {
   const int tiles = cdiv(M, 128) * cdiv(N, 128);
   const int kiters = cdiv(K, 128 / es);
-  int s = cdiv(512, tiles);
+  int s = 512 / tiles;
   if (s > kiters / 4) s = kiters / 4;
   if (s > SPLIT_MAX) s = SPLIT_MAX;
   if (s < 1) s = 1;
   return s;
+}
+
+// Cache hint: the bytes [p, p + bytes) are read on the side stream, after everything
+// enqueued so far on the main stream.
+void prefetch(ttt_ctx* c, const void* p, int64_t bytes) {
+  if (!c->pf || !p || bytes <= 0) return;
+  check(hipEventRecord(c->ev_pf, c->st));
+  check(hipStreamWaitEvent(c->pf, c->ev_pf, 0));
+  check(run_prefetch(c->pf, p, bytes, c->sink));
+}
+// The operands the forward GEMMs read of one fast tensor (bf16: W0^T and rn(D)^T).
+void prefetch_fwd(ttt_ctx* c, const FastTensor& f) {
+  const int64_t n = (int64_t)f.rows * f.cols * c->es;
+  if (c->prec == PREC_BF16) prefetch(c, f.W0T, n);
+  prefetch(c, f.WtT, n);
 }
 
 ttt_status validate(const ttt_config* c, const ttt_weights* w) {
@@ -289,6 +311,22 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   check(hipMemsetAsync(c->losses, 0, c->cfg.max_tokens * 4, c->st));
   check(hipMemsetAsync(c->amax, 0, c->cfg.max_tokens * 4, c->st));
   check(hipMemsetAsync(c->stats, 0, c->max_chunks * 2 * 4, c->st));
+  c->sink = dalloc<uint32_t>(c, 16);
+  check(hipStreamCreateWithFlags(&c->pf, hipStreamNonBlocking));
+  check(hipEventCreateWithFlags(&c->ev_pf, hipEventDisableTiming));
+}
+
+// Wait for the side stream, then release it (before any buffer it may read is freed).
+void release_side_stream(ttt_ctx* c) {
+  if (c->pf) {
+    (void)hipStreamSynchronize(c->pf);
+    (void)hipStreamDestroy(c->pf);
+    c->pf = nullptr;
+  }
+  if (c->ev_pf) {
+    (void)hipEventDestroy(c->ev_pf);
+    c->ev_pf = nullptr;
+  }
 }
 
 void prof_mark(ttt_ctx* c) {
@@ -331,6 +369,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   const int64_t bd = (int64_t)b * d;
   const int tnm = c->dot_tiles;
 
+  if (L > 0 && gelu) prefetch_fwd(c, c->blocks[0].w1);
   // a1 gather
   RUN(TTT_K_GATHER, run_gather(st, prec, tok, b, V, d, c->E_in, c->H, L == 0 ? c->Yb : nullptr, c->tok_prev,
                                c->tok_tgt, c->err));
@@ -339,6 +378,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
     RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
+    prefetch_fwd(c, B.w2);  // for the down-projection
     if (gelu) {
       RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
       GemmSeg2 s2;
@@ -350,6 +390,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
       RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, b, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
                                 foc ? B.ResA : nullptr, m, bp));
     }
+    if (l + 1 < L && gelu) prefetch_fwd(c, c->blocks[l + 1].w1);  // the next up-projection
+    else if (l + 1 == L) prefetch(c, c->E_out, (int64_t)V * d * es);  // the LM head
     const int S = choose_splits(b, d, bf ? 2 * m : m, es);
     GemmSeg2 s2;
     if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
@@ -358,6 +400,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   }
 
   // a5 LM head + CE forward (vocab-tiled online softmax, no b x V buffer)
+  if (L > 0) prefetch(c, c->E_outT, (int64_t)V * d * es);  // the dY GEMMs
   RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, b, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
                                     c->tgt_logit));
   RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_tiles, b, c->tgt_logit, c->lse,
@@ -384,8 +427,10 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
       Block& B = c->blocks[l];
       float* cA = foc ? c->cpart + (int64_t)B.cslot * b : nullptr;        // tnm slots
       float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * b : nullptr;  // one slot
+      prefetch(c, B.w2.Wop, (int64_t)m * d * es);  // for dA
       RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
       if (gelu) {
+        if (l > 0 || (foc && rms)) prefetch(c, B.w1.Wop, (int64_t)d * m * es);  // for dHn
         RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
                               foc ? B.ResA : nullptr, cA, m, bp));
         RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
@@ -461,11 +506,13 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
     check(hipStreamSynchronize(c->st));
   } catch (const HipFail& f) {
     (void)hipStreamSynchronize(c->st);
+    release_side_stream(c);
     free_all(c);
     delete c;
     return f.s;
   } catch (const std::bad_alloc&) {
     (void)hipStreamSynchronize(c->st);
+    release_side_stream(c);
     free_all(c);
     delete c;
     return TTT_ENOMEM;
@@ -492,6 +539,7 @@ ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_token
 ttt_status ttt_sync(ttt_ctx* c) {
   if (!c) return TTT_EINVAL;
   try {
+    if (c->pf) check(hipStreamSynchronize(c->pf));
     return read_sticky(c);
   } catch (const HipFail& f) {
     return f.s;
@@ -591,6 +639,7 @@ ttt_status ttt_profile_read(ttt_ctx* c, double* total_ms, int64_t* launches) {
 ttt_status ttt_destroy(ttt_ctx* c) {
   if (!c) return TTT_OK;
   (void)hipStreamSynchronize(c->st);
+  release_side_stream(c);
   for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   free_all(c);
   delete c;
