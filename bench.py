@@ -9,12 +9,20 @@ the timed region.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
   python bench.py [--steps K] [--warmup W] [--workload s760m] [--no-cpu-baseline]
+                  [--calibrate-copy]   (a 256 MiB device copy first: the reference kernel of
+                                        known size for scaling the FETCH_SIZE / WRITE_SIZE
+                                        counters in a rocprofv3 --pmc run of this script)
+
+roofline.traffic comes from the committed counter summary profiles/traffic_<workload>.md
+and is null unless that summary was taken on the current GEMM sources (sha256 match).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -63,6 +71,53 @@ def kind_flops_per_chunk(w, kind: str) -> float:
     return table.get(kind, 0.0)
 
 
+# GEMM kinds whose launches use a kernel no other kind uses (so a per-kernel counter
+# average is that kind's average); the epilogue type names the kernel.
+KIND_KERNEL = {"up": "EpiGelu", "du": "EpiDU", "dw": "EpiGrad", "ce_fwd": "EpiCEPartial"}
+GEMM_SOURCES = ["test_long_context_chunk_amd/csrc/gemm.h", "test_long_context_chunk_amd/csrc/gemm_inst.hip",
+                "test_long_context_chunk_amd/csrc/common.h"]
+
+
+def gemm_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per launch of `kind` from the committed counter summary, or None.
+
+    The summary holds lines `traffic <kind> <kernel> fetch_kib=<F> write_kib=<W> bytes=<B>`
+    (counters per dispatch, already scaled by the copy-kernel factors) and the sha256 of
+    the GEMM sources the counters were taken on; a different sha means the kernels changed
+    since, and the figure no longer applies.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^gemm_sources_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not m or m.group(1) != gemm_sources_sha256():
+        return None
+    m = re.search(rf"^traffic {re.escape(kind)} \S+ fetch_kib=\S+ write_kib=\S+ bytes=(\S+)", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 256 MiB, three times (for counter scaling)."""
+    import torch
+    n = 64 << 20
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    eprint("[bench] calibration copy: 3 x 268435456 bytes read + written")
+    del src, dst
+
+
 def cpu_baseline(w, P, x, n_chunks: int):
     """The fp64 oracle, as it stands, on the first n_chunks chunks of the same stream."""
     import numpy as np
@@ -90,6 +145,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunks", type=int, default=2)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -103,6 +159,8 @@ def main():
     import ttt_workloads as W
     import test_long_context_chunk_amd as ttt
 
+    if args.calibrate_copy:
+        calibrate_copy()
     w = W.preset(args.workload)
     T = w.n_tokens
     eprint(f"[bench] workload {w.name}: V={w.vocab} d={w.d_model} m={w.d_hidden} L={w.n_blocks} "
@@ -187,8 +245,9 @@ def main():
         "alg_flops_per_token": fpt,
         "roofline": {
             "bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": None,
+            "frac": achieved / peak, "traffic": measured_traffic(args.workload, dom),
             "alg_flops_per_launch": per_launch, "avg_launch_us": avg_s * 1e6, "launches": dom_n,
+            "kernel_name": KIND_KERNEL.get(dom, "EpiStoreF32"),
         },
     }
     if not args.no_cpu_baseline:
