@@ -7,6 +7,7 @@
 typedef uint16_t bf16_t;  // raw bfloat16 bit pattern in memory
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 #define TTT_WAVE 64
 
@@ -41,6 +42,15 @@ template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f
 __device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const uint4& a, const uint4& b, bf16_t) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+// bf16, 32 x 32 output block: one v_mfma_f32_32x32x16_bf16 per 16-k step. Lane l feeds row
+// (l % 32) of A and column (l % 32) of B, 8 consecutive k each, lanes 32..63 the next 8 k;
+// A and B use the same k slots, so the product is exact whatever the slot order. This form
+// runs at twice the rate of the 16 x 16 x 32 form on gfx950 (same issue time, twice the work).
+// Output: lane l, register r holds row 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32.
+__device__ __forceinline__ void mfma32(f32x16_t& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc,
+                                                0, 0, 0);
 }
 __device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const uint4& a, const uint4& b, float) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);

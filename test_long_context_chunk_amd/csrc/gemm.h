@@ -186,6 +186,25 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
   epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
 }
 
+// LDS stages of the direct-load pipeline for an output tile shape: the 256 x 128 tile
+// (bf16, one workgroup per CU) keeps three 48 KB stages; the others two.
+constexpr int gemm_stages(int BM, int BN) { return (BM == 256 && BN == 128) ? 3 : 2; }
+
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS tile row (tile-local row index t;
+// the A rows come first, then the B rows, both regions a multiple of 16 rows). 16 x 16
+// fragments: 8 consecutive rows share a chunk, swizzled by t mod 8. 32 x 32 fragments: 16
+// consecutive lanes read 16 consecutive rows of one chunk; with t / 2 mod 8 the even rows
+// fall in one half of the 256-byte bank window and the odd rows in the other, eight
+// distinct chunks each, so no two lanes share a bank.
+template <bool M32>
+__device__ __forceinline__ int lds_swz(int t) {
+  if constexpr (M32) return (t >> 1) & 7;
+  else return t & 7;
+}
+// Tile configs whose K loop uses 32 x 32 bf16 MFMA blocks and gemm_stages(BM, BN) stages.
+template <class T, int BM, int BN>
+constexpr bool use_mfma32() { return sizeof(T) == 2 && BM == 256 && BN == 128; }
+
 // Direct-to-LDS variant (K of both segments a multiple of the 128-byte slice): every wave
 // streams whole 8-row blocks of the tile with global_load_lds_dwordx4 (64 lanes x 16 B =
 // one 1 KB block), choosing each lane's source chunk so that the block lands in the same
@@ -233,6 +252,162 @@ __device__ __forceinline__ void dma_iteration(const char* __restrict__ cur, char
   }
 }
 
+// bf16 K-iteration on 32 x 32 output blocks (see mfma32): four 16-k steps per 128-byte slice;
+// in step ks, lanes 0..31 read 16-byte chunk 2 ks of their row, lanes 32..63 chunk 2 ks + 1.
+template <int BM, int BN, int WGM, int WGN, int PW>
+__device__ __forceinline__ void dma_iteration32(const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
+                                                const char* const (&src)[PW], int64_t kb, int wm, int wn, int lane,
+                                                f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  constexpr int ROWB = 128;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  if (issue) {
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + kb),
+                                       (__attribute__((address_space(3))) void*)(nxt + q * 1024), 16, 0, 0);
+  }
+  const char* sb = cur + BM * ROWB;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = 2 * ks + (lane >> 5);
+    uint4 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + (lane & 31);
+      af[i] = *(const uint4*)(cur + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * 32 + (lane & 31);
+      bfr[j] = *(const uint4*)(sb + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+  }
+}
+
+// Re-deal a wave's 32 x 32 accumulator blocks into the 16 x 16 register layout the
+// epilogues are written for (lane l, value e of sub-tile (i, j): row 16 i + 4 (l / 16) + e,
+// column 16 j + l % 16). Each block goes through a wave-private column-major LDS scratch
+// (column stride 36 floats: the 16-byte writes and reads of 16 lanes hit distinct banks).
+// Only this wave touches its scratch, and its LDS accesses complete in order.
+template <int FM32, int FN32>
+__device__ __forceinline__ void acc32_to_16(char* smem, int wave, int lane, const f32x16_t (&a32)[FM32][FN32],
+                                            f32x4_t (&a16)[2 * FM32][2 * FN32]) {
+  constexpr int LD = 36;
+  float* buf = (float*)smem + wave * (32 * LD);
+#pragma unroll
+  for (int i = 0; i < FM32; ++i)
+#pragma unroll
+    for (int j = 0; j < FN32; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4_t*)(buf + (lane & 31) * LD + 8 * q + 4 * (lane >> 5)) =
+            f32x4_t{a32[i][j][4 * q], a32[i][j][4 * q + 1], a32[i][j][4 * q + 2], a32[i][j][4 * q + 3]};
+      __asm__ __volatile__("" ::: "memory");
+#pragma unroll
+      for (int sr = 0; sr < 2; ++sr)
+#pragma unroll
+        for (int sc = 0; sc < 2; ++sc)
+          a16[2 * i + sr][2 * j + sc] = *(const f32x4_t*)(buf + (16 * sc + (lane & 15)) * LD + 16 * sr + 4 * (lane >> 4));
+      __asm__ __volatile__("" ::: "memory");
+    }
+}
+
+// ---- bf16 S-stage pipeline (S = gemm_stages): slice it + S - 1 is requested while slice it
+// is multiplied. Every iteration issues the same number of direct loads (the tail re-reads
+// the last slice into a stage that is never read), so "this stage has landed" is always
+// "at most (S - 2) * PW of this wave's loads outstanding".
+template <int PW>
+__device__ __forceinline__ void dma_slice(const char* const (&p1)[PW], const char* const (&p2)[PW], int kit_a, int kit,
+                                          char* dst) {
+  const bool seg2 = kit >= kit_a;
+  const int64_t kb = (int64_t)(seg2 ? kit - kit_a : kit) * 128;
+#pragma unroll
+  for (int q = 0; q < PW; ++q)
+    __builtin_amdgcn_global_load_lds((const void*)((seg2 ? p2[q] : p1[q]) + kb),
+                                     (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
+}
+
+// The four 16-k steps of one 128-byte slice held in `cur`, on 32 x 32 output blocks.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void mma_slice32(const char* cur, int wm, int wn, int lane,
+                                            f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  constexpr int ROWB = 128;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  const char* sb = cur + BM * ROWB;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = 2 * ks + (lane >> 5);
+    uint4 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + (lane & 31);
+      af[i] = *(const uint4*)(cur + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * 32 + (lane & 31);
+      bfr[j] = *(const uint4*)(sb + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+  }
+}
+
+template <int J, int S>
+__device__ __forceinline__ char* stage_ptr(char* s0, char* s1, char* s2) {
+  constexpr int j = J % S;
+  if constexpr (j == 0) return s0;
+  else if constexpr (j == 1) return s1;
+  else return s2;
+}
+
+// One K-iteration on stage J: wait until this wave's loads of the stage have landed (newer
+// stages may stay in flight) and its LDS reads are done, barrier (everyone's loads landed,
+// everyone finished reading the stage refilled next), request slice it + S - 1 into the
+// stage read last iteration, multiply stage J. The barrier is written out because a
+// fence-based barrier would also wait for the newer loads.
+template <int BM, int BN, int WGM, int WGN, int PW, int S, int J>
+__device__ __forceinline__ void step_slice32(char* s0, char* s1, char* s2, const char* const (&p1)[PW],
+                                             const char* const (&p2)[PW], int kit_a, int kit0, int it, int n, int dmaoff,
+                                             int wm, int wn, int lane,
+                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  constexpr int NOUT = (S - 2) * PW;
+  static_assert(NOUT < 64, "vmcnt holds at most 63");
+  __asm__ __volatile__("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NOUT) : "memory");
+  dma_slice<PW>(p1, p2, kit_a, kit0 + min(it + S - 1, n - 1), stage_ptr<J + S - 1, S>(s0, s1, s2) + dmaoff);
+  mma_slice32<BM, BN, WGM, WGN>(stage_ptr<J, S>(s0, s1, s2), wm, wn, lane, acc);
+}
+
+// The K loop. The stage pointers are restrict-qualified (they never overlap) and reach here
+// through an opaque offset, so every LDS read and direct load carries an alias scope: the
+// compiler then never waits for loads into one stage before reading another.
+template <int BM, int BN, int WGM, int WGN, int PW, int S>
+__device__ __forceinline__ void kloop32(char* __restrict__ s0, char* __restrict__ s1, char* __restrict__ s2,
+                                        const char* const (&p1)[PW], const char* const (&p2)[PW], int kit_a, int kit0,
+                                        int n, int dmaoff, int wm, int wn, int lane,
+                                        f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  static_assert(S == 2 || S == 3, "two or three stages");
+  dma_slice<PW>(p1, p2, kit_a, kit0, s0 + dmaoff);
+  if constexpr (S > 2) dma_slice<PW>(p1, p2, kit_a, kit0 + min(1, n - 1), s1 + dmaoff);
+  for (int it = 0; it < n; it += S) {
+    step_slice32<BM, BN, WGM, WGN, PW, S, 0>(s0, s1, s2, p1, p2, kit_a, kit0, it, n, dmaoff, wm, wn, lane, acc);
+    if (it + 1 < n)
+      step_slice32<BM, BN, WGM, WGN, PW, S, 1>(s0, s1, s2, p1, p2, kit_a, kit0, it + 1, n, dmaoff, wm, wn, lane, acc);
+    if constexpr (S > 2)
+      if (it + 2 < n)
+        step_slice32<BM, BN, WGM, WGN, PW, S, 2>(s0, s1, s2, p1, p2, kit_a, kit0, it + 2, n, dmaoff, wm, wn, lane, acc);
+  }
+  __syncthreads();  // every request has landed and every read is done: the LDS is free
+}
+
 template <class T, int BM, int BN, int WGM, int WGN, class Epi>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Epi epi) {
   constexpr int WGM_ = WGM, WGN_ = WGN;
@@ -242,7 +417,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int PW = (BM + BN) / 8 / NW;  // 8-row blocks per wave
-  static_assert(((BM + BN) / 8) % NW == 0 && (BM / 8) % PW == 0, "each wave streams blocks of one operand");
+  static_assert(((BM + BN) / 8) % NW == 0, "whole 8-row blocks per wave");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -261,24 +436,25 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   const int kit0 = split * g.kps;
   const int kit1 = min(g.kiters, kit0 + g.kps);
 
-  // this wave's blocks all belong to X (first BM rows) or all to Y; per-row source
-  // pointers of both K-segments are formed once, outside the K loop
+  // per 8-row block of this wave (A rows first, then B rows): source pointers of both
+  // K-segments, formed once outside the K loop
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const bool xside = wave_s * PW * 8 < BM;
-  const int rbase = xside ? m0 + wave_s * PW * 8 : n0 + wave_s * PW * 8 - BM;
-  const int rlim = (xside ? g.M : g.N) - 1;
   const int rsub = lane >> 3;
-  const int cbyte = (((lane & 7) ^ rsub) << 4);
-  const char* const b1 = (const char*)(xside ? g.X : g.Y);
-  const char* const b2 = (const char*)(xside ? g.X2 : g.Y2);
-  const int64_t l1 = (xside ? g.ldx : g.ldy) * (int64_t)sizeof(T);
-  const int64_t l2 = (xside ? g.ldx2 : g.ldy2) * (int64_t)sizeof(T);
   const bool has2 = g.kiters > g.kit_a;
   const char* p1[PW];
   const char* p2[PW];
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
-    const int r = min(rbase + q * 8 + rsub, rlim);
+    const int blk = wave_s * PW + q;
+    const bool xs = blk * 8 < BM;  // whole 8-row blocks: BM % 8 == 0
+    const int t = blk * 8 + rsub;  // tile-local row
+    const int r = xs ? min(m0 + t, g.M - 1) : min(n0 + t - BM, g.N - 1);
+    // lane L writes physical chunk L & 7 of row t; it loads logical chunk (L & 7) ^ swz(t)
+    const int cbyte = ((lane & 7) ^ lds_swz<use_mfma32<T, BM, BN>()>(t)) << 4;
+    const char* const b1 = (const char*)(xs ? g.X : g.Y);
+    const char* const b2 = (const char*)(xs ? g.X2 : g.Y2);
+    const int64_t l1 = (xs ? g.ldx : g.ldy) * (int64_t)sizeof(T);
+    const int64_t l2 = (xs ? g.ldx2 : g.ldy2) * (int64_t)sizeof(T);
     p1[q] = b1 + (int64_t)r * l1 + cbyte;
     p2[q] = has2 ? b2 + (int64_t)r * l2 + cbyte : p1[q];
   }
@@ -301,22 +477,39 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (kit0 < kit1) issue(kit0, 0);
-  for (int it = kit0; it < kit1; ++it) {
-    const int cur = (it - kit0) & 1;
-    // own requests for this stage are done, then everyone's (and the other stage is free)
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    __syncthreads();
-    const int nit = it + 1;
-    const bool seg2 = nit >= kit_a;
-    const int64_t kb = (int64_t)(seg2 ? nit - kit_a : nit) * ROWB;
-    const char* src[PW];
+  if constexpr (use_mfma32<T, BM, BN>()) {
+    // 32 x 32 MFMA blocks, S-stage pipeline; re-dealt into the 16 x 16 layout after
+    constexpr int S = gemm_stages(BM, BN);
+    f32x16_t acc32[WTM / 32][WTN / 32];
 #pragma unroll
-    for (int q = 0; q < PW; ++q) src[q] = seg2 ? p2[q] : p1[q];
-    dma_iteration<T, BM, BN, WGM, WGN, PW>(smem + cur * STAGE, sdst + (cur ^ 1) * STAGE, nit < kit1, src, kb, wm, wn,
-                                           lane, acc);
+    for (int i = 0; i < WTM / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN / 32; ++j) acc32[i][j] = f32x16_t{};
+    int zero;
+    __asm__ __volatile__("s_mov_b32 %0, 0" : "=s"(zero));
+    char* const sm = smem + zero;
+    if (kit0 < kit1)
+      kloop32<BM, BN, WGM, WGN, PW, S>(sm, sm + STAGE, S > 2 ? sm + 2 * STAGE : sm + STAGE, p1, p2, kit_a, kit0,
+                                       kit1 - kit0, (wave_s * PW) * 1024, wm, wn, lane, acc32);
+    acc32_to_16<WTM / 32, WTN / 32>(smem, wave, lane, acc32, acc);
+    __syncthreads();  // the epilogue may reuse the LDS
+  } else {
+    if (kit0 < kit1) issue(kit0, 0);
+    for (int it = kit0; it < kit1; ++it) {
+      const int cur = (it - kit0) & 1;
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      __syncthreads();
+      const int nit = it + 1;
+      const bool seg2 = nit >= kit_a;
+      const int64_t kb = (int64_t)(seg2 ? nit - kit_a : nit) * ROWB;
+      const char* src[PW];
+#pragma unroll
+      for (int q = 0; q < PW; ++q) src[q] = seg2 ? p2[q] : p1[q];
+      dma_iteration<T, BM, BN, WGM, WGN, PW>(smem + cur * STAGE, sdst + (cur ^ 1) * STAGE, nit < kit1, src, kb, wm,
+                                             wn, lane, acc);
+    }
+    __syncthreads();  // the epilogue may reuse the LDS
   }
-  __syncthreads();  // the epilogue may reuse the LDS
 
   EpiPos pos;
   pos.row0 = m0 + wm * WTM;
@@ -331,7 +524,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   pos.bn = BN;
   pos.tid = tid;
   pos.nthr = NW * 64;
-  pos.smem_bytes = 2 * STAGE;
+  pos.smem_bytes = gemm_stages(BM, BN) * STAGE;
   pos.tm = tm;
   pos.tn = tn;
   pos.tile = tile;
@@ -406,7 +599,7 @@ template <int FM, int FN, int WGM, int WGN>
 struct TileGeo {
   static constexpr int WTM = 16 * FM, WTN = 16 * FN;
   static constexpr int BM = WGM * WTM, BN = WGN * WTN;
-  static constexpr int SMEM = 2 * (BM + BN) * 128;
+  static constexpr int SMEM = gemm_stages(BM, BN) * (BM + BN) * 128;
   static constexpr bool ROWS_PAD = BM * (BN + 8) * 2 <= SMEM;
   static constexpr int LDR = ROWS_PAD ? BN + 8 : BN;         // row-major staging stride
   static constexpr bool ROWS_FIT = BM * LDR * 2 <= SMEM;
@@ -590,6 +783,17 @@ struct EpiStoreF32 {
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float* Cs = C + (int64_t)p.split * split_stride;
+    if (accumulate) {
+      // every old value is requested before any is used (clamped addresses, masked below)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = min(epi_row(p, i, e), p.M - 1);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j][e] += Cs[(int64_t)row * ldc + min(epi_col(p, j), p.N - 1)];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -600,8 +804,7 @@ struct EpiStoreF32 {
         for (int j = 0; j < FN; ++j) {
           const int col = epi_col(p, j);
           if (col >= p.N) continue;
-          float* d = Cs + (int64_t)row * ldc + col;
-          *d = accumulate ? *d + acc[i][j][e] : acc[i][j][e];
+          Cs[(int64_t)row * ldc + col] = acc[i][j][e];
         }
       }
   }
@@ -1145,7 +1348,7 @@ struct Seg2 {
 
 template <class T, int BM, int BN, int WGM, int WGN, class Epi>
 inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, const Epi& epi) {
-  constexpr size_t lds = 2 * (size_t)(BM + BN) * 128;
+  constexpr size_t lds = (size_t)gemm_stages(BM, BN) * (BM + BN) * 128;
   auto kern = gemm_dma_kernel<T, BM, BN, WGM, WGN, Epi>;
   static bool lds_attr = false;  // per instantiation
   if (!lds_attr) {
@@ -1158,15 +1361,28 @@ inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, cons
   return hipGetLastError();
 }
 
-// Tile plan of a GEMM launch (shared with the host code that sizes per-tile buffers).
+// Tile plan of a GEMM launch (shared with the host code that sizes per-tile buffers and
+// picks split-K factors). slots = workgroups the chip runs at once for that tile.
 struct TilePlan {
   int bm, bn;
   bool dma;
+  int slots;
 };
 inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
   const int ke = 128 / es;
-  TilePlan t{128, 128, (K % ke == 0) && (K2 % ke == 0)};
-  if (t.dma && splits <= 1 && ((M + 255) / 256) * ((N + 255) / 256) >= 256) t.bm = t.bn = 256;
+  const bool dma = (K % ke == 0) && (K2 % ke == 0);
+  const int tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (dma && es == 2) {
+    // measured per shape at b = 1024: split-K and the wide-N up / dA GEMMs run best on
+    // 256 x 128 tiles (32 x 32 blocks, 3 stages); short-K weight gradients on 128 x 128
+    // (two per CU); outputs with at least 256 tiles of 256 x 256 (LM head) on those
+    if (splits > 1) return TilePlan{256, 128, true, 256};
+    if (K + K2 <= 1024) return TilePlan{128, 128, true, 512};
+    if (tiles256 >= 256) return TilePlan{256, 256, true, 256};
+    return TilePlan{256, 128, true, 256};
+  }
+  TilePlan t{128, 128, dma, 512};  // 4 waves, 2 stages, 2 per CU
+  if (t.dma && splits <= 1 && tiles256 >= 256) t = TilePlan{256, 256, true, 256};
   return t;
 }
 
@@ -1196,16 +1412,26 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
   g.kiters = g.kit_a + (s2.K + KE - 1) / KE;
   const TilePlan plan = gemm_plan(M, N, K, s2.K, (int)sizeof(T), splits);
   if (plan.dma) {
-    if (plan.bm == 256) {
-      g.tiles_m = (M + 255) / 256;
-      g.tiles_n = (N + 255) / 256;
-      g.kps = g.kiters;
-      return launch_dma<T, 256, 256, 2, 4>(st, g, 1, epi);
+    if constexpr (sizeof(T) == 2) {
+      if (plan.bm == 256 && plan.bn == 128) {
+        g.tiles_m = (M + 255) / 256;
+        g.tiles_n = (N + 127) / 128;
+        g.kps = (g.kiters + splits - 1) / splits;
+        return launch_dma<T, 256, 128, 4, 2>(st, g, splits, epi);
+      }
     }
-    g.tiles_m = (M + 127) / 128;
-    g.tiles_n = (N + 127) / 128;
-    g.kps = (g.kiters + splits - 1) / splits;
-    return launch_dma<T, 128, 128, 2, 2>(st, g, splits, epi);
+    {
+      if (plan.bm == 256) {
+        g.tiles_m = (M + 255) / 256;
+        g.tiles_n = (N + 255) / 256;
+        g.kps = g.kiters;
+        return launch_dma<T, 256, 256, 2, 4>(st, g, 1, epi);
+      }
+      g.tiles_m = (M + 127) / 128;
+      g.tiles_n = (N + 127) / 128;
+      g.kps = (g.kiters + splits - 1) / splits;
+      return launch_dma<T, 128, 128, 2, 2>(st, g, splits, epi);
+    }
   }
   g.tiles_m = (M + 127) / 128;
   g.tiles_n = (N + 127) / 128;

@@ -66,6 +66,17 @@ hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx,
   });
 }
 
+int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits) {
+  const int es = prec == PREC_BF16 ? 2 : 4;
+  const TilePlan t = gemm_plan(M, N, K, K2, es, 2);
+  const int tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  const int kiters = (K + K2) / (128 / es);
+  int s = t.slots / tiles;
+  if (s > kiters / 4) s = kiters / 4;
+  if (s > max_splits) s = max_splits;
+  return s < 1 ? 1 : s;
+}
+
 void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n) {
   const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits);
   *tile_m = t.bm;

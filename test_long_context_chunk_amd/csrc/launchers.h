@@ -67,6 +67,10 @@ hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx,
 // Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits):
 // per-tile buffers (CE partials, sums of squares, partial dots) are sized from it.
 void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n);
+// Split-K slabs for a GEMM with a small output and a long K (K + K2): as many as fit in one
+// round of the workgroups the chip runs at once for its tile shape, at least 4 K-iterations
+// per slab, at most max_splits.
+int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits);
 // Weight-gradient epilogue: G [M x ldg] in the GEMM precision and one sum of squares of the
 // fp32 accumulators per output tile in slot[tile].
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,

@@ -129,18 +129,6 @@ void free_all(ttt_ctx* c) {
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Split-K slabs for a narrow output: as many as still fit in one round of the 512
-// workgroup slots (two 128 x 128 tiles per CU), so no slab waits for a second round.
-int choose_splits(int M, int N, int K, int es) {
-  const int tiles = cdiv(M, 128) * cdiv(N, 128);
-  const int kiters = cdiv(K, 128 / es);
-  int s = 512 / tiles;
-  if (s > kiters / 4) s = kiters / 4;
-  if (s > SPLIT_MAX) s = SPLIT_MAX;
-  if (s < 1) s = 1;
-  return s;
-}
-
 // Cache hint: the bytes [p, p + bytes) are read on the side stream, after everything
 // enqueued so far on the main stream.
 void prefetch(ttt_ctx* c, const void* p, int64_t bytes) {
@@ -392,7 +380,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     }
     if (l + 1 < L && gelu) prefetch_fwd(c, c->blocks[l + 1].w1);  // the next up-projection
     else if (l + 1 == L) prefetch(c, c->E_out, (int64_t)V * d * es);  // the LM head
-    const int S = choose_splits(b, d, bf ? 2 * m : m, es);
+    const int S = gemm_split_k(prec, b, d, m, bf ? m : 0, SPLIT_MAX);
     GemmSeg2 s2;
     if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
     RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, bd, 0, s2));
@@ -409,7 +397,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   const int64_t chunk_idx = tokpos / b;
   if (L > 0) {
     // a6 CE backward: dlogits recomputed per vocab super-tile, dY = sum over tiles of P E_out
-    const int S2 = choose_splits(b, d, c->vs, es);
+    const int S2 = gemm_split_k(prec, b, d, c->vs, 0, SPLIT_MAX);
     const float inv_b = 1.0f / (float)b;
     for (int v0 = 0, s = 0; v0 < V; v0 += c->vs, ++s) {
       const int vn = (V - v0) < c->vs ? (V - v0) : c->vs;
@@ -437,7 +425,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
         // the block input gradient is needed below this block, and for the compensation of
         // a rounded n (the lowest block's n = E_in[x] is exact when there is no norm)
         if (l > 0 || (foc && rms)) {
-          const int S = choose_splits(b, d, m, es);
+          const int S = gemm_split_k(prec, b, d, m, 0, SPLIT_MAX);
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb,
                                            foc ? B.ResN : nullptr, cN, l > 0));
@@ -449,7 +437,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
         RUN(TTT_K_DU, gemm_swiglu_bwd(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, c->UG, B.VU, c->DG, c->DV, B.ResA,
                                       cA, m));
         if (rms) {
-          const int S = choose_splits(b, d, 2 * m, es);
+          const int S = gemm_split_k(prec, b, d, m, m, SPLIT_MAX);
           GemmSeg2 s2{c->DV, m, B.Wu, m, m};
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->DG, m, B.Wg, m, b, d, m, S, c->part, d, bd, 0, s2));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb, B.ResN, cN,
