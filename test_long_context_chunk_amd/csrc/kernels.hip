@@ -68,21 +68,39 @@ __global__ void __launch_bounds__(NT) k_rmsnorm(const float* __restrict__ H, int
   }
 }
 
-// dst[c, r] = src[r, c] for r < R, c < C through a 64 x 64 LDS tile.
+// dst[c, r] = src[r, c] for r < R, c < C through a 64 x 64 LDS tile. Interior tiles move
+// 16-byte pieces both ways (8 bf16 or 4 fp32 consecutive elements of a source row in, of a
+// destination row out); edge tiles go element by element.
 template <class T>
 __global__ void __launch_bounds__(NT) k_transpose(const T* __restrict__ src, int64_t lds, int R, int C,
                                                   T* __restrict__ dst, int64_t ldd) {
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte piece
+  __shared__ T tile[64][64 + V];     // [source column][source row]
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int r = r0 + k, c = c0 + tx;
-    if (r < R && c < C) tile[k][tx] = src[(int64_t)r * lds + c];
+  const bool full = r0 + 64 <= R && c0 + 64 <= C && (lds % V) == 0 && (ldd % V) == 0;
+  if (full) {
+    for (int idx = threadIdx.x; idx < 64 * (64 / V); idx += NT) {
+      const int r = idx / (64 / V), c = (idx % (64 / V)) * V;
+      const uint4 v = *(const uint4*)(src + (int64_t)(r0 + r) * lds + c0 + c);
+      const T* e = (const T*)&v;
+#pragma unroll
+      for (int q = 0; q < V; ++q) tile[c + q][r] = e[q];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 64 * (64 / V); idx += NT) {
+      const int c = idx / (64 / V), r = (idx % (64 / V)) * V;
+      *(uint4*)(dst + (int64_t)(c0 + c) * ldd + r0 + r) = *(const uint4*)&tile[c][r];
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += NT) {
+    const int r = idx / 64, c = idx % 64;
+    if (r0 + r < R && c0 + c < C) tile[c][r] = src[(int64_t)(r0 + r) * lds + c0 + c];
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int c = c0 + k, r = r0 + tx;
-    if (c < C && r < R) dst[(int64_t)c * ldd + r] = tile[tx][k];
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += NT) {
+    const int c = idx / 64, r = idx % 64;
+    if (r0 + r < R && c0 + c < C) dst[(int64_t)(c0 + c) * ldd + r0 + r] = tile[c][r];
   }
 }
 

@@ -94,6 +94,11 @@ struct ttt_ctx {
   hipStream_t pf = nullptr;
   hipEvent_t ev_pf = nullptr;
   uint32_t* sink = nullptr;
+  // off-critical-path work (the transposed copies the weight-gradient GEMMs read) runs on a
+  // third stream (default priority): it starts after an event on the main stream, and the
+  // main stream waits for its event right before the consumer
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_to_aux = nullptr, ev_from_aux = nullptr;
 
   // tracing: event pairs around launches of the kinds set in prof_mask
   uint32_t prof_mask = 0;
@@ -137,6 +142,15 @@ void prefetch(ttt_ctx* c, const void* p, int64_t bytes) {
   check(hipStreamWaitEvent(c->pf, c->ev_pf, 0));
   check(run_prefetch(c->pf, p, bytes, c->sink));
 }
+// Enqueue on the aux stream after everything enqueued so far on the main stream.
+void aux_fork(ttt_ctx* c) {
+  check(hipEventRecord(c->ev_to_aux, c->st));
+  check(hipStreamWaitEvent(c->aux, c->ev_to_aux, 0));
+}
+// Mark the aux work enqueued so far; aux_join makes the main stream wait for it.
+void aux_mark(ttt_ctx* c) { check(hipEventRecord(c->ev_from_aux, c->aux)); }
+void aux_join(ttt_ctx* c) { check(hipStreamWaitEvent(c->st, c->ev_from_aux, 0)); }
+
 // The operands the forward GEMMs read of one fast tensor (bf16: W0^T and rn(D)^T).
 void prefetch_fwd(ttt_ctx* c, const FastTensor& f) {
   const int64_t n = (int64_t)f.rows * f.cols * c->es;
@@ -302,6 +316,9 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->sink = dalloc<uint32_t>(c, 16);
   check(hipStreamCreateWithFlags(&c->pf, hipStreamNonBlocking));
   check(hipEventCreateWithFlags(&c->ev_pf, hipEventDisableTiming));
+  check(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
+  check(hipEventCreateWithFlags(&c->ev_to_aux, hipEventDisableTiming));
+  check(hipEventCreateWithFlags(&c->ev_from_aux, hipEventDisableTiming));
 }
 
 // Wait for the side stream, then release it (before any buffer it may read is freed).
@@ -315,6 +332,16 @@ void release_side_stream(ttt_ctx* c) {
     (void)hipEventDestroy(c->ev_pf);
     c->ev_pf = nullptr;
   }
+  if (c->aux) {
+    (void)hipStreamSynchronize(c->aux);
+    (void)hipStreamDestroy(c->aux);
+    c->aux = nullptr;
+  }
+  for (hipEvent_t* e : {&c->ev_to_aux, &c->ev_from_aux})
+    if (*e) {
+      (void)hipEventDestroy(*e);
+      *e = nullptr;
+    }
 }
 
 void prof_mark(ttt_ctx* c) {
@@ -368,7 +395,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
     prefetch_fwd(c, B.w2);  // for the down-projection
     if (gelu) {
-      RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
+      // Hn^T is read only by the W1 gradient of the backward pass
+      aux_fork(c);
+      check(run_transpose(c->aux, prec, B.Hn, d, b, d, B.HnT, bp));
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
       RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
@@ -396,6 +425,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
 
   const int64_t chunk_idx = tokpos / b;
   if (L > 0) {
+    prefetch(c, c->blocks[L - 1].w2.Wop, (int64_t)m * d * es);  // the top block's dA
     // a6 CE backward: dlogits recomputed per vocab super-tile, dY = sum over tiles of P E_out
     const int S2 = gemm_split_k(prec, b, d, c->vs, 0, SPLIT_MAX);
     const float inv_b = 1.0f / (float)b;
@@ -408,19 +438,23 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     }
     RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, bd, b, d, c->dH, c->dHb, c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
-    RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+    // dH^T (read by the W2 gradient) is made on the aux stream while dA runs
+    aux_fork(c);
+    check(run_transpose(c->aux, prec, c->dHb, d, b, d, c->dHT, bp));
+    aux_mark(c);
 
     // a7 block backward, top to bottom
     for (int l = L - 1; l >= 0; --l) {
       Block& B = c->blocks[l];
       float* cA = foc ? c->cpart + (int64_t)B.cslot * b : nullptr;        // tnm slots
       float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * b : nullptr;  // one slot
-      prefetch(c, B.w2.Wop, (int64_t)m * d * es);  // for dA
-      RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
       if (gelu) {
         if (l > 0 || (foc && rms)) prefetch(c, B.w1.Wop, (int64_t)d * m * es);  // for dHn
         RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
                               foc ? B.ResA : nullptr, cA, m, bp));
+        if (l > 0) prefetch(c, c->blocks[l - 1].w2.Wop, (int64_t)m * d * es);  // the next block's dA
+        aux_join(c);  // dH^T, and every H_n^T of the forward pass
+        RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
         RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
         // the block input gradient is needed below this block, and for the compensation of
         // a rounded n (the lowest block's n = E_in[x] is exact when there is no norm)
@@ -429,9 +463,17 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb,
                                            foc ? B.ResN : nullptr, cN, l > 0));
-          if (l > 0) RUN(TTT_K_TRANSPOSE, run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+          if (l > 0) {
+            aux_fork(c);
+            check(run_transpose(c->aux, prec, c->dHb, d, b, d, c->dHT, bp));
+            aux_mark(c);
+          }
         }
-      } else if (foc) {
+      } else {
+        aux_join(c);  // dH^T
+        RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
+      }
+      if (!gelu && foc) {
         // SwiGLU (one block, W2 only fast): dA, then dn = dG Wg^T + dV Wu^T, only to carry
         // the loss compensation of A and n.
         RUN(TTT_K_DU, gemm_swiglu_bwd(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, c->UG, B.VU, c->DG, c->DV, B.ResA,
@@ -528,6 +570,7 @@ ttt_status ttt_sync(ttt_ctx* c) {
   if (!c) return TTT_EINVAL;
   try {
     if (c->pf) check(hipStreamSynchronize(c->pf));
+    if (c->aux) check(hipStreamSynchronize(c->aux));
     return read_sticky(c);
   } catch (const HipFail& f) {
     return f.s;
