@@ -27,6 +27,7 @@ struct FastTensor {
   void* WtT = nullptr;     // bf16: rn(D)^T, fp32: (W0 + D)^T  [cols x rows]
   void* G = nullptr;       // chunk gradient in the GEMM precision [rows x cols]
   int slot0 = 0;           // first grad-norm slot
+  hipEvent_t ev_upd = nullptr;  // recorded on the aux stream after this tensor's last update
 };
 
 struct Block {
@@ -203,6 +204,7 @@ void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
   int tm = 0, tn = 0;
   gemm_tile_shape(c->prec, rows, cols, c->bp, 0, 1, &tm, &tn);
   c->nslots += cdiv(rows, tm) * cdiv(cols, tn);
+  check(hipEventCreateWithFlags(&f.ev_upd, hipEventDisableTiming));
   c->fast.push_back(&f);
 }
 
@@ -342,6 +344,11 @@ void release_side_stream(ttt_ctx* c) {
       (void)hipEventDestroy(*e);
       *e = nullptr;
     }
+  for (FastTensor* f : c->fast)
+    if (f->ev_upd) {
+      (void)hipEventDestroy(f->ev_upd);
+      f->ev_upd = nullptr;
+    }
 }
 
 void prof_mark(ttt_ctx* c) {
@@ -395,6 +402,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
     prefetch_fwd(c, B.w2);  // for the down-projection
     if (gelu) {
+      check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       // Hn^T is read only by the W1 gradient of the backward pass
       aux_fork(c);
       check(run_transpose(c->aux, prec, B.Hn, d, b, d, B.HnT, bp));
@@ -410,6 +418,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     if (l + 1 < L && gelu) prefetch_fwd(c, c->blocks[l + 1].w1);  // the next up-projection
     else if (l + 1 == L) prefetch(c, c->E_out, (int64_t)V * d * es);  // the LM head
     const int S = gemm_split_k(prec, b, d, m, bf ? m : 0, SPLIT_MAX);
+    check(hipStreamWaitEvent(st, B.w2.ev_upd, 0));  // the previous chunk's step of W2
     GemmSeg2 s2;
     if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
     RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, bd, 0, s2));
@@ -492,9 +501,18 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
 
   // a8 global grad norm and clip scale; a9 update
   RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx, c->err));
-  for (FastTensor* f : c->fast)
-    RUN(TTT_K_UPDATE, run_update(st, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols, c->cfg.lr, c->sc,
-                                 bf ? 1 : 0));
+  // The step runs on the aux stream, in the order the next chunk's forward pass needs the
+  // tensors; each GEMM that reads a fast tensor waits for that tensor's event. (A context
+  // with no blocks has no fast tensors.)
+  if (!c->fast.empty()) {
+    aux_fork(c);
+    for (FastTensor* f : c->fast) {
+      check(run_update(c->aux, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols, c->cfg.lr, c->sc,
+                       bf ? 1 : 0));
+      check(hipEventRecord(f->ev_upd, c->aux));
+    }
+    aux_mark(c);
+  }
 }
 
 ttt_status read_sticky(ttt_ctx* c) {
@@ -617,6 +635,7 @@ ttt_status ttt_fast_weights(ttt_ctx* c, int32_t block, int32_t which, int32_t ki
   if (which == 1 && c->cfg.mlp != TTT_MLP_GELU) return TTT_EINVAL;
   FastTensor& f = which == 1 ? c->blocks[block].w1 : c->blocks[block].w2;
   try {
+    aux_join(c);  // a pending step of the last chunk
     check(run_export(c->st, c->prec, f.D, f.W0, (int64_t)f.rows * f.cols, kind, dst));
     return read_sticky(c);
   } catch (const HipFail& e) {
@@ -627,6 +646,7 @@ ttt_status ttt_fast_weights(ttt_ctx* c, int32_t block, int32_t which, int32_t ki
 ttt_status ttt_reset(ttt_ctx* c) {
   if (!c) return TTT_EINVAL;
   try {
+    aux_join(c);  // no pending step may land after the reset
     for (FastTensor* f : c->fast) reset_fast(c, *f);
     check(run_fill_u32(c->st, c->err, 1, 0u));
   } catch (const HipFail& f) {
