@@ -60,7 +60,6 @@ def kind_flops_per_chunk(w, kind: str) -> float:
     g = w.mlp == "gelu"
     table = {
         "ce_fwd": 2.0 * b * V * d,
-        "ce_prob": 2.0 * b * V * d,
         "ce_dy": 2.0 * b * V * d,
         "up": (2.0 if g else 4.0) * b * d * m * L,
         "down": 2.0 * b * d * m * L,

@@ -154,7 +154,7 @@ typedef enum {
   TTT_K_RESIDUAL = 5,  /* residual add of the down-projection partials       */
   TTT_K_CE_FWD = 6,    /* LM-head GEMM + online-softmax partials             */
   TTT_K_CE_MERGE = 7,  /* per-token merge of the vocab-tile partials         */
-  TTT_K_CE_PROB = 8,   /* logits recompute -> dlogits, per vocab super-tile  */
+  TTT_K_CE_PROB = 8,   /* dlogits from the stored softmax numerators         */
   TTT_K_CE_DY = 9,     /* dlogits x E_out GEMM (split over the vocab)        */
   TTT_K_DY_SUM = 10,   /* sum of the dY partials                             */
   TTT_K_DU = 11,       /* dY W2^T GEMM + GELU' epilogue                      */

@@ -186,9 +186,12 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
   epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
 }
 
-// LDS stages of the direct-load pipeline for an output tile shape: the 256 x 128 tile
-// (bf16, one workgroup per CU) keeps three 48 KB stages; the others two.
-constexpr int gemm_stages(int BM, int BN) { return (BM == 256 && BN == 128) ? 3 : 2; }
+// LDS stages of the direct-load pipeline for an output tile shape: three when three fit the
+// 160 KB of a CU (one workgroup per CU), else two; the 128 x 128 tile keeps two so that two
+// workgroups share a CU.
+constexpr int gemm_stages(int BM, int BN) {
+  return ((BM + BN) * 128 * 3 <= 160 * 1024 && !(BM == 128 && BN == 128)) ? 3 : 2;
+}
 
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS tile row (tile-local row index t;
 // the A rows come first, then the B rows, both regions a multiple of 16 rows). 16 x 16
@@ -201,9 +204,13 @@ __device__ __forceinline__ int lds_swz(int t) {
   if constexpr (M32) return (t >> 1) & 7;
   else return t & 7;
 }
-// Tile configs whose K loop uses 32 x 32 bf16 MFMA blocks and gemm_stages(BM, BN) stages.
-template <class T, int BM, int BN>
-constexpr bool use_mfma32() { return sizeof(T) == 2 && BM == 256 && BN == 128; }
+// Tile shapes whose bf16 K loop runs on 32 x 32 MFMA blocks with gemm_stages(BM, BN) stages
+// (the wave tiles must be multiples of 32).
+constexpr bool tile_m32(int BM, int BN) { return !(BM == 128 && BN == 128) && !(BM == 256 && BN == 256); }
+template <class T, int BM, int BN, int WGM, int WGN>
+constexpr bool use_mfma32() {
+  return sizeof(T) == 2 && tile_m32(BM, BN) && (BM / WGM) % 32 == 0 && (BN / WGN) % 32 == 0;
+}
 
 // Direct-to-LDS variant (K of both segments a multiple of the 128-byte slice): every wave
 // streams whole 8-row blocks of the tile with global_load_lds_dwordx4 (64 lanes x 16 B =
@@ -450,7 +457,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
     const int t = blk * 8 + rsub;  // tile-local row
     const int r = xs ? min(m0 + t, g.M - 1) : min(n0 + t - BM, g.N - 1);
     // lane L writes physical chunk L & 7 of row t; it loads logical chunk (L & 7) ^ swz(t)
-    const int cbyte = ((lane & 7) ^ lds_swz<use_mfma32<T, BM, BN>()>(t)) << 4;
+    const int cbyte = ((lane & 7) ^ lds_swz<use_mfma32<T, BM, BN, WGM, WGN>()>(t)) << 4;
     const char* const b1 = (const char*)(xs ? g.X : g.Y);
     const char* const b2 = (const char*)(xs ? g.X2 : g.Y2);
     const int64_t l1 = (xs ? g.ldx : g.ldy) * (int64_t)sizeof(T);
@@ -477,7 +484,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (use_mfma32<T, BM, BN>()) {
+  if constexpr (use_mfma32<T, BM, BN, WGM, WGN>()) {
     // 32 x 32 MFMA blocks, S-stage pipeline; re-dealt into the 16 x 16 layout after
     constexpr int S = gemm_stages(BM, BN);
     f32x16_t acc32[WTM / 32][WTN / 32];
@@ -1183,9 +1190,8 @@ struct EpiGrad {
   }
 };
 
-// Online-softmax partials of one vocab tile of the LM head: per row, the tile's max
-// logit, sum of exp(z - max) and first argmax; the target logit is stored by the one
-// lane whose column is the row's target.
+// Merge two online-softmax partials (max logit, sum of exp(z - max), first argmax) of
+// disjoint column sets; an empty partial is (-inf, 0, any index).
 __device__ __forceinline__ void ce_combine(float& mx, float& sm, int& ix, float omx, float osm, int oix) {
   const float nm = fmaxf(mx, omx);
   const float a = (mx == -INFINITY) ? 0.f : sm * __builtin_amdgcn_exp2f((mx - nm) * 1.4426950408889634f);
@@ -1195,23 +1201,28 @@ __device__ __forceinline__ void ce_combine(float& mx, float& sm, int& ix, float 
   sm = a + b;
 }
 
+// LM head + online-softmax partials over the full vocabulary, one record per row and per
+// column wave (the wave's WTN consecutive vocabulary entries, record index = column / WTN):
+// max logit, sum of exp(z - max) and first argmax; the target logit is stored by the one
+// lane whose column is the row's target. With Q, also every softmax numerator relative to
+// its record's max, Q[t, v] = exp(z - max), in the GEMM operand precision (missing columns
+// contribute nothing).
+template <class T>
 struct EpiCEPartial {
   const int* tgt;    // [M] target ids
-  float* pmax;       // [tiles_n x ldp]
+  float* pmax;       // [M x nrec]
   float* psum;
   int* pidx;
   float* tgt_logit;  // [M]
-  int ldp;
+  int nrec;
+  T* Q;              // [M x ldq] or null
+  int64_t ldq;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
-    constexpr int WTM = 16 * FM;
     constexpr float L2E = 1.4426950408889634f;
-    // LDS: [wgn][bm] of (max, sum, argmax) per column wave
-    float* lmax = (float*)p.smem;
-    float* lsum = lmax + p.wgn * p.bm;
-    int* lidx = (int*)(lsum + p.wgn * p.bm);
-    const int lc = p.col0 + (p.lane & 15);  // this lane's columns: lc + 16 j
+    const int lc = p.col0 + (p.lane & 15);      // this lane's columns: lc + 16 j
     const bool full = p.col0 + 16 * FN <= p.N;  // wave-uniform: every column of the wave exists
+    const int rec = p.col0 / (16 * FN);
     // all target ids first: independent loads in flight together
     int tgs[FM][4];
 #pragma unroll
@@ -1246,76 +1257,31 @@ struct EpiCEPartial {
         const float nm = mx == -INFINITY ? 0.f : -mx * L2E;
         float sm = 0.f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f(fmaf(v[j], L2E, nm));
+        for (int j = 0; j < FN; ++j) {
+          const float q = __builtin_amdgcn_exp2f(fmaf(v[j], L2E, nm));
+          sm += q;
+          acc[i][j][e] = q;
+        }
         sm = row16_sum(sm);
         if (hit) tgt_logit[row] = tv;
-        const int lr = p.wn * p.bm + p.wm * WTM + 16 * i + 4 * (p.lane >> 4) + e;
-        if ((p.lane & 15) == 0) {
-          lmax[lr] = mx;
-          lsum[lr] = sm;
-          lidx[lr] = ix;
+        if ((p.lane & 15) == 0 && row < p.M && p.col0 < p.N) {
+          const int64_t o = (int64_t)row * nrec + rec;
+          pmax[o] = mx;
+          psum[o] = sm;
+          pidx[o] = ix;
         }
       }
-    __syncthreads();
-    // one thread per tile row merges the column waves' partials
-    const int m0 = p.row0 - p.wm * WTM;
-    for (int t = p.tid; t < p.bm; t += p.nthr) {
-      const int row = m0 + t;
-      if (row >= p.M) continue;
-      float mx = lmax[t], sm = lsum[t];
-      int ix = lidx[t];
-      for (int c = 1; c < p.wgn; ++c) ce_combine(mx, sm, ix, lmax[c * p.bm + t], lsum[c * p.bm + t], lidx[c * p.bm + t]);
-      const int64_t o = (int64_t)p.tn * ldp + row;
-      pmax[o] = mx;
-      psum[o] = sm;
-      pidx[o] = ix;
-    }
-  }
-};
-
-// dlogits of one vocab super-tile, recomputed from the logits tile in registers:
-// P[t, v] = (exp(z - lse_t) - [v == x_t]) / b, stored in the GEMM operand precision.
-template <class T>
-struct EpiCEProb {
-  const int* tgt;
-  const float* lse;
-  T* P;
-  int64_t ldp;
-  int col_base;  // vocab id of column 0
-  float inv_b;
-  template <int FM, int FN, int WGM, int WGN>
-  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
-    if constexpr (sizeof(T) == 2 && TileGeo<FM, FN, WGM, WGN>::ROWS_FIT) {
-      {
-        constexpr float L2E = 1.4426950408889634f;
-        Packed<FM, FN> pp;
-        // every row's lse and target first: independent loads in flight together
-        float nls[FM][4];
-        int tg[FM][4];
+    if (!Q) return;
+    if constexpr (sizeof(T) == 2) {
+      Packed<FM, FN> qq;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = min(epi_row(p, i, e), p.M - 1);
-            nls[i][e] = -L2E * lse[row];
-            tg[i][e] = tgt[row] - col_base;
-          }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = epi_col(p, j);
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              v[e] = (__builtin_amdgcn_exp2f(fmaf(acc[i][j][e], L2E, nls[i][e])) - (col == tg[i][e] ? 1.f : 0.f)) * inv_b;
-            pp[i][j][0] = pack_bf2(v[0], v[1]);
-            pp[i][j][1] = pack_bf2(v[2], v[3]);
-          }
+        for (int j = 0; j < FN; ++j) {
+          qq[i][j][0] = pack_bf2(acc[i][j][0], acc[i][j][1]);
+          qq[i][j][1] = pack_bf2(acc[i][j][2], acc[i][j][3]);
         }
-        stage_rows_bf16<FM, FN, WGM, WGN>(p, pp, (bf16_t*)P, ldp);
-        return;
-      }
+      if (stage_rows_bf16<FM, FN, WGM, WGN>(p, qq, (bf16_t*)Q, ldq)) return;
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -1323,14 +1289,10 @@ struct EpiCEProb {
       for (int e = 0; e < 4; ++e) {
         const int row = epi_row(p, i, e);
         if (row >= p.M) continue;
-        const int tg = tgt[row] - col_base;
-        const float ls = lse[row];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = epi_col(p, j);
-          if (col >= p.N) continue;
-          const float v = (exp_fast(acc[i][j][e] - ls) - (col == tg ? 1.f : 0.f)) * inv_b;
-          P[(int64_t)row * ldp + col] = from_f<T>(v);
+          if (col < p.N) Q[(int64_t)row * ldq + col] = from_f<T>(acc[i][j][e]);
         }
       }
   }
@@ -1367,22 +1329,21 @@ struct TilePlan {
   int bm, bn;
   bool dma;
   int slots;
+  int wtn;  // columns of one wave's sub-tile
 };
 inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
   const int ke = 128 / es;
   const bool dma = (K % ke == 0) && (K2 % ke == 0);
   const int tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (dma && es == 2) {
-    // measured per shape at b = 1024: split-K and the wide-N up / dA GEMMs run best on
-    // 256 x 128 tiles (32 x 32 blocks, 3 stages); short-K weight gradients on 128 x 128
-    // (two per CU); outputs with at least 256 tiles of 256 x 256 (LM head) on those
-    if (splits > 1) return TilePlan{256, 128, true, 256};
-    if (K + K2 <= 1024) return TilePlan{128, 128, true, 512};
-    if (tiles256 >= 256) return TilePlan{256, 256, true, 256};
-    return TilePlan{256, 128, true, 256};
+    // measured per shape at b = 1024: split-K, the wide-N up / dA GEMMs and the LM head
+    // run best on 256 x 128 tiles (32 x 32 blocks, 3 stages); short-K weight gradients on
+    // 128 x 128 (two per CU)
+    if (splits <= 1 && K + K2 <= 1024) return TilePlan{128, 128, true, 512, 64};
+    return TilePlan{256, 128, true, 256, 64};
   }
-  TilePlan t{128, 128, dma, 512};  // 4 waves, 2 stages, 2 per CU
-  if (t.dma && splits <= 1 && tiles256 >= 256) t = TilePlan{256, 256, true, 256};
+  TilePlan t{128, 128, dma, 512, 64};  // 4 waves, 2 stages, 2 per CU
+  if (t.dma && splits <= 1 && tiles256 >= 256) t = TilePlan{256, 256, true, 256, 64};
   return t;
 }
 
@@ -1420,13 +1381,15 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
         return launch_dma<T, 256, 128, 4, 2>(st, g, splits, epi);
       }
     }
-    {
+    if constexpr (sizeof(T) == 4) {
       if (plan.bm == 256) {
         g.tiles_m = (M + 255) / 256;
         g.tiles_n = (N + 255) / 256;
         g.kps = g.kiters;
         return launch_dma<T, 256, 256, 2, 4>(st, g, 1, epi);
       }
+    }
+    {
       g.tiles_m = (M + 127) / 128;
       g.tiles_n = (N + 127) / 128;
       g.kps = (g.kiters + splits - 1) / splits;

@@ -83,6 +83,11 @@ void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* til
   *tile_n = t.bn;
 }
 
+int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits) {
+  const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits);
+  return t.dma ? t.wtn : 64;  // the register-staged kernel: 2 x 2 waves of a 128 x 128 tile
+}
+
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* G, int64_t ldg, float* slot) {
   DISPATCH_T(prec, {
@@ -92,16 +97,10 @@ hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const
 }
 
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
-                           int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit) {
-  EpiCEPartial e{tgt, pmax, psum, pidx, tgt_logit, M};
-  DISPATCH_T(prec, return (launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e)));
-}
-
-hipError_t gemm_ce_prob(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
-                        int N, int K, const int* tgt, const float* lse, void* P, int64_t ldp, int col_base,
-                        float inv_b) {
+                           int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit,
+                           int nrec, void* Q, int64_t ldq) {
   DISPATCH_T(prec, {
-    EpiCEProb<T> e{tgt, lse, (T*)P, ldp, col_base, inv_b};
+    EpiCEPartial<T> e{tgt, pmax, psum, pidx, tgt_logit, nrec, (T*)Q, ldq};
     return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
   });
 }

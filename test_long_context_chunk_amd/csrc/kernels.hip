@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ c
 // a5 merge: combine the per-vocab-tile (max, sum exp, argmax) partials of each row in
 // tile order: lse = M + ln S, l_t = lse - z_t[x_t] ([E2E] eq. 1), argmax (lowest index).
 __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax, const float* __restrict__ psum,
-                                                 const int* __restrict__ pidx, int ntiles, int b,
+                                                 const int* __restrict__ pidx, int nrec, int b,
                                                  const float* __restrict__ tgt_logit, float* __restrict__ lse,
                                                  float* __restrict__ loss, int* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
@@ -175,8 +175,8 @@ __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax,
   if (row >= b) return;
   float mx = -INFINITY, sm = 0.f;
   int ix = 0x7fffffff;
-  for (int j = lane; j < ntiles; j += 64) {
-    const int64_t o = (int64_t)j * b + row;
+  for (int j = lane; j < nrec; j += 64) {
+    const int64_t o = (int64_t)row * nrec + j;
     ce_combine(mx, sm, ix, pmax[o], psum[o], pidx[o]);
   }
 #pragma unroll
@@ -289,6 +289,33 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, floa
   *(uint2*)p = make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
 }
 
+// a6 dlogits of the whole vocabulary, in place ([E2E] eq. 5 through the softmax
+// cross-entropy): Q holds exp(z - m) with m the max of the record (W consecutive vocabulary
+// entries) the column belongs to, so softmax = Q exp(m - lse) and
+//   P[t, v] = (Q[t, v] exp(m - lse_t) - [v == x_t]) / b.
+// Eight consecutive columns per thread (W and V are multiples of 8).
+template <class T>
+__global__ void __launch_bounds__(NT) k_ce_dlogits(T* __restrict__ Q, int b, int V, int W,
+                                                   const float* __restrict__ pmax, int nrec,
+                                                   const float* __restrict__ lse, const int* __restrict__ tgt,
+                                                   float inv_b) {
+  const int per_row = V >> 3;
+  const int64_t n = (int64_t)b * per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * NT) {
+    const int row = (int)(idx / per_row);
+    const int c0 = (int)(idx - (int64_t)row * per_row) << 3;
+    const float s = exp_fast(pmax[(int64_t)row * nrec + c0 / W] - lse[row]) * inv_b;
+    const int tc = tgt[row] - c0;
+    T* q = Q + (int64_t)row * V + c0;
+    const float4 lo = load4<T>(q), hi = load4<T>(q + 4);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = v[k] * s - (k == tc ? inv_b : 0.f);
+    store4<T>(q, v[0], v[1], v[2], v[3]);
+    store4<T>(q + 4, v[4], v[5], v[6], v[7]);
+  }
+}
+
 template <class T>
 __global__ void __launch_bounds__(NT) k_update(const T* __restrict__ G, float* __restrict__ D,
                                                const T* __restrict__ W0, T* __restrict__ Wop,
@@ -350,16 +377,6 @@ __global__ void __launch_bounds__(NT) k_export(const float* __restrict__ D, cons
                                                int kind, float* __restrict__ dst) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
     dst[i] = kind ? D[i] : to_f<T>(W0[i]) + D[i];
-}
-
-// Touch one dword of every 128-byte line of [p, p + bytes): pulls the lines into the
-// memory-side cache ahead of the GEMM that reads them next. `flag` is always 0 at run time;
-// it only keeps the loads from being discarded.
-__global__ void __launch_bounds__(NT) k_prefetch(const uint32_t* __restrict__ p, int64_t lines, int flag,
-                                                 uint32_t* __restrict__ sink) {
-  uint32_t acc = 0;
-  for (int64_t i = blockIdx.x * (int64_t)NT + threadIdx.x; i < lines; i += (int64_t)gridDim.x * NT) acc ^= p[i * 32];
-  if (flag && acc == 0x9e3779b9u) *sink = acc;
 }
 
 __global__ void __launch_bounds__(NT) k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
@@ -425,10 +442,18 @@ hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b
   return hipGetLastError();
 }
 
-hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int ntiles, int b,
+hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int nrec, int b,
                         const float* tgt_logit, float* lse, float* loss, int* amax) {
-  hipLaunchKernelGGL(k_ce_merge, dim3((b + 3) / 4), dim3(NT), 0, st, pmax, psum, pidx, ntiles, b, tgt_logit, lse,
+  hipLaunchKernelGGL(k_ce_merge, dim3((b + 3) / 4), dim3(NT), 0, st, pmax, psum, pidx, nrec, b, tgt_logit, lse,
                      loss, amax);
+  return hipGetLastError();
+}
+
+hipError_t run_ce_dlogits(hipStream_t st, int prec, void* Q, int b, int V, int W, const float* pmax, int nrec,
+                          const float* lse, const int* tgt, float inv_b) {
+  if (V % 8 || W % 8 || W <= 0) return hipErrorInvalidValue;
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_ce_dlogits<T>, dim3(grid_for((int64_t)b * (V / 8))), dim3(NT), 0, st, (T*)Q, b,
+                                      V, W, pmax, nrec, lse, tgt, inv_b));
   return hipGetLastError();
 }
 
@@ -455,15 +480,6 @@ hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const v
 
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst) {
   DISPATCH_T(prec, hipLaunchKernelGGL(k_export<T>, dim3(grid_for(n)), dim3(NT), 0, st, D, (const T*)W0, n, kind, dst));
-  return hipGetLastError();
-}
-
-hipError_t run_prefetch(hipStream_t st, const void* p, int64_t bytes, uint32_t* sink) {
-  const int64_t lines = bytes / 128;
-  if (lines <= 0) return hipSuccess;
-  int64_t g = (lines + NT - 1) / NT;
-  if (g > 1024) g = 1024;
-  hipLaunchKernelGGL(k_prefetch, dim3((unsigned)g), dim3(NT), 0, st, (const uint32_t*)p, lines, 0, sink);
   return hipGetLastError();
 }
 

@@ -19,8 +19,12 @@ hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, i
 hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int b, int d,
                          float* dH, void* dHb, const float* Hres, const void* Yb, float* cdot);
 hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss);
-hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int ntiles, int b,
+hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int nrec, int b,
                         const float* tgt_logit, float* lse, float* loss, int* amax);
+// dlogits in place: Q [b x V] (numerators relative to record max pmax[t][v / W]) becomes
+// P = (Q exp(pmax - lse) - onehot(target)) / b.
+hipError_t run_ce_dlogits(hipStream_t st, int prec, void* Q, int b, int V, int W, const float* pmax, int nrec,
+                          const float* lse, const int* tgt, float inv_b);
 hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int64_t pstride, const void* Hn,
                         const float* r, int b, int d, int rms, float* dH, void* dHb, const void* RES, float* cdot,
                         int update_dh);
@@ -29,8 +33,6 @@ hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const v
                       int C, float lr, const float* sc, int delta_t);
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst);
 hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
-// Cache hint: read one dword per 128-byte line of [p, p + bytes) (sink is never written).
-hipError_t run_prefetch(hipStream_t st, const void* p, int64_t bytes, uint32_t* sink);
 
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
 // Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).
@@ -75,10 +77,11 @@ int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits);
 // fp32 accumulators per output tile in slot[tile].
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* G, int64_t ldg, float* slot);
-// LM head + online-softmax partials over the full vocabulary (N = V).
+// LM head + online-softmax partials over the full vocabulary (N = V): one record per row and
+// per wave column block of gemm_wave_cols() vocabulary entries (records [M x nrec]), and,
+// when Q is non-null, the numerators exp(z - record max) [M x ldq] in the GEMM precision.
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
-                           int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit);
-// Recomputed logits of one vocab super-tile -> dlogits P = (softmax - onehot) / b.
-hipError_t gemm_ce_prob(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
-                        int N, int K, const int* tgt, const float* lse, void* P, int64_t ldp, int col_base,
-                        float inv_b);
+                           int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit,
+                           int nrec, void* Q, int64_t ldq);
+// Columns of one wave's sub-tile for a GEMM of this shape (the CE record width).
+int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits);

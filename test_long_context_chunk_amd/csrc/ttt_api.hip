@@ -10,7 +10,6 @@
 namespace {
 
 constexpr int SPLIT_MAX = 8;       // split-K slabs for the small-M, long-K GEMMs
-constexpr int VOCAB_SUPER = 16384;  // vocab columns of dlogits recomputed per CE-backward pass
 constexpr int PAD = 64;             // token dimension of transposed activations is padded to this
 
 // One fast tensor, natural layout [rows x cols] (W1 [d x m], W2 [m x d]). The forward GEMMs
@@ -54,7 +53,6 @@ struct ttt_ctx {
   hipStream_t st = nullptr;
   int prec = 0, es = 4;
   int b = 0, bp = 0, V = 0, d = 0, m = 0, L = 0;
-  int vs = 0;  // vocab super-tile width
   std::vector<void*> allocs;
 
   void *E_in = nullptr, *E_out = nullptr, *E_outT = nullptr;
@@ -66,7 +64,8 @@ struct ttt_ctx {
   int *tok_prev = nullptr, *tok_tgt = nullptr;
   float *pmax = nullptr, *psum = nullptr, *tgt_logit = nullptr, *lse = nullptr;
   int* pidx = nullptr;
-  int ce_tiles = 0;   // vocab tiles of the LM-head GEMM (one CE partial per tile and row)
+  int ce_w = 0;     // vocabulary entries per CE record (one wave's columns of the LM-head GEMM)
+  int ce_nrec = 0;  // CE records per row: ceil(V / ce_w)
   int dot_tiles = 0;  // column tiles of the dA GEMM (one partial dot per tile and row)
   void* P = nullptr;
   float* part = nullptr;
@@ -89,15 +88,9 @@ struct ttt_ctx {
   int64_t pos = 0;
   ttt_status sticky = TTT_OK;
 
-  // cache hints: reads of the next GEMM's weights run on a second stream (default
-  // priority), ordered after the launches enqueued so far; the main stream never waits
-  // for them
-  hipStream_t pf = nullptr;
-  hipEvent_t ev_pf = nullptr;
-  uint32_t* sink = nullptr;
-  // off-critical-path work (the transposed copies the weight-gradient GEMMs read) runs on a
-  // third stream (default priority): it starts after an event on the main stream, and the
-  // main stream waits for its event right before the consumer
+  // off-critical-path work (the transposed copies the weight-gradient GEMMs read, and the
+  // SGD step) runs on a second stream (default priority): it starts after an event on the
+  // main stream, and the main stream waits for its event right before the consumer
   hipStream_t aux = nullptr;
   hipEvent_t ev_to_aux = nullptr, ev_from_aux = nullptr;
 
@@ -113,6 +106,11 @@ namespace {
 struct HipFail {
   ttt_status s;
 };
+
+// Events that only order work between this library's streams on one device: no timing and a
+// device-scope release (the default system-scope release writes back and invalidates the
+// caches at every record, for a host that never reads this memory).
+constexpr unsigned kSyncEvent = hipEventDisableTiming | hipEventReleaseToDevice;
 
 inline void check(hipError_t e) {
   if (e == hipErrorOutOfMemory) throw HipFail{TTT_ENOMEM};
@@ -135,14 +133,6 @@ void free_all(ttt_ctx* c) {
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Cache hint: the bytes [p, p + bytes) are read on the side stream, after everything
-// enqueued so far on the main stream.
-void prefetch(ttt_ctx* c, const void* p, int64_t bytes) {
-  if (!c->pf || !p || bytes <= 0) return;
-  check(hipEventRecord(c->ev_pf, c->st));
-  check(hipStreamWaitEvent(c->pf, c->ev_pf, 0));
-  check(run_prefetch(c->pf, p, bytes, c->sink));
-}
 // Enqueue on the aux stream after everything enqueued so far on the main stream.
 void aux_fork(ttt_ctx* c) {
   check(hipEventRecord(c->ev_to_aux, c->st));
@@ -151,13 +141,6 @@ void aux_fork(ttt_ctx* c) {
 // Mark the aux work enqueued so far; aux_join makes the main stream wait for it.
 void aux_mark(ttt_ctx* c) { check(hipEventRecord(c->ev_from_aux, c->aux)); }
 void aux_join(ttt_ctx* c) { check(hipStreamWaitEvent(c->st, c->ev_from_aux, 0)); }
-
-// The operands the forward GEMMs read of one fast tensor (bf16: W0^T and rn(D)^T).
-void prefetch_fwd(ttt_ctx* c, const FastTensor& f) {
-  const int64_t n = (int64_t)f.rows * f.cols * c->es;
-  if (c->prec == PREC_BF16) prefetch(c, f.W0T, n);
-  prefetch(c, f.WtT, n);
-}
 
 ttt_status validate(const ttt_config* c, const ttt_weights* w) {
   if (!c || !w) return TTT_EINVAL;
@@ -204,7 +187,7 @@ void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
   int tm = 0, tn = 0;
   gemm_tile_shape(c->prec, rows, cols, c->bp, 0, 1, &tm, &tn);
   c->nslots += cdiv(rows, tm) * cdiv(cols, tn);
-  check(hipEventCreateWithFlags(&f.ev_upd, hipEventDisableTiming));
+  check(hipEventCreateWithFlags(&f.ev_upd, kSyncEvent));
   c->fast.push_back(&f);
 }
 
@@ -273,18 +256,14 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->Yb = dalloc<char>(c, (int64_t)b * d * es);
   c->tok_prev = dalloc<int>(c, (int64_t)b * 4);
   c->tok_tgt = dalloc<int>(c, (int64_t)b * 4);
-  {
-    int tm = 0, tn = 0;
-    gemm_tile_shape(c->prec, b, V, d, 0, 1, &tm, &tn);  // the LM-head GEMM
-    c->ce_tiles = cdiv(V, tn);
-  }
-  c->pmax = dalloc<float>(c, (int64_t)c->ce_tiles * b * 4);
-  c->psum = dalloc<float>(c, (int64_t)c->ce_tiles * b * 4);
-  c->pidx = dalloc<int>(c, (int64_t)c->ce_tiles * b * 4);
+  c->ce_w = gemm_wave_cols(c->prec, b, V, d, 0, 1);  // the LM-head GEMM
+  c->ce_nrec = cdiv(V, c->ce_w);
+  c->pmax = dalloc<float>(c, (int64_t)c->ce_nrec * b * 4);
+  c->psum = dalloc<float>(c, (int64_t)c->ce_nrec * b * 4);
+  c->pidx = dalloc<int>(c, (int64_t)c->ce_nrec * b * 4);
   c->tgt_logit = dalloc<float>(c, (int64_t)b * 4);
   c->lse = dalloc<float>(c, (int64_t)b * 4);
-  c->vs = V < VOCAB_SUPER ? V : VOCAB_SUPER;
-  c->P = dalloc<char>(c, (int64_t)b * c->vs * es);
+  if (L > 0) c->P = dalloc<char>(c, (int64_t)b * V * es);  // softmax numerators, then dlogits
   c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * b * d * 4);
   c->dH = dalloc<float>(c, (int64_t)b * d * 4);
   c->dHb = dalloc<char>(c, (int64_t)b * d * es);
@@ -315,25 +294,13 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   check(hipMemsetAsync(c->losses, 0, c->cfg.max_tokens * 4, c->st));
   check(hipMemsetAsync(c->amax, 0, c->cfg.max_tokens * 4, c->st));
   check(hipMemsetAsync(c->stats, 0, c->max_chunks * 2 * 4, c->st));
-  c->sink = dalloc<uint32_t>(c, 16);
-  check(hipStreamCreateWithFlags(&c->pf, hipStreamNonBlocking));
-  check(hipEventCreateWithFlags(&c->ev_pf, hipEventDisableTiming));
   check(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
-  check(hipEventCreateWithFlags(&c->ev_to_aux, hipEventDisableTiming));
-  check(hipEventCreateWithFlags(&c->ev_from_aux, hipEventDisableTiming));
+  check(hipEventCreateWithFlags(&c->ev_to_aux, kSyncEvent));
+  check(hipEventCreateWithFlags(&c->ev_from_aux, kSyncEvent));
 }
 
-// Wait for the side stream, then release it (before any buffer it may read is freed).
-void release_side_stream(ttt_ctx* c) {
-  if (c->pf) {
-    (void)hipStreamSynchronize(c->pf);
-    (void)hipStreamDestroy(c->pf);
-    c->pf = nullptr;
-  }
-  if (c->ev_pf) {
-    (void)hipEventDestroy(c->ev_pf);
-    c->ev_pf = nullptr;
-  }
+// Wait for the aux stream, then release it (before any buffer it may read is freed).
+void release_aux_stream(ttt_ctx* c) {
   if (c->aux) {
     (void)hipStreamSynchronize(c->aux);
     (void)hipStreamDestroy(c->aux);
@@ -354,7 +321,7 @@ void release_side_stream(ttt_ctx* c) {
 void prof_mark(ttt_ctx* c) {
   if (c->ev_used == c->ev_pool.size()) {
     hipEvent_t e;
-    check(hipEventCreate(&e));
+    check(hipEventCreateWithFlags(&e, hipEventReleaseToDevice));
     c->ev_pool.push_back(e);
   }
   check(hipEventRecord(c->ev_pool[c->ev_used++], c->st));
@@ -382,7 +349,7 @@ void prof_mark(ttt_ctx* c) {
 // the unrounded forward to first order in the rounding error.
 void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   hipStream_t st = c->st;
-  const int prec = c->prec, es = c->es;
+  const int prec = c->prec;
   const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L;
   const int rms = c->cfg.norm == TTT_NORM_RMS;
   const bool gelu = c->cfg.mlp == TTT_MLP_GELU;
@@ -391,7 +358,6 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   const int64_t bd = (int64_t)b * d;
   const int tnm = c->dot_tiles;
 
-  if (L > 0 && gelu) prefetch_fwd(c, c->blocks[0].w1);
   // a1 gather
   RUN(TTT_K_GATHER, run_gather(st, prec, tok, b, V, d, c->E_in, c->H, L == 0 ? c->Yb : nullptr, c->tok_prev,
                                c->tok_tgt, c->err));
@@ -400,12 +366,10 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
     RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
-    prefetch_fwd(c, B.w2);  // for the down-projection
     if (gelu) {
       check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       // Hn^T is read only by the W1 gradient of the backward pass
-      aux_fork(c);
-      check(run_transpose(c->aux, prec, B.Hn, d, b, d, B.HnT, bp));
+      check(run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
       RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
@@ -415,8 +379,6 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
       RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, b, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
                                 foc ? B.ResA : nullptr, m, bp));
     }
-    if (l + 1 < L && gelu) prefetch_fwd(c, c->blocks[l + 1].w1);  // the next up-projection
-    else if (l + 1 == L) prefetch(c, c->E_out, (int64_t)V * d * es);  // the LM head
     const int S = gemm_split_k(prec, b, d, m, bf ? m : 0, SPLIT_MAX);
     check(hipStreamWaitEvent(st, B.w2.ev_upd, 0));  // the previous chunk's step of W2
     GemmSeg2 s2;
@@ -425,32 +387,25 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     RUN(TTT_K_RESIDUAL, run_residual(st, prec, c->H, c->part, S, bd, bd, l == L - 1 ? c->Yb : nullptr));
   }
 
-  // a5 LM head + CE forward (vocab-tiled online softmax, no b x V buffer)
-  if (L > 0) prefetch(c, c->E_outT, (int64_t)V * d * es);  // the dY GEMMs
+  // a5 LM head + CE forward: online softmax over vocabulary records; the numerators are kept
+  // for the backward pass (no logits are recomputed)
   RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, b, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
-                                    c->tgt_logit));
-  RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_tiles, b, c->tgt_logit, c->lse,
+                                    c->tgt_logit, c->ce_nrec, c->P, V));
+  RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_nrec, b, c->tgt_logit, c->lse,
                                    c->losses + tokpos, c->amax + tokpos));
 
   const int64_t chunk_idx = tokpos / b;
   if (L > 0) {
-    prefetch(c, c->blocks[L - 1].w2.Wop, (int64_t)m * d * es);  // the top block's dA
-    // a6 CE backward: dlogits recomputed per vocab super-tile, dY = sum over tiles of P E_out
-    const int S2 = gemm_split_k(prec, b, d, c->vs, 0, SPLIT_MAX);
-    const float inv_b = 1.0f / (float)b;
-    for (int v0 = 0, s = 0; v0 < V; v0 += c->vs, ++s) {
-      const int vn = (V - v0) < c->vs ? (V - v0) : c->vs;
-      RUN(TTT_K_CE_PROB, gemm_ce_prob(st, prec, c->Yb, d, (const char*)c->E_out + (int64_t)v0 * d * es, d, b, vn, d,
-                                      c->tok_tgt, c->lse, c->P, c->vs, v0, inv_b));
-      RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, c->vs, (const char*)c->E_outT + (int64_t)v0 * es, V, b, d, vn, S2,
-                                c->part, d, bd, s > 0));
-    }
+    // a6 CE backward: dlogits in place from the stored numerators, then dY = P E_out over the
+    // whole vocabulary (split-K slabs)
+    RUN(TTT_K_CE_PROB, run_ce_dlogits(st, prec, c->P, b, V, c->ce_w, c->pmax, c->ce_nrec, c->lse, c->tok_tgt,
+                                      1.0f / (float)b));
+    const int S2 = gemm_split_k(prec, b, d, V, 0, SPLIT_MAX);
+    RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, V, c->E_outT, V, b, d, V, S2, c->part, d, bd, 0));
     RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, bd, b, d, c->dH, c->dHb, c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
-    // dH^T (read by the W2 gradient) is made on the aux stream while dA runs
-    aux_fork(c);
-    check(run_transpose(c->aux, prec, c->dHb, d, b, d, c->dHT, bp));
-    aux_mark(c);
+    // dH^T, read by the W2 gradient
+    check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
 
     // a7 block backward, top to bottom
     for (int l = L - 1; l >= 0; --l) {
@@ -458,11 +413,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
       float* cA = foc ? c->cpart + (int64_t)B.cslot * b : nullptr;        // tnm slots
       float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * b : nullptr;  // one slot
       if (gelu) {
-        if (l > 0 || (foc && rms)) prefetch(c, B.w1.Wop, (int64_t)d * m * es);  // for dHn
         RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
                               foc ? B.ResA : nullptr, cA, m, bp));
-        if (l > 0) prefetch(c, c->blocks[l - 1].w2.Wop, (int64_t)m * d * es);  // the next block's dA
-        aux_join(c);  // dH^T, and every H_n^T of the forward pass
         RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
         RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
         // the block input gradient is needed below this block, and for the compensation of
@@ -472,14 +424,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb,
                                            foc ? B.ResN : nullptr, cN, l > 0));
-          if (l > 0) {
-            aux_fork(c);
-            check(run_transpose(c->aux, prec, c->dHb, d, b, d, c->dHT, bp));
-            aux_mark(c);
-          }
+          if (l > 0) check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
         }
       } else {
-        aux_join(c);  // dH^T
         RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
       }
       if (!gelu && foc) {
@@ -554,13 +501,13 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
     check(hipStreamSynchronize(c->st));
   } catch (const HipFail& f) {
     (void)hipStreamSynchronize(c->st);
-    release_side_stream(c);
+    release_aux_stream(c);
     free_all(c);
     delete c;
     return f.s;
   } catch (const std::bad_alloc&) {
     (void)hipStreamSynchronize(c->st);
-    release_side_stream(c);
+    release_aux_stream(c);
     free_all(c);
     delete c;
     return TTT_ENOMEM;
@@ -587,7 +534,6 @@ ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_token
 ttt_status ttt_sync(ttt_ctx* c) {
   if (!c) return TTT_EINVAL;
   try {
-    if (c->pf) check(hipStreamSynchronize(c->pf));
     if (c->aux) check(hipStreamSynchronize(c->aux));
     return read_sticky(c);
   } catch (const HipFail& f) {
@@ -690,7 +636,7 @@ ttt_status ttt_profile_read(ttt_ctx* c, double* total_ms, int64_t* launches) {
 ttt_status ttt_destroy(ttt_ctx* c) {
   if (!c) return TTT_OK;
   (void)hipStreamSynchronize(c->st);
-  release_side_stream(c);
+  release_aux_stream(c);
   for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   free_all(c);
   delete c;
