@@ -1337,9 +1337,16 @@ inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
   const int tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (dma && es == 2) {
     // measured per shape at b = 1024: split-K, the wide-N up / dA GEMMs and the LM head
-    // run best on 256 x 128 tiles (32 x 32 blocks, 3 stages); short-K weight gradients on
-    // 128 x 128 (two per CU)
-    if (splits <= 1 && K + K2 <= 1024) return TilePlan{128, 128, true, 512, 64};
+    // run best on 256 x 128 tiles (32 x 32 blocks, 3 stages). Short-K GEMMs (the weight
+    // gradients) take 128 x 128 tiles (two per CU) or 192 x 192 (one per CU, 32 x 32 blocks),
+    // whichever leaves fewer outputs per CU over its rounds of workgroups.
+    if (splits <= 1 && K + K2 <= 1024) {
+      const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+      const int64_t t192 = (int64_t)((M + 191) / 192) * ((N + 191) / 192);
+      const int64_t load128 = (t128 + 511) / 512 * (2 * 128 * 128), load192 = (t192 + 255) / 256 * (192 * 192);
+      if (load192 < load128) return TilePlan{192, 192, true, 256, 96};
+      return TilePlan{128, 128, true, 512, 64};
+    }
     return TilePlan{256, 128, true, 256, 64};
   }
   TilePlan t{128, 128, dma, 512, 64};  // 4 waves, 2 stages, 2 per CU
@@ -1379,6 +1386,12 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
         g.tiles_n = (N + 127) / 128;
         g.kps = (g.kiters + splits - 1) / splits;
         return launch_dma<T, 256, 128, 4, 2>(st, g, splits, epi);
+      }
+      if (plan.bm == 192) {
+        g.tiles_m = (M + 191) / 192;
+        g.tiles_n = (N + 191) / 192;
+        g.kps = (g.kiters + splits - 1) / splits;
+        return launch_dma<T, 192, 192, 2, 2>(st, g, splits, epi);
       }
     }
     if constexpr (sizeof(T) == 4) {
