@@ -35,6 +35,9 @@ PEAK_HBM = 8.0e12      # MI355X HBM3E, byte/s
 METRIC = "TTT inner-loop tokens/s (fwd+bwd+update) at 1 GPU; % of bf16 MFMA peak"
 
 
+PROFILE_PERIOD = 8
+
+
 def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -191,8 +194,9 @@ def main():
         ctx.prefill(tok)
     torch.cuda.synchronize()
 
-    # timed: exactly `steps` steps; only the dominant kind is bracketed by events
-    ctx.profile([dom])
+    # timed: exactly `steps` steps; only the dominant kind is bracketed by events, in every
+    # PROFILE_PERIOD-th chunk (each event costs a few microseconds of stream time)
+    ctx.profile([dom], period=PROFILE_PERIOD)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

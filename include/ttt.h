@@ -172,6 +172,10 @@ typedef enum {
  * that do not need per-kernel figures. */
 ttt_status ttt_profile_enable(ttt_ctx* ctx, uint32_t mask);
 
+/* Trace only every period-th chunk (period >= 1, default 1), counting from the next chunk;
+ * the other chunks run without events. Returns TTT_EINVAL for period < 1. */
+ttt_status ttt_profile_period(ttt_ctx* ctx, int32_t period);
+
 /* Synchronise, then add the bracketed durations recorded since the last read into
  * total_ms[TTT_K_COUNT] and launches[TTT_K_COUNT] (host arrays, overwritten), and forget them. */
 ttt_status ttt_profile_read(ttt_ctx* ctx, double* total_ms, int64_t* launches);

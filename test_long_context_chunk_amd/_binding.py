@@ -39,6 +39,7 @@ SIGNATURES = {
     "ttt_destroy": (c_int32, [c_void_p]),
     "ttt_status_string": (ctypes.c_char_p, [c_int32]),
     "ttt_profile_enable": (c_int32, [c_void_p, ctypes.c_uint32]),
+    "ttt_profile_period": (c_int32, [c_void_p, c_int32]),
     "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "ttt_test_gemm": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                 c_int32, c_int32, c_int32, c_void_p]),
@@ -210,11 +211,13 @@ class TTT:
                                                0 if kind == "W" else 1, c_void_p(_ptr(out))), "ttt_fast_weights")
         return out
 
-    def profile(self, kinds) -> None:
-        """Bracket launches of the given kernel kinds (names of KERNEL_KINDS) with HIP events."""
+    def profile(self, kinds, period: int = 1) -> None:
+        """Bracket launches of the given kernel kinds (names of KERNEL_KINDS) with HIP events,
+        in every period-th chunk."""
         mask = 0
         for k in kinds:
             mask |= 1 << KERNEL_KINDS.index(k)
+        _check(self._lib.ttt_profile_period(self._ctx, int(period)), "ttt_profile_period")
         _check(self._lib.ttt_profile_enable(self._ctx, mask), "ttt_profile_enable")
 
     def profile_read(self) -> Dict[str, tuple]:

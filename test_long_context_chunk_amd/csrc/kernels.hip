@@ -16,57 +16,240 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// a1: H[t, :] = E_in[x_{t-1}, :] for the b tokens of the chunk ([E2E] eq. 1: f reads
-// x_{t-1}). Ids outside [0, V) raise the sticky range bit and are read as id 0, so no
-// access leaves the table. Also records the clamped conditioning and target ids.
 template <class T>
-__global__ void __launch_bounds__(NT) k_gather(const int* __restrict__ tokens, int V, int d,
-                                               const T* __restrict__ E, float* __restrict__ H,
-                                               T* __restrict__ Yb, int* __restrict__ tok_prev,
-                                               int* __restrict__ tok_tgt, int* __restrict__ err) {
-  const int t = blockIdx.x;
-  int xp = tokens[t], xt = tokens[t + 1];
-  const bool bad = (xp < 0 || xp >= V || xt < 0 || xt >= V);
-  if (xp < 0 || xp >= V) xp = 0;
-  if (xt < 0 || xt >= V) xt = 0;
-  if (threadIdx.x == 0) {
-    tok_prev[t] = xp;
-    tok_tgt[t] = xt;
-    if (bad) atomicOr(err, ERRBIT_RANGE);
-  }
-  const T* src = E + (int64_t)xp * d;
-  float* h = H + (int64_t)t * d;
-  for (int c = threadIdx.x; c < d; c += NT) {
-    const T v = src[c];
-    h[c] = to_f<T>(v);
-    if (Yb) Yb[(int64_t)t * d + c] = v;
-  }
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) { return *(const float4*)p; }
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+template <class T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  *(uint2*)p = make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
 }
 
-// a2: pre-norm of a block. rms: n = h * (mean h^2 + eps)^(-1/2) (no gain); none: n = h.
-// With RES, also the rounding residual n - rn(n) of the stored GEMM operand.
+
+// ---- row kernels: one block per token row; d is a multiple of 8, so every row moves in
+// groups of 4 consecutive elements (16-byte fp32, 8- or 16-byte operand-precision accesses).
+// A thread keeps up to ROW_CACHE of its groups in registers between the two passes over a
+// row (d <= 4 * NT * ROW_CACHE); further groups are read again (the row is L2-resident).
+constexpr int ROW_CACHE = 2;
+
+// The values of v after rounding to the operand precision T.
 template <class T>
-__global__ void __launch_bounds__(NT) k_rmsnorm(const float* __restrict__ H, int d, float eps, int rms,
-                                                T* __restrict__ Hn, float* __restrict__ r, T* __restrict__ RES) {
+__device__ __forceinline__ float4 rounded4(const float4 v) {
+  return make_float4(to_f<T>(from_f<T>(v.x)), to_f<T>(from_f<T>(v.y)), to_f<T>(from_f<T>(v.z)), to_f<T>(from_f<T>(v.w)));
+}
+
+// a1 + a2, a4 + a2: the residual stream entering block l and its pre-norm.
+//   gather (tokens non-null, [E2E] eq. 1: f reads x_{t-1}): h = E_in[x_{t-1}]; ids outside
+//     [0, V) raise the sticky range bit and read row 0; the clamped conditioning and target
+//     ids are recorded;
+//   residual (tokens null): h = H + sum_s part[s] (the down-projection's split-K slabs,
+//     summed in split order first).
+// Stores H = h (fp32) and, when given, Yb = rn(h) (the LM head's operand). When Hn is given,
+// also block l's pre-norm n = h (mean h^2 + eps)^(-1/2) (rms; none: n = h) as rn(n), its
+// scale r, and when RES is given the rounding residual n - rn(n).
+template <class T>
+__global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, int V, const T* __restrict__ E,
+                                               int* __restrict__ tok_prev, int* __restrict__ tok_tgt,
+                                               int* __restrict__ err, const float* __restrict__ part, int S,
+                                               int64_t pstride, float* __restrict__ H, int d, T* __restrict__ Yb,
+                                               float eps, int rms, T* __restrict__ Hn, float* __restrict__ r,
+                                               T* __restrict__ RES) {
   __shared__ float red[4];
   const int t = blockIdx.x;
-  const float* h = H + (int64_t)t * d;
+  const int64_t base = (int64_t)t * d;
+  const T* src = nullptr;
+  if (tokens) {
+    int xp = tokens[t], xt = tokens[t + 1];
+    const bool bad = (xp < 0 || xp >= V || xt < 0 || xt >= V);
+    if (xp < 0 || xp >= V) xp = 0;
+    if (xt < 0 || xt >= V) xt = 0;
+    if (threadIdx.x == 0) {
+      tok_prev[t] = xp;
+      tok_tgt[t] = xt;
+      if (bad) atomicOr(err, ERRBIT_RANGE);
+    }
+    src = E + (int64_t)xp * d;
+  }
+  const int ng = d >> 2;
+  float4 hc[ROW_CACHE];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < ROW_CACHE; ++k) hc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = threadIdx.x, k = 0; g < ng; g += NT, ++k) {
+    const int64_t i = base + (g << 2);
+    float4 h;
+    if (src) {
+      h = load4<T>(src + (g << 2));
+    } else {
+      float4 acc = *(const float4*)(part + i);
+      for (int s = 1; s < S; ++s) {
+        const float4 p = *(const float4*)(part + (int64_t)s * pstride + i);
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
+      }
+      h = *(const float4*)(H + i);
+      h.x += acc.x;
+      h.y += acc.y;
+      h.z += acc.z;
+      h.w += acc.w;
+    }
+    *(float4*)(H + i) = h;
+    if (Yb) store4<T>(Yb + i, h.x, h.y, h.z, h.w);
+    ss += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
+#pragma unroll
+    for (int q = 0; q < ROW_CACHE; ++q)
+      if (q == k) hc[q] = h;
+  }
+  if (!Hn) return;
   float rr = 1.0f;
   if (rms) {
-    float ss = 0.f;
-    for (int c = threadIdx.x; c < d; c += NT) ss += h[c] * h[c];
     ss = block_sum_256(ss, red);
     rr = 1.0f / sqrtf(ss / (float)d + eps);
   }
   if (threadIdx.x == 0) r[t] = rr;
-  T* o = Hn + (int64_t)t * d;
-  for (int c = threadIdx.x; c < d; c += NT) {
-    const float n = h[c] * rr;
-    const T q = from_f<T>(n);
-    o[c] = q;
-    if (RES) RES[(int64_t)t * d + c] = from_f<T>(n - to_f<T>(q));
+  for (int g = threadIdx.x, k = 0; g < ng; g += NT, ++k) {
+    const int64_t i = base + (g << 2);
+    float4 h = hc[0];
+    if (k < ROW_CACHE) {
+#pragma unroll
+      for (int q = 1; q < ROW_CACHE; ++q)
+        if (q == k) h = hc[q];
+    } else {
+      h = *(const float4*)(H + i);  // this thread's own store above
+    }
+    const float4 n = make_float4(h.x * rr, h.y * rr, h.z * rr, h.w * rr);
+    store4<T>(Hn + i, n.x, n.y, n.z, n.w);
+    if (RES) {
+      const float4 q = rounded4<T>(n);
+      store4<T>(RES + i, n.x - q.x, n.y - q.y, n.z - q.z, n.w - q.w);
+    }
   }
 }
+
+// Sum of the S split-K slabs of 4 consecutive elements, in split order.
+__device__ __forceinline__ float4 slab_sum4(const float* __restrict__ part, int S, int64_t pstride, int64_t i) {
+  float4 acc = *(const float4*)(part + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 p = *(const float4*)(part + (int64_t)s * pstride + i);
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  return acc;
+}
+
+// a6 finish: dY = sum_s part[s] (fixed order) into dH and its GEMM-precision copy. With
+// Hres (the fp32 hidden state whose rounded copy Yb fed the LM head), also
+// cdot[t] = <dY_t, H_t - rn(H_t)> for the first-order loss compensation.
+template <class T>
+__global__ void __launch_bounds__(NT) k_dy_finish(const float* __restrict__ part, int S, int64_t pstride, int d,
+                                                  float* __restrict__ dH, T* __restrict__ dHb,
+                                                  const float* __restrict__ Hres, const T* __restrict__ Yb,
+                                                  float* __restrict__ cdot) {
+  __shared__ float red[4];
+  const int64_t base = (int64_t)blockIdx.x * d;
+  float dot = 0.f;
+  for (int g = threadIdx.x; g < (d >> 2); g += NT) {
+    const int64_t i = base + (g << 2);
+    const float4 a = slab_sum4(part, S, pstride, i);
+    *(float4*)(dH + i) = a;
+    store4<T>(dHb + i, a.x, a.y, a.z, a.w);
+    if (cdot) {
+      const float4 h = *(const float4*)(Hres + i), y = load4<T>(Yb + i);
+      dot += a.x * (h.x - y.x) + a.y * (h.y - y.y) + a.z * (h.z - y.z) + a.w * (h.w - y.w);
+    }
+  }
+  if (cdot) {
+    dot = block_sum_256(dot, red);
+    if (threadIdx.x == 0) cdot[blockIdx.x] = dot;
+  }
+}
+
+// a7 norm backward (pre-norm block, through the frozen norm into the residual stream):
+//   dn = sum_s part[s] (= dU W1^T);  rms: dH += r (dn - n mean_j(dn_j n_j));  none: dH += dn.
+// With RES, also cdot[t] = <dn_t, RES_t> (first-order loss compensation of the rounded n);
+// update_dh = 0 computes only that dot (the lowest block, whose input gradient is not needed).
+template <class T>
+__global__ void __launch_bounds__(NT) k_norm_bwd(const float* __restrict__ part, int S, int64_t pstride,
+                                                 const T* __restrict__ Hn, const float* __restrict__ r, int d,
+                                                 int rms, float* __restrict__ dH, T* __restrict__ dHb,
+                                                 const T* __restrict__ RES, float* __restrict__ cdot, int update_dh) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int64_t base = (int64_t)t * d;
+  const int ng = d >> 2;
+  float4 dc[ROW_CACHE];
+#pragma unroll
+  for (int k = 0; k < ROW_CACHE; ++k) dc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float mean = 0.f, rr = 1.f;
+  if (rms || cdot) {
+    float dot = 0.f, cd = 0.f;
+    for (int g = threadIdx.x, k = 0; g < ng; g += NT, ++k) {
+      const int64_t i = base + (g << 2);
+      const float4 dn = slab_sum4(part, S, pstride, i);
+#pragma unroll
+      for (int q = 0; q < ROW_CACHE; ++q)
+        if (q == k) dc[q] = dn;
+      const float4 n = load4<T>(Hn + i);
+      dot += dn.x * n.x + dn.y * n.y + dn.z * n.z + dn.w * n.w;
+      if (cdot) {
+        const float4 e = load4<T>(RES + i);
+        cd += dn.x * e.x + dn.y * e.y + dn.z * e.z + dn.w * e.w;
+      }
+    }
+    if (rms) {
+      dot = block_sum_256(dot, red);
+      mean = dot / (float)d;
+      rr = r[t];
+    }
+    if (cdot) {
+      cd = block_sum_256(cd, red);
+      if (threadIdx.x == 0) cdot[t] = cd;
+    }
+  }
+  if (!update_dh) return;
+  const bool cached = rms || cdot;
+  for (int g = threadIdx.x, k = 0; g < ng; g += NT, ++k) {
+    const int64_t i = base + (g << 2);
+    float4 dn = dc[0];
+    if (cached && k < ROW_CACHE) {
+#pragma unroll
+      for (int q = 1; q < ROW_CACHE; ++q)
+        if (q == k) dn = dc[q];
+    } else {
+      dn = slab_sum4(part, S, pstride, i);
+    }
+    float4 gv = dn;
+    if (rms) {
+      const float4 n = load4<T>(Hn + i);
+      gv = make_float4(rr * (dn.x - n.x * mean), rr * (dn.y - n.y * mean), rr * (dn.z - n.z * mean),
+                       rr * (dn.w - n.w * mean));
+    }
+    float4 v = *(const float4*)(dH + i);
+    v.x += gv.x;
+    v.y += gv.y;
+    v.z += gv.z;
+    v.w += gv.w;
+    *(float4*)(dH + i) = v;
+    store4<T>(dHb + i, v.x, v.y, v.z, v.w);
+  }
+}
+
 
 // dst[c, r] = src[r, c] for r < R, c < C through a 64 x 64 LDS tile. Interior tiles move
 // 16-byte pieces both ways (8 bf16 or 4 fp32 consecutive elements of a source row in, of a
@@ -104,45 +287,6 @@ __global__ void __launch_bounds__(NT) k_transpose(const T* __restrict__ src, int
   }
 }
 
-// a4 residual: H <- H + sum_s part[s] (split-K partials of A W2, summed in split order);
-// optionally also the GEMM-precision copy of the new H.
-template <class T>
-__global__ void __launch_bounds__(NT) k_residual(float* __restrict__ H, const float* __restrict__ part, int S,
-                                                 int64_t pstride, int64_t n, T* __restrict__ Yb) {
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
-    float acc = part[i];
-    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * pstride + i];
-    const float v = H[i] + acc;
-    H[i] = v;
-    if (Yb) Yb[i] = from_f<T>(v);
-  }
-}
-
-// a6 finish, one block per token row: dY = sum_s part[s] (fixed order) into dH and its
-// GEMM-precision copy. With Hres (the fp32 hidden state whose rounded copy Yb fed the LM
-// head), also cdot[t] = <dY_t, H_t - rn(H_t)> for the first-order loss compensation.
-template <class T>
-__global__ void __launch_bounds__(NT) k_dy_finish(const float* __restrict__ part, int S, int64_t pstride, int d,
-                                                  float* __restrict__ dH, T* __restrict__ dHb,
-                                                  const float* __restrict__ Hres, const T* __restrict__ Yb,
-                                                  float* __restrict__ cdot) {
-  __shared__ float red[4];
-  const int t = blockIdx.x;
-  const int64_t base = (int64_t)t * d;
-  float dot = 0.f;
-  for (int c = threadIdx.x; c < d; c += NT) {
-    float acc = part[base + c];
-    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * pstride + base + c];
-    dH[base + c] = acc;
-    dHb[base + c] = from_f<T>(acc);
-    if (cdot) dot += acc * (Hres[base + c] - to_f<T>(Yb[base + c]));
-  }
-  if (cdot) {
-    dot = block_sum_256(dot, red);
-    if (threadIdx.x == 0) cdot[t] = dot;
-  }
-}
-
 // Add the first-order rounding compensation to the recorded losses:
 //   l_t += scale * sum_s cpart[s * b + t]   (fixed order).
 // 16 tokens per block; the 16 threads of a token sum interleaved slots, then combine in a
@@ -164,8 +308,8 @@ __global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ c
   if (threadIdx.x < 16 && t < b) loss[t] += scale * ((red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]));
 }
 
-// a5 merge: combine the per-vocab-tile (max, sum exp, argmax) partials of each row in
-// tile order: lse = M + ln S, l_t = lse - z_t[x_t] ([E2E] eq. 1), argmax (lowest index).
+// a5 merge: combine the (max, sum exp, argmax) records of each row in a fixed order:
+// lse = M + ln S, l_t = lse - z_t[x_t] ([E2E] eq. 1), argmax (lowest index).
 __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax, const float* __restrict__ psum,
                                                  const int* __restrict__ pidx, int nrec, int b,
                                                  const float* __restrict__ tgt_logit, float* __restrict__ lse,
@@ -191,48 +335,6 @@ __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax,
     lse[row] = l;
     loss[row] = l - tgt_logit[row];
     amax[row] = ix;
-  }
-}
-
-// a7 norm backward (pre-norm block, through the frozen norm into the residual stream):
-//   dn = sum_s part[s] (= dU W1^T);  rms: dH += r (dn - n mean_j(dn_j n_j));  none: dH += dn.
-// With RES, also cdot[t] = <dn_t, RES_t> (first-order loss compensation of the rounded n);
-// update_dh = 0 computes only that dot (the lowest block, whose input gradient is not needed).
-template <class T>
-__global__ void __launch_bounds__(NT) k_norm_bwd(const float* __restrict__ part, int S, int64_t pstride,
-                                                 const T* __restrict__ Hn, const float* __restrict__ r, int d,
-                                                 int rms, float* __restrict__ dH, T* __restrict__ dHb,
-                                                 const T* __restrict__ RES, float* __restrict__ cdot, int update_dh) {
-  __shared__ float red[4];
-  const int t = blockIdx.x;
-  const int64_t base = (int64_t)t * d;
-  float mean = 0.f, rr = 1.f;
-  if (rms || cdot) {
-    float dot = 0.f, cd = 0.f;
-    for (int c = threadIdx.x; c < d; c += NT) {
-      float dn = part[base + c];
-      for (int s = 1; s < S; ++s) dn += part[(int64_t)s * pstride + base + c];
-      dot += dn * to_f<T>(Hn[base + c]);
-      if (cdot) cd += dn * to_f<T>(RES[base + c]);
-    }
-    if (rms) {
-      dot = block_sum_256(dot, red);
-      mean = dot / (float)d;
-      rr = r[t];
-    }
-    if (cdot) {
-      cd = block_sum_256(cd, red);
-      if (threadIdx.x == 0) cdot[t] = cd;
-    }
-  }
-  if (!update_dh) return;
-  for (int c = threadIdx.x; c < d; c += NT) {
-    float dn = part[base + c];
-    for (int s = 1; s < S; ++s) dn += part[(int64_t)s * pstride + base + c];
-    const float g = rms ? rr * (dn - to_f<T>(Hn[base + c]) * mean) : dn;
-    const float v = dH[base + c] + g;
-    dH[base + c] = v;
-    dHb[base + c] = from_f<T>(v);
   }
 }
 
@@ -262,33 +364,6 @@ __global__ void __launch_bounds__(NT) k_gradnorm(const float* __restrict__ slot,
   }
 }
 
-// a9: in-place clipped SGD step of one fast tensor [R x C]:
-//   D <- D - lr * s * G;  Wop = rn(W0 + D) row-major (the backward GEMMs' operand);
-//   WtT = transposed copy of rn(D) when delta_t (bf16: the forward GEMMs add X rn(D)^T to
-//   X W0^T, so updates far below W0's rounding step still reach them), else of rn(W0 + D).
-// A block owns a 64 x 64 tile: each thread updates 4 consecutive columns of 4 rows with
-// vector accesses, and the transposed copy leaves through LDS as 16-byte row pieces.
-template <class T>
-__device__ __forceinline__ float4 load4(const T* p);
-template <>
-__device__ __forceinline__ float4 load4<float>(const float* p) { return *(const float4*)p; }
-template <>
-__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
-  const uint2 u = *(const uint2*)p;
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                     __uint_as_float(u.y & 0xffff0000u));
-}
-template <class T>
-__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
-  *(float4*)p = make_float4(a, b, c, d);
-}
-template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
-  *(uint2*)p = make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
-}
-
 // a6 dlogits of the whole vocabulary, in place ([E2E] eq. 5 through the softmax
 // cross-entropy): Q holds exp(z - m) with m the max of the record (W consecutive vocabulary
 // entries) the column belongs to, so softmax = Q exp(m - lse) and
@@ -316,6 +391,12 @@ __global__ void __launch_bounds__(NT) k_ce_dlogits(T* __restrict__ Q, int b, int
   }
 }
 
+// a9: in-place clipped SGD step of one fast tensor [R x C]:
+//   D <- D - lr * s * G;  Wop = rn(W0 + D) row-major (the backward GEMMs' operand);
+//   WtT = transposed copy of rn(D) when delta_t (bf16: the forward GEMMs add X rn(D)^T to
+//   X W0^T, so updates far below W0's rounding step still reach them), else of rn(W0 + D).
+// A block owns a 64 x 64 tile: each thread updates 4 consecutive columns of 4 rows with
+// vector accesses, and the transposed copy leaves through LDS as 16-byte row pieces.
 template <class T>
 __global__ void __launch_bounds__(NT) k_update(const T* __restrict__ G, float* __restrict__ D,
                                                const T* __restrict__ W0, T* __restrict__ Wop,
@@ -403,16 +484,12 @@ inline int grid_for(int64_t n) {
     }                                         \
   } while (0)
 
-hipError_t run_gather(hipStream_t st, int prec, const int* tokens, int b, int V, int d, const void* E, float* H,
-                      void* Yb, int* tok_prev, int* tok_tgt, int* err) {
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_gather<T>, dim3(b), dim3(NT), 0, st, tokens, V, d, (const T*)E, H, (T*)Yb,
-                                      tok_prev, tok_tgt, err));
-  return hipGetLastError();
-}
-
-hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r,
-                       void* RES) {
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_rmsnorm<T>, dim3(b), dim3(NT), 0, st, H, d, eps, rms, (T*)Hn, r, (T*)RES));
+hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, int V, const void* E, int* tok_prev, int* tok_tgt,
+                      int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb, float eps,
+                      int rms, void* Hn, float* r, void* RES) {
+  if (d % 8) return hipErrorInvalidValue;
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_row_in<T>, dim3(b), dim3(NT), 0, st, tokens, V, (const T*)E, tok_prev, tok_tgt,
+                                      err, part, S, pstride, H, d, (T*)Yb, eps, rms, (T*)Hn, r, (T*)RES));
   return hipGetLastError();
 }
 
@@ -420,13 +497,6 @@ hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds,
   if (R <= 0 || C <= 0) return hipSuccess;
   dim3 grid((C + 63) / 64, (R + 63) / 64);
   DISPATCH_T(prec, hipLaunchKernelGGL(k_transpose<T>, grid, dim3(NT), 0, st, (const T*)src, lds, R, C, (T*)dst, ldd));
-  return hipGetLastError();
-}
-
-hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, int S, int64_t pstride, int64_t n,
-                        void* Yb) {
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_residual<T>, dim3(grid_for(n)), dim3(NT), 0, st, H, part, S, pstride, n,
-                                      (T*)Yb));
   return hipGetLastError();
 }
 

@@ -9,13 +9,12 @@
 enum { PREC_FP32 = 0, PREC_BF16 = 1 };
 
 // ---- row / elementwise kernels (kernels.hip)
-hipError_t run_gather(hipStream_t st, int prec, const int* tokens, int b, int V, int d, const void* E, float* H,
-                      void* Yb, int* tok_prev, int* tok_tgt, int* err);
-hipError_t run_rmsnorm(hipStream_t st, int prec, const float* H, int b, int d, float eps, int rms, void* Hn, float* r,
-                       void* RES);
+// The residual stream entering a block (gather of the embeddings when tokens is non-null,
+// else H + the split-K slabs part) and, when Hn is non-null, its pre-norm (see k_row_in).
+hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, int V, const void* E, int* tok_prev, int* tok_tgt,
+                      int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb, float eps,
+                      int rms, void* Hn, float* r, void* RES);
 hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds, int R, int C, void* dst, int64_t ldd);
-hipError_t run_residual(hipStream_t st, int prec, float* H, const float* part, int S, int64_t pstride, int64_t n,
-                        void* Yb);
 hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int b, int d,
                          float* dH, void* dHb, const float* Hres, const void* Yb, float* cdot);
 hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss);

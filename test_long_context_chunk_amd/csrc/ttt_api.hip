@@ -96,6 +96,9 @@ struct ttt_ctx {
 
   // tracing: event pairs around launches of the kinds set in prof_mask
   uint32_t prof_mask = 0;
+  int prof_period = 1;      // trace every prof_period-th chunk
+  int64_t prof_chunks = 0;  // chunks run since tracing was configured
+  bool prof_on = false;     // the current chunk is traced
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
   std::vector<int> ev_kind;
@@ -330,7 +333,7 @@ void prof_mark(ttt_ctx* c) {
 // Enqueue one launch; bracket it with events when its kind is traced.
 #define RUN(kind, expr)                         \
   do {                                          \
-    const bool traced_ = (c->prof_mask >> (kind)) & 1u; \
+    const bool traced_ = c->prof_on && ((c->prof_mask >> (kind)) & 1u); \
     if (traced_) prof_mark(c);                  \
     check(expr);                                \
     if (traced_) {                              \
@@ -349,6 +352,7 @@ void prof_mark(ttt_ctx* c) {
 // the unrounded forward to first order in the rounding error.
 void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   hipStream_t st = c->st;
+  c->prof_on = c->prof_mask != 0 && (c->prof_chunks++ % c->prof_period) == 0;
   const int prec = c->prec;
   const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L;
   const int rms = c->cfg.norm == TTT_NORM_RMS;
@@ -358,14 +362,17 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   const int64_t bd = (int64_t)b * d;
   const int tnm = c->dot_tiles;
 
-  // a1 gather
-  RUN(TTT_K_GATHER, run_gather(st, prec, tok, b, V, d, c->E_in, c->H, L == 0 ? c->Yb : nullptr, c->tok_prev,
-                               c->tok_tgt, c->err));
+  // a1 gather, and a2 the lowest block's pre-norm
+  {
+    Block* B0 = L > 0 ? &c->blocks[0] : nullptr;
+    RUN(TTT_K_GATHER, run_row_in(st, prec, tok, V, c->E_in, c->tok_prev, c->tok_tgt, c->err, nullptr, 0, 0, c->H, b, d,
+                                 L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, B0 ? B0->Hn : nullptr,
+                                 B0 ? B0->r : nullptr, B0 && foc ? B0->ResN : nullptr));
+  }
 
   // a2-a4 forward through the blocks
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
-    RUN(TTT_K_NORM, run_rmsnorm(st, prec, c->H, b, d, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
     if (gelu) {
       check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       // Hn^T is read only by the W1 gradient of the backward pass
@@ -384,7 +391,11 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     GemmSeg2 s2;
     if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
     RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, bd, 0, s2));
-    RUN(TTT_K_RESIDUAL, run_residual(st, prec, c->H, c->part, S, bd, bd, l == L - 1 ? c->Yb : nullptr));
+    // a4 residual, and a2 the next block's pre-norm
+    Block* Bn = l + 1 < L ? &c->blocks[l + 1] : nullptr;
+    RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, V, nullptr, nullptr, nullptr, nullptr, c->part, S, bd, c->H, b, d,
+                                   l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, Bn ? Bn->Hn : nullptr,
+                                   Bn ? Bn->r : nullptr, Bn && foc ? Bn->ResN : nullptr));
   }
 
   // a5 LM head + CE forward: online softmax over vocabulary records; the numerators are kept
@@ -608,6 +619,14 @@ int64_t ttt_tokens_consumed(const ttt_ctx* c) { return c ? c->pos : -1; }
 ttt_status ttt_profile_enable(ttt_ctx* c, uint32_t mask) {
   if (!c || (mask >> TTT_K_COUNT) != 0) return TTT_EINVAL;
   c->prof_mask = mask;
+  c->prof_chunks = 0;
+  return TTT_OK;
+}
+
+ttt_status ttt_profile_period(ttt_ctx* c, int32_t period) {
+  if (!c || period < 1) return TTT_EINVAL;
+  c->prof_period = period;
+  c->prof_chunks = 0;
   return TTT_OK;
 }
 
