@@ -374,9 +374,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
     if (gelu) {
-      check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       // Hn^T is read only by the W1 gradient of the backward pass
       check(run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
+      check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
       RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
