@@ -113,6 +113,29 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
  * Errors (nothing enqueued): TTT_EINVAL, TTT_ESTATE. */
 ttt_status ttt_prefill_chunks(ttt_ctx* ctx, const int32_t* tokens, int64_t n_tokens);
 
+/* Decode n tokens one at a time ([E2E] Method: decoding predicts the next token's
+ * distribution from the current weights; section 3.2: a gradient step is taken only when
+ * the decoded tokens fill a mini-batch, and decoding continues with the updated weights).
+ * tokens: device int32 [n + 1]; tokens[0] is the stream's last token so far (the last id of
+ *         the previous prefill or decode call, BOS if nothing came before); for i in [0, n),
+ *         prediction i is f(tokens[i]; W) at the current fast weights and scores tokens[i + 1].
+ *         Borrowed until the stream passes this call.
+ * For every prediction, the loss and argmax are recorded at the next token position (read
+ * back with ttt_token_losses / ttt_token_argmax, like prefilled tokens); argmax (device int32
+ * [n]) and logits (device fp32 [n x vocab], row i = prediction i) receive them too when
+ * non-NULL. Each time b decoded pairs complete a chunk, that chunk takes the same step as in
+ * ttt_prefill_chunks (which also re-records its losses, then with the bf16 loss compensation)
+ * before the next prediction. Decoded pairs that do not yet fill a chunk stay pending across
+ * calls (ttt_decode_pending); ttt_prefill_chunks is refused (TTT_EINVAL) while any are.
+ * Predictions use fp32 activations against the stored fast weights (bf16: W0 and rn(D) as two
+ * segments, as in the forward GEMMs), so their losses carry no operand rounding. Ids out of
+ * range raise the sticky TTT_ERANGE and read id 0. n = 0 is a no-op.
+ * Errors (nothing enqueued): TTT_EINVAL (n < 0, NULL tokens, capacity), TTT_ESTATE. */
+ttt_status ttt_decode(ttt_ctx* ctx, const int32_t* tokens, int64_t n, int32_t* argmax, float* logits);
+
+/* Decoded pairs waiting for their chunk to fill (0 .. chunk - 1; -1 for NULL). */
+int64_t ttt_decode_pending(const ttt_ctx* ctx);
+
 /* Copy the recorded losses l_t(W_{i-1}) of tokens [offset, offset + n) (counted from the
  * first token of the first prefill since creation or reset) into dst (device fp32 [n]).
  * Synchronises the context's stream; returns a pending sticky error if there is one

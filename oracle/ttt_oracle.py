@@ -303,6 +303,60 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
                      D, Wf)
 
 
+def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logit_probe=None) -> TTTResult:
+    """Token-by-token decoding with test-time training, [E2E] Method and section 3.2.
+
+    tokens = x_0..x_T (any T >= 0). Decoding predicts the next token's distribution from
+    the last token at the current weights (Method: p^_{t+1} = f(x_t; W)), and takes a
+    gradient step only when the decoded tokens fill a mini-batch of b; decoding then goes on
+    with the updated weights (section 3.2). So token t is scored at the weights left by the
+    last completed chunk before it, and a trailing partial chunk takes no step. The step is
+    the clipped mini-batch step of [E2E] eq. (5) / [SGF]. logit_probe(t - 1, z), when given,
+    sees the logits row that scored token t.
+    """
+    P0 = as_f64(P0)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    b = model.chunk
+    T = tokens.shape[0] - 1
+    keys = model.fast_keys()
+    D = {k: np.zeros_like(P0[k]) for k in keys}
+    losses, argm, marg = [], [], []
+    gn, sc, sk = [], [], []
+    start = 0  # the pending mini-batch starts with the pair (x_start, x_start+1)
+    for t in range(1, T + 1):
+        P = dict(P0)
+        for k in keys:
+            P[k] = P0[k] + D[k]
+        z, _, _ = logits(model, P, tokens[t - 1:t])
+        if logit_probe is not None:
+            logit_probe(t - 1, z[0])
+        l, _, am, mg = ce_stats(z, tokens[t:t + 1])
+        losses.append(l[0])
+        argm.append(am[0])
+        marg.append(mg[0])
+        if t - start == b:
+            # the decoded tokens fill a mini-batch: one clipped step on it, at the weights
+            # that scored it
+            _, _, G = chunk_loss_and_grads(model, P, tokens[start:t], tokens[start + 1:t + 1])
+            g = math.sqrt(sum(float(np.sum(G[k] * G[k])) for k in keys))
+            if math.isfinite(g):
+                s = clip_scale(g, model.clip)
+                for k in keys:
+                    D[k] = D[k] - model.lr * s * G[k]
+                gn.append(g)
+                sc.append(s)
+                sk.append(False)
+            else:
+                gn.append(g)
+                sc.append(0.0)
+                sk.append(True)
+            start = t
+    Wf = {k: P0[k] + D[k] for k in keys}
+    return TTTResult(np.asarray(losses, dtype=np.float64), np.asarray(argm, dtype=np.int64),
+                     np.asarray(marg, dtype=np.float64), np.asarray(gn), np.asarray(sc),
+                     np.asarray(sk, dtype=bool), D, Wf)
+
+
 def static_losses(model: Model, P0, tokens, n_tokens: Optional[int] = None) -> np.ndarray:
     """l_t(W_0) for every t: the summands of L_naive, [E2E] eq. (4)."""
     P0 = as_f64(P0)

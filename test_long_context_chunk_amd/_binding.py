@@ -38,6 +38,8 @@ SIGNATURES = {
     "ttt_tokens_consumed": (c_int64, [c_void_p]),
     "ttt_destroy": (c_int32, [c_void_p]),
     "ttt_status_string": (ctypes.c_char_p, [c_int32]),
+    "ttt_decode": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
+    "ttt_decode_pending": (c_int64, [c_void_p]),
     "ttt_profile_enable": (c_int32, [c_void_p, ctypes.c_uint32]),
     "ttt_profile_period": (c_int32, [c_void_p, c_int32]),
     "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
@@ -180,6 +182,23 @@ class TTT:
             raise ValueError("tokens must be a contiguous int32 device tensor")
         n = tokens.numel() - 1
         _check(self._lib.ttt_prefill_chunks(self._ctx, c_void_p(_ptr(tokens)), n), "ttt_prefill_chunks")
+
+    def decode(self, tokens, want_logits: bool = False):
+        """tokens: device int32 [n + 1] (tokens[0] = the stream's last token). Predicts each of
+        tokens[1..n] from the one before at the current weights, stepping whenever a chunk fills.
+        Returns (argmax int32 [n], logits fp32 [n x vocab] or None)."""
+        import torch
+        if tokens.dtype != torch.int32 or not tokens.is_cuda or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 device tensor")
+        n = tokens.numel() - 1
+        am = torch.empty(max(n, 0), dtype=torch.int32, device="cuda")
+        z = torch.empty((max(n, 0), self.vocab), dtype=torch.float32, device="cuda") if want_logits else None
+        _check(self._lib.ttt_decode(self._ctx, c_void_p(_ptr(tokens)), n, c_void_p(_ptr(am) if n > 0 else None),
+                                    c_void_p(_ptr(z)) if (z is not None and n > 0) else None), "ttt_decode")
+        return am, z
+
+    def decode_pending(self) -> int:
+        return int(self._lib.ttt_decode_pending(self._ctx))
 
     def token_losses(self, offset: int = 0, n: Optional[int] = None):
         import torch

@@ -391,6 +391,173 @@ __global__ void __launch_bounds__(NT) k_ce_dlogits(T* __restrict__ Q, int b, int
   }
 }
 
+// ---- decode ([E2E] Method: decoding predicts p^_{t+1} = f(x_t; W); section 3.2: a step only
+// when the decoded tokens fill a mini-batch). One activation row per launch; activations stay
+// in fp32 (the fast weights are the stored bf16 segments), so no operand rounding enters.
+
+// Block input of the decoded token: with tok (the pair x_{t-1}, x_t in the caller's ids),
+// h = E_in[x_{t-1}] into H and the pair copied into the pending-chunk ids pend[0..1] (pend[0]
+// only when first is set); without tok, h = H (already updated in place). Then the pre-norm
+// n = h (mean h^2 + eps)^(-1/2) (rms; none: n = h) into nout (fp32), when given. One block.
+template <class T>
+__global__ void __launch_bounds__(NT) k_dec_row(const int* __restrict__ tok, int first, int* __restrict__ pend,
+                                                int V, const T* __restrict__ E, float* __restrict__ H, int d,
+                                                float eps, int rms, float* __restrict__ nout, int* __restrict__ err) {
+  __shared__ float red[4];
+  const T* src = nullptr;
+  if (tok) {
+    int xp = tok[0];
+    const int xt = tok[1];
+    if (threadIdx.x == 0) {
+      if (first) pend[0] = xp;
+      pend[1] = xt;
+      if (xp < 0 || xp >= V || xt < 0 || xt >= V) atomicOr(err, ERRBIT_RANGE);
+    }
+    if (xp < 0 || xp >= V) xp = 0;
+    src = E + (int64_t)xp * d;
+  }
+  float ss = 0.f;
+  for (int g = threadIdx.x; g < (d >> 2); g += NT) {
+    const int c = g << 2;
+    float4 h;
+    if (src) {
+      h = load4<T>(src + c);
+      *(float4*)(H + c) = h;
+    } else {
+      h = *(const float4*)(H + c);
+    }
+    ss += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
+  }
+  if (!nout) return;
+  float rr = 1.0f;
+  if (rms) {
+    ss = block_sum_256(ss, red);
+    rr = 1.0f / sqrtf(ss / (float)d + eps);
+  }
+  for (int g = threadIdx.x; g < (d >> 2); g += NT) {
+    const int c = g << 2;
+    const float4 h = *(const float4*)(H + c);
+    *(float4*)(nout + c) = make_float4(h.x * rr, h.y * rr, h.z * rr, h.w * rr);
+  }
+}
+
+// Dot of 8 consecutive operand-precision weights with 8 fp32 activations.
+__device__ __forceinline__ float dot8(const bf16_t* w, const float* x) {
+  const uint4 u = *(const uint4*)w;
+  const float4 x0 = *(const float4*)x, x1 = *(const float4*)(x + 4);
+  float s = __uint_as_float(u.x << 16) * x0.x;
+  s = fmaf(__uint_as_float(u.x & 0xffff0000u), x0.y, s);
+  s = fmaf(__uint_as_float(u.y << 16), x0.z, s);
+  s = fmaf(__uint_as_float(u.y & 0xffff0000u), x0.w, s);
+  s = fmaf(__uint_as_float(u.z << 16), x1.x, s);
+  s = fmaf(__uint_as_float(u.z & 0xffff0000u), x1.y, s);
+  s = fmaf(__uint_as_float(u.w << 16), x1.z, s);
+  return fmaf(__uint_as_float(u.w & 0xffff0000u), x1.w, s);
+}
+__device__ __forceinline__ float dot8(const float* w, const float* x) {
+  const float4 w0 = *(const float4*)w, w1 = *(const float4*)(w + 4);
+  const float4 x0 = *(const float4*)x, x1 = *(const float4*)(x + 4);
+  float s = w0.x * x0.x;
+  s = fmaf(w0.y, x0.y, s);
+  s = fmaf(w0.z, x0.z, s);
+  s = fmaf(w0.w, x0.w, s);
+  s = fmaf(w1.x, x1.x, s);
+  s = fmaf(w1.y, x1.y, s);
+  s = fmaf(w1.z, x1.z, s);
+  return fmaf(w1.w, x1.w, s);
+}
+
+// Decode product of one activation row x [K] (fp32) with the rows of Y [N x K] (row stride
+// ldy, operand precision): one wave per output, 16-byte weight loads, x staged in LDS.
+//   STORE:    out[n] = x.Y[n] (+ x.Y2[n], the second K-segment when Y2 is given)
+//   GELU:     out[n] = GELU(x.Y[n] (+ x.Y2[n]))
+//   RESIDUAL: out[n] += x.Y[n] (+ x.Y2[n])
+//   SWIGLU:   out[n] = SiLU(x.Y[n]) * x.Y2[n] (Y the gate, Y2 the up projection)
+// Each wave handles RPW consecutive rows, reading them interleaved.
+template <class T, int MODE, int RPW>
+__global__ void __launch_bounds__(NT) k_gemv(const float* __restrict__ x, int K, const T* __restrict__ Y,
+                                             const T* __restrict__ Y2, int64_t ldy, int N, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  for (int g = threadIdx.x; g < (K >> 2); g += NT) *(float4*)(xs + 4 * g) = *(const float4*)(x + 4 * g);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * RPW;
+  float s1[RPW], s2[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) s1[r] = s2[r] = 0.f;
+  const bool two = Y2 != nullptr;
+#pragma unroll 2
+  for (int k = lane * 8; k < K; k += 512) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int n = min(n0 + r, N - 1);
+      s1[r] += dot8(Y + (int64_t)n * ldy + k, xs + k);
+      if (two) s2[r] += dot8(Y2 + (int64_t)n * ldy + k, xs + k);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = n0 + r;
+    const float a = wave_sum(s1[r]), b = wave_sum(s2[r]);
+    if (lane != 0 || n >= N) continue;
+    if constexpr (MODE == GEMV_STORE) out[n] = a + b;
+    if constexpr (MODE == GEMV_GELU) out[n] = gelu_f(a + b);
+    if constexpr (MODE == GEMV_RESIDUAL) out[n] += a + b;
+    if constexpr (MODE == GEMV_SWIGLU) out[n] = silu_f(a) * b;
+  }
+}
+
+// Decode CE of one logits row z [V] (fp32): lse, first argmax, loss = lse - z[target]
+// (target = pend[0], clamped like the gather). Writes the token's loss and argmax records and,
+// when given, argmax_out. One block of NT threads, fixed partition and order.
+__global__ void __launch_bounds__(NT) k_dec_ce(const float* __restrict__ z, int V, const int* __restrict__ pend,
+                                               float* __restrict__ loss, int* __restrict__ amax,
+                                               int* __restrict__ argmax_out) {
+  __shared__ float smx[NT];
+  __shared__ int six[NT];
+  __shared__ float ssm[NT];
+  float mx = -INFINITY;
+  int ix = 0x7fffffff;
+  for (int v = threadIdx.x; v < V; v += NT) {
+    const float zv = z[v];
+    if (zv > mx) {
+      mx = zv;
+      ix = v;
+    }
+  }
+  smx[threadIdx.x] = mx;
+  six[threadIdx.x] = ix;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      const float om = smx[threadIdx.x + s];
+      const int oi = six[threadIdx.x + s];
+      if (om > smx[threadIdx.x] || (om == smx[threadIdx.x] && oi < six[threadIdx.x])) {
+        smx[threadIdx.x] = om;
+        six[threadIdx.x] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  const float M = smx[0];
+  float sm = 0.f;
+  for (int v = threadIdx.x; v < V; v += NT) sm += expf(z[v] - M);
+  ssm[threadIdx.x] = sm;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) ssm[threadIdx.x] += ssm[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int tg = pend[0];
+    if (tg < 0 || tg >= V) tg = 0;
+    const float lse = M + logf(ssm[0]);
+    loss[0] = lse - z[tg];
+    amax[0] = six[0];
+    if (argmax_out) argmax_out[0] = six[0];
+  }
+}
+
 // a9: in-place clipped SGD step of one fast tensor [R x C]:
 //   D <- D - lr * s * G;  Wop = rn(W0 + D) row-major (the backward GEMMs' operand);
 //   WtT = transposed copy of rn(D) when delta_t (bf16: the forward GEMMs add X rn(D)^T to
@@ -550,6 +717,45 @@ hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const v
 
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst) {
   DISPATCH_T(prec, hipLaunchKernelGGL(k_export<T>, dim3(grid_for(n)), dim3(NT), 0, st, D, (const T*)W0, n, kind, dst));
+  return hipGetLastError();
+}
+
+hipError_t run_dec_row(hipStream_t st, int prec, const int* tok, int first, int* pend, int V, const void* E, float* H,
+                       int d, float eps, int rms, float* nout, int* err) {
+  if (d % 8) return hipErrorInvalidValue;
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_dec_row<T>, dim3(1), dim3(NT), 0, st, tok, first, pend, V, (const T*)E, H, d,
+                                      eps, rms, nout, err));
+  return hipGetLastError();
+}
+
+template <class T, int MODE>
+static hipError_t launch_gemv(hipStream_t st, const float* x, int K, const T* Y, const T* Y2, int64_t ldy, int N,
+                              float* out) {
+  const size_t lds = (size_t)K * sizeof(float);
+  if (N >= 16384) {
+    hipLaunchKernelGGL((k_gemv<T, MODE, 4>), dim3((N + 15) / 16), dim3(NT), lds, st, x, K, Y, Y2, ldy, N, out);
+  } else {
+    hipLaunchKernelGGL((k_gemv<T, MODE, 1>), dim3((N + 3) / 4), dim3(NT), lds, st, x, K, Y, Y2, ldy, N, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_gemv(hipStream_t st, int prec, int mode, const float* x, int K, const void* Y, const void* Y2,
+                    int64_t ldy, int N, float* out) {
+  if (K % 8 || ldy % 8 || N <= 0 || (size_t)K * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
+  DISPATCH_T(prec, {
+    switch (mode) {
+      case GEMV_STORE: return launch_gemv<T, GEMV_STORE>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_GELU: return launch_gemv<T, GEMV_GELU>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_RESIDUAL: return launch_gemv<T, GEMV_RESIDUAL>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_SWIGLU: return launch_gemv<T, GEMV_SWIGLU>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      default: return hipErrorInvalidValue;
+    }
+  });
+}
+
+hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const int* tgt, float* loss, int* amax, int* argmax_out) {
+  hipLaunchKernelGGL(k_dec_ce, dim3(1), dim3(NT), 0, st, z, V, tgt, loss, amax, argmax_out);
   return hipGetLastError();
 }
 

@@ -68,6 +68,11 @@ struct ttt_ctx {
   int ce_nrec = 0;  // CE records per row: ceil(V / ce_w)
   int dot_tiles = 0;  // column tiles of the dA GEMM (one partial dot per tile and row)
   void* P = nullptr;
+  // decode: ids of the pending (not yet stepped) chunk [b + 1], how many of its pairs are
+  // filled, and the one-row fp32 activations
+  int* dec_tok = nullptr;
+  int npend = 0;
+  float *dec_h = nullptr, *dec_n = nullptr, *dec_a = nullptr, *dec_z = nullptr;
   float* part = nullptr;
   float* dH = nullptr;
   void *dHb = nullptr, *dHT = nullptr, *A = nullptr, *dU = nullptr, *dUT = nullptr;
@@ -268,6 +273,11 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->lse = dalloc<float>(c, (int64_t)b * 4);
   if (L > 0) c->P = dalloc<char>(c, (int64_t)b * V * es);  // softmax numerators, then dlogits
   c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * b * d * 4);
+  c->dec_tok = dalloc<int>(c, (int64_t)(b + 1) * 4);
+  c->dec_h = dalloc<float>(c, (int64_t)d * 4);
+  c->dec_n = dalloc<float>(c, (int64_t)d * 4);
+  c->dec_a = dalloc<float>(c, (int64_t)m * 4);
+  c->dec_z = dalloc<float>(c, (int64_t)V * 4);
   c->dH = dalloc<float>(c, (int64_t)b * d * 4);
   c->dHb = dalloc<char>(c, (int64_t)b * d * es);
   c->dHT = dalloc<char>(c, (int64_t)d * bp * es);
@@ -473,6 +483,37 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   }
 }
 
+// Decode of one token ([E2E] Method, decoding; section 3.2): the pair (tok[0], tok[1]) joins
+// the pending chunk, and f(tok[0]; W) at the current weights gives the logits of tok[1]'s
+// position, its loss and argmax (recorded at c->pos, like a prefilled token's). The fast
+// weights are read exactly as the forward GEMMs read them (bf16: W0 and rn(D) as two
+// segments); activations stay in fp32.
+void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out) {
+  hipStream_t st = c->st;
+  const int prec = c->prec;
+  const int V = c->V, d = c->d, m = c->m, L = c->L;
+  const int rms = c->cfg.norm == TTT_NORM_RMS;
+  const bool gelu = c->cfg.mlp == TTT_MLP_GELU;
+  const bool bf = prec == PREC_BF16;
+  const float eps = c->cfg.rms_eps;
+  float* z = z_out ? z_out : c->dec_z;
+  check(run_dec_row(st, prec, tok, c->npend == 0, c->dec_tok + c->npend, V, c->E_in, c->dec_h, d, eps, rms,
+                    L > 0 ? c->dec_n : nullptr, c->err));
+  for (int l = 0; l < L; ++l) {
+    Block& B = c->blocks[l];
+    if (gelu)
+      check(run_gemv(st, prec, GEMV_GELU, c->dec_n, d, bf ? B.w1.W0T : B.w1.WtT, bf ? B.w1.WtT : nullptr, d, m,
+                     c->dec_a));
+    else
+      check(run_gemv(st, prec, GEMV_SWIGLU, c->dec_n, d, B.WgT, B.WuT, d, m, c->dec_a));
+    check(run_gemv(st, prec, GEMV_RESIDUAL, c->dec_a, m, bf ? B.w2.W0T : B.w2.WtT, bf ? B.w2.WtT : nullptr, m, d,
+                   c->dec_h));
+    if (l + 1 < L) check(run_dec_row(st, prec, nullptr, 0, nullptr, V, nullptr, c->dec_h, d, eps, rms, c->dec_n, c->err));
+  }
+  check(run_gemv(st, prec, GEMV_STORE, c->dec_h, d, c->E_out, nullptr, d, V, z));
+  check(run_dec_ce(st, z, V, c->dec_tok + c->npend + 1, c->losses + c->pos, c->amax + c->pos, am_out));
+}
+
 ttt_status read_sticky(ttt_ctx* c) {
   int e = 0;
   check(hipMemcpyAsync(&e, c->err, 4, hipMemcpyDeviceToHost, c->st));
@@ -530,7 +571,7 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
 ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_tokens) {
   if (!c || !tokens) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
-  if (n_tokens <= 0 || n_tokens % c->b) return TTT_EINVAL;
+  if (n_tokens <= 0 || n_tokens % c->b || c->npend != 0) return TTT_EINVAL;
   if (c->pos + n_tokens > c->cfg.max_tokens) return TTT_EINVAL;
   try {
     for (int64_t i = 0; i < n_tokens; i += c->b) run_chunk(c, tokens + i, c->pos + i);
@@ -541,6 +582,32 @@ ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_token
   c->pos += n_tokens;
   return TTT_OK;
 }
+
+ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* argmax, float* logits) {
+  if (!c || !tokens || n < 0) return TTT_EINVAL;
+  if (c->sticky != TTT_OK) return TTT_ESTATE;
+  if (c->pos + n > c->cfg.max_tokens) return TTT_EINVAL;
+  if (n == 0) return TTT_OK;
+  try {
+    aux_join(c);  // a step still in flight on the aux stream lands before these predictions
+    for (int64_t i = 0; i < n; ++i) {
+      decode_token(c, tokens + i, argmax ? argmax + i : nullptr, logits ? logits + i * (int64_t)c->V : nullptr);
+      c->pos += 1;
+      if (++c->npend == c->b) {
+        // the decoded tokens fill a mini-batch: its step, as in prefill ([E2E] section 3.2)
+        run_chunk(c, c->dec_tok, c->pos - c->b);
+        c->npend = 0;
+        aux_join(c);
+      }
+    }
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  return TTT_OK;
+}
+
+int64_t ttt_decode_pending(const ttt_ctx* c) { return c ? c->npend : -1; }
 
 ttt_status ttt_sync(ttt_ctx* c) {
   if (!c) return TTT_EINVAL;
@@ -610,6 +677,7 @@ ttt_status ttt_reset(ttt_ctx* c) {
     return f.s;
   }
   c->pos = 0;
+  c->npend = 0;
   c->sticky = TTT_OK;
   return TTT_OK;
 }

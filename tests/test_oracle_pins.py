@@ -336,6 +336,68 @@ def test_pins_catch_off_by_one_target():
     assert abs(slip[0] - good[0]) > 1.0
 
 
+# ------------------------------------------------------------------ P11/P12 decoding
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+@pytest.mark.parametrize("clip", [0.0, 0.05])
+def test_p11_decoding_full_chunks_equals_prefill(mlp, norm, clip):
+    """[E2E] section 3.2: prefilled tokens are consumed in T/b mini-batches, and decoded tokens
+    take a step each time they fill one, so decoding a stream of whole chunks token by token
+    scores every token at the same weights and ends at the same weights as the chunked loop."""
+    model = tiny_model(mlp, norm, L=2, b=3, lr=0.3, clip=clip)
+    P = tiny_params(model, seed=21)
+    x = tiny_tokens(model, 12, seed=22)
+    pre = O.run_ttt(model, P, x)
+    dec = O.decode_ttt(model, P, x)
+    np.testing.assert_allclose(dec.losses, pre.losses, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(dec.argmax, pre.argmax)
+    np.testing.assert_allclose(dec.grad_norm, pre.grad_norm, rtol=1e-12)
+    np.testing.assert_allclose(dec.scale, pre.scale, rtol=1e-12)
+    for k in model.fast_keys():
+        np.testing.assert_allclose(dec.weights[k], pre.weights[k], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("mlp,norm", [("gelu", "rms"), ("swiglu_w2", "none")])
+def test_p12_partial_chunk_takes_no_step(mlp, norm):
+    """Decoded tokens that do not fill a mini-batch are scored at the last chunk's weights and
+    leave the weights alone (section 3.2: the step waits for a full mini-batch)."""
+    model = tiny_model(mlp, norm, L=2, b=4, lr=0.3, clip=0.0)
+    P = tiny_params(model, seed=23)
+    x = tiny_tokens(model, 11, seed=24)  # two full chunks, then 3 decoded tokens
+    dec = O.decode_ttt(model, P, x)
+    pre = O.run_ttt(model, P, x[:9])
+    assert len(dec.grad_norm) == 2
+    for k in model.fast_keys():
+        np.testing.assert_allclose(dec.weights[k], pre.weights[k], rtol=1e-12, atol=1e-14)
+    Pw = dict(O.as_f64(P))
+    Pw.update(pre.weights)
+    tail, tail_am, _ = O.token_losses(model, Pw, x[8:11], x[9:12])
+    np.testing.assert_allclose(dec.losses[8:], tail, rtol=1e-12)
+    np.testing.assert_array_equal(dec.argmax[8:], tail_am)
+
+
+def test_pins_catch_decode_stepping_one_token_late():
+    """A decode that scores the first token after a full mini-batch before stepping (the step one
+    token late) differs from the chunked loop, so P11 would catch it."""
+    model = tiny_model("gelu", "rms", L=2, b=3, lr=0.3, clip=0.0)
+    P = O.as_f64(tiny_params(model, seed=25))
+    x = tiny_tokens(model, 6, seed=26)
+    pre = O.run_ttt(model, P, x)
+    keys = model.fast_keys()
+    D = {k: np.zeros_like(P[k]) for k in keys}
+    late = []
+    for t in range(1, 7):
+        Pt = dict(P)
+        for k in keys:
+            Pt[k] = P[k] + D[k]
+        l, _, _ = O.token_losses(model, Pt, x[t - 1:t], x[t:t + 1])
+        late.append(l[0])
+        if t == 4:  # should have stepped after t == 3
+            _, _, G = O.chunk_loss_and_grads(model, Pt, x[0:3], x[1:4])
+            for k in keys:
+                D[k] = D[k] - model.lr * G[k]
+    assert abs(late[3] - pre.losses[3]) > 1e-6
+
+
 # ------------------------------------------------------------------ non-finite chunk is skipped
 def test_nonfinite_gradient_skips_update():
     model = tiny_model("gelu", "none", L=1, b=2, lr=0.3)
