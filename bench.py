@@ -36,6 +36,8 @@ METRIC = "TTT inner-loop tokens/s (fwd+bwd+update) at 1 GPU; % of bf16 MFMA peak
 
 
 PROFILE_PERIOD = 8
+DECODE_PERIOD = 16
+PEAK_HBM_GBS = 8000.0
 
 
 def eprint(*a):
@@ -138,6 +140,71 @@ def cpu_baseline(w, P, x, n_chunks: int):
                       f"{dt:.1f} s"}
 
 
+def decode_bytes_per_token(w) -> float:
+    """HBM bytes one decoded token's products read: every weight the forward reads once
+    (bf16: the fast tensors as W0 and rn(D), two segments), plus the LM head."""
+    es = 2 if w.precision == "bf16" else 4
+    segs = 2 if w.precision == "bf16" else 1
+    dm = w.d_model * w.d_hidden * es
+    per_block = (segs * dm if w.mlp == "gelu" else 2 * dm) + segs * dm
+    return float(w.n_blocks * per_block + w.vocab * w.d_model * es)
+
+
+def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
+    """Decode one chunk's worth of tokens (b predictions and the chunk's step) after the timed
+    prefill steps, one token per call of the product path; the one-row products are traced
+    with events in every DECODE_PERIOD-th token."""
+    import numpy as np
+    import torch
+    b = w.chunk
+    T = w.n_tokens
+    ids = np.concatenate([[x[T]], x[1:b + 1]]).astype(np.int32)
+    tok = torch.from_numpy(ids).cuda()
+    ctx.decode(tok)  # warm-up: one full decoded chunk
+    torch.cuda.synchronize()
+    ctx.profile(["dec_gemv"], period=DECODE_PERIOD)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ctx.decode(tok)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    prof = ctx.profile_read()
+    ctx.profile([])
+    gemv_ms, gemv_n = prof.get("dec_gemv", (0.0, 0))
+    per_tok = 2 * w.n_blocks + 1  # up and down per block, then the LM head
+    traced_tokens = max(gemv_n // per_tok, 1)
+    bpt = decode_bytes_per_token(w)
+    gemv_s_per_tok = gemv_ms * 1e-3 / traced_tokens
+    # the products are ~10 us launches, so an event bracket around each adds a large share of
+    # dispatch time: the roofline uses the whole token's time instead (a lower bound on the
+    # kernels' bandwidth), and the bracketed figure is reported beside it
+    achieved = bpt / (dt / b) / 1e9
+    out = {
+        "metric": "decode tokens/s (one prediction per token, the TTT step every chunk)",
+        "value": b / dt, "unit": "tokens/s", "us_per_token": dt / b * 1e6, "tokens": b,
+        "roofline": {"bound": "hbm", "kernel": "decode token (one-row products + CE merge)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_token": bpt,
+                     "gemv_event_us_per_token": gemv_s_per_tok * 1e6, "gemv_launches_traced": gemv_n,
+                     "kernel_name": "k_gemv"},
+    }
+    if cpu:
+        import oracle as O
+        n = 4
+        model = O.Model.from_workload(w)
+        t0 = time.perf_counter()
+        O.decode_ttt(model, P, ids[:n + 1])
+        cdt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:
+            threads = os.cpu_count() or 1
+        out["cpu_baseline"] = {"value": n / cdt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"{n} decoded tokens of the same shape, fp64 numpy, {cdt:.1f} s"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +215,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunks", type=int, default=2)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -218,7 +286,8 @@ def main():
     fpt = alg_flops_per_token(w)
     frac_peak = tokens_per_s * fpt / PEAK_BF16
     dom_ms, dom_n = dprof.get(dom, (0.0, 0))
-    launches_per_chunk = max(1, dom_n // (args.steps * w.n_chunks))
+    # launches of that kind per chunk, from the untimed step where every chunk was traced
+    launches_per_chunk = max(1, round(prof[dom][1] / w.n_chunks))
     per_launch = kind_flops_per_chunk(w, dom) / launches_per_chunk
     avg_s = dom_ms * 1e-3 / max(dom_n, 1)
     achieved = per_launch / avg_s / 1e12 if avg_s > 0 else 0.0
@@ -253,6 +322,8 @@ def main():
             "kernel_name": KIND_KERNEL.get(dom, "EpiStoreF32"),
         },
     }
+    if not args.no_decode:
+        out["decode"] = decode_bench(ctx, w, x, P, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         eprint(f"[bench] timing the fp64 oracle on {args.cpu_chunks} chunks ...")
         out["cpu_baseline"] = cpu_baseline(w, P, x, args.cpu_chunks)

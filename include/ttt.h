@@ -186,7 +186,8 @@ typedef enum {
   TTT_K_NORM_BWD = 14, /* norm backward into the residual gradient           */
   TTT_K_GRADNORM = 15, /* global gradient norm and clip scale                */
   TTT_K_UPDATE = 16,   /* clipped SGD step of one fast tensor                */
-  TTT_K_COUNT = 17
+  TTT_K_DEC_GEMV = 17, /* decode: one-row products with the weights         */
+  TTT_K_COUNT = 18
 } ttt_kernel_kind;
 
 /* Tracing: when bit k of `mask` is set, every later launch of kind k by this context is

@@ -395,50 +395,35 @@ __global__ void __launch_bounds__(NT) k_ce_dlogits(T* __restrict__ Q, int b, int
 // when the decoded tokens fill a mini-batch). One activation row per launch; activations stay
 // in fp32 (the fast weights are the stored bf16 segments), so no operand rounding enters.
 
-// Block input of the decoded token: with tok (the pair x_{t-1}, x_t in the caller's ids),
-// h = E_in[x_{t-1}] into H and the pair copied into the pending-chunk ids pend[0..1] (pend[0]
-// only when first is set); without tok, h = H (already updated in place). Then the pre-norm
-// n = h (mean h^2 + eps)^(-1/2) (rms; none: n = h) into nout (fp32), when given. One block.
+// 8 consecutive weights in the operand precision, as loaded (16 bytes bf16, 32 bytes fp32).
+struct F8 {
+  float4 a, b;
+};
 template <class T>
-__global__ void __launch_bounds__(NT) k_dec_row(const int* __restrict__ tok, int first, int* __restrict__ pend,
-                                                int V, const T* __restrict__ E, float* __restrict__ H, int d,
-                                                float eps, int rms, float* __restrict__ nout, int* __restrict__ err) {
-  __shared__ float red[4];
-  const T* src = nullptr;
-  if (tok) {
-    int xp = tok[0];
-    const int xt = tok[1];
-    if (threadIdx.x == 0) {
-      if (first) pend[0] = xp;
-      pend[1] = xt;
-      if (xp < 0 || xp >= V || xt < 0 || xt >= V) atomicOr(err, ERRBIT_RANGE);
-    }
-    if (xp < 0 || xp >= V) xp = 0;
-    src = E + (int64_t)xp * d;
-  }
-  float ss = 0.f;
-  for (int g = threadIdx.x; g < (d >> 2); g += NT) {
-    const int c = g << 2;
-    float4 h;
-    if (src) {
-      h = load4<T>(src + c);
-      *(float4*)(H + c) = h;
-    } else {
-      h = *(const float4*)(H + c);
-    }
-    ss += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
-  }
-  if (!nout) return;
-  float rr = 1.0f;
-  if (rms) {
-    ss = block_sum_256(ss, red);
-    rr = 1.0f / sqrtf(ss / (float)d + eps);
-  }
-  for (int g = threadIdx.x; g < (d >> 2); g += NT) {
-    const int c = g << 2;
-    const float4 h = *(const float4*)(H + c);
-    *(float4*)(nout + c) = make_float4(h.x * rr, h.y * rr, h.z * rr, h.w * rr);
-  }
+using W8 = typename std::conditional<sizeof(T) == 2, uint4, F8>::type;
+__device__ __forceinline__ uint4 load_w8(const bf16_t* w) { return *(const uint4*)w; }
+__device__ __forceinline__ F8 load_w8(const float* w) { return F8{*(const float4*)w, *(const float4*)(w + 4)}; }
+__device__ __forceinline__ float dot8v(const uint4 u, const float* x) {
+  const float4 x0 = *(const float4*)x, x1 = *(const float4*)(x + 4);
+  float s = __uint_as_float(u.x << 16) * x0.x;
+  s = fmaf(__uint_as_float(u.x & 0xffff0000u), x0.y, s);
+  s = fmaf(__uint_as_float(u.y << 16), x0.z, s);
+  s = fmaf(__uint_as_float(u.y & 0xffff0000u), x0.w, s);
+  s = fmaf(__uint_as_float(u.z << 16), x1.x, s);
+  s = fmaf(__uint_as_float(u.z & 0xffff0000u), x1.y, s);
+  s = fmaf(__uint_as_float(u.w << 16), x1.z, s);
+  return fmaf(__uint_as_float(u.w & 0xffff0000u), x1.w, s);
+}
+__device__ __forceinline__ float dot8v(const F8 w, const float* x) {
+  const float4 x0 = *(const float4*)x, x1 = *(const float4*)(x + 4);
+  float s = w.a.x * x0.x;
+  s = fmaf(w.a.y, x0.y, s);
+  s = fmaf(w.a.z, x0.z, s);
+  s = fmaf(w.a.w, x0.w, s);
+  s = fmaf(w.b.x, x1.x, s);
+  s = fmaf(w.b.y, x1.y, s);
+  s = fmaf(w.b.z, x1.z, s);
+  return fmaf(w.b.w, x1.w, s);
 }
 
 // Dot of 8 consecutive operand-precision weights with 8 fp32 activations.
@@ -467,27 +452,97 @@ __device__ __forceinline__ float dot8(const float* w, const float* x) {
   return fmaf(w1.w, x1.w, s);
 }
 
-// Decode product of one activation row x [K] (fp32) with the rows of Y [N x K] (row stride
-// ldy, operand precision): one wave per output, 16-byte weight loads, x staged in LDS.
+// Decode product of one activation row with the rows of Y [N x K] (row stride ldy, operand
+// precision), fp32 throughout. The block first builds x [K] in LDS:
+//   xin given:  x = xin (the residual stream H or the activation A);
+//   tok given:  x = E_in[tok[0]] (the gather, [E2E] eq. 1: f reads x_{t-1}); block 0 also
+//               writes it to H and copies the pair (tok[0], tok[1]) into the pending-chunk
+//               ids pend (pend[0] only when first), raising the range bit for ids outside
+//               [0, V) (read as id 0);
+//   norm:       then x *= (mean x^2 + eps)^(-1/2) (the block's pre-norm, no gain).
+// Then, with WPR waves per output row splitting K and RPW rows per wave group:
 //   STORE:    out[n] = x.Y[n] (+ x.Y2[n], the second K-segment when Y2 is given)
 //   GELU:     out[n] = GELU(x.Y[n] (+ x.Y2[n]))
 //   RESIDUAL: out[n] += x.Y[n] (+ x.Y2[n])
 //   SWIGLU:   out[n] = SiLU(x.Y[n]) * x.Y2[n] (Y the gate, Y2 the up projection)
-// Each wave handles RPW consecutive rows, reading them interleaved.
-template <class T, int MODE, int RPW>
-__global__ void __launch_bounds__(NT) k_gemv(const float* __restrict__ x, int K, const T* __restrict__ Y,
-                                             const T* __restrict__ Y2, int64_t ldy, int N, float* __restrict__ out) {
+template <class T, int MODE, int WPR, int RPW>
+__global__ void __launch_bounds__(NT) k_gemv(const float* __restrict__ xin, const int* __restrict__ tok, int first,
+                                             int* __restrict__ pend, const T* __restrict__ E, int V,
+                                             float* __restrict__ H, int* __restrict__ err, int norm, float eps,
+                                             int K, const T* __restrict__ Y, const T* __restrict__ Y2, int64_t ldy,
+                                             int N, float* __restrict__ out, float* __restrict__ rmax,
+                                             float* __restrict__ rsum, int* __restrict__ ridx) {
   extern __shared__ __attribute__((aligned(16))) float xs[];
-  for (int g = threadIdx.x; g < (K >> 2); g += NT) *(float4*)(xs + 4 * g) = *(const float4*)(x + 4 * g);
+  __shared__ float red[4];
+  __shared__ float part[2][4][RPW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int GROUPS = (NT / 64) / WPR;  // row groups per block
+  const int grp = wave / WPR, kp = wave % WPR;
+  const int n0 = (blockIdx.x * GROUPS + grp) * RPW;
+  const int kw = K / WPR;  // K per wave (K / WPR is a multiple of 8)
+  const int k_lo = kp * kw, k_hi = k_lo + kw;
+  const bool two = Y2 != nullptr;
+  // the first KP slices of this lane's weights are requested before the activation row is
+  // built: they do not depend on it
+  constexpr int KP = 3;
+  W8<T> w1[KP][RPW], w2[KP][RPW];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int k = min(k_lo + lane * 8 + i * 512, k_hi - 8);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int n = min(n0 + r, N - 1);
+      w1[i][r] = load_w8(Y + (int64_t)n * ldy + k);
+      if (two) w2[i][r] = load_w8(Y2 + (int64_t)n * ldy + k);
+    }
+  }
+  const T* src = nullptr;
+  if (tok) {
+    int xp = tok[0];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const int xt = tok[1];
+      if (first) pend[0] = xp;
+      pend[1] = xt;
+      if (xp < 0 || xp >= V || xt < 0 || xt >= V) atomicOr(err, ERRBIT_RANGE);
+    }
+    if (xp < 0 || xp >= V) xp = 0;
+    src = E + (int64_t)xp * K;
+  }
+  float ss = 0.f;
+  for (int g = threadIdx.x; g < (K >> 2); g += NT) {
+    const float4 v = src ? load4<T>(src + 4 * g) : *(const float4*)(xin + 4 * g);
+    if (src && blockIdx.x == 0) *(float4*)(H + 4 * g) = v;
+    *(float4*)(xs + 4 * g) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  if (norm) {
+    ss = block_sum_256(ss, red);  // includes the barrier that publishes xs
+    const float rr = 1.0f / sqrtf(ss / (float)K + eps);
+    for (int g = threadIdx.x; g < (K >> 2); g += NT) {
+      float4 v = *(float4*)(xs + 4 * g);
+      v.x *= rr;
+      v.y *= rr;
+      v.z *= rr;
+      v.w *= rr;
+      *(float4*)(xs + 4 * g) = v;
+    }
+  }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * RPW;
   float s1[RPW], s2[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) s1[r] = s2[r] = 0.f;
-  const bool two = Y2 != nullptr;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int k = k_lo + lane * 8 + i * 512;
+    if (k >= k_hi) break;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      s1[r] += dot8v(w1[i][r], xs + k);
+      if (two) s2[r] += dot8v(w2[i][r], xs + k);
+    }
+  }
 #pragma unroll 2
-  for (int k = lane * 8; k < K; k += 512) {
+  for (int k = k_lo + lane * 8 + KP * 512; k < k_hi; k += 512) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int n = min(n0 + r, N - 1);
@@ -497,61 +552,99 @@ __global__ void __launch_bounds__(NT) k_gemv(const float* __restrict__ x, int K,
   }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
+    s1[r] = wave_sum(s1[r]);
+    s2[r] = wave_sum(s2[r]);
+  }
+  if constexpr (WPR > 1) {
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        part[0][wave][r] = s1[r];
+        part[1][wave][r] = s2[r];
+      }
+    __syncthreads();
+    if (kp != 0) return;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float a = part[0][grp * WPR][r], b = part[1][grp * WPR][r];
+      for (int q = 1; q < WPR; ++q) {
+        a += part[0][grp * WPR + q][r];
+        b += part[1][grp * WPR + q][r];
+      }
+      s1[r] = a;
+      s2[r] = b;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
     const int n = n0 + r;
-    const float a = wave_sum(s1[r]), b = wave_sum(s2[r]);
     if (lane != 0 || n >= N) continue;
+    const float a = s1[r], b = s2[r];
     if constexpr (MODE == GEMV_STORE) out[n] = a + b;
     if constexpr (MODE == GEMV_GELU) out[n] = gelu_f(a + b);
     if constexpr (MODE == GEMV_RESIDUAL) out[n] += a + b;
     if constexpr (MODE == GEMV_SWIGLU) out[n] = silu_f(a) * b;
   }
-}
-
-// Decode CE of one logits row z [V] (fp32): lse, first argmax, loss = lse - z[target]
-// (target = pend[0], clamped like the gather). Writes the token's loss and argmax records and,
-// when given, argmax_out. One block of NT threads, fixed partition and order.
-__global__ void __launch_bounds__(NT) k_dec_ce(const float* __restrict__ z, int V, const int* __restrict__ pend,
-                                               float* __restrict__ loss, int* __restrict__ amax,
-                                               int* __restrict__ argmax_out) {
-  __shared__ float smx[NT];
-  __shared__ int six[NT];
-  __shared__ float ssm[NT];
-  float mx = -INFINITY;
-  int ix = 0x7fffffff;
-  for (int v = threadIdx.x; v < V; v += NT) {
-    const float zv = z[v];
-    if (zv > mx) {
-      mx = zv;
-      ix = v;
+  if constexpr (MODE == GEMV_STORE && WPR == 1) {
+    // with records: this block's online-softmax record over its rows (max, sum of
+    // exp(z - max), first argmax), for the decode CE merge
+    if (rmax) {
+      __shared__ float zb[(NT / 64) * RPW];
+      if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) zb[wave * RPW + r] = s1[r] + s2[r];
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int base = blockIdx.x * (NT / 64) * RPW;
+        float mx = -INFINITY;
+        int ix = 0x7fffffff;
+        for (int q = 0; q < (NT / 64) * RPW && base + q < N; ++q)
+          if (zb[q] > mx) {
+            mx = zb[q];
+            ix = base + q;
+          }
+        float sm = 0.f;
+        for (int q = 0; q < (NT / 64) * RPW && base + q < N; ++q) sm += expf(zb[q] - mx);
+        rmax[blockIdx.x] = mx;
+        rsum[blockIdx.x] = sm;
+        ridx[blockIdx.x] = ix;
+      }
     }
   }
+}
+
+// Decode CE of one logits row z [V] (fp32) from the LM-head product's per-block records
+// (max, sum of exp(z - max), first argmax), merged in a fixed order: lse, first argmax and
+// loss = lse - z[target] (target = tgt[0], clamped like the gather). Writes the token's loss
+// and argmax records and, when given, argmax_out. One block.
+__global__ void __launch_bounds__(NT) k_dec_ce(const float* __restrict__ z, int V, const float* __restrict__ rmax,
+                                               const float* __restrict__ rsum, const int* __restrict__ ridx, int nrec,
+                                               const int* __restrict__ tgt, float* __restrict__ loss,
+                                               int* __restrict__ amax, int* __restrict__ argmax_out) {
+  __shared__ float smx[NT], ssm[NT];
+  __shared__ int six[NT];
+  float mx = -INFINITY, sm = 0.f;
+  int ix = 0x7fffffff;
+  for (int j = threadIdx.x; j < nrec; j += NT) ce_combine(mx, sm, ix, rmax[j], rsum[j], ridx[j]);
   smx[threadIdx.x] = mx;
+  ssm[threadIdx.x] = sm;
   six[threadIdx.x] = ix;
   __syncthreads();
   for (int s = NT / 2; s > 0; s >>= 1) {
     if (threadIdx.x < s) {
-      const float om = smx[threadIdx.x + s];
-      const int oi = six[threadIdx.x + s];
-      if (om > smx[threadIdx.x] || (om == smx[threadIdx.x] && oi < six[threadIdx.x])) {
-        smx[threadIdx.x] = om;
-        six[threadIdx.x] = oi;
-      }
+      float m0 = smx[threadIdx.x], s0 = ssm[threadIdx.x];
+      int i0 = six[threadIdx.x];
+      ce_combine(m0, s0, i0, smx[threadIdx.x + s], ssm[threadIdx.x + s], six[threadIdx.x + s]);
+      smx[threadIdx.x] = m0;
+      ssm[threadIdx.x] = s0;
+      six[threadIdx.x] = i0;
     }
     __syncthreads();
   }
-  const float M = smx[0];
-  float sm = 0.f;
-  for (int v = threadIdx.x; v < V; v += NT) sm += expf(z[v] - M);
-  ssm[threadIdx.x] = sm;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) ssm[threadIdx.x] += ssm[threadIdx.x + s];
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    int tg = pend[0];
+    int tg = tgt[0];
     if (tg < 0 || tg >= V) tg = 0;
-    const float lse = M + logf(ssm[0]);
+    const float lse = smx[0] + logf(ssm[0]);
     loss[0] = lse - z[tg];
     amax[0] = six[0];
     if (argmax_out) argmax_out[0] = six[0];
@@ -720,42 +813,42 @@ hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, 
   return hipGetLastError();
 }
 
-hipError_t run_dec_row(hipStream_t st, int prec, const int* tok, int first, int* pend, int V, const void* E, float* H,
-                       int d, float eps, int rms, float* nout, int* err) {
-  if (d % 8) return hipErrorInvalidValue;
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_dec_row<T>, dim3(1), dim3(NT), 0, st, tok, first, pend, V, (const T*)E, H, d,
-                                      eps, rms, nout, err));
-  return hipGetLastError();
-}
-
 template <class T, int MODE>
-static hipError_t launch_gemv(hipStream_t st, const float* x, int K, const T* Y, const T* Y2, int64_t ldy, int N,
+static hipError_t launch_gemv(hipStream_t st, const GemvIn& in, int K, const T* Y, const T* Y2, int64_t ldy, int N,
                               float* out) {
   const size_t lds = (size_t)K * sizeof(float);
-  if (N >= 16384) {
-    hipLaunchKernelGGL((k_gemv<T, MODE, 4>), dim3((N + 15) / 16), dim3(NT), lds, st, x, K, Y, Y2, ldy, N, out);
+  const T* E = (const T*)in.E;
+#define TTT_GEMV_ARGS in.xin, in.tok, in.first, in.pend, E, in.V, in.H, in.err, in.norm, in.eps, K, Y, Y2, ldy, N, out, \
+    in.rmax, in.rsum, in.ridx
+  if (K >= 4096 && K % (4 * 8) == 0 && !in.rmax) {  // long rows: four waves share each row
+    hipLaunchKernelGGL((k_gemv<T, MODE, 4, 1>), dim3(N), dim3(NT), lds, st, TTT_GEMV_ARGS);
+  } else if (N >= 16384) {
+    hipLaunchKernelGGL((k_gemv<T, MODE, 1, 4>), dim3((N + 15) / 16), dim3(NT), lds, st, TTT_GEMV_ARGS);
   } else {
-    hipLaunchKernelGGL((k_gemv<T, MODE, 1>), dim3((N + 3) / 4), dim3(NT), lds, st, x, K, Y, Y2, ldy, N, out);
+    hipLaunchKernelGGL((k_gemv<T, MODE, 1, 1>), dim3((N + 3) / 4), dim3(NT), lds, st, TTT_GEMV_ARGS);
   }
+#undef TTT_GEMV_ARGS
   return hipGetLastError();
 }
 
-hipError_t run_gemv(hipStream_t st, int prec, int mode, const float* x, int K, const void* Y, const void* Y2,
+hipError_t run_gemv(hipStream_t st, int prec, int mode, const GemvIn& in, int K, const void* Y, const void* Y2,
                     int64_t ldy, int N, float* out) {
   if (K % 8 || ldy % 8 || N <= 0 || (size_t)K * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
+  if ((in.xin == nullptr) == (in.tok == nullptr)) return hipErrorInvalidValue;
   DISPATCH_T(prec, {
     switch (mode) {
-      case GEMV_STORE: return launch_gemv<T, GEMV_STORE>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
-      case GEMV_GELU: return launch_gemv<T, GEMV_GELU>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
-      case GEMV_RESIDUAL: return launch_gemv<T, GEMV_RESIDUAL>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
-      case GEMV_SWIGLU: return launch_gemv<T, GEMV_SWIGLU>(st, x, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_STORE: return launch_gemv<T, GEMV_STORE>(st, in, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_GELU: return launch_gemv<T, GEMV_GELU>(st, in, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_RESIDUAL: return launch_gemv<T, GEMV_RESIDUAL>(st, in, K, (const T*)Y, (const T*)Y2, ldy, N, out);
+      case GEMV_SWIGLU: return launch_gemv<T, GEMV_SWIGLU>(st, in, K, (const T*)Y, (const T*)Y2, ldy, N, out);
       default: return hipErrorInvalidValue;
     }
   });
 }
 
-hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const int* tgt, float* loss, int* amax, int* argmax_out) {
-  hipLaunchKernelGGL(k_dec_ce, dim3(1), dim3(NT), 0, st, z, V, tgt, loss, amax, argmax_out);
+hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const float* rmax, const float* rsum, const int* ridx,
+                      int nrec, const int* tgt, float* loss, int* amax, int* argmax_out) {
+  hipLaunchKernelGGL(k_dec_ce, dim3(1), dim3(NT), 0, st, z, V, rmax, rsum, ridx, nrec, tgt, loss, amax, argmax_out);
   return hipGetLastError();
 }
 

@@ -34,16 +34,35 @@ hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, 
 hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
 
 // ---- decode (kernels.hip): one activation row, fp32 activations
-// Block input of a decoded token (gather of tok[0] and copy of the pair into pend when tok is
-// non-null) and its pre-norm into nout (fp32) when nout is non-null.
-hipError_t run_dec_row(hipStream_t st, int prec, const int* tok, int first, int* pend, int V, const void* E, float* H,
-                       int d, float eps, int rms, float* nout, int* err);
 enum { GEMV_STORE = 0, GEMV_GELU = 1, GEMV_RESIDUAL = 2, GEMV_SWIGLU = 3 };
-// out[n] (mode) x . Y[n] (+ x . Y2[n]); Y [N x K] row stride ldy in the operand precision, x fp32 [K].
-hipError_t run_gemv(hipStream_t st, int prec, int mode, const float* x, int K, const void* Y, const void* Y2,
+// How a decode product builds its activation row x (see k_gemv): from xin, or by the gather
+// of tok[0] from E (then H, pend and err are written as the gather's side effects); then the
+// pre-norm when norm is set.
+struct GemvIn {
+  const float* xin = nullptr;
+  const int* tok = nullptr;
+  int first = 0;
+  int* pend = nullptr;
+  const void* E = nullptr;
+  int V = 0;
+  float* H = nullptr;
+  int* err = nullptr;
+  int norm = 0;
+  float eps = 0.f;
+  // STORE only: one online-softmax record per block of gemv_rec_rows(N) outputs
+  float* rmax = nullptr;
+  float* rsum = nullptr;
+  int* ridx = nullptr;
+};
+// Outputs per record of a STORE product with records (the records number ceil(N / that)).
+inline int gemv_rec_rows(int N) { return N >= 16384 ? 16 : 4; }
+// out[n] (mode) x . Y[n] (+ x . Y2[n]); Y [N x K] row stride ldy in the operand precision.
+hipError_t run_gemv(hipStream_t st, int prec, int mode, const GemvIn& in, int K, const void* Y, const void* Y2,
                     int64_t ldy, int N, float* out);
-// lse, first argmax and loss = lse - z[*tgt] of one logits row; records loss[0], amax[0].
-hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const int* tgt, float* loss, int* amax, int* argmax_out);
+// lse, first argmax and loss = lse - z[*tgt] of one logits row from the product's records;
+// records loss[0], amax[0] (and argmax_out[0] when non-null).
+hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const float* rmax, const float* rsum, const int* ridx,
+                      int nrec, const int* tgt, float* loss, int* amax, int* argmax_out);
 
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
 // Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).

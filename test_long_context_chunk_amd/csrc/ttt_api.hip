@@ -72,7 +72,8 @@ struct ttt_ctx {
   // filled, and the one-row fp32 activations
   int* dec_tok = nullptr;
   int npend = 0;
-  float *dec_h = nullptr, *dec_n = nullptr, *dec_a = nullptr, *dec_z = nullptr;
+  float *dec_h = nullptr, *dec_a = nullptr, *dec_z = nullptr, *dec_rmax = nullptr, *dec_rsum = nullptr;
+  int* dec_ridx = nullptr;
   float* part = nullptr;
   float* dH = nullptr;
   void *dHb = nullptr, *dHT = nullptr, *A = nullptr, *dU = nullptr, *dUT = nullptr;
@@ -275,9 +276,11 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * b * d * 4);
   c->dec_tok = dalloc<int>(c, (int64_t)(b + 1) * 4);
   c->dec_h = dalloc<float>(c, (int64_t)d * 4);
-  c->dec_n = dalloc<float>(c, (int64_t)d * 4);
   c->dec_a = dalloc<float>(c, (int64_t)m * 4);
   c->dec_z = dalloc<float>(c, (int64_t)V * 4);
+  c->dec_rmax = dalloc<float>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
+  c->dec_rsum = dalloc<float>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
+  c->dec_ridx = dalloc<int>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
   c->dH = dalloc<float>(c, (int64_t)b * d * 4);
   c->dHb = dalloc<char>(c, (int64_t)b * d * es);
   c->dHT = dalloc<char>(c, (int64_t)d * bp * es);
@@ -497,21 +500,41 @@ void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out)
   const bool bf = prec == PREC_BF16;
   const float eps = c->cfg.rms_eps;
   float* z = z_out ? z_out : c->dec_z;
-  check(run_dec_row(st, prec, tok, c->npend == 0, c->dec_tok + c->npend, V, c->E_in, c->dec_h, d, eps, rms,
-                    L > 0 ? c->dec_n : nullptr, c->err));
+  c->prof_on = c->prof_mask != 0 && (c->prof_chunks++ % c->prof_period) == 0;
+  // the first product gathers the token's embedding (and files the pair in the pending chunk)
+  GemvIn g0;
+  g0.tok = tok;
+  g0.first = c->npend == 0;
+  g0.pend = c->dec_tok + c->npend;
+  g0.E = c->E_in;
+  g0.V = V;
+  g0.H = c->dec_h;
+  g0.err = c->err;
+  g0.eps = eps;
+  GemvIn gh;  // the residual stream as the activation row
+  gh.xin = c->dec_h;
+  gh.eps = eps;
+  GemvIn ga;  // the block's activation row
+  ga.xin = c->dec_a;
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
+    GemvIn in = l == 0 ? g0 : gh;
+    in.norm = rms;
     if (gelu)
-      check(run_gemv(st, prec, GEMV_GELU, c->dec_n, d, bf ? B.w1.W0T : B.w1.WtT, bf ? B.w1.WtT : nullptr, d, m,
-                     c->dec_a));
+      RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_GELU, in, d, bf ? B.w1.W0T : B.w1.WtT, bf ? B.w1.WtT : nullptr, d, m,
+                                   c->dec_a));
     else
-      check(run_gemv(st, prec, GEMV_SWIGLU, c->dec_n, d, B.WgT, B.WuT, d, m, c->dec_a));
-    check(run_gemv(st, prec, GEMV_RESIDUAL, c->dec_a, m, bf ? B.w2.W0T : B.w2.WtT, bf ? B.w2.WtT : nullptr, m, d,
-                   c->dec_h));
-    if (l + 1 < L) check(run_dec_row(st, prec, nullptr, 0, nullptr, V, nullptr, c->dec_h, d, eps, rms, c->dec_n, c->err));
+      RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_SWIGLU, in, d, B.WgT, B.WuT, d, m, c->dec_a));
+    RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_RESIDUAL, ga, m, bf ? B.w2.W0T : B.w2.WtT, bf ? B.w2.WtT : nullptr, m,
+                                 d, c->dec_h));
   }
-  check(run_gemv(st, prec, GEMV_STORE, c->dec_h, d, c->E_out, nullptr, d, V, z));
-  check(run_dec_ce(st, z, V, c->dec_tok + c->npend + 1, c->losses + c->pos, c->amax + c->pos, am_out));
+  GemvIn gz = L == 0 ? g0 : gh;
+  gz.rmax = c->dec_rmax;
+  gz.rsum = c->dec_rsum;
+  gz.ridx = c->dec_ridx;
+  RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_STORE, gz, d, c->E_out, nullptr, d, V, z));
+  check(run_dec_ce(st, z, V, c->dec_rmax, c->dec_rsum, c->dec_ridx, cdiv(V, gemv_rec_rows(V)),
+                   c->dec_tok + c->npend + 1, c->losses + c->pos, c->amax + c->pos, am_out));
 }
 
 ttt_status read_sticky(ttt_ctx* c) {

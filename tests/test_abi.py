@@ -93,6 +93,9 @@ def test_null_context_calls_are_rejected(lib):
     assert lib.ttt_sync(None) == -1
     assert lib.ttt_destroy(None) == 0
     assert lib.ttt_tokens_consumed(None) == -1
+    assert lib.ttt_decode(None, None, 1, None, None) == -1
+    assert lib.ttt_decode_pending(None) == -1
+    assert lib.ttt_profile_period(None, 1) == -1
 
 
 def test_gemm_hook_validates_shapes(lib):
@@ -100,3 +103,14 @@ def test_gemm_hook_validates_shapes(lib):
     assert lib.ttt_test_gemm(1, 1, 8, 1, 8, 1, 8, 4, 4, 6, None) == -1
     assert lib.ttt_test_gemm(0, 1, 8, 1, 8, 1, 8, 4, 4, 6, None) == -1
     assert lib.ttt_test_gemm(7, 1, 8, 1, 8, 1, 8, 4, 4, 8, None) == -1
+
+
+def test_kernel_kind_names_match_the_header():
+    """The binding's kind names index the per-kind arrays that ttt_profile_read fills."""
+    import re
+    from test_long_context_chunk_amd import _binding
+    hdr = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    kinds = re.findall(r"TTT_K_(\w+) = (\d+),", hdr)
+    count = int(re.search(r"TTT_K_COUNT = (\d+)", hdr).group(1))
+    assert [int(v) for _, v in kinds] == list(range(count))
+    assert len(_binding.KERNEL_KINDS) == count
