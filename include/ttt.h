@@ -136,6 +136,34 @@ ttt_status ttt_decode(ttt_ctx* ctx, const int32_t* tokens, int64_t n, int32_t* a
 /* Decoded pairs waiting for their chunk to fill (0 .. chunk - 1; -1 for NULL). */
 int64_t ttt_decode_pending(const ttt_ctx* ctx);
 
+/* Loss of a passage at the current fast weights, without any step ([SGF]: a held-out
+ * real-text passage is scored against the state; scoring changes nothing).
+ * q: device int32 [nq + 1]; q[0] conditions q[1]; nq a positive multiple of the chunk size.
+ * losses: device fp32 [nq], per-token losses (bf16: with the same loss compensation as the
+ * recorded prefill losses); mean: device fp32 scalar, their mean. Either may be NULL. The
+ * stream (token count, records, pending decode pairs, fast weights) is unchanged.
+ * Errors (nothing enqueued): TTT_EINVAL, TTT_ESTATE. */
+ttt_status ttt_evaluate(ttt_ctx* ctx, const int32_t* q, int64_t nq, float* losses, float* mean);
+
+/* Snapshot of the fast state (one slot per context; the first call allocates it, about
+ * 8 bytes per fast parameter in bf16 mode), and restore of that snapshot. Enqueued.
+ * ttt_restore returns TTT_ESTATE when no snapshot was taken. ttt_settle_chunk uses the same
+ * slot. Errors: TTT_EINVAL, TTT_ESTATE. */
+ttt_status ttt_snapshot(ttt_ctx* ctx);
+ttt_status ttt_restore(ttt_ctx* ctx);
+
+/* The Settlement rule ([SGF], Settlement): the candidate chunk (tokens: device int32
+ * [chunk + 1], as for one prefill chunk) is scored at W and stepped to W + delta as in
+ * ttt_prefill_chunks; the held-out passage q (as for ttt_evaluate) gives
+ *   A = L(q, W) - L(q, W + delta)   (mean per-token losses),
+ * and delta is kept only if A >= 0; otherwise the fast weights return to W. The candidate's
+ * losses, argmax and chunk statistics are recorded either way and the token count advances
+ * by one chunk. A (device fp32) and committed (device int32, 1 = kept) receive the outcome
+ * when non-NULL. The decision and the restore happen on the device: nothing synchronises.
+ * Refused (TTT_EINVAL) while decoded pairs are pending. Errors: TTT_EINVAL, TTT_ESTATE. */
+ttt_status ttt_settle_chunk(ttt_ctx* ctx, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
+                            int32_t* committed);
+
 /* Copy the recorded losses l_t(W_{i-1}) of tokens [offset, offset + n) (counted from the
  * first token of the first prefill since creation or reset) into dst (device fp32 [n]).
  * Synchronises the context's stream; returns a pending sticky error if there is one

@@ -357,6 +357,35 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
                      np.asarray(sk, dtype=bool), D, Wf)
 
 
+def passage_loss(model: Model, P: Dict[str, np.ndarray], q: np.ndarray) -> float:
+    """L(q, W): the mean next-token loss of a passage q_0..q_n at fixed weights (no step)."""
+    q = np.asarray(q, dtype=np.int64)
+    l, _, _ = token_losses(model, as_f64(P), q[:-1], q[1:])
+    return float(l.mean())
+
+
+def settle_step(model: Model, P: Dict[str, np.ndarray], cand: np.ndarray, q: np.ndarray):
+    """The Settlement rule of [SGF] for one candidate chunk.
+
+    From the current weights W (P), the candidate's update delta is the clipped mini-batch
+    step of [E2E] eq. (5) on the candidate chunk cand_0..cand_b. On the held-out passage q,
+    A(delta; W, q) = L(q, W) - L(q, W + delta), and delta is committed only if A >= 0.
+    Returns (A, committed, the weights after the decision, g, s).
+    """
+    P = as_f64(P)
+    cand = np.asarray(cand, dtype=np.int64)
+    keys = model.fast_keys()
+    _, _, G = chunk_loss_and_grads(model, P, cand[:-1], cand[1:])
+    g = math.sqrt(sum(float(np.sum(G[k] * G[k])) for k in keys))
+    s = clip_scale(g, model.clip) if math.isfinite(g) else 0.0
+    Pd = dict(P)
+    for k in keys:
+        Pd[k] = P[k] - model.lr * s * G[k]
+    A = passage_loss(model, P, q) - passage_loss(model, Pd, q)
+    keep = bool(A >= 0.0)
+    return A, keep, ({k: Pd[k] for k in keys} if keep else {k: P[k] for k in keys}), g, s
+
+
 def static_losses(model: Model, P0, tokens, n_tokens: Optional[int] = None) -> np.ndarray:
     """l_t(W_0) for every t: the summands of L_naive, [E2E] eq. (4)."""
     P0 = as_f64(P0)

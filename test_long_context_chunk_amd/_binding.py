@@ -40,6 +40,10 @@ SIGNATURES = {
     "ttt_status_string": (ctypes.c_char_p, [c_int32]),
     "ttt_decode": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
     "ttt_decode_pending": (c_int64, [c_void_p]),
+    "ttt_evaluate": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
+    "ttt_snapshot": (c_int32, [c_void_p]),
+    "ttt_restore": (c_int32, [c_void_p]),
+    "ttt_settle_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
     "ttt_profile_enable": (c_int32, [c_void_p, ctypes.c_uint32]),
     "ttt_profile_period": (c_int32, [c_void_p, c_int32]),
     "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
@@ -196,6 +200,38 @@ class TTT:
         _check(self._lib.ttt_decode(self._ctx, c_void_p(_ptr(tokens)), n, c_void_p(_ptr(am) if n > 0 else None),
                                     c_void_p(_ptr(z)) if (z is not None and n > 0) else None), "ttt_decode")
         return am, z
+
+    def evaluate(self, q):
+        """q: device int32 [nq + 1]. Returns (per-token losses fp32 [nq], mean fp32 [1]) at the
+        current weights; nothing changes."""
+        import torch
+        if q.dtype != torch.int32 or not q.is_cuda or not q.is_contiguous():
+            raise ValueError("q must be a contiguous int32 device tensor")
+        nq = q.numel() - 1
+        losses = torch.empty(max(nq, 1), dtype=torch.float32, device="cuda")
+        mean = torch.empty(1, dtype=torch.float32, device="cuda")
+        _check(self._lib.ttt_evaluate(self._ctx, c_void_p(_ptr(q)), nq, c_void_p(_ptr(losses)), c_void_p(_ptr(mean))),
+               "ttt_evaluate")
+        return losses[:nq], mean
+
+    def snapshot(self) -> None:
+        _check(self._lib.ttt_snapshot(self._ctx), "ttt_snapshot")
+
+    def restore(self) -> None:
+        _check(self._lib.ttt_restore(self._ctx), "ttt_restore")
+
+    def settle(self, tokens, q):
+        """One candidate chunk (tokens: device int32 [chunk + 1]) under the Settlement rule
+        against the passage q (device int32 [nq + 1]). Returns (A fp32 [1], committed int32 [1])."""
+        import torch
+        for t in (tokens, q):
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tokens and q must be contiguous int32 device tensors")
+        A = torch.empty(1, dtype=torch.float32, device="cuda")
+        kept = torch.empty(1, dtype=torch.int32, device="cuda")
+        _check(self._lib.ttt_settle_chunk(self._ctx, c_void_p(_ptr(tokens)), c_void_p(_ptr(q)), q.numel() - 1,
+                                          c_void_p(_ptr(A)), c_void_p(_ptr(kept))), "ttt_settle_chunk")
+        return A, kept
 
     def decode_pending(self) -> int:
         return int(self._lib.ttt_decode_pending(self._ctx))

@@ -651,6 +651,55 @@ __global__ void __launch_bounds__(NT) k_dec_ce(const float* __restrict__ z, int 
   }
 }
 
+// ---- evaluation and Settlement ([SGF], Settlement: a candidate step is committed only if
+// it does not raise the loss of a held-out passage).
+
+// Add the n losses of one evaluated chunk to acc[0] (fp64, fixed order; zeroed first when
+// first is set), copy them to out when given, and when last is set write acc[0] / count into
+// mean (when given). One block.
+__global__ void __launch_bounds__(NT) k_eval_accum(const float* __restrict__ loss, int n, double* __restrict__ acc,
+                                                   float* __restrict__ out, int first, int last, int64_t count,
+                                                   float* __restrict__ mean) {
+  __shared__ double red[NT];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const float v = loss[i];
+    s += (double)v;
+    if (out) out[i] = v;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = NT / 2; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double t = (first ? 0.0 : acc[0]) + red[0];
+    acc[0] = t;
+    if (last && mean) mean[0] = (float)(t / (double)count);
+  }
+}
+
+// A = (sum0 - sum1) / count = L(q, W) - L(q, W + delta); commit = A >= 0 (a non-finite A
+// rejects). Writes A and the decision to the context's words and, when given, the caller's.
+__global__ void k_settle_decide(const double* __restrict__ sums, int64_t count, float* __restrict__ A,
+                                int* __restrict__ commit, float* __restrict__ A_out, int* __restrict__ commit_out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const double a = (sums[0] - sums[1]) / (double)count;
+  const int ok = (a >= 0.0) ? 1 : 0;  // false for NaN
+  A[0] = (float)a;
+  commit[0] = ok;
+  if (A_out) A_out[0] = (float)a;
+  if (commit_out) commit_out[0] = ok;
+}
+
+// dst <- src (n bytes, 16-byte aligned, n a multiple of 16) unless *commit is set.
+__global__ void __launch_bounds__(NT) k_restore_unless(const int* __restrict__ commit, const uint4* __restrict__ src,
+                                                       uint4* __restrict__ dst, int64_t n16) {
+  if (commit[0]) return;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n16; i += (int64_t)gridDim.x * NT) dst[i] = src[i];
+}
+
 // a9: in-place clipped SGD step of one fast tensor [R x C]:
 //   D <- D - lr * s * G;  Wop = rn(W0 + D) row-major (the backward GEMMs' operand);
 //   WtT = transposed copy of rn(D) when delta_t (bf16: the forward GEMMs add X rn(D)^T to
@@ -849,6 +898,27 @@ hipError_t run_gemv(hipStream_t st, int prec, int mode, const GemvIn& in, int K,
 hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const float* rmax, const float* rsum, const int* ridx,
                       int nrec, const int* tgt, float* loss, int* amax, int* argmax_out) {
   hipLaunchKernelGGL(k_dec_ce, dim3(1), dim3(NT), 0, st, z, V, rmax, rsum, ridx, nrec, tgt, loss, amax, argmax_out);
+  return hipGetLastError();
+}
+
+hipError_t run_eval_accum(hipStream_t st, const float* loss, int n, double* acc, float* out, int first, int last,
+                          int64_t count, float* mean) {
+  hipLaunchKernelGGL(k_eval_accum, dim3(1), dim3(NT), 0, st, loss, n, acc, out, first, last, count, mean);
+  return hipGetLastError();
+}
+
+hipError_t run_settle_decide(hipStream_t st, const double* sums, int64_t count, float* A, int* commit, float* A_out,
+                             int* commit_out) {
+  hipLaunchKernelGGL(k_settle_decide, dim3(1), dim3(64), 0, st, sums, count, A, commit, A_out, commit_out);
+  return hipGetLastError();
+}
+
+hipError_t run_restore_unless(hipStream_t st, const int* commit, const void* src, void* dst, int64_t bytes) {
+  if (bytes % 16) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_restore_unless, dim3(grid_for(n16)), dim3(NT), 0, st, commit, (const uint4*)src, (uint4*)dst,
+                     n16);
   return hipGetLastError();
 }
 

@@ -64,6 +64,17 @@ hipError_t run_gemv(hipStream_t st, int prec, int mode, const GemvIn& in, int K,
 hipError_t run_dec_ce(hipStream_t st, const float* z, int V, const float* rmax, const float* rsum, const int* ridx,
                       int nrec, const int* tgt, float* loss, int* amax, int* argmax_out);
 
+// ---- evaluation and Settlement (kernels.hip)
+// acc[0] (fp64) += sum of n losses (zeroed first when first); out <- losses when non-null; when
+// last, mean[0] = acc[0] / count (when mean is non-null).
+hipError_t run_eval_accum(hipStream_t st, const float* loss, int n, double* acc, float* out, int first, int last,
+                          int64_t count, float* mean);
+// A = (sums[0] - sums[1]) / count, commit = A >= 0; also into A_out / commit_out when non-null.
+hipError_t run_settle_decide(hipStream_t st, const double* sums, int64_t count, float* A, int* commit, float* A_out,
+                             int* commit_out);
+// dst <- src (bytes, a multiple of 16) unless *commit.
+hipError_t run_restore_unless(hipStream_t st, const int* commit, const void* src, void* dst, int64_t bytes);
+
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
 // Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).
 struct GemmSeg2 {

@@ -27,6 +27,10 @@ struct FastTensor {
   void* G = nullptr;       // chunk gradient in the GEMM precision [rows x cols]
   int slot0 = 0;           // first grad-norm slot
   hipEvent_t ev_upd = nullptr;  // recorded on the aux stream after this tensor's last update
+  // snapshot of the state a step changes (D, Wop, WtT), allocated at the first snapshot
+  void* snapD = nullptr;
+  void* snapWop = nullptr;
+  void* snapWtT = nullptr;
 };
 
 struct Block {
@@ -72,6 +76,13 @@ struct ttt_ctx {
   // filled, and the one-row fp32 activations
   int* dec_tok = nullptr;
   int npend = 0;
+  // evaluation and Settlement: one chunk's losses and argmax, fp64 loss sums, A and the decision
+  float* eval_loss = nullptr;
+  int* eval_amax = nullptr;
+  double* eval_acc = nullptr;  // [3]: ttt_evaluate, L(q, W), L(q, W + delta)
+  float* settle_A = nullptr;
+  int* settle_commit = nullptr;
+  bool has_snap = false;
   float *dec_h = nullptr, *dec_a = nullptr, *dec_z = nullptr, *dec_rmax = nullptr, *dec_rsum = nullptr;
   int* dec_ridx = nullptr;
   float* part = nullptr;
@@ -275,6 +286,11 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   if (L > 0) c->P = dalloc<char>(c, (int64_t)b * V * es);  // softmax numerators, then dlogits
   c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * b * d * 4);
   c->dec_tok = dalloc<int>(c, (int64_t)(b + 1) * 4);
+  c->eval_loss = dalloc<float>(c, (int64_t)b * 4);
+  c->eval_amax = dalloc<int>(c, (int64_t)b * 4);
+  c->eval_acc = dalloc<double>(c, 3 * 8);
+  c->settle_A = dalloc<float>(c, 4);
+  c->settle_commit = dalloc<int>(c, 4);
   c->dec_h = dalloc<float>(c, (int64_t)d * 4);
   c->dec_a = dalloc<float>(c, (int64_t)m * 4);
   c->dec_z = dalloc<float>(c, (int64_t)V * 4);
@@ -355,15 +371,18 @@ void prof_mark(ttt_ctx* c) {
     }                                           \
   } while (0)
 
-// One chunk of [E2E] eq. (5): forward at W_{i-1}, record l_t(W_{i-1}) (eq. 6), backward
-// to every fast tensor, global-norm clip ([SGF]), SGD step.
+// One chunk of [E2E] eq. (5): forward at W_{i-1}, record l_t(W_{i-1}) (eq. 6) into loss_out
+// and the argmax into amax_out, backward to every fast tensor, global-norm clip ([SGF]), SGD
+// step (chunk statistics at chunk_idx). With train = false, an evaluation at the current
+// weights: the same losses, with the backward run only as far as the loss compensation needs
+// it (no weight gradients, no step).
 //
 // bf16 only, first-order loss compensation: the forward rounds three kinds of GEMM operands
 // to bf16 (block inputs n, activations A, the LM-head input Y). Each recorded loss is
 // corrected by b * sum <dL/dX_t, X_t - rn(X_t)> over those operands, with dL/dX the
 // chunk-mean-loss gradients the backward pass computes anyway, so l_t matches the loss of
 // the unrounded forward to first order in the rounding error.
-void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
+void run_chunk(ttt_ctx* c, const int32_t* tok, float* loss_out, int* amax_out, bool train, int64_t chunk_idx) {
   hipStream_t st = c->st;
   c->prof_on = c->prof_mask != 0 && (c->prof_chunks++ % c->prof_period) == 0;
   const int prec = c->prec;
@@ -388,7 +407,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     Block& B = c->blocks[l];
     if (gelu) {
       // Hn^T is read only by the W1 gradient of the backward pass
-      check(run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
+      if (train) check(run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
       check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
@@ -416,10 +435,10 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
   RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, b, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
                                     c->tgt_logit, c->ce_nrec, c->P, V));
   RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_nrec, b, c->tgt_logit, c->lse,
-                                   c->losses + tokpos, c->amax + tokpos));
+                                   loss_out, amax_out));
 
-  const int64_t chunk_idx = tokpos / b;
-  if (L > 0) {
+  // an evaluation (no step) runs the backward only for the loss compensation
+  if (L > 0 && (train || foc)) {
     // a6 CE backward: dlogits in place from the stored numerators, then dY = P E_out over the
     // whole vocabulary (split-K slabs)
     RUN(TTT_K_CE_PROB, run_ce_dlogits(st, prec, c->P, b, V, c->ce_w, c->pmax, c->ce_nrec, c->lse, c->tok_tgt,
@@ -429,7 +448,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
     RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, bd, b, d, c->dH, c->dHb, c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
     // dH^T, read by the W2 gradient
-    check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+    if (train) check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
 
     // a7 block backward, top to bottom
     for (int l = L - 1; l >= 0; --l) {
@@ -439,8 +458,10 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
       if (gelu) {
         RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
                               foc ? B.ResA : nullptr, cA, m, bp));
-        RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
-        RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
+        if (train) {
+          RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
+          RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
+        }
         // the block input gradient is needed below this block, and for the compensation of
         // a rounded n (the lowest block's n = E_in[x] is exact when there is no norm)
         if (l > 0 || (foc && rms)) {
@@ -448,9 +469,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb,
                                            foc ? B.ResN : nullptr, cN, l > 0));
-          if (l > 0) check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+          if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
         }
-      } else {
+      } else if (train) {
         RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
       }
       if (!gelu && foc) {
@@ -467,8 +488,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t tokpos) {
         }
       }
     }
-    if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, b, (float)b, c->losses + tokpos));
+    if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, b, (float)b, loss_out));
   }
+  if (!train) return;
 
   // a8 global grad norm and clip scale; a9 update
   RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx, c->err));
@@ -537,6 +559,41 @@ void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out)
                    c->dec_tok + c->npend + 1, c->losses + c->pos, c->amax + c->pos, am_out));
 }
 
+// Losses of a passage q (nq + 1 ids, nq a multiple of b) at the current weights, chunk by
+// chunk, without any step; their fp64 sum lands in acc[0], and the losses / their mean in the
+// caller's buffers when given.
+void evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, double* acc, float* losses, float* mean) {
+  const int b = c->b;
+  for (int64_t i = 0; i < nq; i += b) {
+    run_chunk(c, q + i, c->eval_loss, c->eval_amax, false, 0);
+    check(run_eval_accum(c->st, c->eval_loss, b, acc, losses ? losses + i : nullptr, i == 0, i + b >= nq, nq,
+                         mean));
+  }
+}
+
+// Copy the state a step changes (D, Wop, WtT of every fast tensor) into the snapshot, or back.
+void copy_state(ttt_ctx* c, bool to_snapshot) {
+  aux_join(c);  // no step may still be writing the state
+  for (FastTensor* f : c->fast) {
+    const int64_t n = (int64_t)f->rows * f->cols;
+    if (!f->snapD) {
+      f->snapD = dalloc<char>(c, n * 4);
+      f->snapWop = dalloc<char>(c, n * c->es);
+      f->snapWtT = dalloc<char>(c, n * c->es);
+    }
+    const hipMemcpyKind k = hipMemcpyDeviceToDevice;
+    if (to_snapshot) {
+      check(hipMemcpyAsync(f->snapD, f->D, n * 4, k, c->st));
+      check(hipMemcpyAsync(f->snapWop, f->Wop, n * c->es, k, c->st));
+      check(hipMemcpyAsync(f->snapWtT, f->WtT, n * c->es, k, c->st));
+    } else {
+      check(hipMemcpyAsync(f->D, f->snapD, n * 4, k, c->st));
+      check(hipMemcpyAsync(f->Wop, f->snapWop, n * c->es, k, c->st));
+      check(hipMemcpyAsync(f->WtT, f->snapWtT, n * c->es, k, c->st));
+    }
+  }
+}
+
 ttt_status read_sticky(ttt_ctx* c) {
   int e = 0;
   check(hipMemcpyAsync(&e, c->err, 4, hipMemcpyDeviceToHost, c->st));
@@ -597,7 +654,8 @@ ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_token
   if (n_tokens <= 0 || n_tokens % c->b || c->npend != 0) return TTT_EINVAL;
   if (c->pos + n_tokens > c->cfg.max_tokens) return TTT_EINVAL;
   try {
-    for (int64_t i = 0; i < n_tokens; i += c->b) run_chunk(c, tokens + i, c->pos + i);
+    for (int64_t i = 0; i < n_tokens; i += c->b)
+      run_chunk(c, tokens + i, c->losses + c->pos + i, c->amax + c->pos + i, true, (c->pos + i) / c->b);
   } catch (const HipFail& f) {
     c->sticky = f.s;
     return f.s;
@@ -618,7 +676,7 @@ ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* arg
       c->pos += 1;
       if (++c->npend == c->b) {
         // the decoded tokens fill a mini-batch: its step, as in prefill ([E2E] section 3.2)
-        run_chunk(c, c->dec_tok, c->pos - c->b);
+        run_chunk(c, c->dec_tok, c->losses + c->pos - c->b, c->amax + c->pos - c->b, true, (c->pos - c->b) / c->b);
         c->npend = 0;
         aux_join(c);
       }
@@ -631,6 +689,71 @@ ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* arg
 }
 
 int64_t ttt_decode_pending(const ttt_ctx* c) { return c ? c->npend : -1; }
+
+ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses, float* mean) {
+  if (!c || !q || nq <= 0 || nq % c->b) return TTT_EINVAL;
+  if (c->sticky != TTT_OK) return TTT_ESTATE;
+  try {
+    evaluate(c, q, nq, c->eval_acc, losses, mean);
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  return TTT_OK;
+}
+
+ttt_status ttt_snapshot(ttt_ctx* c) {
+  if (!c) return TTT_EINVAL;
+  if (c->sticky != TTT_OK) return TTT_ESTATE;
+  try {
+    copy_state(c, true);
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  c->has_snap = true;
+  return TTT_OK;
+}
+
+ttt_status ttt_restore(ttt_ctx* c) {
+  if (!c) return TTT_EINVAL;
+  if (c->sticky != TTT_OK || !c->has_snap) return TTT_ESTATE;
+  try {
+    copy_state(c, false);
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  return TTT_OK;
+}
+
+ttt_status ttt_settle_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
+                            int32_t* committed) {
+  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0) return TTT_EINVAL;
+  if (c->sticky != TTT_OK) return TTT_ESTATE;
+  if (c->pos + c->b > c->cfg.max_tokens) return TTT_EINVAL;
+  try {
+    evaluate(c, q, nq, c->eval_acc + 1, nullptr, nullptr);  // L(q, W)
+    copy_state(c, true);
+    c->has_snap = true;
+    // the candidate chunk: scored at W and stepped to W + delta, as in prefill
+    run_chunk(c, tokens, c->losses + c->pos, c->amax + c->pos, true, c->pos / c->b);
+    evaluate(c, q, nq, c->eval_acc + 2, nullptr, nullptr);  // L(q, W + delta)
+    check(run_settle_decide(c->st, c->eval_acc + 1, nq, c->settle_A, c->settle_commit, A, committed));
+    aux_join(c);
+    for (FastTensor* f : c->fast) {
+      const int64_t n = (int64_t)f->rows * f->cols;
+      check(run_restore_unless(c->st, c->settle_commit, f->snapD, f->D, n * 4));
+      check(run_restore_unless(c->st, c->settle_commit, f->snapWop, f->Wop, n * c->es));
+      check(run_restore_unless(c->st, c->settle_commit, f->snapWtT, f->WtT, n * c->es));
+    }
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  c->pos += c->b;
+  return TTT_OK;
+}
 
 ttt_status ttt_sync(ttt_ctx* c) {
   if (!c) return TTT_EINVAL;

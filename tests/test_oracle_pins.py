@@ -398,6 +398,59 @@ def test_pins_catch_decode_stepping_one_token_late():
     assert abs(late[3] - pre.losses[3]) > 1e-6
 
 
+# ------------------------------------------------------------------ P13/P14 Settlement
+@pytest.mark.parametrize("mlp,norm", COMBOS)
+def test_p13_settlement_gain_is_first_order_descent(mlp, norm):
+    """With the candidate's own text as the passage and no clipping, W + delta = W - eta G with
+    G = grad L(q, W), so A(delta; W, q) = L(q, W) - L(q, W - eta G) = eta ||G||^2 + O(eta^2):
+    A / eta tends to ||G||^2 (calculus, [SGF] Settlement's A), and the step is kept."""
+    model = tiny_model(mlp, norm, L=2, b=4, lr=1.0, clip=0.0)
+    P = O.as_f64(tiny_params(model, seed=31))
+    cand = tiny_tokens(model, 4, seed=32)
+    _, _, G = O.chunk_loss_and_grads(model, P, cand[:-1], cand[1:])
+    g2 = sum(float(np.sum(G[k] ** 2)) for k in model.fast_keys())
+    errs = []
+    for eta in (1e-3, 5e-4):
+        m = O.Model(**{**model.__dict__, "lr": eta})
+        A, keep, _, _, _ = O.settle_step(m, P, cand, cand)
+        assert keep
+        errs.append(abs(A / eta - g2) / g2)
+    assert errs[1] < errs[0] and errs[1] < 5e-3  # the O(eta) remainder halves with eta
+
+
+def test_p14_settlement_keeps_or_restores_exactly():
+    """A >= 0 keeps exactly the prefill step; A < 0 leaves W untouched (the rule's two branches)."""
+    model = tiny_model("gelu", "rms", L=2, b=4, lr=0.5, clip=0.0)
+    P = O.as_f64(tiny_params(model, seed=33))
+    cand = tiny_tokens(model, 4, seed=34)
+    kept, rejected = 0, 0
+    for seed in range(35, 47):
+        q = tiny_tokens(model, 8, seed=seed)
+        A, keep, Wn, g, s = O.settle_step(model, P, cand, q)
+        direct = O.passage_loss(model, P, q) - O.passage_loss(model, {**P, **Wn}, q)
+        if keep:
+            kept += 1
+            step = O.run_ttt(model, P, cand)
+            for k in model.fast_keys():
+                np.testing.assert_allclose(Wn[k], step.weights[k], rtol=1e-12, atol=1e-14)
+            assert direct == pytest.approx(A, abs=1e-12)
+        else:
+            rejected += 1
+            for k in model.fast_keys():
+                assert np.array_equal(Wn[k], P[k])
+            assert A < 0 and direct == 0.0
+    assert kept > 0 and rejected > 0
+
+
+def test_pins_catch_settlement_sign_slip():
+    """A written as L(q, W + delta) - L(q, W) fails P13 (the own-text step would be rejected)."""
+    model = tiny_model("gelu", "none", L=1, b=4, lr=1e-3, clip=0.0)
+    P = O.as_f64(tiny_params(model, seed=48))
+    cand = tiny_tokens(model, 4, seed=49)
+    A, keep, _, _, _ = O.settle_step(model, P, cand, cand)
+    assert keep and A > 0 and not (-A >= 0.0)
+
+
 # ------------------------------------------------------------------ non-finite chunk is skipped
 def test_nonfinite_gradient_skips_update():
     model = tiny_model("gelu", "none", L=1, b=2, lr=0.3)
