@@ -190,7 +190,7 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
     }
     if cpu:
         import oracle as O
-        n = 4
+        n = 32
         model = O.Model.from_workload(w)
         t0 = time.perf_counter()
         O.decode_ttt(model, P, ids[:n + 1])
@@ -205,6 +205,54 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
     return out
 
 
+def fwd_flops_per_token(w) -> float:
+    """Algorithmic flops of one token's forward pass (the blocks and the LM head)."""
+    d, m, L, V = w.d_model, w.d_hidden, w.n_blocks, w.vocab
+    blocks = (4 if w.mlp == "gelu" else 6) * d * m * L
+    return float(blocks + 2 * V * d)
+
+
+def settle_bench(ctx, w, x, P, cpu: bool, n: int = 3) -> dict:
+    """The Settlement rule on one candidate chunk with a one-chunk held-out passage, timed over
+    n settlements after a warm-up one: two passage evaluations and one training chunk each."""
+    import numpy as np
+    import torch
+    b = w.chunk
+    cand = torch.from_numpy(x[:b + 1].astype(np.int32)).cuda()
+    q = torch.from_numpy(x[b:2 * b + 1].astype(np.int32)).cuda()
+    ctx.settle(cand, q)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        ctx.settle(cand, q)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    flops = 2 * b * fwd_flops_per_token(w) + b * alg_flops_per_token(w)
+    achieved = flops / dt / 1e12
+    peak = (PEAK_BF16 if w.precision == "bf16" else PEAK_FP32) / 1e12
+    out = {
+        "metric": "Settlement candidates/s (one candidate chunk, one-chunk held-out passage)",
+        "value": 1.0 / dt, "unit": "candidates/s", "ms_per_candidate": dt * 1e3, "candidates": n,
+        "roofline": {"bound": "mfma", "kernel": "whole rule (2 passage evaluations + 1 training chunk)",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None, "alg_flops_per_candidate": flops},
+    }
+    if cpu:
+        import oracle as O
+        model = O.Model.from_workload(w)
+        t0 = time.perf_counter()
+        O.settle_step(model, P, x[:b + 1], x[b:2 * b + 1])
+        cdt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:
+            threads = os.cpu_count() or 1
+        out["cpu_baseline"] = {"value": 1.0 / cdt, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"one candidate at the same shape, fp64 numpy, {cdt:.1f} s"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,9 +261,10 @@ def main():
     ap.add_argument("--workload", default="s760m")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-chunks", type=int, default=2)
+    ap.add_argument("--cpu-chunks", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-settle", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -324,6 +373,8 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = decode_bench(ctx, w, x, P, cpu=not args.no_cpu_baseline)
+    if not args.no_settle:
+        out["settle"] = settle_bench(ctx, w, x, P, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         eprint(f"[bench] timing the fp64 oracle on {args.cpu_chunks} chunks ...")
         out["cpu_baseline"] = cpu_baseline(w, P, x, args.cpu_chunks)
