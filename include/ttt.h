@@ -104,6 +104,32 @@ typedef struct {
  * Errors: TTT_EINVAL (config), TTT_ENOMEM, TTT_EDEVICE. On error *out is NULL. */
 ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out);
 
+/* Largest number of streams of one batched context. */
+#define TTT_MAX_STREAMS 4096
+
+/* Create a context that advances `streams` independent token streams together ([SGF], How
+ * it works: several sequences are adapted side by side, each stream from the same initial
+ * weights with its own fast weights and its own clipped step per chunk). The frozen weights
+ * and W0 are stored once; each stream has its own fast state D, records (losses, argmax,
+ * chunk statistics) and clip. Every result of a stream equals that of a single-stream
+ * context fed the same tokens, up to the summation order of products that now cover all
+ * streams' rows. One chunk step covers all streams: the products with a stream's own fast
+ * weights run as grouped launches, those with frozen weights (LM head, CE backward) once
+ * over the streams' stacked rows. Each stream beyond the first costs 10 bytes (bf16) or 16
+ * bytes (fp32) per fast parameter (D, Wop, WtT, G) and its share of the per-token buffers
+ * (the largest, the CE numerators, chunk x vocab elements).
+ * streams in [1, TTT_MAX_STREAMS]; with streams > 1 the chunk size must be a multiple of
+ * 64 and streams * chunk at most 2^21. ttt_create(...) is ttt_create_batch(..., 1, ...).
+ * A batched context (streams > 1) supports ttt_prefill_batch, the ttt_stream_* readers, the
+ * stream-0 readers, ttt_reset, ttt_sync, the profiling calls and ttt_destroy; ttt_prefill_chunks,
+ * ttt_decode, ttt_evaluate, ttt_snapshot, ttt_restore and ttt_settle_chunk return TTT_EINVAL.
+ * Errors: as ttt_create. */
+ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t streams, void* stream,
+                            ttt_ctx** out);
+
+/* Number of streams of the context (-1 for NULL). */
+int32_t ttt_streams(const ttt_ctx* ctx);
+
 /* Run the inner loop over n_tokens new tokens ([E2E] Method: prefill; section 3 eq. 5).
  * tokens: device int32 [n_tokens + 1]; tokens[0] conditions the first prediction (BOS on
  *         the first call, else the previous call's last token); tokens[1..n_tokens] are
@@ -112,6 +138,13 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
  * capacity (max_tokens - tokens already consumed). Enqueued; returns immediately.
  * Errors (nothing enqueued): TTT_EINVAL, TTT_ESTATE. */
 ttt_status ttt_prefill_chunks(ttt_ctx* ctx, const int32_t* tokens, int64_t n_tokens);
+
+/* ttt_prefill_chunks for every stream of the context at once: tokens is device int32
+ * [streams x ld_tokens], row z holding stream z's n_tokens + 1 ids (as for
+ * ttt_prefill_chunks); ld_tokens >= n_tokens + 1 when streams > 1 (ignored for one stream).
+ * Chunk i of every stream is computed in one step, the streams' chunks in lockstep; the
+ * streams never exchange data. Enqueued. Errors (nothing enqueued): TTT_EINVAL, TTT_ESTATE. */
+ttt_status ttt_prefill_batch(ttt_ctx* ctx, const int32_t* tokens, int64_t ld_tokens, int64_t n_tokens);
 
 /* Decode n tokens one at a time ([E2E] Method: decoding predicts the next token's
  * distribution from the current weights; section 3.2: a gradient step is taken only when
@@ -183,7 +216,14 @@ ttt_status ttt_chunk_stats(ttt_ctx* ctx, float* dst, int64_t offset, int64_t n);
  * Errors: TTT_EINVAL (block/which/kind). */
 ttt_status ttt_fast_weights(ttt_ctx* ctx, int32_t block, int32_t which, int32_t kind, float* dst);
 
-/* Restore W = W0, forget recorded losses, and clear a sticky error. Enqueued. */
+/* The readers above for stream s of the context (the ones above read stream 0). Errors as
+ * there, and TTT_EINVAL for s outside [0, streams). */
+ttt_status ttt_stream_token_losses(ttt_ctx* ctx, int32_t s, float* dst, int64_t offset, int64_t n);
+ttt_status ttt_stream_token_argmax(ttt_ctx* ctx, int32_t s, int32_t* dst, int64_t offset, int64_t n);
+ttt_status ttt_stream_chunk_stats(ttt_ctx* ctx, int32_t s, float* dst, int64_t offset, int64_t n);
+ttt_status ttt_stream_fast_weights(ttt_ctx* ctx, int32_t s, int32_t block, int32_t which, int32_t kind, float* dst);
+
+/* Restore W = W0 (every stream), forget recorded losses, and clear a sticky error. Enqueued. */
 ttt_status ttt_reset(ttt_ctx* ctx);
 
 /* Wait for the context's stream; return a pending sticky error if there is one. */

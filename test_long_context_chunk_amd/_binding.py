@@ -28,7 +28,14 @@ KERNEL_KINDS = ["gather", "norm", "transpose", "up", "down", "residual", "ce_fwd
 # Functions declared in include/ttt.h, with their ctypes signatures.
 SIGNATURES = {
     "ttt_create": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
+    "ttt_create_batch": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "ttt_streams": (c_int32, [c_void_p]),
     "ttt_prefill_chunks": (c_int32, [c_void_p, c_void_p, c_int64]),
+    "ttt_prefill_batch": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
+    "ttt_stream_token_losses": (c_int32, [c_void_p, c_int32, c_void_p, c_int64, c_int64]),
+    "ttt_stream_token_argmax": (c_int32, [c_void_p, c_int32, c_void_p, c_int64, c_int64]),
+    "ttt_stream_chunk_stats": (c_int32, [c_void_p, c_int32, c_void_p, c_int64, c_int64]),
+    "ttt_stream_fast_weights": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "ttt_token_losses": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
     "ttt_token_argmax": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
     "ttt_chunk_stats": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
@@ -138,16 +145,19 @@ def to_device(a, precision: str, device="cuda"):
 
 
 class TTT:
-    """One context of the library: private fast weights, bound to one HIP stream."""
+    """One context of the library: private fast weights, bound to one HIP stream. With
+    streams > 1, that many independent token streams advanced together (prefill_batch and
+    the readers' `s` argument)."""
 
     def __init__(self, *, vocab: int, d_model: int, d_hidden: int, n_blocks: int, mlp: str,
                  norm: str, precision: str, chunk: int, max_tokens: int, lr: float, clip: float,
-                 rms_eps: float = 1e-6, weights: Dict[str, "object"], stream=None):
+                 rms_eps: float = 1e-6, weights: Dict[str, "object"], stream=None, streams: int = 1):
         import torch
         self._lib = load_library()
         self.vocab, self.d_model, self.d_hidden, self.n_blocks = vocab, d_model, d_hidden, n_blocks
         self.mlp, self.norm, self.precision, self.chunk = mlp, norm, precision, chunk
         self.max_tokens = max_tokens
+        self.streams = streams
         self._stream = stream if stream is not None else torch.cuda.current_stream()
         dt = torch.bfloat16 if precision == "bf16" else torch.float32
         for k, t in weights.items():
@@ -165,8 +175,9 @@ class TTT:
                     ctypes.cast(wup, ctypes.POINTER(c_void_p)) if wup is not None else None,
                     ctypes.cast(w2, ctypes.POINTER(c_void_p)))
         ctx = c_void_p()
-        _check(self._lib.ttt_create(ctypes.byref(cfg), ctypes.byref(w),
-                                    c_void_p(_stream_handle(self._stream)), ctypes.byref(ctx)), "ttt_create")
+        _check(self._lib.ttt_create_batch(ctypes.byref(cfg), ctypes.byref(w), streams,
+                                          c_void_p(_stream_handle(self._stream)), ctypes.byref(ctx)),
+               "ttt_create_batch")
         self._ctx = ctx
 
     @classmethod
@@ -186,6 +197,18 @@ class TTT:
             raise ValueError("tokens must be a contiguous int32 device tensor")
         n = tokens.numel() - 1
         _check(self._lib.ttt_prefill_chunks(self._ctx, c_void_p(_ptr(tokens)), n), "ttt_prefill_chunks")
+
+    def prefill_batch(self, tokens) -> None:
+        """tokens: device int32 [streams x ld] (row z: stream z's n + 1 ids, n = ld - 1); runs
+        n / chunk steps of every stream (enqueued)."""
+        import torch
+        if tokens.dtype != torch.int32 or not tokens.is_cuda or tokens.dim() != 2 or tokens.stride(1) != 1:
+            raise ValueError("tokens must be an int32 device tensor [streams x ld] with unit column stride")
+        if tokens.shape[0] != self.streams:
+            raise ValueError(f"tokens has {tokens.shape[0]} rows for {self.streams} streams")
+        n = tokens.shape[1] - 1
+        _check(self._lib.ttt_prefill_batch(self._ctx, c_void_p(_ptr(tokens)), tokens.stride(0), n),
+               "ttt_prefill_batch")
 
     def decode(self, tokens, want_logits: bool = False):
         """tokens: device int32 [n + 1] (tokens[0] = the stream's last token). Predicts each of
@@ -236,34 +259,38 @@ class TTT:
     def decode_pending(self) -> int:
         return int(self._lib.ttt_decode_pending(self._ctx))
 
-    def token_losses(self, offset: int = 0, n: Optional[int] = None):
+    def token_losses(self, offset: int = 0, n: Optional[int] = None, s: int = 0):
         import torch
         n = self.consumed() - offset if n is None else n
         out = torch.empty(n, dtype=torch.float32, device="cuda")
-        _check_copy(self._lib.ttt_token_losses(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_losses")
+        _check_copy(self._lib.ttt_stream_token_losses(self._ctx, s, c_void_p(_ptr(out)), offset, n),
+                    "ttt_stream_token_losses")
         return out
 
-    def token_argmax(self, offset: int = 0, n: Optional[int] = None):
+    def token_argmax(self, offset: int = 0, n: Optional[int] = None, s: int = 0):
         import torch
         n = self.consumed() - offset if n is None else n
         out = torch.empty(n, dtype=torch.int32, device="cuda")
-        _check_copy(self._lib.ttt_token_argmax(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_token_argmax")
+        _check_copy(self._lib.ttt_stream_token_argmax(self._ctx, s, c_void_p(_ptr(out)), offset, n),
+                    "ttt_stream_token_argmax")
         return out
 
-    def chunk_stats(self, offset: int = 0, n: Optional[int] = None):
+    def chunk_stats(self, offset: int = 0, n: Optional[int] = None, s: int = 0):
         import torch
         n = self.consumed() // self.chunk - offset if n is None else n
         out = torch.empty((n, 2), dtype=torch.float32, device="cuda")
-        _check_copy(self._lib.ttt_chunk_stats(self._ctx, c_void_p(_ptr(out)), offset, n), "ttt_chunk_stats")
+        _check_copy(self._lib.ttt_stream_chunk_stats(self._ctx, s, c_void_p(_ptr(out)), offset, n),
+                    "ttt_stream_chunk_stats")
         return out
 
-    def fast_weight(self, block: int, which: str, kind: str = "W"):
-        """which: "W1" | "W2"; kind: "W" (current) | "delta" (W - W0). fp32 device tensor."""
+    def fast_weight(self, block: int, which: str, kind: str = "W", s: int = 0):
+        """which: "W1" | "W2"; kind: "W" (current) | "delta" (W - W0); s: stream. fp32 device tensor."""
         import torch
         shape = (self.d_model, self.d_hidden) if which == "W1" else (self.d_hidden, self.d_model)
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
-        _check_copy(self._lib.ttt_fast_weights(self._ctx, block, 1 if which == "W1" else 2,
-                                               0 if kind == "W" else 1, c_void_p(_ptr(out))), "ttt_fast_weights")
+        _check_copy(self._lib.ttt_stream_fast_weights(self._ctx, s, block, 1 if which == "W1" else 2,
+                                                      0 if kind == "W" else 1, c_void_p(_ptr(out))),
+                    "ttt_stream_fast_weights")
         return out
 
     def profile(self, kinds, period: int = 1) -> None:

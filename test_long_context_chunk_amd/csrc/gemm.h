@@ -16,7 +16,9 @@
 //   * workgroups are renumbered so that each XCD (dispatch is round-robin over the 8 XCDs)
 //     receives a contiguous run of tiles: neighbouring tiles share operand slabs in the
 //     same L2;
-//   * optional split-K over gridDim.y; each split hands its partial tile to the epilogue.
+//   * optional split-K over gridDim.y; each split hands its partial tile to the epilogue;
+//   * optional grouping over gridDim.z: independent products of one shape whose operands
+//     sit at fixed strides, with their outputs stacked row-wise (see GemmArgs).
 // The epilogue receives the wave's accumulators and their coordinates:
 //   acc[i][j][e] holds C[row0 + 16 i + 4 (lane / 16) + e][col0 + 16 j + lane % 16].
 #pragma once
@@ -36,7 +38,45 @@ struct GemmArgs {
   int kit_a;   // K-iterations (of 128 bytes) of the first segment
   int kiters;  // K-iterations of both segments
   int kps;     // K-iterations per split
+  // Grouped launch: gridDim.z independent products of this shape. Product z reads its
+  // operands at z * (gx, gy, gx2, gy2) elements past X, Y, X2, Y2 (0: shared by every
+  // product), and its epilogue sees stacked coordinates: rows z * M + i (bound (z + 1) * M)
+  // and tile ids z * gtile + t.
+  int64_t gx, gy, gx2, gy2;
+  int gtile;
 };
+
+// Which product, split and output tile a workgroup computes. The linear workgroup index is
+// renumbered so that consecutive ids share an XCD (a bijection of [0, nblk); correctness
+// never depends on it); products vary slowest, then splits, then tiles.
+struct GemmWork {
+  int z, split, tile;
+};
+__device__ __forceinline__ GemmWork gemm_work(const GemmArgs& g) {
+  const int nblk = gridDim.x * gridDim.y * gridDim.z;
+  const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int xcd = lin & 7;
+  int id = xcd * per + min(xcd, rem) + (lin >> 3);
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int pz = ntiles * gridDim.y;
+  GemmWork w;
+  w.z = id / pz;
+  id -= w.z * pz;
+  w.split = id / ntiles;
+  w.tile = id - w.split * ntiles;
+  return w;
+}
+
+// Operand bases of product z.
+template <class T>
+__device__ __forceinline__ void gemm_group_bases(const GemmArgs& g, int z, const char*& X, const char*& Y,
+                                                 const char*& X2, const char*& Y2) {
+  X = (const char*)g.X + (int64_t)z * g.gx * (int64_t)sizeof(T);
+  Y = (const char*)g.Y + (int64_t)z * g.gy * (int64_t)sizeof(T);
+  X2 = (const char*)g.X2 + (int64_t)z * g.gx2 * (int64_t)sizeof(T);
+  Y2 = (const char*)g.Y2 + (int64_t)z * g.gy2 * (int64_t)sizeof(T);
+}
 
 struct EpiPos {
   int row0, col0;  // global coordinates of this wave's sub-tile
@@ -71,25 +111,20 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // XCD-aware renumbering (a bijection of [0, nblk); correctness never depends on it).
-  const int nblk = gridDim.x * gridDim.y;
-  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int xcd = lin & 7;
-  const int id = xcd * per + min(xcd, rem) + (lin >> 3);
-  const int ntiles = g.tiles_m * g.tiles_n;
-  const int split = id / ntiles;
-  const int tile = id - split * ntiles;
+  const GemmWork w = gemm_work(g);
+  const int split = w.split, tile = w.tile;
   const int tm = tile % g.tiles_m, tn = tile / g.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kit0 = split * g.kps;
   const int kit1 = min(g.kiters, kit0 + g.kps);
 
   const int lrow = tid >> 3, lch = tid & 7;
-  const char* __restrict__ Xp = (const char*)g.X;
-  const char* __restrict__ Yp = (const char*)g.Y;
-  const char* __restrict__ X2p = (const char*)g.X2;
-  const char* __restrict__ Y2p = (const char*)g.Y2;
+  const char *Xb, *Yb, *X2b, *Y2b;
+  gemm_group_bases<T>(g, w.z, Xb, Yb, X2b, Y2b);
+  const char* __restrict__ Xp = Xb;
+  const char* __restrict__ Yp = Yb;
+  const char* __restrict__ X2p = X2b;
+  const char* __restrict__ Y2p = Y2b;
   uint4 ra[BM / 32], rb[BN / 32];
 
   auto gload = [&](int kit) {
@@ -163,7 +198,7 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
   }
 
   EpiPos pos;
-  pos.row0 = m0 + wm * WTM;
+  pos.row0 = w.z * g.M + m0 + wm * WTM;
   pos.col0 = n0 + wn * WTN;
   pos.lane = lane;
   pos.wave = wave;
@@ -178,9 +213,9 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
   pos.smem_bytes = 2 * STAGE;
   pos.tm = tm;
   pos.tn = tn;
-  pos.tile = tile;
+  pos.tile = w.z * g.gtile + tile;
   pos.split = split;
-  pos.M = g.M;
+  pos.M = (w.z + 1) * g.M;
   pos.N = g.N;
   pos.smem = smem;
   epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
@@ -430,14 +465,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  const int nblk = gridDim.x * gridDim.y;
-  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int xcd = lin & 7;
-  const int id = xcd * per + min(xcd, rem) + (lin >> 3);
-  const int ntiles = g.tiles_m * g.tiles_n;
-  const int split = id / ntiles;
-  const int tile = id - split * ntiles;
+  const GemmWork w = gemm_work(g);
+  const int split = w.split, tile = w.tile;
   const int tm = tile % g.tiles_m, tn = tile / g.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kit0 = split * g.kps;
@@ -448,6 +477,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int rsub = lane >> 3;
   const bool has2 = g.kiters > g.kit_a;
+  const char *gX, *gY, *gX2, *gY2;
+  gemm_group_bases<T>(g, w.z, gX, gY, gX2, gY2);
   const char* p1[PW];
   const char* p2[PW];
 #pragma unroll
@@ -458,8 +489,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
     const int r = xs ? min(m0 + t, g.M - 1) : min(n0 + t - BM, g.N - 1);
     // lane L writes physical chunk L & 7 of row t; it loads logical chunk (L & 7) ^ swz(t)
     const int cbyte = ((lane & 7) ^ lds_swz<use_mfma32<T, BM, BN, WGM, WGN>()>(t)) << 4;
-    const char* const b1 = (const char*)(xs ? g.X : g.Y);
-    const char* const b2 = (const char*)(xs ? g.X2 : g.Y2);
+    const char* const b1 = xs ? gX : gY;
+    const char* const b2 = xs ? gX2 : gY2;
     const int64_t l1 = (xs ? g.ldx : g.ldy) * (int64_t)sizeof(T);
     const int64_t l2 = (xs ? g.ldx2 : g.ldy2) * (int64_t)sizeof(T);
     p1[q] = b1 + (int64_t)r * l1 + cbyte;
@@ -519,7 +550,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   }
 
   EpiPos pos;
-  pos.row0 = m0 + wm * WTM;
+  pos.row0 = w.z * g.M + m0 + wm * WTM;
   pos.col0 = n0 + wn * WTN;
   pos.lane = lane;
   pos.wave = wave;
@@ -534,9 +565,9 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   pos.smem_bytes = gemm_stages(BM, BN) * STAGE;
   pos.tm = tm;
   pos.tn = tn;
-  pos.tile = tile;
+  pos.tile = w.z * g.gtile + tile;
   pos.split = split;
-  pos.M = g.M;
+  pos.M = (w.z + 1) * g.M;
   pos.N = g.N;
   pos.smem = smem;
   epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
@@ -970,8 +1001,8 @@ struct EpiDU {
   T* DU;         // [M x ld]
   T* DUT;        // [N x ldt]
   const T* RES;  // [M x ld] or null
-  float* cdot;   // [tiles_n x M] or null
-  int64_t ld, ldt;
+  float* cdot;   // [tiles_n x ldc] or null (ldc >= rows of the stacked output)
+  int64_t ld, ldt, ldc;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float dots[FM][4];
@@ -1027,7 +1058,7 @@ struct EpiDU {
 #pragma unroll
               for (int off = 1; off < TPR; off <<= 1) dot += __shfl_xor(dot, off, TTT_WAVE);
             }
-            if ((p.tid % TPR) == 0) cdot[(int64_t)p.tn * p.M + m0 + r] = dot;
+            if ((p.tid % TPR) == 0) cdot[(int64_t)p.tn * ldc + m0 + r] = dot;
           }
         }
         __syncthreads();
@@ -1058,7 +1089,7 @@ struct EpiDU {
         if (cdot) {
 #pragma unroll
           for (int off = 1; off < 32; off <<= 1) dot += __shfl_xor(dot, off, TTT_WAVE);
-          if ((p.lane & 31) == 0 && gr < p.M) cdot[(int64_t)p.tn * p.M + gr] = dot;
+          if ((p.lane & 31) == 0 && gr < p.M) cdot[(int64_t)p.tn * ldc + gr] = dot;
         }
       }
       __syncthreads();
@@ -1087,7 +1118,7 @@ struct EpiDU {
         store4_t<T>(DUT + (int64_t)col * ldt + r0, v[0], v[1], v[2], v[3], nv);
       }
     }
-    if (cdot) row_partial_store<FM>(p, dots, cdot, p.M);
+    if (cdot) row_partial_store<FM>(p, dots, cdot, ldc);
   }
 };
 
@@ -1101,8 +1132,8 @@ struct EpiSwigluBwd {
   T* DG;
   T* DV;
   const T* RES;
-  float* cdot;
-  int64_t ld;
+  float* cdot;  // [tiles_n x ldc]
+  int64_t ld, ldc;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     float dots[FM][4];
@@ -1126,7 +1157,7 @@ struct EpiSwigluBwd {
           dots[i][e] += da * to_f<T>(RES[o]);
         }
       }
-    row_partial_store<FM>(p, dots, cdot, p.M);
+    row_partial_store<FM>(p, dots, cdot, ldc);
   }
 };
 
@@ -1308,8 +1339,16 @@ struct Seg2 {
   int K = 0;
 };
 
+// n products of one shape in one launch (see GemmArgs): per-product operand offsets in
+// elements, and the tile-id stride of their epilogues.
+struct Group {
+  int n = 1;
+  int64_t x = 0, y = 0, x2 = 0, y2 = 0;
+  int tile = 0;
+};
+
 template <class T, int BM, int BN, int WGM, int WGN, class Epi>
-inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, const Epi& epi) {
+inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, int groups, const Epi& epi) {
   constexpr size_t lds = (size_t)gemm_stages(BM, BN) * (BM + BN) * 128;
   auto kern = gemm_dma_kernel<T, BM, BN, WGM, WGN, Epi>;
   static bool lds_attr = false;  // per instantiation
@@ -1318,7 +1357,7 @@ inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, cons
     if (e != hipSuccess) return e;
     lds_attr = true;
   }
-  dim3 grid(g.tiles_m * g.tiles_n, splits);
+  dim3 grid(g.tiles_m * g.tiles_n, splits, groups);
   hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, g, epi);
   return hipGetLastError();
 }
@@ -1359,8 +1398,10 @@ inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
 // (at least one 256 x 256 tile per CU) use 256 x 256 tiles with 8 waves; the rest 128 x 128.
 template <class T, class Epi>
 inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                              int K, int splits, const Epi& epi, const Seg2& s2 = Seg2()) {
-  if (M <= 0 || N <= 0) return hipSuccess;
+                              int K, int splits, const Epi& epi, const Seg2& s2 = Seg2(),
+                              const Group& gr = Group()) {
+  if (M <= 0 || N <= 0 || gr.n <= 0) return hipSuccess;
+  if (gr.n > 65535) return hipErrorInvalidValue;
   constexpr int KE = 128 / (int)sizeof(T);
   if (splits < 1) splits = 1;
   GemmArgs g;
@@ -1378,6 +1419,11 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
   g.K2 = s2.K;
   g.kit_a = (K + KE - 1) / KE;
   g.kiters = g.kit_a + (s2.K + KE - 1) / KE;
+  g.gx = gr.x;
+  g.gy = gr.y;
+  g.gx2 = s2.K > 0 ? gr.x2 : 0;
+  g.gy2 = s2.K > 0 ? gr.y2 : 0;
+  g.gtile = gr.tile;
   const TilePlan plan = gemm_plan(M, N, K, s2.K, (int)sizeof(T), splits);
   if (plan.dma) {
     if constexpr (sizeof(T) == 2) {
@@ -1385,13 +1431,13 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
         g.tiles_m = (M + 255) / 256;
         g.tiles_n = (N + 127) / 128;
         g.kps = (g.kiters + splits - 1) / splits;
-        return launch_dma<T, 256, 128, 4, 2>(st, g, splits, epi);
+        return launch_dma<T, 256, 128, 4, 2>(st, g, splits, gr.n, epi);
       }
       if (plan.bm == 192) {
         g.tiles_m = (M + 191) / 192;
         g.tiles_n = (N + 191) / 192;
         g.kps = (g.kiters + splits - 1) / splits;
-        return launch_dma<T, 192, 192, 2, 2>(st, g, splits, epi);
+        return launch_dma<T, 192, 192, 2, 2>(st, g, splits, gr.n, epi);
       }
     }
     if constexpr (sizeof(T) == 4) {
@@ -1399,20 +1445,20 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
         g.tiles_m = (M + 255) / 256;
         g.tiles_n = (N + 255) / 256;
         g.kps = g.kiters;
-        return launch_dma<T, 256, 256, 2, 4>(st, g, 1, epi);
+        return launch_dma<T, 256, 256, 2, 4>(st, g, 1, gr.n, epi);
       }
     }
     {
       g.tiles_m = (M + 127) / 128;
       g.tiles_n = (N + 127) / 128;
       g.kps = (g.kiters + splits - 1) / splits;
-      return launch_dma<T, 128, 128, 2, 2>(st, g, splits, epi);
+      return launch_dma<T, 128, 128, 2, 2>(st, g, splits, gr.n, epi);
     }
   }
   g.tiles_m = (M + 127) / 128;
   g.tiles_n = (N + 127) / 128;
   g.kps = (g.kiters + splits - 1) / splits;
-  dim3 grid(g.tiles_m * g.tiles_n, splits);
+  dim3 grid(g.tiles_m * g.tiles_n, splits, gr.n);
   hipLaunchKernelGGL((gemm_reg_kernel<T, 128, 128, Epi>), grid, dim3(256), 0, st, g, epi);
   return hipGetLastError();
 }

@@ -15,6 +15,16 @@
   } while (0)
 
 namespace {
+inline Group grp(const GemmGroup& g) {
+  Group r;
+  r.n = g.n;
+  r.x = g.x;
+  r.y = g.y;
+  r.x2 = g.x2;
+  r.y2 = g.y2;
+  r.tile = g.tile;
+  return r;
+}
 inline Seg2 seg(const GemmSeg2& s) {
   Seg2 r;
   r.X = s.X;
@@ -28,16 +38,17 @@ inline Seg2 seg(const GemmSeg2& s) {
 
 hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                     int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate,
-                    const GemmSeg2& s2) {
+                    const GemmSeg2& s2, const GemmGroup& gg) {
   EpiStoreF32 e{C, ldc, split_stride, accumulate};
-  DISPATCH_T(prec, return (launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, splits, e, seg(s2))));
+  DISPATCH_T(prec, return (launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, splits, e, seg(s2), grp(gg))));
 }
 
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat, const GemmSeg2& s2) {
+                     int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat, const GemmSeg2& s2,
+                     const GemmGroup& gg) {
   DISPATCH_T(prec, {
     EpiGelu<T> e{(T*)A, (T*)AT, (T*)GP, (T*)RES, lda, ldat};
-    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2), grp(gg));
   });
 }
 
@@ -50,19 +61,20 @@ hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, con
 }
 
 hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                   int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt) {
+                   int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt,
+                   int64_t ldc, const GemmGroup& gg) {
   DISPATCH_T(prec, {
-    EpiDU<T> e{(const T*)GP, (T*)DU, (T*)DUT, (const T*)RES, cdot, ld, ldt};
-    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    EpiDU<T> e{(const T*)GP, (T*)DU, (T*)DUT, (const T*)RES, cdot, ld, ldt, ldc};
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, Seg2(), grp(gg));
   });
 }
 
 hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const float* UG, const float* VU, void* DG, void* DV, const void* RES,
-                           float* cdot, int64_t ld) {
+                           float* cdot, int64_t ld, int64_t ldc, const GemmGroup& gg) {
   DISPATCH_T(prec, {
-    EpiSwigluBwd<T> e{UG, VU, (T*)DG, (T*)DV, (const T*)RES, cdot, ld};
-    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    EpiSwigluBwd<T> e{UG, VU, (T*)DG, (T*)DV, (const T*)RES, cdot, ld, ldc};
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, Seg2(), grp(gg));
   });
 }
 
@@ -89,10 +101,10 @@ int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits) {
 }
 
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, void* G, int64_t ldg, float* slot) {
+                     int K, void* G, int64_t ldg, float* slot, const GemmGroup& gg) {
   DISPATCH_T(prec, {
     EpiGrad<T> e{(T*)G, ldg, slot};
-    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, Seg2(), grp(gg));
   });
 }
 

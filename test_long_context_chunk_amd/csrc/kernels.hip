@@ -60,7 +60,8 @@ __device__ __forceinline__ float4 rounded4(const float4 v) {
 // also block l's pre-norm n = h (mean h^2 + eps)^(-1/2) (rms; none: n = h) as rn(n), its
 // scale r, and when RES is given the rounding residual n - rn(n).
 template <class T>
-__global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, int V, const T* __restrict__ E,
+__global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, StreamRows sr, int V,
+                                               const T* __restrict__ E,
                                                int* __restrict__ tok_prev, int* __restrict__ tok_tgt,
                                                int* __restrict__ err, const float* __restrict__ part, int S,
                                                int64_t pstride, float* __restrict__ H, int d, T* __restrict__ Yb,
@@ -71,7 +72,9 @@ __global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, i
   const int64_t base = (int64_t)t * d;
   const T* src = nullptr;
   if (tokens) {
-    int xp = tokens[t], xt = tokens[t + 1];
+    const int z = t / sr.bs;
+    const int* tk = tokens + z * sr.ld + (t - z * sr.bs);
+    int xp = tk[0], xt = tk[1];
     const bool bad = (xp < 0 || xp >= V || xt < 0 || xt >= V);
     if (xp < 0 || xp >= V) xp = 0;
     if (xt < 0 || xt >= V) xt = 0;
@@ -288,11 +291,12 @@ __global__ void __launch_bounds__(NT) k_transpose(const T* __restrict__ src, int
 }
 
 // Add the first-order rounding compensation to the recorded losses:
-//   l_t += scale * sum_s cpart[s * b + t]   (fixed order).
+//   l_t += scale * sum_s cpart[s * b + t]   (fixed order; b rows of all streams, the loss of
+// row t at its stream's record).
 // 16 tokens per block; the 16 threads of a token sum interleaved slots, then combine in a
 // fixed butterfly order.
-__global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ cpart, int nslot, int b, float scale,
-                                                     float* __restrict__ loss) {
+__global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ cpart, int nslot, int b, StreamRows sr,
+                                                     float scale, float* __restrict__ loss) {
   const int t = blockIdx.x * 16 + (threadIdx.x & 15);
   const int part = threadIdx.x >> 4;  // 0..15
   float acc = 0.f;
@@ -305,13 +309,13 @@ __global__ void __launch_bounds__(NT) k_loss_correct(const float* __restrict__ c
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane < 16) red[wave][lane] = acc;
   __syncthreads();
-  if (threadIdx.x < 16 && t < b) loss[t] += scale * ((red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]));
+  if (threadIdx.x < 16 && t < b) loss[sr.ld * (t / sr.bs) + t % sr.bs] += scale * ((red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]));
 }
 
 // a5 merge: combine the (max, sum exp, argmax) records of each row in a fixed order:
 // lse = M + ln S, l_t = lse - z_t[x_t] ([E2E] eq. 1), argmax (lowest index).
 __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax, const float* __restrict__ psum,
-                                                 const int* __restrict__ pidx, int nrec, int b,
+                                                 const int* __restrict__ pidx, int nrec, int b, StreamRows sr,
                                                  const float* __restrict__ tgt_logit, float* __restrict__ lse,
                                                  float* __restrict__ loss, int* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
@@ -333,17 +337,23 @@ __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax,
   if (lane == 0) {
     const float l = mx + logf(sm);
     lse[row] = l;
-    loss[row] = l - tgt_logit[row];
-    amax[row] = ix;
+    const int64_t o = sr.ld * (row / sr.bs) + row % sr.bs;
+    loss[o] = l - tgt_logit[row];
+    amax[o] = ix;
   }
 }
 
 // a8: g = sqrt(sum of the per-tile sums of squares of every fast gradient), in fp64 and a
-// fixed order; s = min(1, clip / g) (clip <= 0: 1); a non-finite g skips the step.
+// fixed order; s = min(1, clip / g) (clip <= 0: 1); a non-finite g skips the step. One block
+// per stream: stream z's slots, scale pair and statistics pair start at z * nslot, 4 z and
+// z * stat_ld.
 __global__ void __launch_bounds__(NT) k_gradnorm(const float* __restrict__ slot, int nslot, float clip,
-                                                 float* __restrict__ sc, float* __restrict__ stat,
+                                                 float* __restrict__ sc, float* __restrict__ stat, int64_t stat_ld,
                                                  int* __restrict__ err) {
   __shared__ double red[4];
+  slot += (int64_t)blockIdx.x * nslot;
+  sc += 4 * blockIdx.x;
+  stat += stat_ld * blockIdx.x;
   double acc = 0.0;
   for (int i = threadIdx.x; i < nslot; i += NT) acc += (double)slot[i];
   acc = wave_sum_d(acc);
@@ -711,6 +721,15 @@ __global__ void __launch_bounds__(NT) k_update(const T* __restrict__ G, float* _
                                                const T* __restrict__ W0, T* __restrict__ Wop,
                                                T* __restrict__ WtT, int R, int C, float lr,
                                                const float* __restrict__ sc, int delta_t) {
+  // stream blockIdx.z: its own G, D, Wop, WtT (R x C apart) and scale pair; W0 is shared
+  {
+    const int64_t zo = (int64_t)blockIdx.z * R * C;
+    G += zo;
+    D += zo;
+    Wop += zo;
+    WtT += zo;
+    sc += 4 * blockIdx.z;
+  }
   if (sc[1] != 0.f) return;  // non-finite gradient norm: no step for this chunk
   const float step = lr * sc[0];
   __shared__ T tile[64][64 + 16 / sizeof(T)];  // [col][row] of the transposed output
@@ -793,11 +812,11 @@ inline int grid_for(int64_t n) {
     }                                         \
   } while (0)
 
-hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, int V, const void* E, int* tok_prev, int* tok_tgt,
-                      int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb, float eps,
-                      int rms, void* Hn, float* r, void* RES) {
-  if (d % 8) return hipErrorInvalidValue;
-  DISPATCH_T(prec, hipLaunchKernelGGL(k_row_in<T>, dim3(b), dim3(NT), 0, st, tokens, V, (const T*)E, tok_prev, tok_tgt,
+hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, StreamRows sr, int V, const void* E, int* tok_prev,
+                      int* tok_tgt, int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb,
+                      float eps, int rms, void* Hn, float* r, void* RES) {
+  if (d % 8 || sr.bs < 1) return hipErrorInvalidValue;
+  DISPATCH_T(prec, hipLaunchKernelGGL(k_row_in<T>, dim3(b), dim3(NT), 0, st, tokens, sr, V, (const T*)E, tok_prev, tok_tgt,
                                       err, part, S, pstride, H, d, (T*)Yb, eps, rms, (T*)Hn, r, (T*)RES));
   return hipGetLastError();
 }
@@ -816,14 +835,17 @@ hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int
   return hipGetLastError();
 }
 
-hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss) {
-  hipLaunchKernelGGL(k_loss_correct, dim3((b + 15) / 16), dim3(NT), 0, st, cpart, nslot, b, scale, loss);
+hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, StreamRows sr, float scale,
+                            float* loss) {
+  if (sr.bs < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_loss_correct, dim3((b + 15) / 16), dim3(NT), 0, st, cpart, nslot, b, sr, scale, loss);
   return hipGetLastError();
 }
 
 hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int nrec, int b,
-                        const float* tgt_logit, float* lse, float* loss, int* amax) {
-  hipLaunchKernelGGL(k_ce_merge, dim3((b + 3) / 4), dim3(NT), 0, st, pmax, psum, pidx, nrec, b, tgt_logit, lse,
+                        StreamRows sr, const float* tgt_logit, float* lse, float* loss, int* amax) {
+  if (sr.bs < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ce_merge, dim3((b + 3) / 4), dim3(NT), 0, st, pmax, psum, pidx, nrec, b, sr, tgt_logit, lse,
                      loss, amax);
   return hipGetLastError();
 }
@@ -844,14 +866,17 @@ hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int6
   return hipGetLastError();
 }
 
-hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat, int* err) {
-  hipLaunchKernelGGL(k_gradnorm, dim3(1), dim3(NT), 0, st, slot, nslot, clip, sc, stat, err);
+hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat,
+                        int64_t stat_ld, int streams, int* err) {
+  if (streams < 1 || streams > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gradnorm, dim3(streams), dim3(NT), 0, st, slot, nslot, clip, sc, stat, stat_ld, err);
   return hipGetLastError();
 }
 
 hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const void* W0, void* Wop, void* WtT, int R,
-                      int C, float lr, const float* sc, int delta_t) {
-  dim3 grid((C + 63) / 64, (R + 63) / 64);
+                      int C, float lr, const float* sc, int delta_t, int streams) {
+  if (streams < 1 || streams > 65535) return hipErrorInvalidValue;
+  dim3 grid((C + 63) / 64, (R + 63) / 64, streams);
   DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, (const T*)G, D, (const T*)W0, (T*)Wop,
                                       (T*)WtT, R, C, lr, sc, delta_t));
   return hipGetLastError();

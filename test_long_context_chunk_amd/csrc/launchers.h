@@ -8,18 +8,27 @@
 
 enum { PREC_FP32 = 0, PREC_BF16 = 1 };
 
+// Rows of a chunk step that stacks several independent streams: row t is position t % bs of
+// stream t / bs; that stream's per-token records (token ids, losses, argmax) start at
+// (t / bs) * ld. One stream: bs = rows, ld unused.
+struct StreamRows {
+  int bs;
+  int64_t ld;
+};
+
 // ---- row / elementwise kernels (kernels.hip)
 // The residual stream entering a block (gather of the embeddings when tokens is non-null,
 // else H + the split-K slabs part) and, when Hn is non-null, its pre-norm (see k_row_in).
-hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, int V, const void* E, int* tok_prev, int* tok_tgt,
-                      int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb, float eps,
-                      int rms, void* Hn, float* r, void* RES);
+hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, StreamRows sr, int V, const void* E, int* tok_prev,
+                      int* tok_tgt, int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb,
+                      float eps, int rms, void* Hn, float* r, void* RES);
 hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds, int R, int C, void* dst, int64_t ldd);
 hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int b, int d,
                          float* dH, void* dHb, const float* Hres, const void* Yb, float* cdot);
-hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, float scale, float* loss);
+hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b, StreamRows sr, float scale,
+                            float* loss);
 hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int nrec, int b,
-                        const float* tgt_logit, float* lse, float* loss, int* amax);
+                        StreamRows sr, const float* tgt_logit, float* lse, float* loss, int* amax);
 // dlogits in place: Q [b x V] (numerators relative to record max pmax[t][v / W]) becomes
 // P = (Q exp(pmax - lse) - onehot(target)) / b.
 hipError_t run_ce_dlogits(hipStream_t st, int prec, void* Q, int b, int V, int W, const float* pmax, int nrec,
@@ -27,9 +36,12 @@ hipError_t run_ce_dlogits(hipStream_t st, int prec, void* Q, int b, int V, int W
 hipError_t run_norm_bwd(hipStream_t st, int prec, const float* part, int S, int64_t pstride, const void* Hn,
                         const float* r, int b, int d, int rms, float* dH, void* dHb, const void* RES, float* cdot,
                         int update_dh);
-hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat, int* err);
+// One clip scale per stream: stream z reads slot[z nslot ..], writes sc[4 z ..], stat[z stat_ld ..].
+hipError_t run_gradnorm(hipStream_t st, const float* slot, int nslot, float clip, float* sc, float* stat,
+                        int64_t stat_ld, int streams, int* err);
+// One fast tensor of every stream: G, D, Wop, WtT of stream z lie R C elements apart, W0 is shared.
 hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const void* W0, void* Wop, void* WtT, int R,
-                      int C, float lr, const float* sc, int delta_t);
+                      int C, float lr, const float* sc, int delta_t, int streams);
 hipError_t run_export(hipStream_t st, int prec, const float* D, const void* W0, int64_t n, int kind, float* dst);
 hipError_t run_fill_u32(hipStream_t st, void* p, int64_t n, uint32_t v);
 
@@ -85,28 +97,41 @@ struct GemmSeg2 {
   int K = 0;
 };
 
+// n independent products of one shape in one launch. Product z reads X, Y, X2, Y2 at
+// z * (x, y, x2, y2) elements past the given pointers (0: one operand shared by all), and
+// writes its outputs as rows z * M .. z * M + M - 1 of outputs stacked over the products
+// (so every output pointer and leading dimension below describes the stacked [n M x ...]
+// array, and transposed outputs hold product z in columns z * M ..); per-tile slots of
+// product z start at z * tile.
+struct GemmGroup {
+  int n = 1;
+  int64_t x = 0, y = 0, x2 = 0, y2 = 0;
+  int tile = 0;
+};
+
 // Plain fp32 output; split-K partial slab s lands at C + s * split_stride; accumulate adds
 // to the existing values instead of overwriting them.
 hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                     int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate,
-                    const GemmSeg2& s2 = GemmSeg2());
+                    const GemmSeg2& s2 = GemmSeg2(), const GemmGroup& gg = GemmGroup());
 // GELU up-projection epilogue: A = GELU(U) [M x lda], A^T [N x ldat], GELU'(U) [M x lda],
 // and (RES non-null) the rounding residual A - rn(A) [M x lda].
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat,
-                     const GemmSeg2& s2 = GemmSeg2());
+                     const GemmSeg2& s2 = GemmSeg2(), const GemmGroup& gg = GemmGroup());
 // SwiGLU up epilogue: V = X Y^T kept in VU (fp32, may be null), A = SiLU(UG) * V stored as
 // A [M x lda] and A^T [N x ldat], RES as above.
 hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                        int K, const float* UG, float* VU, void* A, void* AT, void* RES, int64_t lda, int64_t ldat);
 // GELU backward epilogue: dU = (X Y^T) * GP, dU [M x ld], dU^T [N x ldt]; with RES, per-token
-// partial dots <X Y^T, RES> of each column tile into cdot [tiles x M].
+// partial dots <X Y^T, RES> of each column tile into cdot [tiles x ldc].
 hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                   int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt);
+                   int K, const void* GP, void* DU, void* DUT, const void* RES, float* cdot, int64_t ld, int64_t ldt,
+                   int64_t ldc, const GemmGroup& gg = GemmGroup());
 // SwiGLU backward through frozen gate/up: dA = X Y^T; dG, dV [M x ld]; partial dots with RES.
 hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const float* UG, const float* VU, void* DG, void* DV, const void* RES,
-                           float* cdot, int64_t ld);
+                           float* cdot, int64_t ld, int64_t ldc, const GemmGroup& gg = GemmGroup());
 // Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits):
 // per-tile buffers (CE partials, sums of squares, partial dots) are sized from it.
 void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n);
@@ -117,7 +142,7 @@ int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits);
 // Weight-gradient epilogue: G [M x ldg] in the GEMM precision and one sum of squares of the
 // fp32 accumulators per output tile in slot[tile].
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                     int K, void* G, int64_t ldg, float* slot);
+                     int K, void* G, int64_t ldg, float* slot, const GemmGroup& gg = GemmGroup());
 // LM head + online-softmax partials over the full vocabulary (N = V): one record per row and
 // per wave column block of gemm_wave_cols() vocabulary entries (records [M x nrec]), and,
 // when Q is non-null, the numerators exp(z - record max) [M x ldq] in the GEMM precision.

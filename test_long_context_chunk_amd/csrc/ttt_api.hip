@@ -12,8 +12,9 @@ namespace {
 constexpr int SPLIT_MAX = 8;       // split-K slabs for the small-M, long-K GEMMs
 constexpr int PAD = 64;             // token dimension of transposed activations is padded to this
 
-// One fast tensor, natural layout [rows x cols] (W1 [d x m], W2 [m x d]). The forward GEMMs
-// read it transposed, the backward GEMMs row-major:
+// One fast tensor, natural layout [rows x cols] (W1 [d x m], W2 [m x d]), one copy of its
+// state per stream (D, Wop, WtT, G: stream z at z rows cols elements) over a shared W0. The
+// forward GEMMs read it transposed, the backward GEMMs row-major:
 //   fp32: forward X (W0 + D)^T via WtT; backward X (W0 + D) via Wop.
 //   bf16: forward X W0^T + X rn(D)^T via W0T and WtT (two K-segments, so updates far below
 //         the rounding step of W0 still reach the forward pass); backward X rn(W0 + D) via Wop.
@@ -21,11 +22,11 @@ struct FastTensor {
   int rows = 0, cols = 0;
   void* W0 = nullptr;      // initial weights (GEMM precision) [rows x cols]
   void* W0T = nullptr;     // bf16 only: W0^T [cols x rows]
-  float* D = nullptr;      // accumulated update, fp32 [rows x cols]
-  void* Wop = nullptr;     // rn(W0 + D) [rows x cols]
-  void* WtT = nullptr;     // bf16: rn(D)^T, fp32: (W0 + D)^T  [cols x rows]
-  void* G = nullptr;       // chunk gradient in the GEMM precision [rows x cols]
-  int slot0 = 0;           // first grad-norm slot
+  float* D = nullptr;      // accumulated update, fp32 [streams][rows x cols]
+  void* Wop = nullptr;     // rn(W0 + D) [streams][rows x cols]
+  void* WtT = nullptr;     // bf16: rn(D)^T, fp32: (W0 + D)^T  [streams][cols x rows]
+  void* G = nullptr;       // chunk gradient in the GEMM precision [streams][rows x cols]
+  int slot0 = 0;           // first grad-norm slot (within a stream's slots)
   hipEvent_t ev_upd = nullptr;  // recorded on the aux stream after this tensor's last update
   // snapshot of the state a step changes (D, Wop, WtT), allocated at the first snapshot
   void* snapD = nullptr;
@@ -39,14 +40,16 @@ struct Block {
   void* WuT = nullptr;      // SwiGLU frozen up, [m x d]
   void* Wg = nullptr;       // SwiGLU frozen gate/up, natural [d x m] (loss compensation only)
   void* Wu = nullptr;
-  void* Hn = nullptr;       // normed block input [b x d]
-  void* HnT = nullptr;      // its transpose [d x bp]
-  float* r = nullptr;       // RMSNorm scale per token [b]
-  void* AT = nullptr;       // activation transpose [m x bp]
-  void* GP = nullptr;       // GELU'(U) [b x m]
-  void* ResN = nullptr;     // bf16 only: n - rn(n) [b x d]
-  void* ResA = nullptr;     // bf16 only: A - rn(A) [b x m]
-  float* VU = nullptr;      // SwiGLU + bf16: up projection n Wu [b x m] fp32
+  // per-token buffers hold the R = streams x b rows of one step (stream z: rows z b ..);
+  // transposed ones [.. x Rp] hold stream z in columns z bp ..
+  void* Hn = nullptr;       // normed block input [R x d]
+  void* HnT = nullptr;      // its transpose [d x Rp]
+  float* r = nullptr;       // RMSNorm scale per token [R]
+  void* AT = nullptr;       // activation transpose [m x Rp]
+  void* GP = nullptr;       // GELU'(U) [R x m]
+  void* ResN = nullptr;     // bf16 only: n - rn(n) [R x d]
+  void* ResA = nullptr;     // bf16 only: A - rn(A) [R x m]
+  float* VU = nullptr;      // SwiGLU + bf16: up projection n Wu [R x m] fp32
   int cslot = 0;            // first loss-compensation slot of this block
 };
 
@@ -57,6 +60,9 @@ struct ttt_ctx {
   hipStream_t st = nullptr;
   int prec = 0, es = 4;
   int b = 0, bp = 0, V = 0, d = 0, m = 0, L = 0;
+  // independent token streams advanced together (each with its own fast state, records and
+  // clip); a step covers R = nb b token rows, Rp = nb bp columns of the transposed buffers
+  int nb = 1, R = 0, Rp = 0;
   std::vector<void*> allocs;
 
   void *E_in = nullptr, *E_out = nullptr, *E_outT = nullptr;
@@ -91,14 +97,14 @@ struct ttt_ctx {
   float* UG = nullptr;
   void *DG = nullptr, *DV = nullptr;  // SwiGLU + bf16: gradients at the gate / up outputs
   bool foc = false;                   // first-order loss compensation (bf16 with blocks)
-  float* cpart = nullptr;             // compensation slots [ncslot x b]
+  float* cpart = nullptr;             // compensation slots [ncslot x R]
   int ncslot = 0;
-  float* slots = nullptr;
-  int nslots = 0;
-  float* sc = nullptr;
-  float* losses = nullptr;
-  int* amax = nullptr;
-  float* stats = nullptr;
+  float* slots = nullptr;  // grad-norm slots [nb x nslots]
+  int nslots = 0;          // per stream
+  float* sc = nullptr;     // clip scale and skip flag, 4 floats per stream
+  float* losses = nullptr;  // [nb x max_tokens]
+  int* amax = nullptr;      // [nb x max_tokens]
+  float* stats = nullptr;   // [nb x max_chunks x 2]
   int* err = nullptr;
   int64_t max_chunks = 0;
 
@@ -193,11 +199,12 @@ void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
   const int64_t n = (int64_t)rows * cols;
   f.rows = rows;
   f.cols = cols;
+  const int64_t nz = n * c->nb;
   f.W0 = dalloc<char>(c, n * c->es);
-  f.D = dalloc<float>(c, n * 4);
-  f.Wop = dalloc<char>(c, n * c->es);
-  f.WtT = dalloc<char>(c, n * c->es);
-  f.G = dalloc<char>(c, n * c->es);
+  f.D = dalloc<float>(c, nz * 4);
+  f.Wop = dalloc<char>(c, nz * c->es);
+  f.WtT = dalloc<char>(c, nz * c->es);
+  f.G = dalloc<char>(c, nz * c->es);
   check(hipMemcpyAsync(f.W0, src, n * c->es, hipMemcpyDeviceToDevice, c->st));
   if (c->prec == PREC_BF16) {
     f.W0T = dalloc<char>(c, n * c->es);
@@ -213,16 +220,18 @@ void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
 
 void reset_fast(ttt_ctx* c, FastTensor& f) {
   const int64_t n = (int64_t)f.rows * f.cols;
-  check(run_fill_u32(c->st, f.D, n, 0u));
-  check(hipMemcpyAsync(f.Wop, f.W0, n * c->es, hipMemcpyDeviceToDevice, c->st));
-  if (c->prec == PREC_BF16)
-    check(run_fill_u32(c->st, f.WtT, n * c->es / 4, 0u));  // rn(D)^T with D = 0
-  else
-    check(run_transpose(c->st, c->prec, f.W0, f.cols, f.rows, f.cols, f.WtT, f.rows));
+  check(run_fill_u32(c->st, f.D, n * c->nb, 0u));
+  if (c->prec == PREC_BF16) check(run_fill_u32(c->st, f.WtT, n * c->nb * c->es / 4, 0u));  // rn(D)^T with D = 0
+  for (int z = 0; z < c->nb; ++z) {
+    check(hipMemcpyAsync((char*)f.Wop + z * n * c->es, f.W0, n * c->es, hipMemcpyDeviceToDevice, c->st));
+    if (c->prec != PREC_BF16)
+      check(run_transpose(c->st, c->prec, f.W0, f.cols, f.rows, f.cols, (char*)f.WtT + z * n * c->es, f.rows));
+  }
 }
 
 void build(ttt_ctx* c, const ttt_weights* w) {
-  const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L, es = c->es;
+  const int b = c->b, V = c->V, d = c->d, m = c->m, L = c->L, es = c->es;
+  const int Rr = c->R, Rp = c->Rp, nb = c->nb;
   const int64_t Vd = (int64_t)V * d;
   c->E_in = dalloc<char>(c, Vd * es);
   c->E_out = dalloc<char>(c, Vd * es);
@@ -242,9 +251,9 @@ void build(ttt_ctx* c, const ttt_weights* w) {
     Block& B = c->blocks[l];
     if (c->cfg.mlp == TTT_MLP_GELU) {
       init_fast(c, B.w1, d, m, w->w1[l]);
-      B.GP = dalloc<char>(c, (int64_t)b * m * es);
-      B.HnT = dalloc<char>(c, (int64_t)d * bp * es);
-      check(hipMemsetAsync(B.HnT, 0, (int64_t)d * bp * es, c->st));
+      B.GP = dalloc<char>(c, (int64_t)Rr * m * es);
+      B.HnT = dalloc<char>(c, (int64_t)d * Rp * es);
+      check(hipMemsetAsync(B.HnT, 0, (int64_t)d * Rp * es, c->st));
     } else {
       B.WgT = dalloc<char>(c, (int64_t)m * d * es);
       B.WuT = dalloc<char>(c, (int64_t)m * d * es);
@@ -255,36 +264,36 @@ void build(ttt_ctx* c, const ttt_weights* w) {
         B.Wu = dalloc<char>(c, (int64_t)m * d * es);
         check(hipMemcpyAsync(B.Wg, w->w1[l], (int64_t)m * d * es, hipMemcpyDeviceToDevice, c->st));
         check(hipMemcpyAsync(B.Wu, w->w_up[l], (int64_t)m * d * es, hipMemcpyDeviceToDevice, c->st));
-        B.VU = dalloc<float>(c, (int64_t)b * m * 4);
+        B.VU = dalloc<float>(c, (int64_t)Rr * m * 4);
       }
     }
     init_fast(c, B.w2, m, d, w->w2[l]);
-    B.Hn = dalloc<char>(c, (int64_t)b * d * es);
-    B.r = dalloc<float>(c, (int64_t)b * 4);
-    B.AT = dalloc<char>(c, (int64_t)m * bp * es);
-    check(hipMemsetAsync(B.AT, 0, (int64_t)m * bp * es, c->st));
+    B.Hn = dalloc<char>(c, (int64_t)Rr * d * es);
+    B.r = dalloc<float>(c, (int64_t)Rr * 4);
+    B.AT = dalloc<char>(c, (int64_t)m * Rp * es);
+    check(hipMemsetAsync(B.AT, 0, (int64_t)m * Rp * es, c->st));
     if (c->foc) {
-      B.ResN = dalloc<char>(c, (int64_t)b * d * es);
-      B.ResA = dalloc<char>(c, (int64_t)b * m * es);
+      B.ResN = dalloc<char>(c, (int64_t)Rr * d * es);
+      B.ResA = dalloc<char>(c, (int64_t)Rr * m * es);
       B.cslot = c->ncslot;
       c->ncslot += tnm + 1;  // tnm partial dots for A, one for n
     }
   }
   for (FastTensor* f : c->fast) reset_fast(c, *f);
 
-  c->H = dalloc<float>(c, (int64_t)b * d * 4);
-  c->Yb = dalloc<char>(c, (int64_t)b * d * es);
-  c->tok_prev = dalloc<int>(c, (int64_t)b * 4);
-  c->tok_tgt = dalloc<int>(c, (int64_t)b * 4);
-  c->ce_w = gemm_wave_cols(c->prec, b, V, d, 0, 1);  // the LM-head GEMM
+  c->H = dalloc<float>(c, (int64_t)Rr * d * 4);
+  c->Yb = dalloc<char>(c, (int64_t)Rr * d * es);
+  c->tok_prev = dalloc<int>(c, (int64_t)Rr * 4);
+  c->tok_tgt = dalloc<int>(c, (int64_t)Rr * 4);
+  c->ce_w = gemm_wave_cols(c->prec, Rr, V, d, 0, 1);  // the LM-head GEMM (all streams' rows)
   c->ce_nrec = cdiv(V, c->ce_w);
-  c->pmax = dalloc<float>(c, (int64_t)c->ce_nrec * b * 4);
-  c->psum = dalloc<float>(c, (int64_t)c->ce_nrec * b * 4);
-  c->pidx = dalloc<int>(c, (int64_t)c->ce_nrec * b * 4);
-  c->tgt_logit = dalloc<float>(c, (int64_t)b * 4);
-  c->lse = dalloc<float>(c, (int64_t)b * 4);
-  if (L > 0) c->P = dalloc<char>(c, (int64_t)b * V * es);  // softmax numerators, then dlogits
-  c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * b * d * 4);
+  c->pmax = dalloc<float>(c, (int64_t)c->ce_nrec * Rr * 4);
+  c->psum = dalloc<float>(c, (int64_t)c->ce_nrec * Rr * 4);
+  c->pidx = dalloc<int>(c, (int64_t)c->ce_nrec * Rr * 4);
+  c->tgt_logit = dalloc<float>(c, (int64_t)Rr * 4);
+  c->lse = dalloc<float>(c, (int64_t)Rr * 4);
+  if (L > 0) c->P = dalloc<char>(c, (int64_t)Rr * V * es);  // softmax numerators, then dlogits
+  c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * Rr * d * 4);
   c->dec_tok = dalloc<int>(c, (int64_t)(b + 1) * 4);
   c->eval_loss = dalloc<float>(c, (int64_t)b * 4);
   c->eval_amax = dalloc<int>(c, (int64_t)b * 4);
@@ -297,35 +306,37 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->dec_rmax = dalloc<float>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
   c->dec_rsum = dalloc<float>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
   c->dec_ridx = dalloc<int>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
-  c->dH = dalloc<float>(c, (int64_t)b * d * 4);
-  c->dHb = dalloc<char>(c, (int64_t)b * d * es);
-  c->dHT = dalloc<char>(c, (int64_t)d * bp * es);
-  check(hipMemsetAsync(c->dHT, 0, (int64_t)d * bp * es, c->st));
-  c->A = dalloc<char>(c, (int64_t)b * m * es);
-  c->dU = dalloc<char>(c, (int64_t)b * m * es);
-  c->dUT = dalloc<char>(c, (int64_t)m * bp * es);
-  check(hipMemsetAsync(c->dUT, 0, (int64_t)m * bp * es, c->st));
-  if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)b * m * 4);
+  c->dH = dalloc<float>(c, (int64_t)Rr * d * 4);
+  c->dHb = dalloc<char>(c, (int64_t)Rr * d * es);
+  c->dHT = dalloc<char>(c, (int64_t)d * Rp * es);
+  check(hipMemsetAsync(c->dHT, 0, (int64_t)d * Rp * es, c->st));
+  c->A = dalloc<char>(c, (int64_t)Rr * m * es);
+  c->dU = dalloc<char>(c, (int64_t)Rr * m * es);
+  c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
+  check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
+  if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)Rr * m * 4);
   if (c->foc && c->cfg.mlp == TTT_MLP_SWIGLU_W2) {
-    c->DG = dalloc<char>(c, (int64_t)b * m * es);
-    c->DV = dalloc<char>(c, (int64_t)b * m * es);
+    c->DG = dalloc<char>(c, (int64_t)Rr * m * es);
+    c->DV = dalloc<char>(c, (int64_t)Rr * m * es);
   }
   if (c->foc) {
-    c->cpart = dalloc<float>(c, (int64_t)c->ncslot * b * 4);
-    check(hipMemsetAsync(c->cpart, 0, (int64_t)c->ncslot * b * 4, c->st));
+    c->cpart = dalloc<float>(c, (int64_t)c->ncslot * Rr * 4);
+    check(hipMemsetAsync(c->cpart, 0, (int64_t)c->ncslot * Rr * 4, c->st));
   }
-  c->slots = dalloc<float>(c, (int64_t)(c->nslots > 0 ? c->nslots : 1) * 4);
-  check(hipMemsetAsync(c->slots, 0, (int64_t)(c->nslots > 0 ? c->nslots : 1) * 4, c->st));
-  c->sc = dalloc<float>(c, 4 * 4);
-  c->losses = dalloc<float>(c, c->cfg.max_tokens * 4);
-  c->amax = dalloc<int>(c, c->cfg.max_tokens * 4);
+  const int64_t nsl = (int64_t)nb * (c->nslots > 0 ? c->nslots : 1);
+  c->slots = dalloc<float>(c, nsl * 4);
+  check(hipMemsetAsync(c->slots, 0, nsl * 4, c->st));
+  c->sc = dalloc<float>(c, (int64_t)nb * 4 * 4);
+  const int64_t ntok = (int64_t)nb * c->cfg.max_tokens;
+  c->losses = dalloc<float>(c, ntok * 4);
+  c->amax = dalloc<int>(c, ntok * 4);
   c->max_chunks = c->cfg.max_tokens / b;
-  c->stats = dalloc<float>(c, c->max_chunks * 2 * 4);
+  c->stats = dalloc<float>(c, nb * c->max_chunks * 2 * 4);
   c->err = dalloc<int>(c, 4);
   check(hipMemsetAsync(c->err, 0, 4, c->st));
-  check(hipMemsetAsync(c->losses, 0, c->cfg.max_tokens * 4, c->st));
-  check(hipMemsetAsync(c->amax, 0, c->cfg.max_tokens * 4, c->st));
-  check(hipMemsetAsync(c->stats, 0, c->max_chunks * 2 * 4, c->st));
+  check(hipMemsetAsync(c->losses, 0, ntok * 4, c->st));
+  check(hipMemsetAsync(c->amax, 0, ntok * 4, c->st));
+  check(hipMemsetAsync(c->stats, 0, nb * c->max_chunks * 2 * 4, c->st));
   check(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
   check(hipEventCreateWithFlags(&c->ev_to_aux, kSyncEvent));
   check(hipEventCreateWithFlags(&c->ev_from_aux, kSyncEvent));
@@ -382,23 +393,48 @@ void prof_mark(ttt_ctx* c) {
 // corrected by b * sum <dL/dX_t, X_t - rn(X_t)> over those operands, with dL/dX the
 // chunk-mean-loss gradients the backward pass computes anyway, so l_t matches the loss of
 // the unrounded forward to first order in the rounding error.
-void run_chunk(ttt_ctx* c, const int32_t* tok, float* loss_out, int* amax_out, bool train, int64_t chunk_idx) {
+void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, int* amax_out, int64_t ldl, bool train,
+               int64_t chunk_idx) {
   hipStream_t st = c->st;
   c->prof_on = c->prof_mask != 0 && (c->prof_chunks++ % c->prof_period) == 0;
   const int prec = c->prec;
   const int b = c->b, bp = c->bp, V = c->V, d = c->d, m = c->m, L = c->L;
+  // all streams' rows at once: R rows, transposed buffers Rp wide
+  const int nb = c->nb, Rr = c->R, Rp = c->Rp;
   const int rms = c->cfg.norm == TTT_NORM_RMS;
   const bool gelu = c->cfg.mlp == TTT_MLP_GELU;
   const bool bf = prec == PREC_BF16;
   const bool foc = c->foc;
-  const int64_t bd = (int64_t)b * d;
+  const int64_t Rd = (int64_t)Rr * d;
+  const int64_t n1 = (int64_t)d * m, n2 = (int64_t)m * d;  // elements of one stream's W1, W2
   const int tnm = c->dot_tiles;
+  const StreamRows srt{b, ldtok}, srl{b, ldl};
+  // Products with a stream's own fast weights run as one grouped launch over the streams
+  // (stream z: token rows z b .., its weights z n .. past the first stream's); products
+  // with frozen weights run once over all R rows.
+  auto fw = [&](int64_t rows_x, int64_t ldx, int64_t nw, bool w_shared) {
+    GemmGroup g;
+    g.n = nb;
+    g.x = rows_x * ldx;
+    g.y = w_shared ? 0 : nw;
+    g.x2 = rows_x * ldx;
+    g.y2 = nw;
+    return g;
+  };
+  auto gradg = [&](int64_t slot_stride) {  // weight gradients: K = a stream's token columns
+    GemmGroup g;
+    g.n = nb;
+    g.x = bp;
+    g.y = bp;
+    g.tile = (int)slot_stride;
+    return g;
+  };
 
   // a1 gather, and a2 the lowest block's pre-norm
   {
     Block* B0 = L > 0 ? &c->blocks[0] : nullptr;
-    RUN(TTT_K_GATHER, run_row_in(st, prec, tok, V, c->E_in, c->tok_prev, c->tok_tgt, c->err, nullptr, 0, 0, c->H, b, d,
-                                 L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, B0 ? B0->Hn : nullptr,
+    RUN(TTT_K_GATHER, run_row_in(st, prec, tok, srt, V, c->E_in, c->tok_prev, c->tok_tgt, c->err, nullptr, 0, 0, c->H,
+                                 Rr, d, L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, B0 ? B0->Hn : nullptr,
                                  B0 ? B0->r : nullptr, B0 && foc ? B0->ResN : nullptr));
   }
 
@@ -407,93 +443,99 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, float* loss_out, int* amax_out, b
     Block& B = c->blocks[l];
     if (gelu) {
       // Hn^T is read only by the W1 gradient of the backward pass
-      if (train) check(run_transpose(st, prec, B.Hn, d, b, d, B.HnT, bp));
+      if (train) check(run_transpose(st, prec, B.Hn, d, Rr, d, B.HnT, Rp));
       check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
       RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
-                              foc ? B.ResA : nullptr, m, bp, s2));
+                              foc ? B.ResA : nullptr, m, Rp, s2, fw(b, d, n1, bf)));
     } else {
-      RUN(TTT_K_UP, gemm_f32(st, prec, B.Hn, d, B.WgT, d, b, m, d, 1, c->UG, m, 0, 0));
-      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, b, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
-                                foc ? B.ResA : nullptr, m, bp));
+      RUN(TTT_K_UP, gemm_f32(st, prec, B.Hn, d, B.WgT, d, Rr, m, d, 1, c->UG, m, 0, 0));
+      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, Rr, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
+                                foc ? B.ResA : nullptr, m, Rp));
     }
-    const int S = gemm_split_k(prec, b, d, m, bf ? m : 0, SPLIT_MAX);
+    const int S = gemm_split_k(prec, Rr, d, m, bf ? m : 0, SPLIT_MAX);
     check(hipStreamWaitEvent(st, B.w2.ev_upd, 0));  // the previous chunk's step of W2
     GemmSeg2 s2;
     if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
-    RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, bd, 0, s2));
+    RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, Rd, 0, s2,
+                             fw(b, m, n2, bf)));
     // a4 residual, and a2 the next block's pre-norm
     Block* Bn = l + 1 < L ? &c->blocks[l + 1] : nullptr;
-    RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, V, nullptr, nullptr, nullptr, nullptr, c->part, S, bd, c->H, b, d,
-                                   l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, Bn ? Bn->Hn : nullptr,
+    RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, S, Rd, c->H,
+                                   Rr, d, l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, Bn ? Bn->Hn : nullptr,
                                    Bn ? Bn->r : nullptr, Bn && foc ? Bn->ResN : nullptr));
   }
 
   // a5 LM head + CE forward: online softmax over vocabulary records; the numerators are kept
   // for the backward pass (no logits are recomputed)
-  RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, b, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
+  RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, Rr, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
                                     c->tgt_logit, c->ce_nrec, c->P, V));
-  RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_nrec, b, c->tgt_logit, c->lse,
+  RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_nrec, Rr, srl, c->tgt_logit, c->lse,
                                    loss_out, amax_out));
 
   // an evaluation (no step) runs the backward only for the loss compensation
   if (L > 0 && (train || foc)) {
     // a6 CE backward: dlogits in place from the stored numerators, then dY = P E_out over the
     // whole vocabulary (split-K slabs)
-    RUN(TTT_K_CE_PROB, run_ce_dlogits(st, prec, c->P, b, V, c->ce_w, c->pmax, c->ce_nrec, c->lse, c->tok_tgt,
+    RUN(TTT_K_CE_PROB, run_ce_dlogits(st, prec, c->P, Rr, V, c->ce_w, c->pmax, c->ce_nrec, c->lse, c->tok_tgt,
                                       1.0f / (float)b));
-    const int S2 = gemm_split_k(prec, b, d, V, 0, SPLIT_MAX);
-    RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, V, c->E_outT, V, b, d, V, S2, c->part, d, bd, 0));
-    RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, bd, b, d, c->dH, c->dHb, c->H, c->Yb,
+    const int S2 = gemm_split_k(prec, Rr, d, V, 0, SPLIT_MAX);
+    RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, V, c->E_outT, V, Rr, d, V, S2, c->part, d, Rd, 0));
+    RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, Rd, Rr, d, c->dH, c->dHb, c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
     // dH^T, read by the W2 gradient
-    if (train) check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+    if (train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
 
     // a7 block backward, top to bottom
     for (int l = L - 1; l >= 0; --l) {
       Block& B = c->blocks[l];
-      float* cA = foc ? c->cpart + (int64_t)B.cslot * b : nullptr;        // tnm slots
-      float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * b : nullptr;  // one slot
+      float* cA = foc ? c->cpart + (int64_t)B.cslot * Rr : nullptr;        // tnm slots
+      float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * Rr : nullptr;  // one slot
       if (gelu) {
         RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
-                              foc ? B.ResA : nullptr, cA, m, bp));
+                              foc ? B.ResA : nullptr, cA, m, Rp, Rr, fw(b, d, n2, false)));
         if (train) {
-          RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
-          RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, bp, c->dUT, bp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0));
+          RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
+                                  gradg(c->nslots)));
+          RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, Rp, c->dUT, Rp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0,
+                                  gradg(c->nslots)));
         }
         // the block input gradient is needed below this block, and for the compensation of
         // a rounded n (the lowest block's n = E_in[x] is exact when there is no norm)
         if (l > 0 || (foc && rms)) {
-          const int S = gemm_split_k(prec, b, d, m, 0, SPLIT_MAX);
-          RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, bd, 0));
-          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb,
+          const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
+          RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
+                                  fw(b, m, n1, false)));
+          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, c->dHb,
                                            foc ? B.ResN : nullptr, cN, l > 0));
-          if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, b, d, c->dHT, bp));
+          if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
         }
       } else if (train) {
-        RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, bp, c->dHT, bp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0));
+        RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
+                                gradg(c->nslots)));
       }
       if (!gelu && foc) {
         // SwiGLU (one block, W2 only fast): dA, then dn = dG Wg^T + dV Wu^T, only to carry
         // the loss compensation of A and n.
         RUN(TTT_K_DU, gemm_swiglu_bwd(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, c->UG, B.VU, c->DG, c->DV, B.ResA,
-                                      cA, m));
+                                      cA, m, Rr, fw(b, d, n2, false)));
         if (rms) {
-          const int S = gemm_split_k(prec, b, d, m, m, SPLIT_MAX);
+          const int S = gemm_split_k(prec, Rr, d, m, m, SPLIT_MAX);
           GemmSeg2 s2{c->DV, m, B.Wu, m, m};
-          RUN(TTT_K_DHN, gemm_f32(st, prec, c->DG, m, B.Wg, m, b, d, m, S, c->part, d, bd, 0, s2));
-          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, bd, B.Hn, B.r, b, d, rms, c->dH, c->dHb, B.ResN, cN,
-                                           0));
+          RUN(TTT_K_DHN, gemm_f32(st, prec, c->DG, m, B.Wg, m, Rr, d, m, S, c->part, d, Rd, 0, s2));
+          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, c->dHb, B.ResN,
+                                           cN, 0));
         }
       }
     }
-    if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, b, (float)b, loss_out));
+    if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, Rr, srl, (float)b, loss_out));
   }
   if (!train) return;
 
-  // a8 global grad norm and clip scale; a9 update
-  RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx, c->err));
+  // a8 global grad norm and clip scale, one per stream; a9 update
+  RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx,
+                                   2 * c->max_chunks, nb, c->err));
   // The step runs on the aux stream, in the order the next chunk's forward pass needs the
   // tensors; each GEMM that reads a fast tensor waits for that tensor's event. (A context
   // with no blocks has no fast tensors.)
@@ -501,7 +543,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, float* loss_out, int* amax_out, b
     aux_fork(c);
     for (FastTensor* f : c->fast) {
       check(run_update(c->aux, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols, c->cfg.lr, c->sc,
-                       bf ? 1 : 0));
+                       bf ? 1 : 0, nb));
       check(hipEventRecord(f->ev_upd, c->aux));
     }
     aux_mark(c);
@@ -565,7 +607,7 @@ void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out)
 void evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, double* acc, float* losses, float* mean) {
   const int b = c->b;
   for (int64_t i = 0; i < nq; i += b) {
-    run_chunk(c, q + i, c->eval_loss, c->eval_amax, false, 0);
+    run_chunk(c, q + i, 0, c->eval_loss, c->eval_amax, b, false, 0);
     check(run_eval_accum(c->st, c->eval_loss, b, acc, losses ? losses + i : nullptr, i == 0, i + b >= nq, nq,
                          mean));
   }
@@ -609,11 +651,16 @@ ttt_status read_sticky(ttt_ctx* c) {
 
 extern "C" {
 
-ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out) {
+ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t streams, void* stream,
+                            ttt_ctx** out) {
   if (!out) return TTT_EINVAL;
   *out = nullptr;
   ttt_status v = validate(cfg, w);
   if (v != TTT_OK) return v;
+  if (streams < 1 || streams > TTT_MAX_STREAMS) return TTT_EINVAL;
+  // several streams stack their rows: whole PAD-wide column groups per stream in the
+  // transposed buffers, and a bounded row count per step
+  if (streams > 1 && (cfg->chunk % PAD || (int64_t)streams * cfg->chunk > ((int64_t)1 << 21))) return TTT_EINVAL;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return TTT_EDEVICE;
   ttt_ctx* c = new (std::nothrow) ttt_ctx();
@@ -624,6 +671,9 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
   c->es = c->prec == PREC_BF16 ? 2 : 4;
   c->b = cfg->chunk;
   c->bp = (cfg->chunk + PAD - 1) / PAD * PAD;
+  c->nb = streams;
+  c->R = streams * c->b;
+  c->Rp = streams * c->bp;
   c->V = cfg->vocab;
   c->d = cfg->d_model;
   c->m = cfg->d_hidden;
@@ -648,14 +698,28 @@ ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream,
   return TTT_OK;
 }
 
+ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out) {
+  return ttt_create_batch(cfg, w, 1, stream, out);
+}
+
+int32_t ttt_streams(const ttt_ctx* c) { return c ? c->nb : -1; }
+
 ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_tokens) {
+  if (!c || c->nb != 1) return TTT_EINVAL;
+  return ttt_prefill_batch(c, tokens, n_tokens + 1, n_tokens);
+}
+
+ttt_status ttt_prefill_batch(ttt_ctx* c, const int32_t* tokens, int64_t ld_tokens, int64_t n_tokens) {
   if (!c || !tokens) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (n_tokens <= 0 || n_tokens % c->b || c->npend != 0) return TTT_EINVAL;
+  if (c->nb > 1 && ld_tokens < n_tokens + 1) return TTT_EINVAL;
+  const int64_t ldtok = c->nb > 1 ? ld_tokens : 0;
   if (c->pos + n_tokens > c->cfg.max_tokens) return TTT_EINVAL;
   try {
     for (int64_t i = 0; i < n_tokens; i += c->b)
-      run_chunk(c, tokens + i, c->losses + c->pos + i, c->amax + c->pos + i, true, (c->pos + i) / c->b);
+      run_chunk(c, tokens + i, ldtok, c->losses + c->pos + i, c->amax + c->pos + i, c->cfg.max_tokens, true,
+                (c->pos + i) / c->b);
   } catch (const HipFail& f) {
     c->sticky = f.s;
     return f.s;
@@ -665,7 +729,7 @@ ttt_status ttt_prefill_chunks(ttt_ctx* c, const int32_t* tokens, int64_t n_token
 }
 
 ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* argmax, float* logits) {
-  if (!c || !tokens || n < 0) return TTT_EINVAL;
+  if (!c || !tokens || n < 0 || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + n > c->cfg.max_tokens) return TTT_EINVAL;
   if (n == 0) return TTT_OK;
@@ -676,7 +740,8 @@ ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* arg
       c->pos += 1;
       if (++c->npend == c->b) {
         // the decoded tokens fill a mini-batch: its step, as in prefill ([E2E] section 3.2)
-        run_chunk(c, c->dec_tok, c->losses + c->pos - c->b, c->amax + c->pos - c->b, true, (c->pos - c->b) / c->b);
+        run_chunk(c, c->dec_tok, 0, c->losses + c->pos - c->b, c->amax + c->pos - c->b, c->b, true,
+                  (c->pos - c->b) / c->b);
         c->npend = 0;
         aux_join(c);
       }
@@ -691,7 +756,7 @@ ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* arg
 int64_t ttt_decode_pending(const ttt_ctx* c) { return c ? c->npend : -1; }
 
 ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses, float* mean) {
-  if (!c || !q || nq <= 0 || nq % c->b) return TTT_EINVAL;
+  if (!c || !q || nq <= 0 || nq % c->b || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
     evaluate(c, q, nq, c->eval_acc, losses, mean);
@@ -703,7 +768,7 @@ ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses,
 }
 
 ttt_status ttt_snapshot(ttt_ctx* c) {
-  if (!c) return TTT_EINVAL;
+  if (!c || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
     copy_state(c, true);
@@ -716,7 +781,7 @@ ttt_status ttt_snapshot(ttt_ctx* c) {
 }
 
 ttt_status ttt_restore(ttt_ctx* c) {
-  if (!c) return TTT_EINVAL;
+  if (!c || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK || !c->has_snap) return TTT_ESTATE;
   try {
     copy_state(c, false);
@@ -729,7 +794,7 @@ ttt_status ttt_restore(ttt_ctx* c) {
 
 ttt_status ttt_settle_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
                             int32_t* committed) {
-  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0) return TTT_EINVAL;
+  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0 || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + c->b > c->cfg.max_tokens) return TTT_EINVAL;
   try {
@@ -737,7 +802,7 @@ ttt_status ttt_settle_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* q,
     copy_state(c, true);
     c->has_snap = true;
     // the candidate chunk: scored at W and stepped to W + delta, as in prefill
-    run_chunk(c, tokens, c->losses + c->pos, c->amax + c->pos, true, c->pos / c->b);
+    run_chunk(c, tokens, 0, c->losses + c->pos, c->amax + c->pos, c->b, true, c->pos / c->b);
     evaluate(c, q, nq, c->eval_acc + 2, nullptr, nullptr);  // L(q, W + delta)
     check(run_settle_decide(c->st, c->eval_acc + 1, nq, c->settle_A, c->settle_commit, A, committed));
     aux_join(c);
@@ -777,40 +842,59 @@ static ttt_status copy_record(ttt_ctx* c, void* dst, const void* src, int64_t of
   }
 }
 
-ttt_status ttt_token_losses(ttt_ctx* c, float* dst, int64_t offset, int64_t n) {
-  if (!c) return TTT_EINVAL;
-  return copy_record(c, dst, c->losses, offset, n, c->pos, 4);
+ttt_status ttt_stream_token_losses(ttt_ctx* c, int32_t s, float* dst, int64_t offset, int64_t n) {
+  if (!c || s < 0 || s >= c->nb) return TTT_EINVAL;
+  return copy_record(c, dst, c->losses + (int64_t)s * c->cfg.max_tokens, offset, n, c->pos, 4);
 }
 
-ttt_status ttt_token_argmax(ttt_ctx* c, int32_t* dst, int64_t offset, int64_t n) {
-  if (!c) return TTT_EINVAL;
-  return copy_record(c, dst, c->amax, offset, n, c->pos, 4);
+ttt_status ttt_stream_token_argmax(ttt_ctx* c, int32_t s, int32_t* dst, int64_t offset, int64_t n) {
+  if (!c || s < 0 || s >= c->nb) return TTT_EINVAL;
+  return copy_record(c, dst, c->amax + (int64_t)s * c->cfg.max_tokens, offset, n, c->pos, 4);
 }
 
-ttt_status ttt_chunk_stats(ttt_ctx* c, float* dst, int64_t offset, int64_t n) {
-  if (!c) return TTT_EINVAL;
+ttt_status ttt_stream_chunk_stats(ttt_ctx* c, int32_t s, float* dst, int64_t offset, int64_t n) {
+  if (!c || s < 0 || s >= c->nb) return TTT_EINVAL;
   if (!dst && n > 0) return TTT_EINVAL;
   if (offset < 0 || n < 0 || offset + n > c->pos / c->b) return TTT_EINVAL;
   try {
-    if (n > 0) check(hipMemcpyAsync(dst, c->stats + 2 * offset, n * 8, hipMemcpyDeviceToDevice, c->st));
+    const float* src = c->stats + (int64_t)s * 2 * c->max_chunks + 2 * offset;
+    if (n > 0) check(hipMemcpyAsync(dst, src, n * 8, hipMemcpyDeviceToDevice, c->st));
     return read_sticky(c);
   } catch (const HipFail& f) {
     return f.s;
   }
 }
 
-ttt_status ttt_fast_weights(ttt_ctx* c, int32_t block, int32_t which, int32_t kind, float* dst) {
-  if (!c || !dst || block < 0 || block >= c->L || (kind != 0 && kind != 1)) return TTT_EINVAL;
+ttt_status ttt_stream_fast_weights(ttt_ctx* c, int32_t s, int32_t block, int32_t which, int32_t kind, float* dst) {
+  if (!c || !dst || s < 0 || s >= c->nb || block < 0 || block >= c->L || (kind != 0 && kind != 1))
+    return TTT_EINVAL;
   if (which != 1 && which != 2) return TTT_EINVAL;
   if (which == 1 && c->cfg.mlp != TTT_MLP_GELU) return TTT_EINVAL;
   FastTensor& f = which == 1 ? c->blocks[block].w1 : c->blocks[block].w2;
+  const int64_t n = (int64_t)f.rows * f.cols;
   try {
     aux_join(c);  // a pending step of the last chunk
-    check(run_export(c->st, c->prec, f.D, f.W0, (int64_t)f.rows * f.cols, kind, dst));
+    check(run_export(c->st, c->prec, f.D + s * n, f.W0, n, kind, dst));
     return read_sticky(c);
   } catch (const HipFail& e) {
     return e.s;
   }
+}
+
+ttt_status ttt_token_losses(ttt_ctx* c, float* dst, int64_t offset, int64_t n) {
+  return ttt_stream_token_losses(c, 0, dst, offset, n);
+}
+
+ttt_status ttt_token_argmax(ttt_ctx* c, int32_t* dst, int64_t offset, int64_t n) {
+  return ttt_stream_token_argmax(c, 0, dst, offset, n);
+}
+
+ttt_status ttt_chunk_stats(ttt_ctx* c, float* dst, int64_t offset, int64_t n) {
+  return ttt_stream_chunk_stats(c, 0, dst, offset, n);
+}
+
+ttt_status ttt_fast_weights(ttt_ctx* c, int32_t block, int32_t which, int32_t kind, float* dst) {
+  return ttt_stream_fast_weights(c, 0, block, which, kind, dst);
 }
 
 ttt_status ttt_reset(ttt_ctx* c) {

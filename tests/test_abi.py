@@ -87,6 +87,21 @@ def test_create_rejects_missing_weights(lib):
     assert lib.ttt_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out)) == -1
 
 
+@pytest.mark.parametrize("streams,chunk,max_tokens", [
+    (0, 64, 128), (-3, 64, 128), (4097, 64, 128),  # stream count outside [1, TTT_MAX_STREAMS]
+    (2, 1, 128), (3, 96, 192),                      # several streams need whole 64-row groups
+    (64, 65536, 65536),                             # more than 2^21 rows per step
+])
+def test_create_batch_rejects_bad_stream_counts_before_touching_a_device(lib, streams, chunk, max_tokens):
+    cfg = _cfg(chunk=chunk, max_tokens=max_tokens)
+    dummy = (ctypes.c_void_p * 1)(1)
+    w = B.Weights(1, 1, ctypes.cast(dummy, ctypes.POINTER(ctypes.c_void_p)), None,
+                  ctypes.cast(dummy, ctypes.POINTER(ctypes.c_void_p)))
+    out = ctypes.c_void_p(12345)
+    assert lib.ttt_create_batch(ctypes.byref(cfg), ctypes.byref(w), streams, None, ctypes.byref(out)) == -1
+    assert out.value is None
+
+
 def test_null_context_calls_are_rejected(lib):
     assert lib.ttt_prefill_chunks(None, None, 8) == -1
     assert lib.ttt_token_losses(None, None, 0, 0) == -1
@@ -96,6 +111,12 @@ def test_null_context_calls_are_rejected(lib):
     assert lib.ttt_decode(None, None, 1, None, None) == -1
     assert lib.ttt_decode_pending(None) == -1
     assert lib.ttt_profile_period(None, 1) == -1
+    assert lib.ttt_streams(None) == -1
+    assert lib.ttt_prefill_batch(None, None, 9, 8) == -1
+    assert lib.ttt_stream_token_losses(None, 0, None, 0, 0) == -1
+    assert lib.ttt_stream_token_argmax(None, 0, None, 0, 0) == -1
+    assert lib.ttt_stream_chunk_stats(None, 0, None, 0, 0) == -1
+    assert lib.ttt_stream_fast_weights(None, 0, 0, 2, 0, None) == -1
 
 
 def test_gemm_hook_validates_shapes(lib):
