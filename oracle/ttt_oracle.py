@@ -17,7 +17,8 @@ hand-derived backpropagation, written from these pages:
               W_i = W_{i-1} - eta * (1/b) * sum_{t in chunk i} grad l_t(W_{i-1}).
         - section 3, eq. (6): L(W_0; X) = (1/T) sum_i sum_{t in chunk i} l_t(W_{i-1}).
         - section 3.1: only the MLP layers are updated; embedding and normalisation
-          layers stay frozen.
+          layers stay frozen; "two MLP layers per block": a static MLP is added to
+          each TTT'd block to hold pre-trained knowledge, and only the other is updated.
   [IPT] "[논문리뷰] In-Place Test-Time Training" (blog.secrett2633.cloud)
         - section 1 (Key Terms): the MLP block's final projection is the fast
           weight; the sequence is split into chunks updated one after another.
@@ -30,6 +31,9 @@ notes of the repository):
   * f = embedding -> L residual MLP blocks -> LM head; no biases, no final norm,
     untied input embedding E_in and output head E_out (both frozen).
   * "rms" blocks are pre-norm: n = h * (mean_j h_j^2 + eps)^(-1/2), no gain.
+  * the static MLP (when present) is a frozen GELU MLP with its own pre-norm and residual,
+    placed before the fast MLP of the same block: h <- h + GELU(norm(h) Ws1) Ws2, then
+    h <- h + MLP_fast(norm(h)).
   * GELU is the exact erf form; its derivative is Phi(u) + u * phi(u).
   * SwiGLU block (In-Place shape): a = SiLU(n Wg) * (n Wu); Wg, Wu frozen, W2 fast.
   * clipping: global L2 norm g over all fast tensors of the chunk-mean gradient,
@@ -37,8 +41,8 @@ notes of the repository):
   * a chunk whose g is not finite takes no step (the update is skipped).
   * argmax ties resolve to the lowest index.
 
-Arrays: E_in, E_out [V, d]; W1, Wg, Wu [d, m]; W2 [m, d]; all row-major, rows of
-activations are tokens.
+Arrays: E_in, E_out [V, d]; W1, Wg, Wu [d, m]; W2 [m, d]; Ws1 [d, m_s]; Ws2 [m_s, d];
+all row-major, rows of activations are tokens.
 """
 from __future__ import annotations
 
@@ -65,12 +69,14 @@ class Model:
     chunk: int = 1           # b
     lr: float = 0.0          # eta
     clip: float = 0.0        # c; <= 0 disables clipping
+    static_hidden: int = 0   # m_s of the frozen static MLP in every block (0: none)
 
     @classmethod
     def from_workload(cls, w, **kw) -> "Model":
         base = dict(vocab=w.vocab, d_model=w.d_model, d_hidden=w.d_hidden,
                     n_blocks=w.n_blocks, mlp=w.mlp, norm=w.norm, eps=w.eps,
-                    chunk=w.chunk, lr=w.lr, clip=w.clip)
+                    chunk=w.chunk, lr=w.lr, clip=w.clip,
+                    static_hidden=getattr(w, "static_hidden", 0))
         base.update(kw)
         return cls(**base)
 
@@ -117,31 +123,59 @@ def logsumexp_rows(z: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------- model f(x; W)
+def pre_norm(model: Model, h: np.ndarray):
+    """The block's pre-norm: (n, r) with n = h r, r = (mean_j h_j^2 + eps)^(-1/2) for "rms";
+    (h, None) for "none"."""
+    if model.norm == "rms":
+        r = 1.0 / np.sqrt(np.mean(h * h, axis=1) + model.eps)
+        return h * r[:, None], r
+    return h, None
+
+
+def pre_norm_backward(model: Model, n: np.ndarray, r, dn: np.ndarray) -> np.ndarray:
+    """Gradient at h from the gradient dn at n = norm(h):
+    rms: r (dn - n mean_j(dn_j n_j)); none: dn."""
+    if model.norm == "rms":
+        return r[:, None] * (dn - n * np.mean(dn * n, axis=1)[:, None])
+    return dn
+
+
+def static_mlp_backward(model: Model, P, l: int, c, dh: np.ndarray) -> np.ndarray:
+    """Gradient at the static MLP's input h from the gradient dh at its output
+    h + GELU(n Ws1) Ws2 (frozen weights: no weight gradient)."""
+    da = dh @ P[f"Ws2.{l}"].T
+    du = da * gelu_prime(c["us"])
+    dn = du @ P[f"Ws1.{l}"].T
+    return dh + pre_norm_backward(model, c["ns"], c["rs"], dn)
+
+
 def forward(model: Model, P: Dict[str, np.ndarray], x_prev: np.ndarray):
     """Hidden state h^L for each conditioning token x_{t-1}, plus a cache for backprop.
 
     [E2E] section 1: f reads only x_{t-1} in the MLP-only model. The stack is
-    h^0 = E_in[x_{t-1}]; h^l = h^{l-1} + MLP_l(norm(h^{l-1})).
+    h^0 = E_in[x_{t-1}]; h^l = h^{l-1} + MLP_l(norm(h^{l-1})), with the frozen static MLP
+    of the block first when the model has one ([E2E] section 3.1).
     """
     h = P["E_in"][x_prev]
     cache = []
     for l in range(model.n_blocks):
+        c = {}
+        if model.static_hidden > 0:
+            ns, rs = pre_norm(model, h)
+            us = ns @ P[f"Ws1.{l}"]
+            h = h + gelu(us) @ P[f"Ws2.{l}"]
+            c.update(ns=ns, rs=rs, us=us)
         h_in = h
-        if model.norm == "rms":
-            r = 1.0 / np.sqrt(np.mean(h_in * h_in, axis=1) + model.eps)
-            n = h_in * r[:, None]
-        else:
-            r = None
-            n = h_in
+        n, r = pre_norm(model, h_in)
         if model.mlp == "gelu":
             u = n @ P[f"W1.{l}"]
             a = gelu(u)
-            c = dict(n=n, r=r, u=u, a=a)
+            c.update(n=n, r=r, u=u, a=a)
         else:
             g = n @ P[f"Wg.{l}"]
             v = n @ P[f"Wu.{l}"]
             a = silu(g) * v
-            c = dict(n=n, r=r, g=g, v=v, a=a)
+            c.update(n=n, r=r, g=g, v=v, a=a)
         h = h_in + a @ P[f"W2.{l}"]
         cache.append(c)
     return h, cache
@@ -187,6 +221,7 @@ def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None):
         swiglu: dg = da * v * silu'(g) ; dv = da * silu(g) ; dn = dg Wg^T + dv Wu^T
         rms:    dh <- dh + r * (dn - n * mean_j(dn_j n_j))
         none:   dh <- dh + dn
+        static MLP below the fast one: dh <- its input gradient (static_mlp_backward)
       (the embedding is frozen, so the lowest block stops after its weight grads)
     """
     b = x_prev.shape[0]
@@ -219,11 +254,9 @@ def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None):
             dg = da * c["v"] * silu_prime(c["g"])
             dv = da * silu(c["g"])
             dn = dg @ P[f"Wg.{l}"].T + dv @ P[f"Wu.{l}"].T
-        if model.norm == "rms":
-            n = c["n"]
-            dh = dh + c["r"][:, None] * (dn - n * np.mean(dn * n, axis=1)[:, None])
-        else:
-            dh = dh + dn
+        dh = dh + pre_norm_backward(model, c["n"], c["r"], dn)
+        if model.static_hidden > 0:
+            dh = static_mlp_backward(model, P, l, c, dh)
     return float(losses.mean()), dict(losses=losses, argmax=am, margin=margin), grads
 
 

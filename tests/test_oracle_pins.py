@@ -20,9 +20,9 @@ import oracle.ttt_oracle as O
 import ttt_workloads as W
 
 
-def tiny_model(mlp="gelu", norm="none", L=2, b=3, lr=0.3, clip=0.0, V=11, d=6, m=10):
+def tiny_model(mlp="gelu", norm="none", L=2, b=3, lr=0.3, clip=0.0, V=11, d=6, m=10, ms=0):
     return O.Model(vocab=V, d_model=d, d_hidden=m, n_blocks=L, mlp=mlp, norm=norm,
-                   eps=1e-6, chunk=b, lr=lr, clip=clip)
+                   eps=1e-6, chunk=b, lr=lr, clip=clip, static_hidden=ms)
 
 
 def tiny_params(model, seed=0, std=0.5):
@@ -36,6 +36,9 @@ def tiny_params(model, seed=0, std=0.5):
             P[f"Wg.{l}"] = rng.normal(0, std, (model.d_model, model.d_hidden))
             P[f"Wu.{l}"] = rng.normal(0, std, (model.d_model, model.d_hidden))
         P[f"W2.{l}"] = rng.normal(0, std, (model.d_hidden, model.d_model))
+    for l in range(model.n_blocks if model.static_hidden > 0 else 0):
+        P[f"Ws1.{l}"] = rng.normal(0, std, (model.d_model, model.static_hidden))
+        P[f"Ws2.{l}"] = rng.normal(0, std, (model.static_hidden, model.d_model))
     return P
 
 
@@ -204,7 +207,7 @@ def torch_ttt(model, P0, tokens):
     """Independent implementation of eq. (5)/(6) + clipped step with torch fp64 autograd."""
     t = lambda a: torch.tensor(a, dtype=torch.float64)
     E_in, E_out = t(P0["E_in"]), t(P0["E_out"])
-    frozen = {k: t(v) for k, v in P0.items() if k.startswith(("Wg", "Wu"))}
+    frozen = {k: t(v) for k, v in P0.items() if k.startswith(("Wg", "Wu", "Ws"))}
     fast = {k: t(P0[k]) for k in model.fast_keys()}
     x = torch.tensor(np.asarray(tokens), dtype=torch.long)
     b = model.chunk
@@ -213,10 +216,17 @@ def torch_ttt(model, P0, tokens):
         params = {k: v.clone().requires_grad_(True) for k, v in fast.items()}
         ctx, tgt = x[i * b:(i + 1) * b], x[i * b + 1:(i + 1) * b + 1]
         h = E_in[ctx]
-        for l in range(model.n_blocks):
-            n = h
+
+        def norm(v):
             if model.norm == "rms":
-                n = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + model.eps)
+                return v * torch.rsqrt(v.pow(2).mean(-1, keepdim=True) + model.eps)
+            return v
+
+        for l in range(model.n_blocks):
+            if model.static_hidden > 0:
+                hs = torch.nn.functional.gelu(norm(h) @ frozen[f"Ws1.{l}"], approximate="none")
+                h = h + hs @ frozen[f"Ws2.{l}"]
+            n = norm(h)
             if model.mlp == "gelu":
                 a = torch.nn.functional.gelu(n @ params[f"W1.{l}"], approximate="none")
             else:
@@ -248,6 +258,47 @@ def test_p10_torch_autograd_second_opinion(mlp, norm, clip):
         np.testing.assert_allclose(res.weights[k], tw[k], rtol=1e-12, atol=1e-14)
         # the update itself (the part the stated weight gate cannot see)
         np.testing.assert_allclose(res.delta[k], tw[k] - P[k], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("norm", ["none", "rms"])
+def test_p10_static_mlp_second_opinion(norm):
+    """With a frozen static MLP before each fast one ([E2E] section 3.1): losses, norms and
+    updates against torch autograd, which differentiates through the static MLPs itself."""
+    model = tiny_model("gelu", norm, L=3, b=3, lr=0.4, clip=0.2, ms=7)
+    P = tiny_params(model, seed=21)
+    x = tiny_tokens(model, 12, seed=22)
+    res = O.run_ttt(model, P, x)
+    tl, tg, tw = torch_ttt(model, P, x)
+    np.testing.assert_allclose(res.losses, tl, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(res.grad_norm, tg, rtol=1e-12)
+    for k in model.fast_keys():
+        np.testing.assert_allclose(res.delta[k], tw[k] - P[k], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("norm", ["none", "rms"])
+def test_p1_finite_differences_through_static_mlps(norm):
+    """The lower blocks' gradients pass through the static MLPs of the blocks above."""
+    model = tiny_model("gelu", norm, L=2, b=3, ms=5)
+    P = tiny_params(model, seed=23)
+    x = tiny_tokens(model, 3, seed=24)
+    assert fd_check(model, P, x[:-1], x[1:]) < 1e-6
+
+
+def test_p15_zero_static_projection_is_the_plain_model():
+    """Ws2 = 0: every static MLP adds exactly zero and passes the gradient through
+    unchanged, so the run equals the model without static MLPs, bit for bit."""
+    model = tiny_model("gelu", "rms", L=3, b=2, lr=0.3, clip=0.5, ms=4)
+    P = tiny_params(model, seed=25)
+    for l in range(model.n_blocks):
+        P[f"Ws2.{l}"] = np.zeros_like(P[f"Ws2.{l}"])
+    x = tiny_tokens(model, 8, seed=26)
+    a = O.run_ttt(model, P, x)
+    plain = tiny_model("gelu", "rms", L=3, b=2, lr=0.3, clip=0.5)
+    b = O.run_ttt(plain, {k: v for k, v in P.items() if not k.startswith("Ws")}, x)
+    assert np.array_equal(a.losses, b.losses)
+    assert np.array_equal(a.grad_norm, b.grad_norm)
+    for k in model.fast_keys():
+        assert np.array_equal(a.weights[k], b.weights[k])
 
 
 def test_p10_realistic_shape_one_chunk():
@@ -312,6 +363,18 @@ def test_pins_catch_wrong_silu_derivative(monkeypatch):
     model = tiny_model("swiglu_w2", "rms", L=2, b=3)
     P = tiny_params(model, seed=3)
     x = tiny_tokens(model, 3, seed=4)
+    assert fd_check(model, P, x[:-1], x[1:]) > 1e-3
+
+
+def test_pins_catch_static_mlp_backward_without_norm_jacobian(monkeypatch):
+    """Planting a dropped pre-norm Jacobian in the static MLP's backward fails the FD pin."""
+    def wrong(model, P, l, c, dh):
+        da = dh @ P[f"Ws2.{l}"].T
+        return dh + (da * O.gelu_prime(c["us"])) @ P[f"Ws1.{l}"].T
+    monkeypatch.setattr(O, "static_mlp_backward", wrong)
+    model = tiny_model("gelu", "rms", L=2, b=3, ms=5)
+    P = tiny_params(model, seed=23)
+    x = tiny_tokens(model, 3, seed=24)
     assert fd_check(model, P, x[:-1], x[1:]) > 1e-3
 
 

@@ -37,7 +37,8 @@ import numpy as np
 
 BOS = 0
 
-# The five workloads. "fp32" workloads keep weights in float32; "bf16" ones
+# The five benchmark workloads, and the fuller-block variant of the 760M shape. "fp32"
+# workloads keep weights in float32; "bf16" ones
 # round every initial tensor to bfloat16.
 PRESETS: Dict[str, dict] = {
     # MLP-only bigram toy: per-token update (chunk 1), no clipping.
@@ -56,6 +57,11 @@ PRESETS: Dict[str, dict] = {
     "s760m": dict(vocab=32000, d_model=1536, d_hidden=6144, n_blocks=3,
                   mlp="gelu", norm="rms", precision="bf16", n_tokens=32768,
                   chunk=1024, lr=0.005, clip=1.0, stream="zipf_markov"),
+    # Fuller TTT-E2E block at the 760M shape: a frozen static MLP beside the fast one in
+    # each block, the MLP hidden size split between the two so the parameters stay equal.
+    "e2e760m": dict(vocab=32000, d_model=1536, d_hidden=3072, n_blocks=3,
+                    mlp="gelu", norm="rms", precision="bf16", n_tokens=32768,
+                    chunk=1024, lr=0.005, clip=1.0, stream="zipf_markov", static_hidden=3072),
     # In-Place-TTT shape: SwiGLU with frozen gate/up, only the down-projection fast.
     "inplace": dict(vocab=151936, d_model=2560, d_hidden=9728, n_blocks=1,
                     mlp="swiglu_w2", norm="rms", precision="bf16",
@@ -83,6 +89,7 @@ class Workload:
     clip: float       # <= 0 disables clipping
     stream: str       # "markov" | "zipf_markov"
     eps: float = RMS_EPS
+    static_hidden: int = 0  # hidden size of a frozen static MLP before the fast one (0: none)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -190,6 +197,9 @@ def weight_shapes(w: Workload) -> Dict[str, tuple]:
             shapes[f"Wg.{l}"] = (w.d_model, w.d_hidden)
             shapes[f"Wu.{l}"] = (w.d_model, w.d_hidden)
         shapes[f"W2.{l}"] = (w.d_hidden, w.d_model)
+        if w.static_hidden > 0:
+            shapes[f"Ws1.{l}"] = (w.d_model, w.static_hidden)
+            shapes[f"Ws2.{l}"] = (w.static_hidden, w.d_model)
     return shapes
 
 
