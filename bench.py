@@ -253,6 +253,69 @@ def settle_bench(ctx, w, x, P, cpu: bool, n: int = 3) -> dict:
     return out
 
 
+def batch_bench(w, P, seed: int, streams: int, steps: int, warmup: int) -> dict:
+    """Several independent streams advanced by one batched context: every step runs the full
+    stream of each of `streams` token streams (seeds seed .. seed + streams - 1) in lockstep,
+    chunk i of all streams in one chunk step. Reports whole-job tokens/s over all streams and
+    the roofline of the dominant GEMM kind (grouped over the streams)."""
+    import numpy as np
+    import torch
+    import ttt_workloads as W
+    import test_long_context_chunk_amd as ttt
+    T = w.n_tokens
+    dev = {k: ttt.to_device(v, w.precision) for k, v in P.items()}
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * (warmup + steps + 1), streams=streams)
+    del dev
+    tok = np.stack([W.token_stream(w, seed + z).astype(np.int32) for z in range(streams)])
+    tok = torch.from_numpy(tok).cuda()
+    torch.cuda.synchronize()
+    ctx.profile(ttt._binding.KERNEL_KINDS)
+    ctx.prefill_batch(tok)
+    prof = ctx.profile_read()
+    ctx.profile([])
+    gemm_kinds = {k: v for k, v in prof.items() if kind_flops_per_chunk(w, k) > 0}
+    dom = max(gemm_kinds, key=lambda k: gemm_kinds[k][0])
+    for _ in range(warmup):
+        ctx.prefill_batch(tok)
+    torch.cuda.synchronize()
+    ctx.profile([dom], period=PROFILE_PERIOD)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx.prefill_batch(tok)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dprof = ctx.profile_read()
+    ctx.profile([])
+    status = ctx.sync()
+    last = [ctx.token_losses(T * warmup + T, 8, s=z).cpu().numpy() for z in (0, streams - 1)]
+    ctx.close()
+    if status != 0 or not all(np.all(np.isfinite(v)) for v in last):
+        eprint(f"[bench] batched streams: status {status} or non-finite losses")
+        sys.exit(1)
+    value = steps * T * streams / elapsed
+    dom_ms, dom_n = dprof.get(dom, (0.0, 0))
+    launches_per_chunk = max(1, round(prof[dom][1] / w.n_chunks))
+    per_launch = streams * kind_flops_per_chunk(w, dom) / launches_per_chunk
+    avg_s = dom_ms * 1e-3 / max(dom_n, 1)
+    achieved = per_launch / avg_s / 1e12 if avg_s > 0 else 0.0
+    peak = (PEAK_BF16 if w.precision == "bf16" else PEAK_FP32) / 1e12
+    eprint(f"[bench] {streams} batched streams: {value:.0f} tokens/s, {elapsed / steps * 1e3:.1f} ms per step; "
+           f"{dom} {avg_s * 1e6:.1f} us per launch, {achieved:.1f} TFLOP/s")
+    return {
+        "metric": "TTT inner-loop tokens/s over independent streams advanced together (all streams)",
+        "value": value, "unit": "tokens/s", "streams": streams, "tokens_per_step": T * streams,
+        "ms_per_step": elapsed / steps * 1e3, "steps": steps, "warmup": warmup,
+        "frac_of_bf16_peak": value * alg_flops_per_token(w) / PEAK_BF16,
+        "roofline": {
+            "bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": None, "alg_flops_per_launch": per_launch,
+            "avg_launch_us": avg_s * 1e6, "launches": dom_n,
+            "kernel_name": KIND_KERNEL.get(dom, "EpiStoreF32"),
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +328,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-settle", action="store_true")
+    ap.add_argument("--streams", type=int, default=8,
+                    help="independent streams of the batched measurement (0: skip it)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -375,10 +440,15 @@ def main():
         out["decode"] = decode_bench(ctx, w, x, P, cpu=not args.no_cpu_baseline)
     if not args.no_settle:
         out["settle"] = settle_bench(ctx, w, x, P, cpu=not args.no_cpu_baseline)
+    ctx.close()
+    if args.streams > 0:
+        out["batch"] = batch_bench(w, P, args.seed, args.streams, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         eprint(f"[bench] timing the fp64 oracle on {args.cpu_chunks} chunks ...")
         out["cpu_baseline"] = cpu_baseline(w, P, x, args.cpu_chunks)
-    ctx.close()
+        if "batch" in out:
+            # the oracle runs streams one after another: its per-token rate is the same
+            out["batch"]["cpu_baseline"] = out["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

@@ -130,6 +130,28 @@ ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t
 /* Number of streams of the context (-1 for NULL). */
 int32_t ttt_streams(const ttt_ctx* ctx);
 
+/* Frozen layers added to every TTT'd block ([E2E] section 3.1, "two MLP layers per block":
+ * a static MLP in each updated block keeps what pre-training stored while the other MLP is
+ * updated). With static_hidden = m_s > 0 each block is
+ *   h <- h + GELU(norm(h) Ws1) Ws2        (frozen static MLP, its own pre-norm)
+ *   h <- h + MLP(norm(h))                 (the fast MLP of ttt_config)
+ * The inner loop backpropagates through the static MLPs of the blocks above each fast one;
+ * nothing of them is updated. TTT_MLP_GELU only; m_s a multiple of 8.
+ *   ws1[l]  [d x m_s], ws2[l]  [m_s x d]: HOST arrays of n_blocks device pointers, element
+ *   type as the other weights; copied at creation like them. */
+typedef struct {
+  int32_t static_hidden;   /* m_s (0: no static MLP; the arrays are then ignored) */
+  int32_t reserved[3];     /* must be 0 */
+  const void* const* ws1;
+  const void* const* ws2;
+} ttt_block_ext;
+
+/* ttt_create_batch with the block extension (NULL ext: none). Errors: as ttt_create_batch,
+ * TTT_EINVAL for a bad extension (m_s not a multiple of 8, a missing pointer, the SwiGLU
+ * block, nonzero reserved fields). */
+ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt_block_ext* ext, int32_t streams,
+                          void* stream, ttt_ctx** out);
+
 /* Run the inner loop over n_tokens new tokens ([E2E] Method: prefill; section 3 eq. 5).
  * tokens: device int32 [n_tokens + 1]; tokens[0] conditions the first prediction (BOS on
  *         the first call, else the previous call's last token); tokens[1..n_tokens] are

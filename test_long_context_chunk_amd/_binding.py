@@ -29,6 +29,7 @@ KERNEL_KINDS = ["gather", "norm", "transpose", "up", "down", "residual", "ce_fwd
 SIGNATURES = {
     "ttt_create": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p]),
     "ttt_create_batch": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "ttt_create_ext": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "ttt_streams": (c_int32, [c_void_p]),
     "ttt_prefill_chunks": (c_int32, [c_void_p, c_void_p, c_int64]),
     "ttt_prefill_batch": (c_int32, [c_void_p, c_void_p, c_int64, c_int64]),
@@ -70,6 +71,11 @@ class Config(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("lm_head", c_void_p), ("w1", ctypes.POINTER(c_void_p)),
                 ("w_up", ctypes.POINTER(c_void_p)), ("w2", ctypes.POINTER(c_void_p))]
+
+
+class BlockExt(ctypes.Structure):
+    _fields_ = [("static_hidden", c_int32), ("reserved", c_int32 * 3),
+                ("ws1", ctypes.POINTER(c_void_p)), ("ws2", ctypes.POINTER(c_void_p))]
 
 
 class TTTError(RuntimeError):
@@ -151,13 +157,15 @@ class TTT:
 
     def __init__(self, *, vocab: int, d_model: int, d_hidden: int, n_blocks: int, mlp: str,
                  norm: str, precision: str, chunk: int, max_tokens: int, lr: float, clip: float,
-                 rms_eps: float = 1e-6, weights: Dict[str, "object"], stream=None, streams: int = 1):
+                 rms_eps: float = 1e-6, weights: Dict[str, "object"], stream=None, streams: int = 1,
+                 static_hidden: int = 0):
         import torch
         self._lib = load_library()
         self.vocab, self.d_model, self.d_hidden, self.n_blocks = vocab, d_model, d_hidden, n_blocks
         self.mlp, self.norm, self.precision, self.chunk = mlp, norm, precision, chunk
         self.max_tokens = max_tokens
         self.streams = streams
+        self.static_hidden = static_hidden
         self._stream = stream if stream is not None else torch.cuda.current_stream()
         dt = torch.bfloat16 if precision == "bf16" else torch.float32
         for k, t in weights.items():
@@ -174,10 +182,16 @@ class TTT:
                     ctypes.cast(w1, ctypes.POINTER(c_void_p)),
                     ctypes.cast(wup, ctypes.POINTER(c_void_p)) if wup is not None else None,
                     ctypes.cast(w2, ctypes.POINTER(c_void_p)))
+        ext = None
+        if static_hidden > 0:
+            ws1 = (c_void_p * max(L, 1))(*[_ptr(weights[f"Ws1.{l}"]) for l in range(L)])
+            ws2 = (c_void_p * max(L, 1))(*[_ptr(weights[f"Ws2.{l}"]) for l in range(L)])
+            ext = BlockExt(static_hidden, (c_int32 * 3)(0, 0, 0), ctypes.cast(ws1, ctypes.POINTER(c_void_p)),
+                           ctypes.cast(ws2, ctypes.POINTER(c_void_p)))
         ctx = c_void_p()
-        _check(self._lib.ttt_create_batch(ctypes.byref(cfg), ctypes.byref(w), streams,
-                                          c_void_p(_stream_handle(self._stream)), ctypes.byref(ctx)),
-               "ttt_create_batch")
+        _check(self._lib.ttt_create_ext(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ext) if ext else None,
+                                        streams, c_void_p(_stream_handle(self._stream)), ctypes.byref(ctx)),
+               "ttt_create_ext")
         self._ctx = ctx
 
     @classmethod
@@ -185,7 +199,8 @@ class TTT:
         """Create from a workload description (any object with the preset fields)."""
         args = dict(vocab=w.vocab, d_model=w.d_model, d_hidden=w.d_hidden, n_blocks=w.n_blocks,
                     mlp=w.mlp, norm=w.norm, precision=w.precision, chunk=w.chunk,
-                    max_tokens=max_tokens or w.n_tokens, lr=w.lr, clip=w.clip, rms_eps=w.eps)
+                    max_tokens=max_tokens or w.n_tokens, lr=w.lr, clip=w.clip, rms_eps=w.eps,
+                    static_hidden=getattr(w, "static_hidden", 0))
         args.update(kw)
         return cls(weights=weights, stream=stream, **args)
 

@@ -885,7 +885,7 @@ __device__ __forceinline__ void row_partial_store(const EpiPos& p, float (&v)[FM
 template <class T>
 struct EpiGelu {
   T* A;     // [M x lda]
-  T* AT;    // [N x ldat]
+  T* AT;    // [N x ldat] or null
   T* GP;    // [M x lda]
   T* RES;   // [M x lda] or null
   int64_t lda, ldat;
@@ -922,7 +922,7 @@ struct EpiGelu {
         }
       }
       __syncthreads();
-      lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)AT, ldat);
+      if (AT) lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)AT, ldat);
       return;
     }
 #pragma unroll
@@ -947,7 +947,7 @@ struct EpiGelu {
             if (RES) RES[o] = from_f<T>(a[e] - to_f<T>(q));
           }
         }
-        store4_t<T>(AT + (int64_t)col * ldat + r0, a[0], a[1], a[2], a[3], nv);
+        if (AT) store4_t<T>(AT + (int64_t)col * ldat + r0, a[0], a[1], a[2], a[3], nv);
       }
     }
   }
@@ -986,7 +986,7 @@ struct EpiSwiglu {
             if (RES) RES[o] = from_f<T>(a[e] - to_f<T>(q));
           }
         }
-        store4_t<T>(AT + (int64_t)col * ldat + r0, a[0], a[1], a[2], a[3], nv);
+        if (AT) store4_t<T>(AT + (int64_t)col * ldat + r0, a[0], a[1], a[2], a[3], nv);
       }
     }
   }
@@ -999,7 +999,7 @@ template <class T>
 struct EpiDU {
   const T* GP;   // [M x ld]
   T* DU;         // [M x ld]
-  T* DUT;        // [N x ldt]
+  T* DUT;        // [N x ldt] or null
   const T* RES;  // [M x ld] or null
   float* cdot;   // [tiles_n x ldc] or null (ldc >= rows of the stacked output)
   int64_t ld, ldt, ldc;
@@ -1062,7 +1062,7 @@ struct EpiDU {
           }
         }
         __syncthreads();
-        lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
+        if (DUT) lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
         return;
       }
 #pragma unroll 1
@@ -1093,7 +1093,7 @@ struct EpiDU {
         }
       }
       __syncthreads();
-      lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
+      if (DUT) lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
       return;
     }
 #pragma unroll
@@ -1115,7 +1115,7 @@ struct EpiDU {
             if (RES) dots[i][e] += acc[i][j][e] * to_f<T>(RES[o]);
           }
         }
-        store4_t<T>(DUT + (int64_t)col * ldt + r0, v[0], v[1], v[2], v[3], nv);
+        if (DUT) store4_t<T>(DUT + (int64_t)col * ldt + r0, v[0], v[1], v[2], v[3], nv);
       }
     }
     if (cdot) row_partial_store<FM>(p, dots, cdot, ldc);

@@ -51,6 +51,18 @@ struct Block {
   void* ResA = nullptr;     // bf16 only: A - rn(A) [R x m]
   float* VU = nullptr;      // SwiGLU + bf16: up projection n Wu [R x m] fp32
   int cslot = 0;            // first loss-compensation slot of this block
+  // frozen static MLP before the fast one (m_s > 0): its weights in both orientations, and
+  // what its backward reads
+  void* SW1T = nullptr;     // Ws1^T [m_s x d] (forward)
+  void* SW2T = nullptr;     // Ws2^T [d x m_s] (forward)
+  void* SW1 = nullptr;      // Ws1 [d x m_s] (backward)
+  void* SW2 = nullptr;      // Ws2 [m_s x d] (backward)
+  void* Sn = nullptr;       // its normed input [R x d]
+  float* Sr = nullptr;      // its RMSNorm scale [R]
+  void* SGP = nullptr;      // GELU'(U_s) [R x m_s]
+  void* SResN = nullptr;    // bf16 only: n_s - rn(n_s) [R x d]
+  void* SResA = nullptr;    // bf16 only: A_s - rn(A_s) [R x m_s]
+  int scslot = 0;           // first loss-compensation slot of the static MLP
 };
 
 }  // namespace
@@ -63,6 +75,8 @@ struct ttt_ctx {
   // independent token streams advanced together (each with its own fast state, records and
   // clip); a step covers R = nb b token rows, Rp = nb bp columns of the transposed buffers
   int nb = 1, R = 0, Rp = 0;
+  int ms = 0;          // hidden size of the static MLP of every block (0: none)
+  int dot_tiles_s = 0;  // column tiles of the static dA GEMM
   std::vector<void*> allocs;
 
   void *E_in = nullptr, *E_out = nullptr, *E_outT = nullptr;
@@ -195,6 +209,27 @@ ttt_status validate(const ttt_config* c, const ttt_weights* w) {
   return TTT_OK;
 }
 
+ttt_status validate_ext(const ttt_config* c, const ttt_block_ext* e) {
+  if (!e || e->static_hidden == 0) return TTT_OK;
+  if (e->reserved[0] || e->reserved[1] || e->reserved[2]) return TTT_EINVAL;
+  if (e->static_hidden < 8 || e->static_hidden % 8 || c->mlp != TTT_MLP_GELU) return TTT_EINVAL;
+  if (c->n_blocks > 0) {
+    if (!e->ws1 || !e->ws2) return TTT_EINVAL;
+    for (int l = 0; l < c->n_blocks; ++l)
+      if (!e->ws1[l] || !e->ws2[l]) return TTT_EINVAL;
+  }
+  return TTT_OK;
+}
+
+// A frozen weight [rows x cols] copied into the library in natural and transposed layout.
+void frozen_pair(ttt_ctx* c, const void* src, int rows, int cols, void** nat, void** tr) {
+  const int64_t bytes = (int64_t)rows * cols * c->es;
+  *nat = dalloc<char>(c, bytes);
+  *tr = dalloc<char>(c, bytes);
+  check(hipMemcpyAsync(*nat, src, bytes, hipMemcpyDeviceToDevice, c->st));
+  check(run_transpose(c->st, c->prec, src, cols, rows, cols, *tr, rows));
+}
+
 void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
   const int64_t n = (int64_t)rows * cols;
   f.rows = rows;
@@ -229,9 +264,10 @@ void reset_fast(ttt_ctx* c, FastTensor& f) {
   }
 }
 
-void build(ttt_ctx* c, const ttt_weights* w) {
+void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   const int b = c->b, V = c->V, d = c->d, m = c->m, L = c->L, es = c->es;
-  const int Rr = c->R, Rp = c->Rp, nb = c->nb;
+  const int Rr = c->R, Rp = c->Rp, nb = c->nb, ms = c->ms;
+  const int mx = m > ms ? m : ms;  // widest hidden activation
   const int64_t Vd = (int64_t)V * d;
   c->E_in = dalloc<char>(c, Vd * es);
   c->E_out = dalloc<char>(c, Vd * es);
@@ -245,6 +281,13 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   gemm_tile_shape(c->prec, b, m, d, 0, 1, &tmm, &tnm_w);  // the dA GEMM (M = b, N = m, K = d)
   const int tnm = cdiv(m, tnm_w);
   c->dot_tiles = tnm;
+  int tns = 0;
+  if (ms > 0) {
+    int tsm = 0, tsn = 0;
+    gemm_tile_shape(c->prec, Rr, ms, d, 0, 1, &tsm, &tsn);  // the static dA GEMM
+    tns = cdiv(ms, tsn);
+  }
+  c->dot_tiles_s = tns;
   c->ncslot = 1;  // slot 0: the LM-head input Y
   c->blocks.resize(L);
   for (int l = 0; l < L; ++l) {
@@ -268,6 +311,19 @@ void build(ttt_ctx* c, const ttt_weights* w) {
       }
     }
     init_fast(c, B.w2, m, d, w->w2[l]);
+    if (ms > 0) {
+      frozen_pair(c, ext->ws1[l], d, ms, &B.SW1, &B.SW1T);
+      frozen_pair(c, ext->ws2[l], ms, d, &B.SW2, &B.SW2T);
+      B.Sn = dalloc<char>(c, (int64_t)Rr * d * es);
+      B.Sr = dalloc<float>(c, (int64_t)Rr * 4);
+      B.SGP = dalloc<char>(c, (int64_t)Rr * ms * es);
+      if (c->foc) {
+        B.SResN = dalloc<char>(c, (int64_t)Rr * d * es);
+        B.SResA = dalloc<char>(c, (int64_t)Rr * ms * es);
+        B.scslot = c->ncslot;
+        c->ncslot += tns + 1;  // tns partial dots for A_s, one for n_s
+      }
+    }
     B.Hn = dalloc<char>(c, (int64_t)Rr * d * es);
     B.r = dalloc<float>(c, (int64_t)Rr * 4);
     B.AT = dalloc<char>(c, (int64_t)m * Rp * es);
@@ -301,7 +357,7 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->settle_A = dalloc<float>(c, 4);
   c->settle_commit = dalloc<int>(c, 4);
   c->dec_h = dalloc<float>(c, (int64_t)d * 4);
-  c->dec_a = dalloc<float>(c, (int64_t)m * 4);
+  c->dec_a = dalloc<float>(c, (int64_t)mx * 4);
   c->dec_z = dalloc<float>(c, (int64_t)V * 4);
   c->dec_rmax = dalloc<float>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
   c->dec_rsum = dalloc<float>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
@@ -310,8 +366,8 @@ void build(ttt_ctx* c, const ttt_weights* w) {
   c->dHb = dalloc<char>(c, (int64_t)Rr * d * es);
   c->dHT = dalloc<char>(c, (int64_t)d * Rp * es);
   check(hipMemsetAsync(c->dHT, 0, (int64_t)d * Rp * es, c->st));
-  c->A = dalloc<char>(c, (int64_t)Rr * m * es);
-  c->dU = dalloc<char>(c, (int64_t)Rr * m * es);
+  c->A = dalloc<char>(c, (int64_t)Rr * mx * es);
+  c->dU = dalloc<char>(c, (int64_t)Rr * mx * es);
   c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
   check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
   if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)Rr * m * 4);
@@ -430,17 +486,44 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     return g;
   };
 
+  const int ms = c->ms;
+  // where a row kernel leaves the pre-norm of the next MLP: block l's static MLP (when the
+  // blocks have one) comes before its fast MLP
+  struct NormOut {
+    void* n = nullptr;
+    float* r = nullptr;
+    void* res = nullptr;
+  };
+  auto first_norm = [&](int l) {
+    NormOut o;
+    if (l >= L) return o;
+    Block& B = c->blocks[l];
+    o.n = ms > 0 ? B.Sn : B.Hn;
+    o.r = ms > 0 ? B.Sr : B.r;
+    o.res = foc ? (ms > 0 ? B.SResN : B.ResN) : nullptr;
+    return o;
+  };
+
   // a1 gather, and a2 the lowest block's pre-norm
   {
-    Block* B0 = L > 0 ? &c->blocks[0] : nullptr;
+    const NormOut o = first_norm(0);
     RUN(TTT_K_GATHER, run_row_in(st, prec, tok, srt, V, c->E_in, c->tok_prev, c->tok_tgt, c->err, nullptr, 0, 0, c->H,
-                                 Rr, d, L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, B0 ? B0->Hn : nullptr,
-                                 B0 ? B0->r : nullptr, B0 && foc ? B0->ResN : nullptr));
+                                 Rr, d, L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res));
   }
 
   // a2-a4 forward through the blocks
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
+    if (ms > 0) {
+      // the frozen static MLP ([E2E] section 3.1), once over all streams' rows; its
+      // transposed activation is never needed
+      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Sn, d, B.SW1T, d, Rr, ms, d, c->A, nullptr, B.SGP, foc ? B.SResA : nullptr,
+                              ms, 0));
+      const int Ss = gemm_split_k(prec, Rr, d, ms, 0, SPLIT_MAX);
+      RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, ms, B.SW2T, ms, Rr, d, ms, Ss, c->part, d, Rd, 0));
+      RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, Ss, Rd,
+                                     c->H, Rr, d, nullptr, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
+    }
     if (gelu) {
       // Hn^T is read only by the W1 gradient of the backward pass
       if (train) check(run_transpose(st, prec, B.Hn, d, Rr, d, B.HnT, Rp));
@@ -461,10 +544,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, Rd, 0, s2,
                              fw(b, m, n2, bf)));
     // a4 residual, and a2 the next block's pre-norm
-    Block* Bn = l + 1 < L ? &c->blocks[l + 1] : nullptr;
+    const NormOut o = first_norm(l + 1);
     RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, S, Rd, c->H,
-                                   Rr, d, l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, Bn ? Bn->Hn : nullptr,
-                                   Bn ? Bn->r : nullptr, Bn && foc ? Bn->ResN : nullptr));
+                                   Rr, d, l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res));
   }
 
   // a5 LM head + CE forward: online softmax over vocabulary records; the numerators are kept
@@ -501,15 +583,32 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, Rp, c->dUT, Rp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0,
                                   gradg(c->nslots)));
         }
-        // the block input gradient is needed below this block, and for the compensation of
-        // a rounded n (the lowest block's n = E_in[x] is exact when there is no norm)
-        if (l > 0 || (foc && rms)) {
+        // the fast MLP's input gradient is needed below it (a lower block, or this block's
+        // static MLP while the loss compensation runs), and for the compensation of a
+        // rounded n (the lowest block's n = E_in[x] is exact when there is no norm and no
+        // static MLP)
+        const bool below = l > 0 || (ms > 0 && foc);
+        if (below || (foc && rms)) {
           const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
                                   fw(b, m, n1, false)));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, c->dHb,
-                                           foc ? B.ResN : nullptr, cN, l > 0));
-          if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+                                           foc ? B.ResN : nullptr, cN, below));
+          if (ms == 0 && l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+        }
+        if (ms > 0 && below) {
+          // back through the static MLP (frozen: no weight gradient), once over all rows
+          float* cAs = foc ? c->cpart + (int64_t)B.scslot * Rr : nullptr;
+          float* cNs = foc ? c->cpart + (int64_t)(B.scslot + c->dot_tiles_s) * Rr : nullptr;
+          RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.SW2, d, Rr, ms, d, B.SGP, c->dU, nullptr,
+                                foc ? B.SResA : nullptr, cAs, ms, 0, Rr));
+          if (l > 0 || (foc && rms)) {
+            const int Ss = gemm_split_k(prec, Rr, d, ms, 0, SPLIT_MAX);
+            RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, ms, B.SW1, ms, Rr, d, ms, Ss, c->part, d, Rd, 0));
+            RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Ss, Rd, B.Sn, B.Sr, Rr, d, rms, c->dH, c->dHb,
+                                             foc ? B.SResN : nullptr, cNs, l > 0));
+            if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+          }
         }
       } else if (train) {
         RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
@@ -580,10 +679,20 @@ void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out)
   gh.eps = eps;
   GemvIn ga;  // the block's activation row
   ga.xin = c->dec_a;
+  bool gathered = false;  // the first product of the token gathers its embedding
+  auto next_in = [&]() {
+    GemvIn in = gathered ? gh : g0;
+    in.norm = rms;
+    gathered = true;
+    return in;
+  };
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
-    GemvIn in = l == 0 ? g0 : gh;
-    in.norm = rms;
+    if (c->ms > 0) {  // the frozen static MLP first
+      RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_GELU, next_in(), d, B.SW1T, nullptr, d, c->ms, c->dec_a));
+      RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_RESIDUAL, ga, c->ms, B.SW2T, nullptr, c->ms, d, c->dec_h));
+    }
+    GemvIn in = next_in();
     if (gelu)
       RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_GELU, in, d, bf ? B.w1.W0T : B.w1.WtT, bf ? B.w1.WtT : nullptr, d, m,
                                    c->dec_a));
@@ -651,11 +760,13 @@ ttt_status read_sticky(ttt_ctx* c) {
 
 extern "C" {
 
-ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t streams, void* stream,
-                            ttt_ctx** out) {
+ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt_block_ext* ext, int32_t streams,
+                          void* stream, ttt_ctx** out) {
   if (!out) return TTT_EINVAL;
   *out = nullptr;
   ttt_status v = validate(cfg, w);
+  if (v != TTT_OK) return v;
+  v = validate_ext(cfg, ext);
   if (v != TTT_OK) return v;
   if (streams < 1 || streams > TTT_MAX_STREAMS) return TTT_EINVAL;
   // several streams stack their rows: whole PAD-wide column groups per stream in the
@@ -674,12 +785,13 @@ ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t
   c->nb = streams;
   c->R = streams * c->b;
   c->Rp = streams * c->bp;
+  c->ms = ext ? ext->static_hidden : 0;
   c->V = cfg->vocab;
   c->d = cfg->d_model;
   c->m = cfg->d_hidden;
   c->L = cfg->n_blocks;
   try {
-    build(c, w);
+    build(c, w, ext);
     check(hipStreamSynchronize(c->st));
   } catch (const HipFail& f) {
     (void)hipStreamSynchronize(c->st);
@@ -699,7 +811,12 @@ ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t
 }
 
 ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out) {
-  return ttt_create_batch(cfg, w, 1, stream, out);
+  return ttt_create_ext(cfg, w, nullptr, 1, stream, out);
+}
+
+ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t streams, void* stream,
+                            ttt_ctx** out) {
+  return ttt_create_ext(cfg, w, nullptr, streams, stream, out);
 }
 
 int32_t ttt_streams(const ttt_ctx* c) { return c ? c->nb : -1; }

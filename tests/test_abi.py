@@ -102,6 +102,29 @@ def test_create_batch_rejects_bad_stream_counts_before_touching_a_device(lib, st
     assert out.value is None
 
 
+@pytest.mark.parametrize("ms,reserved,mlp,ptrs", [
+    (12, 0, 0, True),   # static hidden size not a multiple of 8
+    (4, 0, 0, True),    # below 8
+    (16, 1, 0, True),   # reserved field set
+    (16, 0, 1, True),   # static MLP with the SwiGLU block
+    (16, 0, 0, False),  # missing weight arrays
+])
+def test_create_ext_rejects_bad_extensions_before_touching_a_device(lib, ms, reserved, mlp, ptrs):
+    cfg = _cfg(mlp=mlp)
+    dummy = (ctypes.c_void_p * 1)(1)
+    arr = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_void_p))
+    w = B.Weights(1, 1, arr, arr if mlp == 1 else None, arr)
+    ext = B.BlockExt(ms, (ctypes.c_int32 * 3)(reserved, 0, 0), arr if ptrs else None, arr if ptrs else None)
+    out = ctypes.c_void_p(12345)
+    assert lib.ttt_create_ext(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ext), 1, None, ctypes.byref(out)) == -1
+    assert out.value is None
+
+
+def test_block_ext_struct_layout_matches_header():
+    assert B.BlockExt.ws1.offset == 16
+    assert ctypes.sizeof(B.BlockExt) == 16 + 2 * ctypes.sizeof(ctypes.c_void_p)
+
+
 def test_null_context_calls_are_rejected(lib):
     assert lib.ttt_prefill_chunks(None, None, 8) == -1
     assert lib.ttt_token_losses(None, None, 0, 0) == -1

@@ -107,10 +107,10 @@ def test_batched_chunk_smaller_than_a_tile(ttt_lib):
         compare(g, oracle_run(w, P, x, 2), w, "bf16", 2, label=f"batch-5 stream {z}")
 
 
-@pytest.mark.parametrize("streams", [4])
+@pytest.mark.parametrize("streams", [8])
 def test_s760m_batched_sampled(ttt_lib, streams):
-    """The 760M shape in the batched benchmark's launch configuration (4 streams, chunk
-    1024), 4 chunks: streams 0 and 3 (sampled) against the oracle, every stream finite."""
+    """The 760M shape in the batched benchmark's launch configuration (8 streams, chunk
+    1024), 4 chunks: streams 0 and 7 (sampled) against the oracle, every stream finite."""
     w = W.preset("s760m", n_tokens=4096)
     P = W.init_weights(w, 0)
     xs = [W.token_stream(w, z) for z in range(streams)]
