@@ -16,9 +16,11 @@ hand-derived backpropagation, written from these pages:
         - section 3, eq. (5): mini-batch update
               W_i = W_{i-1} - eta * (1/b) * sum_{t in chunk i} grad l_t(W_{i-1}).
         - section 3, eq. (6): L(W_0; X) = (1/T) sum_i sum_{t in chunk i} l_t(W_{i-1}).
-        - section 3.1: only the MLP layers are updated; embedding and normalisation
-          layers stay frozen; "two MLP layers per block": a static MLP is added to
-          each TTT'd block to hold pre-trained knowledge, and only the other is updated.
+        - section 3: sliding-window attention of a fixed window k, with k >= b so that
+          the tokens of a mini-batch see each other before the step.
+        - section 3.1: only the MLP layers are updated; embedding, normalisation and
+          attention layers stay frozen; "two MLP layers per block": a static MLP is added
+          to each TTT'd block to hold pre-trained knowledge, and only the other is updated.
   [IPT] "[논문리뷰] In-Place Test-Time Training" (blog.secrett2633.cloud)
         - section 1 (Key Terms): the MLP block's final projection is the fast
           weight; the sequence is split into chunks updated one after another.
@@ -34,6 +36,14 @@ notes of the repository):
   * the static MLP (when present) is a frozen GELU MLP with its own pre-norm and residual,
     placed before the fast MLP of the same block: h <- h + GELU(norm(h) Ws1) Ws2, then
     h <- h + MLP_fast(norm(h)).
+  * sliding-window attention (when present) comes first in each block, with its own
+    pre-norm and residual: H heads of size d/H, q = n Wq, k = n Wk, v = n Wv, softmax of
+    q.k / sqrt(d/H) over the keys of the last `window` positions up to and including the
+    query's own, o = sum p v, output o Wo; no positional encoding (the causal window is the
+    only order the pages give). Row t of the stream (conditioning token x_t) is position t.
+    Each position's key and value are computed once, when its chunk is processed, at that
+    chunk's weights W_{i-1}; later chunks read them as constants (no gradient flows into an
+    earlier chunk's keys or values).
   * GELU is the exact erf form; its derivative is Phi(u) + u * phi(u).
   * SwiGLU block (In-Place shape): a = SiLU(n Wg) * (n Wu); Wg, Wu frozen, W2 fast.
   * clipping: global L2 norm g over all fast tensors of the chunk-mean gradient,
@@ -42,7 +52,7 @@ notes of the repository):
   * argmax ties resolve to the lowest index.
 
 Arrays: E_in, E_out [V, d]; W1, Wg, Wu [d, m]; W2 [m, d]; Ws1 [d, m_s]; Ws2 [m_s, d];
-all row-major, rows of activations are tokens.
+Wq, Wk, Wv, Wo [d, d]; all row-major, rows of activations are tokens.
 """
 from __future__ import annotations
 
@@ -70,13 +80,16 @@ class Model:
     lr: float = 0.0          # eta
     clip: float = 0.0        # c; <= 0 disables clipping
     static_hidden: int = 0   # m_s of the frozen static MLP in every block (0: none)
+    swa_window: int = 0      # keys per query of the frozen sliding-window attention (0: none)
+    swa_heads: int = 0       # its heads (head size d / heads)
 
     @classmethod
     def from_workload(cls, w, **kw) -> "Model":
         base = dict(vocab=w.vocab, d_model=w.d_model, d_hidden=w.d_hidden,
                     n_blocks=w.n_blocks, mlp=w.mlp, norm=w.norm, eps=w.eps,
                     chunk=w.chunk, lr=w.lr, clip=w.clip,
-                    static_hidden=getattr(w, "static_hidden", 0))
+                    static_hidden=getattr(w, "static_hidden", 0),
+                    swa_window=getattr(w, "swa_window", 0), swa_heads=getattr(w, "swa_heads", 0))
         base.update(kw)
         return cls(**base)
 
@@ -149,17 +162,100 @@ def static_mlp_backward(model: Model, P, l: int, c, dh: np.ndarray) -> np.ndarra
     return dh + pre_norm_backward(model, c["ns"], c["rs"], dn)
 
 
-def forward(model: Model, P: Dict[str, np.ndarray], x_prev: np.ndarray):
+def window_mask(nc: int, b: int, window: int) -> np.ndarray:
+    """[b, nc + b] boolean: query i (position nc + i) sees key j (position j) when
+    pos_i - window < j <= pos_i, i.e. the last `window` positions up to its own."""
+    pq = nc + np.arange(b)[:, None]
+    pk = np.arange(nc + b)[None, :]
+    return (pk <= pq) & (pk > pq - window)
+
+
+def swa_forward(model: Model, P, l: int, n: np.ndarray, kv):
+    """Sliding-window attention of block l over the chunk's rows (normed input n [b, d]).
+
+    kv: the keys and values of the positions before the chunk (dict k, v [n_c, d], n_c <
+    window; None for none). Query i sits at position n_c + i, key j of [cached; chunk] at j;
+    query i sees keys j with pos_i - window < j <= pos_i. Returns the output [b, d] and what
+    the backward needs (including the chunk's own keys and values, for the next chunk)."""
+    b, d = n.shape
+    H = model.swa_heads
+    dh = d // H
+    q = n @ P[f"Wq.{l}"]
+    k = n @ P[f"Wk.{l}"]
+    v = n @ P[f"Wv.{l}"]
+    kc = kv["k"] if kv is not None else np.zeros((0, d))
+    vc = kv["v"] if kv is not None else np.zeros((0, d))
+    K = np.vstack([kc, k])
+    V = np.vstack([vc, v])
+    nc = kc.shape[0]
+    mask = window_mask(nc, b, model.swa_window)
+    o = np.zeros((b, d))
+    probs = []
+    for hd in range(H):
+        cs = slice(hd * dh, (hd + 1) * dh)
+        sc = (q[:, cs] @ K[:, cs].T) / math.sqrt(dh)
+        sc = np.where(mask, sc, -np.inf)
+        mx = sc.max(axis=1, keepdims=True)
+        e = np.exp(sc - mx)
+        p = e / e.sum(axis=1, keepdims=True)
+        o[:, cs] = p @ V[:, cs]
+        probs.append(p)
+    return o @ P[f"Wo.{l}"], dict(q=q, k=k, v=v, K=K, V=V, probs=probs, o=o, nc=nc)
+
+
+def swa_backward(model: Model, P, l: int, c, dh: np.ndarray) -> np.ndarray:
+    """Gradient at the attention's normed input from the gradient dh at its output (frozen
+    weights; the cached keys and values of earlier chunks are constants)."""
+    a = c["att"]
+    b, d = dh.shape
+    H = model.swa_heads
+    dhd = d // H
+    do = dh @ P[f"Wo.{l}"].T
+    dq = np.zeros((b, d))
+    dK = np.zeros_like(a["K"])
+    dV = np.zeros_like(a["V"])
+    for hd in range(H):
+        cs = slice(hd * dhd, (hd + 1) * dhd)
+        p = a["probs"][hd]
+        dV[:, cs] = p.T @ do[:, cs]
+        dp = do[:, cs] @ a["V"][:, cs].T
+        ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+        dq[:, cs] = ds @ a["K"][:, cs] / math.sqrt(dhd)
+        dK[:, cs] = ds.T @ a["q"][:, cs] / math.sqrt(dhd)
+    nc = a["nc"]
+    dk, dv = dK[nc:], dV[nc:]
+    return dq @ P[f"Wq.{l}"].T + dk @ P[f"Wk.{l}"].T + dv @ P[f"Wv.{l}"].T
+
+
+def next_kv(model: Model, kv, c):
+    """The cache after a chunk: the last window - 1 positions of [cached; chunk]."""
+    keep = model.swa_window - 1
+    out = []
+    for l in range(model.n_blocks):
+        a = c[l]["att"]
+        out.append(dict(k=a["K"][a["K"].shape[0] - keep:] if keep > 0 else a["K"][:0],
+                        v=a["V"][a["V"].shape[0] - keep:] if keep > 0 else a["V"][:0]))
+    return out
+
+
+def forward(model: Model, P: Dict[str, np.ndarray], x_prev: np.ndarray, kv=None):
     """Hidden state h^L for each conditioning token x_{t-1}, plus a cache for backprop.
 
     [E2E] section 1: f reads only x_{t-1} in the MLP-only model. The stack is
     h^0 = E_in[x_{t-1}]; h^l = h^{l-1} + MLP_l(norm(h^{l-1})), with the frozen static MLP
-    of the block first when the model has one ([E2E] section 3.1).
+    of the block first when the model has one ([E2E] section 3.1), and the frozen
+    sliding-window attention before both when the model has one ([E2E] section 3; kv holds
+    each block's keys and values of the positions before these rows).
     """
     h = P["E_in"][x_prev]
     cache = []
     for l in range(model.n_blocks):
         c = {}
+        if model.swa_window > 0:
+            na, ra = pre_norm(model, h)
+            out, att = swa_forward(model, P, l, na, kv[l] if kv is not None else None)
+            h = h + out
+            c.update(na=na, ra=ra, att=att)
         if model.static_hidden > 0:
             ns, rs = pre_norm(model, h)
             us = ns @ P[f"Ws1.{l}"]
@@ -181,8 +277,8 @@ def forward(model: Model, P: Dict[str, np.ndarray], x_prev: np.ndarray):
     return h, cache
 
 
-def logits(model: Model, P, x_prev):
-    h, cache = forward(model, P, x_prev)
+def logits(model: Model, P, x_prev, kv=None):
+    h, cache = forward(model, P, x_prev, kv)
     return h @ P["E_out"].T, h, cache
 
 
@@ -200,17 +296,17 @@ def ce_stats(z: np.ndarray, x_tgt: np.ndarray):
     return loss, lse, am.astype(np.int64), margin
 
 
-def token_losses(model: Model, P, x_prev, x_tgt):
+def token_losses(model: Model, P, x_prev, x_tgt, kv=None):
     """[E2E] eq. (1): l_t = CE(f(x_{t-1}; W), x_t) = logsumexp(z_t) - z_t[x_t].
 
     Also returns argmax_t (lowest index on ties) and the top-2 logit margin.
     """
-    z, _, _ = logits(model, P, x_prev)
+    z, _, _ = logits(model, P, x_prev, kv)
     loss, _, am, margin = ce_stats(z, x_tgt)
     return loss, am, margin
 
 
-def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None):
+def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None, kv=None):
     """Mean chunk loss (1/b) sum_t l_t(W) and its gradient w.r.t. every fast tensor.
 
     This is the quantity differentiated in [E2E] eq. (5). Backprop by hand:
@@ -222,10 +318,13 @@ def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None):
         rms:    dh <- dh + r * (dn - n * mean_j(dn_j n_j))
         none:   dh <- dh + dn
         static MLP below the fast one: dh <- its input gradient (static_mlp_backward)
+        attention below both: dh <- dh + norm'(swa_backward(dh))
       (the embedding is frozen, so the lowest block stops after its weight grads)
+    With attention, kv holds the earlier positions' keys and values, and the returned info
+    carries the cache after this chunk ("kv").
     """
     b = x_prev.shape[0]
-    z, h, cache = logits(model, P, x_prev)
+    z, h, cache = logits(model, P, x_prev, kv)
     if logit_probe is not None:
         logit_probe(z)
     losses, lse, am, margin = ce_stats(z, x_tgt)
@@ -257,7 +356,12 @@ def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None):
         dh = dh + pre_norm_backward(model, c["n"], c["r"], dn)
         if model.static_hidden > 0:
             dh = static_mlp_backward(model, P, l, c, dh)
-    return float(losses.mean()), dict(losses=losses, argmax=am, margin=margin), grads
+        if model.swa_window > 0:
+            dh = dh + pre_norm_backward(model, c["na"], c["ra"], swa_backward(model, P, l, c, dh))
+    info = dict(losses=losses, argmax=am, margin=margin)
+    if model.swa_window > 0:
+        info["kv"] = next_kv(model, kv, cache)
+    return float(losses.mean()), info, grads
 
 
 def clip_scale(g: float, c: float) -> float:
@@ -305,6 +409,7 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
     D = {k: np.zeros_like(P0[k]) for k in keys}
     losses, argm, marg = [], [], []
     gn, sc, sk = [], [], []
+    kv = None  # attention: keys and values of the positions before the chunk
     for i in range(nc):
         P = dict(P0)
         for k in keys:
@@ -312,7 +417,8 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
         x_prev = tokens[i * b: i * b + b]
         x_tgt = tokens[i * b + 1: i * b + b + 1]
         _, st, G = chunk_loss_and_grads(model, P, x_prev, x_tgt, logit_probe=(
-            None if logit_probe is None else (lambda z, i=i: logit_probe(i, z))))
+            None if logit_probe is None else (lambda z, i=i: logit_probe(i, z))), kv=kv)
+        kv = st.get("kv")
         losses.append(st["losses"])
         argm.append(st["argmax"])
         marg.append(st["margin"])
@@ -347,6 +453,8 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
     the clipped mini-batch step of [E2E] eq. (5) / [SGF]. logit_probe(t - 1, z), when given,
     sees the logits row that scored token t.
     """
+    if model.swa_window > 0:
+        raise NotImplementedError("decoding with sliding-window attention")
     P0 = as_f64(P0)
     tokens = np.asarray(tokens, dtype=np.int64)
     b = model.chunk
@@ -392,6 +500,8 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
 
 def passage_loss(model: Model, P: Dict[str, np.ndarray], q: np.ndarray) -> float:
     """L(q, W): the mean next-token loss of a passage q_0..q_n at fixed weights (no step)."""
+    if model.swa_window > 0:
+        raise NotImplementedError("passage evaluation with sliding-window attention")
     q = np.asarray(q, dtype=np.int64)
     l, _, _ = token_losses(model, as_f64(P), q[:-1], q[1:])
     return float(l.mean())
@@ -425,9 +535,13 @@ def static_losses(model: Model, P0, tokens, n_tokens: Optional[int] = None) -> n
     tokens = np.asarray(tokens, dtype=np.int64)
     T = tokens.shape[0] - 1 if n_tokens is None else n_tokens
     out = []
-    step = 4096
+    step = 4096 if model.swa_window == 0 else max(model.chunk, 1)
+    kv = None
     for s in range(0, T, step):
         e = min(T, s + step)
-        l, _, _ = token_losses(model, P0, tokens[s:e], tokens[s + 1:e + 1])
+        z, _, cache = logits(model, P0, tokens[s:e], kv)
+        l, _, _, _ = ce_stats(z, tokens[s + 1:e + 1])
+        if model.swa_window > 0:
+            kv = next_kv(model, kv, cache)
         out.append(l)
     return np.concatenate(out)

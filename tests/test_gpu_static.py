@@ -19,7 +19,7 @@ import ttt_workloads as W
 pytestmark = pytest.mark.gpu
 
 SMALL = dict(vocab=2000, d_model=128, d_hidden=256, n_blocks=3, n_tokens=256, chunk=64, static_hidden=192,
-             lr=0.05)
+             lr=0.05, swa_window=0, swa_heads=0)
 
 
 def _tok(x):
@@ -87,7 +87,7 @@ def test_static_mlp_decode_matches_oracle_decode(ttt_lib, precision):
 def test_e2e760m_two_chunks_sampled(ttt_lib):
     """The fuller-block 760M shape (d=1536, fast and static hidden 3072, 3 blocks) in the
     benchmark's launch configuration: the first two chunks against the oracle."""
-    w = W.preset("e2e760m", n_tokens=2048)
+    w = W.preset("e2e760m", n_tokens=2048, swa_window=0, swa_heads=0)
     P = W.init_weights(w, 0)
     x = W.token_stream(w, 0)
     log("static e2e760m")

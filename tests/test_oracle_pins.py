@@ -20,9 +20,9 @@ import oracle.ttt_oracle as O
 import ttt_workloads as W
 
 
-def tiny_model(mlp="gelu", norm="none", L=2, b=3, lr=0.3, clip=0.0, V=11, d=6, m=10, ms=0):
+def tiny_model(mlp="gelu", norm="none", L=2, b=3, lr=0.3, clip=0.0, V=11, d=6, m=10, ms=0, win=0, heads=0):
     return O.Model(vocab=V, d_model=d, d_hidden=m, n_blocks=L, mlp=mlp, norm=norm,
-                   eps=1e-6, chunk=b, lr=lr, clip=clip, static_hidden=ms)
+                   eps=1e-6, chunk=b, lr=lr, clip=clip, static_hidden=ms, swa_window=win, swa_heads=heads)
 
 
 def tiny_params(model, seed=0, std=0.5):
@@ -39,6 +39,9 @@ def tiny_params(model, seed=0, std=0.5):
     for l in range(model.n_blocks if model.static_hidden > 0 else 0):
         P[f"Ws1.{l}"] = rng.normal(0, std, (model.d_model, model.static_hidden))
         P[f"Ws2.{l}"] = rng.normal(0, std, (model.static_hidden, model.d_model))
+    for l in range(model.n_blocks if model.swa_window > 0 else 0):
+        for n in ("Wq", "Wk", "Wv", "Wo"):
+            P[f"{n}.{l}"] = rng.normal(0, std, (model.d_model, model.d_model))
     return P
 
 
@@ -207,11 +210,12 @@ def torch_ttt(model, P0, tokens):
     """Independent implementation of eq. (5)/(6) + clipped step with torch fp64 autograd."""
     t = lambda a: torch.tensor(a, dtype=torch.float64)
     E_in, E_out = t(P0["E_in"]), t(P0["E_out"])
-    frozen = {k: t(v) for k, v in P0.items() if k.startswith(("Wg", "Wu", "Ws"))}
+    frozen = {k: t(v) for k, v in P0.items() if k.startswith(("Wg", "Wu", "Ws", "Wq", "Wk", "Wv", "Wo"))}
     fast = {k: t(P0[k]) for k in model.fast_keys()}
     x = torch.tensor(np.asarray(tokens), dtype=torch.long)
     b = model.chunk
     losses, gnorms = [], []
+    past = [None] * model.n_blocks  # attention: detached keys/values of earlier positions
     for i in range((len(tokens) - 1) // b):
         params = {k: v.clone().requires_grad_(True) for k, v in fast.items()}
         ctx, tgt = x[i * b:(i + 1) * b], x[i * b + 1:(i + 1) * b + 1]
@@ -223,6 +227,22 @@ def torch_ttt(model, P0, tokens):
             return v
 
         for l in range(model.n_blocks):
+            if model.swa_window > 0:
+                na = norm(h)
+                q, k, v = na @ frozen[f"Wq.{l}"], na @ frozen[f"Wk.{l}"], na @ frozen[f"Wv.{l}"]
+                K = k if past[l] is None else torch.cat([past[l][0], k])
+                Vv = v if past[l] is None else torch.cat([past[l][1], v])
+                start = i * b - (K.shape[0] - b)  # absolute position of the first key
+                pq = torch.arange(i * b, i * b + b)[:, None]
+                pk = torch.arange(start, start + K.shape[0])[None, :]
+                allowed = (pk <= pq) & (pk > pq - model.swa_window)
+                H = model.swa_heads
+                split = lambda a: a.reshape(a.shape[0], H, -1).transpose(0, 1)
+                o = torch.nn.functional.scaled_dot_product_attention(split(q), split(K), split(Vv),
+                                                                     attn_mask=allowed)
+                h = h + o.transpose(0, 1).reshape(b, -1) @ frozen[f"Wo.{l}"]
+                keep = model.swa_window - 1
+                past[l] = (K[K.shape[0] - keep:].detach(), Vv[Vv.shape[0] - keep:].detach()) if keep > 0 else None
             if model.static_hidden > 0:
                 hs = torch.nn.functional.gelu(norm(h) @ frozen[f"Ws1.{l}"], approximate="none")
                 h = h + hs @ frozen[f"Ws2.{l}"]
@@ -282,6 +302,80 @@ def test_p1_finite_differences_through_static_mlps(norm):
     P = tiny_params(model, seed=23)
     x = tiny_tokens(model, 3, seed=24)
     assert fd_check(model, P, x[:-1], x[1:]) < 1e-6
+
+
+@pytest.mark.parametrize("norm,win,b,ms", [("rms", 5, 3, 0), ("none", 4, 4, 6), ("rms", 20, 3, 5), ("rms", 1, 3, 0)])
+def test_p16_attention_second_opinion(norm, win, b, ms):
+    """Sliding-window attention ([E2E] section 3) with its key/value cache across chunks:
+    losses, norms and updates against torch autograd over torch's own masked attention
+    (window shorter and longer than the stream, equal to the chunk, and 1)."""
+    model = tiny_model("gelu", norm, L=3, b=b, lr=0.4, clip=0.3, ms=ms, win=win, heads=2)
+    P = tiny_params(model, seed=31)
+    x = tiny_tokens(model, 4 * b, seed=32)
+    res = O.run_ttt(model, P, x)
+    tl, tg, tw = torch_ttt(model, P, x)
+    np.testing.assert_allclose(res.losses, tl, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(res.grad_norm, tg, rtol=1e-11)
+    for k in model.fast_keys():
+        np.testing.assert_allclose(res.delta[k], tw[k] - P[k], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("norm", ["none", "rms"])
+def test_p1_finite_differences_through_attention(norm):
+    """The lower blocks' gradients pass through the attention of the blocks above (within a
+    chunk: the chunk's queries, keys and values all depend on the fast weights below)."""
+    model = tiny_model("gelu", norm, L=2, b=4, win=3, heads=2)
+    P = tiny_params(model, seed=33)
+    x = tiny_tokens(model, 4, seed=34)
+    assert fd_check(model, P, x[:-1], x[1:]) < 1e-6
+
+
+def test_p17_zero_output_projection_is_the_plain_model():
+    """Wo = 0: the attention adds exact zeros and passes the gradient through unchanged."""
+    model = tiny_model("gelu", "rms", L=2, b=3, lr=0.3, clip=0.5, ms=4, win=4, heads=2)
+    P = tiny_params(model, seed=35)
+    for l in range(model.n_blocks):
+        P[f"Wo.{l}"] = np.zeros_like(P[f"Wo.{l}"])
+    x = tiny_tokens(model, 9, seed=36)
+    a = O.run_ttt(model, P, x)
+    plain = tiny_model("gelu", "rms", L=2, b=3, lr=0.3, clip=0.5, ms=4)
+    b = O.run_ttt(plain, {k: v for k, v in P.items() if k[:2] not in ("Wq", "Wk", "Wv", "Wo")}, x)
+    assert np.array_equal(a.losses, b.losses)
+    for k in model.fast_keys():
+        assert np.array_equal(a.weights[k], b.weights[k])
+
+
+def test_p18_window_one_is_a_linear_residual_map():
+    """Window 1: each query sees only its own key, so the attention output is n Wv Wo; the
+    losses equal those of a model whose block adds norm(h) Wv Wo, computed here directly."""
+    model = tiny_model("gelu", "rms", L=1, b=3, lr=0.0, win=1, heads=2)
+    P = tiny_params(model, seed=37)
+    x = tiny_tokens(model, 6, seed=38)
+    res = O.run_ttt(model, P, x)
+    h = P["E_in"][x[:-1]]
+    n = h / np.sqrt(np.mean(h * h, axis=1) + model.eps)[:, None]
+    h = h + n @ P["Wv.0"] @ P["Wo.0"]
+    n = h / np.sqrt(np.mean(h * h, axis=1) + model.eps)[:, None]
+    h = h + O.gelu(n @ P["W1.0"]) @ P["W2.0"]
+    z = h @ P["E_out"].T
+    ref = scipy.special.logsumexp(z, axis=1) - z[np.arange(len(z)), x[1:]]
+    np.testing.assert_allclose(res.losses, ref, rtol=1e-12)
+
+
+def test_pins_catch_a_window_one_key_too_wide(monkeypatch):
+    """A window mask that lets each query see window + 1 keys (an off-by-one) is caught by
+    the torch second opinion once the stream is longer than the window."""
+    def wrong(nc, b, window):
+        pq = nc + np.arange(b)[:, None]
+        pk = np.arange(nc + b)[None, :]
+        return (pk <= pq) & (pk >= pq - window)
+    monkeypatch.setattr(O, "window_mask", wrong)
+    model = tiny_model("gelu", "rms", L=2, b=3, lr=0.4, win=4, heads=2)
+    P = tiny_params(model, seed=39)
+    x = tiny_tokens(model, 12, seed=40)
+    res = O.run_ttt(model, P, x)
+    tl, _, _ = torch_ttt(model, P, x)
+    assert np.max(np.abs(res.losses - tl)) > 1e-6
 
 
 def test_p15_zero_static_projection_is_the_plain_model():

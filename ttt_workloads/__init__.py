@@ -57,11 +57,13 @@ PRESETS: Dict[str, dict] = {
     "s760m": dict(vocab=32000, d_model=1536, d_hidden=6144, n_blocks=3,
                   mlp="gelu", norm="rms", precision="bf16", n_tokens=32768,
                   chunk=1024, lr=0.005, clip=1.0, stream="zipf_markov"),
-    # Fuller TTT-E2E block at the 760M shape: a frozen static MLP beside the fast one in
-    # each block, the MLP hidden size split between the two so the parameters stay equal.
+    # Fuller TTT-E2E block at the 760M shape: frozen sliding-window attention (window 8K
+    # over 1K chunks, 12 heads of 128) and a frozen static MLP before the fast one in each
+    # block, the MLP hidden size split between the two so the parameters stay equal.
     "e2e760m": dict(vocab=32000, d_model=1536, d_hidden=3072, n_blocks=3,
                     mlp="gelu", norm="rms", precision="bf16", n_tokens=32768,
-                    chunk=1024, lr=0.005, clip=1.0, stream="zipf_markov", static_hidden=3072),
+                    chunk=1024, lr=0.005, clip=1.0, stream="zipf_markov", static_hidden=3072,
+                    swa_window=8192, swa_heads=12),
     # In-Place-TTT shape: SwiGLU with frozen gate/up, only the down-projection fast.
     "inplace": dict(vocab=151936, d_model=2560, d_hidden=9728, n_blocks=1,
                     mlp="swiglu_w2", norm="rms", precision="bf16",
@@ -90,6 +92,8 @@ class Workload:
     stream: str       # "markov" | "zipf_markov"
     eps: float = RMS_EPS
     static_hidden: int = 0  # hidden size of a frozen static MLP before the fast one (0: none)
+    swa_window: int = 0     # keys per query of a frozen sliding-window attention first (0: none)
+    swa_heads: int = 0      # its heads
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -200,6 +204,9 @@ def weight_shapes(w: Workload) -> Dict[str, tuple]:
         if w.static_hidden > 0:
             shapes[f"Ws1.{l}"] = (w.d_model, w.static_hidden)
             shapes[f"Ws2.{l}"] = (w.static_hidden, w.d_model)
+        if w.swa_window > 0:
+            for n in ("Wk", "Wo", "Wq", "Wv"):
+                shapes[f"{n}.{l}"] = (w.d_model, w.d_model)
     return shapes
 
 
