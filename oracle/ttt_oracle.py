@@ -233,8 +233,8 @@ def next_kv(model: Model, kv, c):
     out = []
     for l in range(model.n_blocks):
         a = c[l]["att"]
-        out.append(dict(k=a["K"][a["K"].shape[0] - keep:] if keep > 0 else a["K"][:0],
-                        v=a["V"][a["V"].shape[0] - keep:] if keep > 0 else a["V"][:0]))
+        start = max(0, a["K"].shape[0] - keep)  # fewer rows than that so far: all of them
+        out.append(dict(k=a["K"][start:], v=a["V"][start:]))
     return out
 
 

@@ -215,7 +215,9 @@ def torch_ttt(model, P0, tokens):
     x = torch.tensor(np.asarray(tokens), dtype=torch.long)
     b = model.chunk
     losses, gnorms = [], []
-    past = [None] * model.n_blocks  # attention: detached keys/values of earlier positions
+    # attention: the detached keys/values of every earlier position (the whole history; the
+    # window is applied by the position mask alone)
+    past = [None] * model.n_blocks
     for i in range((len(tokens) - 1) // b):
         params = {k: v.clone().requires_grad_(True) for k, v in fast.items()}
         ctx, tgt = x[i * b:(i + 1) * b], x[i * b + 1:(i + 1) * b + 1]
@@ -241,8 +243,7 @@ def torch_ttt(model, P0, tokens):
                 o = torch.nn.functional.scaled_dot_product_attention(split(q), split(K), split(Vv),
                                                                      attn_mask=allowed)
                 h = h + o.transpose(0, 1).reshape(b, -1) @ frozen[f"Wo.{l}"]
-                keep = model.swa_window - 1
-                past[l] = (K[K.shape[0] - keep:].detach(), Vv[Vv.shape[0] - keep:].detach()) if keep > 0 else None
+                past[l] = (K.detach(), Vv.detach())
             if model.static_hidden > 0:
                 hs = torch.nn.functional.gelu(norm(h) @ frozen[f"Ws1.{l}"], approximate="none")
                 h = h + hs @ frozen[f"Ws2.{l}"]
@@ -304,7 +305,8 @@ def test_p1_finite_differences_through_static_mlps(norm):
     assert fd_check(model, P, x[:-1], x[1:]) < 1e-6
 
 
-@pytest.mark.parametrize("norm,win,b,ms", [("rms", 5, 3, 0), ("none", 4, 4, 6), ("rms", 20, 3, 5), ("rms", 1, 3, 0)])
+@pytest.mark.parametrize("norm,win,b,ms", [("rms", 5, 3, 0), ("none", 4, 4, 6), ("rms", 20, 3, 5), ("rms", 1, 3, 0),
+                                           ("rms", 7, 4, 0), ("none", 11, 3, 4)])
 def test_p16_attention_second_opinion(norm, win, b, ms):
     """Sliding-window attention ([E2E] section 3) with its key/value cache across chunks:
     losses, norms and updates against torch autograd over torch's own masked attention
@@ -360,6 +362,23 @@ def test_p18_window_one_is_a_linear_residual_map():
     z = h @ P["E_out"].T
     ref = scipy.special.logsumexp(z, axis=1) - z[np.arange(len(z)), x[1:]]
     np.testing.assert_allclose(res.losses, ref, rtol=1e-12)
+
+
+def test_pins_catch_a_cache_cut_short_by_index_wrap(monkeypatch):
+    """A cache that keeps only the last (window - 1) - n rows while fewer than window - 1
+    positions exist (a negative slice start wrapping around) is caught by the torch second
+    opinion, which keeps the whole history and masks by position."""
+    def wrong(model, kv, c):
+        keep = model.swa_window - 1
+        return [dict(k=c[l]["att"]["K"][c[l]["att"]["K"].shape[0] - keep:],
+                     v=c[l]["att"]["V"][c[l]["att"]["V"].shape[0] - keep:]) for l in range(model.n_blocks)]
+    monkeypatch.setattr(O, "next_kv", wrong)
+    model = tiny_model("gelu", "rms", L=2, b=4, lr=0.4, win=7, heads=2)
+    P = tiny_params(model, seed=41)
+    x = tiny_tokens(model, 12, seed=42)
+    res = O.run_ttt(model, P, x)
+    tl, _, _ = torch_ttt(model, P, x)
+    assert np.max(np.abs(res.losses - tl)) > 1e-6
 
 
 def test_pins_catch_a_window_one_key_too_wide(monkeypatch):
