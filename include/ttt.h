@@ -130,25 +130,41 @@ ttt_status ttt_create_batch(const ttt_config* cfg, const ttt_weights* w, int32_t
 /* Number of streams of the context (-1 for NULL). */
 int32_t ttt_streams(const ttt_ctx* ctx);
 
-/* Frozen layers added to every TTT'd block ([E2E] section 3.1, "two MLP layers per block":
- * a static MLP in each updated block keeps what pre-training stored while the other MLP is
- * updated). With static_hidden = m_s > 0 each block is
- *   h <- h + GELU(norm(h) Ws1) Ws2        (frozen static MLP, its own pre-norm)
+/* Frozen layers added to every TTT'd block, before its fast MLP, each with its own pre-norm
+ * and residual:
+ *   h <- h + Attn(norm(h))                (swa_window = k > 0: sliding-window attention,
+ *                                          [E2E] section 3, window k >= chunk recommended)
+ *   h <- h + GELU(norm(h) Ws1) Ws2        (static_hidden = m_s > 0: the static MLP of
+ *                                          [E2E] section 3.1, "two MLP layers per block")
  *   h <- h + MLP(norm(h))                 (the fast MLP of ttt_config)
- * The inner loop backpropagates through the static MLPs of the blocks above each fast one;
- * nothing of them is updated. TTT_MLP_GELU only; m_s a multiple of 8.
- *   ws1[l]  [d x m_s], ws2[l]  [m_s x d]: HOST arrays of n_blocks device pointers, element
- *   type as the other weights; copied at creation like them. */
+ * The inner loop backpropagates through the frozen layers of the blocks above each fast
+ * one; nothing of them is updated. TTT_MLP_GELU only.
+ * Attention: swa_heads heads of 128 (d_model = 128 swa_heads), TTT_BF16 only;
+ * q = n Wq, k = n Wk, v = n Wv, softmax(q.k / sqrt(128)) over the keys of the last k
+ * positions up to the query's own (no positional encoding), output o Wo. Each position's key
+ * and value are computed once, at the weights of the chunk that first processes it, and kept
+ * in a ring of k positions per block and stream (4 k d bytes); later chunks read them as
+ * constants. A context with attention supports prefill (single or batched) and the readers;
+ * decode, evaluation, snapshots and Settlement return TTT_EINVAL.
+ *   ws1[l] [d x m_s], ws2[l] [m_s x d], wq/wk/wv/wo[l] [d x d]: HOST arrays of n_blocks
+ *   device pointers, element type as the other weights; copied at creation like them.
+ *   Arrays of an absent layer are ignored. */
 typedef struct {
-  int32_t static_hidden;   /* m_s (0: no static MLP; the arrays are then ignored) */
-  int32_t reserved[3];     /* must be 0 */
+  int32_t static_hidden;   /* m_s, a multiple of 8 (0: no static MLP)            */
+  int32_t swa_window;      /* k (0: no attention)                               */
+  int32_t swa_heads;       /* heads of 128                                      */
+  int32_t reserved;        /* must be 0                                         */
   const void* const* ws1;
   const void* const* ws2;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
 } ttt_block_ext;
 
 /* ttt_create_batch with the block extension (NULL ext: none). Errors: as ttt_create_batch,
  * TTT_EINVAL for a bad extension (m_s not a multiple of 8, a missing pointer, the SwiGLU
- * block, nonzero reserved fields). */
+ * block, attention outside bf16 or with d_model != 128 heads, a nonzero reserved field). */
 ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt_block_ext* ext, int32_t streams,
                           void* stream, ttt_ctx** out);
 
@@ -277,7 +293,8 @@ typedef enum {
   TTT_K_GRADNORM = 15, /* global gradient norm and clip scale                */
   TTT_K_UPDATE = 16,   /* clipped SGD step of one fast tensor                */
   TTT_K_DEC_GEMV = 17, /* decode: one-row products with the weights         */
-  TTT_K_COUNT = 18
+  TTT_K_ATTN = 18,     /* sliding-window attention: q|k|v product, forward, backward */
+  TTT_K_COUNT = 19
 } ttt_kernel_kind;
 
 /* Tracing: when bit k of `mask` is set, every later launch of kind k by this context is

@@ -23,7 +23,7 @@ NORM = {"none": 0, "rms": 1}
 PRECISION = {"fp32": 0, "bf16": 1}
 # ttt_kernel_kind order of include/ttt.h
 KERNEL_KINDS = ["gather", "norm", "transpose", "up", "down", "residual", "ce_fwd", "ce_merge", "ce_prob",
-                "ce_dy", "dy_sum", "du", "dw", "dhn", "norm_bwd", "gradnorm", "update", "dec_gemv"]
+                "ce_dy", "dy_sum", "du", "dw", "dhn", "norm_bwd", "gradnorm", "update", "dec_gemv", "attn"]
 
 # Functions declared in include/ttt.h, with their ctypes signatures.
 SIGNATURES = {
@@ -74,8 +74,8 @@ class Weights(ctypes.Structure):
 
 
 class BlockExt(ctypes.Structure):
-    _fields_ = [("static_hidden", c_int32), ("reserved", c_int32 * 3),
-                ("ws1", ctypes.POINTER(c_void_p)), ("ws2", ctypes.POINTER(c_void_p))]
+    _fields_ = [("static_hidden", c_int32), ("swa_window", c_int32), ("swa_heads", c_int32),
+                ("reserved", c_int32)] + [(n, ctypes.POINTER(c_void_p)) for n in ("ws1", "ws2", "wq", "wk", "wv", "wo")]
 
 
 class TTTError(RuntimeError):
@@ -158,7 +158,7 @@ class TTT:
     def __init__(self, *, vocab: int, d_model: int, d_hidden: int, n_blocks: int, mlp: str,
                  norm: str, precision: str, chunk: int, max_tokens: int, lr: float, clip: float,
                  rms_eps: float = 1e-6, weights: Dict[str, "object"], stream=None, streams: int = 1,
-                 static_hidden: int = 0):
+                 static_hidden: int = 0, swa_window: int = 0, swa_heads: int = 0):
         import torch
         self._lib = load_library()
         self.vocab, self.d_model, self.d_hidden, self.n_blocks = vocab, d_model, d_hidden, n_blocks
@@ -166,6 +166,7 @@ class TTT:
         self.max_tokens = max_tokens
         self.streams = streams
         self.static_hidden = static_hidden
+        self.swa_window, self.swa_heads = swa_window, swa_heads
         self._stream = stream if stream is not None else torch.cuda.current_stream()
         dt = torch.bfloat16 if precision == "bf16" else torch.float32
         for k, t in weights.items():
@@ -183,11 +184,17 @@ class TTT:
                     ctypes.cast(wup, ctypes.POINTER(c_void_p)) if wup is not None else None,
                     ctypes.cast(w2, ctypes.POINTER(c_void_p)))
         ext = None
-        if static_hidden > 0:
-            ws1 = (c_void_p * max(L, 1))(*[_ptr(weights[f"Ws1.{l}"]) for l in range(L)])
-            ws2 = (c_void_p * max(L, 1))(*[_ptr(weights[f"Ws2.{l}"]) for l in range(L)])
-            ext = BlockExt(static_hidden, (c_int32 * 3)(0, 0, 0), ctypes.cast(ws1, ctypes.POINTER(c_void_p)),
-                           ctypes.cast(ws2, ctypes.POINTER(c_void_p)))
+        if static_hidden > 0 or swa_window > 0:
+            def arr(name, on):
+                if not on:
+                    return None
+                a = (c_void_p * max(L, 1))(*[_ptr(weights[f"{name}.{l}"]) for l in range(L)])
+                self._keep.append(a)
+                return ctypes.cast(a, ctypes.POINTER(c_void_p))
+            self._keep = []
+            s_on, a_on = static_hidden > 0, swa_window > 0
+            ext = BlockExt(static_hidden, swa_window, swa_heads, 0, arr("Ws1", s_on), arr("Ws2", s_on),
+                           arr("Wq", a_on), arr("Wk", a_on), arr("Wv", a_on), arr("Wo", a_on))
         ctx = c_void_p()
         _check(self._lib.ttt_create_ext(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ext) if ext else None,
                                         streams, c_void_p(_stream_handle(self._stream)), ctypes.byref(ctx)),
@@ -200,7 +207,8 @@ class TTT:
         args = dict(vocab=w.vocab, d_model=w.d_model, d_hidden=w.d_hidden, n_blocks=w.n_blocks,
                     mlp=w.mlp, norm=w.norm, precision=w.precision, chunk=w.chunk,
                     max_tokens=max_tokens or w.n_tokens, lr=w.lr, clip=w.clip, rms_eps=w.eps,
-                    static_hidden=getattr(w, "static_hidden", 0))
+                    static_hidden=getattr(w, "static_hidden", 0), swa_window=getattr(w, "swa_window", 0),
+                    swa_heads=getattr(w, "swa_heads", 0))
         args.update(kw)
         return cls(weights=weights, stream=stream, **args)
 

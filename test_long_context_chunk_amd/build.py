@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libttt_mi355x.so"
-SOURCES = ["kernels.hip", "gemm_inst.hip", "ttt_api.hip"]
+SOURCES = ["kernels.hip", "gemm_inst.hip", "attention.hip", "ttt_api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

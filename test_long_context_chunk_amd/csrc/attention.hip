@@ -1,0 +1,494 @@
+// Frozen sliding-window attention of a TTT'd block ([E2E] section 3): per head of 128,
+// softmax(q.k / sqrt(128)) over the keys of the last `window` positions up to the query's
+// own, o = sum p v. The keys and values of positions before the chunk come from a ring of
+// `cr` positions per stream (written by k_kv_append after the chunk's step); the chunk's own
+// come from the QKV product of this chunk. Three MFMA kernels:
+//   k_swa_fwd      online-softmax forward: O (fp32 and bf16) and the log-sum-exp per query;
+//   k_swa_bwd_dq   dQ over every key a query sees (cached keys included);
+//   k_swa_bwd_dkdv dK, dV of the chunk's own keys (cached keys are constants).
+// Each lane of a wave owns one query (forward, dQ) or one key (dK/dV) as the column of
+// 16 x 16 x 32 bf16 MFMA blocks; the probabilities never leave registers: the products that
+// contract over them take them as the B operand in the k-slot order they already have, and
+// read the other operand from LDS in that same order.
+#include "launchers.h"
+#include "common.h"
+
+namespace {
+
+constexpr int DH = 128;      // head size
+constexpr int BLK = 64;      // queries or keys per workgroup and per staged block
+constexpr int NT_A = 256;    // 4 waves x 16 rows
+constexpr int LDR = DH + 8;  // row stride (elements) of a [row][dim] tile: 272 B
+constexpr int LDT = BLK + 4; // row stride of a [dim][row] tile: 136 B
+
+struct SwaGeo {
+  const bf16_t* qkv;  // [R x 3d] q | k | v of the chunk's rows (stream z: rows z b ..)
+  const bf16_t* kc;   // key ring [nb][cr x d]: position p at slot p % cr
+  const bf16_t* vc;
+  const bf16_t* qkv_lo;  // the rounding residuals of the same (the forward's second terms)
+  const bf16_t* kc_lo;
+  const bf16_t* vc_lo;
+  int cr, b, d, window;
+  int64_t pos;        // position of the chunk's first row
+};
+
+// Source row of key/value position kp of stream z (kp >= 0 and not after the chunk); lo:
+// the rounding-residual term.
+__device__ __forceinline__ const bf16_t* kv_row(const SwaGeo& g, int z, int64_t kp, int which, int h,
+                                                bool lo = false) {
+  if (kp >= g.pos)
+    return (lo ? g.qkv_lo : g.qkv) + ((int64_t)z * g.b + (kp - g.pos)) * (3 * (int64_t)g.d) + (int64_t)which * g.d +
+           h * DH;
+  const bf16_t* ring = which == 1 ? (lo ? g.kc_lo : g.kc) : (lo ? g.vc_lo : g.vc);
+  return ring + ((int64_t)z * g.cr + kp % g.cr) * g.d + h * DH;
+}
+
+// The value rows of a key block as a [dim][key] tile.
+__device__ __forceinline__ void stage_vt(bf16_t* T, const SwaGeo& g, int z, int64_t kb, int64_t khi, int h, bool lo) {
+  for (int idx = threadIdx.x; idx < BLK * (DH / 8); idx += NT_A) {
+    const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
+    const int64_t kp = kb + r;
+    const uint4 v = kp <= khi ? *(const uint4*)(kv_row(g, z, kp, 2, h, lo) + c) : make_uint4(0, 0, 0, 0);
+    const bf16_t* e = (const bf16_t*)&v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) T[(c + i) * LDT + r] = e[i];
+  }
+}
+
+// Stage BLK rows (row r at source src(r), null: zeros) into a [row][dim] tile and,
+// when T is non-null, also into a [dim][row] tile. Each thread moves whole 16-byte chunks.
+template <class Src>
+__device__ __forceinline__ void stage_rows(bf16_t* tile, bf16_t* T, Src src) {
+  for (int idx = threadIdx.x; idx < BLK * (DH / 8); idx += NT_A) {
+    const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
+    const bf16_t* s = src(r);
+    const uint4 v = s ? *(const uint4*)(s + c) : make_uint4(0, 0, 0, 0);
+    *(uint4*)(tile + r * LDR + c) = v;
+    if (T) {
+      const bf16_t* e = (const bf16_t*)&v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) T[(c + i) * LDT + r] = e[i];
+    }
+  }
+}
+
+// A operand chunk from a [dim][row] tile: row dim, rows {32t + 4g .. +3, 32t + 16 + 4g .. +3}
+// (the k-slot order of an accumulator pair held by lane group g).
+__device__ __forceinline__ uint4 tchunk(const bf16_t* T, int dim, int t, int g) {
+  const uint2 lo = *(const uint2*)(T + dim * LDT + 32 * t + 4 * g);
+  const uint2 hi = *(const uint2*)(T + dim * LDT + 32 * t + 16 + 4 * g);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// B operand chunk from two accumulator blocks (4 values each) in that same slot order.
+__device__ __forceinline__ uint4 pchunk(const f32x4_t& a, const f32x4_t& b) {
+  return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------- forward
+// grid (ceil(b / 64), H, streams). Outputs O fp32 and bf16 [R x d] (head h in columns
+// 128 h ..), lse2 [streams][H][b] = log2 of the softmax denominator in units of the scaled
+// logits s log2(e) / sqrt(128). Every operand enters as two bf16 terms (q, k, v stored as
+// hi + lo, p split in registers) and each product as three MFMAs (hi hi + lo hi + hi lo), so
+// the recorded losses carry no bf16 rounding of q, k, v or p to first order.
+__global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ Of, bf16_t* __restrict__ Ob,
+                                                  bf16_t* __restrict__ Ol, float* __restrict__ lse2) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) bf16_t sKl[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[DH * LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t sVtl[DH * LDT];
+  const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q0 = blockIdx.x * BLK;
+  const int q = q0 + wave * 16 + lr;  // this lane's query (chunk row)
+  const bool qok = q < g.b;
+  const int64_t qp = g.pos + q;
+  const float sc = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
+
+  // this lane's query as B-operand chunks (dims 32 s + 8 lg ..)
+  uint4 qf[4], qfl[4];
+  {
+    const int64_t o = ((int64_t)z * g.b + (qok ? q : 0)) * (3 * (int64_t)g.d) + h * DH;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[s] = qok ? *(const uint4*)(g.qkv + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      qfl[s] = qok ? *(const uint4*)(g.qkv_lo + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  f32x4_t ot[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) ot[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
+  int64_t klo = qlo - g.window + 1;
+  if (klo < 0) klo = 0;
+  for (int64_t kb = klo; kb <= qhi; kb += BLK) {
+    __syncthreads();  // the previous block's tiles are no longer read
+    stage_rows(sK, nullptr, [&](int r) -> const bf16_t* {
+      const int64_t kp = kb + r;
+      return kp <= qhi ? kv_row(g, z, kp, 1, h) : nullptr;
+    });
+    stage_rows(sKl, nullptr, [&](int r) -> const bf16_t* {
+      const int64_t kp = kb + r;
+      return kp <= qhi ? kv_row(g, z, kp, 1, h, true) : nullptr;
+    });
+    stage_vt(sVt, g, z, kb, qhi, h, false);
+    stage_vt(sVtl, g, z, kb, qhi, h, true);
+    __syncthreads();
+
+    // S^T = K Q^T: st[j][e] = s(key kb + 16 j + 4 lg + e, query q)
+    f32x4_t st[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 a = *(const uint4*)(sK + (16 * j + lr) * LDR + 32 * s + 8 * lg);
+        const uint4 al = *(const uint4*)(sKl + (16 * j + lr) * LDR + 32 * s + 8 * lg);
+        mfma_chunk(st[j], a, qf[s], bf16_t());
+        mfma_chunk(st[j], al, qf[s], bf16_t());
+        mfma_chunk(st[j], a, qfl[s], bf16_t());
+      }
+    }
+    // mask and block max (in scaled units)
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t kp = kb + 16 * j + 4 * lg + e;
+        const bool ok = qok && kp <= qp && kp > qp - g.window;
+        st[j][e] = ok ? st[j][e] * sc : -INFINITY;
+        bm = fmaxf(bm, st[j][e]);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, TTT_WAVE));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, TTT_WAVE));
+    // online softmax; a query with no visible key yet keeps m = -inf and adds zeros (no
+    // branch: the MFMAs below run for the whole wave)
+    const float mn = fmaxf(m, bm);
+    const float alpha = (m == -INFINITY || mn == -INFINITY) ? (m == mn ? 1.f : 0.f) : __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ot[c] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = st[j][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[j][e] - mn);
+        st[j][e] = p;
+        lsum += p;
+      }
+    // O^T += V^T P^T: ot[c][e] = o(dim 16 c + 4 lg + e, query q), p as hi + lo
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4_t r0, r1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r0[e] = st[2 * t][e] - bf2f(f2bf(st[2 * t][e]));
+        r1[e] = st[2 * t + 1][e] - bf2f(f2bf(st[2 * t + 1][e]));
+      }
+      const uint4 pb = pchunk(st[2 * t], st[2 * t + 1]);
+      const uint4 pl = pchunk(r0, r1);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 vh = tchunk(sVt, 16 * c + lr, t, lg);
+        mfma_chunk(ot[c], vh, pb, bf16_t());
+        mfma_chunk(ot[c], tchunk(sVtl, 16 * c + lr, t, lg), pb, bf16_t());
+        mfma_chunk(ot[c], vh, pl, bf16_t());
+      }
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, TTT_WAVE);
+  lsum += __shfl_xor(lsum, 32, TTT_WAVE);
+  if (!qok) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int64_t row = (int64_t)z * g.b + q;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int col = h * DH + 16 * c + 4 * lg;
+    const float4 o = make_float4(ot[c][0] * inv, ot[c][1] * inv, ot[c][2] * inv, ot[c][3] * inv);
+    *(float4*)(Of + row * g.d + col) = o;
+    const uint2 hb = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+    *(uint2*)(Ob + row * g.d + col) = hb;
+    const bf16_t* hv = (const bf16_t*)&hb;
+    *(uint2*)(Ol + row * g.d + col) = make_uint2(pack_bf16x2(o.x - bf2f(hv[0]), o.y - bf2f(hv[1])),
+                                                 pack_bf16x2(o.z - bf2f(hv[2]), o.w - bf2f(hv[3])));
+  }
+  if (lg == 0) lse2[((int64_t)z * H + h) * g.b + q] = m + log2f(lsum);
+}
+
+// ---------------------------------------------------------------------------- backward
+// Dq[z][h][q] = sum over the head's dims of dO * O (the row term of the softmax backward).
+__global__ void __launch_bounds__(64) k_swa_dsum(const float* __restrict__ dO, const float* __restrict__ O, int d,
+                                                 int b, float* __restrict__ Dq) {
+  const int row = blockIdx.x, h = blockIdx.y, H = gridDim.y;
+  const int64_t o = (int64_t)row * d + h * DH + 2 * threadIdx.x;
+  float v = dO[o] * O[o] + dO[o + 1] * O[o + 1];
+  v = wave_sum(v);
+  if (threadIdx.x == 0) {
+    const int z = row / b, q = row - z * b;
+    Dq[((int64_t)z * H + h) * b + q] = v;
+  }
+}
+
+// dQ: grid (ceil(b / 64), H, streams). dQ = (1 / sqrt(128)) sum_key dS K with
+// dS = P (dP - D), P recomputed from the stored lse2; written (bf16) into columns 128 h ..
+// of dQKV [R x 3d].
+__global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __restrict__ dOb,
+                                                     const float* __restrict__ lse2, const float* __restrict__ Dq,
+                                                     bf16_t* __restrict__ dQKV) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[DH * LDT];
+  const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q0 = blockIdx.x * BLK;
+  const int q = q0 + wave * 16 + lr;
+  const bool qok = q < g.b;
+  const int64_t qp = g.pos + q;
+  const float sc = LOG2E * 0.08838834764831845f;
+  const int64_t row = (int64_t)z * g.b + (qok ? q : 0);
+
+  uint4 qf[4], df[4];
+  {
+    const bf16_t* qr = g.qkv + row * (3 * (int64_t)g.d) + h * DH;
+    const bf16_t* dr = dOb + row * g.d + h * DH;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[s] = qok ? *(const uint4*)(qr + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      df[s] = qok ? *(const uint4*)(dr + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const float L2 = qok ? lse2[((int64_t)z * H + h) * g.b + q] : 0.f;
+  const float Dv = qok ? Dq[((int64_t)z * H + h) * g.b + q] : 0.f;
+  f32x4_t dq[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dq[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
+  int64_t klo = qlo - g.window + 1;
+  if (klo < 0) klo = 0;
+  for (int64_t kb = klo; kb <= qhi; kb += BLK) {
+    __syncthreads();
+    stage_rows(sK, sKt, [&](int r) -> const bf16_t* {
+      const int64_t kp = kb + r;
+      return kp <= qhi ? kv_row(g, z, kp, 1, h) : nullptr;
+    });
+    stage_rows(sV, nullptr, [&](int r) -> const bf16_t* {
+      const int64_t kp = kb + r;
+      return kp <= qhi ? kv_row(g, z, kp, 2, h) : nullptr;
+    });
+    __syncthreads();
+    f32x4_t st[4], dp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dp[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        mfma_chunk(st[j], *(const uint4*)(sK + (16 * j + lr) * LDR + 32 * s + 8 * lg), qf[s], bf16_t());
+        mfma_chunk(dp[j], *(const uint4*)(sV + (16 * j + lr) * LDR + 32 * s + 8 * lg), df[s], bf16_t());
+      }
+    }
+    // dS = P (dP - D), P = exp2(s sc - lse2) on the window, 0 elsewhere
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t kp = kb + 16 * j + 4 * lg + e;
+        const bool ok = qok && kp <= qp && kp > qp - g.window;
+        const float p = ok ? __builtin_amdgcn_exp2f(st[j][e] * sc - L2) : 0.f;
+        st[j][e] = p * (dp[j][e] - Dv);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint4 sb = pchunk(st[2 * t], st[2 * t + 1]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) mfma_chunk(dq[c], tchunk(sKt, 16 * c + lr, t, lg), sb, bf16_t());
+    }
+  }
+  if (!qok) return;
+  const float rs = 0.08838834764831845f;
+  bf16_t* out = dQKV + ((int64_t)z * g.b + q) * (3 * (int64_t)g.d) + h * DH;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    *(uint2*)(out + 16 * c + 4 * lg) =
+        make_uint2(pack_bf16x2(dq[c][0] * rs, dq[c][1] * rs), pack_bf16x2(dq[c][2] * rs, dq[c][3] * rs));
+}
+
+// dK, dV of the chunk's own keys: grid (ceil(b / 64), H, streams); each lane owns one key.
+// dV = sum_q P dO, dK = (1 / sqrt(128)) sum_q dS Q over the chunk's queries that see the key;
+// written (bf16) into columns d + 128 h .. and 2 d + 128 h .. of dQKV.
+__global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* __restrict__ dOb,
+                                                       const float* __restrict__ lse2, const float* __restrict__ Dq,
+                                                       bf16_t* __restrict__ dQKV) {
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) bf16_t sD[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[DH * LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t sDt[DH * LDT];
+  __shared__ float sL[BLK], sDq[BLK];
+  const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int k0 = blockIdx.x * BLK;
+  const int kq = k0 + wave * 16 + lr;  // this lane's key (chunk row)
+  const bool kok = kq < g.b;
+  const int64_t kp = g.pos + kq;
+  const float sc = LOG2E * 0.08838834764831845f;
+
+  uint4 kf[4], vf[4];
+  {
+    const int64_t row = (int64_t)z * g.b + (kok ? kq : 0);
+    const bf16_t* kr = g.qkv + row * (3 * (int64_t)g.d) + g.d + h * DH;
+    const bf16_t* vr = kr + g.d;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[s] = kok ? *(const uint4*)(kr + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      vf[s] = kok ? *(const uint4*)(vr + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  f32x4_t dk[8], dv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    dk[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // chunk queries that see a key of this block: from its first key to the window's end
+  const int kmax = min(k0 + BLK, g.b) - 1;
+  const int qend = (int)min((int64_t)g.b - 1, (int64_t)kmax + g.window - 1);
+  for (int qb = k0; qb <= qend; qb += BLK) {
+    __syncthreads();
+    const int64_t base = (int64_t)z * g.b;
+    stage_rows(sQ, sQt, [&](int r) -> const bf16_t* {
+      return qb + r <= qend ? g.qkv + (base + qb + r) * (3 * (int64_t)g.d) + h * DH : nullptr;
+    });
+    stage_rows(sD, sDt, [&](int r) -> const bf16_t* {
+      return qb + r <= qend ? dOb + (base + qb + r) * g.d + h * DH : nullptr;
+    });
+    if (threadIdx.x < BLK) {
+      const int qq = qb + threadIdx.x;
+      const int64_t o = ((int64_t)z * H + h) * g.b + qq;
+      sL[threadIdx.x] = qq <= qend ? lse2[o] : 0.f;
+      sDq[threadIdx.x] = qq <= qend ? Dq[o] : 0.f;
+    }
+    __syncthreads();
+    // S[q][key] and dP[q][key]: sa[i][e], pa[i][e] for query qb + 16 i + 4 lg + e
+    f32x4_t sa[4], pa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        mfma_chunk(sa[i], *(const uint4*)(sQ + (16 * i + lr) * LDR + 32 * s + 8 * lg), kf[s], bf16_t());
+        mfma_chunk(pa[i], *(const uint4*)(sD + (16 * i + lr) * LDR + 32 * s + 8 * lg), vf[s], bf16_t());
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ql = 16 * i + 4 * lg + e;
+        const int64_t qpos = g.pos + qb + ql;
+        const bool ok = kok && qb + ql <= qend && kp <= qpos && kp > qpos - g.window;
+        const float p = ok ? __builtin_amdgcn_exp2f(sa[i][e] * sc - sL[ql]) : 0.f;
+        sa[i][e] = p;
+        pa[i][e] = p * (pa[i][e] - sDq[ql]);
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint4 pb = pchunk(sa[2 * t], sa[2 * t + 1]);
+      const uint4 db = pchunk(pa[2 * t], pa[2 * t + 1]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        mfma_chunk(dv[c], tchunk(sDt, 16 * c + lr, t, lg), pb, bf16_t());
+        mfma_chunk(dk[c], tchunk(sQt, 16 * c + lr, t, lg), db, bf16_t());
+      }
+    }
+  }
+  if (!kok) return;
+  const float rs = 0.08838834764831845f;
+  bf16_t* out = dQKV + ((int64_t)z * g.b + kq) * (3 * (int64_t)g.d) + h * DH;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int col = 16 * c + 4 * lg;
+    *(uint2*)(out + g.d + col) =
+        make_uint2(pack_bf16x2(dk[c][0] * rs, dk[c][1] * rs), pack_bf16x2(dk[c][2] * rs, dk[c][3] * rs));
+    *(uint2*)(out + 2 * g.d + col) =
+        make_uint2(pack_bf16x2(dv[c][0], dv[c][1]), pack_bf16x2(dv[c][2], dv[c][3]));
+  }
+}
+
+// The last min(b, cr) keys and values of the chunk into the ring: grid (rows, streams).
+__global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ qkv_lo,
+                                                  int b, int d, int64_t pos, int cr, bf16_t* __restrict__ kc,
+                                                  bf16_t* __restrict__ vc, bf16_t* __restrict__ kc_lo,
+                                                  bf16_t* __restrict__ vc_lo) {
+  const int n = min(b, cr);
+  const int r = b - n + blockIdx.x, z = blockIdx.y;
+  const int64_t so = ((int64_t)z * b + r) * (3 * (int64_t)d);
+  const int64_t dst = ((int64_t)z * cr + (pos + r) % cr) * d;
+  for (int c = threadIdx.x * 8; c < d; c += 64 * 8) {
+    *(uint4*)(kc + dst + c) = *(const uint4*)(qkv + so + d + c);
+    *(uint4*)(vc + dst + c) = *(const uint4*)(qkv + so + 2 * d + c);
+    *(uint4*)(kc_lo + dst + c) = *(const uint4*)(qkv_lo + so + d + c);
+    *(uint4*)(vc_lo + dst + c) = *(const uint4*)(qkv_lo + so + 2 * d + c);
+  }
+}
+
+SwaGeo geo(const SwaShape& s) {
+  SwaGeo g;
+  g.qkv = (const bf16_t*)s.qkv;
+  g.kc = (const bf16_t*)s.kc;
+  g.vc = (const bf16_t*)s.vc;
+  g.qkv_lo = (const bf16_t*)s.qkv_lo;
+  g.kc_lo = (const bf16_t*)s.kc_lo;
+  g.vc_lo = (const bf16_t*)s.vc_lo;
+  g.cr = s.cr;
+  g.b = s.b;
+  g.d = s.d;
+  g.window = s.window;
+  g.pos = s.pos;
+  return g;
+}
+
+bool shape_ok(const SwaShape& s) {
+  return s.d % DH == 0 && s.d >= DH && s.b >= 1 && s.streams >= 1 && s.streams <= 65535 && s.window >= 1 &&
+         s.cr >= 1 && s.pos >= 0 && s.qkv && s.kc && s.vc && s.qkv_lo && s.kc_lo && s.vc_lo;
+}
+
+}  // namespace
+
+hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2) {
+  if (!shape_ok(s) || !Ol) return hipErrorInvalidValue;
+  dim3 grid((s.b + BLK - 1) / BLK, s.d / DH, s.streams);
+  hipLaunchKernelGGL(k_swa_fwd, grid, dim3(NT_A), 0, st, geo(s), Of, (bf16_t*)Ob, (bf16_t*)Ol, lse2);
+  return hipGetLastError();
+}
+
+hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
+                       const float* lse2, float* Dq, void* dQKV) {
+  if (!shape_ok(s)) return hipErrorInvalidValue;
+  const int H = s.d / DH;
+  hipLaunchKernelGGL(k_swa_dsum, dim3((unsigned)((int64_t)s.streams * s.b), H), dim3(64), 0, st, dOf, Of, s.d, s.b,
+                     Dq);
+  dim3 grid((s.b + BLK - 1) / BLK, H, s.streams);
+  hipLaunchKernelGGL(k_swa_bwd_dq, grid, dim3(NT_A), 0, st, geo(s), (const bf16_t*)dOb, lse2, Dq, (bf16_t*)dQKV);
+  hipLaunchKernelGGL(k_swa_bwd_dkdv, grid, dim3(NT_A), 0, st, geo(s), (const bf16_t*)dOb, lse2, Dq, (bf16_t*)dQKV);
+  return hipGetLastError();
+}
+
+hipError_t run_kv_append(hipStream_t st, const SwaShape& s) {
+  if (!shape_ok(s)) return hipErrorInvalidValue;
+  const int n = s.b < s.cr ? s.b : s.cr;
+  hipLaunchKernelGGL(k_kv_append, dim3(n, s.streams), dim3(64), 0, st, (const bf16_t*)s.qkv, (const bf16_t*)s.qkv_lo,
+                     s.b, s.d, s.pos, s.cr, (bf16_t*)s.kc, (bf16_t*)s.vc, (bf16_t*)s.kc_lo, (bf16_t*)s.vc_lo);
+  return hipGetLastError();
+}

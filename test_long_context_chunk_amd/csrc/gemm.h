@@ -889,6 +889,7 @@ struct EpiGelu {
   T* GP;    // [M x lda]
   T* RES;   // [M x lda] or null
   int64_t lda, ldat;
+  const float* ADD = nullptr;  // [M x lda] fp32 added to U before the GELU, or null
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
     if constexpr (sizeof(T) == 2 && AccTile<FM, FN, WGM, WGN>::FITS) {
@@ -904,7 +905,12 @@ struct EpiGelu {
         const int gr = m0 + r, gc = n0 + c;
         float4* up = (float4*)(U + r * G::BN + c);
         const float4 u0 = up[0], u1 = up[1];
-        const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        if (ADD && gr < p.M) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (gc + q < p.N) uu[q] += ADD[(int64_t)gr * lda + gc + q];
+        }
         float a[8], gp[8], rs[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -938,7 +944,8 @@ struct EpiGelu {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float gp;
-          gelu_pair(acc[i][j][e], a[e], gp);
+          const float add = (ADD && e < nv) ? ADD[(int64_t)(r0 + e) * lda + col] : 0.f;
+          gelu_pair(acc[i][j][e] + add, a[e], gp);
           if (e < nv) {
             const int64_t o = (int64_t)(r0 + e) * lda + col;
             const T q = from_f<T>(a[e]);
@@ -1216,6 +1223,67 @@ struct EpiGrad {
         for (int j = 0; j < FN; ++j) {
           const int col = epi_col(p, j);
           if (col < p.N) G[(int64_t)row * ldg + col] = from_f<T>(acc[i][j][e]);
+        }
+      }
+  }
+};
+
+// Plain store in the GEMM operand precision (bf16 tiles through LDS as 16-byte row pieces).
+template <class T>
+struct EpiStoreT {
+  T* C;
+  int64_t ldc;
+  template <int FM, int FN, int WGM, int WGN>
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    if constexpr (sizeof(T) == 2 && TileGeo<FM, FN, WGM, WGN>::ROWS_FIT) {
+      Packed<FM, FN> pc;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          pc[i][j][0] = pack_bf2(acc[i][j][0], acc[i][j][1]);
+          pc[i][j][1] = pack_bf2(acc[i][j][2], acc[i][j][3]);
+        }
+      stage_rows_bf16<FM, FN, WGM, WGN>(p, pc, (bf16_t*)C, ldc);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = epi_row(p, i, e);
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = epi_col(p, j);
+          if (col < p.N) C[(int64_t)row * ldc + col] = from_f<T>(acc[i][j][e]);
+        }
+      }
+  }
+};
+
+// The product as two bf16 terms, C ~= Ch + Cl with Ch = rn(C), Cl = rn(C - Ch) (about 16
+// significant bits together), for operands a later product reads at higher precision.
+struct EpiStoreSplit {
+  bf16_t* Ch;
+  bf16_t* Cl;
+  int64_t ldc;
+  template <int FM, int FN, int WGM, int WGN>
+  __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = epi_row(p, i, e);
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = epi_col(p, j);
+          if (col >= p.N) continue;
+          const float v = acc[i][j][e];
+          const bf16_t h = f2bf(v);
+          Ch[(int64_t)row * ldc + col] = h;
+          Cl[(int64_t)row * ldc + col] = f2bf(v - bf2f(h));
         }
       }
   }

@@ -45,9 +45,9 @@ hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const 
 
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat, const GemmSeg2& s2,
-                     const GemmGroup& gg) {
+                     const GemmGroup& gg, const float* add) {
   DISPATCH_T(prec, {
-    EpiGelu<T> e{(T*)A, (T*)AT, (T*)GP, (T*)RES, lda, ldat};
+    EpiGelu<T> e{(T*)A, (T*)AT, (T*)GP, (T*)RES, lda, ldat, add};
     return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2), grp(gg));
   });
 }
@@ -76,6 +76,20 @@ hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx,
     EpiSwigluBwd<T> e{UG, VU, (T*)DG, (T*)DV, (const T*)RES, cdot, ld, ldc};
     return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, Seg2(), grp(gg));
   });
+}
+
+hipError_t gemm_store(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                      int K, void* C, int64_t ldc) {
+  DISPATCH_T(prec, {
+    EpiStoreT<T> e{(T*)C, ldc};
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+  });
+}
+
+hipError_t gemm_store_split(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                            int K, void* Ch, void* Cl, int64_t ldc, const GemmSeg2& s2) {
+  EpiStoreSplit e{(bf16_t*)Ch, (bf16_t*)Cl, ldc};
+  return launch_gemm<bf16_t>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
 }
 
 int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits) {
@@ -110,9 +124,9 @@ hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const
 
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit,
-                           int nrec, void* Q, int64_t ldq) {
+                           int nrec, void* Q, int64_t ldq, const GemmSeg2& s2) {
   DISPATCH_T(prec, {
     EpiCEPartial<T> e{tgt, pmax, psum, pidx, tgt_logit, nrec, (T*)Q, ldq};
-    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e);
+    return launch_gemm<T>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
   });
 }

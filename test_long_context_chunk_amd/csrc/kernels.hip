@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, S
                                                int* __restrict__ err, const float* __restrict__ part, int S,
                                                int64_t pstride, float* __restrict__ H, int d, T* __restrict__ Yb,
                                                float eps, int rms, T* __restrict__ Hn, float* __restrict__ r,
-                                               T* __restrict__ RES) {
+                                               T* __restrict__ RES, T* __restrict__ Yl) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t base = (int64_t)t * d;
@@ -112,6 +112,10 @@ __global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, S
     }
     *(float4*)(H + i) = h;
     if (Yb) store4<T>(Yb + i, h.x, h.y, h.z, h.w);
+    if (Yl) {
+      const float4 q = rounded4<T>(h);
+      store4<T>(Yl + i, h.x - q.x, h.y - q.y, h.z - q.z, h.w - q.w);
+    }
     ss += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
 #pragma unroll
     for (int q = 0; q < ROW_CACHE; ++q)
@@ -814,10 +818,10 @@ inline int grid_for(int64_t n) {
 
 hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, StreamRows sr, int V, const void* E, int* tok_prev,
                       int* tok_tgt, int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb,
-                      float eps, int rms, void* Hn, float* r, void* RES) {
+                      float eps, int rms, void* Hn, float* r, void* RES, void* Yl) {
   if (d % 8 || sr.bs < 1) return hipErrorInvalidValue;
   DISPATCH_T(prec, hipLaunchKernelGGL(k_row_in<T>, dim3(b), dim3(NT), 0, st, tokens, sr, V, (const T*)E, tok_prev, tok_tgt,
-                                      err, part, S, pstride, H, d, (T*)Yb, eps, rms, (T*)Hn, r, (T*)RES));
+                                      err, part, S, pstride, H, d, (T*)Yb, eps, rms, (T*)Hn, r, (T*)RES, (T*)Yl));
   return hipGetLastError();
 }
 

@@ -19,9 +19,10 @@ struct StreamRows {
 // ---- row / elementwise kernels (kernels.hip)
 // The residual stream entering a block (gather of the embeddings when tokens is non-null,
 // else H + the split-K slabs part) and, when Hn is non-null, its pre-norm (see k_row_in).
+// Yl (with Yb): the rounding residual rn(h - rn(h)) of the LM head's operand.
 hipError_t run_row_in(hipStream_t st, int prec, const int* tokens, StreamRows sr, int V, const void* E, int* tok_prev,
                       int* tok_tgt, int* err, const float* part, int S, int64_t pstride, float* H, int b, int d, void* Yb,
-                      float eps, int rms, void* Hn, float* r, void* RES);
+                      float eps, int rms, void* Hn, float* r, void* RES, void* Yl = nullptr);
 hipError_t run_transpose(hipStream_t st, int prec, const void* src, int64_t lds, int R, int C, void* dst, int64_t ldd);
 hipError_t run_dy_finish(hipStream_t st, int prec, const float* part, int S, int64_t pstride, int b, int d,
                          float* dH, void* dHb, const float* Hres, const void* Yb, float* cdot);
@@ -87,6 +88,33 @@ hipError_t run_settle_decide(hipStream_t st, const double* sums, int64_t count, 
 // dst <- src (bytes, a multiple of 16) unless *commit.
 hipError_t run_restore_unless(hipStream_t st, const int* commit, const void* src, void* dst, int64_t bytes);
 
+// ---- sliding-window attention (attention.hip), bf16, heads of 128
+// One chunk step of `streams` streams: qkv [streams b x 3d] holds the chunk's q | k | v
+// (stream z: rows z b ..); kc, vc [streams][cr x d] the ring of earlier keys and values
+// (position p at slot p % cr, cr >= window - 1); pos the position of the chunk's first row.
+// The forward reads q, k, v as two bf16 terms each (hi + lo: qkv_lo, kc_lo, vc_lo hold the
+// rounding residuals), so its products carry about 16 significant bits; the backward reads
+// the hi terms.
+struct SwaShape {
+  const void* qkv = nullptr;
+  const void* qkv_lo = nullptr;
+  void* kc = nullptr;
+  void* vc = nullptr;
+  void* kc_lo = nullptr;
+  void* vc_lo = nullptr;
+  int cr = 0, b = 0, d = 0, window = 0, streams = 1;
+  int64_t pos = 0;
+};
+// O (fp32 Of, bf16 Ob and its rounding residual Ol, [streams b x d]) and lse2
+// [streams][d / 128][b].
+hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2);
+// From dO (fp32 dOf for the row term D, bf16 dOb for the products): dQ, dK, dV of the
+// chunk's rows (bf16) into dQKV [streams b x 3d]; Dq [streams][d / 128][b] is scratch.
+hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
+                       const float* lse2, float* Dq, void* dQKV);
+// The chunk's last min(b, cr) keys and values into the ring.
+hipError_t run_kv_append(hipStream_t st, const SwaShape& s);
+
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
 // Optional second K-segment of a GEMM: C = X Y^T + X2 Y2^T (K2 = 0: absent).
 struct GemmSeg2 {
@@ -114,11 +142,12 @@ struct GemmGroup {
 hipError_t gemm_f32(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                     int K, int splits, float* C, int64_t ldc, int64_t split_stride, int accumulate,
                     const GemmSeg2& s2 = GemmSeg2(), const GemmGroup& gg = GemmGroup());
-// GELU up-projection epilogue: A = GELU(U) [M x lda], A^T [N x ldat], GELU'(U) [M x lda],
-// and (RES non-null) the rounding residual A - rn(A) [M x lda].
+// GELU up-projection epilogue: A = GELU(U) [M x lda], A^T [N x ldat] (AT may be null),
+// GELU'(U) [M x lda], and (RES non-null) the rounding residual A - rn(A) [M x lda]; with add
+// (fp32 [M x lda]), U = X Y^T + add.
 hipError_t gemm_gelu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* A, void* AT, void* GP, void* RES, int64_t lda, int64_t ldat,
-                     const GemmSeg2& s2 = GemmSeg2(), const GemmGroup& gg = GemmGroup());
+                     const GemmSeg2& s2 = GemmSeg2(), const GemmGroup& gg = GemmGroup(), const float* add = nullptr);
 // SwiGLU up epilogue: V = X Y^T kept in VU (fp32, may be null), A = SiLU(UG) * V stored as
 // A [M x lda] and A^T [N x ldat], RES as above.
 hipError_t gemm_swiglu(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
@@ -132,6 +161,12 @@ hipError_t gemm_du(hipStream_t st, int prec, const void* X, int64_t ldx, const v
 hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const float* UG, const float* VU, void* DG, void* DV, const void* RES,
                            float* cdot, int64_t ld, int64_t ldc, const GemmGroup& gg = GemmGroup());
+// C [M x ldc] in the GEMM operand precision.
+hipError_t gemm_store(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                      int K, void* C, int64_t ldc);
+// bf16 operands: C ~= Ch + Cl, Ch = rn(C), Cl = rn(C - Ch), both [M x ldc] bf16.
+hipError_t gemm_store_split(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                            int K, void* Ch, void* Cl, int64_t ldc, const GemmSeg2& s2 = GemmSeg2());
 // Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits):
 // per-tile buffers (CE partials, sums of squares, partial dots) are sized from it.
 void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n);
@@ -148,6 +183,6 @@ hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const
 // when Q is non-null, the numerators exp(z - record max) [M x ldq] in the GEMM precision.
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit,
-                           int nrec, void* Q, int64_t ldq);
+                           int nrec, void* Q, int64_t ldq, const GemmSeg2& s2 = GemmSeg2());
 // Columns of one wave's sub-tile for a GEMM of this shape (the CE record width).
 int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits);

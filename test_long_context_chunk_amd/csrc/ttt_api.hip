@@ -63,6 +63,25 @@ struct Block {
   void* SResN = nullptr;    // bf16 only: n_s - rn(n_s) [R x d]
   void* SResA = nullptr;    // bf16 only: A_s - rn(A_s) [R x m_s]
   int scslot = 0;           // first loss-compensation slot of the static MLP
+  // frozen sliding-window attention first in the block (window > 0)
+  void* WqkvT = nullptr;    // [Wq Wk Wv]^T [3d x d] (forward)
+  void* Wqkv = nullptr;     // [Wq Wk Wv] [d x 3d] (backward)
+  void* WoT = nullptr;      // Wo^T [d x d] (forward)
+  void* Wo = nullptr;       // Wo [d x d] (backward)
+  void* Na = nullptr;       // its normed input [R x d]
+  float* ra = nullptr;      // its RMSNorm scale [R]
+  void* ResNa = nullptr;    // bf16 only: n_a - rn(n_a)
+  void* QKV = nullptr;      // the chunk's q | k | v [R x 3d]
+  void* QKVl = nullptr;     // and their rounding residuals (the forward's second terms)
+  float* Of = nullptr;      // attention output, fp32 [R x d]
+  void* Ob = nullptr;       // and its GEMM operand copy
+  void* Obl = nullptr;      // and that copy's rounding residual
+  float* lse2 = nullptr;    // log2 softmax denominators [streams][heads][b]
+  void* Kc = nullptr;       // ring of earlier keys / values [streams][cr x d], and residuals
+  void* Vc = nullptr;
+  void* Kcl = nullptr;
+  void* Vcl = nullptr;
+  int acslot = 0;           // loss-compensation slots of the attention: O, n_a
 };
 
 }  // namespace
@@ -76,6 +95,10 @@ struct ttt_ctx {
   // clip); a step covers R = nb b token rows, Rp = nb bp columns of the transposed buffers
   int nb = 1, R = 0, Rp = 0;
   int ms = 0;          // hidden size of the static MLP of every block (0: none)
+  int window = 0;      // keys per query of the attention of every block (0: none)
+  int cr = 0;          // ring positions per stream and block (the window)
+  float *dOf = nullptr, *Dq = nullptr;  // attention backward scratch: dO fp32, row terms
+  void *dOb = nullptr, *dQKV = nullptr;
   int dot_tiles_s = 0;  // column tiles of the static dA GEMM
   std::vector<void*> allocs;
 
@@ -111,6 +134,11 @@ struct ttt_ctx {
   float* UG = nullptr;
   void *DG = nullptr, *DV = nullptr;  // SwiGLU + bf16: gradients at the gate / up outputs
   bool foc = false;                   // first-order loss compensation (bf16 with blocks)
+  // bf16 with attention: every forward product reads its activation operand as two bf16
+  // terms (the value and its rounding residual), instead of the loss compensation
+  bool split = false;
+  float* Ul = nullptr;                // split: the residual term of the fast up-projection [R x m]
+  void* Yl = nullptr;                 // split: the residual of the LM head's operand [R x d]
   float* cpart = nullptr;             // compensation slots [ncslot x R]
   int ncslot = 0;
   float* slots = nullptr;  // grad-norm slots [nb x nslots]
@@ -210,13 +238,26 @@ ttt_status validate(const ttt_config* c, const ttt_weights* w) {
 }
 
 ttt_status validate_ext(const ttt_config* c, const ttt_block_ext* e) {
-  if (!e || e->static_hidden == 0) return TTT_OK;
-  if (e->reserved[0] || e->reserved[1] || e->reserved[2]) return TTT_EINVAL;
-  if (e->static_hidden < 8 || e->static_hidden % 8 || c->mlp != TTT_MLP_GELU) return TTT_EINVAL;
-  if (c->n_blocks > 0) {
-    if (!e->ws1 || !e->ws2) return TTT_EINVAL;
-    for (int l = 0; l < c->n_blocks; ++l)
-      if (!e->ws1[l] || !e->ws2[l]) return TTT_EINVAL;
+  if (!e) return TTT_OK;
+  if (e->reserved) return TTT_EINVAL;
+  if (e->static_hidden < 0 || e->swa_window < 0) return TTT_EINVAL;
+  if (e->static_hidden > 0) {
+    if (e->static_hidden < 8 || e->static_hidden % 8 || c->mlp != TTT_MLP_GELU) return TTT_EINVAL;
+    if (c->n_blocks > 0) {
+      if (!e->ws1 || !e->ws2) return TTT_EINVAL;
+      for (int l = 0; l < c->n_blocks; ++l)
+        if (!e->ws1[l] || !e->ws2[l]) return TTT_EINVAL;
+    }
+  }
+  if (e->swa_window > 0) {
+    // bf16 heads of 128 over the GELU block
+    if (c->precision != TTT_BF16 || c->mlp != TTT_MLP_GELU || e->swa_window > (1 << 24)) return TTT_EINVAL;
+    if (e->swa_heads < 1 || c->d_model != e->swa_heads * 128) return TTT_EINVAL;
+    if (c->n_blocks > 0) {
+      if (!e->wq || !e->wk || !e->wv || !e->wo) return TTT_EINVAL;
+      for (int l = 0; l < c->n_blocks; ++l)
+        if (!e->wq[l] || !e->wk[l] || !e->wv[l] || !e->wo[l]) return TTT_EINVAL;
+    }
   }
   return TTT_OK;
 }
@@ -228,6 +269,24 @@ void frozen_pair(ttt_ctx* c, const void* src, int rows, int cols, void** nat, vo
   *tr = dalloc<char>(c, bytes);
   check(hipMemcpyAsync(*nat, src, bytes, hipMemcpyDeviceToDevice, c->st));
   check(run_transpose(c->st, c->prec, src, cols, rows, cols, *tr, rows));
+}
+
+// The attention's problem description for block B's chunk starting at position pos.
+SwaShape swa_shape(ttt_ctx* c, Block& B, int64_t pos) {
+  SwaShape s;
+  s.qkv = B.QKV;
+  s.qkv_lo = B.QKVl;
+  s.kc = B.Kc;
+  s.vc = B.Vc;
+  s.kc_lo = B.Kcl;
+  s.vc_lo = B.Vcl;
+  s.cr = c->cr;
+  s.b = c->b;
+  s.d = c->d;
+  s.window = c->window;
+  s.streams = c->nb;
+  s.pos = pos;
+  return s;
 }
 
 void init_fast(ttt_ctx* c, FastTensor& f, int rows, int cols, const void* src) {
@@ -276,7 +335,9 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   check(hipMemcpyAsync(c->E_out, w->lm_head, Vd * es, hipMemcpyDeviceToDevice, c->st));
   check(run_transpose(c->st, c->prec, c->E_out, d, V, d, c->E_outT, V));
 
-  c->foc = c->prec == PREC_BF16 && L > 0;
+  c->foc = c->prec == PREC_BF16 && L > 0 && c->window == 0;
+  c->split = c->prec == PREC_BF16 && L > 0 && c->window > 0;
+  const bool res = c->foc || c->split;  // rounding residuals of the forward operands are kept
   int tmm = 0, tnm_w = 0;
   gemm_tile_shape(c->prec, b, m, d, 0, 1, &tmm, &tnm_w);  // the dA GEMM (M = b, N = m, K = d)
   const int tnm = cdiv(m, tnm_w);
@@ -311,15 +372,46 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
       }
     }
     init_fast(c, B.w2, m, d, w->w2[l]);
+    if (c->window > 0) {
+      const int64_t dd = (int64_t)d * d * es;
+      B.WqkvT = dalloc<char>(c, 3 * dd);
+      B.Wqkv = dalloc<char>(c, 3 * dd);
+      const void* const* src[3] = {ext->wq, ext->wk, ext->wv};
+      for (int j = 0; j < 3; ++j) {
+        check(run_transpose(c->st, c->prec, src[j][l], d, d, d, (char*)B.WqkvT + j * dd, d));
+        check(hipMemcpy2DAsync((char*)B.Wqkv + (int64_t)j * d * es, (size_t)3 * d * es, src[j][l], (size_t)d * es,
+                               (size_t)d * es, d, hipMemcpyDeviceToDevice, c->st));
+      }
+      frozen_pair(c, ext->wo[l], d, d, &B.Wo, &B.WoT);
+      B.Na = dalloc<char>(c, (int64_t)Rr * d * es);
+      B.ra = dalloc<float>(c, (int64_t)Rr * 4);
+      B.QKV = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
+      B.QKVl = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
+      B.Of = dalloc<float>(c, (int64_t)Rr * d * 4);
+      B.Ob = dalloc<char>(c, (int64_t)Rr * d * es);
+      B.Obl = dalloc<char>(c, (int64_t)Rr * d * es);
+      B.lse2 = dalloc<float>(c, (int64_t)Rr * (d / 128) * 4);
+      B.Kc = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
+      B.Vc = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
+      B.Kcl = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
+      B.Vcl = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
+      if (res) B.ResNa = dalloc<char>(c, (int64_t)Rr * d * es);
+      if (c->foc) {
+        B.acslot = c->ncslot;
+        c->ncslot += 2;  // O, n_a
+      }
+    }
     if (ms > 0) {
       frozen_pair(c, ext->ws1[l], d, ms, &B.SW1, &B.SW1T);
       frozen_pair(c, ext->ws2[l], ms, d, &B.SW2, &B.SW2T);
       B.Sn = dalloc<char>(c, (int64_t)Rr * d * es);
       B.Sr = dalloc<float>(c, (int64_t)Rr * 4);
       B.SGP = dalloc<char>(c, (int64_t)Rr * ms * es);
-      if (c->foc) {
+      if (res) {
         B.SResN = dalloc<char>(c, (int64_t)Rr * d * es);
         B.SResA = dalloc<char>(c, (int64_t)Rr * ms * es);
+      }
+      if (c->foc) {
         B.scslot = c->ncslot;
         c->ncslot += tns + 1;  // tns partial dots for A_s, one for n_s
       }
@@ -328,9 +420,11 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
     B.r = dalloc<float>(c, (int64_t)Rr * 4);
     B.AT = dalloc<char>(c, (int64_t)m * Rp * es);
     check(hipMemsetAsync(B.AT, 0, (int64_t)m * Rp * es, c->st));
-    if (c->foc) {
+    if (res) {
       B.ResN = dalloc<char>(c, (int64_t)Rr * d * es);
       B.ResA = dalloc<char>(c, (int64_t)Rr * m * es);
+    }
+    if (c->foc) {
       B.cslot = c->ncslot;
       c->ncslot += tnm + 1;  // tnm partial dots for A, one for n
     }
@@ -341,7 +435,7 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   c->Yb = dalloc<char>(c, (int64_t)Rr * d * es);
   c->tok_prev = dalloc<int>(c, (int64_t)Rr * 4);
   c->tok_tgt = dalloc<int>(c, (int64_t)Rr * 4);
-  c->ce_w = gemm_wave_cols(c->prec, Rr, V, d, 0, 1);  // the LM-head GEMM (all streams' rows)
+  c->ce_w = gemm_wave_cols(c->prec, Rr, V, d, c->split ? d : 0, 1);  // the LM-head GEMM (all streams' rows)
   c->ce_nrec = cdiv(V, c->ce_w);
   c->pmax = dalloc<float>(c, (int64_t)c->ce_nrec * Rr * 4);
   c->psum = dalloc<float>(c, (int64_t)c->ce_nrec * Rr * 4);
@@ -349,7 +443,12 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   c->tgt_logit = dalloc<float>(c, (int64_t)Rr * 4);
   c->lse = dalloc<float>(c, (int64_t)Rr * 4);
   if (L > 0) c->P = dalloc<char>(c, (int64_t)Rr * V * es);  // softmax numerators, then dlogits
-  c->part = dalloc<float>(c, (int64_t)SPLIT_MAX * Rr * d * 4);
+  // split-K slabs; the split forward adds the residual terms' slabs after the main ones
+  c->part = dalloc<float>(c, (int64_t)(c->split ? 2 : 1) * SPLIT_MAX * Rr * d * 4);
+  if (c->split) {
+    c->Ul = dalloc<float>(c, (int64_t)Rr * m * 4);
+    c->Yl = dalloc<char>(c, (int64_t)Rr * d * es);
+  }
   c->dec_tok = dalloc<int>(c, (int64_t)(b + 1) * 4);
   c->eval_loss = dalloc<float>(c, (int64_t)b * 4);
   c->eval_amax = dalloc<int>(c, (int64_t)b * 4);
@@ -371,6 +470,12 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
   check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
   if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)Rr * m * 4);
+  if (c->window > 0 && L > 0) {
+    c->dOf = dalloc<float>(c, (int64_t)Rr * d * 4);
+    c->dOb = dalloc<char>(c, (int64_t)Rr * d * es);
+    c->Dq = dalloc<float>(c, (int64_t)Rr * (d / 128) * 4);
+    c->dQKV = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
+  }
   if (c->foc && c->cfg.mlp == TTT_MLP_SWIGLU_W2) {
     c->DG = dalloc<char>(c, (int64_t)Rr * m * es);
     c->DV = dalloc<char>(c, (int64_t)Rr * m * es);
@@ -465,6 +570,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
   const int64_t n1 = (int64_t)d * m, n2 = (int64_t)m * d;  // elements of one stream's W1, W2
   const int tnm = c->dot_tiles;
   const StreamRows srt{b, ldtok}, srl{b, ldl};
+  const int64_t chunk_pos = chunk_idx * b;  // position of the chunk's first row in each stream
   // Products with a stream's own fast weights run as one grouped launch over the streams
   // (stream z: token rows z b .., its weights z n .. past the first stream's); products
   // with frozen weights run once over all R rows.
@@ -494,35 +600,63 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     float* r = nullptr;
     void* res = nullptr;
   };
+  const bool split = c->split, keep_res = foc || split;
+  auto mlp_norm = [&](Block& B) {  // the first MLP of the block
+    NormOut o;
+    o.n = ms > 0 ? B.Sn : B.Hn;
+    o.r = ms > 0 ? B.Sr : B.r;
+    o.res = keep_res ? (ms > 0 ? B.SResN : B.ResN) : nullptr;
+    return o;
+  };
   auto first_norm = [&](int l) {
     NormOut o;
     if (l >= L) return o;
     Block& B = c->blocks[l];
-    o.n = ms > 0 ? B.Sn : B.Hn;
-    o.r = ms > 0 ? B.Sr : B.r;
-    o.res = foc ? (ms > 0 ? B.SResN : B.ResN) : nullptr;
-    return o;
+    if (c->window > 0) {
+      o.n = B.Na;
+      o.r = B.ra;
+      o.res = keep_res ? B.ResNa : nullptr;
+      return o;
+    }
+    return mlp_norm(B);
   };
 
   // a1 gather, and a2 the lowest block's pre-norm
   {
     const NormOut o = first_norm(0);
     RUN(TTT_K_GATHER, run_row_in(st, prec, tok, srt, V, c->E_in, c->tok_prev, c->tok_tgt, c->err, nullptr, 0, 0, c->H,
-                                 Rr, d, L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res));
+                                 Rr, d, L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res,
+                                 L == 0 && split ? c->Yl : nullptr));
   }
 
   // a2-a4 forward through the blocks
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
+    if (c->window > 0) {
+      // the frozen sliding-window attention ([E2E] section 3), once over all streams' rows:
+      // q | k | v, attention against the ring and the chunk's own keys, output projection
+      RUN(TTT_K_ATTN, gemm_store_split(st, B.Na, d, B.WqkvT, d, Rr, 3 * d, d, B.QKV, B.QKVl, 3 * d,
+                                       split ? GemmSeg2{B.ResNa, d, B.WqkvT, d, d} : GemmSeg2()));
+      RUN(TTT_K_ATTN, run_swa_fwd(st, swa_shape(c, B, chunk_pos), B.Of, B.Ob, B.Obl, B.lse2));
+      const int So = gemm_split_k(prec, Rr, d, d, split ? d : 0, SPLIT_MAX);
+      RUN(TTT_K_DOWN, gemm_f32(st, prec, B.Ob, d, B.WoT, d, Rr, d, d, So, c->part, d, Rd, 0,
+                               split ? GemmSeg2{B.Obl, d, B.WoT, d, d} : GemmSeg2()));
+      const NormOut o = mlp_norm(B);
+      RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, So, Rd,
+                                     c->H, Rr, d, nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res));
+    }
     if (ms > 0) {
       // the frozen static MLP ([E2E] section 3.1), once over all streams' rows; its
       // transposed activation is never needed
-      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Sn, d, B.SW1T, d, Rr, ms, d, c->A, nullptr, B.SGP, foc ? B.SResA : nullptr,
-                              ms, 0));
-      const int Ss = gemm_split_k(prec, Rr, d, ms, 0, SPLIT_MAX);
-      RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, ms, B.SW2T, ms, Rr, d, ms, Ss, c->part, d, Rd, 0));
+      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Sn, d, B.SW1T, d, Rr, ms, d, c->A, nullptr, B.SGP,
+                              keep_res ? B.SResA : nullptr, ms, 0,
+                              split ? GemmSeg2{B.SResN, d, B.SW1T, d, d} : GemmSeg2()));
+      const int Ss = gemm_split_k(prec, Rr, d, ms, split ? ms : 0, SPLIT_MAX);
+      RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, ms, B.SW2T, ms, Rr, d, ms, Ss, c->part, d, Rd, 0,
+                               split ? GemmSeg2{B.SResA, ms, B.SW2T, ms, ms} : GemmSeg2()));
       RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, Ss, Rd,
-                                     c->H, Rr, d, nullptr, c->cfg.rms_eps, rms, B.Hn, B.r, foc ? B.ResN : nullptr));
+                                     c->H, Rr, d, nullptr, c->cfg.rms_eps, rms, B.Hn, B.r,
+                                     keep_res ? B.ResN : nullptr));
     }
     if (gelu) {
       // Hn^T is read only by the W1 gradient of the backward pass
@@ -530,8 +664,12 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
+      // split: the input's residual term against W0 as its own product, added before the GELU
+      if (split)
+        RUN(TTT_K_UP, gemm_f32(st, prec, B.ResN, d, B.w1.W0T, d, b, m, d, 1, c->Ul, m, 0, 0, GemmSeg2(),
+                               fw(b, d, n1, true)));
       RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
-                              foc ? B.ResA : nullptr, m, Rp, s2, fw(b, d, n1, bf)));
+                              keep_res ? B.ResA : nullptr, m, Rp, s2, fw(b, d, n1, bf), split ? c->Ul : nullptr));
     } else {
       RUN(TTT_K_UP, gemm_f32(st, prec, B.Hn, d, B.WgT, d, Rr, m, d, 1, c->UG, m, 0, 0));
       RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, Rr, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
@@ -543,16 +681,26 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
     RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, Rd, 0, s2,
                              fw(b, m, n2, bf)));
+    int St = S;  // slabs the residual sums
+    if (split) {
+      // the activation's residual term against W0, as more slabs after the main ones
+      const int Sx = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
+      RUN(TTT_K_DOWN, gemm_f32(st, prec, B.ResA, m, B.w2.W0T, m, b, d, m, Sx, c->part + (int64_t)S * Rd, d, Rd, 0,
+                               GemmSeg2(), fw(b, m, n2, true)));
+      St += Sx;
+    }
     // a4 residual, and a2 the next block's pre-norm
     const NormOut o = first_norm(l + 1);
-    RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, S, Rd, c->H,
-                                   Rr, d, l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res));
+    RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, St, Rd, c->H,
+                                   Rr, d, l == L - 1 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res,
+                                   l == L - 1 && split ? c->Yl : nullptr));
   }
 
   // a5 LM head + CE forward: online softmax over vocabulary records; the numerators are kept
   // for the backward pass (no logits are recomputed)
   RUN(TTT_K_CE_FWD, gemm_ce_partial(st, prec, c->Yb, d, c->E_out, d, Rr, V, d, c->tok_tgt, c->pmax, c->psum, c->pidx,
-                                    c->tgt_logit, c->ce_nrec, c->P, V));
+                                    c->tgt_logit, c->ce_nrec, c->P, V,
+                                    c->split ? GemmSeg2{c->Yl, d, c->E_out, d, d} : GemmSeg2()));
   RUN(TTT_K_CE_MERGE, run_ce_merge(st, c->pmax, c->psum, c->pidx, c->ce_nrec, Rr, srl, c->tgt_logit, c->lse,
                                    loss_out, amax_out));
 
@@ -583,33 +731,54 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, Rp, c->dUT, Rp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0,
                                   gradg(c->nslots)));
         }
-        // the fast MLP's input gradient is needed below it (a lower block, or this block's
-        // static MLP while the loss compensation runs), and for the compensation of a
-        // rounded n (the lowest block's n = E_in[x] is exact when there is no norm and no
-        // static MLP)
-        const bool below = l > 0 || (ms > 0 && foc);
-        if (below || (foc && rms)) {
+        // Which input gradients this block needs, going down (fast MLP, static MLP,
+        // attention): a sublayer's input gradient is needed when a fast block lies below, or
+        // a frozen sublayer below it in this block has rounded operands to compensate (bf16);
+        // its pre-norm's backward also runs for the compensation of a rounded n (every n but
+        // the lowest block's first, E_in[x], when there is no norm).
+        const bool has_s = ms > 0, has_a = c->window > 0;
+        const bool below_f = l > 0 || (foc && (has_s || has_a));
+        const bool first_f = !has_s && !has_a;
+        if (below_f || (foc && (rms || !first_f))) {
           const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
           RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
                                   fw(b, m, n1, false)));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, c->dHb,
-                                           foc ? B.ResN : nullptr, cN, below));
-          if (ms == 0 && l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+                                           foc ? B.ResN : nullptr, cN, below_f));
         }
-        if (ms > 0 && below) {
+        const bool below_s = l > 0 || (foc && has_a);
+        if (has_s && below_f) {
           // back through the static MLP (frozen: no weight gradient), once over all rows
           float* cAs = foc ? c->cpart + (int64_t)B.scslot * Rr : nullptr;
           float* cNs = foc ? c->cpart + (int64_t)(B.scslot + c->dot_tiles_s) * Rr : nullptr;
           RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.SW2, d, Rr, ms, d, B.SGP, c->dU, nullptr,
                                 foc ? B.SResA : nullptr, cAs, ms, 0, Rr));
-          if (l > 0 || (foc && rms)) {
+          if (below_s || (foc && (rms || has_a))) {
             const int Ss = gemm_split_k(prec, Rr, d, ms, 0, SPLIT_MAX);
             RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, ms, B.SW1, ms, Rr, d, ms, Ss, c->part, d, Rd, 0));
             RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Ss, Rd, B.Sn, B.Sr, Rr, d, rms, c->dH, c->dHb,
-                                             foc ? B.SResN : nullptr, cNs, l > 0));
-            if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+                                             foc ? B.SResN : nullptr, cNs, below_s));
           }
         }
+        if (has_a && (has_s ? below_s : below_f)) {
+          // back through the attention (frozen): dO = dH Wo^T, with the compensation of the
+          // rounded O; then dQ, dK, dV of the chunk's rows and dn = [dQ dK dV] [Wq Wk Wv]^T
+          float* cO = foc ? c->cpart + (int64_t)B.acslot * Rr : nullptr;
+          float* cNa = foc ? c->cpart + (int64_t)(B.acslot + 1) * Rr : nullptr;
+          const int So = gemm_split_k(prec, Rr, d, d, 0, SPLIT_MAX);
+          RUN(TTT_K_DHN, gemm_f32(st, prec, c->dHb, d, B.Wo, d, Rr, d, d, So, c->part, d, Rd, 0));
+          RUN(TTT_K_NORM_BWD, run_dy_finish(st, prec, c->part, So, Rd, Rr, d, c->dOf, c->dOb, foc ? B.Of : nullptr,
+                                            foc ? B.Ob : nullptr, cO));
+          if (l > 0 || (foc && rms)) {
+            RUN(TTT_K_ATTN, run_swa_bwd(st, swa_shape(c, B, chunk_pos), c->dOf, c->dOb, B.Of, B.lse2, c->Dq, c->dQKV));
+            const int Sq = gemm_split_k(prec, Rr, d, 3 * d, 0, SPLIT_MAX);
+            RUN(TTT_K_DHN, gemm_f32(st, prec, c->dQKV, 3 * d, B.Wqkv, 3 * d, Rr, d, 3 * d, Sq, c->part, d, Rd, 0));
+            RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Sq, Rd, B.Na, B.ra, Rr, d, rms, c->dH, c->dHb,
+                                             foc ? B.ResNa : nullptr, cNa, l > 0));
+          }
+        }
+        // dH^T at this block's input, read by the W2 gradient of the block below
+        if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
       } else if (train) {
         RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
                                 gradg(c->nslots)));
@@ -631,6 +800,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, Rr, srl, (float)b, loss_out));
   }
   if (!train) return;
+
+  // the chunk's keys and values join each attention ring once nothing reads the old slots
+  for (int l = 0; l < L && c->window > 0; ++l) check(run_kv_append(st, swa_shape(c, c->blocks[l], chunk_pos)));
 
   // a8 global grad norm and clip scale, one per stream; a9 update
   RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx,
@@ -786,6 +958,8 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   c->R = streams * c->b;
   c->Rp = streams * c->bp;
   c->ms = ext ? ext->static_hidden : 0;
+  c->window = ext ? ext->swa_window : 0;
+  c->cr = c->window;
   c->V = cfg->vocab;
   c->d = cfg->d_model;
   c->m = cfg->d_hidden;
@@ -846,7 +1020,7 @@ ttt_status ttt_prefill_batch(ttt_ctx* c, const int32_t* tokens, int64_t ld_token
 }
 
 ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* argmax, float* logits) {
-  if (!c || !tokens || n < 0 || c->nb != 1) return TTT_EINVAL;
+  if (!c || !tokens || n < 0 || c->nb != 1 || c->window > 0) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + n > c->cfg.max_tokens) return TTT_EINVAL;
   if (n == 0) return TTT_OK;
@@ -873,7 +1047,7 @@ ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* arg
 int64_t ttt_decode_pending(const ttt_ctx* c) { return c ? c->npend : -1; }
 
 ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses, float* mean) {
-  if (!c || !q || nq <= 0 || nq % c->b || c->nb != 1) return TTT_EINVAL;
+  if (!c || !q || nq <= 0 || nq % c->b || c->nb != 1 || c->window > 0) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
     evaluate(c, q, nq, c->eval_acc, losses, mean);
@@ -885,7 +1059,7 @@ ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses,
 }
 
 ttt_status ttt_snapshot(ttt_ctx* c) {
-  if (!c || c->nb != 1) return TTT_EINVAL;
+  if (!c || c->nb != 1 || c->window > 0) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
     copy_state(c, true);
@@ -898,7 +1072,7 @@ ttt_status ttt_snapshot(ttt_ctx* c) {
 }
 
 ttt_status ttt_restore(ttt_ctx* c) {
-  if (!c || c->nb != 1) return TTT_EINVAL;
+  if (!c || c->nb != 1 || c->window > 0) return TTT_EINVAL;
   if (c->sticky != TTT_OK || !c->has_snap) return TTT_ESTATE;
   try {
     copy_state(c, false);
@@ -911,7 +1085,7 @@ ttt_status ttt_restore(ttt_ctx* c) {
 
 ttt_status ttt_settle_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
                             int32_t* committed) {
-  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0 || c->nb != 1) return TTT_EINVAL;
+  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0 || c->nb != 1 || c->window > 0) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + c->b > c->cfg.max_tokens) return TTT_EINVAL;
   try {

@@ -102,19 +102,26 @@ def test_create_batch_rejects_bad_stream_counts_before_touching_a_device(lib, st
     assert out.value is None
 
 
-@pytest.mark.parametrize("ms,reserved,mlp,ptrs", [
-    (12, 0, 0, True),   # static hidden size not a multiple of 8
-    (4, 0, 0, True),    # below 8
-    (16, 1, 0, True),   # reserved field set
-    (16, 0, 1, True),   # static MLP with the SwiGLU block
-    (16, 0, 0, False),  # missing weight arrays
+@pytest.mark.parametrize("ms,win,heads,reserved,mlp,prec,d,ptrs", [
+    (12, 0, 0, 0, 0, 1, 128, True),    # static hidden size not a multiple of 8
+    (4, 0, 0, 0, 0, 1, 128, True),     # below 8
+    (16, 0, 0, 1, 0, 1, 128, True),    # reserved field set
+    (16, 0, 0, 0, 1, 1, 128, True),    # static MLP with the SwiGLU block
+    (16, 0, 0, 0, 0, 1, 128, False),   # missing weight arrays
+    (0, 64, 1, 0, 0, 0, 128, True),    # attention in fp32
+    (0, 64, 2, 0, 0, 1, 128, True),    # heads of 64, not 128
+    (0, 64, 0, 0, 0, 1, 128, True),    # no heads
+    (0, 64, 1, 0, 0, 1, 128, False),   # missing attention weights
+    (0, -1, 1, 0, 0, 1, 128, True),    # negative window
 ])
-def test_create_ext_rejects_bad_extensions_before_touching_a_device(lib, ms, reserved, mlp, ptrs):
-    cfg = _cfg(mlp=mlp)
+def test_create_ext_rejects_bad_extensions_before_touching_a_device(lib, ms, win, heads, reserved, mlp, prec, d,
+                                                                     ptrs):
+    cfg = _cfg(mlp=mlp, precision=prec, d_model=d)
     dummy = (ctypes.c_void_p * 1)(1)
     arr = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_void_p))
     w = B.Weights(1, 1, arr, arr if mlp == 1 else None, arr)
-    ext = B.BlockExt(ms, (ctypes.c_int32 * 3)(reserved, 0, 0), arr if ptrs else None, arr if ptrs else None)
+    p = arr if ptrs else None
+    ext = B.BlockExt(ms, win, heads, reserved, p, p, p, p, p, p)
     out = ctypes.c_void_p(12345)
     assert lib.ttt_create_ext(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ext), 1, None, ctypes.byref(out)) == -1
     assert out.value is None
@@ -122,7 +129,8 @@ def test_create_ext_rejects_bad_extensions_before_touching_a_device(lib, ms, res
 
 def test_block_ext_struct_layout_matches_header():
     assert B.BlockExt.ws1.offset == 16
-    assert ctypes.sizeof(B.BlockExt) == 16 + 2 * ctypes.sizeof(ctypes.c_void_p)
+    assert B.BlockExt.wo.offset == 16 + 5 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(B.BlockExt) == 16 + 6 * ctypes.sizeof(ctypes.c_void_p)
 
 
 def test_null_context_calls_are_rejected(lib):
