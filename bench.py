@@ -122,15 +122,20 @@ def calibrate_copy():
     del src, dst
 
 
+def cpu_cores() -> int:
+    """Threads the oracle's numpy BLAS runs with (the host cores it uses)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((i.get("num_threads", 1) for i in threadpool_info()), default=1))
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, P, x, n_chunks: int):
     """The fp64 oracle, as it stands, on the first n_chunks chunks of the same stream."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = cpu_cores()
     model = O.Model.from_workload(w)
     t0 = time.perf_counter()
     O.run_ttt(model, P, x[:n_chunks * w.chunk + 1], n_chunks=n_chunks)
@@ -195,11 +200,7 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
         t0 = time.perf_counter()
         O.decode_ttt(model, P, ids[:n + 1])
         cdt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-        except Exception:
-            threads = os.cpu_count() or 1
+        threads = cpu_cores()
         out["cpu_baseline"] = {"value": n / cdt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
                                "sample": f"{n} decoded tokens of the same shape, fp64 numpy, {cdt:.1f} s"}
     return out
@@ -243,11 +244,7 @@ def settle_bench(ctx, w, x, P, cpu: bool, n: int = 3) -> dict:
         t0 = time.perf_counter()
         O.settle_step(model, P, x[:b + 1], x[b:2 * b + 1])
         cdt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-        except Exception:
-            threads = os.cpu_count() or 1
+        threads = cpu_cores()
         out["cpu_baseline"] = {"value": 1.0 / cdt, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
                                "sample": f"one candidate at the same shape, fp64 numpy, {cdt:.1f} s"}
     return out
@@ -316,6 +313,116 @@ def batch_bench(w, P, seed: int, streams: int, steps: int, warmup: int) -> dict:
     }
 
 
+def visible_keys(w, pos: int, n: int) -> int:
+    """Keys the attention reads for the n rows from position pos: sum of min(window, p + 1)."""
+    k = w.swa_window
+    total = 0
+    for p in range(pos, pos + n):
+        total += min(k, p + 1)
+    return total
+
+
+def e2e_flops_per_step(w) -> dict:
+    """Algorithmic flops of one step over the whole stream of the fuller block (attention,
+    static MLP, fast MLP per block), no recompute: per token and block, the attention
+    projections 8d^2 forward and (blocks above the lowest) 8d^2 backward, the attention core
+    4d per visible key forward and 4d per visible key plus 4d per visible key of the chunk
+    backward; the static MLP 4 d m_s forward and 4 d m_s backward above the lowest; the fast
+    MLP and LM head as in the plain step."""
+    d, ms, L, T, b = w.d_model, w.static_hidden, w.n_blocks, w.n_tokens, w.chunk
+    keys = visible_keys(w, 0, T)
+    chunk_keys = 0  # visible keys that lie in the query's own chunk
+    for i in range(T // b):
+        for q in range(b):
+            chunk_keys += min(w.swa_window, q + 1)
+    proj = 8.0 * d * d * T * (L + (L - 1))
+    core_fwd = 4.0 * d * keys * L
+    core_bwd = (4.0 * d * keys + 4.0 * d * chunk_keys) * (L - 1)
+    static = 4.0 * d * ms * T * (L + (L - 1))
+    return dict(total=alg_flops_per_token(w) * T + proj + core_fwd + core_bwd + static, attn_fwd=core_fwd)
+
+
+def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2) -> dict:
+    """The fuller TTT-E2E block at the 760M shape: frozen sliding-window attention (window 8K,
+    12 heads) and a frozen static MLP before each of the 3 fast MLPs; one stream, whole-stream
+    steps. Roofline: the attention forward kernel, traced on every chunk."""
+    import numpy as np
+    import torch
+    import ttt_workloads as W
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m")
+    T = w.n_tokens
+    P = W.init_weights(w, seed)
+    x = W.token_stream(w, seed)
+    dev = {k: ttt.to_device(v, w.precision) for k, v in P.items()}
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * (warmup + steps + 1))
+    del dev
+    tok = torch.from_numpy(x.astype(np.int32)).cuda()
+    torch.cuda.synchronize()
+    ctx.profile(ttt._binding.KERNEL_KINDS)
+    ctx.prefill(tok)
+    prof = ctx.profile_read()
+    ctx.profile([])
+    tot = sum(v[0] for v in prof.values())
+    eprint(f"[bench] e2e760m per-kind time of one traced step ({tot:.1f} ms with events):")
+    for k, (ms, n) in sorted(prof.items(), key=lambda kv: -kv[1][0])[:8]:
+        eprint(f"  {k:10s} {ms:9.3f} ms {100 * ms / tot:5.1f}%  {n:5d} launches")
+    for _ in range(warmup):
+        ctx.prefill(tok)
+    torch.cuda.synchronize()
+    ctx.profile(["attn"], period=1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx.prefill(tok)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    aprof = ctx.profile_read()
+    ctx.profile([])
+    status = ctx.sync()
+    last = ctx.token_losses(T * (warmup + 1), 8).cpu().numpy()
+    ctx.close()
+    if status != 0 or not np.all(np.isfinite(last)):
+        eprint(f"[bench] e2e760m: status {status} or non-finite losses")
+        sys.exit(1)
+    fl = e2e_flops_per_step(w)
+    value = steps * T / elapsed
+    a_ms, a_n = aprof.get("attn", (0.0, 0))
+    per_launch = fl["attn_fwd"] / max(1, w.n_chunks * w.n_blocks)
+    avg_s = a_ms * 1e-3 / max(a_n, 1)
+    achieved = per_launch / avg_s / 1e12 if avg_s > 0 else 0.0
+    eprint(f"[bench] e2e760m: {value:.0f} tokens/s, {elapsed / steps * 1e3:.1f} ms per step; attention forward "
+           f"{avg_s * 1e6:.1f} us per launch, {achieved:.1f} TFLOP/s (algorithmic)")
+    out = {
+        "metric": "TTT inner-loop tokens/s with the fuller block (sliding-window attention + static MLP + fast MLP)",
+        "value": value, "unit": "tokens/s", "ms_per_step": elapsed / steps * 1e3, "steps": steps, "warmup": warmup,
+        "config": {"workload": f"e2e760m: 3 x [SWA window {w.swa_window}, {w.swa_heads} heads; static MLP "
+                               f"m_s={w.static_hidden}; fast GELU MLP m={w.d_hidden}], d={w.d_model}, V={w.vocab}",
+                   "tokens_per_step": T, "chunk": w.chunk},
+        "frac_of_bf16_peak": value * fl["total"] / T / PEAK_BF16,
+        "alg_flops_per_token": fl["total"] / T,
+        "roofline": {
+            "bound": "mfma", "kernel": "attn", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": achieved * 1e12 / PEAK_BF16, "traffic": None, "alg_flops_per_launch": per_launch,
+            "avg_launch_us": avg_s * 1e6, "launches": a_n, "kernel_name": "k_swa_fwd",
+            "note": "the forward runs each product as three bf16 MFMAs (hi and residual terms): executed flops "
+                    "are 3x the algorithmic ones",
+        },
+    }
+    if cpu:
+        import oracle as O
+        eprint(f"[bench] timing the fp64 oracle on {cpu_chunks} chunks of e2e760m ...")
+        model = O.Model.from_workload(w)
+        t0 = time.perf_counter()
+        O.run_ttt(model, P, x[:cpu_chunks * w.chunk + 1])
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": cpu_chunks * w.chunk / dt, "unit": "tokens/s", "cores": cpu_cores(),
+                               "kind": "oracle",
+                               "sample": f"first {cpu_chunks} chunks ({cpu_chunks * w.chunk} tokens) of the same "
+                                         f"stream, fp64 numpy, {dt:.1f} s (early chunks see fewer keys)"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +437,7 @@ def main():
     ap.add_argument("--no-settle", action="store_true")
     ap.add_argument("--streams", type=int, default=8,
                     help="independent streams of the batched measurement (0: skip it)")
+    ap.add_argument("--no-e2e", action="store_true", help="skip the fuller-block (attention) measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -443,6 +551,8 @@ def main():
     ctx.close()
     if args.streams > 0:
         out["batch"] = batch_bench(w, P, args.seed, args.streams, args.steps, args.warmup)
+    if not args.no_e2e:
+        out["e2e"] = e2e_bench(args.steps, args.warmup, args.seed, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         eprint(f"[bench] timing the fp64 oracle on {args.cpu_chunks} chunks ...")
         out["cpu_baseline"] = cpu_baseline(w, P, x, args.cpu_chunks)

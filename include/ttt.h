@@ -293,8 +293,9 @@ typedef enum {
   TTT_K_GRADNORM = 15, /* global gradient norm and clip scale                */
   TTT_K_UPDATE = 16,   /* clipped SGD step of one fast tensor                */
   TTT_K_DEC_GEMV = 17, /* decode: one-row products with the weights         */
-  TTT_K_ATTN = 18,     /* sliding-window attention: q|k|v product, forward, backward */
-  TTT_K_COUNT = 19
+  TTT_K_ATTN = 18,     /* sliding-window attention forward (online softmax)  */
+  TTT_K_ATTN_BWD = 19, /* sliding-window attention backward (dQ, dK, dV)     */
+  TTT_K_COUNT = 20
 } ttt_kernel_kind;
 
 /* Tracing: when bit k of `mask` is set, every later launch of kind k by this context is

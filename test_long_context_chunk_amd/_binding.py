@@ -23,7 +23,7 @@ NORM = {"none": 0, "rms": 1}
 PRECISION = {"fp32": 0, "bf16": 1}
 # ttt_kernel_kind order of include/ttt.h
 KERNEL_KINDS = ["gather", "norm", "transpose", "up", "down", "residual", "ce_fwd", "ce_merge", "ce_prob",
-                "ce_dy", "dy_sum", "du", "dw", "dhn", "norm_bwd", "gradnorm", "update", "dec_gemv", "attn"]
+                "ce_dy", "dy_sum", "du", "dw", "dhn", "norm_bwd", "gradnorm", "update", "dec_gemv", "attn", "attn_bwd"]
 
 # Functions declared in include/ttt.h, with their ctypes signatures.
 SIGNATURES = {

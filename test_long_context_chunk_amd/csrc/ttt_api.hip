@@ -635,7 +635,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     if (c->window > 0) {
       // the frozen sliding-window attention ([E2E] section 3), once over all streams' rows:
       // q | k | v, attention against the ring and the chunk's own keys, output projection
-      RUN(TTT_K_ATTN, gemm_store_split(st, B.Na, d, B.WqkvT, d, Rr, 3 * d, d, B.QKV, B.QKVl, 3 * d,
+      RUN(TTT_K_UP, gemm_store_split(st, B.Na, d, B.WqkvT, d, Rr, 3 * d, d, B.QKV, B.QKVl, 3 * d,
                                        split ? GemmSeg2{B.ResNa, d, B.WqkvT, d, d} : GemmSeg2()));
       RUN(TTT_K_ATTN, run_swa_fwd(st, swa_shape(c, B, chunk_pos), B.Of, B.Ob, B.Obl, B.lse2));
       const int So = gemm_split_k(prec, Rr, d, d, split ? d : 0, SPLIT_MAX);
@@ -770,7 +770,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           RUN(TTT_K_NORM_BWD, run_dy_finish(st, prec, c->part, So, Rd, Rr, d, c->dOf, c->dOb, foc ? B.Of : nullptr,
                                             foc ? B.Ob : nullptr, cO));
           if (l > 0 || (foc && rms)) {
-            RUN(TTT_K_ATTN, run_swa_bwd(st, swa_shape(c, B, chunk_pos), c->dOf, c->dOb, B.Of, B.lse2, c->Dq, c->dQKV));
+            RUN(TTT_K_ATTN_BWD, run_swa_bwd(st, swa_shape(c, B, chunk_pos), c->dOf, c->dOb, B.Of, B.lse2, c->Dq,
+                                            c->dQKV));
             const int Sq = gemm_split_k(prec, Rr, d, 3 * d, 0, SPLIT_MAX);
             RUN(TTT_K_DHN, gemm_f32(st, prec, c->dQKV, 3 * d, B.Wqkv, 3 * d, Rr, d, 3 * d, Sq, c->part, d, Rd, 0));
             RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Sq, Rd, B.Na, B.ra, Rr, d, rms, c->dH, c->dHb,
