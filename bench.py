@@ -438,6 +438,8 @@ def main():
     ap.add_argument("--streams", type=int, default=8,
                     help="independent streams of the batched measurement (0: skip it)")
     ap.add_argument("--no-e2e", action="store_true", help="skip the fuller-block (attention) measurement")
+    ap.add_argument("--only", choices=["batch", "e2e"], default=None,
+                    help="run only that measurement and print its object as the line (for kernel traces)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -453,6 +455,14 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+    if args.only == "e2e":
+        print(json.dumps(e2e_bench(args.steps, args.warmup, args.seed, cpu=not args.no_cpu_baseline)), flush=True)
+        return
+    if args.only == "batch":
+        wb = W.preset(args.workload)
+        print(json.dumps(batch_bench(wb, W.init_weights(wb, args.seed), args.seed, args.streams, args.steps,
+                                     args.warmup)), flush=True)
+        return
     w = W.preset(args.workload)
     T = w.n_tokens
     eprint(f"[bench] workload {w.name}: V={w.vocab} d={w.d_model} m={w.d_hidden} L={w.n_blocks} "

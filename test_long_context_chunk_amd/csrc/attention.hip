@@ -43,31 +43,34 @@ __device__ __forceinline__ const bf16_t* kv_row(const SwaGeo& g, int z, int64_t 
   return ring + ((int64_t)z * g.cr + kp % g.cr) * g.d + h * DH;
 }
 
-// The value rows of a key block as a [dim][key] tile.
-__device__ __forceinline__ void stage_vt(bf16_t* T, const SwaGeo& g, int z, int64_t kb, int64_t khi, int h, bool lo) {
-  for (int idx = threadIdx.x; idx < BLK * (DH / 8); idx += NT_A) {
-    const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
-    const int64_t kp = kb + r;
-    const uint4 v = kp <= khi ? *(const uint4*)(kv_row(g, z, kp, 2, h, lo) + c) : make_uint4(0, 0, 0, 0);
-    const bf16_t* e = (const bf16_t*)&v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) T[(c + i) * LDT + r] = e[i];
-  }
-}
-
-// Stage BLK rows (row r at source src(r), null: zeros) into a [row][dim] tile and,
-// when T is non-null, also into a [dim][row] tile. Each thread moves whole 16-byte chunks.
+// Staging through registers: a block of BLK rows is 1024 16-byte chunks, four per thread.
+// All four are requested before any is stored, and a loop requests the next block's chunks
+// before computing on the current one, so global latency overlaps the MFMAs.
+constexpr int CPT = BLK * (DH / 8) / NT_A;  // chunks per thread per tile
+struct Chunks {
+  uint4 v[CPT];
+};
 template <class Src>
-__device__ __forceinline__ void stage_rows(bf16_t* tile, bf16_t* T, Src src) {
-  for (int idx = threadIdx.x; idx < BLK * (DH / 8); idx += NT_A) {
+__device__ __forceinline__ void fetch(Chunks& R, Src src) {
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * NT_A;
     const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
     const bf16_t* s = src(r);
-    const uint4 v = s ? *(const uint4*)(s + c) : make_uint4(0, 0, 0, 0);
-    *(uint4*)(tile + r * LDR + c) = v;
-    if (T) {
-      const bf16_t* e = (const bf16_t*)&v;
+    R.v[i] = s ? *(const uint4*)(s + c) : make_uint4(0, 0, 0, 0);
+  }
+}
+// Into a [row][dim] tile (when tile) and a [dim][row] tile (when T).
+__device__ __forceinline__ void put(const Chunks& R, bf16_t* tile, bf16_t* T) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) T[(c + i) * LDT + r] = e[i];
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * NT_A;
+    const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
+    if (tile) *(uint4*)(tile + r * LDR + c) = R.v[i];
+    if (T) {
+      const bf16_t* e = (const bf16_t*)&R.v[i];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) T[(c + q) * LDT + r] = e[q];
     }
   }
 }
@@ -126,19 +129,28 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
   const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
   int64_t klo = qlo - g.window + 1;
   if (klo < 0) klo = 0;
+  Chunks ck, ckl, cv, cvl;
+  auto fetch_block = [&](int64_t kb) {
+    auto row = [&](int which, bool lo) {
+      return [&, which, lo](int r) -> const bf16_t* {
+        const int64_t kp = kb + r;
+        return kp <= qhi ? kv_row(g, z, kp, which, h, lo) : nullptr;
+      };
+    };
+    fetch(ck, row(1, false));
+    fetch(ckl, row(1, true));
+    fetch(cv, row(2, false));
+    fetch(cvl, row(2, true));
+  };
+  if (klo <= qhi) fetch_block(klo);
   for (int64_t kb = klo; kb <= qhi; kb += BLK) {
     __syncthreads();  // the previous block's tiles are no longer read
-    stage_rows(sK, nullptr, [&](int r) -> const bf16_t* {
-      const int64_t kp = kb + r;
-      return kp <= qhi ? kv_row(g, z, kp, 1, h) : nullptr;
-    });
-    stage_rows(sKl, nullptr, [&](int r) -> const bf16_t* {
-      const int64_t kp = kb + r;
-      return kp <= qhi ? kv_row(g, z, kp, 1, h, true) : nullptr;
-    });
-    stage_vt(sVt, g, z, kb, qhi, h, false);
-    stage_vt(sVtl, g, z, kb, qhi, h, true);
+    put(ck, sK, nullptr);
+    put(ckl, sKl, nullptr);
+    put(cv, nullptr, sVt);
+    put(cvl, nullptr, sVtl);
     __syncthreads();
+    if (kb + BLK <= qhi) fetch_block(kb + BLK);  // in flight during this block's MFMAs
 
     // S^T = K Q^T: st[j][e] = s(key kb + 16 j + 4 lg + e, query q)
     f32x4_t st[4];
@@ -274,17 +286,24 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __r
   const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
   int64_t klo = qlo - g.window + 1;
   if (klo < 0) klo = 0;
-  for (int64_t kb = klo; kb <= qhi; kb += BLK) {
-    __syncthreads();
-    stage_rows(sK, sKt, [&](int r) -> const bf16_t* {
+  Chunks ck, cv;
+  auto fetch_block = [&](int64_t kb) {
+    fetch(ck, [&](int r) -> const bf16_t* {
       const int64_t kp = kb + r;
       return kp <= qhi ? kv_row(g, z, kp, 1, h) : nullptr;
     });
-    stage_rows(sV, nullptr, [&](int r) -> const bf16_t* {
+    fetch(cv, [&](int r) -> const bf16_t* {
       const int64_t kp = kb + r;
       return kp <= qhi ? kv_row(g, z, kp, 2, h) : nullptr;
     });
+  };
+  if (klo <= qhi) fetch_block(klo);
+  for (int64_t kb = klo; kb <= qhi; kb += BLK) {
     __syncthreads();
+    put(ck, sK, sKt);
+    put(cv, sV, nullptr);
+    __syncthreads();
+    if (kb + BLK <= qhi) fetch_block(kb + BLK);
     f32x4_t st[4], dp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -363,22 +382,34 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* _
   // chunk queries that see a key of this block: from its first key to the window's end
   const int kmax = min(k0 + BLK, g.b) - 1;
   const int qend = (int)min((int64_t)g.b - 1, (int64_t)kmax + g.window - 1);
-  for (int qb = k0; qb <= qend; qb += BLK) {
-    __syncthreads();
-    const int64_t base = (int64_t)z * g.b;
-    stage_rows(sQ, sQt, [&](int r) -> const bf16_t* {
+  const int64_t base = (int64_t)z * g.b;
+  Chunks cq, cd;
+  float fl = 0.f, fd = 0.f;
+  auto fetch_block = [&](int qb) {
+    fetch(cq, [&](int r) -> const bf16_t* {
       return qb + r <= qend ? g.qkv + (base + qb + r) * (3 * (int64_t)g.d) + h * DH : nullptr;
     });
-    stage_rows(sD, sDt, [&](int r) -> const bf16_t* {
+    fetch(cd, [&](int r) -> const bf16_t* {
       return qb + r <= qend ? dOb + (base + qb + r) * g.d + h * DH : nullptr;
     });
     if (threadIdx.x < BLK) {
       const int qq = qb + threadIdx.x;
       const int64_t o = ((int64_t)z * H + h) * g.b + qq;
-      sL[threadIdx.x] = qq <= qend ? lse2[o] : 0.f;
-      sDq[threadIdx.x] = qq <= qend ? Dq[o] : 0.f;
+      fl = qq <= qend ? lse2[o] : 0.f;
+      fd = qq <= qend ? Dq[o] : 0.f;
+    }
+  };
+  if (k0 <= qend) fetch_block(k0);
+  for (int qb = k0; qb <= qend; qb += BLK) {
+    __syncthreads();
+    put(cq, sQ, sQt);
+    put(cd, sD, sDt);
+    if (threadIdx.x < BLK) {
+      sL[threadIdx.x] = fl;
+      sDq[threadIdx.x] = fd;
     }
     __syncthreads();
+    if (qb + BLK <= qend) fetch_block(qb + BLK);
     // S[q][key] and dP[q][key]: sa[i][e], pa[i][e] for query qb + 16 i + 4 lg + e
     f32x4_t sa[4], pa[4];
 #pragma unroll
