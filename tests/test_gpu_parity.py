@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 # ---------------------------------------------------------------------- GEMM tile engine
 GEMM_SHAPES = [(1, 64, 64), (1, 256, 256), (16, 8, 8), (37, 100, 136), (128, 128, 64), (1024, 16384, 64), (520, 33000, 128),
-               (130, 129, 520), (257, 300, 72), (64, 64, 6144), (1024, 768, 200)]
+               (130, 129, 520), (257, 300, 72), (64, 64, 6144), (1024, 768, 200), (300, 700, 2048), (1024, 6144, 3072)]
 
 
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
