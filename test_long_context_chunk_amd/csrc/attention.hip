@@ -32,15 +32,33 @@ struct SwaGeo {
   int64_t pos;        // position of the chunk's first row
 };
 
-// Source row of key/value position kp of stream z (kp >= 0 and not after the chunk); lo:
-// the rounding-residual term.
-__device__ __forceinline__ const bf16_t* kv_row(const SwaGeo& g, int z, int64_t kp, int which, int h,
-                                                bool lo = false) {
-  if (kp >= g.pos)
-    return (lo ? g.qkv_lo : g.qkv) + ((int64_t)z * g.b + (kp - g.pos)) * (3 * (int64_t)g.d) + (int64_t)which * g.d +
-           h * DH;
-  const bf16_t* ring = which == 1 ? (lo ? g.kc_lo : g.kc) : (lo ? g.vc_lo : g.vc);
-  return ring + ((int64_t)z * g.cr + kp % g.cr) * g.d + h * DH;
+// Where the rows of one key block [kb, kb + BLK) come from, with 32-bit per-row arithmetic:
+// the first nr rows from the ring (slot s0 + r, wrapping at cr), the others from the chunk's
+// own rows (chunk row c0 + r - nr); rows past `last` (block-relative) are absent.
+struct KeySrc {
+  int nr, s0, c0, last;
+};
+__device__ __forceinline__ KeySrc key_src(const SwaGeo& g, int64_t kb, int64_t khi) {
+  KeySrc k;
+  const int64_t before = g.pos - kb;
+  k.nr = before <= 0 ? 0 : (before >= BLK ? BLK : (int)before);
+  k.s0 = k.nr > 0 ? (int)(kb % g.cr) : 0;
+  k.c0 = (int)(kb + k.nr - g.pos);
+  const int64_t l = khi - kb;
+  k.last = l >= BLK ? BLK - 1 : (int)l;
+  return k;
+}
+__device__ __forceinline__ const bf16_t* key_row(const SwaGeo& g, const KeySrc& k, int z, int r, int which, int h,
+                                                 bool lo = false) {
+  if (r > k.last) return nullptr;
+  if (r < k.nr) {
+    int slot = k.s0 + r;
+    if (slot >= g.cr) slot -= g.cr;
+    const bf16_t* ring = which == 1 ? (lo ? g.kc_lo : g.kc) : (lo ? g.vc_lo : g.vc);
+    return ring + ((int64_t)z * g.cr + slot) * g.d + h * DH;
+  }
+  return (lo ? g.qkv_lo : g.qkv) + ((int64_t)z * g.b + k.c0 + (r - k.nr)) * (3 * (int64_t)g.d) +
+         (int64_t)which * g.d + h * DH;
 }
 
 // Staging through registers: a block of BLK rows is 1024 16-byte chunks, four per thread.
@@ -131,16 +149,11 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
   if (klo < 0) klo = 0;
   Chunks ck, ckl, cv, cvl;
   auto fetch_block = [&](int64_t kb) {
-    auto row = [&](int which, bool lo) {
-      return [&, which, lo](int r) -> const bf16_t* {
-        const int64_t kp = kb + r;
-        return kp <= qhi ? kv_row(g, z, kp, which, h, lo) : nullptr;
-      };
-    };
-    fetch(ck, row(1, false));
-    fetch(ckl, row(1, true));
-    fetch(cv, row(2, false));
-    fetch(cvl, row(2, true));
+    const KeySrc ks = key_src(g, kb, qhi);
+    fetch(ck, [&](int r) { return key_row(g, ks, z, r, 1, h, false); });
+    fetch(ckl, [&](int r) { return key_row(g, ks, z, r, 1, h, true); });
+    fetch(cv, [&](int r) { return key_row(g, ks, z, r, 2, h, false); });
+    fetch(cvl, [&](int r) { return key_row(g, ks, z, r, 2, h, true); });
   };
   if (klo <= qhi) fetch_block(klo);
   for (int64_t kb = klo; kb <= qhi; kb += BLK) {
@@ -166,14 +179,15 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
         mfma_chunk(st[j], a, qfl[s], bf16_t());
       }
     }
-    // mask and block max (in scaled units)
+    // mask (distance query - key in [0, window), 32-bit) and block max (scaled units)
     float bm = -INFINITY;
+    const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t kp = kb + 16 * j + 4 * lg + e;
-        const bool ok = qok && kp <= qp && kp > qp - g.window;
+        const int dist = dq0 - 16 * j - e;
+        const bool ok = dist >= 0 && dist < g.window;
         st[j][e] = ok ? st[j][e] * sc : -INFINITY;
         bm = fmaxf(bm, st[j][e]);
       }
@@ -288,14 +302,9 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __r
   if (klo < 0) klo = 0;
   Chunks ck, cv;
   auto fetch_block = [&](int64_t kb) {
-    fetch(ck, [&](int r) -> const bf16_t* {
-      const int64_t kp = kb + r;
-      return kp <= qhi ? kv_row(g, z, kp, 1, h) : nullptr;
-    });
-    fetch(cv, [&](int r) -> const bf16_t* {
-      const int64_t kp = kb + r;
-      return kp <= qhi ? kv_row(g, z, kp, 2, h) : nullptr;
-    });
+    const KeySrc ks = key_src(g, kb, qhi);
+    fetch(ck, [&](int r) { return key_row(g, ks, z, r, 1, h); });
+    fetch(cv, [&](int r) { return key_row(g, ks, z, r, 2, h); });
   };
   if (klo <= qhi) fetch_block(klo);
   for (int64_t kb = klo; kb <= qhi; kb += BLK) {
@@ -316,12 +325,13 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __r
       }
     }
     // dS = P (dP - D), P = exp2(s sc - lse2) on the window, 0 elsewhere
+    const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t kp = kb + 16 * j + 4 * lg + e;
-        const bool ok = qok && kp <= qp && kp > qp - g.window;
+        const int dist = dq0 - 16 * j - e;
+        const bool ok = dist >= 0 && dist < g.window;
         const float p = ok ? __builtin_amdgcn_exp2f(st[j][e] * sc - L2) : 0.f;
         st[j][e] = p * (dp[j][e] - Dv);
       }
@@ -359,7 +369,6 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* _
   const int k0 = blockIdx.x * BLK;
   const int kq = k0 + wave * 16 + lr;  // this lane's key (chunk row)
   const bool kok = kq < g.b;
-  const int64_t kp = g.pos + kq;
   const float sc = LOG2E * 0.08838834764831845f;
 
   uint4 kf[4], vf[4];
@@ -427,8 +436,8 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* _
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ql = 16 * i + 4 * lg + e;
-        const int64_t qpos = g.pos + qb + ql;
-        const bool ok = kok && qb + ql <= qend && kp <= qpos && kp > qpos - g.window;
+        const int dist = qb + ql - kq;  // query - key, both chunk rows
+        const bool ok = kok && qb + ql <= qend && dist >= 0 && dist < g.window;
         const float p = ok ? __builtin_amdgcn_exp2f(sa[i][e] * sc - sL[ql]) : 0.f;
         sa[i][e] = p;
         pa[i][e] = p * (pa[i][e] - sDq[ql]);
