@@ -19,7 +19,7 @@ constexpr int DH = 128;      // head size
 constexpr int BLK = 64;      // queries or keys per workgroup and per staged block
 constexpr int NT_A = 256;    // 4 waves x 16 rows
 constexpr int LDR = DH + 8;  // row stride (elements) of a [row][dim] tile: 272 B
-constexpr int LDT = BLK + 4; // row stride of a [dim][row] tile: 136 B
+constexpr int LDT = BLK + 8; // row stride of a [dim][row] tile: 144 B (conflict-free pair stores)
 
 struct SwaGeo {
   const bf16_t* qkv;  // [R x 3d] q | k | v of the chunk's rows (stream z: rows z b ..)
@@ -78,17 +78,43 @@ __device__ __forceinline__ void fetch(Chunks& R, Src src) {
     R.v[i] = s ? *(const uint4*)(s + c) : make_uint4(0, 0, 0, 0);
   }
 }
-// Into a [row][dim] tile (when tile) and a [dim][row] tile (when T).
-__device__ __forceinline__ void put(const Chunks& R, bf16_t* tile, bf16_t* T) {
+// Into a [row][dim] tile.
+__device__ __forceinline__ void put(const Chunks& R, bf16_t* tile) {
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int idx = threadIdx.x + i * NT_A;
     const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
-    if (tile) *(uint4*)(tile + r * LDR + c) = R.v[i];
-    if (T) {
-      const bf16_t* e = (const bf16_t*)&R.v[i];
+    *(uint4*)(tile + r * LDR + c) = R.v[i];
+  }
+}
+
+// Blocks that also go into a [dim][row] tile are fetched as row pairs: chunk i of a thread is
+// row 2 p + (i % 2), p = lane-in-32, at 16-byte column (t / 32) + 8 (i / 2). A pair gives one
+// 4-byte word per dim, and the 64 lanes of a wave store to 64 distinct banks (row stride 72).
+template <class Src>
+__device__ __forceinline__ void fetch_p(Chunks& R, Src src) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) T[(c + q) * LDT + r] = e[q];
+  for (int i = 0; i < CPT; ++i) {
+    const int p = threadIdx.x & 31, c = ((threadIdx.x >> 5) + 8 * (i >> 1)) * 8;
+    const bf16_t* s = src(2 * p + (i & 1));
+    R.v[i] = s ? *(const uint4*)(s + c) : make_uint4(0, 0, 0, 0);
+  }
+}
+__device__ __forceinline__ void put_p(const Chunks& R, bf16_t* tile, bf16_t* T) {
+#pragma unroll
+  for (int ip = 0; ip < CPT / 2; ++ip) {
+    const int p = threadIdx.x & 31, c = ((threadIdx.x >> 5) + 8 * ip) * 8;
+    const uint4 a = R.v[2 * ip], b = R.v[2 * ip + 1];
+    if (tile) {
+      *(uint4*)(tile + (2 * p) * LDR + c) = a;
+      *(uint4*)(tile + (2 * p + 1) * LDR + c) = b;
+    }
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // dims c + 2q (low halves) and c + 2q + 1 (high halves) of rows 2p, 2p + 1
+      *(uint32_t*)(T + (c + 2 * q) * LDT + 2 * p) = __builtin_amdgcn_perm(wb[q], wa[q], 0x05040100u);
+      *(uint32_t*)(T + (c + 2 * q + 1) * LDT + 2 * p) = __builtin_amdgcn_perm(wb[q], wa[q], 0x07060302u);
     }
   }
 }
@@ -152,16 +178,16 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
     const KeySrc ks = key_src(g, kb, qhi);
     fetch(ck, [&](int r) { return key_row(g, ks, z, r, 1, h, false); });
     fetch(ckl, [&](int r) { return key_row(g, ks, z, r, 1, h, true); });
-    fetch(cv, [&](int r) { return key_row(g, ks, z, r, 2, h, false); });
-    fetch(cvl, [&](int r) { return key_row(g, ks, z, r, 2, h, true); });
+    fetch_p(cv, [&](int r) { return key_row(g, ks, z, r, 2, h, false); });
+    fetch_p(cvl, [&](int r) { return key_row(g, ks, z, r, 2, h, true); });
   };
   if (klo <= qhi) fetch_block(klo);
   for (int64_t kb = klo; kb <= qhi; kb += BLK) {
     __syncthreads();  // the previous block's tiles are no longer read
-    put(ck, sK, nullptr);
-    put(ckl, sKl, nullptr);
-    put(cv, nullptr, sVt);
-    put(cvl, nullptr, sVtl);
+    put(ck, sK);
+    put(ckl, sKl);
+    put_p(cv, nullptr, sVt);
+    put_p(cvl, nullptr, sVtl);
     __syncthreads();
     if (kb + BLK <= qhi) fetch_block(kb + BLK);  // in flight during this block's MFMAs
 
@@ -303,14 +329,14 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __r
   Chunks ck, cv;
   auto fetch_block = [&](int64_t kb) {
     const KeySrc ks = key_src(g, kb, qhi);
-    fetch(ck, [&](int r) { return key_row(g, ks, z, r, 1, h); });
+    fetch_p(ck, [&](int r) { return key_row(g, ks, z, r, 1, h); });
     fetch(cv, [&](int r) { return key_row(g, ks, z, r, 2, h); });
   };
   if (klo <= qhi) fetch_block(klo);
   for (int64_t kb = klo; kb <= qhi; kb += BLK) {
     __syncthreads();
-    put(ck, sK, sKt);
-    put(cv, sV, nullptr);
+    put_p(ck, sK, sKt);
+    put(cv, sV);
     __syncthreads();
     if (kb + BLK <= qhi) fetch_block(kb + BLK);
     f32x4_t st[4], dp[4];
@@ -395,10 +421,10 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* _
   Chunks cq, cd;
   float fl = 0.f, fd = 0.f;
   auto fetch_block = [&](int qb) {
-    fetch(cq, [&](int r) -> const bf16_t* {
+    fetch_p(cq, [&](int r) -> const bf16_t* {
       return qb + r <= qend ? g.qkv + (base + qb + r) * (3 * (int64_t)g.d) + h * DH : nullptr;
     });
-    fetch(cd, [&](int r) -> const bf16_t* {
+    fetch_p(cd, [&](int r) -> const bf16_t* {
       return qb + r <= qend ? dOb + (base + qb + r) * g.d + h * DH : nullptr;
     });
     if (threadIdx.x < BLK) {
@@ -411,8 +437,8 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* _
   if (k0 <= qend) fetch_block(k0);
   for (int qb = k0; qb <= qend; qb += BLK) {
     __syncthreads();
-    put(cq, sQ, sQt);
-    put(cd, sD, sDt);
+    put_p(cq, sQ, sQt);
+    put_p(cd, sD, sDt);
     if (threadIdx.x < BLK) {
       sL[threadIdx.x] = fl;
       sDq[threadIdx.x] = fd;
