@@ -140,8 +140,19 @@ constexpr float LOG2E = 1.4426950408889634f;
 // logits s log2(e) / sqrt(128). Every operand enters as two bf16 terms (q, k, v stored as
 // hi + lo, p split in registers) and each product as three MFMAs (hi hi + lo hi + hi lo), so
 // the recorded losses carry no bf16 rounding of q, k, v or p to first order.
-__global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ Of, bf16_t* __restrict__ Ob,
-                                                  bf16_t* __restrict__ Ol, float* __restrict__ lse2) {
+// With nsplit > 1 the key blocks of each query block are divided among nsplit workgroups
+// (blockIdx.x = query block * nsplit + split), each leaving its unnormalised partial O and its
+// (max, sum) in part / pm / pl for k_swa_merge.
+struct SwaSplit {
+  int n;        // workgroups per query block
+  float* part;  // [n][R x d] partial O (scaled by 2^-max)
+  float* pm;    // [n][streams][H][b] running max (scaled base-2 units)
+  float* pl;    // [n][streams][H][b] sum of 2^(s - max)
+};
+
+__global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
+                                                  bf16_t* __restrict__ Ob, bf16_t* __restrict__ Ol,
+                                                  float* __restrict__ lse2) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
   __shared__ __attribute__((aligned(16))) bf16_t sKl[BLK * LDR];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[DH * LDT];
@@ -149,7 +160,8 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
   const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int q0 = blockIdx.x * BLK;
+  const int split = blockIdx.x % sp.n;
+  const int q0 = (blockIdx.x / sp.n) * BLK;
   const int q = q0 + wave * 16 + lr;  // this lane's query (chunk row)
   const bool qok = q < g.b;
   const int64_t qp = g.pos + q;
@@ -173,6 +185,14 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
   const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
   int64_t klo = qlo - g.window + 1;
   if (klo < 0) klo = 0;
+  // this workgroup's share of the key blocks [klo, qhi]
+  int64_t kend = qhi;
+  if (sp.n > 1) {
+    const int64_t nblk = (qhi - klo) / BLK + 1;
+    const int64_t b0 = nblk * split / sp.n, b1 = nblk * (split + 1) / sp.n;
+    kend = min(qhi, klo + b1 * BLK - 1);
+    klo += b0 * BLK;
+  }
   Chunks ck, ckl, cv, cvl;
   auto fetch_block = [&](int64_t kb) {
     const KeySrc ks = key_src(g, kb, qhi);
@@ -181,15 +201,15 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
     fetch_p(cv, [&](int r) { return key_row(g, ks, z, r, 2, h, false); });
     fetch_p(cvl, [&](int r) { return key_row(g, ks, z, r, 2, h, true); });
   };
-  if (klo <= qhi) fetch_block(klo);
-  for (int64_t kb = klo; kb <= qhi; kb += BLK) {
+  if (klo <= kend) fetch_block(klo);
+  for (int64_t kb = klo; kb <= kend; kb += BLK) {
     __syncthreads();  // the previous block's tiles are no longer read
     put(ck, sK);
     put(ckl, sKl);
     put_p(cv, nullptr, sVt);
     put_p(cvl, nullptr, sVtl);
     __syncthreads();
-    if (kb + BLK <= qhi) fetch_block(kb + BLK);  // in flight during this block's MFMAs
+    if (kb + BLK <= kend) fetch_block(kb + BLK);  // in flight during this block's MFMAs
 
     // S^T = K Q^T: st[j][e] = s(key kb + 16 j + 4 lg + e, query q)
     f32x4_t st[4];
@@ -258,8 +278,21 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
   lsum += __shfl_xor(lsum, 16, TTT_WAVE);
   lsum += __shfl_xor(lsum, 32, TTT_WAVE);
   if (!qok) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int64_t row = (int64_t)z * g.b + q;
+  if (sp.n > 1) {
+    // partial state: O unnormalised, its max and sum
+    float* P = sp.part + (int64_t)split * ((int64_t)gridDim.z * g.b) * g.d;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *(float4*)(P + row * g.d + h * DH + 16 * c + 4 * lg) = make_float4(ot[c][0], ot[c][1], ot[c][2], ot[c][3]);
+    if (lg == 0) {
+      const int64_t o = ((int64_t)split * gridDim.z * H + (int64_t)z * H + h) * g.b + q;
+      sp.pm[o] = m;
+      sp.pl[o] = lsum;
+    }
+    return;
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int col = h * DH + 16 * c + 4 * lg;
@@ -272,6 +305,39 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, float* __restrict__ 
                                                  pack_bf16x2(o.z - bf2f(hv[2]), o.w - bf2f(hv[3])));
   }
   if (lg == 0) lse2[((int64_t)z * H + h) * g.b + q] = m + log2f(lsum);
+}
+
+// Merge of the split partial states: grid (streams b rows, H), 64 threads x 2 dims.
+__global__ void __launch_bounds__(64) k_swa_merge(SwaSplit sp, int b, int d, float* __restrict__ Of,
+                                                  bf16_t* __restrict__ Ob, bf16_t* __restrict__ Ol,
+                                                  float* __restrict__ lse2) {
+  const int64_t row = blockIdx.x;
+  const int h = blockIdx.y, H = gridDim.y;
+  const int64_t R = (int64_t)gridDim.x;
+  const int z = (int)(row / b), q = (int)(row - (int64_t)z * b);
+  const int64_t nz = R / b;
+  float M = -INFINITY;
+  for (int s = 0; s < sp.n; ++s) M = fmaxf(M, sp.pm[((int64_t)s * nz * H + (int64_t)z * H + h) * b + q]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const int64_t col = (int64_t)h * DH + 2 * threadIdx.x;
+  for (int s = 0; s < sp.n; ++s) {
+    const int64_t i = ((int64_t)s * nz * H + (int64_t)z * H + h) * b + q;
+    const float ms = sp.pm[i];
+    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L += w * sp.pl[i];
+    const float2 pv = *(const float2*)(sp.part + (int64_t)s * R * d + row * d + col);
+    o0 += w * pv.x;
+    o1 += w * pv.y;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  o0 *= inv;
+  o1 *= inv;
+  *(float2*)(Of + row * d + col) = make_float2(o0, o1);
+  const uint32_t hb = pack_bf16x2(o0, o1);
+  *(uint32_t*)(Ob + row * d + col) = hb;
+  const bf16_t* hv = (const bf16_t*)&hb;
+  *(uint32_t*)(Ol + row * d + col) = pack_bf16x2(o0 - bf2f(hv[0]), o1 - bf2f(hv[1]));
+  if (threadIdx.x == 0) lse2[((int64_t)z * H + h) * b + q] = M + log2f(L);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -532,10 +598,27 @@ bool shape_ok(const SwaShape& s) {
 
 }  // namespace
 
-hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2) {
+int swa_fwd_splits(const SwaShape& s) {
+  // enough workgroups for two per CU on 256 CUs, whole key blocks per split, at most 4
+  const int64_t wg = (int64_t)((s.b + BLK - 1) / BLK) * (s.d / DH) * s.streams;
+  const int64_t kblocks = ((int64_t)(s.window < s.b ? s.b : s.window) + BLK - 1) / BLK;
+  int n = (int)((512 + wg - 1) / wg);
+  if (n > 4) n = 4;
+  if (n > kblocks) n = (int)kblocks;
+  return n < 1 ? 1 : n;
+}
+
+hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
+                       float* pm, float* pl) {
   if (!shape_ok(s) || !Ol) return hipErrorInvalidValue;
-  dim3 grid((s.b + BLK - 1) / BLK, s.d / DH, s.streams);
-  hipLaunchKernelGGL(k_swa_fwd, grid, dim3(NT_A), 0, st, geo(s), Of, (bf16_t*)Ob, (bf16_t*)Ol, lse2);
+  SwaSplit sp{swa_fwd_splits(s), part, pm, pl};
+  if (sp.n > 1 && (!part || !pm || !pl)) return hipErrorInvalidValue;
+  const int H = s.d / DH;
+  dim3 grid((s.b + BLK - 1) / BLK * sp.n, H, s.streams);
+  hipLaunchKernelGGL(k_swa_fwd, grid, dim3(NT_A), 0, st, geo(s), sp, Of, (bf16_t*)Ob, (bf16_t*)Ol, lse2);
+  if (sp.n > 1)
+    hipLaunchKernelGGL(k_swa_merge, dim3((unsigned)((int64_t)s.streams * s.b), H), dim3(64), 0, st, sp, s.b, s.d, Of,
+                       (bf16_t*)Ob, (bf16_t*)Ol, lse2);
   return hipGetLastError();
 }
 

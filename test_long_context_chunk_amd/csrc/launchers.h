@@ -106,8 +106,12 @@ struct SwaShape {
   int64_t pos = 0;
 };
 // O (fp32 Of, bf16 Ob and its rounding residual Ol, [streams b x d]) and lse2
-// [streams][d / 128][b].
-hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2);
+// [streams][d / 128][b]. When swa_fwd_splits(s) > 1 the key range of each query block is
+// shared by that many workgroups, whose partial states (part [n][streams b x d], pm and pl
+// [n][streams][d / 128][b], scratch) a merge combines.
+int swa_fwd_splits(const SwaShape& s);
+hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
+                       float* pm, float* pl);
 // From dO (fp32 dOf for the row term D, bf16 dOb for the products): dQ, dK, dV of the
 // chunk's rows (bf16) into dQKV [streams b x 3d]; Dq [streams][d / 128][b] is scratch.
 hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,

@@ -98,6 +98,7 @@ struct ttt_ctx {
   int window = 0;      // keys per query of the attention of every block (0: none)
   int cr = 0;          // ring positions per stream and block (the window)
   float *dOf = nullptr, *Dq = nullptr;  // attention backward scratch: dO fp32, row terms
+  float *swa_part = nullptr, *swa_m = nullptr, *swa_l = nullptr;  // forward split partials
   void *dOb = nullptr, *dQKV = nullptr;
   int dot_tiles_s = 0;  // column tiles of the static dA GEMM
   std::vector<void*> allocs;
@@ -475,6 +476,12 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
     c->dOb = dalloc<char>(c, (int64_t)Rr * d * es);
     c->Dq = dalloc<float>(c, (int64_t)Rr * (d / 128) * 4);
     c->dQKV = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
+    const int ns = swa_fwd_splits(swa_shape(c, c->blocks[0], 0));
+    if (ns > 1) {
+      c->swa_part = dalloc<float>(c, (int64_t)ns * Rr * d * 4);
+      c->swa_m = dalloc<float>(c, (int64_t)ns * Rr * (d / 128) * 4);
+      c->swa_l = dalloc<float>(c, (int64_t)ns * Rr * (d / 128) * 4);
+    }
   }
   if (c->foc && c->cfg.mlp == TTT_MLP_SWIGLU_W2) {
     c->DG = dalloc<char>(c, (int64_t)Rr * m * es);
@@ -637,7 +644,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       // q | k | v, attention against the ring and the chunk's own keys, output projection
       RUN(TTT_K_UP, gemm_store_split(st, B.Na, d, B.WqkvT, d, Rr, 3 * d, d, B.QKV, B.QKVl, 3 * d,
                                        split ? GemmSeg2{B.ResNa, d, B.WqkvT, d, d} : GemmSeg2()));
-      RUN(TTT_K_ATTN, run_swa_fwd(st, swa_shape(c, B, chunk_pos), B.Of, B.Ob, B.Obl, B.lse2));
+      RUN(TTT_K_ATTN, run_swa_fwd(st, swa_shape(c, B, chunk_pos), B.Of, B.Ob, B.Obl, B.lse2, c->swa_part, c->swa_m,
+                                  c->swa_l));
       const int So = gemm_split_k(prec, Rr, d, d, split ? d : 0, SPLIT_MAX);
       RUN(TTT_K_DOWN, gemm_f32(st, prec, B.Ob, d, B.WoT, d, Rr, d, d, So, c->part, d, Rd, 0,
                                split ? GemmSeg2{B.Obl, d, B.WoT, d, d} : GemmSeg2()));
