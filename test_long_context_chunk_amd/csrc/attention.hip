@@ -357,16 +357,20 @@ __global__ void __launch_bounds__(64) k_swa_dsum(const float* __restrict__ dO, c
 // dQ: grid (ceil(b / 64), H, streams). dQ = (1 / sqrt(128)) sum_key dS K with
 // dS = P (dP - D), P recomputed from the stored lse2; written (bf16) into columns 128 h ..
 // of dQKV [R x 3d].
-__global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __restrict__ dOb,
-                                                     const float* __restrict__ lse2, const float* __restrict__ Dq,
-                                                     bf16_t* __restrict__ dQKV) {
+// With nsplit > 1 (blockIdx.x = query block * nsplit + split) each workgroup takes a share of
+// the key blocks and writes its fp32 partial dQ into part[split]; k_swa_dq_sum adds them in
+// split order.
+__global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, int nsplit, float* __restrict__ part,
+                                                     const bf16_t* __restrict__ dOb, const float* __restrict__ lse2,
+                                                     const float* __restrict__ Dq, bf16_t* __restrict__ dQKV) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
   __shared__ __attribute__((aligned(16))) bf16_t sV[BLK * LDR];
   __shared__ __attribute__((aligned(16))) bf16_t sKt[DH * LDT];
   const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int q0 = blockIdx.x * BLK;
+  const int split = blockIdx.x % nsplit;
+  const int q0 = (blockIdx.x / nsplit) * BLK;
   const int q = q0 + wave * 16 + lr;
   const bool qok = q < g.b;
   const int64_t qp = g.pos + q;
@@ -392,19 +396,26 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __r
   const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
   int64_t klo = qlo - g.window + 1;
   if (klo < 0) klo = 0;
+  int64_t kend = qhi;
+  if (nsplit > 1) {
+    const int64_t nblk = (qhi - klo) / BLK + 1;
+    const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
+    kend = min(qhi, klo + b1 * BLK - 1);
+    klo += b0 * BLK;
+  }
   Chunks ck, cv;
   auto fetch_block = [&](int64_t kb) {
     const KeySrc ks = key_src(g, kb, qhi);
     fetch_p(ck, [&](int r) { return key_row(g, ks, z, r, 1, h); });
     fetch(cv, [&](int r) { return key_row(g, ks, z, r, 2, h); });
   };
-  if (klo <= qhi) fetch_block(klo);
-  for (int64_t kb = klo; kb <= qhi; kb += BLK) {
+  if (klo <= kend) fetch_block(klo);
+  for (int64_t kb = klo; kb <= kend; kb += BLK) {
     __syncthreads();
     put_p(ck, sK, sKt);
     put(cv, sV);
     __syncthreads();
-    if (kb + BLK <= qhi) fetch_block(kb + BLK);
+    if (kb + BLK <= kend) fetch_block(kb + BLK);
     f32x4_t st[4], dp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -437,11 +448,39 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, const bf16_t* __r
   }
   if (!qok) return;
   const float rs = 0.08838834764831845f;
+  if (nsplit > 1) {
+    float* P = part + ((int64_t)split * gridDim.z * g.b + (int64_t)z * g.b + q) * g.d + h * DH;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *(float4*)(P + 16 * c + 4 * lg) = make_float4(dq[c][0] * rs, dq[c][1] * rs, dq[c][2] * rs, dq[c][3] * rs);
+    return;
+  }
   bf16_t* out = dQKV + ((int64_t)z * g.b + q) * (3 * (int64_t)g.d) + h * DH;
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     *(uint2*)(out + 16 * c + 4 * lg) =
         make_uint2(pack_bf16x2(dq[c][0] * rs, dq[c][1] * rs), pack_bf16x2(dq[c][2] * rs, dq[c][3] * rs));
+}
+
+// dQ = sum of the split partials in split order, into columns 0 .. d of dQKV (bf16):
+// grid (streams b rows), 256 threads x 8 columns.
+__global__ void __launch_bounds__(NT_A) k_swa_dq_sum(const float* __restrict__ part, int nsplit, int d,
+                                                     bf16_t* __restrict__ dQKV) {
+  const int64_t row = blockIdx.x, R = gridDim.x;
+  for (int c = threadIdx.x * 8; c < d; c += NT_A * 8) {
+    float acc[8];
+    const float4 a0 = *(const float4*)(part + row * d + c), a1 = *(const float4*)(part + row * d + c + 4);
+    acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
+    acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
+    for (int s = 1; s < nsplit; ++s) {
+      const float* p = part + ((int64_t)s * R + row) * d + c;
+      const float4 b0 = *(const float4*)p, b1 = *(const float4*)(p + 4);
+      acc[0] += b0.x; acc[1] += b0.y; acc[2] += b0.z; acc[3] += b0.w;
+      acc[4] += b1.x; acc[5] += b1.y; acc[6] += b1.z; acc[7] += b1.w;
+    }
+    *(uint4*)(dQKV + row * (3 * (int64_t)d) + c) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
 }
 
 // dK, dV of the chunk's own keys: grid (ceil(b / 64), H, streams); each lane owns one key.
@@ -623,13 +662,18 @@ hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, v
 }
 
 hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
-                       const float* lse2, float* Dq, void* dQKV) {
+                       const float* lse2, float* Dq, void* dQKV, float* part) {
   if (!shape_ok(s)) return hipErrorInvalidValue;
   const int H = s.d / DH;
-  hipLaunchKernelGGL(k_swa_dsum, dim3((unsigned)((int64_t)s.streams * s.b), H), dim3(64), 0, st, dOf, Of, s.d, s.b,
-                     Dq);
+  const int ns = swa_fwd_splits(s);  // the dQ pass divides its key blocks the same way
+  if (ns > 1 && !part) return hipErrorInvalidValue;
+  const unsigned R = (unsigned)((int64_t)s.streams * s.b);
+  hipLaunchKernelGGL(k_swa_dsum, dim3(R, H), dim3(64), 0, st, dOf, Of, s.d, s.b, Dq);
+  dim3 gq((s.b + BLK - 1) / BLK * ns, H, s.streams);
+  hipLaunchKernelGGL(k_swa_bwd_dq, gq, dim3(NT_A), 0, st, geo(s), ns, part, (const bf16_t*)dOb, lse2, Dq,
+                     (bf16_t*)dQKV);
+  if (ns > 1) hipLaunchKernelGGL(k_swa_dq_sum, dim3(R), dim3(NT_A), 0, st, part, ns, s.d, (bf16_t*)dQKV);
   dim3 grid((s.b + BLK - 1) / BLK, H, s.streams);
-  hipLaunchKernelGGL(k_swa_bwd_dq, grid, dim3(NT_A), 0, st, geo(s), (const bf16_t*)dOb, lse2, Dq, (bf16_t*)dQKV);
   hipLaunchKernelGGL(k_swa_bwd_dkdv, grid, dim3(NT_A), 0, st, geo(s), (const bf16_t*)dOb, lse2, Dq, (bf16_t*)dQKV);
   return hipGetLastError();
 }

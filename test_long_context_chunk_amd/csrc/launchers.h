@@ -114,8 +114,9 @@ hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, v
                        float* pm, float* pl);
 // From dO (fp32 dOf for the row term D, bf16 dOb for the products): dQ, dK, dV of the
 // chunk's rows (bf16) into dQKV [streams b x 3d]; Dq [streams][d / 128][b] is scratch.
+// part: scratch for the split dQ partials, [swa_fwd_splits(s)][streams b x d] fp32.
 hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
-                       const float* lse2, float* Dq, void* dQKV);
+                       const float* lse2, float* Dq, void* dQKV, float* part);
 // The chunk's last min(b, cr) keys and values into the ring.
 hipError_t run_kv_append(hipStream_t st, const SwaShape& s);
 

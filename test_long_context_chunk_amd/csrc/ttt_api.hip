@@ -779,7 +779,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
                                             foc ? B.Ob : nullptr, cO));
           if (l > 0 || (foc && rms)) {
             RUN(TTT_K_ATTN_BWD, run_swa_bwd(st, swa_shape(c, B, chunk_pos), c->dOf, c->dOb, B.Of, B.lse2, c->Dq,
-                                            c->dQKV));
+                                            c->dQKV, c->swa_part));
             const int Sq = gemm_split_k(prec, Rr, d, 3 * d, 0, SPLIT_MAX);
             RUN(TTT_K_DHN, gemm_f32(st, prec, c->dQKV, 3 * d, B.Wqkv, 3 * d, Rr, d, 3 * d, Sq, c->part, d, Rd, 0));
             RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Sq, Rd, B.Na, B.ra, Rr, d, rms, c->dH, c->dHb,
