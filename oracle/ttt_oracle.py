@@ -452,9 +452,12 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
     last completed chunk before it, and a trailing partial chunk takes no step. The step is
     the clipped mini-batch step of [E2E] eq. (5) / [SGF]. logit_probe(t - 1, z), when given,
     sees the logits row that scored token t.
+
+    With attention, each decoded token's key and value are computed at the weights current
+    when it is decoded and join the cache at once; a filled mini-batch's step starts from the
+    cache as it stood before the mini-batch (its own keys come from its own rows, computed at
+    the same weights).
     """
-    if model.swa_window > 0:
-        raise NotImplementedError("decoding with sliding-window attention")
     P0 = as_f64(P0)
     tokens = np.asarray(tokens, dtype=np.int64)
     b = model.chunk
@@ -464,11 +467,16 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
     losses, argm, marg = [], [], []
     gn, sc, sk = [], [], []
     start = 0  # the pending mini-batch starts with the pair (x_start, x_start+1)
+    att = model.swa_window > 0
+    kv = None        # attention: keys and values of the positions decoded so far
+    kv_start = None  # and as they stood before the pending mini-batch
     for t in range(1, T + 1):
         P = dict(P0)
         for k in keys:
             P[k] = P0[k] + D[k]
-        z, _, _ = logits(model, P, tokens[t - 1:t])
+        z, _, cache = logits(model, P, tokens[t - 1:t], kv)
+        if att:
+            kv = next_kv(model, kv, cache)
         if logit_probe is not None:
             logit_probe(t - 1, z[0])
         l, _, am, mg = ce_stats(z, tokens[t:t + 1])
@@ -478,7 +486,7 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
         if t - start == b:
             # the decoded tokens fill a mini-batch: one clipped step on it, at the weights
             # that scored it
-            _, _, G = chunk_loss_and_grads(model, P, tokens[start:t], tokens[start + 1:t + 1])
+            _, _, G = chunk_loss_and_grads(model, P, tokens[start:t], tokens[start + 1:t + 1], kv=kv_start)
             g = math.sqrt(sum(float(np.sum(G[k] * G[k])) for k in keys))
             if math.isfinite(g):
                 s = clip_scale(g, model.clip)
@@ -492,6 +500,7 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
                 sc.append(0.0)
                 sk.append(True)
             start = t
+            kv_start = kv
     Wf = {k: P0[k] + D[k] for k in keys}
     return TTTResult(np.asarray(losses, dtype=np.float64), np.asarray(argm, dtype=np.int64),
                      np.asarray(marg, dtype=np.float64), np.asarray(gn), np.asarray(sc),

@@ -364,6 +364,40 @@ def test_p18_window_one_is_a_linear_residual_map():
     np.testing.assert_allclose(res.losses, ref, rtol=1e-12)
 
 
+@pytest.mark.parametrize("win,b,ms", [(5, 3, 0), (2, 4, 3), (40, 3, 0)])
+def test_p19_decoding_with_attention_equals_prefill(win, b, ms):
+    """[E2E] section 3.2 with the attention of section 3: decoding whole mini-batches token by
+    token (each token's key and value joining the cache at once) takes the same steps and
+    scores the same losses as prefilling them, to rounding."""
+    model = tiny_model("gelu", "rms", L=2, b=b, lr=0.4, clip=0.3, ms=ms, win=win, heads=2)
+    P = tiny_params(model, seed=43)
+    x = tiny_tokens(model, 4 * b, seed=44)
+    pre = O.run_ttt(model, P, x)
+    dec = O.decode_ttt(model, P, x)
+    np.testing.assert_allclose(dec.losses, pre.losses, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dec.grad_norm, pre.grad_norm, rtol=1e-12)
+    for k in model.fast_keys():
+        np.testing.assert_allclose(dec.weights[k], pre.weights[k], rtol=1e-12, atol=1e-15)
+
+
+def test_pins_catch_a_decode_cache_one_token_behind(monkeypatch):
+    """A decoded token that does not see the token just before it (the cache extended one
+    token late) breaks the decode = prefill identity."""
+    model = tiny_model("gelu", "rms", L=2, b=3, lr=0.4, win=5, heads=2)
+    P = tiny_params(model, seed=45)
+    x = tiny_tokens(model, 9, seed=46)
+    pre = O.run_ttt(model, P, x)
+    real_swa = O.swa_forward
+
+    def lagging(model, P, l, n, kv):
+        if n.shape[0] == 1 and kv is not None and kv["k"].shape[0] > 0:
+            kv = dict(k=kv["k"][:-1], v=kv["v"][:-1])
+        return real_swa(model, P, l, n, kv)
+    monkeypatch.setattr(O, "swa_forward", lagging)
+    dec = O.decode_ttt(model, P, x)
+    assert np.max(np.abs(dec.losses - pre.losses)) > 1e-6
+
+
 def test_pins_catch_a_cache_cut_short_by_index_wrap(monkeypatch):
     """A cache that keeps only the last (window - 1) - n rows while fewer than window - 1
     positions exist (a negative slice start wrapping around) is caught by the torch second
