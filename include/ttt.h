@@ -142,10 +142,11 @@ int32_t ttt_streams(const ttt_ctx* ctx);
  * Attention: swa_heads heads of 128 (d_model = 128 swa_heads), TTT_BF16 only;
  * q = n Wq, k = n Wk, v = n Wv, softmax(q.k / sqrt(128)) over the keys of the last k
  * positions up to the query's own (no positional encoding), output o Wo. Each position's key
- * and value are computed once, at the weights of the chunk that first processes it, and kept
- * in a ring of k positions per block and stream (4 k d bytes); later chunks read them as
- * constants. A context with attention supports prefill (single or batched) and the readers;
- * decode, evaluation, snapshots and Settlement return TTT_EINVAL.
+ * and value are computed once, at the weights of the chunk (or the decoded token) that first
+ * processes it, and kept in a ring of k + chunk positions per block and stream, hi and lo
+ * bf16 terms (8 (k + chunk) d bytes); later chunks read them as constants. A context with
+ * attention supports prefill (single or batched), decode (single stream) and the readers;
+ * evaluation, snapshots and Settlement return TTT_EINVAL.
  *   ws1[l] [d x m_s], ws2[l] [m_s x d], wq/wk/wv/wo[l] [d x d]: HOST arrays of n_blocks
  *   device pointers, element type as the other weights; copied at creation like them.
  *   Arrays of an absent layer are ignored. */

@@ -382,6 +382,7 @@ class TTTResult:
     skipped: np.ndarray         # chunk took no step (non-finite g)
     delta: Dict[str, np.ndarray]   # D = W_{T/b} - W_0 per fast tensor
     weights: Dict[str, np.ndarray]  # W_{T/b} = W_0 + D
+    kv: Optional[list] = None   # attention: the keys and values the run leaves in the cache
 
     @property
     def mean_loss(self) -> float:
@@ -439,7 +440,7 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
                      np.concatenate(argm) if argm else np.zeros(0, np.int64),
                      np.concatenate(marg) if marg else np.zeros(0),
                      np.asarray(gn), np.asarray(sc), np.asarray(sk, dtype=bool),
-                     D, Wf)
+                     D, Wf, kv)
 
 
 def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logit_probe=None) -> TTTResult:
@@ -504,7 +505,7 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
     Wf = {k: P0[k] + D[k] for k in keys}
     return TTTResult(np.asarray(losses, dtype=np.float64), np.asarray(argm, dtype=np.int64),
                      np.asarray(marg, dtype=np.float64), np.asarray(gn), np.asarray(sc),
-                     np.asarray(sk, dtype=bool), D, Wf)
+                     np.asarray(sk, dtype=bool), D, Wf, kv)
 
 
 def passage_loss(model: Model, P: Dict[str, np.ndarray], q: np.ndarray) -> float:

@@ -614,6 +614,122 @@ __global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv
   }
 }
 
+// ---------------------------------------------------------------------------- decode
+// One decoded row (position p, its q | k | v in fp32, qkv [3d]): its key and value join the
+// ring first (hi + lo bf16 terms, as the chunk path stores them), then the attention reads
+// keys max(0, p - window + 1) .. p of the ring in fp32 (hi + lo). Work: grid (H, nsplit), each
+// workgroup a contiguous share of the keys in blocks of 256, online softmax over the blocks;
+// k_swa_dec_merge combines the shares per head.
+constexpr int DEC_KB = 256;  // keys per block of the decode kernel
+
+__global__ void __launch_bounds__(NT_A) k_swa_dec_append(const float* __restrict__ qkv, int d, int64_t p, int cr,
+                                                         bf16_t* __restrict__ kc, bf16_t* __restrict__ kc_lo,
+                                                         bf16_t* __restrict__ vc, bf16_t* __restrict__ vc_lo) {
+  const int64_t o = (p % cr) * d;
+  for (int i = threadIdx.x; i < d; i += NT_A) {
+    const float k = qkv[d + i], v = qkv[2 * d + i];
+    const bf16_t kh = f2bf(k), vh = f2bf(v);
+    kc[o + i] = kh;
+    kc_lo[o + i] = f2bf(k - bf2f(kh));
+    vc[o + i] = vh;
+    vc_lo[o + i] = f2bf(v - bf2f(vh));
+  }
+}
+
+__global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv, const bf16_t* __restrict__ kc,
+                                                  const bf16_t* __restrict__ kc_lo, const bf16_t* __restrict__ vc,
+                                                  const bf16_t* __restrict__ vc_lo, int d, int64_t p, int cr,
+                                                  int window, float* __restrict__ part) {
+  __shared__ float sq[DH];
+  __shared__ float sp[DEC_KB];
+  __shared__ float red[8];
+  __shared__ float so[DH];
+  const int h = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
+  const int t = threadIdx.x;
+  if (t < DH) sq[t] = qkv[h * DH + t] * 0.08838834764831845f;  // q / sqrt(128)
+  int64_t k0 = p - window + 1;
+  if (k0 < 0) k0 = 0;
+  const int64_t nk = p - k0 + 1;
+  const int64_t nblk = (nk + DEC_KB - 1) / DEC_KB;
+  const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
+  float m = -INFINITY, l = 0.f, acc = 0.f;  // acc: dim t % 128, keys of half t / 128
+  const int dim = t & (DH - 1), half = t >> 7;
+  __syncthreads();
+  for (int64_t blk = b0; blk < b1; ++blk) {
+    const int64_t kb = k0 + blk * DEC_KB;
+    const int64_t kp = kb + t;
+    // score of key kp (one key per thread)
+    float s = -INFINITY;
+    if (kp <= p) {
+      const int64_t r = (kp % cr) * d + h * DH;
+      float a = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < DH; c += 8) {
+        const uint4 u = *(const uint4*)(kc + r + c), w = *(const uint4*)(kc_lo + r + c);
+        const bf16_t* e = (const bf16_t*)&u;
+        const bf16_t* f = (const bf16_t*)&w;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a = fmaf(bf2f(e[q]) + bf2f(f[q]), sq[c + q], a);
+      }
+      s = a * LOG2E;
+    }
+    // block max and the rescale of the running state
+    float bm = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off, TTT_WAVE));
+    if ((t & 63) == 0) red[t >> 6] = bm;
+    __syncthreads();
+    bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float mn = fmaxf(m, bm);
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float pk = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mn);
+    sp[t] = pk;
+    float ps = pk;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) ps += __shfl_xor(ps, off, TTT_WAVE);
+    __syncthreads();  // sp complete; red free again
+    if ((t & 63) == 0) red[4 + (t >> 6)] = ps;
+    __syncthreads();
+    l = l * alpha + ((red[4] + red[5]) + (red[6] + red[7]));
+    m = mn;
+    // this thread's dim over its half of the block's keys
+    acc *= alpha;
+    for (int j = half * (DEC_KB / 2); j < (half + 1) * (DEC_KB / 2); ++j) {
+      const int64_t kq = kb + j;
+      if (kq > p) break;
+      const int64_t r = (kq % cr) * d + h * DH + dim;
+      acc = fmaf(sp[j], bf2f(vc[r]) + bf2f(vc_lo[r]), acc);
+    }
+    __syncthreads();  // sp and red are rewritten by the next block
+  }
+  // the two halves' sums per dim, then this share's (max, sum, o[128])
+  if (half == 1) so[dim] = acc;
+  __syncthreads();
+  float* P = part + ((int64_t)h * nsplit + split) * (DH + 2);
+  if (half == 0) P[dim] = acc + so[dim];
+  if (t == 0) {
+    P[DH] = m;
+    P[DH + 1] = l;
+  }
+}
+
+// o [d] = per head, the shares' states combined: grid (H), 128 threads.
+__global__ void __launch_bounds__(DH) k_swa_dec_merge(const float* __restrict__ part, int nsplit,
+                                                      float* __restrict__ o) {
+  const int h = blockIdx.x, t = threadIdx.x;
+  const float* P = part + (int64_t)h * nsplit * (DH + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P[s * (DH + 2) + DH]);
+  float L = 0.f, a = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = P[s * (DH + 2) + DH];
+    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L += w * P[s * (DH + 2) + DH + 1];
+    a += w * P[s * (DH + 2) + t];
+  }
+  o[h * DH + t] = L > 0.f ? a / L : 0.f;
+}
+
 SwaGeo geo(const SwaShape& s) {
   SwaGeo g;
   g.qkv = (const bf16_t*)s.qkv;
@@ -675,6 +791,24 @@ hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, cons
   if (ns > 1) hipLaunchKernelGGL(k_swa_dq_sum, dim3(R), dim3(NT_A), 0, st, part, ns, s.d, (bf16_t*)dQKV);
   dim3 grid((s.b + BLK - 1) / BLK, H, s.streams);
   hipLaunchKernelGGL(k_swa_bwd_dkdv, grid, dim3(NT_A), 0, st, geo(s), (const bf16_t*)dOb, lse2, Dq, (bf16_t*)dQKV);
+  return hipGetLastError();
+}
+
+int swa_dec_splits(int window) {
+  const int blocks = (window + DEC_KB - 1) / DEC_KB;
+  return blocks < 16 ? (blocks < 1 ? 1 : blocks) : 16;
+}
+
+hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o) {
+  if (!qkv || !part || !o || s.d % DH || s.cr < 1 || s.window < 1 || s.pos < 0 || !s.kc || !s.vc || !s.kc_lo ||
+      !s.vc_lo)
+    return hipErrorInvalidValue;
+  const int H = s.d / DH, ns = swa_dec_splits(s.window);
+  hipLaunchKernelGGL(k_swa_dec_append, dim3(1), dim3(NT_A), 0, st, qkv, s.d, s.pos, s.cr, (bf16_t*)s.kc,
+                     (bf16_t*)s.kc_lo, (bf16_t*)s.vc, (bf16_t*)s.vc_lo);
+  hipLaunchKernelGGL(k_swa_dec, dim3(H, ns), dim3(NT_A), 0, st, qkv, (const bf16_t*)s.kc, (const bf16_t*)s.kc_lo,
+                     (const bf16_t*)s.vc, (const bf16_t*)s.vc_lo, s.d, s.pos, s.cr, s.window, part);
+  hipLaunchKernelGGL(k_swa_dec_merge, dim3(H), dim3(DH), 0, st, part, ns, o);
   return hipGetLastError();
 }
 

@@ -117,6 +117,11 @@ hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, v
 // part: scratch for the split dQ partials, [swa_fwd_splits(s)][streams b x d] fp32.
 hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
                        const float* lse2, float* Dq, void* dQKV, float* part);
+// Decode of one row at position s.pos (single stream): its q | k | v (fp32 qkv [3d]) join the
+// ring, then o [d] (fp32) = its attention over the window; part is scratch of
+// d / 128 * swa_dec_splits(window) * 130 floats.
+int swa_dec_splits(int window);
+hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o);
 // The chunk's last min(b, cr) keys and values into the ring.
 hipError_t run_kv_append(hipStream_t st, const SwaShape& s);
 

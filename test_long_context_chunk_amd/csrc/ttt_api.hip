@@ -129,6 +129,9 @@ struct ttt_ctx {
   bool has_snap = false;
   float *dec_h = nullptr, *dec_a = nullptr, *dec_z = nullptr, *dec_rmax = nullptr, *dec_rsum = nullptr;
   int* dec_ridx = nullptr;
+  // decode with attention: the row's q | k | v [3d], the attention output [d] and the
+  // attention's per-share states
+  float *dec_qkv = nullptr, *dec_o = nullptr, *dec_part = nullptr;
   float* part = nullptr;
   float* dH = nullptr;
   void *dHb = nullptr, *dHT = nullptr, *A = nullptr, *dU = nullptr, *dUT = nullptr;
@@ -472,6 +475,9 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
   if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)Rr * m * 4);
   if (c->window > 0 && L > 0) {
+    c->dec_qkv = dalloc<float>(c, (int64_t)3 * d * 4);
+    c->dec_o = dalloc<float>(c, (int64_t)d * 4);
+    c->dec_part = dalloc<float>(c, (int64_t)(d / 128) * swa_dec_splits(c->window) * 130 * 4);
     c->dOf = dalloc<float>(c, (int64_t)Rr * d * 4);
     c->dOb = dalloc<char>(c, (int64_t)Rr * d * es);
     c->Dq = dalloc<float>(c, (int64_t)Rr * (d / 128) * 4);
@@ -869,6 +875,15 @@ void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out)
   };
   for (int l = 0; l < L; ++l) {
     Block& B = c->blocks[l];
+    if (c->window > 0) {
+      // the frozen sliding-window attention first: q | k | v of the row, its key and value
+      // join the ring at position pos, the attention over the window, the output projection
+      RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_STORE, next_in(), d, B.WqkvT, nullptr, d, 3 * d, c->dec_qkv));
+      RUN(TTT_K_ATTN, run_swa_decode(st, swa_shape(c, B, c->pos), c->dec_qkv, c->dec_part, c->dec_o));
+      GemvIn go;
+      go.xin = c->dec_o;
+      RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_RESIDUAL, go, d, B.WoT, nullptr, d, d, c->dec_h));
+    }
     if (c->ms > 0) {  // the frozen static MLP first
       RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_GELU, next_in(), d, B.SW1T, nullptr, d, c->ms, c->dec_a));
       RUN(TTT_K_DEC_GEMV, run_gemv(st, prec, GEMV_RESIDUAL, ga, c->ms, B.SW2T, nullptr, c->ms, d, c->dec_h));
@@ -968,7 +983,9 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   c->Rp = streams * c->bp;
   c->ms = ext ? ext->static_hidden : 0;
   c->window = ext ? ext->swa_window : 0;
-  c->cr = c->window;
+  // ring positions: the window, plus the b positions a pending decoded chunk writes before
+  // its step reads the window in front of it
+  c->cr = c->window > 0 ? c->window + c->b : 0;
   c->V = cfg->vocab;
   c->d = cfg->d_model;
   c->m = cfg->d_hidden;
@@ -1029,7 +1046,7 @@ ttt_status ttt_prefill_batch(ttt_ctx* c, const int32_t* tokens, int64_t ld_token
 }
 
 ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* argmax, float* logits) {
-  if (!c || !tokens || n < 0 || c->nb != 1 || c->window > 0) return TTT_EINVAL;
+  if (!c || !tokens || n < 0 || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + n > c->cfg.max_tokens) return TTT_EINVAL;
   if (n == 0) return TTT_OK;

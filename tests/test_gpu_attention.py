@@ -7,14 +7,16 @@ its own chunk's weights and kept in a ring; later chunks read them as constants,
 inner loop backpropagates through the current chunk's queries, keys and values into the fast
 blocks below. Checks: windows shorter than, equal to and longer than the chunk and than the
 whole stream, one and two heads, with and without the static MLP, several prefill calls,
-batched streams, the fuller-block 760M shape (sampled), and the calls an attention context
-refuses. Gates are those of tests/_parity.py (bf16).
+batched streams, the fuller-block 760M shape (sampled), decoding (each decoded row's key and
+value join the ring at once; a filled chunk's step reads the window in front of it), and the
+calls an attention context refuses. Gates are those of tests/_parity.py (bf16).
 """
 import numpy as np
 import pytest
 
-from _parity import compare, device_weights, gpu_run, log, oracle_run
+from _parity import TOL, compare, device_weights, gpu_run, log, oracle_run, rel_l2
 
+import oracle as O
 import ttt_workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -74,10 +76,103 @@ def test_attention_context_refuses_single_row_calls(ttt_lib):
     lib, c = ctx._lib, ctx._ctx
     tok = torch.zeros(130, dtype=torch.int32, device="cuda")
     p = ctypes.c_void_p(tok.data_ptr())
-    assert lib.ttt_decode(c, p, 1, None, None) == -1
     assert lib.ttt_evaluate(c, p, 64, None, None) == -1
     assert lib.ttt_snapshot(c) == -1
     assert lib.ttt_settle_chunk(c, p, p, 64, None, None) == -1
     ctx.prefill(tok[:65])
     assert ctx.sync() == 0 and ctx.consumed() == 64
     ctx.close()
+
+
+def _tok(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+@pytest.mark.parametrize("window,d", [(40, 128), (96, 256), (1000, 128)])
+def test_attention_decode_matches_oracle_decode(ttt_lib, window, d):
+    """One prefilled chunk, then 1.5 chunks decoded in two calls (one step in between):
+    every decoded row's logits and the fast weights after the step, against the oracle's
+    token-by-token decode."""
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m", **dict(BASE, d_model=d, swa_heads=d // 128, swa_window=window, static_hidden=128))
+    P = W.init_weights(w, 17)
+    x = W.token_stream(w, 18)
+    b = w.chunk
+    n = b + b // 2
+    log(f"attention decode window={window} d={d}")
+    ctx = ttt.TTT.from_workload(w, device_weights(P, "bf16"), max_tokens=w.n_tokens)
+    ctx.prefill(_tok(x[:b + 1]))
+    _, z1 = ctx.decode(_tok(x[b:b + 40 + 1]), want_logits=True)
+    _, z2 = ctx.decode(_tok(x[b + 40:b + n + 1]), want_logits=True)
+    zg = np.concatenate([z1.cpu().numpy(), z2.cpu().numpy()]).astype(np.float64)
+    assert ctx.decode_pending() == n - b
+    Dg = {f"{k}.{l}": ctx.fast_weight(l, k, "delta").cpu().numpy().astype(np.float64)
+          for l in range(w.n_blocks) for k in w.fast_names()}
+    assert ctx.sync() == 0
+    ctx.close()
+    rows = []
+    orc = O.decode_ttt(O.Model.from_workload(w), P, x[:b + n + 1], logit_probe=lambda t, z: rows.append((t, z.copy())))
+    Z = np.stack([z for t, z in rows if t >= b])
+    tol = TOL["bf16"]
+    dz = float(np.max(np.abs(zg - Z)))
+    dd = max(rel_l2(Dg[k], orc.delta[k]) for k in orc.delta)
+    log(f"[attention decode w{window}] logits {dz:.3g} D {dd:.3g}")
+    assert dz <= tol["logit"]
+    assert dd <= tol["dw"]
+
+
+def test_attention_decoded_chunk_is_bitwise_the_prefilled_step(ttt_lib):
+    """Prefill of chunks 0-1 vs prefill of chunk 0 and chunk 1 decoded (three uneven calls),
+    then chunk 2 prefilled on both: chunk 1's step re-files its keys from its own forward, so
+    every loss, step and update of the two contexts is bitwise equal."""
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m", **dict(BASE, swa_window=100, static_hidden=128))
+    P = W.init_weights(w, 19)
+    x = W.token_stream(w, 20)
+    b = w.chunk
+    dev = device_weights(P, "bf16")
+    a = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
+    a.prefill(_tok(x[:2 * b + 1]))
+    c = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
+    c.prefill(_tok(x[:b + 1]))
+    for s0, e in [(b, b + 5), (b + 5, b + 50), (b + 50, 2 * b)]:
+        c.decode(_tok(x[s0:e + 1]))
+    assert c.decode_pending() == 0 and c.consumed() == 2 * b
+    for ctx in (a, c):
+        ctx.prefill(_tok(x[2 * b:3 * b + 1]))
+    assert np.array_equal(a.token_losses().cpu().numpy(), c.token_losses().cpu().numpy())
+    assert np.array_equal(a.chunk_stats().cpu().numpy(), c.chunk_stats().cpu().numpy())
+    for l in range(w.n_blocks):
+        for k in w.fast_names():
+            assert np.array_equal(a.fast_weight(l, k, "delta").cpu().numpy(),
+                                  c.fast_weight(l, k, "delta").cpu().numpy()), (k, l)
+    assert a.sync() == 0 and c.sync() == 0
+    a.close()
+    c.close()
+
+
+def test_e2e760m_attention_decode_sampled(ttt_lib):
+    """The fuller 760M block: two prefilled chunks, then 16 decoded rows scored at the
+    stepped weights against the oracle's logits (the rows read the prefilled keys)."""
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m", n_tokens=3072)
+    P = W.init_weights(w, 0)
+    x = W.token_stream(w, 0)
+    b, n = w.chunk, 16
+    T0 = 2 * b
+    log("attention decode e2e760m")
+    ctx = ttt.TTT.from_workload(w, device_weights(P, "bf16"), max_tokens=T0 + b)
+    ctx.prefill(_tok(x[:T0 + 1]))
+    _, z = ctx.decode(_tok(x[T0:T0 + n + 1]), want_logits=True)
+    z = z.cpu().numpy().astype(np.float64)
+    assert ctx.sync() == 0
+    ctx.close()
+    model = O.Model.from_workload(w)
+    orc = oracle_run(w, P, x, 2)
+    Pw = dict(O.as_f64(P))
+    Pw.update(orc.weights)
+    zo, _, _ = O.logits(model, Pw, x[T0:T0 + n], orc.kv)
+    dz = float(np.max(np.abs(z - zo)))
+    log(f"[attention decode e2e760m] logits {dz:.3g}")
+    assert dz <= TOL["bf16"]["logit"]
