@@ -34,7 +34,7 @@ struct SwaGeo {
 
 // Where the rows of one key block [kb, kb + BLK) come from, with 32-bit per-row arithmetic:
 // the first nr rows from the ring (slot s0 + r, wrapping at cr), the others from the chunk's
-// own rows (chunk row c0 + r - nr); rows past `last` (block-relative) are absent.
+// own rows (chunk row c0 + r - nr); rows past `last` (block-relative) lie beyond the range.
 struct KeySrc {
   int nr, s0, c0, last;
 };
@@ -48,18 +48,6 @@ __device__ __forceinline__ KeySrc key_src(const SwaGeo& g, int64_t kb, int64_t k
   k.last = l >= BLK ? BLK - 1 : (int)l;
   return k;
 }
-__device__ __forceinline__ const bf16_t* key_row(const SwaGeo& g, const KeySrc& k, int z, int r, int which, int h,
-                                                 bool lo = false) {
-  if (r > k.last) return nullptr;
-  if (r < k.nr) {
-    int slot = k.s0 + r;
-    if (slot >= g.cr) slot -= g.cr;
-    const bf16_t* ring = which == 1 ? (lo ? g.kc_lo : g.kc) : (lo ? g.vc_lo : g.vc);
-    return ring + ((int64_t)z * g.cr + slot) * g.d + h * DH;
-  }
-  return (lo ? g.qkv_lo : g.qkv) + ((int64_t)z * g.b + k.c0 + (r - k.nr)) * (3 * (int64_t)g.d) +
-         (int64_t)which * g.d + h * DH;
-}
 
 // Staging through registers: a block of BLK rows is 1024 16-byte chunks, four per thread.
 // All four are requested before any is stored, and a loop requests the next block's chunks
@@ -68,26 +56,6 @@ constexpr int CPT = BLK * (DH / 8) / NT_A;  // chunks per thread per tile
 struct Chunks {
   uint4 v[CPT];
 };
-template <class Src>
-__device__ __forceinline__ void fetch(Chunks& R, Src src) {
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * NT_A;
-    const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
-    const bf16_t* s = src(r);
-    R.v[i] = s ? *(const uint4*)(s + c) : make_uint4(0, 0, 0, 0);
-  }
-}
-// Into a [row][dim] tile.
-__device__ __forceinline__ void put(const Chunks& R, bf16_t* tile) {
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * NT_A;
-    const int r = idx / (DH / 8), c = (idx % (DH / 8)) * 8;
-    *(uint4*)(tile + r * LDR + c) = R.v[i];
-  }
-}
-
 // Blocks that also go into a [dim][row] tile are fetched as row pairs: chunk i of a thread is
 // row 2 p + (i % 2), p = lane-in-32, at 16-byte column (t / 32) + 8 (i / 2). A pair gives one
 // 4-byte word per dim, and the 64 lanes of a wave store to 64 distinct banks (row stride 72).
@@ -109,12 +77,51 @@ __device__ __forceinline__ void put_p(const Chunks& R, bf16_t* tile, bf16_t* T) 
       *(uint4*)(tile + (2 * p) * LDR + c) = a;
       *(uint4*)(tile + (2 * p + 1) * LDR + c) = b;
     }
+    if (!T) continue;
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // dims c + 2q (low halves) and c + 2q + 1 (high halves) of rows 2p, 2p + 1
       *(uint32_t*)(T + (c + 2 * q) * LDT + 2 * p) = __builtin_amdgcn_perm(wb[q], wa[q], 0x05040100u);
       *(uint32_t*)(T + (c + 2 * q + 1) * LDT + 2 * p) = __builtin_amdgcn_perm(wb[q], wa[q], 0x07060302u);
+    }
+  }
+}
+
+// Key-block fetch in the row-pair layout of fetch_p for several tiles at once (keys or
+// values, hi or lo terms). Each tile's base pointers for the workgroup's stream and head are
+// set up once (uniform over the workgroup); per block a thread resolves its two rows (ring
+// slot or chunk row, plus its 16-byte column) once and reads every tile from them. Rows past the block's last
+// key repeat that key: its scores are masked and its probabilities are zero, so the values
+// only have to be finite.
+struct KvBase {
+  const bf16_t* ring;   // slot 0 of the stream's ring
+  const bf16_t* chunk;  // row 0 of the stream's chunk rows (q | k | v)
+};
+__device__ __forceinline__ KvBase kv_base(const SwaGeo& g, int z, int h, int which, bool lo) {
+  const bf16_t* ring = which == 1 ? (lo ? g.kc_lo : g.kc) : (lo ? g.vc_lo : g.vc);
+  KvBase b;
+  b.ring = ring + (int64_t)z * g.cr * g.d + h * DH;
+  b.chunk = (lo ? g.qkv_lo : g.qkv) + (int64_t)z * g.b * (3 * (int64_t)g.d) + (int64_t)which * g.d + h * DH;
+  return b;
+}
+template <int NTL>
+__device__ __forceinline__ void fetch_rows(Chunks (&R)[NTL], const KvBase (&B)[NTL], const SwaGeo& g,
+                                           const KeySrc& ks) {
+  const int p = threadIdx.x & 31, col = (threadIdx.x >> 5) * 8;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int r = min(2 * p + a, ks.last);
+    const bool ring = r < ks.nr;
+    int slot = ks.s0 + r;  // used for ring rows only: then below 2 cr
+    if (slot >= g.cr) slot -= g.cr;
+    const int64_t ro = (int64_t)slot * g.d + col;
+    const int64_t co = (int64_t)(ks.c0 + r - ks.nr) * (3 * (int64_t)g.d) + col;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const bf16_t* src = ring ? B[t].ring + ro : B[t].chunk + co;
+      R[t].v[a] = *(const uint4*)src;
+      R[t].v[2 + a] = *(const uint4*)(src + 64);
     }
   }
 }
@@ -150,7 +157,7 @@ struct SwaSplit {
   float* pl;    // [n][streams][H][b] sum of 2^(s - max)
 };
 
-__global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
+__global__ void __launch_bounds__(NT_A, 2) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
                                                   bf16_t* __restrict__ Ob, bf16_t* __restrict__ Ol,
                                                   float* __restrict__ lse2) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
@@ -193,21 +200,19 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, SwaSplit sp, float* 
     kend = min(qhi, klo + b1 * BLK - 1);
     klo += b0 * BLK;
   }
-  Chunks ck, ckl, cv, cvl;
-  auto fetch_block = [&](int64_t kb) {
-    const KeySrc ks = key_src(g, kb, qhi);
-    fetch(ck, [&](int r) { return key_row(g, ks, z, r, 1, h, false); });
-    fetch(ckl, [&](int r) { return key_row(g, ks, z, r, 1, h, true); });
-    fetch_p(cv, [&](int r) { return key_row(g, ks, z, r, 2, h, false); });
-    fetch_p(cvl, [&](int r) { return key_row(g, ks, z, r, 2, h, true); });
-  };
+  Chunks cb[4];  // K, K lo, V, V lo
+  const KvBase kvb[4] = {kv_base(g, z, h, 1, false), kv_base(g, z, h, 1, true), kv_base(g, z, h, 2, false),
+                         kv_base(g, z, h, 2, true)};
+  auto fetch_block = [&](int64_t kb) { fetch_rows<4>(cb, kvb, g, key_src(g, kb, qhi)); };
+  // the wave's first query position (its 16 queries follow)
+  const int64_t qw0 = g.pos + q0 + wave * 16;
   if (klo <= kend) fetch_block(klo);
   for (int64_t kb = klo; kb <= kend; kb += BLK) {
     __syncthreads();  // the previous block's tiles are no longer read
-    put(ck, sK);
-    put(ckl, sKl);
-    put_p(cv, nullptr, sVt);
-    put_p(cvl, nullptr, sVtl);
+    put_p(cb[0], sK, nullptr);
+    put_p(cb[1], sKl, nullptr);
+    put_p(cb[2], nullptr, sVt);
+    put_p(cb[3], nullptr, sVtl);
     __syncthreads();
     if (kb + BLK <= kend) fetch_block(kb + BLK);  // in flight during this block's MFMAs
 
@@ -225,18 +230,29 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, SwaSplit sp, float* 
         mfma_chunk(st[j], a, qfl[s], bf16_t());
       }
     }
-    // mask (distance query - key in [0, window), 32-bit) and block max (scaled units)
+    // mask (distance query - key in [0, window), 32-bit) and block max (scaled units); a
+    // block that every query of the wave sees whole needs no mask
     float bm = -INFINITY;
-    const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
+    if (qw0 - (kb + BLK - 1) >= 0 && qw0 + 15 - kb < g.window) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dist = dq0 - 16 * j - e;
-        const bool ok = dist >= 0 && dist < g.window;
-        st[j][e] = ok ? st[j][e] * sc : -INFINITY;
-        bm = fmaxf(bm, st[j][e]);
-      }
+        for (int e = 0; e < 4; ++e) {
+          st[j][e] *= sc;
+          bm = fmaxf(bm, st[j][e]);
+        }
+    } else {
+      const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dist = dq0 - 16 * j - e;
+          const bool ok = dist >= 0 && dist < g.window;
+          st[j][e] = ok ? st[j][e] * sc : -INFINITY;
+          bm = fmaxf(bm, st[j][e]);
+        }
+    }
     bm = fmaxf(bm, __shfl_xor(bm, 16, TTT_WAVE));
     bm = fmaxf(bm, __shfl_xor(bm, 32, TTT_WAVE));
     // online softmax; a query with no visible key yet keeps m = -inf and adds zeros (no
@@ -245,8 +261,10 @@ __global__ void __launch_bounds__(NT_A) k_swa_fwd(SwaGeo g, SwaSplit sp, float* 
     const float alpha = (m == -INFINITY || mn == -INFINITY) ? (m == mn ? 1.f : 0.f) : __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     lsum *= alpha;
+    if (__any(alpha != 1.f)) {  // once the maxima settle, most blocks leave O as it is
 #pragma unroll
-    for (int c = 0; c < 8; ++c) ot[c] *= alpha;
+      for (int c = 0; c < 8; ++c) ot[c] *= alpha;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -403,17 +421,15 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, int nsplit, float
     kend = min(qhi, klo + b1 * BLK - 1);
     klo += b0 * BLK;
   }
-  Chunks ck, cv;
-  auto fetch_block = [&](int64_t kb) {
-    const KeySrc ks = key_src(g, kb, qhi);
-    fetch_p(ck, [&](int r) { return key_row(g, ks, z, r, 1, h); });
-    fetch(cv, [&](int r) { return key_row(g, ks, z, r, 2, h); });
-  };
+  Chunks cb[2];  // K, V
+  const KvBase kvb[2] = {kv_base(g, z, h, 1, false), kv_base(g, z, h, 2, false)};
+  auto fetch_block = [&](int64_t kb) { fetch_rows<2>(cb, kvb, g, key_src(g, kb, qhi)); };
+  const int64_t qw0 = g.pos + q0 + wave * 16;
   if (klo <= kend) fetch_block(klo);
   for (int64_t kb = klo; kb <= kend; kb += BLK) {
     __syncthreads();
-    put_p(ck, sK, sKt);
-    put(cv, sV);
+    put_p(cb[0], sK, sKt);
+    put_p(cb[1], sV, nullptr);
     __syncthreads();
     if (kb + BLK <= kend) fetch_block(kb + BLK);
     f32x4_t st[4], dp[4];
@@ -427,17 +443,25 @@ __global__ void __launch_bounds__(NT_A) k_swa_bwd_dq(SwaGeo g, int nsplit, float
         mfma_chunk(dp[j], *(const uint4*)(sV + (16 * j + lr) * LDR + 32 * s + 8 * lg), df[s], bf16_t());
       }
     }
-    // dS = P (dP - D), P = exp2(s sc - lse2) on the window, 0 elsewhere
-    const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
+    // dS = P (dP - D), P = exp2(s sc - lse2) on the window, 0 elsewhere (no mask for a
+    // block every query of the wave sees whole)
+    if (qw0 - (kb + BLK - 1) >= 0 && qw0 + 15 - kb < g.window) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dist = dq0 - 16 * j - e;
-        const bool ok = dist >= 0 && dist < g.window;
-        const float p = ok ? __builtin_amdgcn_exp2f(st[j][e] * sc - L2) : 0.f;
-        st[j][e] = p * (dp[j][e] - Dv);
-      }
+        for (int e = 0; e < 4; ++e) st[j][e] = __builtin_amdgcn_exp2f(st[j][e] * sc - L2) * (dp[j][e] - Dv);
+    } else {
+      const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dist = dq0 - 16 * j - e;
+          const bool ok = dist >= 0 && dist < g.window;
+          const float p = ok ? __builtin_amdgcn_exp2f(st[j][e] * sc - L2) : 0.f;
+          st[j][e] = p * (dp[j][e] - Dv);
+        }
+    }
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -486,7 +510,7 @@ __global__ void __launch_bounds__(NT_A) k_swa_dq_sum(const float* __restrict__ p
 // dK, dV of the chunk's own keys: grid (ceil(b / 64), H, streams); each lane owns one key.
 // dV = sum_q P dO, dK = (1 / sqrt(128)) sum_q dS Q over the chunk's queries that see the key;
 // written (bf16) into columns d + 128 h .. and 2 d + 128 h .. of dQKV.
-__global__ void __launch_bounds__(NT_A) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* __restrict__ dOb,
+__global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* __restrict__ dOb,
                                                        const float* __restrict__ lse2, const float* __restrict__ Dq,
                                                        bf16_t* __restrict__ dQKV) {
   __shared__ __attribute__((aligned(16))) bf16_t sQ[BLK * LDR];
