@@ -378,6 +378,7 @@ __device__ __forceinline__ void dma_slice(const char* const (&p1)[PW], const cha
 template <int BM, int BN, int WGM, int WGN>
 __device__ __forceinline__ void mma_slice32(const char* cur, int wm, int wn, int lane,
                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  __builtin_amdgcn_iglp_opt(0);  // let the scheduler interleave the LDS reads with the MFMAs
   constexpr int ROWB = 128;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
