@@ -509,26 +509,35 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
 
 
 def passage_loss(model: Model, P: Dict[str, np.ndarray], q: np.ndarray) -> float:
-    """L(q, W): the mean next-token loss of a passage q_0..q_n at fixed weights (no step)."""
-    if model.swa_window > 0:
-        raise NotImplementedError("passage evaluation with sliding-window attention")
+    """L(q, W): the mean next-token loss of a passage q_0..q_n at fixed weights (no step).
+
+    With attention the passage is a sequence of its own: its positions attend only within it
+    (an empty cache at q_0), and the stream's cache is neither read nor changed. [SGF],
+    Settlement, compares the two candidate states with the attention left as it is, so only
+    the fast weights differ between the two scores; scoring the passage apart from the stream
+    is the plainest reading of that.
+    """
     q = np.asarray(q, dtype=np.int64)
     l, _, _ = token_losses(model, as_f64(P), q[:-1], q[1:])
     return float(l.mean())
 
 
-def settle_step(model: Model, P: Dict[str, np.ndarray], cand: np.ndarray, q: np.ndarray):
+def settle_step(model: Model, P: Dict[str, np.ndarray], cand: np.ndarray, q: np.ndarray, kv=None):
     """The Settlement rule of [SGF] for one candidate chunk.
 
     From the current weights W (P), the candidate's update delta is the clipped mini-batch
     step of [E2E] eq. (5) on the candidate chunk cand_0..cand_b. On the held-out passage q,
     A(delta; W, q) = L(q, W) - L(q, W + delta), and delta is committed only if A >= 0.
     Returns (A, committed, the weights after the decision, g, s).
+
+    With attention, kv is the stream's cache in front of the candidate chunk. The chunk is
+    part of the stream whatever the decision: its keys and values (computed at W) join the
+    cache, as chunk_loss_and_grads(..., kv=kv)[1]["kv"] gives them.
     """
     P = as_f64(P)
     cand = np.asarray(cand, dtype=np.int64)
     keys = model.fast_keys()
-    _, _, G = chunk_loss_and_grads(model, P, cand[:-1], cand[1:])
+    _, _, G = chunk_loss_and_grads(model, P, cand[:-1], cand[1:], kv=kv)
     g = math.sqrt(sum(float(np.sum(G[k] * G[k])) for k in keys))
     s = clip_scale(g, model.clip) if math.isfinite(g) else 0.0
     Pd = dict(P)

@@ -380,6 +380,38 @@ def test_p19_decoding_with_attention_equals_prefill(win, b, ms):
         np.testing.assert_allclose(dec.weights[k], pre.weights[k], rtol=1e-12, atol=1e-15)
 
 
+def test_p20_passage_with_attention_is_a_stream_of_its_own():
+    """[SGF] Settlement scores a passage with the attention left as it is; read as a sequence
+    of its own, L(q, W) equals the mean loss of prefilling q from an empty cache at eta = 0
+    (chunk by chunk, each chunk reading the cache of the ones before)."""
+    model = tiny_model("gelu", "rms", L=2, b=3, lr=0.0, win=4, heads=2, ms=3)
+    P = tiny_params(model, seed=47)
+    q = tiny_tokens(model, 12, seed=48)
+    whole = O.passage_loss(model, P, q)
+    chunked = O.run_ttt(model, P, q)
+    assert abs(whole - float(chunked.losses.mean())) <= 1e-12 * abs(whole)
+
+
+def test_p21_kept_candidate_with_attention_is_the_stream_step():
+    """A kept Settlement candidate, stepped from the stream's cache in front of it, lands on
+    the weights the plain chunk loop reaches after the same chunk ([SGF] Settlement with the
+    step of [E2E] eq. (5)); the candidate here is scored on its own text, so it is kept."""
+    model = tiny_model("gelu", "rms", L=2, b=3, lr=0.2, clip=0.5, win=5, heads=2)
+    P = tiny_params(model, seed=49)
+    x = tiny_tokens(model, 6, seed=50)
+    one = O.run_ttt(model, P, x[:4])
+    two = O.run_ttt(model, P, x)
+    W1 = {**O.as_f64(P), **one.weights}
+    cand = x[3:]
+    A, keep, Wn, g, s = O.settle_step(model, W1, cand, cand, kv=one.kv)
+    assert keep and A > 0
+    for k in model.fast_keys():
+        np.testing.assert_allclose(Wn[k], two.weights[k], rtol=1e-12, atol=1e-15)
+    # without the stream's cache the candidate's step is another one
+    _, _, Wc, _, _ = O.settle_step(model, W1, cand, cand)
+    assert max(np.max(np.abs(Wc[k] - two.weights[k])) for k in model.fast_keys()) > 1e-6
+
+
 def test_pins_catch_a_decode_cache_one_token_behind(monkeypatch):
     """A decoded token that does not see the token just before it (the cache extended one
     token late) breaks the decode = prefill identity."""
