@@ -144,9 +144,13 @@ int32_t ttt_streams(const ttt_ctx* ctx);
  * positions up to the query's own (no positional encoding), output o Wo. Each position's key
  * and value are computed once, at the weights of the chunk (or the decoded token) that first
  * processes it, and kept in a ring of k + chunk positions per block and stream, hi and lo
- * bf16 terms (8 (k + chunk) d bytes); later chunks read them as constants. A context with
- * attention supports prefill (single or batched), decode (single stream) and the readers;
- * evaluation, snapshots and Settlement return TTT_EINVAL.
+ * bf16 terms (8 (k + chunk) d bytes); later chunks read them as constants. A single-stream
+ * context keeps a second set of rings for passages: ttt_evaluate scores a passage as a
+ * sequence of its own (its positions attend only within it) and leaves the stream's rings as
+ * they are ([SGF], Settlement: the two scores leave the attention unchanged). Snapshots hold
+ * the fast state only; a Settlement candidate's keys and values join the stream's rings
+ * whatever the decision, as its tokens join the stream. A batched context with attention
+ * supports prefill and the readers.
  *   ws1[l] [d x m_s], ws2[l] [m_s x d], wq/wk/wv/wo[l] [d x d]: HOST arrays of n_blocks
  *   device pointers, element type as the other weights; copied at creation like them.
  *   Arrays of an absent layer are ignored. */

@@ -81,6 +81,10 @@ struct Block {
   void* Vc = nullptr;
   void* Kcl = nullptr;
   void* Vcl = nullptr;
+  void* Ke = nullptr;       // the same for a passage being scored (single stream) [cr x d]
+  void* Ve = nullptr;
+  void* Kel = nullptr;
+  void* Vel = nullptr;
   int acslot = 0;           // loss-compensation slots of the attention: O, n_a
 };
 
@@ -96,7 +100,8 @@ struct ttt_ctx {
   int nb = 1, R = 0, Rp = 0;
   int ms = 0;          // hidden size of the static MLP of every block (0: none)
   int window = 0;      // keys per query of the attention of every block (0: none)
-  int cr = 0;          // ring positions per stream and block (the window)
+  int cr = 0;          // ring positions per stream and block (window + chunk)
+  bool eval_ring = false;  // the attention reads and fills the passage rings (evaluation)
   float *dOf = nullptr, *Dq = nullptr;  // attention backward scratch: dO fp32, row terms
   float *swa_part = nullptr, *swa_m = nullptr, *swa_l = nullptr;  // forward split partials
   void *dOb = nullptr, *dQKV = nullptr;
@@ -280,10 +285,11 @@ SwaShape swa_shape(ttt_ctx* c, Block& B, int64_t pos) {
   SwaShape s;
   s.qkv = B.QKV;
   s.qkv_lo = B.QKVl;
-  s.kc = B.Kc;
-  s.vc = B.Vc;
-  s.kc_lo = B.Kcl;
-  s.vc_lo = B.Vcl;
+  const bool e = c->eval_ring;
+  s.kc = e ? B.Ke : B.Kc;
+  s.vc = e ? B.Ve : B.Vc;
+  s.kc_lo = e ? B.Kel : B.Kcl;
+  s.vc_lo = e ? B.Vel : B.Vcl;
   s.cr = c->cr;
   s.b = c->b;
   s.d = c->d;
@@ -399,6 +405,12 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
       B.Vc = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
       B.Kcl = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
       B.Vcl = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
+      if (nb == 1) {  // evaluation (single-stream contexts only)
+        B.Ke = dalloc<char>(c, (int64_t)c->cr * d * es);
+        B.Ve = dalloc<char>(c, (int64_t)c->cr * d * es);
+        B.Kel = dalloc<char>(c, (int64_t)c->cr * d * es);
+        B.Vel = dalloc<char>(c, (int64_t)c->cr * d * es);
+      }
       if (res) B.ResNa = dalloc<char>(c, (int64_t)Rr * d * es);
       if (c->foc) {
         B.acslot = c->ncslot;
@@ -814,7 +826,11 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     }
     if (foc) RUN(TTT_K_CE_MERGE, run_loss_correct(st, c->cpart, c->ncslot, Rr, srl, (float)b, loss_out));
   }
-  if (!train) return;
+  if (!train) {
+    // an evaluated passage's keys and values join its own ring for its next chunk
+    for (int l = 0; l < L && c->window > 0; ++l) check(run_kv_append(st, swa_shape(c, c->blocks[l], chunk_pos)));
+    return;
+  }
 
   // the chunk's keys and values join each attention ring once nothing reads the old slots
   for (int l = 0; l < L && c->window > 0; ++l) check(run_kv_append(st, swa_shape(c, c->blocks[l], chunk_pos)));
@@ -909,10 +925,19 @@ void decode_token(ttt_ctx* c, const int32_t* tok, int32_t* am_out, float* z_out)
 // Losses of a passage q (nq + 1 ids, nq a multiple of b) at the current weights, chunk by
 // chunk, without any step; their fp64 sum lands in acc[0], and the losses / their mean in the
 // caller's buffers when given.
+//
+// With attention the passage is a sequence of its own ([SGF], Settlement: the two scores
+// leave the attention as it is): its chunks sit at positions 0, b, .. of the passage rings,
+// which start empty, and the stream's rings are neither read nor changed.
 void evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, double* acc, float* losses, float* mean) {
   const int b = c->b;
+  struct PassageRings {
+    ttt_ctx* c;
+    explicit PassageRings(ttt_ctx* x) : c(x) { c->eval_ring = c->window > 0; }
+    ~PassageRings() { c->eval_ring = false; }
+  } rings(c);
   for (int64_t i = 0; i < nq; i += b) {
-    run_chunk(c, q + i, 0, c->eval_loss, c->eval_amax, b, false, 0);
+    run_chunk(c, q + i, 0, c->eval_loss, c->eval_amax, b, false, i / b);
     check(run_eval_accum(c->st, c->eval_loss, b, acc, losses ? losses + i : nullptr, i == 0, i + b >= nq, nq,
                          mean));
   }
@@ -1073,7 +1098,7 @@ ttt_status ttt_decode(ttt_ctx* c, const int32_t* tokens, int64_t n, int32_t* arg
 int64_t ttt_decode_pending(const ttt_ctx* c) { return c ? c->npend : -1; }
 
 ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses, float* mean) {
-  if (!c || !q || nq <= 0 || nq % c->b || c->nb != 1 || c->window > 0) return TTT_EINVAL;
+  if (!c || !q || nq <= 0 || nq % c->b || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
     evaluate(c, q, nq, c->eval_acc, losses, mean);
@@ -1085,7 +1110,7 @@ ttt_status ttt_evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, float* losses,
 }
 
 ttt_status ttt_snapshot(ttt_ctx* c) {
-  if (!c || c->nb != 1 || c->window > 0) return TTT_EINVAL;
+  if (!c || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
     copy_state(c, true);
@@ -1098,7 +1123,7 @@ ttt_status ttt_snapshot(ttt_ctx* c) {
 }
 
 ttt_status ttt_restore(ttt_ctx* c) {
-  if (!c || c->nb != 1 || c->window > 0) return TTT_EINVAL;
+  if (!c || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK || !c->has_snap) return TTT_ESTATE;
   try {
     copy_state(c, false);
@@ -1111,7 +1136,7 @@ ttt_status ttt_restore(ttt_ctx* c) {
 
 ttt_status ttt_settle_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
                             int32_t* committed) {
-  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0 || c->nb != 1 || c->window > 0) return TTT_EINVAL;
+  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0 || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + c->b > c->cfg.max_tokens) return TTT_EINVAL;
   try {

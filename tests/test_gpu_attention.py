@@ -8,8 +8,10 @@ inner loop backpropagates through the current chunk's queries, keys and values i
 blocks below. Checks: windows shorter than, equal to and longer than the chunk and than the
 whole stream, one and two heads, with and without the static MLP, several prefill calls,
 batched streams, the fuller-block 760M shape (sampled), decoding (each decoded row's key and
-value join the ring at once; a filled chunk's step reads the window in front of it), and the
-calls an attention context refuses. Gates are those of tests/_parity.py (bf16).
+value join the ring at once; a filled chunk's step reads the window in front of it),
+passage scoring and Settlement (the passage is a sequence of its own, scored over rings of
+its own; the stream's rings are left as they are), and the calls an attention context
+refuses. Gates are those of tests/_parity.py (bf16).
 """
 import numpy as np
 import pytest
@@ -66,21 +68,21 @@ def test_e2e760m_attention_sampled(ttt_lib):
     compare(g, oracle_run(w, P, x, 2), w, "bf16", 2, label="e2e760m-attn")
 
 
-def test_attention_context_refuses_single_row_calls(ttt_lib):
+def test_batched_attention_context_refuses_single_stream_calls(ttt_lib):
     import ctypes
     import torch
     import test_long_context_chunk_amd as ttt
     w = W.preset("e2e760m", **dict(BASE, swa_window=64, static_hidden=0, n_blocks=1))
     P = W.init_weights(w, 0)
-    ctx = ttt.TTT.from_workload(w, device_weights(P, "bf16"), max_tokens=128)
+    ctx = ttt.TTT.from_workload(w, device_weights(P, "bf16"), max_tokens=128, streams=2)
     lib, c = ctx._lib, ctx._ctx
     tok = torch.zeros(130, dtype=torch.int32, device="cuda")
     p = ctypes.c_void_p(tok.data_ptr())
+    assert lib.ttt_decode(c, p, 1, None, None) == -1
     assert lib.ttt_evaluate(c, p, 64, None, None) == -1
     assert lib.ttt_snapshot(c) == -1
     assert lib.ttt_settle_chunk(c, p, p, 64, None, None) == -1
-    ctx.prefill(tok[:65])
-    assert ctx.sync() == 0 and ctx.consumed() == 64
+    assert ctx.consumed() == 0 and ctx.sync() == 0
     ctx.close()
 
 
@@ -176,3 +178,103 @@ def test_e2e760m_attention_decode_sampled(ttt_lib):
     dz = float(np.max(np.abs(z - zo)))
     log(f"[attention decode e2e760m] logits {dz:.3g}")
     assert dz <= TOL["bf16"]["logit"]
+
+
+SETTLE = dict(BASE, swa_window=96, static_hidden=128)
+
+
+def test_attention_evaluate_scores_the_passage_alone(ttt_lib):
+    """A three-chunk passage (its rings wrap) scored after one prefilled chunk: per-token
+    losses and their mean against the oracle's passage scoring at the stepped weights; then the
+    stream goes on exactly as if nothing had been scored (losses and updates bitwise)."""
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m", **SETTLE)
+    P = W.init_weights(w, 21)
+    x = W.token_stream(w, 22)
+    q = W.token_stream(w, 23)[:3 * w.chunk + 1]
+    b = w.chunk
+    dev = device_weights(P, "bf16")
+    a = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
+    a.prefill(_tok(x[:b + 1]))
+    losses, mean = a.evaluate(_tok(q))
+    losses = losses.cpu().numpy().astype(np.float64)
+    mean = float(mean.cpu().numpy()[0])
+    a.prefill(_tok(x[b:2 * b + 1]))
+    c = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
+    c.prefill(_tok(x[:2 * b + 1]))
+    assert np.array_equal(a.token_losses().cpu().numpy(), c.token_losses().cpu().numpy())
+    for l in range(w.n_blocks):
+        for k in w.fast_names():
+            assert np.array_equal(a.fast_weight(l, k, "delta").cpu().numpy(),
+                                  c.fast_weight(l, k, "delta").cpu().numpy()), (k, l)
+    assert a.sync() == 0 and c.sync() == 0
+    a.close()
+    c.close()
+    model = O.Model.from_workload(w)
+    one = O.run_ttt(model, P, x[:b + 1])
+    W1 = {**O.as_f64(P), **one.weights}
+    lo, _, _ = O.token_losses(model, W1, q[:-1], q[1:])
+    dl = float(np.max(np.abs(losses - lo)))
+    dm = abs(mean - O.passage_loss(model, W1, q))
+    log(f"[attention evaluate] losses {dl:.3g} mean {dm:.3g}")
+    assert dl <= TOL["bf16"]["loss"] and dm <= TOL["bf16"]["loss"]
+
+
+@pytest.mark.parametrize("lr,expect", [(1.0, 1), (20.0, 0)])
+def test_attention_settlement_matches_oracle(ttt_lib, lr, expect):
+    """One prefilled chunk, then a candidate chunk under the Settlement rule with the passage
+    = its own text (kept at a moderate rate, rejected at an overshooting one), then one more
+    prefilled chunk. A twin context prefills the candidate instead, which gives the GPU's own
+    W and W + delta (the candidate's step is the prefill step, bit for bit). Checks: the
+    oracle's settle_step from the stream's cache takes the same decision; A equals the
+    oracle's L(q, W) - L(q, W + delta) at the GPU's two weight sets within the A gate of
+    tests/test_gpu_settle.py (the step's own error is left to the update gate: at an
+    overshooting rate A magnifies it); the state after the decision is the twin's W + delta
+    or W bit for bit; and the next chunk's losses (which read the candidate's keys either way)
+    match the oracle's."""
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m", **dict(SETTLE, lr=lr))
+    P = W.init_weights(w, 21)
+    x = W.token_stream(w, 22)
+    b = w.chunk
+    dev = device_weights(P, "bf16")
+
+    def state(ctx, kind):
+        return {f"{k}.{l}": ctx.fast_weight(l, k, kind).cpu().numpy().astype(np.float64)
+                for l in range(w.n_blocks) for k in w.fast_names()}
+    twin = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens, lr=lr)
+    twin.prefill(_tok(x[:b + 1]))
+    W1g, D1g = state(twin, "W"), state(twin, "delta")
+    twin.prefill(_tok(x[b:2 * b + 1]))
+    W2g, D2g = state(twin, "W"), state(twin, "delta")
+    assert twin.sync() == 0
+    twin.close()
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens, lr=lr)
+    ctx.prefill(_tok(x[:b + 1]))
+    cand = x[b:2 * b + 1]
+    A, kept = ctx.settle(_tok(cand), _tok(cand))
+    A, kept = float(A.cpu().numpy()[0]), int(kept.cpu().numpy()[0])
+    Dg = state(ctx, "delta")
+    ctx.prefill(_tok(x[2 * b:3 * b + 1]))
+    nxt = ctx.token_losses(2 * b, b).cpu().numpy().astype(np.float64)
+    assert ctx.consumed() == 3 * b and ctx.sync() == 0
+    ctx.close()
+    model = O.Model.from_workload(w, lr=lr)
+    Pf = O.as_f64(P)
+    one = O.run_ttt(model, P, x[:b + 1])
+    W1 = {**Pf, **one.weights}
+    A_o, keep_o, Wn, _, _ = O.settle_step(model, W1, cand, cand, kv=one.kv)
+    assert int(keep_o) == expect
+    A_g = O.passage_loss(model, {**Pf, **W1g}, cand) - O.passage_loss(model, {**Pf, **W2g}, cand)
+    kv = O.chunk_loss_and_grads(model, W1, cand[:-1], cand[1:], kv=one.kv)[1]["kv"]
+    lo, _, _ = O.token_losses(model, {**W1, **Wn}, x[2 * b:3 * b], x[2 * b + 1:3 * b + 1], kv=kv)
+    tol = 2e-4 + 1e-3 * abs(A_g)
+    dl = float(np.max(np.abs(nxt - lo)))
+    log(f"[attention settle lr={lr}] A {A:.6g} vs {A_g:.6g} at the GPU's weights ({A_o:.6g} oracle's) "
+        f"kept {kept} next-chunk losses {dl:.3g}")
+    assert abs(A - A_g) <= tol and abs(A_g) > tol
+    assert kept == expect
+    after = D2g if kept else D1g
+    for k in Dg:
+        assert np.array_equal(Dg[k], after[k]), k
+    assert dl <= TOL["bf16"]["loss"]
