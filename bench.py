@@ -146,12 +146,17 @@ def cpu_baseline(w, P, x, n_chunks: int):
 
 
 def decode_bytes_per_token(w) -> float:
-    """HBM bytes one decoded token's products read: every weight the forward reads once
-    (bf16: the fast tensors as W0 and rn(D), two segments), plus the LM head."""
+    """HBM bytes one decoded token reads: every weight the forward reads once (bf16: the fast
+    tensors as W0 and rn(D), two segments), plus the LM head; with the fuller block also the
+    static MLP, q|k|v and Wo, and the keys and values of a full window (hi and lo terms)."""
     es = 2 if w.precision == "bf16" else 4
     segs = 2 if w.precision == "bf16" else 1
     dm = w.d_model * w.d_hidden * es
     per_block = (segs * dm if w.mlp == "gelu" else 2 * dm) + segs * dm
+    ms = getattr(w, "static_hidden", 0)
+    per_block += 2 * w.d_model * ms * es
+    if getattr(w, "swa_window", 0) > 0:
+        per_block += 4 * w.d_model * w.d_model * es + 4 * w.swa_window * w.d_model * 2
     return float(w.n_blocks * per_block + w.vocab * w.d_model * es)
 
 
@@ -176,7 +181,9 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
     prof = ctx.profile_read()
     ctx.profile([])
     gemv_ms, gemv_n = prof.get("dec_gemv", (0.0, 0))
-    per_tok = 2 * w.n_blocks + 1  # up and down per block, then the LM head
+    # per block: up and down, the static MLP's two, q|k|v and Wo; then the LM head
+    per_block = 2 + (2 if getattr(w, "static_hidden", 0) > 0 else 0) + (2 if getattr(w, "swa_window", 0) > 0 else 0)
+    per_tok = per_block * w.n_blocks + 1
     traced_tokens = max(gemv_n // per_tok, 1)
     bpt = decode_bytes_per_token(w)
     gemv_s_per_tok = gemv_ms * 1e-3 / traced_tokens
@@ -184,10 +191,12 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
     # dispatch time: the roofline uses the whole token's time instead (a lower bound on the
     # kernels' bandwidth), and the bracketed figure is reported beside it
     achieved = bpt / (dt / b) / 1e9
+    att = getattr(w, "swa_window", 0) > 0
     out = {
         "metric": "decode tokens/s (one prediction per token, the TTT step every chunk)",
         "value": b / dt, "unit": "tokens/s", "us_per_token": dt / b * 1e6, "tokens": b,
-        "roofline": {"bound": "hbm", "kernel": "decode token (one-row products + CE merge)",
+        "roofline": {"bound": "hbm", "kernel": "decode token (one-row products + CE merge" +
+                     (" + attention over a full window)" if att else ")"),
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": None, "bytes_per_token": bpt,
                      "gemv_event_us_per_token": gemv_s_per_tok * 1e6, "gemv_launches_traced": gemv_n,
@@ -342,7 +351,7 @@ def e2e_flops_per_step(w) -> dict:
     return dict(total=alg_flops_per_token(w) * T + proj + core_fwd + core_bwd + static, attn_fwd=core_fwd)
 
 
-def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2) -> dict:
+def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2, decode: bool = True) -> dict:
     """The fuller TTT-E2E block at the 760M shape: frozen sliding-window attention (window 8K,
     12 heads) and a frozen static MLP before each of the 3 fast MLPs; one stream, whole-stream
     steps. Roofline: the attention forward kernel, traced on every chunk."""
@@ -355,7 +364,7 @@ def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2
     P = W.init_weights(w, seed)
     x = W.token_stream(w, seed)
     dev = {k: ttt.to_device(v, w.precision) for k, v in P.items()}
-    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * (warmup + steps + 1))
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * (warmup + steps + 1) + 2 * w.chunk)
     del dev
     tok = torch.from_numpy(x.astype(np.int32)).cuda()
     torch.cuda.synchronize()
@@ -379,6 +388,7 @@ def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2
     elapsed = time.perf_counter() - t0
     aprof = ctx.profile_read()
     ctx.profile([])
+    dec = decode_bench(ctx, w, x, P, cpu=cpu) if decode else None
     status = ctx.sync()
     last = ctx.token_losses(T * (warmup + 1), 8).cpu().numpy()
     ctx.close()
@@ -409,6 +419,8 @@ def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2
                     "are 3x the algorithmic ones",
         },
     }
+    if dec is not None:
+        out["decode"] = dec
     if cpu:
         import oracle as O
         eprint(f"[bench] timing the fp64 oracle on {cpu_chunks} chunks of e2e760m ...")
