@@ -642,9 +642,12 @@ __global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv
 // One decoded row (position p, its q | k | v in fp32, qkv [3d]): its key and value join the
 // ring first (hi + lo bf16 terms, as the chunk path stores them), then the attention reads
 // keys max(0, p - window + 1) .. p of the ring in fp32 (hi + lo). Work: grid (H, nsplit), each
-// workgroup a contiguous share of the keys in blocks of 256, online softmax over the blocks;
-// k_swa_dec_merge combines the shares per head.
-constexpr int DEC_KB = 256;  // keys per block of the decode kernel
+// workgroup a contiguous share of the keys in blocks of 64, online softmax over the blocks.
+// Per block, four lanes score a key (32 dims each, 16-byte loads, two shuffles), one wave
+// turns the 64 scores into probabilities, and each lane accumulates 8 dims of o over a
+// sixteenth of the keys (16-byte loads of consecutive dims); the sixteenths are summed in
+// LDS at the end. k_swa_dec_merge combines the shares per head.
+constexpr int DEC_KB = 64;  // keys per block of the decode kernel
 
 __global__ void __launch_bounds__(NT_A) k_swa_dec_append(const float* __restrict__ qkv, int d, int64_t p, int cr,
                                                          bf16_t* __restrict__ kc, bf16_t* __restrict__ kc_lo,
@@ -664,73 +667,111 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
                                                   const bf16_t* __restrict__ kc_lo, const bf16_t* __restrict__ vc,
                                                   const bf16_t* __restrict__ vc_lo, int d, int64_t p, int cr,
                                                   int window, float* __restrict__ part) {
-  __shared__ float sq[DH];
-  __shared__ float sp[DEC_KB];
-  __shared__ float red[8];
-  __shared__ float so[DH];
+  __shared__ float sp[DEC_KB];      // the block's probabilities
+  __shared__ float sacc[16][DH];    // per key subset, the partial o
+  __shared__ float sml[2];          // the block's (max, sum)
   const int h = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
   const int t = threadIdx.x;
-  if (t < DH) sq[t] = qkv[h * DH + t] * 0.08838834764831845f;  // q / sqrt(128)
+  // scores: four lanes per key, 32 dims each (hi + lo terms, 16-byte loads)
+  const int kj = t >> 2, kq = (t & 3) * 32;
+  float q[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) q[i] = qkv[h * DH + kq + i] * 0.08838834764831845f;  // q / sqrt(128)
+  // values: lane group g of 8 dims, key subset ks (keys ks, ks + 16, ..)
+  const int g = (t & 15) * 8, ks = t >> 4;
   int64_t k0 = p - window + 1;
   if (k0 < 0) k0 = 0;
   const int64_t nk = p - k0 + 1;
   const int64_t nblk = (nk + DEC_KB - 1) / DEC_KB;
   const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
-  float m = -INFINITY, l = 0.f, acc = 0.f;  // acc: dim t % 128, keys of half t / 128
-  const int dim = t & (DH - 1), half = t >> 7;
-  __syncthreads();
+  float m = -INFINITY, l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // a block's operands, requested one block ahead: this lane's key (32 dims, hi and lo) and
+  // its four value rows (8 dims, hi and lo); ring slots are in range for any position, and
+  // keys past p are neither scored nor accumulated
+  struct Ops {
+    uint4 kh[4], kl[4], vh[4], vl[4];
+  };
+  auto load = [&](Ops& o, int64_t kb) {
+    const int64_t rk = ((kb + kj) % cr) * d + h * DH + kq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      o.kh[c] = *(const uint4*)(kc + rk + 8 * c);
+      o.kl[c] = *(const uint4*)(kc_lo + rk + 8 * c);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int64_t rv = ((kb + ks + 16 * jj) % cr) * d + h * DH + g;
+      o.vh[jj] = *(const uint4*)(vc + rv);
+      o.vl[jj] = *(const uint4*)(vc_lo + rv);
+    }
+  };
+  Ops cur, nxt;
+  if (b0 < b1) load(cur, k0 + b0 * DEC_KB);
   for (int64_t blk = b0; blk < b1; ++blk) {
     const int64_t kb = k0 + blk * DEC_KB;
-    const int64_t kp = kb + t;
-    // score of key kp (one key per thread)
-    float s = -INFINITY;
-    if (kp <= p) {
-      const int64_t r = (kp % cr) * d + h * DH;
+    if (blk + 1 < b1) load(nxt, kb + DEC_KB);
+    {
+      const int64_t kp = kb + kj;
       float a = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < DH; c += 8) {
-        const uint4 u = *(const uint4*)(kc + r + c), w = *(const uint4*)(kc_lo + r + c);
-        const bf16_t* e = (const bf16_t*)&u;
-        const bf16_t* f = (const bf16_t*)&w;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a = fmaf(bf2f(e[q]) + bf2f(f[q]), sq[c + q], a);
+      for (int c = 0; c < 4; ++c) {
+        const bf16_t* e = (const bf16_t*)&cur.kh[c];
+        const bf16_t* f = (const bf16_t*)&cur.kl[c];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) a = fmaf(bf2f(e[x]) + bf2f(f[x]), q[8 * c + x], a);
       }
-      s = a * LOG2E;
+      a += __shfl_xor(a, 1, TTT_WAVE);
+      a += __shfl_xor(a, 2, TTT_WAVE);
+      if ((t & 3) == 0) sp[kj] = kp <= p ? a * LOG2E : -INFINITY;
     }
-    // block max and the rescale of the running state
-    float bm = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off, TTT_WAVE));
-    if ((t & 63) == 0) red[t >> 6] = bm;
     __syncthreads();
-    bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float mn = fmaxf(m, bm);
+    if (t < 64) {  // the block's max, probabilities and sum (one wave)
+      const float sv = sp[t];
+      float bm = sv;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off, TTT_WAVE));
+      const float mn = fmaxf(m, bm);
+      const float pk = sv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv - mn);
+      sp[t] = pk;
+      float ps = pk;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) ps += __shfl_xor(ps, off, TTT_WAVE);
+      if (t == 0) {
+        sml[0] = mn;
+        sml[1] = ps;
+      }
+    }
+    __syncthreads();
+    const float mn = sml[0];
     const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-    const float pk = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mn);
-    sp[t] = pk;
-    float ps = pk;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) ps += __shfl_xor(ps, off, TTT_WAVE);
-    __syncthreads();  // sp complete; red free again
-    if ((t & 63) == 0) red[4 + (t >> 6)] = ps;
-    __syncthreads();
-    l = l * alpha + ((red[4] + red[5]) + (red[6] + red[7]));
+    l = l * alpha + sml[1];
     m = mn;
-    // this thread's dim over its half of the block's keys
-    acc *= alpha;
-    for (int j = half * (DEC_KB / 2); j < (half + 1) * (DEC_KB / 2); ++j) {
-      const int64_t kq = kb + j;
-      if (kq > p) break;
-      const int64_t r = (kq % cr) * d + h * DH + dim;
-      acc = fmaf(sp[j], bf2f(vc[r]) + bf2f(vc_lo[r]), acc);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = ks + 16 * jj;
+      if (kb + j > p) break;
+      const bf16_t* e = (const bf16_t*)&cur.vh[jj];
+      const bf16_t* f = (const bf16_t*)&cur.vl[jj];
+      const float pj = sp[j];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] = fmaf(pj, bf2f(e[x]) + bf2f(f[x]), acc[x]);
     }
-    __syncthreads();  // sp and red are rewritten by the next block
+    __syncthreads();  // sp and sml are rewritten by the next block
+    cur = nxt;
   }
-  // the two halves' sums per dim, then this share's (max, sum, o[128])
-  if (half == 1) so[dim] = acc;
+  // the 16 key subsets' sums per dim, then this share's (max, sum, o[128])
+#pragma unroll
+  for (int x = 0; x < 8; ++x) sacc[ks][g + x] = acc[x];
   __syncthreads();
   float* P = part + ((int64_t)h * nsplit + split) * (DH + 2);
-  if (half == 0) P[dim] = acc + so[dim];
+  if (t < DH) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o += sacc[k][t];
+    P[t] = o;
+  }
   if (t == 0) {
     P[DH] = m;
     P[DH + 1] = l;
@@ -819,8 +860,10 @@ hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, cons
 }
 
 int swa_dec_splits(int window) {
+  // about two blocks of keys per workgroup, at most 64 workgroups per head
   const int blocks = (window + DEC_KB - 1) / DEC_KB;
-  return blocks < 16 ? (blocks < 1 ? 1 : blocks) : 16;
+  const int n = (blocks + 1) / 2;
+  return n < 1 ? 1 : (n > 64 ? 64 : n);
 }
 
 hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o) {
