@@ -778,20 +778,33 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
   }
 }
 
-// o [d] = per head, the shares' states combined: grid (H), 128 threads.
+// o [d] = per head, the shares' states combined: grid (H), 128 threads. The shares' maxima
+// and sums go through LDS first (one wave reduces them), so the per-dim sums then issue all
+// their loads independently.
+constexpr int DEC_SPLIT_MAX = 64;
 __global__ void __launch_bounds__(DH) k_swa_dec_merge(const float* __restrict__ part, int nsplit,
                                                       float* __restrict__ o) {
+  __shared__ float wts[DEC_SPLIT_MAX];
+  __shared__ float sL;
   const int h = blockIdx.x, t = threadIdx.x;
   const float* P = part + (int64_t)h * nsplit * (DH + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P[s * (DH + 2) + DH]);
-  float L = 0.f, a = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = P[s * (DH + 2) + DH];
+  if (t < 64) {
+    const float ms = t < nsplit ? P[t * (DH + 2) + DH] : -INFINITY;
+    float M = ms;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, TTT_WAVE));
     const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L += w * P[s * (DH + 2) + DH + 1];
-    a += w * P[s * (DH + 2) + t];
+    float L = t < nsplit ? w * P[t * (DH + 2) + DH + 1] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off, TTT_WAVE);
+    wts[t] = w;
+    if (t == 0) sL = L;
   }
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) a += wts[s] * P[s * (DH + 2) + t];
+  const float L = sL;
   o[h * DH + t] = L > 0.f ? a / L : 0.f;
 }
 
@@ -863,7 +876,7 @@ int swa_dec_splits(int window) {
   // about two blocks of keys per workgroup, at most 64 workgroups per head
   const int blocks = (window + DEC_KB - 1) / DEC_KB;
   const int n = (blocks + 1) / 2;
-  return n < 1 ? 1 : (n > 64 ? 64 : n);
+  return n < 1 ? 1 : (n > DEC_SPLIT_MAX ? DEC_SPLIT_MAX : n);
 }
 
 hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o) {
