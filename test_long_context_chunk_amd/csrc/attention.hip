@@ -17,6 +17,7 @@ namespace {
 
 constexpr int DH = 128;      // head size
 constexpr int BLK = 64;      // queries or keys per workgroup and per staged block
+constexpr int SPLIT_CAP = 16;  // most workgroups one query block's key range is divided among
 constexpr int NT_A = 256;    // 4 waves x 16 rows
 constexpr int LDR = DH + 8;  // row stride (elements) of a [row][dim] tile: 272 B
 constexpr int LDT = BLK + 8; // row stride of a [dim][row] tile: 144 B (conflict-free pair stores)
@@ -832,13 +833,22 @@ bool shape_ok(const SwaShape& s) {
 }  // namespace
 
 int swa_fwd_splits(const SwaShape& s) {
-  // enough workgroups for two per CU on 256 CUs, whole key blocks per split, at most 4
+  // Two workgroups fit a CU (512 slots on 256 CUs) and they take about equal time, so a
+  // launch costs about ceil(wg n / 512) rounds of 1/n of the key range: the split count n
+  // (at most 16, whole key blocks per split) minimising rounds / n, the smallest on ties.
+  // At 192 query blocks (a 1024-token chunk of 12 heads) that is 8: three full rounds.
   const int64_t wg = (int64_t)((s.b + BLK - 1) / BLK) * (s.d / DH) * s.streams;
   const int64_t kblocks = ((int64_t)(s.window < s.b ? s.b : s.window) + BLK - 1) / BLK;
-  int n = (int)((512 + wg - 1) / wg);
-  if (n > 4) n = 4;
-  if (n > kblocks) n = (int)kblocks;
-  return n < 1 ? 1 : n;
+  int best = 1;
+  double cost = 1e30;
+  for (int n = 1; n <= SPLIT_CAP && n <= kblocks; ++n) {
+    const double c = (double)((wg * n + 511) / 512) / n;
+    if (c < cost - 1e-12) {
+      cost = c;
+      best = n;
+    }
+  }
+  return best;
 }
 
 hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
