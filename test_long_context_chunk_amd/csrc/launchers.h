@@ -122,7 +122,7 @@ hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, cons
 // d / 128 * swa_dec_splits(window) * 130 floats.
 int swa_dec_splits(int window);
 hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o);
-// The chunk's last min(b, cr) keys and values into the ring.
+// The chunk's keys and values (its last min(b, cr), cr being at least b) into the ring.
 hipError_t run_kv_append(hipStream_t st, const SwaShape& s);
 
 // ---- GEMMs, C = X Y^T with X [M x K], Y [N x K] (gemm_inst.hip)
