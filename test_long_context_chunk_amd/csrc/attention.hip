@@ -158,39 +158,48 @@ struct SwaSplit {
   float* pl;    // [n][streams][H][b] sum of 2^(s - max)
 };
 
-__global__ void __launch_bounds__(NT_A, 2) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
-                                                  bf16_t* __restrict__ Ob, bf16_t* __restrict__ Ol,
-                                                  float* __restrict__ lse2) {
+// QG query groups of 16 per wave (a workgroup covers 64 QG queries): every K and V operand
+// read from LDS feeds QG products, so a larger QG moves fewer tile bytes per query.
+template <int QG>
+__global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
+                                                                   bf16_t* __restrict__ Ob, bf16_t* __restrict__ Ol,
+                                                                   float* __restrict__ lse2) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
   __shared__ __attribute__((aligned(16))) bf16_t sKl[BLK * LDR];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[DH * LDT];
   __shared__ __attribute__((aligned(16))) bf16_t sVtl[DH * LDT];
+  constexpr int QB = BLK * QG;  // queries per workgroup
   const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int split = blockIdx.x % sp.n;
-  const int q0 = (blockIdx.x / sp.n) * BLK;
-  const int q = q0 + wave * 16 + lr;  // this lane's query (chunk row)
-  const bool qok = q < g.b;
-  const int64_t qp = g.pos + q;
+  const int q0 = (blockIdx.x / sp.n) * QB;
   const float sc = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
-  // this lane's query as B-operand chunks (dims 32 s + 8 lg ..)
-  uint4 qf[4], qfl[4];
-  {
-    const int64_t o = ((int64_t)z * g.b + (qok ? q : 0)) * (3 * (int64_t)g.d) + h * DH;
+  // this lane's queries (chunk rows q0 + 16 (QG wave + gq) + lr) as B-operand chunks (dims
+  // 32 s + 8 lg ..), and their running O, max and sum
+  int q[QG];
+  bool qok[QG];
+  uint4 qf[QG][4], qfl[QG][4];
+  f32x4_t ot[QG][8];
+  float m[QG], lsum[QG];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    q[gq] = q0 + 16 * (QG * wave + gq) + lr;
+    qok[gq] = q[gq] < g.b;
+    const int64_t o = ((int64_t)z * g.b + (qok[gq] ? q[gq] : 0)) * (3 * (int64_t)g.d) + h * DH;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      qf[s] = qok ? *(const uint4*)(g.qkv + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
-      qfl[s] = qok ? *(const uint4*)(g.qkv_lo + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      qf[gq][s] = qok[gq] ? *(const uint4*)(g.qkv + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      qfl[gq][s] = qok[gq] ? *(const uint4*)(g.qkv_lo + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
     }
-  }
-  f32x4_t ot[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) ot[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+    for (int c = 0; c < 8; ++c) ot[gq][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[gq] = -INFINITY;
+    lsum[gq] = 0.f;
+  }
 
-  const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + BLK, g.b) - 1;
+  const int64_t qlo = g.pos + q0, qhi = g.pos + min(q0 + QB, g.b) - 1;
   int64_t klo = qlo - g.window + 1;
   if (klo < 0) klo = 0;
   // this workgroup's share of the key blocks [klo, qhi]
@@ -205,8 +214,8 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_fwd(SwaGeo g, SwaSplit sp, floa
   const KvBase kvb[4] = {kv_base(g, z, h, 1, false), kv_base(g, z, h, 1, true), kv_base(g, z, h, 2, false),
                          kv_base(g, z, h, 2, true)};
   auto fetch_block = [&](int64_t kb) { fetch_rows<4>(cb, kvb, g, key_src(g, kb, qhi)); };
-  // the wave's first query position (its 16 queries follow)
-  const int64_t qw0 = g.pos + q0 + wave * 16;
+  // the wave's first query position (its 16 QG queries follow)
+  const int64_t qw0 = g.pos + q0 + 16 * QG * wave;
   if (klo <= kend) fetch_block(klo);
   for (int64_t kb = klo; kb <= kend; kb += BLK) {
     __syncthreads();  // the previous block's tiles are no longer read
@@ -217,113 +226,136 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_fwd(SwaGeo g, SwaSplit sp, floa
     __syncthreads();
     if (kb + BLK <= kend) fetch_block(kb + BLK);  // in flight during this block's MFMAs
 
-    // S^T = K Q^T: st[j][e] = s(key kb + 16 j + 4 lg + e, query q)
-    f32x4_t st[4];
+    // S^T = K Q^T: st[gq][j][e] = s(key kb + 16 j + 4 lg + e, query q[gq])
+    f32x4_t st[QG][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      st[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) st[gq][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint4 a = *(const uint4*)(sK + (16 * j + lr) * LDR + 32 * s + 8 * lg);
         const uint4 al = *(const uint4*)(sKl + (16 * j + lr) * LDR + 32 * s + 8 * lg);
-        mfma_chunk(st[j], a, qf[s], bf16_t());
-        mfma_chunk(st[j], al, qf[s], bf16_t());
-        mfma_chunk(st[j], a, qfl[s], bf16_t());
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+          mfma_chunk(st[gq][j], a, qf[gq][s], bf16_t());
+          mfma_chunk(st[gq][j], al, qf[gq][s], bf16_t());
+          mfma_chunk(st[gq][j], a, qfl[gq][s], bf16_t());
+        }
       }
     }
     // mask (distance query - key in [0, window), 32-bit) and block max (scaled units); a
     // block that every query of the wave sees whole needs no mask
-    float bm = -INFINITY;
-    if (qw0 - (kb + BLK - 1) >= 0 && qw0 + 15 - kb < g.window) {
+    const bool whole = qw0 - (kb + BLK - 1) >= 0 && qw0 + 16 * QG - 1 - kb < g.window;
+    uint4 pb[QG][2], pl[QG][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int gq = 0; gq < QG; ++gq) {
+      float bm = -INFINITY;
+      if (whole) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          st[j][e] *= sc;
-          bm = fmaxf(bm, st[j][e]);
-        }
-    } else {
-      const int dq0 = qok ? (int)(qp - kb) - 4 * lg : -(1 << 30);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+          for (int e = 0; e < 4; ++e) {
+            st[gq][j][e] *= sc;
+            bm = fmaxf(bm, st[gq][j][e]);
+          }
+      } else {
+        const int dq0 = qok[gq] ? (int)(g.pos + q[gq] - kb) - 4 * lg : -(1 << 30);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dist = dq0 - 16 * j - e;
-          const bool ok = dist >= 0 && dist < g.window;
-          st[j][e] = ok ? st[j][e] * sc : -INFINITY;
-          bm = fmaxf(bm, st[j][e]);
-        }
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, TTT_WAVE));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, TTT_WAVE));
-    // online softmax; a query with no visible key yet keeps m = -inf and adds zeros (no
-    // branch: the MFMAs below run for the whole wave)
-    const float mn = fmaxf(m, bm);
-    const float alpha = (m == -INFINITY || mn == -INFINITY) ? (m == mn ? 1.f : 0.f) : __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
-    lsum *= alpha;
-    if (__any(alpha != 1.f)) {  // once the maxima settle, most blocks leave O as it is
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) ot[c] *= alpha;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = st[j][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[j][e] - mn);
-        st[j][e] = p;
-        lsum += p;
+          for (int e = 0; e < 4; ++e) {
+            const int dist = dq0 - 16 * j - e;
+            const bool ok = dist >= 0 && dist < g.window;
+            st[gq][j][e] = ok ? st[gq][j][e] * sc : -INFINITY;
+            bm = fmaxf(bm, st[gq][j][e]);
+          }
       }
-    // O^T += V^T P^T: ot[c][e] = o(dim 16 c + 4 lg + e, query q), p as hi + lo
+      bm = fmaxf(bm, __shfl_xor(bm, 16, TTT_WAVE));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, TTT_WAVE));
+      // online softmax; a query with no visible key yet keeps m = -inf and adds zeros (no
+      // branch: the MFMAs below run for the whole wave)
+      const float mn = fmaxf(m[gq], bm);
+      const float alpha =
+          (m[gq] == -INFINITY || mn == -INFINITY) ? (m[gq] == mn ? 1.f : 0.f) : __builtin_amdgcn_exp2f(m[gq] - mn);
+      m[gq] = mn;
+      lsum[gq] *= alpha;
+      if (__any(alpha != 1.f)) {  // once the maxima settle, most blocks leave O as it is
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ot[gq][c] *= alpha;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = st[gq][j][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[gq][j][e] - mn);
+          st[gq][j][e] = p;
+          lsum[gq] += p;
+        }
+      // p as hi + lo B operands, in the k-slot order of tchunk
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4_t r0, r1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r0[e] = st[gq][2 * t][e] - bf2f(f2bf(st[gq][2 * t][e]));
+          r1[e] = st[gq][2 * t + 1][e] - bf2f(f2bf(st[gq][2 * t + 1][e]));
+        }
+        pb[gq][t] = pchunk(st[gq][2 * t], st[gq][2 * t + 1]);
+        pl[gq][t] = pchunk(r0, r1);
+      }
+    }
+    // O^T += V^T P^T: ot[gq][c][e] = o(dim 16 c + 4 lg + e, query q[gq])
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f32x4_t r0, r1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r0[e] = st[2 * t][e] - bf2f(f2bf(st[2 * t][e]));
-        r1[e] = st[2 * t + 1][e] - bf2f(f2bf(st[2 * t + 1][e]));
-      }
-      const uint4 pb = pchunk(st[2 * t], st[2 * t + 1]);
-      const uint4 pl = pchunk(r0, r1);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const uint4 vh = tchunk(sVt, 16 * c + lr, t, lg);
-        mfma_chunk(ot[c], vh, pb, bf16_t());
-        mfma_chunk(ot[c], tchunk(sVtl, 16 * c + lr, t, lg), pb, bf16_t());
-        mfma_chunk(ot[c], vh, pl, bf16_t());
+        const uint4 vl = tchunk(sVtl, 16 * c + lr, t, lg);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+          mfma_chunk(ot[gq][c], vh, pb[gq][t], bf16_t());
+          mfma_chunk(ot[gq][c], vl, pb[gq][t], bf16_t());
+          mfma_chunk(ot[gq][c], vh, pl[gq][t], bf16_t());
+        }
       }
     }
   }
-  lsum += __shfl_xor(lsum, 16, TTT_WAVE);
-  lsum += __shfl_xor(lsum, 32, TTT_WAVE);
-  if (!qok) return;
-  const int64_t row = (int64_t)z * g.b + q;
-  if (sp.n > 1) {
-    // partial state: O unnormalised, its max and sum
-    float* P = sp.part + (int64_t)split * ((int64_t)gridDim.z * g.b) * g.d;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      *(float4*)(P + row * g.d + h * DH + 16 * c + 4 * lg) = make_float4(ot[c][0], ot[c][1], ot[c][2], ot[c][3]);
-    if (lg == 0) {
-      const int64_t o = ((int64_t)split * gridDim.z * H + (int64_t)z * H + h) * g.b + q;
-      sp.pm[o] = m;
-      sp.pl[o] = lsum;
+  for (int gq = 0; gq < QG; ++gq) {
+    float ls = lsum[gq];
+    ls += __shfl_xor(ls, 16, TTT_WAVE);
+    ls += __shfl_xor(ls, 32, TTT_WAVE);
+    if (!qok[gq]) continue;
+    const int64_t row = (int64_t)z * g.b + q[gq];
+    if (sp.n > 1) {
+      // partial state: O unnormalised, its max and sum
+      float* P = sp.part + (int64_t)split * ((int64_t)gridDim.z * g.b) * g.d;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *(float4*)(P + row * g.d + h * DH + 16 * c + 4 * lg) =
+            make_float4(ot[gq][c][0], ot[gq][c][1], ot[gq][c][2], ot[gq][c][3]);
+      if (lg == 0) {
+        const int64_t o = ((int64_t)split * gridDim.z * H + (int64_t)z * H + h) * g.b + q[gq];
+        sp.pm[o] = m[gq];
+        sp.pl[o] = ls;
+      }
+      continue;
     }
-    return;
-  }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int col = h * DH + 16 * c + 4 * lg;
-    const float4 o = make_float4(ot[c][0] * inv, ot[c][1] * inv, ot[c][2] * inv, ot[c][3] * inv);
-    *(float4*)(Of + row * g.d + col) = o;
-    const uint2 hb = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
-    *(uint2*)(Ob + row * g.d + col) = hb;
-    const bf16_t* hv = (const bf16_t*)&hb;
-    *(uint2*)(Ol + row * g.d + col) = make_uint2(pack_bf16x2(o.x - bf2f(hv[0]), o.y - bf2f(hv[1])),
-                                                 pack_bf16x2(o.z - bf2f(hv[2]), o.w - bf2f(hv[3])));
+    for (int c = 0; c < 8; ++c) {
+      const int col = h * DH + 16 * c + 4 * lg;
+      const float4 o = make_float4(ot[gq][c][0] * inv, ot[gq][c][1] * inv, ot[gq][c][2] * inv, ot[gq][c][3] * inv);
+      *(float4*)(Of + row * g.d + col) = o;
+      const uint2 hb = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+      *(uint2*)(Ob + row * g.d + col) = hb;
+      const bf16_t* hv = (const bf16_t*)&hb;
+      *(uint2*)(Ol + row * g.d + col) = make_uint2(pack_bf16x2(o.x - bf2f(hv[0]), o.y - bf2f(hv[1])),
+                                                   pack_bf16x2(o.z - bf2f(hv[2]), o.w - bf2f(hv[3])));
+    }
+    if (lg == 0) lse2[((int64_t)z * H + h) * g.b + q[gq]] = m[gq] + log2f(ls);
   }
-  if (lg == 0) lse2[((int64_t)z * H + h) * g.b + q] = m + log2f(lsum);
 }
 
 // Merge of the split partial states: grid (streams b rows, H), 64 threads x 2 dims.
@@ -832,17 +864,21 @@ bool shape_ok(const SwaShape& s) {
 
 }  // namespace
 
-int swa_fwd_splits(const SwaShape& s) {
-  // Two workgroups fit a CU (512 slots on 256 CUs) and they take about equal time, so a
-  // launch costs about ceil(wg n / 512) rounds of 1/n of the key range: the split count n
-  // (at most 16, whole key blocks per split) minimising rounds / n, the smallest on ties.
-  // At 192 query blocks (a 1024-token chunk of 12 heads) that is 8: three full rounds.
-  const int64_t wg = (int64_t)((s.b + BLK - 1) / BLK) * (s.d / DH) * s.streams;
+// Query groups of 16 per wave in the forward kernel. Two halve the tile bytes per query but
+// take about 370 registers (one workgroup per CU instead of two) and measured slower at the
+// 760M fuller block (342 against 324 us per launch).
+constexpr int FWD_QG = 1;
+
+// Workgroups of one launch take about equal time, so a launch of wg query blocks split n
+// ways costs about ceil(wg n / slots) rounds of 1/n of the key range (slots: workgroups
+// resident at once on 256 CUs): the n (at most SPLIT_CAP, whole key blocks per split)
+// minimising rounds / n, the smallest on ties.
+static int split_count(int64_t wg, const SwaShape& s, int slots) {
   const int64_t kblocks = ((int64_t)(s.window < s.b ? s.b : s.window) + BLK - 1) / BLK;
   int best = 1;
   double cost = 1e30;
   for (int n = 1; n <= SPLIT_CAP && n <= kblocks; ++n) {
-    const double c = (double)((wg * n + 511) / 512) / n;
+    const double c = (double)((wg * n + slots - 1) / slots) / n;
     if (c < cost - 1e-12) {
       cost = c;
       best = n;
@@ -851,14 +887,28 @@ int swa_fwd_splits(const SwaShape& s) {
   return best;
 }
 
+int swa_fwd_splits(const SwaShape& s) {
+  // 64 FWD_QG queries per workgroup; one workgroup per CU at two query groups a wave (its
+  // registers), two at one
+  const int qb = BLK * FWD_QG;
+  const int64_t wg = (int64_t)((s.b + qb - 1) / qb) * (s.d / DH) * s.streams;
+  return split_count(wg, s, FWD_QG == 1 ? 512 : 256);
+}
+
+int swa_dq_splits(const SwaShape& s) {
+  // 64 queries per workgroup, two workgroups per CU; at a 1024-token chunk of 12 heads, 8
+  const int64_t wg = (int64_t)((s.b + BLK - 1) / BLK) * (s.d / DH) * s.streams;
+  return split_count(wg, s, 512);
+}
+
 hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
                        float* pm, float* pl) {
   if (!shape_ok(s) || !Ol) return hipErrorInvalidValue;
   SwaSplit sp{swa_fwd_splits(s), part, pm, pl};
   if (sp.n > 1 && (!part || !pm || !pl)) return hipErrorInvalidValue;
-  const int H = s.d / DH;
-  dim3 grid((s.b + BLK - 1) / BLK * sp.n, H, s.streams);
-  hipLaunchKernelGGL(k_swa_fwd, grid, dim3(NT_A), 0, st, geo(s), sp, Of, (bf16_t*)Ob, (bf16_t*)Ol, lse2);
+  const int H = s.d / DH, qb = BLK * FWD_QG;
+  dim3 grid((s.b + qb - 1) / qb * sp.n, H, s.streams);
+  hipLaunchKernelGGL(k_swa_fwd<FWD_QG>, grid, dim3(NT_A), 0, st, geo(s), sp, Of, (bf16_t*)Ob, (bf16_t*)Ol, lse2);
   if (sp.n > 1)
     hipLaunchKernelGGL(k_swa_merge, dim3((unsigned)((int64_t)s.streams * s.b), H), dim3(64), 0, st, sp, s.b, s.d, Of,
                        (bf16_t*)Ob, (bf16_t*)Ol, lse2);
@@ -869,7 +919,7 @@ hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, cons
                        const float* lse2, float* Dq, void* dQKV, float* part) {
   if (!shape_ok(s)) return hipErrorInvalidValue;
   const int H = s.d / DH;
-  const int ns = swa_fwd_splits(s);  // the dQ pass divides its key blocks the same way
+  const int ns = swa_dq_splits(s);
   if (ns > 1 && !part) return hipErrorInvalidValue;
   const unsigned R = (unsigned)((int64_t)s.streams * s.b);
   hipLaunchKernelGGL(k_swa_dsum, dim3(R, H), dim3(64), 0, st, dOf, Of, s.d, s.b, Dq);

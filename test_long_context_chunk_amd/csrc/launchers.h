@@ -110,11 +110,13 @@ struct SwaShape {
 // shared by that many workgroups, whose partial states (part [n][streams b x d], pm and pl
 // [n][streams][d / 128][b], scratch) a merge combines.
 int swa_fwd_splits(const SwaShape& s);
+// Workgroups per query block of the dQ pass (its partial dQ take part [splits][R x d]).
+int swa_dq_splits(const SwaShape& s);
 hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
                        float* pm, float* pl);
 // From dO (fp32 dOf for the row term D, bf16 dOb for the products): dQ, dK, dV of the
 // chunk's rows (bf16) into dQKV [streams b x 3d]; Dq [streams][d / 128][b] is scratch.
-// part: scratch for the split dQ partials, [swa_fwd_splits(s)][streams b x d] fp32.
+// part: scratch for the split dQ partials, [swa_dq_splits(s)][streams b x d] fp32.
 hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
                        const float* lse2, float* Dq, void* dQKV, float* part);
 // Decode of one row at position s.pos (single stream): its q | k | v (fp32 qkv [3d]) join the
