@@ -205,8 +205,12 @@ ttt_status ttt_prefill_batch(ttt_ctx* ctx, const int32_t* tokens, int64_t ld_tok
  * calls (ttt_decode_pending); ttt_prefill_chunks is refused (TTT_EINVAL) while any are.
  * Predictions use fp32 activations against the stored fast weights (bf16: W0 and rn(D) as two
  * segments, as in the forward GEMMs), so their losses carry no operand rounding. Ids out of
- * range raise the sticky TTT_ERANGE and read id 0. n = 0 is a no-op.
- * Errors (nothing enqueued): TTT_EINVAL (n < 0, NULL tokens, capacity), TTT_ESTATE. */
+ * range raise the sticky TTT_ERANGE and read id 0. n = 0 is a no-op. With attention, each
+ * prediction's key and value join the stream's rings at its position before it attends over
+ * the window (fp32 scores over the rings' hi + lo terms); a filled chunk's step re-files the
+ * chunk's keys and values from its own forward pass, as prefill would.
+ * Errors (nothing enqueued): TTT_EINVAL (n < 0, NULL tokens, capacity, a batched context),
+ * TTT_ESTATE. */
 ttt_status ttt_decode(ttt_ctx* ctx, const int32_t* tokens, int64_t n, int32_t* argmax, float* logits);
 
 /* Decoded pairs waiting for their chunk to fill (0 .. chunk - 1; -1 for NULL). */
