@@ -26,14 +26,17 @@ pytestmark = pytest.mark.gpu
 BASE = dict(vocab=2000, d_model=128, d_hidden=256, n_blocks=3, n_tokens=256, chunk=64, lr=0.05, swa_heads=1)
 
 
-@pytest.mark.parametrize("window,static,d,calls", [
-    (96, 192, 128, 2),   # window between the chunk and the stream, static MLP, two calls
-    (64, 0, 256, 1),     # window = chunk, two heads, no static MLP
-    (40, 0, 128, 4),     # window shorter than the chunk, one call per chunk
-    (1000, 128, 128, 1), # window longer than the stream (full causal attention)
+@pytest.mark.parametrize("window,static,d,calls,chunk", [
+    (96, 192, 128, 2, 64),   # window between the chunk and the stream, static MLP, two calls
+    (64, 0, 256, 1, 64),     # window = chunk, two heads, no static MLP
+    (40, 0, 128, 4, 64),     # window shorter than the chunk, one call per chunk
+    (1000, 128, 128, 1, 64), # window longer than the stream (full causal attention)
+    (1, 0, 128, 2, 64),      # window 1: each position attends to itself only
+    (80, 128, 128, 1, 48),   # chunk of 48: a ragged query block and key blocks across chunks
 ])
-def test_attention_blocks_match_the_oracle(ttt_lib, window, static, d, calls):
-    w = W.preset("e2e760m", **dict(BASE, d_model=d, swa_heads=d // 128, swa_window=window, static_hidden=static))
+def test_attention_blocks_match_the_oracle(ttt_lib, window, static, d, calls, chunk):
+    w = W.preset("e2e760m", **dict(BASE, d_model=d, swa_heads=d // 128, swa_window=window, static_hidden=static,
+                                   chunk=chunk, n_tokens=4 * chunk))
     P = W.init_weights(w, 12)
     x = W.token_stream(w, 13)
     log(f"attention window={window} static={static} d={d} calls={calls}")
@@ -91,7 +94,7 @@ def _tok(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
 
 
-@pytest.mark.parametrize("window,d", [(40, 128), (96, 256), (1000, 128)])
+@pytest.mark.parametrize("window,d", [(40, 128), (96, 256), (1000, 128), (1, 128)])
 def test_attention_decode_matches_oracle_decode(ttt_lib, window, d):
     """One prefilled chunk, then 1.5 chunks decoded in two calls (one step in between):
     every decoded row's logits and the fast weights after the step, against the oracle's
