@@ -543,7 +543,12 @@ __global__ void __launch_bounds__(NT_A) k_swa_dq_sum(const float* __restrict__ p
 // dK, dV of the chunk's own keys: grid (ceil(b / 64), H, streams); each lane owns one key.
 // dV = sum_q P dO, dK = (1 / sqrt(128)) sum_q dS Q over the chunk's queries that see the key;
 // written (bf16) into columns d + 128 h .. and 2 d + 128 h .. of dQKV.
-__global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, const bf16_t* __restrict__ dOb,
+// With nsplit > 1 (blockIdx.x = key block * nsplit + split) each workgroup takes a share of
+// the query blocks that see its keys and writes fp32 partial dK | dV into part[split] ([R x
+// 2d]); k_swa_dkdv_sum adds them in split order. The share is what balances the launch: the
+// first key block of a chunk is seen by every query block, the last by one.
+__global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, int nsplit, float* __restrict__ part,
+                                                       const bf16_t* __restrict__ dOb,
                                                        const float* __restrict__ lse2, const float* __restrict__ Dq,
                                                        bf16_t* __restrict__ dQKV) {
   __shared__ __attribute__((aligned(16))) bf16_t sQ[BLK * LDR];
@@ -554,7 +559,8 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, const bf16_t
   const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int k0 = blockIdx.x * BLK;
+  const int split = blockIdx.x % nsplit;
+  const int k0 = (blockIdx.x / nsplit) * BLK;
   const int kq = k0 + wave * 16 + lr;  // this lane's key (chunk row)
   const bool kok = kq < g.b;
   const float sc = LOG2E * 0.08838834764831845f;
@@ -578,7 +584,14 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, const bf16_t
   }
   // chunk queries that see a key of this block: from its first key to the window's end
   const int kmax = min(k0 + BLK, g.b) - 1;
-  const int qend = (int)min((int64_t)g.b - 1, (int64_t)kmax + g.window - 1);
+  int qend = (int)min((int64_t)g.b - 1, (int64_t)kmax + g.window - 1);
+  int qfirst = k0;  // this workgroup's share of the query blocks [k0, qend]
+  if (nsplit > 1) {
+    const int nq = (qend - k0) / BLK + 1;
+    const int b0 = nq * split / nsplit, b1 = nq * (split + 1) / nsplit;
+    qend = min(qend, k0 + b1 * BLK - 1);
+    qfirst = k0 + b0 * BLK;
+  }
   const int64_t base = (int64_t)z * g.b;
   Chunks cq, cd;
   float fl = 0.f, fd = 0.f;
@@ -596,8 +609,8 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, const bf16_t
       fd = qq <= qend ? Dq[o] : 0.f;
     }
   };
-  if (k0 <= qend) fetch_block(k0);
-  for (int qb = k0; qb <= qend; qb += BLK) {
+  if (qfirst <= qend) fetch_block(qfirst);
+  for (int qb = qfirst; qb <= qend; qb += BLK) {
     __syncthreads();
     put_p(cq, sQ, sQt);
     put_p(cd, sD, sDt);
@@ -643,6 +656,16 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, const bf16_t
   }
   if (!kok) return;
   const float rs = 0.08838834764831845f;
+  if (nsplit > 1) {
+    float* P = part + ((int64_t)split * gridDim.z * g.b + (int64_t)z * g.b + kq) * (2 * (int64_t)g.d) + h * DH;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int col = 16 * c + 4 * lg;
+      *(float4*)(P + col) = make_float4(dk[c][0] * rs, dk[c][1] * rs, dk[c][2] * rs, dk[c][3] * rs);
+      *(float4*)(P + g.d + col) = make_float4(dv[c][0], dv[c][1], dv[c][2], dv[c][3]);
+    }
+    return;
+  }
   bf16_t* out = dQKV + ((int64_t)z * g.b + kq) * (3 * (int64_t)g.d) + h * DH;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -864,6 +887,29 @@ bool shape_ok(const SwaShape& s) {
 
 }  // namespace
 
+// dK | dV = the sum of the split partials in split order, into columns d .. 3d of dQKV
+// (bf16): grid (streams b rows), 256 threads x 8 columns.
+__global__ void __launch_bounds__(NT_A) k_swa_dkdv_sum(const float* __restrict__ part, int nsplit, int d,
+                                                       bf16_t* __restrict__ dQKV) {
+  const int64_t row = blockIdx.x, R = gridDim.x;
+  for (int c = threadIdx.x * 8; c < 2 * d; c += NT_A * 8) {
+    float acc[8];
+    const float* p0 = part + row * (2 * (int64_t)d) + c;
+    const float4 a0 = *(const float4*)p0, a1 = *(const float4*)(p0 + 4);
+    acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
+    acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
+    for (int s = 1; s < nsplit; ++s) {
+      const float* p = part + ((int64_t)s * R + row) * (2 * (int64_t)d) + c;
+      const float4 b0 = *(const float4*)p, b1 = *(const float4*)(p + 4);
+      acc[0] += b0.x; acc[1] += b0.y; acc[2] += b0.z; acc[3] += b0.w;
+      acc[4] += b1.x; acc[5] += b1.y; acc[6] += b1.z; acc[7] += b1.w;
+    }
+    *(uint4*)(dQKV + row * (3 * (int64_t)d) + d + c) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                   pack_bf16x2(acc[6], acc[7]));
+  }
+}
+
 // Query groups of 16 per wave in the forward kernel. Two halve the tile bytes per query but
 // take about 370 registers (one workgroup per CU instead of two) and measured slower at the
 // 760M fuller block (342 against 324 us per launch).
@@ -893,6 +939,13 @@ int swa_fwd_splits(const SwaShape& s) {
   const int qb = BLK * FWD_QG;
   const int64_t wg = (int64_t)((s.b + qb - 1) / qb) * (s.d / DH) * s.streams;
   return split_count(wg, s, FWD_QG == 1 ? 512 : 256);
+}
+
+int swa_dkdv_splits(const SwaShape& s) {
+  // the first key block is seen by the most query blocks: shares of about four of them
+  const int64_t first = (int64_t)(s.window + BLK - 2 < s.b - 1 ? s.window + BLK - 2 : s.b - 1) / BLK + 1;
+  const int n = (int)((first + 3) / 4);
+  return n < 1 ? 1 : (n > 4 ? 4 : n);
 }
 
 int swa_dq_splits(const SwaShape& s) {
@@ -927,8 +980,12 @@ hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, cons
   hipLaunchKernelGGL(k_swa_bwd_dq, gq, dim3(NT_A), 0, st, geo(s), ns, part, (const bf16_t*)dOb, lse2, Dq,
                      (bf16_t*)dQKV);
   if (ns > 1) hipLaunchKernelGGL(k_swa_dq_sum, dim3(R), dim3(NT_A), 0, st, part, ns, s.d, (bf16_t*)dQKV);
-  dim3 grid((s.b + BLK - 1) / BLK, H, s.streams);
-  hipLaunchKernelGGL(k_swa_bwd_dkdv, grid, dim3(NT_A), 0, st, geo(s), (const bf16_t*)dOb, lse2, Dq, (bf16_t*)dQKV);
+  const int nk = swa_dkdv_splits(s);
+  if (nk > 1 && !part) return hipErrorInvalidValue;
+  dim3 grid((s.b + BLK - 1) / BLK * nk, H, s.streams);
+  hipLaunchKernelGGL(k_swa_bwd_dkdv, grid, dim3(NT_A), 0, st, geo(s), nk, part, (const bf16_t*)dOb, lse2, Dq,
+                     (bf16_t*)dQKV);
+  if (nk > 1) hipLaunchKernelGGL(k_swa_dkdv_sum, dim3(R), dim3(NT_A), 0, st, part, nk, s.d, (bf16_t*)dQKV);
   return hipGetLastError();
 }
 

@@ -112,6 +112,8 @@ struct SwaShape {
 int swa_fwd_splits(const SwaShape& s);
 // Workgroups per query block of the dQ pass (its partial dQ take part [splits][R x d]).
 int swa_dq_splits(const SwaShape& s);
+// Workgroups per key block of the dK, dV pass (partials take part [2 splits][R x d]).
+int swa_dkdv_splits(const SwaShape& s);
 hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
                        float* pm, float* pl);
 // From dO (fp32 dOf for the row term D, bf16 dOb for the products): dQ, dK, dV of the

@@ -495,7 +495,7 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
     c->Dq = dalloc<float>(c, (int64_t)Rr * (d / 128) * 4);
     c->dQKV = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
     const SwaShape sh = swa_shape(c, c->blocks[0], 0);
-    const int ns = std::max(swa_fwd_splits(sh), swa_dq_splits(sh));
+    const int ns = std::max({swa_fwd_splits(sh), swa_dq_splits(sh), 2 * swa_dkdv_splits(sh)});
     if (ns > 1) {
       c->swa_part = dalloc<float>(c, (int64_t)ns * Rr * d * 4);
       c->swa_m = dalloc<float>(c, (int64_t)ns * Rr * (d / 128) * 4);

@@ -33,6 +33,7 @@ BASE = dict(vocab=2000, d_model=128, d_hidden=256, n_blocks=3, n_tokens=256, chu
     (1000, 128, 128, 1, 64), # window longer than the stream (full causal attention)
     (1, 0, 128, 2, 64),      # window 1: each position attends to itself only
     (80, 128, 128, 1, 48),   # chunk of 48: a ragged query block and key blocks across chunks
+    (300, 0, 128, 2, 512),   # chunk of 512: the dK, dV pass split over query-block shares
 ])
 def test_attention_blocks_match_the_oracle(ttt_lib, window, static, d, calls, chunk):
     w = W.preset("e2e760m", **dict(BASE, d_model=d, swa_heads=d // 128, swa_window=window, static_hidden=static,
