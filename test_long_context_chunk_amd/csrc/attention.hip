@@ -9,7 +9,10 @@
 // Each lane of a wave owns one query (forward, dQ) or one key (dK/dV) as the column of
 // 16 x 16 x 32 bf16 MFMA blocks; the probabilities never leave registers: the products that
 // contract over them take them as the B operand in the k-slot order they already have, and
-// read the other operand from LDS in that same order.
+// read the other operand from LDS in that same order. Each pass can divide its range among
+// several workgroups (k_swa_merge, k_swa_dq_sum and k_swa_dkdv_sum combine the partials in
+// a fixed order). Decoding one row: k_swa_dec_append files its key and value, k_swa_dec and
+// k_swa_dec_merge attend over the window in fp32.
 #include "launchers.h"
 #include "common.h"
 
