@@ -282,3 +282,36 @@ def test_attention_settlement_matches_oracle(ttt_lib, lr, expect):
     for k in Dg:
         assert np.array_equal(Dg[k], after[k]), k
     assert dl <= TOL["bf16"]["loss"]
+
+
+def test_attention_scoring_between_decoded_tokens_leaves_the_stream_alone(ttt_lib):
+    """Prefill, decode part of a chunk, score a passage, decode the rest of the chunk and
+    prefill one more: every loss, step and update equals the same calls without the passage
+    (the passage rings are apart from the stream's, and a pending chunk keeps its ids)."""
+    import test_long_context_chunk_amd as ttt
+    w = W.preset("e2e760m", **dict(BASE, swa_window=100, static_hidden=128))
+    P = W.init_weights(w, 24)
+    x = W.token_stream(w, 25)
+    q = W.token_stream(w, 26)[:2 * w.chunk + 1]
+    b = w.chunk
+    dev = device_weights(P, "bf16")
+    runs = []
+    for score in (False, True):
+        ctx = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
+        ctx.prefill(_tok(x[:b + 1]))
+        ctx.decode(_tok(x[b:b + 30 + 1]))
+        if score:
+            ctx.evaluate(_tok(q))
+        ctx.decode(_tok(x[b + 30:2 * b + 1]))
+        ctx.prefill(_tok(x[2 * b:3 * b + 1]))
+        out = dict(losses=ctx.token_losses().cpu().numpy(), stats=ctx.chunk_stats().cpu().numpy(),
+                   D={f"{k}.{l}": ctx.fast_weight(l, k, "delta").cpu().numpy()
+                      for l in range(w.n_blocks) for k in w.fast_names()})
+        assert ctx.sync() == 0 and ctx.consumed() == 3 * b
+        ctx.close()
+        runs.append(out)
+    a, c = runs
+    assert np.array_equal(a["losses"], c["losses"])
+    assert np.array_equal(a["stats"], c["stats"])
+    for k in a["D"]:
+        assert np.array_equal(a["D"][k], c["D"][k]), k
