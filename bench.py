@@ -456,8 +456,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        eprint("bench.py measures one GPU only: the inner loop of one token stream runs on a single "
-               "MI355X here and this build has no multi-GPU path; run with --gpus 1.")
+        eprint("bench.py measures one GPU only: the library runs each token stream's inner loop on a "
+               "single MI355X and has no multi-GPU path; run with --gpus 1.")
         sys.exit(2)
 
     import numpy as np
