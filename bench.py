@@ -331,15 +331,16 @@ def visible_keys(w, pos: int, n: int) -> int:
     return total
 
 
-def e2e_flops_per_step(w) -> dict:
-    """Algorithmic flops of one step over the whole stream of the fuller block (attention,
-    static MLP, fast MLP per block), no recompute: per token and block, the attention
-    projections 8d^2 forward and (blocks above the lowest) 8d^2 backward, the attention core
-    4d per visible key forward and 4d per visible key plus 4d per visible key of the chunk
-    backward; the static MLP 4 d m_s forward and 4 d m_s backward above the lowest; the fast
-    MLP and LM head as in the plain step."""
+def e2e_flops_per_step(w, pos: int = 0) -> dict:
+    """Algorithmic flops of one step over T tokens of the fuller block from stream position
+    pos (attention, static MLP, fast MLP per block), no recompute: per token and block, the
+    attention projections 8d^2 forward and (blocks above the lowest) 8d^2 backward, the
+    attention core 4d per visible key forward and 4d per visible key plus 4d per visible key
+    of the chunk backward; the static MLP 4 d m_s forward and 4 d m_s backward above the
+    lowest; the fast MLP and LM head as in the plain step. The timed steps continue the stream
+    past its first window, where every query sees the whole window."""
     d, ms, L, T, b = w.d_model, w.static_hidden, w.n_blocks, w.n_tokens, w.chunk
-    keys = visible_keys(w, 0, T)
+    keys = visible_keys(w, pos, T)
     chunk_keys = 0  # visible keys that lie in the query's own chunk
     for i in range(T // b):
         for q in range(b):
@@ -395,7 +396,7 @@ def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2
     if status != 0 or not np.all(np.isfinite(last)):
         eprint(f"[bench] e2e760m: status {status} or non-finite losses")
         sys.exit(1)
-    fl = e2e_flops_per_step(w)
+    fl = e2e_flops_per_step(w, T * (warmup + 1))  # the timed steps' positions
     value = steps * T / elapsed
     a_ms, a_n = aprof.get("attn", (0.0, 0))
     per_launch = fl["attn_fwd"] / max(1, w.n_chunks * w.n_blocks)
