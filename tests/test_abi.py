@@ -166,3 +166,9 @@ def test_kernel_kind_names_match_the_header():
     count = int(re.search(r"TTT_K_COUNT = (\d+)", hdr).group(1))
     assert [int(v) for _, v in kinds] == list(range(count))
     assert len(_binding.KERNEL_KINDS) == count
+
+
+def test_a_missing_library_raises_instead_of_falling_back(tmp_path):
+    """No compute path exists outside the HIP library: loading one that is not there raises."""
+    with pytest.raises(RuntimeError, match="not built"):
+        B.load_library(str(tmp_path / "libttt_missing.so"))
