@@ -55,11 +55,15 @@ typedef enum {
 
 enum { TTT_MLP_GELU = 0, TTT_MLP_SWIGLU_W2 = 1 };
 enum { TTT_NORM_NONE = 0, TTT_NORM_RMS = 1 };
-/* TTT_FP32: fp32 GEMM operands and fp32 fast weights.
+/* TTT_FP32: fp32 GEMM operands and fp32 fast weights (kept as W0 + D, D the fp32
+ *           accumulated update).
  * TTT_BF16: bf16 GEMM operands (weights and activations rounded to nearest even),
- *           fp32 accumulation, fp32 residual stream, losses and gradients; the fast
- *           state is kept as W0 + D with D the fp32 accumulated update, and the GEMMs
- *           read bf16(W0 + D). */
+ *           fp32 accumulation, fp32 residual stream and losses. The fast state is kept as
+ *           W0 + D with D the fp32 accumulated update. The forward products read it as two
+ *           bf16 K-segments, W0 and rn(D) (a single rn(W0 + D) would drop updates smaller
+ *           than half a bf16 ulp of W0); the backward products read rn(W0 + D). Chunk
+ *           gradients are stored in bf16; their squared norm is summed from the fp32
+ *           accumulators. */
 enum { TTT_FP32 = 0, TTT_BF16 = 1 };
 
 typedef struct {
@@ -97,9 +101,11 @@ typedef struct {
   const void* const* w2;
 } ttt_weights;
 
-/* Create a context: validates the configuration, allocates all device memory the
- * chunk loop needs, and copies every weight into library-owned memory (the caller may
- * free its tensors when this returns). Synchronous. `stream` is a hipStream_t (NULL =
+/* Create a context for one token stream ([E2E] Method: the model reads a prefix x_0..x_T
+ * with x_0 = BOS and keeps learning from it; [IPT] section 1: the fast weights are private
+ * state of the stream, updated while it is read, the rest of the model frozen). Validates
+ * the configuration, allocates all device memory the chunk loop needs, and copies every
+ * weight into library-owned memory (the caller may free its tensors when this returns). Synchronous. `stream` is a hipStream_t (NULL =
  * the default stream) on which every later call of this context is enqueued.
  * Errors: TTT_EINVAL (config), TTT_ENOMEM, TTT_EDEVICE. On error *out is NULL. */
 ttt_status ttt_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out);
@@ -246,6 +252,8 @@ ttt_status ttt_settle_chunk(ttt_ctx* ctx, const int32_t* tokens, const int32_t* 
 
 /* Copy the recorded losses l_t(W_{i-1}) of tokens [offset, offset + n) (counted from the
  * first token of the first prefill since creation or reset) into dst (device fp32 [n]).
+ * These are the summands of [E2E] eq. (6), L = (1/T) sum_i sum_{t in chunk i} l_t(W_{i-1}):
+ * each token is scored at its chunk's weights before that chunk's step.
  * Synchronises the context's stream; returns a pending sticky error if there is one
  * (the copy is still made). Errors: TTT_EINVAL (range), TTT_ERANGE, TTT_ENONFINITE. */
 ttt_status ttt_token_losses(ttt_ctx* ctx, float* dst, int64_t offset, int64_t n);
@@ -258,7 +266,9 @@ ttt_status ttt_token_argmax(ttt_ctx* ctx, int32_t* dst, int64_t offset, int64_t 
 ttt_status ttt_chunk_stats(ttt_ctx* ctx, float* dst, int64_t offset, int64_t n);
 
 /* Export a fast tensor as fp32 into dst (device, same shape/layout as its initial
- * weight: W1 [d x m], W2 [m x d]). which: 1 = W1 (GELU only), 2 = W2.
+ * weight: W1 [d x m], W2 [m x d]): the fast weights W_i after the last step of [E2E]
+ * eq. (5) ([E2E] section 3.1: the MLP weights; [IPT] section 1: the final projection only).
+ * which: 1 = W1 (GELU only), 2 = W2.
  * kind: 0 = current W = W0 + D;  1 = accumulated update D = W - W0. Synchronises.
  * Errors: TTT_EINVAL (block/which/kind). */
 ttt_status ttt_fast_weights(ttt_ctx* ctx, int32_t block, int32_t which, int32_t kind, float* dst);

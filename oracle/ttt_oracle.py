@@ -326,7 +326,7 @@ def chunk_loss_and_grads(model: Model, P, x_prev, x_tgt, logit_probe=None, kv=No
     b = x_prev.shape[0]
     z, h, cache = logits(model, P, x_prev, kv)
     if logit_probe is not None:
-        logit_probe(z)
+        logit_probe(z, h)
     losses, lse, am, margin = ce_stats(z, x_tgt)
     rows = np.arange(b)
     p = np.exp(z - lse[:, None])
@@ -396,8 +396,9 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
     tokens = x_0..x_T with T a multiple of b. Chunk i scores and differentiates
     tokens t = (i-1)b+1 .. ib at W_{i-1} (the weights before its own step), then
     steps W_i = W_{i-1} - eta * s_i * G_i. The fast state is kept as W_0 + D so
-    that the accumulated update D is exact. logit_probe(i, z), when given, sees chunk
-    i's logits (for checks that need logits the result does not keep).
+    that the accumulated update D is exact. logit_probe(i, z, h), when given, sees chunk
+    i's logits z and the hidden rows h that produced them (for checks that need values the
+    result does not keep).
     """
     P0 = as_f64(P0)
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -418,7 +419,7 @@ def run_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray,
         x_prev = tokens[i * b: i * b + b]
         x_tgt = tokens[i * b + 1: i * b + b + 1]
         _, st, G = chunk_loss_and_grads(model, P, x_prev, x_tgt, logit_probe=(
-            None if logit_probe is None else (lambda z, i=i: logit_probe(i, z))), kv=kv)
+            None if logit_probe is None else (lambda z, h, i=i: logit_probe(i, z, h))), kv=kv)
         kv = st.get("kv")
         losses.append(st["losses"])
         argm.append(st["argmax"])
@@ -451,8 +452,8 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
     gradient step only when the decoded tokens fill a mini-batch of b; decoding then goes on
     with the updated weights (section 3.2). So token t is scored at the weights left by the
     last completed chunk before it, and a trailing partial chunk takes no step. The step is
-    the clipped mini-batch step of [E2E] eq. (5) / [SGF]. logit_probe(t - 1, z), when given,
-    sees the logits row that scored token t.
+    the clipped mini-batch step of [E2E] eq. (5) / [SGF]. logit_probe(t - 1, z, h), when
+    given, sees the logits row that scored token t and the hidden row that produced it.
 
     With attention, each decoded token's key and value are computed at the weights current
     when it is decoded and join the cache at once; a filled mini-batch's step starts from the
@@ -475,11 +476,11 @@ def decode_ttt(model: Model, P0: Dict[str, np.ndarray], tokens: np.ndarray, logi
         P = dict(P0)
         for k in keys:
             P[k] = P0[k] + D[k]
-        z, _, cache = logits(model, P, tokens[t - 1:t], kv)
+        z, hL, cache = logits(model, P, tokens[t - 1:t], kv)
         if att:
             kv = next_kv(model, kv, cache)
         if logit_probe is not None:
-            logit_probe(t - 1, z[0])
+            logit_probe(t - 1, z[0], hL[0])
         l, _, am, mg = ce_stats(z, tokens[t:t + 1])
         losses.append(l[0])
         argm.append(am[0])

@@ -190,8 +190,12 @@ struct HipFail {
 constexpr unsigned kSyncEvent = hipEventDisableTiming | hipEventReleaseToDevice;
 
 inline void check(hipError_t e) {
+  if (e == hipSuccess) return;
+  // clear the runtime's last-error state, so that a refused allocation is reported here
+  // only and not again by the caller's next unrelated HIP call
+  (void)hipGetLastError();
   if (e == hipErrorOutOfMemory) throw HipFail{TTT_ENOMEM};
-  if (e != hipSuccess) throw HipFail{TTT_EDEVICE};
+  throw HipFail{TTT_EDEVICE};
 }
 
 template <class P>

@@ -16,7 +16,7 @@ refuses. Gates are those of tests/_parity.py (bf16).
 import numpy as np
 import pytest
 
-from _parity import TOL, compare, device_weights, gpu_run, log, oracle_run, rel_l2
+from _parity import TOL, argmax_gate_rows, compare, device_weights, gpu_run, log, oracle_run, rel_l2
 
 import oracle as O
 import ttt_workloads as W
@@ -60,16 +60,20 @@ def test_attention_batched_streams(ttt_lib):
     assert np.array_equal(gs[0]["losses"], gs[2]["losses"])
 
 
-def test_e2e760m_attention_sampled(ttt_lib):
+def test_e2e760m_attention_past_the_window(ttt_lib):
     """The fuller 760M block (12 heads, window 8K, static MLP) in the benchmark's launch
-    configuration: the first two chunks against the oracle."""
-    w = W.preset("e2e760m", n_tokens=2048)
+    configuration, 11 chunks in one prefill call: chunks 9-11 see a full 8192-key window and
+    the key/value ring (window + chunk = 9216 slots) wraps at chunk 10; every token, step
+    and update against the oracle."""
+    n_chunks = 11
+    w = W.preset("e2e760m", n_tokens=n_chunks * 1024)
     P = W.init_weights(w, 0)
     x = W.token_stream(w, 0)
-    log("attention e2e760m")
+    log(f"attention e2e760m: {n_chunks} chunks")
     g = gpu_run(w, P, x)
     assert g["status"] == 0
-    compare(g, oracle_run(w, P, x, 2), w, "bf16", 2, label="e2e760m-attn")
+    log(f"oracle e2e760m: {n_chunks} chunks")
+    compare(g, oracle_run(w, P, x, n_chunks), w, "bf16", n_chunks, label="e2e760m-attn")
 
 
 def test_batched_attention_context_refuses_single_stream_calls(ttt_lib):
@@ -109,23 +113,27 @@ def test_attention_decode_matches_oracle_decode(ttt_lib, window, d):
     log(f"attention decode window={window} d={d}")
     ctx = ttt.TTT.from_workload(w, device_weights(P, "bf16"), max_tokens=w.n_tokens)
     ctx.prefill(_tok(x[:b + 1]))
-    _, z1 = ctx.decode(_tok(x[b:b + 40 + 1]), want_logits=True)
-    _, z2 = ctx.decode(_tok(x[b + 40:b + n + 1]), want_logits=True)
+    am1, z1 = ctx.decode(_tok(x[b:b + 40 + 1]), want_logits=True)
+    am2, z2 = ctx.decode(_tok(x[b + 40:b + n + 1]), want_logits=True)
     zg = np.concatenate([z1.cpu().numpy(), z2.cpu().numpy()]).astype(np.float64)
+    am = np.concatenate([am1.cpu().numpy(), am2.cpu().numpy()]).astype(np.int64)
     assert ctx.decode_pending() == n - b
     Dg = {f"{k}.{l}": ctx.fast_weight(l, k, "delta").cpu().numpy().astype(np.float64)
           for l in range(w.n_blocks) for k in w.fast_names()}
     assert ctx.sync() == 0
     ctx.close()
     rows = []
-    orc = O.decode_ttt(O.Model.from_workload(w), P, x[:b + n + 1], logit_probe=lambda t, z: rows.append((t, z.copy())))
-    Z = np.stack([z for t, z in rows if t >= b])
+    orc = O.decode_ttt(O.Model.from_workload(w), P, x[:b + n + 1],
+                       logit_probe=lambda t, z, h: rows.append((t, z.copy(), h.copy())))
+    Z = np.stack([z for t, z, h in rows if t >= b])
+    H = np.stack([h for t, z, h in rows if t >= b])
     tol = TOL["bf16"]
     dz = float(np.max(np.abs(zg - Z)))
     dd = max(rel_l2(Dg[k], orc.delta[k]) for k in orc.delta)
     log(f"[attention decode w{window}] logits {dz:.3g} D {dd:.3g}")
     assert dz <= tol["logit"]
     assert dd <= tol["dw"]
+    argmax_gate_rows(am, Z, H, P["E_out"], "bf16", f"attention decode w{window}")
 
 
 def test_attention_decoded_chunk_is_bitwise_the_prefilled_step(ttt_lib):
@@ -170,18 +178,20 @@ def test_e2e760m_attention_decode_sampled(ttt_lib):
     log("attention decode e2e760m")
     ctx = ttt.TTT.from_workload(w, device_weights(P, "bf16"), max_tokens=T0 + b)
     ctx.prefill(_tok(x[:T0 + 1]))
-    _, z = ctx.decode(_tok(x[T0:T0 + n + 1]), want_logits=True)
+    am, z = ctx.decode(_tok(x[T0:T0 + n + 1]), want_logits=True)
     z = z.cpu().numpy().astype(np.float64)
+    am = am.cpu().numpy().astype(np.int64)
     assert ctx.sync() == 0
     ctx.close()
     model = O.Model.from_workload(w)
     orc = oracle_run(w, P, x, 2)
     Pw = dict(O.as_f64(P))
     Pw.update(orc.weights)
-    zo, _, _ = O.logits(model, Pw, x[T0:T0 + n], orc.kv)
+    zo, ho, _ = O.logits(model, Pw, x[T0:T0 + n], orc.kv)
     dz = float(np.max(np.abs(z - zo)))
     log(f"[attention decode e2e760m] logits {dz:.3g}")
     assert dz <= TOL["bf16"]["logit"]
+    argmax_gate_rows(am, zo, ho, P["E_out"], "bf16", "attention decode e2e760m")
 
 
 SETTLE = dict(BASE, swa_window=96, static_hidden=128)

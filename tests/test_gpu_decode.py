@@ -16,7 +16,8 @@ Gates are those of tests/_parity.py.
 import numpy as np
 import pytest
 
-from _parity import TOL, device_weights, inputs, log, oracle_run, rel_l2
+from _parity import TOL, LogitRecord, argmax_gate, argmax_gate_rows, device_weights, inputs, log, oracle_run, rel_l2, \
+    rms_row_norm
 
 import oracle as O
 
@@ -48,19 +49,13 @@ def _weights(ctx, w, kind):
     return out
 
 
-def _check_argmax(am_gpu, z_at_pick, z_max, tol, label):
-    worst = float(np.max(z_max - z_at_pick)) if len(am_gpu) else 0.0
-    log(f"[decode {label}] argmax worst pick gap {worst:.3g}")
-    assert worst <= tol
-
-
 def test_decode_toy_fp32_matches_oracle_decode(ttt_lib):
     """b = 1: every decoded token is its own mini-batch; three calls over the whole stream."""
     w, x, P = inputs("toy")
     model = O.Model.from_workload(w)
-    rows = []
-    orc = O.decode_ttt(model, P, x, logit_probe=lambda t, z: rows.append(z.copy()))
-    Z = np.stack(rows)
+    rows, hs = [], []
+    orc = O.decode_ttt(model, P, x, logit_probe=lambda t, z, h: (rows.append(z.copy()), hs.append(h.copy())))
+    Z, H = np.stack(rows), np.stack(hs)
     ctx = _ctx(w, device_weights(P, "fp32"), w.n_tokens, "fp32")
     am, zs = [], []
     for a, b in [(0, 40), (40, 90), (90, w.n_tokens)]:
@@ -82,7 +77,7 @@ def test_decode_toy_fp32_matches_oracle_decode(ttt_lib):
     ctx.close()
     assert dl <= tol["loss"] and dr <= tol["loss"] and dz <= tol["logit"]
     assert wr <= tol["w"] and dr2 <= tol["dw"]
-    _check_argmax(am, Z[np.arange(len(am)), am], Z.max(axis=1), tol["logit"], "toy")
+    argmax_gate_rows(am, Z, H, P["E_out"], "fp32", "decode toy")
 
 
 def test_decoded_chunk_is_bitwise_the_prefilled_step(ttt_lib):
@@ -127,19 +122,18 @@ def test_decode_single_matches_oracle(ttt_lib, precision):
     ctx.close()
     # oracle: chunk 2 scored at W_1 (its logits seen through the probe), then the tail at W_2
     sample = np.arange(0, b, 97)
-    at_pick, top, zs = [], [], {}
+    rec2, zs = LogitRecord(), {}
 
-    def probe(i, zz):
+    def probe(i, zz, h):
         if i == 1:
-            at_pick.append(zz[np.arange(b), am[:b]])
-            top.append(zz.max(axis=1))
+            rec2.add(zz, h)
             for r in sample:
                 zs[r] = zz[r].copy()
 
     orc = O.run_ttt(model, P, x[:2 * b + 1], logit_probe=probe)
     Pw = dict(O.as_f64(P))
     Pw.update(orc.weights)
-    zt, _, _ = O.logits(model, Pw, x[2 * b:2 * b + 64])
+    zt, ht, _ = O.logits(model, Pw, x[2 * b:2 * b + 64])
     l_tail, _, _, _ = O.ce_stats(zt, x[2 * b + 1:2 * b + 65])
     ref = np.concatenate([orc.losses[b:2 * b], l_tail])
     tol = TOL[precision]
@@ -154,9 +148,10 @@ def test_decode_single_matches_oracle(ttt_lib, precision):
     assert dl <= tol["loss"] and dtail <= tol["loss"]
     assert dz <= tol["logit"] and dzt <= tol["logit"]
     assert wr <= tol["w"] and dr <= tol["dw"]
-    pick = np.concatenate([np.concatenate(at_pick), zt[np.arange(64), am[b:]]])
-    mx = np.concatenate([np.concatenate(top), zt.max(axis=1)])
-    _check_argmax(am, pick, mx, tol["logit"], f"single {precision}")
+    rec2.add(zt, ht)
+    vals, ids, hn = rec2.arrays()
+    am_o = np.concatenate([orc.argmax[b:2 * b], np.argmax(zt, axis=1)])
+    argmax_gate(am, am_o, vals, ids, hn, rms_row_norm(P["E_out"]), w.d_model, precision, f"decode single")
 
 
 @pytest.mark.parametrize("name,pre_chunks,n", [("s760m", 2, 48), ("inplace", 1, 16)])
@@ -176,14 +171,14 @@ def test_decode_partial_chunk_large_shapes(ttt_lib, name, pre_chunks, n):
     orc = oracle_run(w, P, x, pre_chunks, key=name)
     Pw = dict(O.as_f64(P))
     Pw.update(orc.weights)
-    zo, _, _ = O.logits(model, Pw, x[T0:T0 + n])
+    zo, ho, _ = O.logits(model, Pw, x[T0:T0 + n])
     lo, _, _, _ = O.ce_stats(zo, x[T0 + 1:T0 + n + 1])
     tol = TOL["bf16"]
     dl = np.abs(rec - lo).max()
     dz = np.abs(z - zo).max()
     log(f"[decode {name}] loss {dl:.3g} logits {dz:.3g}")
     assert dl <= tol["loss"] and dz <= tol["logit"]
-    _check_argmax(am, zo[np.arange(n), am], zo.max(axis=1), tol["logit"], name)
+    argmax_gate_rows(am, zo, ho, P["E_out"], "bf16", f"decode {name}")
 
 
 def test_decode_state_and_argument_errors(ttt_lib):

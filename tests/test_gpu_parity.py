@@ -95,33 +95,66 @@ def test_single_block_full_stream(ttt_lib, single_oracle, precision):
     w, x, P = inputs("single")
     g = gpu_run(w, P, x, precision=precision)
     assert g["status"] == 0
-    orc = single_oracle
-    # the argmax validity gate needs the oracle logits at the GPU's picks
-    orc_p = oracle_run(w, P, x, 2, gpu_argmax=g["argmax"])
-    compare(g, orc_p, w, precision, 2, check_weights=False, label="single-argmax")
-    compare(g, orc, w, precision, w.n_chunks, label="single")
+    compare(g, single_oracle, w, precision, w.n_chunks, label="single")
+
+
+def _ttt_change_gate(g, g_static, orc, orc_static, n, label):
+    """fp32 mode: the loss change that test-time training causes, l_t - l_t(W0), matches the
+    oracle's within 5% of the oracle's largest change plus 2e-6 (the loss gates alone cannot
+    see it where it is smaller than they are)."""
+    ch_g = g["losses"][:n] - g_static[:n]
+    ch_o = orc.losses[:n] - orc_static[:n]
+    bound = 0.05 * float(np.max(np.abs(ch_o))) + 2e-6
+    err = float(np.max(np.abs(ch_g - ch_o)))
+    log(f"[ttt-change {label}] oracle max |change| {float(np.max(np.abs(ch_o))):.3g} mean {float(np.mean(ch_o)):.3g}; "
+        f"GPU error {err:.3g} (bound {bound:.3g})")
+    assert float(np.max(np.abs(ch_o))) > 0.0
+    assert err <= bound
+
+
+def test_single_block_fp32_ttt_loss_change(ttt_lib, single_oracle):
+    """fp32, all 8 chunks of the single-block stream: the TTT-induced loss change."""
+    w, x, P = inputs("single")
+    dev = device_weights(P, "fp32")
+    g = gpu_run(w, P, x, precision="fp32", dev=dev)
+    g0 = gpu_run(w, P, x, precision="fp32", dev=dev, lr=0.0)
+    orc_static = O.static_losses(O.Model.from_workload(w), P, x)
+    _ttt_change_gate(g, g0["losses"], single_oracle, orc_static, w.n_tokens, "single fp32")
 
 
 @pytest.fixture(scope="module")
 def s760m_oracle():
+    """The whole 32-chunk 760M-shape stream (about 40 s of fp64 on 16 host cores)."""
     w, x, P = inputs("s760m")
-    return oracle_run(w, P, x, 2, key="s760m")
+    log("oracle s760m: 32 chunks")
+    return oracle_run(w, P, x, w.n_chunks, key="s760m")
 
 
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
-def test_s760m_two_chunk_prefix(ttt_lib, s760m_oracle, precision):
-    """760M shape (3 pre-RMSNorm GELU blocks, d=1536, m=6144): first two chunks."""
+def test_s760m_full_stream(ttt_lib, s760m_oracle, precision):
+    """760M shape (3 pre-RMSNorm GELU blocks, d=1536, m=6144), the whole 32K stream in the
+    benchmark's launch configuration (one prefill call), every token and every chunk."""
     w, x, P = inputs("s760m")
-    g = gpu_run(w, P, x, n_tokens=2 * w.chunk, precision=precision)
+    g = gpu_run(w, P, x, precision=precision)
     assert g["status"] == 0
-    compare(g, s760m_oracle, w, precision, 2, label="s760m")
+    compare(g, s760m_oracle, w, precision, w.n_chunks, label="s760m")
 
 
-def test_s760m_full_stream_properties(ttt_lib, s760m_oracle):
-    """Full 32K-token stream in the benchmark's launch configuration (one prefill call):
-    its first two chunks match the oracle's prefix; the first chunks obey the clip identity
+def test_s760m_fp32_ttt_loss_change(ttt_lib, s760m_oracle):
+    """fp32, first 4 chunks of the 760M shape: the TTT-induced loss change."""
+    w, x, P = inputs("s760m")
+    n = 4 * w.chunk
+    dev = device_weights(P, "fp32")
+    g = gpu_run(w, P, x, n_tokens=n, precision="fp32", dev=dev)
+    g0 = gpu_run(w, P, x, n_tokens=n, precision="fp32", dev=dev, lr=0.0)
+    orc_static = O.static_losses(O.Model.from_workload(w), P, x, n_tokens=n)
+    _ttt_change_gate(g, g0["losses"], s760m_oracle, orc_static, n, "s760m fp32")
+
+
+def test_s760m_full_stream_properties(ttt_lib):
+    """Full 32K-token stream: the first chunks obey the clip identity
     ||W_i - W_{i-1}||_F = lr * min(g_i, c); the same stream fed as per-chunk calls gives
-    bitwise identical losses and updates."""
+    bitwise identical losses and updates to one call."""
     import torch
     import test_long_context_chunk_amd as ttt
     w, x, P = inputs("s760m")
@@ -129,10 +162,6 @@ def test_s760m_full_stream_properties(ttt_lib, s760m_oracle):
     full = gpu_run(w, P, x, dev=dev)
     assert full["status"] == 0
     assert np.all(np.isfinite(full["losses"]))
-    orc = s760m_oracle
-    n = 2 * w.chunk
-    assert np.max(np.abs(full["losses"][:n] - orc.losses[:n])) <= TOL["bf16"]["loss"]
-    assert np.max(np.abs(full["stats"][:2, 0] - orc.grad_norm[:2]) / orc.grad_norm[:2]) <= TOL["bf16"]["g"]
 
     ctx = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
     tok = torch.from_numpy(x.astype(np.int32)).cuda()
@@ -177,23 +206,30 @@ def test_s760m_zero_lr_full_stream_is_static(ttt_lib):
         assert not D.any()
 
 
-@pytest.mark.parametrize("precision", ["bf16", "fp32"])
-def test_s125m_two_chunk_prefix(ttt_lib, precision):
-    """125M-style stack (3 pre-RMSNorm blocks, d=768): first two chunks of the 128K stream."""
+@pytest.fixture(scope="module")
+def s125m_oracle():
     w, x, P = inputs("s125m")
-    orc = oracle_run(w, P, x, 2, key="s125m")
-    g = gpu_run(w, P, x, n_tokens=2 * w.chunk, precision=precision)
+    log("oracle s125m: 16 chunks")
+    return oracle_run(w, P, x, 16, key="s125m")
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp32"])
+def test_s125m_sixteen_chunk_prefix(ttt_lib, s125m_oracle, precision):
+    """125M-style stack (3 pre-RMSNorm blocks, d=768): the first 16 chunks of the 128K stream."""
+    w, x, P = inputs("s125m")
+    g = gpu_run(w, P, x, n_tokens=16 * w.chunk, precision=precision)
     assert g["status"] == 0
-    compare(g, orc, w, precision, 2, label="s125m")
+    compare(g, s125m_oracle, w, precision, 16, label="s125m")
 
 
-def test_inplace_swiglu_first_chunk(ttt_lib):
-    """In-Place shape: SwiGLU (gate/up frozen), only W2 fast, V=151936, b=512."""
+def test_inplace_swiglu_four_chunks(ttt_lib):
+    """In-Place shape: SwiGLU (gate/up frozen), only W2 fast, V=151936, b=512; 4 chunks."""
     w, x, P = inputs("inplace")
-    orc = oracle_run(w, P, x, 1, key="inplace")
-    g = gpu_run(w, P, x, n_tokens=w.chunk)
+    log("oracle inplace: 4 chunks")
+    orc = oracle_run(w, P, x, 4, key="inplace")
+    g = gpu_run(w, P, x, n_tokens=4 * w.chunk)
     assert g["status"] == 0
-    compare(g, orc, w, "bf16", 1, label="inplace")
+    compare(g, orc, w, "bf16", 4, label="inplace")
 
 
 # ---------------------------------------------------------------------- determinism, errors
@@ -256,6 +292,23 @@ def test_nonfinite_gradient_skips_the_step(ttt_lib):
     assert g["stats"][0, 1] == 0.0
     for D in g["D"].values():
         assert not D.any()
+
+
+def test_absurd_capacity_is_out_of_memory(ttt_lib):
+    """A context whose per-token records cannot fit (max_tokens = 2^42: 16 TiB of losses)
+    fails with TTT_ENOMEM, frees what it had allocated, and leaves the device usable: a
+    normal context created next runs and matches a fresh run bit for bit."""
+    import torch
+    import test_long_context_chunk_amd as ttt
+    w, x, P = inputs("single", n_tokens=1024)
+    dev = device_weights(P, "bf16")
+    with pytest.raises(ttt.TTTError) as e:
+        ttt.TTT.from_workload(w, dev, max_tokens=1 << 42)
+    assert e.value.status == -2  # TTT_ENOMEM
+    torch.cuda.synchronize()
+    a = gpu_run(w, P, x, dev=dev)
+    b = gpu_run(w, P, x, dev=dev)
+    assert a["status"] == 0 and np.array_equal(a["losses"], b["losses"])
 
 
 def test_prefill_argument_errors(ttt_lib):

@@ -11,7 +11,7 @@ Gates are those of tests/_parity.py.
 import numpy as np
 import pytest
 
-from _parity import TOL, compare, device_weights, gpu_run, log, oracle_run, rel_l2
+from _parity import TOL, argmax_gate_rows, compare, device_weights, gpu_run, log, oracle_run, rel_l2
 
 import oracle as O
 import ttt_workloads as W
@@ -65,6 +65,7 @@ def test_static_mlp_decode_matches_oracle_decode(ttt_lib, precision):
     am1, z1 = ctx.decode(_tok(x[b:b + 40 + 1]), want_logits=True)
     am2, z2 = ctx.decode(_tok(x[b + 40:b + n + 1]), want_logits=True)
     zg = np.concatenate([z1.cpu().numpy(), z2.cpu().numpy()]).astype(np.float64)
+    am = np.concatenate([am1.cpu().numpy(), am2.cpu().numpy()]).astype(np.int64)
     assert ctx.decode_pending() == n - b
     Dg = {f"{k}.{l}": ctx.fast_weight(l, k, "delta").cpu().numpy().astype(np.float64)
           for l in range(w.n_blocks) for k in w.fast_names()}
@@ -74,14 +75,16 @@ def test_static_mlp_decode_matches_oracle_decode(ttt_lib, precision):
     rows = []
     # the oracle's decode: one prefilled chunk's step, then token by token with a step at the
     # chunk boundary (the first b tokens decoded, then prefill-equivalent)
-    orc = O.decode_ttt(model, P, x[:b + n + 1], logit_probe=lambda t, z: rows.append((t, z.copy())))
-    Z = np.stack([z for t, z in rows if t >= b])
+    orc = O.decode_ttt(model, P, x[:b + n + 1], logit_probe=lambda t, z, h: rows.append((t, z.copy(), h.copy())))
+    Z = np.stack([z for t, z, h in rows if t >= b])
+    H = np.stack([h for t, z, h in rows if t >= b])
     tol = TOL[precision]
     dz = float(np.max(np.abs(zg - Z)))
     dd = max(rel_l2(Dg[k], orc.delta[k]) for k in orc.delta)
     log(f"[static decode {precision}] logits {dz:.3g} D {dd:.3g}")
     assert dz <= tol["logit"]
     assert dd <= tol["dw"]
+    argmax_gate_rows(am, Z, H, P["E_out"], precision, f"static decode")
 
 
 def test_e2e760m_two_chunks_sampled(ttt_lib):

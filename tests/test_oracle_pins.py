@@ -265,6 +265,25 @@ def torch_ttt(model, P0, tokens):
     return np.concatenate(losses), np.array(gnorms), {k: v.numpy() for k, v in fast.items()}
 
 
+def test_p9b_ce_stats_worked_rows():
+    """ce_stats on hand-made rows whose results are known exactly: the argmax is the first
+    maximum (ties to the lowest index), the margin is the gap between the two largest values
+    (0 at a tie), the loss is lse minus the target's logit, and a one-column row has loss 0
+    and an infinite margin."""
+    z = np.array([[1.0, 3.0, 2.0, 3.0],
+                  [0.5, -1.0, 2.25, 0.0],
+                  [-4.0, -4.0, -4.0, -4.0]])
+    loss, lse, am, margin = O.ce_stats(z, np.array([2, 2, 3]))
+    assert am.tolist() == [1, 2, 0]
+    assert margin.tolist() == [0.0, 1.75, 0.0]
+    assert lse[0] == pytest.approx(math.log(math.exp(1) + 2 * math.exp(3) + math.exp(2)), rel=1e-15)
+    assert lse[1] == pytest.approx(math.log(math.exp(0.5) + math.exp(-1) + math.exp(2.25) + 1.0), rel=1e-15)
+    assert lse[2] == pytest.approx(-4.0 + math.log(4.0), rel=1e-15)
+    assert loss.tolist() == pytest.approx([lse[0] - 2.0, lse[1] - 2.25, math.log(4.0)], rel=1e-15)
+    l1, _, a1, m1 = O.ce_stats(np.array([[7.0], [-2.0]]), np.array([0, 0]))
+    assert l1.tolist() == [0.0, 0.0] and a1.tolist() == [0, 0] and np.all(np.isinf(m1))
+
+
 @pytest.mark.parametrize("mlp,norm", COMBOS)
 @pytest.mark.parametrize("clip", [0.0, 0.1])
 def test_p10_torch_autograd_second_opinion(mlp, norm, clip):
