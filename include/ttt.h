@@ -250,6 +250,29 @@ ttt_status ttt_restore(ttt_ctx* ctx);
 ttt_status ttt_settle_chunk(ttt_ctx* ctx, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
                             int32_t* committed);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ttt_settle_chunk with the pre-candidate
+ * snapshot kept in the library's static scratch, a device array of
+ * TTT_STATIC_SCRATCH_BYTES bytes per GPU, instead of the context's snapshot slot that
+ * ttt_settle_chunk allocates on first use. The array's device address is looked up when the
+ * first context is created on a GPU (the runtime may back it with memory then), and the GPU
+ * holds it until the process ends. This call itself allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine. Results (A, the decision, the recorded losses and the
+ * state it leaves) are those of ttt_settle_chunk; the context's own snapshot slot is
+ * neither used nor changed (ttt_restore still returns to the last ttt_snapshot).
+ * The snapshot needs, per fast tensor of n parameters, 4 n + 2 n e bytes, each part rounded
+ * up to 256 (e = 2 in bf16, 4 in fp32): about 8 bytes per fast parameter in bf16, so
+ * contexts up to about 8.3M fast parameters in bf16 (5.5M in fp32).
+ * Every call on one GPU uses that GPU's one array: calls whose work may overlap on the GPU
+ * (other streams, other contexts) race on it and must be ordered by the caller; calls on one
+ * context are ordered by its stream. The array keeps the last call's contents; nothing in it
+ * needs to start at zero (the snapshot is written before it is read).
+ * Errors (nothing enqueued): TTT_EINVAL (as ttt_settle_chunk, and a snapshot larger than
+ * TTT_STATIC_SCRATCH_BYTES), TTT_ESTATE, TTT_EDEVICE (the array's address is unavailable). */
+#define TTT_STATIC_SCRATCH_BYTES (64ll << 20)
+ttt_status ttt_settle_chunk_noalloc(ttt_ctx* ctx, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
+                                    int32_t* committed);
+
 /* Copy the recorded losses l_t(W_{i-1}) of tokens [offset, offset + n) (counted from the
  * first token of the first prefill since creation or reset) into dst (device fp32 [n]).
  * These are the summands of [E2E] eq. (6), L = (1/T) sum_i sum_{t in chunk i} l_t(W_{i-1}):

@@ -52,6 +52,7 @@ SIGNATURES = {
     "ttt_snapshot": (c_int32, [c_void_p]),
     "ttt_restore": (c_int32, [c_void_p]),
     "ttt_settle_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
+    "ttt_settle_chunk_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
     "ttt_profile_enable": (c_int32, [c_void_p, ctypes.c_uint32]),
     "ttt_profile_period": (c_int32, [c_void_p, c_int32]),
     "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
@@ -278,6 +279,17 @@ class TTT:
         _check(self._lib.ttt_settle_chunk(self._ctx, c_void_p(_ptr(tokens)), c_void_p(_ptr(q)), q.numel() - 1,
                                           c_void_p(_ptr(A)), c_void_p(_ptr(kept))), "ttt_settle_chunk")
         return A, kept
+
+    def settle_noalloc(self, tokens, q, A, kept) -> None:
+        """settle() through ttt_settle_chunk_noalloc, into caller-provided outputs (A: device
+        fp32 [1], kept: device int32 [1]); the library allocates nothing for it."""
+        import torch
+        for t in (tokens, q):
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tokens and q must be contiguous int32 device tensors")
+        _check(self._lib.ttt_settle_chunk_noalloc(self._ctx, c_void_p(_ptr(tokens)), c_void_p(_ptr(q)),
+                                                  q.numel() - 1, c_void_p(_ptr(A)), c_void_p(_ptr(kept))),
+               "ttt_settle_chunk_noalloc")
 
     def decode_pending(self) -> int:
         return int(self._lib.ttt_decode_pending(self._ctx))

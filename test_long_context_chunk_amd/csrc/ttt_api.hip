@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/ttt.h: configuration checks, the device
 // memory plan, weight ingestion, and the chunk loop that enqueues the kernels.
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -132,6 +133,7 @@ struct ttt_ctx {
   float* settle_A = nullptr;
   int* settle_commit = nullptr;
   bool has_snap = false;
+  int dev = 0;  // the device current at creation (the stream's device)
   float *dec_h = nullptr, *dec_a = nullptr, *dec_z = nullptr, *dec_rmax = nullptr, *dec_rsum = nullptr;
   int* dec_ridx = nullptr;
   // decode with attention: the row's q | k | v [3d], the attention output [d] and the
@@ -948,9 +950,14 @@ void evaluate(ttt_ctx* c, const int32_t* q, int64_t nq, double* acc, float* loss
   }
 }
 
-// Copy the state a step changes (D, Wop, WtT of every fast tensor) into the snapshot, or back.
-void copy_state(ttt_ctx* c, bool to_snapshot) {
-  aux_join(c);  // no step may still be writing the state
+// Where a snapshot of the state a step changes (D, Wop, WtT of every fast tensor) lives.
+struct SnapSlots {
+  std::vector<char*> D, Wop, WtT;
+};
+
+// The context's own snapshot slot (allocated on first use).
+SnapSlots ctx_slots(ttt_ctx* c) {
+  SnapSlots s;
   for (FastTensor* f : c->fast) {
     const int64_t n = (int64_t)f->rows * f->cols;
     if (!f->snapD) {
@@ -958,17 +965,99 @@ void copy_state(ttt_ctx* c, bool to_snapshot) {
       f->snapWop = dalloc<char>(c, n * c->es);
       f->snapWtT = dalloc<char>(c, n * c->es);
     }
+    s.D.push_back((char*)f->snapD);
+    s.Wop.push_back((char*)f->snapWop);
+    s.WtT.push_back((char*)f->snapWtT);
+  }
+  return s;
+}
+
+// Copy the state into the slots, or back.
+void copy_state(ttt_ctx* c, const SnapSlots& s, bool to_snapshot) {
+  aux_join(c);  // no step may still be writing the state
+  for (size_t i = 0; i < c->fast.size(); ++i) {
+    FastTensor* f = c->fast[i];
+    const int64_t n = (int64_t)f->rows * f->cols;
     const hipMemcpyKind k = hipMemcpyDeviceToDevice;
     if (to_snapshot) {
-      check(hipMemcpyAsync(f->snapD, f->D, n * 4, k, c->st));
-      check(hipMemcpyAsync(f->snapWop, f->Wop, n * c->es, k, c->st));
-      check(hipMemcpyAsync(f->snapWtT, f->WtT, n * c->es, k, c->st));
+      check(hipMemcpyAsync(s.D[i], f->D, n * 4, k, c->st));
+      check(hipMemcpyAsync(s.Wop[i], f->Wop, n * c->es, k, c->st));
+      check(hipMemcpyAsync(s.WtT[i], f->WtT, n * c->es, k, c->st));
     } else {
-      check(hipMemcpyAsync(f->D, f->snapD, n * 4, k, c->st));
-      check(hipMemcpyAsync(f->Wop, f->snapWop, n * c->es, k, c->st));
-      check(hipMemcpyAsync(f->WtT, f->snapWtT, n * c->es, k, c->st));
+      check(hipMemcpyAsync(f->D, s.D[i], n * 4, k, c->st));
+      check(hipMemcpyAsync(f->Wop, s.Wop[i], n * c->es, k, c->st));
+      check(hipMemcpyAsync(f->WtT, s.WtT[i], n * c->es, k, c->st));
     }
   }
+}
+
+// The Settlement rule ([SGF], Settlement) for one candidate chunk, with the pre-candidate
+// state kept in the given slots: L(q, W); snapshot; the candidate chunk scored at W and
+// stepped to W + delta as in prefill; L(q, W + delta); A and the decision on the device; the
+// slots copied back unless the candidate is kept.
+void settle(ttt_ctx* c, const int32_t* tokens, const int32_t* q, int64_t nq, float* A, int32_t* committed,
+            const SnapSlots& s) {
+  evaluate(c, q, nq, c->eval_acc + 1, nullptr, nullptr);  // L(q, W)
+  copy_state(c, s, true);
+  run_chunk(c, tokens, 0, c->losses + c->pos, c->amax + c->pos, c->b, true, c->pos / c->b);
+  evaluate(c, q, nq, c->eval_acc + 2, nullptr, nullptr);  // L(q, W + delta)
+  check(run_settle_decide(c->st, c->eval_acc + 1, nq, c->settle_A, c->settle_commit, A, committed));
+  aux_join(c);
+  for (size_t i = 0; i < c->fast.size(); ++i) {
+    FastTensor* f = c->fast[i];
+    const int64_t n = (int64_t)f->rows * f->cols;
+    check(run_restore_unless(c->st, c->settle_commit, s.D[i], f->D, n * 4));
+    check(run_restore_unless(c->st, c->settle_commit, s.Wop[i], f->Wop, n * c->es));
+    check(run_restore_unless(c->st, c->settle_commit, s.WtT[i], f->WtT, n * c->es));
+  }
+}
+
+// ---- the library's static scratch, for callers that cannot allocate device memory.
+// One copy per GPU, alive until the process ends. Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept here.
+static __device__ __align__(256) char scratch[TTT_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+ttt_status scratch_address(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return TTT_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) {
+      (void)hipGetLastError();
+      return TTT_EDEVICE;
+    }
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return TTT_EDEVICE;
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return TTT_EDEVICE;
+    }
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TTT_OK;
+}
+
+inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Bytes of the static scratch a context's Settlement snapshot needs.
+int64_t static_settle_bytes(const ttt_ctx* c) {
+  int64_t total = 0;
+  for (const FastTensor* f : c->fast) {
+    const int64_t n = (int64_t)f->rows * f->cols;
+    total += align256(n * 4) + 2 * align256(n * c->es);
+  }
+  return total;
 }
 
 ttt_status read_sticky(ttt_ctx* c) {
@@ -1000,9 +1089,15 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   if (streams > 1 && (cfg->chunk % PAD || (int64_t)streams * cfg->chunk > ((int64_t)1 << 21))) return TTT_EINVAL;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return TTT_EDEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return TTT_EDEVICE;
+  }
   ttt_ctx* c = new (std::nothrow) ttt_ctx();
   if (!c) return TTT_ENOMEM;
   c->cfg = *cfg;
+  c->dev = dev;
   c->st = (hipStream_t)stream;
   c->prec = cfg->precision == TTT_BF16 ? PREC_BF16 : PREC_FP32;
   c->es = c->prec == PREC_BF16 ? 2 : 4;
@@ -1020,6 +1115,13 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   c->d = cfg->d_model;
   c->m = cfg->d_hidden;
   c->L = cfg->n_blocks;
+  // set-up of the static scratch on this device (its address is looked up once per device;
+  // the runtime may back the array with memory at that point, so it happens here and not in
+  // the entry point that must not allocate); a failure here only resurfaces in that entry point
+  {
+    char* unused = nullptr;
+    (void)scratch_address(dev, &unused);
+  }
   try {
     build(c, w, ext);
     check(hipStreamSynchronize(c->st));
@@ -1118,7 +1220,7 @@ ttt_status ttt_snapshot(ttt_ctx* c) {
   if (!c || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   try {
-    copy_state(c, true);
+    copy_state(c, ctx_slots(c), true);
   } catch (const HipFail& f) {
     c->sticky = f.s;
     return f.s;
@@ -1131,7 +1233,7 @@ ttt_status ttt_restore(ttt_ctx* c) {
   if (!c || c->nb != 1) return TTT_EINVAL;
   if (c->sticky != TTT_OK || !c->has_snap) return TTT_ESTATE;
   try {
-    copy_state(c, false);
+    copy_state(c, ctx_slots(c), false);
   } catch (const HipFail& f) {
     c->sticky = f.s;
     return f.s;
@@ -1145,20 +1247,39 @@ ttt_status ttt_settle_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* q,
   if (c->sticky != TTT_OK) return TTT_ESTATE;
   if (c->pos + c->b > c->cfg.max_tokens) return TTT_EINVAL;
   try {
-    evaluate(c, q, nq, c->eval_acc + 1, nullptr, nullptr);  // L(q, W)
-    copy_state(c, true);
-    c->has_snap = true;
-    // the candidate chunk: scored at W and stepped to W + delta, as in prefill
-    run_chunk(c, tokens, 0, c->losses + c->pos, c->amax + c->pos, c->b, true, c->pos / c->b);
-    evaluate(c, q, nq, c->eval_acc + 2, nullptr, nullptr);  // L(q, W + delta)
-    check(run_settle_decide(c->st, c->eval_acc + 1, nq, c->settle_A, c->settle_commit, A, committed));
-    aux_join(c);
-    for (FastTensor* f : c->fast) {
-      const int64_t n = (int64_t)f->rows * f->cols;
-      check(run_restore_unless(c->st, c->settle_commit, f->snapD, f->D, n * 4));
-      check(run_restore_unless(c->st, c->settle_commit, f->snapWop, f->Wop, n * c->es));
-      check(run_restore_unless(c->st, c->settle_commit, f->snapWtT, f->WtT, n * c->es));
-    }
+    const SnapSlots slots = ctx_slots(c);
+    c->has_snap = true;  // the slot holds W from here on (ttt_restore returns to it)
+    settle(c, tokens, q, nq, A, committed, slots);
+  } catch (const HipFail& f) {
+    c->sticky = f.s;
+    return f.s;
+  }
+  c->pos += c->b;
+  return TTT_OK;
+}
+
+ttt_status ttt_settle_chunk_noalloc(ttt_ctx* c, const int32_t* tokens, const int32_t* q, int64_t nq, float* A,
+                                    int32_t* committed) {
+  if (!c || !tokens || !q || nq <= 0 || nq % c->b || c->npend != 0 || c->nb != 1) return TTT_EINVAL;
+  if (c->sticky != TTT_OK) return TTT_ESTATE;
+  if (c->pos + c->b > c->cfg.max_tokens) return TTT_EINVAL;
+  if (static_settle_bytes(c) > (int64_t)TTT_STATIC_SCRATCH_BYTES) return TTT_EINVAL;
+  char* base = nullptr;
+  const ttt_status st = scratch_address(c->dev, &base);
+  if (st != TTT_OK) return st;
+  SnapSlots slots;
+  int64_t off = 0;
+  for (const FastTensor* f : c->fast) {
+    const int64_t n = (int64_t)f->rows * f->cols;
+    slots.D.push_back(base + off);
+    off += align256(n * 4);
+    slots.Wop.push_back(base + off);
+    off += align256(n * c->es);
+    slots.WtT.push_back(base + off);
+    off += align256(n * c->es);
+  }
+  try {
+    settle(c, tokens, q, nq, A, committed, slots);
   } catch (const HipFail& f) {
     c->sticky = f.s;
     return f.s;
