@@ -44,6 +44,28 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def device_peak() -> dict:
+    """The bf16 dense MFMA peak derived from the device itself: compute units x peak engine
+    clock x 4096 flop per clock and CU (gfx950: a 32x32x16 bf16 MFMA per SIMD every 8 x 4 clocks,
+    four SIMDs), beside the published 2.5 PFLOP/s."""
+    import ctypes
+    import torch
+    cus = int(torch.cuda.get_device_properties(0).multi_processor_count)
+    khz = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0 and 500_000 <= v.value <= 5_000_000:
+            khz = v.value  # hipDeviceAttributeClockRate: peak clock in kHz
+    except OSError:
+        pass
+    out = {"cus": cus, "flop_per_clk_per_cu": 4096, "published_tflops": PEAK_BF16 / 1e12}
+    if khz is not None:
+        out["max_engine_clock_mhz"] = khz / 1e3
+        out["device_tflops"] = cus * khz * 1e3 * 4096 / 1e12
+    return out
+
+
 def alg_flops_per_token(w) -> float:
     """Algorithmic flops per token: what the method must compute, no recompute.
 
@@ -80,6 +102,43 @@ def kind_flops_per_chunk(w, kind: str) -> float:
 KIND_KERNEL = {"up": "EpiGelu", "du": "EpiDU", "dw": "EpiGrad", "ce_fwd": "EpiCEPartial"}
 GEMM_SOURCES = ["test_long_context_chunk_amd/csrc/gemm.h", "test_long_context_chunk_amd/csrc/gemm_inst.hip",
                 "test_long_context_chunk_amd/csrc/common.h"]
+
+
+def split_k(M: int, N: int, K: int, K2: int) -> int:
+    """Split-K slabs the library gives a bf16 product on 256 x 128 tiles (256 workgroup slots,
+    at least 4 K-slices of 64 per slab, at most 8 slabs): host-side accounting only."""
+    tiles = -(-M // 256) * -(-N // 128)
+    return max(1, min(256 // tiles, (K + K2) // 64 // 4, 8))
+
+
+def hbm_kernel_bytes(w, kind: str) -> float:
+    """Bytes one launch of an HBM-bound kernel kind moves (reads + writes), from the shapes; the
+    split-K slabs the row kernels sum are counted. bf16 workloads (2-byte operands)."""
+    b, d, m, V, L = w.chunk, w.d_model, w.d_hidden, w.vocab, w.n_blocks
+    es = 2 if w.precision == "bf16" else 4
+    comp = w.precision == "bf16"  # the bf16 loss compensation keeps rounding residuals
+    nrec = -(-V // 64)
+    if kind == "update":  # per fast tensor: G, D read and written, W0, Wop, WtT
+        params = d * m
+        return float(params * (es + 8 + es + es + es))
+    if kind == "ce_prob":  # numerators read, dlogits written in place, one record per 64 columns
+        return float(2 * b * V * es + b * nrec * 4 + 2 * b * 4)
+    if kind == "gather":  # embedding rows in; residual, normed rows, their residual, scale out
+        return float(b * 4 + b * d * es + b * d * 4 + b * d * es + (b * d * es if comp else 0) + b * 4)
+    if kind == "residual":  # slabs and residual in; residual, next pre-norm (and residual) out
+        S = split_k(b, d, m, m if es == 2 else 0)
+        return float(S * b * d * 4 + b * d * 4 + b * d * 4 + b * d * es + (b * d * es if comp else 0) + b * 4)
+    if kind == "norm_bwd":  # slabs, normed rows, scale, residual gradient in; gradient out (fp32, bf16)
+        S = split_k(b, d, m, 0)
+        return float(S * b * d * 4 + b * d * es + b * 4 + b * d * 4 + (b * d * es if comp else 0) + b * d * 4 +
+                     b * d * es)
+    if kind == "dy_sum":  # slabs in; dY (fp32, bf16) out; H and its bf16 copy for the compensation
+        S = split_k(b, d, V, 0)
+        return float(S * b * d * 4 + b * d * 4 + b * d * es + ((b * d * 4 + b * d * es) if comp else 0))
+    return 0.0
+
+
+HBM_KINDS = ["update", "ce_prob", "gather", "residual", "norm_bwd", "dy_sum"]
 
 
 def gemm_sources_sha256() -> str:
@@ -146,9 +205,23 @@ def cpu_baseline(w, P, x, n_chunks: int):
 
 
 def decode_bytes_per_token(w) -> float:
-    """HBM bytes one decoded token reads: every weight the forward reads once (bf16: the fast
-    tensors as W0 and rn(D), two segments), plus the LM head; with the fuller block also the
-    static MLP, q|k|v and Wo, and the keys and values of a full window (hi and lo terms)."""
+    """Algorithmic HBM bytes of one decoded token: one copy, in the workload's precision, of
+    every weight the forward reads (the fast tensors as W = W0 + D), plus the LM head; with the
+    fuller block also the static MLP, q|k|v and Wo, and one copy of the keys and values of a full
+    window."""
+    es = 2 if w.precision == "bf16" else 4
+    dm = w.d_model * w.d_hidden * es
+    per_block = (2 * dm if w.mlp == "gelu" else 3 * dm)
+    ms = getattr(w, "static_hidden", 0)
+    per_block += 2 * w.d_model * ms * es
+    if getattr(w, "swa_window", 0) > 0:
+        per_block += 4 * w.d_model * w.d_model * es + 2 * w.swa_window * w.d_model * es
+    return float(w.n_blocks * per_block + w.vocab * w.d_model * es)
+
+
+def decode_impl_bytes_per_token(w) -> float:
+    """What this implementation reads per decoded token: the bf16 fast tensors as two segments
+    (W0 and rn(D)) and, with attention, the keys and values as hi and lo bf16 terms."""
     es = 2 if w.precision == "bf16" else 4
     segs = 2 if w.precision == "bf16" else 1
     dm = w.d_model * w.d_hidden * es
@@ -186,6 +259,7 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
     per_tok = per_block * w.n_blocks + 1
     traced_tokens = max(gemv_n // per_tok, 1)
     bpt = decode_bytes_per_token(w)
+    impl_bpt = decode_impl_bytes_per_token(w)
     gemv_s_per_tok = gemv_ms * 1e-3 / traced_tokens
     # the products are ~10 us launches, so an event bracket around each adds a large share of
     # dispatch time: the roofline uses the whole token's time instead (a lower bound on the
@@ -199,6 +273,8 @@ def decode_bench(ctx, w, x, P, cpu: bool) -> dict:
                      (" + attention over a full window)" if att else ")"),
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": None, "bytes_per_token": bpt,
+                     "impl_bytes_per_token": impl_bpt,
+                     "impl_achieved": impl_bpt / (dt / b) / 1e9,
                      "gemv_event_us_per_token": gemv_s_per_tok * 1e6, "gemv_launches_traced": gemv_n,
                      "kernel_name": "k_gemv"},
     }
@@ -424,16 +500,146 @@ def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2
         out["decode"] = dec
     if cpu:
         import oracle as O
-        eprint(f"[bench] timing the fp64 oracle on {cpu_chunks} chunks of e2e760m ...")
+        eprint(f"[bench] timing the fp64 oracle on {cpu_chunks} full-window chunks of e2e760m ...")
         model = O.Model.from_workload(w)
+        Pf = O.as_f64(P)
+        rng = np.random.default_rng(seed)
+        # a cache of window - 1 positions per block, as every chunk of the timed steps sees: its
+        # keys and values are synthetic (their values do not change the oracle's work)
+        kv = [dict(k=rng.standard_normal((w.swa_window - 1, w.d_model)),
+                   v=rng.standard_normal((w.swa_window - 1, w.d_model))) for _ in range(w.n_blocks)]
+        b = w.chunk
         t0 = time.perf_counter()
-        O.run_ttt(model, P, x[:cpu_chunks * w.chunk + 1])
+        for i in range(cpu_chunks):
+            _, st, _ = O.chunk_loss_and_grads(model, Pf, x[i * b:i * b + b], x[i * b + 1:i * b + b + 1], kv=kv)
+            kv = st["kv"]
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": cpu_chunks * w.chunk / dt, "unit": "tokens/s", "cores": cpu_cores(),
+        out["cpu_baseline"] = {"value": cpu_chunks * b / dt, "unit": "tokens/s", "cores": cpu_cores(),
                                "kind": "oracle",
-                               "sample": f"first {cpu_chunks} chunks ({cpu_chunks * w.chunk} tokens) of the same "
-                                         f"stream, fp64 numpy, {dt:.1f} s (early chunks see fewer keys)"}
+                               "sample": f"{cpu_chunks} chunks ({cpu_chunks * b} tokens) at a full window: the oracle's "
+                                         f"chunk step (forward, loss, gradients) with a cache of {w.swa_window - 1} "
+                                         f"earlier positions per block, fp64 numpy, {dt:.1f} s"}
     return out
+
+
+def workload_bench(w, P, x, steps: int, warmup: int, keep_ctx: bool = False, seed: int = 0):
+    """Whole-stream prefill steps of workload w: tokens/s, the fraction of the bf16 peak in
+    algorithmic flops, the dominant GEMM kind's roofline (HIP events on the library stream, every
+    PROFILE_PERIOD-th chunk of the timed steps), and the bandwidth of the HBM-bound kernel kinds
+    (events around every launch of one untimed traced step)."""
+    import numpy as np
+    import torch
+    import test_long_context_chunk_amd as ttt
+    T = w.n_tokens
+    eprint(f"[bench] workload {w.name}: V={w.vocab} d={w.d_model} m={w.d_hidden} L={w.n_blocks} "
+           f"mlp={w.mlp} norm={w.norm} T={T} b={w.chunk} {w.precision}")
+    dev = {k: ttt.to_device(v, w.precision) for k, v in P.items()}
+    total_steps = warmup + steps + 2
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * total_steps)
+    del dev
+    tok = torch.from_numpy(x.astype(np.int32)).cuda()
+    torch.cuda.synchronize()
+
+    # untimed: one step with every kernel kind traced -> breakdown and the dominant kind
+    ctx.profile(ttt._binding.KERNEL_KINDS)
+    ctx.prefill(tok)
+    prof = ctx.profile_read()
+    ctx.profile([])
+    tot = sum(v[0] for k, v in prof.items() if k != "update")
+    eprint(f"[bench] {w.name}: per-kind time of one traced step (events around every launch; the SGD steps run "
+           f"beside the main stream and are listed apart):")
+    for k, (ms, n) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
+        f = kind_flops_per_chunk(w, k) * w.n_chunks
+        rate = f / (ms * 1e-3) / 1e12 if f > 0 and ms > 0 else 0.0
+        by = hbm_kernel_bytes(w, k) * n
+        bw = by / (ms * 1e-3) / 1e9 if by > 0 and ms > 0 else 0.0
+        eprint(f"  {k:10s} {ms:9.3f} ms {100 * ms / tot if k != 'update' else 0.0:5.1f}%  {n:5d} launches  "
+               f"{rate:8.1f} TFLOP/s {bw:8.1f} GB/s")
+    hbm = {}
+    for k in HBM_KINDS:
+        ms, n = prof.get(k, (0.0, 0))
+        by = hbm_kernel_bytes(w, k)
+        if n > 0 and ms > 0 and by > 0:
+            gbs = by * n / (ms * 1e-3) / 1e9
+            hbm[k] = {"bytes_per_launch": by, "avg_launch_us": ms * 1e3 / n, "achieved": gbs, "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "launches": n}
+    gemm_kinds = {k: v for k, v in prof.items() if kind_flops_per_chunk(w, k) > 0}
+    dom = max(gemm_kinds, key=lambda k: gemm_kinds[k][0])
+
+    for _ in range(warmup):
+        ctx.prefill(tok)
+    torch.cuda.synchronize()
+
+    # timed: exactly `steps` steps; only the dominant kind is bracketed by events, in every
+    # PROFILE_PERIOD-th chunk (each event costs a few microseconds of stream time)
+    ctx.profile([dom], period=PROFILE_PERIOD)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx.prefill(tok)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dprof = ctx.profile_read()
+    ctx.profile([])
+    status = ctx.sync()
+    if status != 0:
+        eprint(f"[bench] library reported status {status}")
+        sys.exit(1)
+    losses = ctx.token_losses(T * (total_steps - steps - 2 + 1), 8).cpu().numpy()
+    if not np.all(np.isfinite(losses)):
+        eprint("[bench] non-finite losses")
+        sys.exit(1)
+
+    tokens_per_s = steps * T / elapsed
+    fpt = alg_flops_per_token(w)
+    dom_ms, dom_n = dprof.get(dom, (0.0, 0))
+    # launches of that kind per chunk, from the untimed step where every chunk was traced
+    launches_per_chunk = max(1, round(prof[dom][1] / w.n_chunks))
+    per_launch = kind_flops_per_chunk(w, dom) / launches_per_chunk
+    avg_s = dom_ms * 1e-3 / max(dom_n, 1)
+    achieved = per_launch / avg_s / 1e12 if avg_s > 0 else 0.0
+    peak = (PEAK_BF16 if w.precision == "bf16" else PEAK_FP32) / 1e12
+    eprint(f"[bench] {w.name}: {tokens_per_s:.0f} tokens/s, {elapsed / steps * 1e3:.2f} ms per step; {dom} "
+           f"{avg_s * 1e6:.1f} us per launch, {achieved:.1f} TFLOP/s")
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": elapsed / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.precision,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.n_blocks} x {'pre-RMSNorm ' if w.norm == 'rms' else ''}"
+                        f"{'GELU' if w.mlp == 'gelu' else 'SwiGLU(W2 fast)'} block, d={w.d_model}, "
+                        f"m={w.d_hidden}, V={w.vocab}",
+            "tokens_per_step": T, "chunk": w.chunk, "lr": w.lr, "clip": w.clip,
+            "stream": f"Zipf(1.1) + sparse Markov, seed {seed}",
+        },
+        "frac_of_bf16_peak": tokens_per_s * fpt / PEAK_BF16,
+        "alg_flops_per_token": fpt,
+        "roofline": {
+            "bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": measured_traffic(w.name, dom),
+            "alg_flops_per_launch": per_launch, "avg_launch_us": avg_s * 1e6, "launches": dom_n,
+            "kernel_name": KIND_KERNEL.get(dom, "EpiStoreF32"),
+        },
+        "hbm_kernels": hbm,
+    }
+    if keep_ctx:
+        return out, ctx
+    ctx.close()
+    return out
+
+
+# The other workloads of the survey's table, measured beside the headline: name, oracle chunks
+# timed for their CPU baseline (about 2 - 10 s each on 16 host cores).
+OTHER_WORKLOADS = [("single", 8), ("s125m", 16), ("inplace", 4)]
 
 
 def main():
@@ -451,6 +657,8 @@ def main():
     ap.add_argument("--streams", type=int, default=8,
                     help="independent streams of the batched measurement (0: skip it)")
     ap.add_argument("--no-e2e", action="store_true", help="skip the fuller-block (attention) measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (single block, 125M-style stack, In-Place shape)")
     ap.add_argument("--only", choices=["batch", "e2e"], default=None,
                     help="run only that measurement and print its object as the line (for kernel traces)")
     args = ap.parse_args()
@@ -477,96 +685,10 @@ def main():
                                      args.warmup)), flush=True)
         return
     w = W.preset(args.workload)
-    T = w.n_tokens
-    eprint(f"[bench] workload {w.name}: V={w.vocab} d={w.d_model} m={w.d_hidden} L={w.n_blocks} "
-           f"mlp={w.mlp} norm={w.norm} T={T} b={w.chunk} {w.precision}")
     x = W.token_stream(w, args.seed)
     P = W.init_weights(w, args.seed)
-    dev = {k: ttt.to_device(v, w.precision) for k, v in P.items()}
-    total_steps = args.warmup + args.steps + 2
-    ctx = ttt.TTT.from_workload(w, dev, max_tokens=T * total_steps)
-    del dev
-    tok = torch.from_numpy(x.astype(np.int32)).cuda()
-    torch.cuda.synchronize()
-
-    # untimed: one step with every kernel kind traced -> breakdown and the dominant kind
-    ctx.profile(ttt._binding.KERNEL_KINDS)
-    ctx.prefill(tok)
-    prof = ctx.profile_read()
-    ctx.profile([])
-    tot = sum(v[0] for v in prof.values())
-    eprint("[bench] per-kind time of one traced step (events around every launch):")
-    for k, (ms, n) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
-        f = kind_flops_per_chunk(w, k) * w.n_chunks
-        rate = f / (ms * 1e-3) / 1e12 if f > 0 and ms > 0 else 0.0
-        eprint(f"  {k:10s} {ms:9.3f} ms {100 * ms / tot:5.1f}%  {n:5d} launches  {rate:8.1f} TFLOP/s")
-    gemm_kinds = {k: v for k, v in prof.items() if kind_flops_per_chunk(w, k) > 0}
-    dom = max(gemm_kinds, key=lambda k: gemm_kinds[k][0])
-
-    for _ in range(args.warmup):
-        ctx.prefill(tok)
-    torch.cuda.synchronize()
-
-    # timed: exactly `steps` steps; only the dominant kind is bracketed by events, in every
-    # PROFILE_PERIOD-th chunk (each event costs a few microseconds of stream time)
-    ctx.profile([dom], period=PROFILE_PERIOD)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        ctx.prefill(tok)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    dprof = ctx.profile_read()
-    ctx.profile([])
-    status = ctx.sync()
-    if status != 0:
-        eprint(f"[bench] library reported status {status}")
-        sys.exit(1)
-    losses = ctx.token_losses(T * (total_steps - args.steps - 2 + 1), 8).cpu().numpy()
-    if not np.all(np.isfinite(losses)):
-        eprint("[bench] non-finite losses")
-        sys.exit(1)
-
-    tokens_per_s = args.steps * T / elapsed
-    fpt = alg_flops_per_token(w)
-    frac_peak = tokens_per_s * fpt / PEAK_BF16
-    dom_ms, dom_n = dprof.get(dom, (0.0, 0))
-    # launches of that kind per chunk, from the untimed step where every chunk was traced
-    launches_per_chunk = max(1, round(prof[dom][1] / w.n_chunks))
-    per_launch = kind_flops_per_chunk(w, dom) / launches_per_chunk
-    avg_s = dom_ms * 1e-3 / max(dom_n, 1)
-    achieved = per_launch / avg_s / 1e12 if avg_s > 0 else 0.0
-    peak = (PEAK_BF16 if w.precision == "bf16" else PEAK_FP32) / 1e12
-
-    out = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": elapsed / args.steps * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.precision,
-        "data": "synthetic",
-        "config": {
-            "workload": f"{w.name}: {w.n_blocks} x {'pre-RMSNorm ' if w.norm == 'rms' else ''}"
-                        f"{'GELU' if w.mlp == 'gelu' else 'SwiGLU(W2 fast)'} block, d={w.d_model}, "
-                        f"m={w.d_hidden}, V={w.vocab}",
-            "tokens_per_step": T, "chunk": w.chunk, "lr": w.lr, "clip": w.clip,
-            "stream": f"Zipf(1.1) + sparse Markov, seed {args.seed}",
-        },
-        "frac_of_bf16_peak": frac_peak,
-        "alg_flops_per_token": fpt,
-        "roofline": {
-            "bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": measured_traffic(args.workload, dom),
-            "alg_flops_per_launch": per_launch, "avg_launch_us": avg_s * 1e6, "launches": dom_n,
-            "kernel_name": KIND_KERNEL.get(dom, "EpiStoreF32"),
-        },
-    }
+    out, ctx = workload_bench(w, P, x, args.steps, args.warmup, keep_ctx=True, seed=args.seed)
+    out["device_peak"] = device_peak()
     if not args.no_decode:
         out["decode"] = decode_bench(ctx, w, x, P, cpu=not args.no_cpu_baseline)
     if not args.no_settle:
@@ -576,6 +698,18 @@ def main():
         out["batch"] = batch_bench(w, P, args.seed, args.streams, args.steps, args.warmup)
     if not args.no_e2e:
         out["e2e"] = e2e_bench(args.steps, args.warmup, args.seed, cpu=not args.no_cpu_baseline)
+    if not args.no_configs:
+        out["configs"] = {}
+        for name, cchunks in OTHER_WORKLOADS:
+            wo = W.preset(name)
+            xo, Po = W.token_stream(wo, args.seed), W.init_weights(wo, args.seed)
+            o = workload_bench(wo, Po, xo, args.steps, args.warmup, seed=args.seed)
+            for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
+                o.pop(key, None)
+            if not args.no_cpu_baseline:
+                eprint(f"[bench] timing the fp64 oracle on {cchunks} chunks of {name} ...")
+                o["cpu_baseline"] = cpu_baseline(wo, Po, xo, cchunks)
+            out["configs"][name] = o
     if not args.no_cpu_baseline:
         eprint(f"[bench] timing the fp64 oracle on {args.cpu_chunks} chunks ...")
         out["cpu_baseline"] = cpu_baseline(w, P, x, args.cpu_chunks)

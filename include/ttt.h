@@ -333,7 +333,8 @@ typedef enum {
   TTT_K_DHN = 13,      /* dU W1^T GEMM (split-K partials)                    */
   TTT_K_NORM_BWD = 14, /* norm backward into the residual gradient           */
   TTT_K_GRADNORM = 15, /* global gradient norm and clip scale                */
-  TTT_K_UPDATE = 16,   /* clipped SGD step of one fast tensor                */
+  TTT_K_UPDATE = 16,   /* clipped SGD step of one fast tensor (bracketed on
+                          the library's second stream, beside the main one)  */
   TTT_K_DEC_GEMV = 17, /* decode: one-row products with the weights         */
   TTT_K_ATTN = 18,     /* sliding-window attention forward (online softmax)  */
   TTT_K_ATTN_BWD = 19, /* sliding-window attention backward (dQ, dK, dV)     */

@@ -50,6 +50,47 @@ __device__ __forceinline__ float4 rounded4(const float4 v) {
   return make_float4(to_f<T>(from_f<T>(v.x)), to_f<T>(from_f<T>(v.y)), to_f<T>(from_f<T>(v.z)), to_f<T>(from_f<T>(v.w)));
 }
 
+// Sum of the S split-K slabs of 4 consecutive elements, in split order. For the slab counts
+// the planner uses (1 .. 8) every slab's load is issued before the first add, so a thread has
+// all of them in flight at once; the sum order is the same either way.
+template <int S>
+__device__ __forceinline__ float4 slab_sum4_n(const float* __restrict__ part, int64_t pstride, int64_t i) {
+  float4 p[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) p[s] = *(const float4*)(part + (int64_t)s * pstride + i);
+  float4 acc = p[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) {
+    acc.x += p[s].x;
+    acc.y += p[s].y;
+    acc.z += p[s].z;
+    acc.w += p[s].w;
+  }
+  return acc;
+}
+__device__ __forceinline__ float4 slab_sum4(const float* __restrict__ part, int S, int64_t pstride, int64_t i) {
+  switch (S) {
+    case 1: return slab_sum4_n<1>(part, pstride, i);
+    case 2: return slab_sum4_n<2>(part, pstride, i);
+    case 3: return slab_sum4_n<3>(part, pstride, i);
+    case 4: return slab_sum4_n<4>(part, pstride, i);
+    case 5: return slab_sum4_n<5>(part, pstride, i);
+    case 6: return slab_sum4_n<6>(part, pstride, i);
+    case 7: return slab_sum4_n<7>(part, pstride, i);
+    case 8: return slab_sum4_n<8>(part, pstride, i);
+    default: break;
+  }
+  float4 acc = *(const float4*)(part + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 p = *(const float4*)(part + (int64_t)s * pstride + i);
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  return acc;
+}
+
 // a1 + a2, a4 + a2: the residual stream entering block l and its pre-norm.
 //   gather (tokens non-null, [E2E] eq. 1: f reads x_{t-1}): h = E_in[x_{t-1}]; ids outside
 //     [0, V) raise the sticky range bit and read row 0; the clamped conditioning and target
@@ -96,14 +137,7 @@ __global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, S
     if (src) {
       h = load4<T>(src + (g << 2));
     } else {
-      float4 acc = *(const float4*)(part + i);
-      for (int s = 1; s < S; ++s) {
-        const float4 p = *(const float4*)(part + (int64_t)s * pstride + i);
-        acc.x += p.x;
-        acc.y += p.y;
-        acc.z += p.z;
-        acc.w += p.w;
-      }
+      const float4 acc = slab_sum4(part, S, pstride, i);
       h = *(const float4*)(H + i);
       h.x += acc.x;
       h.y += acc.y;
@@ -147,18 +181,6 @@ __global__ void __launch_bounds__(NT) k_row_in(const int* __restrict__ tokens, S
   }
 }
 
-// Sum of the S split-K slabs of 4 consecutive elements, in split order.
-__device__ __forceinline__ float4 slab_sum4(const float* __restrict__ part, int S, int64_t pstride, int64_t i) {
-  float4 acc = *(const float4*)(part + i);
-  for (int s = 1; s < S; ++s) {
-    const float4 p = *(const float4*)(part + (int64_t)s * pstride + i);
-    acc.x += p.x;
-    acc.y += p.y;
-    acc.z += p.z;
-    acc.w += p.w;
-  }
-  return acc;
-}
 
 // a6 finish: dY = sum_s part[s] (fixed order) into dH and its GEMM-precision copy. With
 // Hres (the fp32 hidden state whose rounded copy Yb fed the LM head), also
@@ -785,6 +807,88 @@ __global__ void __launch_bounds__(NT) k_update(const T* __restrict__ G, float* _
   }
 }
 
+// a9 for bf16 tensors with C a multiple of 8: the same step with 16-byte accesses throughout.
+// A block owns a 64 x 64 tile; thread t updates rows 2p, 2p + 1 (p = t / 8) at columns
+// 8 (t % 8) .. + 7. The transposed copy goes through LDS as row pairs packed into dwords,
+// [column][row pair] with a row stride of 33 dwords: for each column offset q the 64 lanes of
+// a wave write 64 distinct banks (8 (t % 8) + t / 8 + 33 q mod 64), and each transposed
+// row piece leaves as 16 bytes.
+__device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+__global__ void __launch_bounds__(NT) k_update_bf16x8(const bf16_t* __restrict__ G, float* __restrict__ D,
+                                                      const bf16_t* __restrict__ W0, bf16_t* __restrict__ Wop,
+                                                      bf16_t* __restrict__ WtT, int R, int C, float lr,
+                                                      const float* __restrict__ sc, int delta_t) {
+  {
+    const int64_t zo = (int64_t)blockIdx.z * R * C;
+    G += zo;
+    D += zo;
+    Wop += zo;
+    WtT += zo;
+    sc += 4 * blockIdx.z;
+  }
+  if (sc[1] != 0.f) return;  // non-finite gradient norm: no step for this chunk
+  const float step = lr * sc[0];
+  constexpr int LDT = 33;                 // dwords per transposed row (32 row pairs + 1)
+  __shared__ uint32_t tile[64 * LDT];     // [column][row pair]
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int cg = threadIdx.x & 7, p = threadIdx.x >> 3;  // p in 0..31
+  const int c = c0 + 8 * cg;
+  float wt[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + 2 * p + h;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) wt[h][q] = 0.f;
+    if (r >= R || c >= C) continue;
+    const int64_t i = (int64_t)r * C + c;
+    float g[8], w0[8];
+    unpack8_bf16(*(const uint4*)(G + i), g);
+    unpack8_bf16(*(const uint4*)(W0 + i), w0);
+    const float4 da = *(const float4*)(D + i), db = *(const float4*)(D + i + 4);
+    const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+    float dn[8], wv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      dn[q] = d8[q] - step * g[q];
+      wv[q] = w0[q] + dn[q];
+      wt[h][q] = delta_t ? dn[q] : wv[q];
+    }
+    *(float4*)(D + i) = make_float4(dn[0], dn[1], dn[2], dn[3]);
+    *(float4*)(D + i + 4) = make_float4(dn[4], dn[5], dn[6], dn[7]);
+    *(uint4*)(Wop + i) = pack8_bf16(wv);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) tile[(8 * cg + q) * LDT + p] = pack_bf16x2(wt[0][q], wt[1][q]);
+  __syncthreads();
+  // transposed rows WtT[c][r0 .. r0 + 63]: 64 columns x 8 pieces of 16 bytes (4 row pairs)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = threadIdx.x + k * NT;
+    const int cl = idx >> 3, j = idx & 7;
+    const int cc = c0 + cl, r = r0 + 8 * j;
+    if (cc >= C || r >= R) continue;
+    const uint32_t* src = tile + cl * LDT + 4 * j;
+    bf16_t* dst = WtT + (int64_t)cc * R + r;
+    if ((R % 8) == 0) {
+      *(uint4*)dst = make_uint4(src[0], src[1], src[2], src[3]);
+    } else {
+      for (int q = 0; q < 8 && r + q < R; ++q) dst[q] = (bf16_t)((src[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+    }
+  }
+}
+
 template <class T>
 __global__ void __launch_bounds__(NT) k_export(const float* __restrict__ D, const T* __restrict__ W0, int64_t n,
                                                int kind, float* __restrict__ dst) {
@@ -881,6 +985,11 @@ hipError_t run_update(hipStream_t st, int prec, const void* G, float* D, const v
                       int C, float lr, const float* sc, int delta_t, int streams) {
   if (streams < 1 || streams > 65535) return hipErrorInvalidValue;
   dim3 grid((C + 63) / 64, (R + 63) / 64, streams);
+  if (prec == PREC_BF16 && C % 8 == 0 && R % 2 == 0) {
+    hipLaunchKernelGGL(k_update_bf16x8, grid, dim3(NT), 0, st, (const bf16_t*)G, D, (const bf16_t*)W0, (bf16_t*)Wop,
+                       (bf16_t*)WtT, R, C, lr, sc, delta_t);
+    return hipGetLastError();
+  }
   DISPATCH_T(prec, hipLaunchKernelGGL(k_update<T>, grid, dim3(NT), 0, st, (const T*)G, D, (const T*)W0, (T*)Wop,
                                       (T*)WtT, R, C, lr, sc, delta_t));
   return hipGetLastError();

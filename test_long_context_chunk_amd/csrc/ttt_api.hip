@@ -554,26 +554,28 @@ void release_aux_stream(ttt_ctx* c) {
     }
 }
 
-void prof_mark(ttt_ctx* c) {
+void prof_mark(ttt_ctx* c, hipStream_t st) {
   if (c->ev_used == c->ev_pool.size()) {
     hipEvent_t e;
     check(hipEventCreateWithFlags(&e, hipEventReleaseToDevice));
     c->ev_pool.push_back(e);
   }
-  check(hipEventRecord(c->ev_pool[c->ev_used++], c->st));
+  check(hipEventRecord(c->ev_pool[c->ev_used++], st));
 }
 
-// Enqueue one launch; bracket it with events when its kind is traced.
-#define RUN(kind, expr)                         \
+// Enqueue one launch on stream `st`; bracket it with events on that stream when its kind is
+// traced.
+#define RUN_ON(kind, st_, expr)                 \
   do {                                          \
     const bool traced_ = c->prof_on && ((c->prof_mask >> (kind)) & 1u); \
-    if (traced_) prof_mark(c);                  \
+    if (traced_) prof_mark(c, (st_));           \
     check(expr);                                \
     if (traced_) {                              \
-      prof_mark(c);                             \
+      prof_mark(c, (st_));                      \
       c->ev_kind.push_back(kind);               \
     }                                           \
   } while (0)
+#define RUN(kind, expr) RUN_ON(kind, c->st, expr)
 
 // One chunk of [E2E] eq. (5): forward at W_{i-1}, record l_t(W_{i-1}) (eq. 6) into loss_out
 // and the argmax into amax_out, backward to every fast tensor, global-norm clip ([SGF]), SGD
@@ -851,8 +853,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
   if (!c->fast.empty()) {
     aux_fork(c);
     for (FastTensor* f : c->fast) {
-      check(run_update(c->aux, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols, c->cfg.lr, c->sc,
-                       bf ? 1 : 0, nb));
+      RUN_ON(TTT_K_UPDATE, c->aux, run_update(c->aux, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols,
+                                              c->cfg.lr, c->sc, bf ? 1 : 0, nb));
       check(hipEventRecord(f->ev_upd, c->aux));
     }
     aux_mark(c);
@@ -1404,6 +1406,7 @@ ttt_status ttt_profile_read(ttt_ctx* c, double* total_ms, int64_t* launches) {
   }
   try {
     check(hipStreamSynchronize(c->st));
+    if (c->aux) check(hipStreamSynchronize(c->aux));  // the SGD steps are traced on the aux stream
     for (size_t p = 0; p < c->ev_kind.size(); ++p) {
       float ms = 0.f;
       check(hipEventElapsedTime(&ms, c->ev_pool[2 * p], c->ev_pool[2 * p + 1]));

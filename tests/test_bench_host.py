@@ -15,16 +15,28 @@ def test_step_flops_per_token_at_the_760m_shape():
 
 
 def test_decode_bytes_per_token():
-    """One decoded token reads each weight once: bf16 fast tensors as two terms (W0, rn(D)),
-    the LM head, and for the fuller block the static MLP, [Wq Wk Wv], Wo and a full window of
-    keys and values (hi and lo terms)."""
+    """The method reads each weight once per decoded token, in one bf16 copy: the fast tensors
+    W1 and W2 of every block, the LM head, and for the fuller block the static MLP, [Wq Wk Wv],
+    Wo and one copy of a full window's keys and values (about 211 MB and 419 MB)."""
     d, m, V = 1536, 6144, 32000
-    fast = 2 * (2 * d * m * 2)  # W1 and W2, two bf16 terms each
-    assert bench.decode_bytes_per_token(W.preset("s760m")) == 3 * fast + V * d * 2 == 324796416
+    fast = 2 * (d * m * 2)  # W1 and W2, one bf16 copy each
+    assert bench.decode_bytes_per_token(W.preset("s760m")) == 3 * fast + V * d * 2 == 211550208
+    w = W.preset("e2e760m")
+    d, m, ms, k = w.d_model, w.d_hidden, w.static_hidden, w.swa_window
+    per_block = 2 * (d * m * 2) + 2 * d * ms * 2 + 4 * d * d * 2 + 2 * k * d * 2
+    assert bench.decode_bytes_per_token(w) == 3 * per_block + w.vocab * d * 2 == 419168256
+
+
+def test_decode_implementation_bytes_per_token():
+    """What the implementation reads besides: bf16 fast tensors as two terms (W0, rn(D)) and the
+    keys and values as hi and lo terms."""
+    d, m, V = 1536, 6144, 32000
+    fast = 2 * (2 * d * m * 2)
+    assert bench.decode_impl_bytes_per_token(W.preset("s760m")) == 3 * fast + V * d * 2 == 324796416
     w = W.preset("e2e760m")
     d, m, ms, k = w.d_model, w.d_hidden, w.static_hidden, w.swa_window
     per_block = 2 * (2 * d * m * 2) + 2 * d * ms * 2 + 4 * d * d * 2 + 4 * k * d * 2
-    assert bench.decode_bytes_per_token(w) == 3 * per_block + w.vocab * d * 2 == 626786304
+    assert bench.decode_impl_bytes_per_token(w) == 3 * per_block + w.vocab * d * 2 == 626786304
 
 
 def test_visible_keys_brute_force():
