@@ -240,19 +240,21 @@ def test_attention_settlement_matches_oracle(ttt_lib, lr, expect):
     """One prefilled chunk, then a candidate chunk under the Settlement rule with the passage
     = its own text (kept at a moderate rate, rejected at an overshooting one), then one more
     prefilled chunk. A twin context prefills the candidate instead, which gives the GPU's own
-    W and W + delta (the candidate's step is the prefill step, bit for bit). Checks: the
-    oracle's settle_step from the stream's cache takes the same decision; A equals the
-    oracle's L(q, W) - L(q, W + delta) at the GPU's two weight sets within the A gate of
-    tests/test_gpu_settle.py (the step's own error is left to the update gate: at an
-    overshooting rate A magnifies it); the state after the decision is the twin's W + delta
-    or W bit for bit; and the next chunk's losses (which read the candidate's keys either way)
-    match the oracle's."""
+    W and W + delta (the candidate's step is the prefill step, bit for bit), and scores the
+    passage at each. Checks: the oracle's settle_step from the stream's cache takes the same
+    decision; A is the difference of the GPU's own passage means at W and W + delta; those
+    passage losses match the oracle's at the GPU's two weight sets, token by token, within the
+    bf16 loss gate (the step's own error is left to the update gate: at an overshooting rate
+    A magnifies it); the state after the decision is the twin's W + delta or W bit for bit;
+    and the next chunk's losses (which read the candidate's keys either way) match the
+    oracle's."""
     import test_long_context_chunk_amd as ttt
     w = W.preset("e2e760m", **dict(SETTLE, lr=lr))
     P = W.init_weights(w, 21)
     x = W.token_stream(w, 22)
     b = w.chunk
     dev = device_weights(P, "bf16")
+    cand = x[b:2 * b + 1]
 
     def state(ctx, kind):
         return {f"{k}.{l}": ctx.fast_weight(l, k, kind).cpu().numpy().astype(np.float64)
@@ -260,13 +262,14 @@ def test_attention_settlement_matches_oracle(ttt_lib, lr, expect):
     twin = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens, lr=lr)
     twin.prefill(_tok(x[:b + 1]))
     W1g, D1g = state(twin, "W"), state(twin, "delta")
-    twin.prefill(_tok(x[b:2 * b + 1]))
+    E1 = twin.evaluate(_tok(cand))[0].cpu().numpy().astype(np.float64)
+    twin.prefill(_tok(cand))
     W2g, D2g = state(twin, "W"), state(twin, "delta")
+    E2 = twin.evaluate(_tok(cand))[0].cpu().numpy().astype(np.float64)
     assert twin.sync() == 0
     twin.close()
     ctx = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens, lr=lr)
     ctx.prefill(_tok(x[:b + 1]))
-    cand = x[b:2 * b + 1]
     A, kept = ctx.settle(_tok(cand), _tok(cand))
     A, kept = float(A.cpu().numpy()[0]), int(kept.cpu().numpy()[0])
     Dg = state(ctx, "delta")
@@ -280,14 +283,20 @@ def test_attention_settlement_matches_oracle(ttt_lib, lr, expect):
     W1 = {**Pf, **one.weights}
     A_o, keep_o, Wn, _, _ = O.settle_step(model, W1, cand, cand, kv=one.kv)
     assert int(keep_o) == expect
-    A_g = O.passage_loss(model, {**Pf, **W1g}, cand) - O.passage_loss(model, {**Pf, **W2g}, cand)
+    t1, _, _ = O.token_losses(model, {**Pf, **W1g}, cand[:-1], cand[1:])
+    t2, _, _ = O.token_losses(model, {**Pf, **W2g}, cand[:-1], cand[1:])
+    A_g = float(np.mean(t1) - np.mean(t2))
+    A_e = float(np.mean(E1) - np.mean(E2))
     kv = O.chunk_loss_and_grads(model, W1, cand[:-1], cand[1:], kv=one.kv)[1]["kv"]
     lo, _, _ = O.token_losses(model, {**W1, **Wn}, x[2 * b:3 * b], x[2 * b + 1:3 * b + 1], kv=kv)
-    tol = 2e-4 + 1e-3 * abs(A_g)
     dl = float(np.max(np.abs(nxt - lo)))
-    log(f"[attention settle lr={lr}] A {A:.6g} vs {A_g:.6g} at the GPU's weights ({A_o:.6g} oracle's) "
+    d1, d2 = float(np.max(np.abs(E1 - t1))), float(np.max(np.abs(E2 - t2)))
+    log(f"[attention settle lr={lr}] A {A:.6g} vs {A_e:.6g} from the GPU's passage scores, {A_g:.6g} oracle's at "
+        f"the GPU's weights ({A_o:.6g} oracle's own); passage losses at W {d1:.3g}, at W + delta {d2:.3g}; "
         f"kept {kept} next-chunk losses {dl:.3g}")
-    assert abs(A - A_g) <= tol and abs(A_g) > tol
+    assert abs(A - A_e) <= 1e-6 * (1.0 + abs(A_e))
+    assert d1 <= TOL["bf16"]["loss"] and d2 <= TOL["bf16"]["loss"]
+    assert (A_g >= 0) == bool(expect) and (A >= 0) == bool(expect)
     assert kept == expect
     after = D2g if kept else D1g
     for k in Dg:
