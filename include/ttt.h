@@ -149,8 +149,9 @@ int32_t ttt_streams(const ttt_ctx* ctx);
  * q = n Wq, k = n Wk, v = n Wv, softmax(q.k / sqrt(128)) over the keys of the last k
  * positions up to the query's own (no positional encoding), output o Wo. Each position's key
  * and value are computed once, at the weights of the chunk (or the decoded token) that first
- * processes it, and kept in a ring of k + chunk positions per block and stream, hi and lo
- * bf16 terms (8 (k + chunk) d bytes); later chunks read them as constants. A single-stream
+ * processes it, and kept in a ring of k + chunk positions per block and stream, in half
+ * precision (read by the forward and decode) and in bf16 (read by the backward): 8 (k +
+ * chunk) d bytes; later chunks read them as constants. A single-stream
  * context keeps a second set of rings for passages: ttt_evaluate scores a passage as a
  * sequence of its own (its positions attend only within it) and leaves the stream's rings as
  * they are ([SGF], Settlement: the two scores leave the attention unchanged). Snapshots hold
@@ -213,7 +214,8 @@ ttt_status ttt_prefill_batch(ttt_ctx* ctx, const int32_t* tokens, int64_t ld_tok
  * segments, as in the forward GEMMs), so their losses carry no operand rounding. Ids out of
  * range raise the sticky TTT_ERANGE and read id 0. n = 0 is a no-op. With attention, each
  * prediction's key and value join the stream's rings at its position before it attends over
- * the window (fp32 scores over the rings' hi + lo terms); a filled chunk's step re-files the
+ * the window (fp32 arithmetic over the rings' half-precision keys and values); a filled
+ * chunk's step re-files the
  * chunk's keys and values from its own forward pass, as prefill would.
  * Errors (nothing enqueued): TTT_EINVAL (n < 0, NULL tokens, capacity, a batched context),
  * TTT_ESTATE. */

@@ -2,17 +2,20 @@
 // softmax(q.k / sqrt(128)) over the keys of the last `window` positions up to the query's
 // own, o = sum p v. The keys and values of positions before the chunk come from a ring of
 // `cr` positions per stream (written by k_kv_append after the chunk's step); the chunk's own
-// come from the QKV product of this chunk. Three MFMA kernels:
-//   k_swa_fwd      online-softmax forward: O (fp32 and bf16) and the log-sum-exp per query;
-//   k_swa_bwd_dq   dQ over every key a query sees (cached keys included);
-//   k_swa_bwd_dkdv dK, dV of the chunk's own keys (cached keys are constants).
+// come from the QKV product of this chunk. q, k and v are held in two 16-bit forms: half
+// precision (11 significant bits) for the forward and decode, bf16 for the backward. Three
+// MFMA kernels:
+//   k_swa_fwd      online-softmax forward in half precision: O (fp32 and bf16) and the
+//                  log-sum-exp per query;
+//   k_swa_bwd_dq   dQ over every key a query sees (cached keys included), bf16;
+//   k_swa_bwd_dkdv dK, dV of the chunk's own keys (cached keys are constants), bf16.
 // Each lane of a wave owns one query (forward, dQ) or one key (dK/dV) as the column of
-// 16 x 16 x 32 bf16 MFMA blocks; the probabilities never leave registers: the products that
+// 16 x 16 x 32 MFMA blocks; the probabilities never leave registers: the products that
 // contract over them take them as the B operand in the k-slot order they already have, and
 // read the other operand from LDS in that same order. Each pass can divide its range among
 // several workgroups (k_swa_merge, k_swa_dq_sum and k_swa_dkdv_sum combine the partials in
 // a fixed order). Decoding one row: k_swa_dec_append files its key and value, k_swa_dec and
-// k_swa_dec_merge attend over the window in fp32.
+// k_swa_dec_merge attend over the window in fp32 (keys and values read in half precision).
 #include "launchers.h"
 #include "common.h"
 
@@ -26,12 +29,12 @@ constexpr int LDR = DH + 8;  // row stride (elements) of a [row][dim] tile: 272 
 constexpr int LDT = BLK + 8; // row stride of a [dim][row] tile: 144 B (conflict-free pair stores)
 
 struct SwaGeo {
-  const bf16_t* qkv;  // [R x 3d] q | k | v of the chunk's rows (stream z: rows z b ..)
-  const bf16_t* kc;   // key ring [nb][cr x d]: position p at slot p % cr
+  const bf16_t* qkv;  // [R x 3d] q | k | v of the chunk's rows (stream z: rows z b ..), bf16
+  const bf16_t* kc;   // key ring [nb][cr x d]: position p at slot p % cr, bf16
   const bf16_t* vc;
-  const bf16_t* qkv_lo;  // the rounding residuals of the same (the forward's second terms)
-  const bf16_t* kc_lo;
-  const bf16_t* vc_lo;
+  const f16_t* qkv16;  // the same three in half precision (the forward's operands)
+  const f16_t* kc16;
+  const f16_t* vc16;
   int cr, b, d, window;
   int64_t pos;        // position of the chunk's first row
 };
@@ -93,20 +96,20 @@ __device__ __forceinline__ void put_p(const Chunks& R, bf16_t* tile, bf16_t* T) 
 }
 
 // Key-block fetch in the row-pair layout of fetch_p for several tiles at once (keys or
-// values, hi or lo terms). Each tile's base pointers for the workgroup's stream and head are
+// values, bf16 or half). Each tile's base pointers for the workgroup's stream and head are
 // set up once (uniform over the workgroup); per block a thread resolves its two rows (ring
 // slot or chunk row, plus its 16-byte column) once and reads every tile from them. Rows past the block's last
 // key repeat that key: its scores are masked and its probabilities are zero, so the values
 // only have to be finite.
 struct KvBase {
-  const bf16_t* ring;   // slot 0 of the stream's ring
-  const bf16_t* chunk;  // row 0 of the stream's chunk rows (q | k | v)
+  const uint16_t* ring;   // slot 0 of the stream's ring
+  const uint16_t* chunk;  // row 0 of the stream's chunk rows (q | k | v)
 };
-__device__ __forceinline__ KvBase kv_base(const SwaGeo& g, int z, int h, int which, bool lo) {
-  const bf16_t* ring = which == 1 ? (lo ? g.kc_lo : g.kc) : (lo ? g.vc_lo : g.vc);
+__device__ __forceinline__ KvBase kv_base(const SwaGeo& g, int z, int h, int which, bool half) {
+  const uint16_t* ring = which == 1 ? (half ? g.kc16 : g.kc) : (half ? g.vc16 : g.vc);
   KvBase b;
   b.ring = ring + (int64_t)z * g.cr * g.d + h * DH;
-  b.chunk = (lo ? g.qkv_lo : g.qkv) + (int64_t)z * g.b * (3 * (int64_t)g.d) + (int64_t)which * g.d + h * DH;
+  b.chunk = (half ? g.qkv16 : g.qkv) + (int64_t)z * g.b * (3 * (int64_t)g.d) + (int64_t)which * g.d + h * DH;
   return b;
 }
 template <int NTL>
@@ -123,7 +126,7 @@ __device__ __forceinline__ void fetch_rows(Chunks (&R)[NTL], const KvBase (&B)[N
     const int64_t co = (int64_t)(ks.c0 + r - ks.nr) * (3 * (int64_t)g.d) + col;
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
-      const bf16_t* src = ring ? B[t].ring + ro : B[t].chunk + co;
+      const uint16_t* src = ring ? B[t].ring + ro : B[t].chunk + co;
       R[t].v[a] = *(const uint4*)src;
       R[t].v[2 + a] = *(const uint4*)(src + 64);
     }
@@ -142,15 +145,17 @@ __device__ __forceinline__ uint4 tchunk(const bf16_t* T, int dim, int t, int g) 
 __device__ __forceinline__ uint4 pchunk(const f32x4_t& a, const f32x4_t& b) {
   return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
 }
+__device__ __forceinline__ uint4 pchunk_f16(const f32x4_t& a, const f32x4_t& b) {
+  return make_uint4(pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]), pack_f16x2(b[0], b[1]), pack_f16x2(b[2], b[3]));
+}
 
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------- forward
 // grid (ceil(b / 64), H, streams). Outputs O fp32 and bf16 [R x d] (head h in columns
 // 128 h ..), lse2 [streams][H][b] = log2 of the softmax denominator in units of the scaled
-// logits s log2(e) / sqrt(128). Every operand enters as two bf16 terms (q, k, v stored as
-// hi + lo, p split in registers) and each product as three MFMAs (hi hi + lo hi + hi lo), so
-// the recorded losses carry no bf16 rounding of q, k, v or p to first order.
+// logits s log2(e) / sqrt(128). q, k, v and p enter in half precision (relative rounding
+// 2^-12, an eighth of bf16's), one MFMA per 32-k step of each product, fp32 accumulation.
 // With nsplit > 1 the key blocks of each query block are divided among nsplit workgroups
 // (blockIdx.x = query block * nsplit + split), each leaving its unnormalised partial O and its
 // (max, sum) in part / pm / pl for k_swa_merge.
@@ -164,13 +169,11 @@ struct SwaSplit {
 // QG query groups of 16 per wave (a workgroup covers 64 QG queries): every K and V operand
 // read from LDS feeds QG products, so a larger QG moves fewer tile bytes per query.
 template <int QG>
-__global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
+__global__ void __launch_bounds__(NT_A, 2) k_swa_fwd(SwaGeo g, SwaSplit sp, float* __restrict__ Of,
                                                                    bf16_t* __restrict__ Ob, bf16_t* __restrict__ Ol,
                                                                    float* __restrict__ lse2) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[BLK * LDR];
-  __shared__ __attribute__((aligned(16))) bf16_t sKl[BLK * LDR];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[DH * LDT];
-  __shared__ __attribute__((aligned(16))) bf16_t sVtl[DH * LDT];
+  __shared__ __attribute__((aligned(16))) f16_t sK[BLK * LDR];
+  __shared__ __attribute__((aligned(16))) f16_t sVt[DH * LDT];
   constexpr int QB = BLK * QG;  // queries per workgroup
   const int z = blockIdx.z, h = blockIdx.y, H = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -183,7 +186,7 @@ __global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, Swa
   // 32 s + 8 lg ..), and their running O, max and sum
   int q[QG];
   bool qok[QG];
-  uint4 qf[QG][4], qfl[QG][4];
+  uint4 qf[QG][4];
   f32x4_t ot[QG][8];
   float m[QG], lsum[QG];
 #pragma unroll
@@ -193,8 +196,7 @@ __global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, Swa
     const int64_t o = ((int64_t)z * g.b + (qok[gq] ? q[gq] : 0)) * (3 * (int64_t)g.d) + h * DH;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      qf[gq][s] = qok[gq] ? *(const uint4*)(g.qkv + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
-      qfl[gq][s] = qok[gq] ? *(const uint4*)(g.qkv_lo + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      qf[gq][s] = qok[gq] ? *(const uint4*)(g.qkv16 + o + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) ot[gq][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -213,19 +215,16 @@ __global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, Swa
     kend = min(qhi, klo + b1 * BLK - 1);
     klo += b0 * BLK;
   }
-  Chunks cb[4];  // K, K lo, V, V lo
-  const KvBase kvb[4] = {kv_base(g, z, h, 1, false), kv_base(g, z, h, 1, true), kv_base(g, z, h, 2, false),
-                         kv_base(g, z, h, 2, true)};
-  auto fetch_block = [&](int64_t kb) { fetch_rows<4>(cb, kvb, g, key_src(g, kb, qhi)); };
+  Chunks cb[2];  // K, V (half precision)
+  const KvBase kvb[2] = {kv_base(g, z, h, 1, true), kv_base(g, z, h, 2, true)};
+  auto fetch_block = [&](int64_t kb) { fetch_rows<2>(cb, kvb, g, key_src(g, kb, qhi)); };
   // the wave's first query position (its 16 QG queries follow)
   const int64_t qw0 = g.pos + q0 + 16 * QG * wave;
   if (klo <= kend) fetch_block(klo);
   for (int64_t kb = klo; kb <= kend; kb += BLK) {
     __syncthreads();  // the previous block's tiles are no longer read
     put_p(cb[0], sK, nullptr);
-    put_p(cb[1], sKl, nullptr);
-    put_p(cb[2], nullptr, sVt);
-    put_p(cb[3], nullptr, sVtl);
+    put_p(cb[1], nullptr, sVt);
     __syncthreads();
     if (kb + BLK <= kend) fetch_block(kb + BLK);  // in flight during this block's MFMAs
 
@@ -238,19 +237,14 @@ __global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, Swa
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint4 a = *(const uint4*)(sK + (16 * j + lr) * LDR + 32 * s + 8 * lg);
-        const uint4 al = *(const uint4*)(sKl + (16 * j + lr) * LDR + 32 * s + 8 * lg);
 #pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-          mfma_chunk(st[gq][j], a, qf[gq][s], bf16_t());
-          mfma_chunk(st[gq][j], al, qf[gq][s], bf16_t());
-          mfma_chunk(st[gq][j], a, qfl[gq][s], bf16_t());
-        }
+        for (int gq = 0; gq < QG; ++gq) mfma_chunk_f16(st[gq][j], a, qf[gq][s]);
       }
     }
     // mask (distance query - key in [0, window), 32-bit) and block max (scaled units); a
     // block that every query of the wave sees whole needs no mask
     const bool whole = qw0 - (kb + BLK - 1) >= 0 && qw0 + 16 * QG - 1 - kb < g.window;
-    uint4 pb[QG][2], pl[QG][2];
+    uint4 pb[QG][2];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
       float bm = -INFINITY;
@@ -295,18 +289,9 @@ __global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, Swa
           st[gq][j][e] = p;
           lsum[gq] += p;
         }
-      // p as hi + lo B operands, in the k-slot order of tchunk
+      // p (at most 1) as half-precision B operands, in the k-slot order of tchunk
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4_t r0, r1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r0[e] = st[gq][2 * t][e] - bf2f(f2bf(st[gq][2 * t][e]));
-          r1[e] = st[gq][2 * t + 1][e] - bf2f(f2bf(st[gq][2 * t + 1][e]));
-        }
-        pb[gq][t] = pchunk(st[gq][2 * t], st[gq][2 * t + 1]);
-        pl[gq][t] = pchunk(r0, r1);
-      }
+      for (int t = 0; t < 2; ++t) pb[gq][t] = pchunk_f16(st[gq][2 * t], st[gq][2 * t + 1]);
     }
     // O^T += V^T P^T: ot[gq][c][e] = o(dim 16 c + 4 lg + e, query q[gq])
 #pragma unroll
@@ -314,13 +299,8 @@ __global__ void __launch_bounds__(NT_A, QG == 1 ? 2 : 1) k_swa_fwd(SwaGeo g, Swa
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const uint4 vh = tchunk(sVt, 16 * c + lr, t, lg);
-        const uint4 vl = tchunk(sVtl, 16 * c + lr, t, lg);
 #pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-          mfma_chunk(ot[gq][c], vh, pb[gq][t], bf16_t());
-          mfma_chunk(ot[gq][c], vl, pb[gq][t], bf16_t());
-          mfma_chunk(ot[gq][c], vh, pl[gq][t], bf16_t());
-        }
+        for (int gq = 0; gq < QG; ++gq) mfma_chunk_f16(ot[gq][c], vh, pb[gq][t]);
       }
     }
   }
@@ -680,11 +660,12 @@ __global__ void __launch_bounds__(NT_A, 2) k_swa_bwd_dkdv(SwaGeo g, int nsplit, 
   }
 }
 
-// The last min(b, cr) keys and values of the chunk into the ring: grid (rows, streams).
-__global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ qkv_lo,
+// The last min(b, cr) keys and values of the chunk into the ring (both forms): grid (rows,
+// streams).
+__global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv, const f16_t* __restrict__ qkv16,
                                                   int b, int d, int64_t pos, int cr, bf16_t* __restrict__ kc,
-                                                  bf16_t* __restrict__ vc, bf16_t* __restrict__ kc_lo,
-                                                  bf16_t* __restrict__ vc_lo) {
+                                                  bf16_t* __restrict__ vc, f16_t* __restrict__ kc16,
+                                                  f16_t* __restrict__ vc16) {
   const int n = min(b, cr);
   const int r = b - n + blockIdx.x, z = blockIdx.y;
   const int64_t so = ((int64_t)z * b + r) * (3 * (int64_t)d);
@@ -692,15 +673,15 @@ __global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv
   for (int c = threadIdx.x * 8; c < d; c += 64 * 8) {
     *(uint4*)(kc + dst + c) = *(const uint4*)(qkv + so + d + c);
     *(uint4*)(vc + dst + c) = *(const uint4*)(qkv + so + 2 * d + c);
-    *(uint4*)(kc_lo + dst + c) = *(const uint4*)(qkv_lo + so + d + c);
-    *(uint4*)(vc_lo + dst + c) = *(const uint4*)(qkv_lo + so + 2 * d + c);
+    *(uint4*)(kc16 + dst + c) = *(const uint4*)(qkv16 + so + d + c);
+    *(uint4*)(vc16 + dst + c) = *(const uint4*)(qkv16 + so + 2 * d + c);
   }
 }
 
 // ---------------------------------------------------------------------------- decode
 // One decoded row (position p, its q | k | v in fp32, qkv [3d]): its key and value join the
-// ring first (hi + lo bf16 terms, as the chunk path stores them), then the attention reads
-// keys max(0, p - window + 1) .. p of the ring in fp32 (hi + lo). Work: grid (H, nsplit), each
+// ring first (bf16 and half, as the chunk path stores them), then the attention reads keys
+// max(0, p - window + 1) .. p of the ring (half precision) in fp32 arithmetic. Work: grid (H, nsplit), each
 // workgroup a contiguous share of the keys in blocks of 64, online softmax over the blocks.
 // Per block, four lanes score a key (32 dims each, 16-byte loads, two shuffles), one wave
 // turns the 64 scores into probabilities, and each lane accumulates 8 dims of o over a
@@ -709,29 +690,27 @@ __global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv
 constexpr int DEC_KB = 64;  // keys per block of the decode kernel
 
 __global__ void __launch_bounds__(NT_A) k_swa_dec_append(const float* __restrict__ qkv, int d, int64_t p, int cr,
-                                                         bf16_t* __restrict__ kc, bf16_t* __restrict__ kc_lo,
-                                                         bf16_t* __restrict__ vc, bf16_t* __restrict__ vc_lo) {
+                                                         bf16_t* __restrict__ kc, f16_t* __restrict__ kc16,
+                                                         bf16_t* __restrict__ vc, f16_t* __restrict__ vc16) {
   const int64_t o = (p % cr) * d;
   for (int i = threadIdx.x; i < d; i += NT_A) {
     const float k = qkv[d + i], v = qkv[2 * d + i];
-    const bf16_t kh = f2bf(k), vh = f2bf(v);
-    kc[o + i] = kh;
-    kc_lo[o + i] = f2bf(k - bf2f(kh));
-    vc[o + i] = vh;
-    vc_lo[o + i] = f2bf(v - bf2f(vh));
+    kc[o + i] = f2bf(k);
+    kc16[o + i] = f2h(k);
+    vc[o + i] = f2bf(v);
+    vc16[o + i] = f2h(v);
   }
 }
 
-__global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv, const bf16_t* __restrict__ kc,
-                                                  const bf16_t* __restrict__ kc_lo, const bf16_t* __restrict__ vc,
-                                                  const bf16_t* __restrict__ vc_lo, int d, int64_t p, int cr,
-                                                  int window, float* __restrict__ part) {
+__global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv, const f16_t* __restrict__ kc,
+                                                  const f16_t* __restrict__ vc, int d, int64_t p, int cr, int window,
+                                                  float* __restrict__ part) {
   __shared__ float sp[DEC_KB];      // the block's probabilities
   __shared__ float sacc[16][DH];    // per key subset, the partial o
   __shared__ float sml[2];          // the block's (max, sum)
   const int h = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
   const int t = threadIdx.x;
-  // scores: four lanes per key, 32 dims each (hi + lo terms, 16-byte loads)
+  // scores: four lanes per key, 32 dims each (16-byte loads)
   const int kj = t >> 2, kq = (t & 3) * 32;
   float q[32];
 #pragma unroll
@@ -744,25 +723,18 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
   const int64_t nblk = (nk + DEC_KB - 1) / DEC_KB;
   const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
   float m = -INFINITY, l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // a block's operands, requested one block ahead: this lane's key (32 dims, hi and lo) and
-  // its four value rows (8 dims, hi and lo); ring slots are in range for any position, and
-  // keys past p are neither scored nor accumulated
+  // a block's operands, requested one block ahead: this lane's key (32 dims) and its four
+  // value rows (8 dims); ring slots are in range for any position, and keys past p are
+  // neither scored nor accumulated
   struct Ops {
-    uint4 kh[4], kl[4], vh[4], vl[4];
+    uint4 k[4], v[4];
   };
   auto load = [&](Ops& o, int64_t kb) {
     const int64_t rk = ((kb + kj) % cr) * d + h * DH + kq;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      o.kh[c] = *(const uint4*)(kc + rk + 8 * c);
-      o.kl[c] = *(const uint4*)(kc_lo + rk + 8 * c);
-    }
+    for (int c = 0; c < 4; ++c) o.k[c] = *(const uint4*)(kc + rk + 8 * c);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int64_t rv = ((kb + ks + 16 * jj) % cr) * d + h * DH + g;
-      o.vh[jj] = *(const uint4*)(vc + rv);
-      o.vl[jj] = *(const uint4*)(vc_lo + rv);
-    }
+    for (int jj = 0; jj < 4; ++jj) o.v[jj] = *(const uint4*)(vc + ((kb + ks + 16 * jj) % cr) * d + h * DH + g);
   };
   Ops cur, nxt;
   if (b0 < b1) load(cur, k0 + b0 * DEC_KB);
@@ -774,10 +746,9 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
       float a = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16_t* e = (const bf16_t*)&cur.kh[c];
-        const bf16_t* f = (const bf16_t*)&cur.kl[c];
+        const f16_t* e = (const f16_t*)&cur.k[c];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) a = fmaf(bf2f(e[x]) + bf2f(f[x]), q[8 * c + x], a);
+        for (int x = 0; x < 8; ++x) a = fmaf(h2f(e[x]), q[8 * c + x], a);
       }
       a += __shfl_xor(a, 1, TTT_WAVE);
       a += __shfl_xor(a, 2, TTT_WAVE);
@@ -811,11 +782,10 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
     for (int jj = 0; jj < 4; ++jj) {
       const int j = ks + 16 * jj;
       if (kb + j > p) break;
-      const bf16_t* e = (const bf16_t*)&cur.vh[jj];
-      const bf16_t* f = (const bf16_t*)&cur.vl[jj];
+      const f16_t* e = (const f16_t*)&cur.v[jj];
       const float pj = sp[j];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc[x] = fmaf(pj, bf2f(e[x]) + bf2f(f[x]), acc[x]);
+      for (int x = 0; x < 8; ++x) acc[x] = fmaf(pj, h2f(e[x]), acc[x]);
     }
     __syncthreads();  // sp and sml are rewritten by the next block
     cur = nxt;
@@ -872,9 +842,9 @@ SwaGeo geo(const SwaShape& s) {
   g.qkv = (const bf16_t*)s.qkv;
   g.kc = (const bf16_t*)s.kc;
   g.vc = (const bf16_t*)s.vc;
-  g.qkv_lo = (const bf16_t*)s.qkv_lo;
-  g.kc_lo = (const bf16_t*)s.kc_lo;
-  g.vc_lo = (const bf16_t*)s.vc_lo;
+  g.qkv16 = (const f16_t*)s.qkv16;
+  g.kc16 = (const f16_t*)s.kc16;
+  g.vc16 = (const f16_t*)s.vc16;
   g.cr = s.cr;
   g.b = s.b;
   g.d = s.d;
@@ -885,7 +855,7 @@ SwaGeo geo(const SwaShape& s) {
 
 bool shape_ok(const SwaShape& s) {
   return s.d % DH == 0 && s.d >= DH && s.b >= 1 && s.streams >= 1 && s.streams <= 65535 && s.window >= 1 &&
-         s.cr >= 1 && s.pos >= 0 && s.qkv && s.kc && s.vc && s.qkv_lo && s.kc_lo && s.vc_lo;
+         s.cr >= 1 && s.pos >= 0 && s.qkv && s.kc && s.vc && s.qkv16 && s.kc16 && s.vc16;
 }
 
 }  // namespace
@@ -913,9 +883,7 @@ __global__ void __launch_bounds__(NT_A) k_swa_dkdv_sum(const float* __restrict__
   }
 }
 
-// Query groups of 16 per wave in the forward kernel. Two halve the tile bytes per query but
-// take about 370 registers (one workgroup per CU instead of two) and measured slower at the
-// 760M fuller block (342 against 324 us per launch).
+// Query groups of 16 per wave in the forward kernel. Two halve the LDS reads per query.
 constexpr int FWD_QG = 1;
 
 // Workgroups of one launch take about equal time, so a launch of wg query blocks split n
@@ -937,11 +905,12 @@ static int split_count(int64_t wg, const SwaShape& s, int slots) {
 }
 
 int swa_fwd_splits(const SwaShape& s) {
-  // 64 FWD_QG queries per workgroup; one workgroup per CU at two query groups a wave (its
-  // registers), two at one
+  // 64 FWD_QG queries per workgroup, two workgroups per CU (about 160 registers at one query
+  // group a wave, 230 at two). Three per CU at one group, or two groups a wave, measured no
+  // faster at the 760M fuller block: 169 and 165 against 165 us per launch.
   const int qb = BLK * FWD_QG;
   const int64_t wg = (int64_t)((s.b + qb - 1) / qb) * (s.d / DH) * s.streams;
-  return split_count(wg, s, FWD_QG == 1 ? 512 : 256);
+  return split_count(wg, s, 512);
 }
 
 int swa_dkdv_splits(const SwaShape& s) {
@@ -1000,14 +969,14 @@ int swa_dec_splits(int window) {
 }
 
 hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o) {
-  if (!qkv || !part || !o || s.d % DH || s.cr < 1 || s.window < 1 || s.pos < 0 || !s.kc || !s.vc || !s.kc_lo ||
-      !s.vc_lo)
+  if (!qkv || !part || !o || s.d % DH || s.cr < 1 || s.window < 1 || s.pos < 0 || !s.kc || !s.vc || !s.kc16 ||
+      !s.vc16)
     return hipErrorInvalidValue;
   const int H = s.d / DH, ns = swa_dec_splits(s.window);
   hipLaunchKernelGGL(k_swa_dec_append, dim3(1), dim3(NT_A), 0, st, qkv, s.d, s.pos, s.cr, (bf16_t*)s.kc,
-                     (bf16_t*)s.kc_lo, (bf16_t*)s.vc, (bf16_t*)s.vc_lo);
-  hipLaunchKernelGGL(k_swa_dec, dim3(H, ns), dim3(NT_A), 0, st, qkv, (const bf16_t*)s.kc, (const bf16_t*)s.kc_lo,
-                     (const bf16_t*)s.vc, (const bf16_t*)s.vc_lo, s.d, s.pos, s.cr, s.window, part);
+                     (f16_t*)s.kc16, (bf16_t*)s.vc, (f16_t*)s.vc16);
+  hipLaunchKernelGGL(k_swa_dec, dim3(H, ns), dim3(NT_A), 0, st, qkv, (const f16_t*)s.kc16, (const f16_t*)s.vc16, s.d,
+                     s.pos, s.cr, s.window, part);
   hipLaunchKernelGGL(k_swa_dec_merge, dim3(H), dim3(DH), 0, st, part, ns, o);
   return hipGetLastError();
 }
@@ -1015,7 +984,7 @@ hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, f
 hipError_t run_kv_append(hipStream_t st, const SwaShape& s) {
   if (!shape_ok(s)) return hipErrorInvalidValue;
   const int n = s.b < s.cr ? s.b : s.cr;
-  hipLaunchKernelGGL(k_kv_append, dim3(n, s.streams), dim3(64), 0, st, (const bf16_t*)s.qkv, (const bf16_t*)s.qkv_lo,
-                     s.b, s.d, s.pos, s.cr, (bf16_t*)s.kc, (bf16_t*)s.vc, (bf16_t*)s.kc_lo, (bf16_t*)s.vc_lo);
+  hipLaunchKernelGGL(k_kv_append, dim3(n, s.streams), dim3(64), 0, st, (const bf16_t*)s.qkv, (const f16_t*)s.qkv16,
+                     s.b, s.d, s.pos, s.cr, (bf16_t*)s.kc, (bf16_t*)s.vc, (f16_t*)s.kc16, (f16_t*)s.vc16);
   return hipGetLastError();
 }

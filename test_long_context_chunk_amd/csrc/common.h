@@ -25,6 +25,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// IEEE half precision (11 significant bits, 3 more than bfloat16, for O(1) operands such as
+// attention's q, k, v and probabilities), stored as raw 16-bit patterns.
+typedef uint16_t f16_t;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float h2f(f16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
+// float -> half, round to nearest even (the hardware conversion in the default mode)
+__device__ __forceinline__ f16_t f2h(float f) { return __builtin_bit_cast(f16_t, (_Float16)f); }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
 template <class T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
@@ -51,6 +63,11 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const uint4& a, const u
 __device__ __forceinline__ void mfma32(f32x16_t& acc, const uint4& a, const uint4& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc,
                                                 0, 0, 0);
+}
+// half precision, same lane layout as the bf16 form: one v_mfma_f32_16x16x32_f16.
+__device__ __forceinline__ void mfma_chunk_f16(f32x4_t& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc, 0,
+                                               0, 0);
 }
 __device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const uint4& a, const uint4& b, float) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);

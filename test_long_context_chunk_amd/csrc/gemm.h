@@ -1263,11 +1263,11 @@ struct EpiStoreT {
   }
 };
 
-// The product as two bf16 terms, C ~= Ch + Cl with Ch = rn(C), Cl = rn(C - Ch) (about 16
-// significant bits together), for operands a later product reads at higher precision.
-struct EpiStoreSplit {
+// The product in two 16-bit forms: Ch = rn_bf16(C) for products that take bf16 operands, and
+// Cf = rn_f16(C) (11 significant bits) for products that read it in half precision.
+struct EpiStoreBf16F16 {
   bf16_t* Ch;
-  bf16_t* Cl;
+  f16_t* Cf;
   int64_t ldc;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
@@ -1282,9 +1282,8 @@ struct EpiStoreSplit {
           const int col = epi_col(p, j);
           if (col >= p.N) continue;
           const float v = acc[i][j][e];
-          const bf16_t h = f2bf(v);
-          Ch[(int64_t)row * ldc + col] = h;
-          Cl[(int64_t)row * ldc + col] = f2bf(v - bf2f(h));
+          Ch[(int64_t)row * ldc + col] = f2bf(v);
+          Cf[(int64_t)row * ldc + col] = f2h(v);
         }
       }
   }

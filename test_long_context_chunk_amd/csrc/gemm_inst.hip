@@ -86,9 +86,9 @@ hipError_t gemm_store(hipStream_t st, int prec, const void* X, int64_t ldx, cons
   });
 }
 
-hipError_t gemm_store_split(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                            int K, void* Ch, void* Cl, int64_t ldc, const GemmSeg2& s2) {
-  EpiStoreSplit e{(bf16_t*)Ch, (bf16_t*)Cl, ldc};
+hipError_t gemm_store_bf16_f16(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                              int K, void* Ch, void* Cf, int64_t ldc, const GemmSeg2& s2) {
+  EpiStoreBf16F16 e{(bf16_t*)Ch, (f16_t*)Cf, ldc};
   return launch_gemm<bf16_t>(st, X, ldx, Y, ldy, M, N, K, 1, e, seg(s2));
 }
 

@@ -92,16 +92,15 @@ hipError_t run_restore_unless(hipStream_t st, const int* commit, const void* src
 // One chunk step of `streams` streams: qkv [streams b x 3d] holds the chunk's q | k | v
 // (stream z: rows z b ..); kc, vc [streams][cr x d] the ring of earlier keys and values
 // (position p at slot p % cr, cr >= window - 1); pos the position of the chunk's first row.
-// The forward reads q, k, v as two bf16 terms each (hi + lo: qkv_lo, kc_lo, vc_lo hold the
-// rounding residuals), so its products carry about 16 significant bits; the backward reads
-// the hi terms.
+// Each of q, k, v is held twice: bf16 (qkv, kc, vc), read by the backward, and half precision
+// (qkv16, kc16, vc16: 11 significant bits), read by the forward and by decode.
 struct SwaShape {
   const void* qkv = nullptr;
-  const void* qkv_lo = nullptr;
+  const void* qkv16 = nullptr;
   void* kc = nullptr;
   void* vc = nullptr;
-  void* kc_lo = nullptr;
-  void* vc_lo = nullptr;
+  void* kc16 = nullptr;
+  void* vc16 = nullptr;
   int cr = 0, b = 0, d = 0, window = 0, streams = 1;
   int64_t pos = 0;
 };
@@ -178,9 +177,9 @@ hipError_t gemm_swiglu_bwd(hipStream_t st, int prec, const void* X, int64_t ldx,
 // C [M x ldc] in the GEMM operand precision.
 hipError_t gemm_store(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                       int K, void* C, int64_t ldc);
-// bf16 operands: C ~= Ch + Cl, Ch = rn(C), Cl = rn(C - Ch), both [M x ldc] bf16.
-hipError_t gemm_store_split(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
-                            int K, void* Ch, void* Cl, int64_t ldc, const GemmSeg2& s2 = GemmSeg2());
+// bf16 operands: C stored twice, Ch = rn_bf16(C) and Cf = rn_f16(C), both [M x ldc].
+hipError_t gemm_store_bf16_f16(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
+                              int K, void* Ch, void* Cf, int64_t ldc, const GemmSeg2& s2 = GemmSeg2());
 // Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits):
 // per-tile buffers (CE partials, sums of squares, partial dots) are sized from it.
 void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n);

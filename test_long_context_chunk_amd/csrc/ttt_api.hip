@@ -73,19 +73,19 @@ struct Block {
   float* ra = nullptr;      // its RMSNorm scale [R]
   void* ResNa = nullptr;    // bf16 only: n_a - rn(n_a)
   void* QKV = nullptr;      // the chunk's q | k | v [R x 3d]
-  void* QKVl = nullptr;     // and their rounding residuals (the forward's second terms)
+  void* QKV16 = nullptr;    // the same in half precision (the attention forward's operands)
   float* Of = nullptr;      // attention output, fp32 [R x d]
   void* Ob = nullptr;       // and its GEMM operand copy
   void* Obl = nullptr;      // and that copy's rounding residual
   float* lse2 = nullptr;    // log2 softmax denominators [streams][heads][b]
-  void* Kc = nullptr;       // ring of earlier keys / values [streams][cr x d], and residuals
+  void* Kc = nullptr;       // ring of earlier keys / values [streams][cr x d], bf16
   void* Vc = nullptr;
-  void* Kcl = nullptr;
-  void* Vcl = nullptr;
+  void* Kc16 = nullptr;     // and in half precision
+  void* Vc16 = nullptr;
   void* Ke = nullptr;       // the same for a passage being scored (single stream) [cr x d]
   void* Ve = nullptr;
-  void* Kel = nullptr;
-  void* Vel = nullptr;
+  void* Ke16 = nullptr;
+  void* Ve16 = nullptr;
   int acslot = 0;           // loss-compensation slots of the attention: O, n_a
 };
 
@@ -290,12 +290,12 @@ void frozen_pair(ttt_ctx* c, const void* src, int rows, int cols, void** nat, vo
 SwaShape swa_shape(ttt_ctx* c, Block& B, int64_t pos) {
   SwaShape s;
   s.qkv = B.QKV;
-  s.qkv_lo = B.QKVl;
+  s.qkv16 = B.QKV16;
   const bool e = c->eval_ring;
   s.kc = e ? B.Ke : B.Kc;
   s.vc = e ? B.Ve : B.Vc;
-  s.kc_lo = e ? B.Kel : B.Kcl;
-  s.vc_lo = e ? B.Vel : B.Vcl;
+  s.kc16 = e ? B.Ke16 : B.Kc16;
+  s.vc16 = e ? B.Ve16 : B.Vc16;
   s.cr = c->cr;
   s.b = c->b;
   s.d = c->d;
@@ -402,20 +402,20 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
       B.Na = dalloc<char>(c, (int64_t)Rr * d * es);
       B.ra = dalloc<float>(c, (int64_t)Rr * 4);
       B.QKV = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
-      B.QKVl = dalloc<char>(c, (int64_t)Rr * 3 * d * es);
+      B.QKV16 = dalloc<char>(c, (int64_t)Rr * 3 * d * 2);
       B.Of = dalloc<float>(c, (int64_t)Rr * d * 4);
       B.Ob = dalloc<char>(c, (int64_t)Rr * d * es);
       B.Obl = dalloc<char>(c, (int64_t)Rr * d * es);
       B.lse2 = dalloc<float>(c, (int64_t)Rr * (d / 128) * 4);
       B.Kc = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
       B.Vc = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
-      B.Kcl = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
-      B.Vcl = dalloc<char>(c, (int64_t)nb * c->cr * d * es);
+      B.Kc16 = dalloc<char>(c, (int64_t)nb * c->cr * d * 2);
+      B.Vc16 = dalloc<char>(c, (int64_t)nb * c->cr * d * 2);
       if (nb == 1) {  // evaluation (single-stream contexts only)
         B.Ke = dalloc<char>(c, (int64_t)c->cr * d * es);
         B.Ve = dalloc<char>(c, (int64_t)c->cr * d * es);
-        B.Kel = dalloc<char>(c, (int64_t)c->cr * d * es);
-        B.Vel = dalloc<char>(c, (int64_t)c->cr * d * es);
+        B.Ke16 = dalloc<char>(c, (int64_t)c->cr * d * 2);
+        B.Ve16 = dalloc<char>(c, (int64_t)c->cr * d * 2);
       }
       if (res) B.ResNa = dalloc<char>(c, (int64_t)Rr * d * es);
       if (c->foc) {
@@ -669,8 +669,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     if (c->window > 0) {
       // the frozen sliding-window attention ([E2E] section 3), once over all streams' rows:
       // q | k | v, attention against the ring and the chunk's own keys, output projection
-      RUN(TTT_K_UP, gemm_store_split(st, B.Na, d, B.WqkvT, d, Rr, 3 * d, d, B.QKV, B.QKVl, 3 * d,
-                                       split ? GemmSeg2{B.ResNa, d, B.WqkvT, d, d} : GemmSeg2()));
+      RUN(TTT_K_UP, gemm_store_bf16_f16(st, B.Na, d, B.WqkvT, d, Rr, 3 * d, d, B.QKV, B.QKV16, 3 * d,
+                                          split ? GemmSeg2{B.ResNa, d, B.WqkvT, d, d} : GemmSeg2()));
       RUN(TTT_K_ATTN, run_swa_fwd(st, swa_shape(c, B, chunk_pos), B.Of, B.Ob, B.Obl, B.lse2, c->swa_part, c->swa_m,
                                   c->swa_l));
       const int So = gemm_split_k(prec, Rr, d, d, split ? d : 0, SPLIT_MAX);

@@ -28,15 +28,15 @@ def test_decode_bytes_per_token():
 
 
 def test_decode_implementation_bytes_per_token():
-    """What the implementation reads besides: bf16 fast tensors as two terms (W0, rn(D)) and the
-    keys and values as hi and lo terms."""
+    """What the implementation reads: bf16 fast tensors as two terms (W0, rn(D)); the keys and
+    values in one half-precision copy (as many bytes as the method's bf16 copy)."""
     d, m, V = 1536, 6144, 32000
     fast = 2 * (2 * d * m * 2)
     assert bench.decode_impl_bytes_per_token(W.preset("s760m")) == 3 * fast + V * d * 2 == 324796416
     w = W.preset("e2e760m")
     d, m, ms, k = w.d_model, w.d_hidden, w.static_hidden, w.swa_window
-    per_block = 2 * (2 * d * m * 2) + 2 * d * ms * 2 + 4 * d * d * 2 + 4 * k * d * 2
-    assert bench.decode_impl_bytes_per_token(w) == 3 * per_block + w.vocab * d * 2 == 626786304
+    per_block = 2 * (2 * d * m * 2) + 2 * d * ms * 2 + 4 * d * d * 2 + 2 * k * d * 2
+    assert bench.decode_impl_bytes_per_token(w) == 3 * per_block + w.vocab * d * 2 == 475791360
 
 
 def test_visible_keys_brute_force():
