@@ -1104,6 +1104,66 @@ struct EpiDU {
       if (DUT) lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
       return;
     }
+    if constexpr (sizeof(T) == 2 && TileGeo<FM, FN, WGM, WGN>::BN != 128 &&
+                  (TileGeo<FM, FN, WGM, WGN>::BM * TileGeo<FM, FN, WGM, WGN>::BN * 4 +
+                   TileGeo<FM, FN, WGM, WGN>::BM * (TileGeo<FM, FN, WGM, WGN>::BN / 8) * 4) <=
+                      TileGeo<FM, FN, WGM, WGN>::SMEM) {
+      // other tile widths: the fp32 tile in LDS, rows of 8 columns per thread (16-byte
+      // accesses), each piece's partial dot kept in LDS and summed per row in column order
+      using G = TileGeo<FM, FN, WGM, WGN>;
+      constexpr int CH = G::BN / 8, NT = WGM * WGN * 64;
+      acc_to_lds<FM, FN, WGM, WGN>(p, acc);
+      float* U = (float*)p.smem;
+      float* red = U + G::BM * G::BN;
+      const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+      const bool vec = (ld & 7) == 0;
+#pragma unroll 1
+      for (int idx = p.tid; idx < G::BM * CH; idx += NT) {
+        const int r = idx / CH, c = (idx - r * CH) * 8;
+        const int gr = m0 + r, gc = n0 + c;
+        float* up = U + r * G::BN + c;
+        float du[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float dot = 0.f;
+        if (gr < p.M && gc < p.N) {
+          const int64_t o = (int64_t)gr * ld + gc;
+          const int nv = min(8, p.N - gc);
+          if (vec && nv == 8) {
+            const uint4 gq = *(const uint4*)((const bf16_t*)GP + o);
+            const uint4 rq = RES ? *(const uint4*)((const bf16_t*)RES + o) : make_uint4(0, 0, 0, 0);
+            const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, rw[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float a0 = up[2 * q], a1 = up[2 * q + 1];
+              du[2 * q] = a0 * __uint_as_float(gw[q] << 16);
+              du[2 * q + 1] = a1 * __uint_as_float(gw[q] & 0xffff0000u);
+              dot = fmaf(a0, __uint_as_float(rw[q] << 16), dot);
+              dot = fmaf(a1, __uint_as_float(rw[q] & 0xffff0000u), dot);
+            }
+            *(uint4*)((bf16_t*)DU + o) = make_uint4(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                                                    pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7]));
+          } else {
+            for (int k = 0; k < nv; ++k) {
+              du[k] = up[k] * to_f<T>(GP[o + k]);
+              DU[o + k] = from_f<T>(du[k]);
+              if (RES) dot = fmaf(up[k], to_f<T>(RES[o + k]), dot);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) up[k] = du[k];
+        red[idx] = dot;
+      }
+      __syncthreads();
+      if (cdot) {
+        for (int r = p.tid; r < G::BM; r += NT) {
+          float sum = red[r * CH];
+          for (int k = 1; k < CH; ++k) sum += red[r * CH + k];
+          if (m0 + r < p.M) cdot[(int64_t)p.tn * ldc + m0 + r] = sum;
+        }
+      }
+      if (DUT) lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)DUT, ldt);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r0 = epi_row(p, i, 0);
@@ -1271,6 +1331,18 @@ struct EpiStoreBf16F16 {
   int64_t ldc;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    // each form staged through LDS as whole rows (16-byte stores); direct stores otherwise
+    Packed<FM, FN> h, f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        h[i][j][0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        h[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        f[i][j][0] = pack_f16x2(acc[i][j][0], acc[i][j][1]);
+        f[i][j][1] = pack_f16x2(acc[i][j][2], acc[i][j][3]);
+      }
+    if (stage_rows_bf16<FM, FN, WGM, WGN>(p, h, Ch, ldc) && stage_rows_bf16<FM, FN, WGM, WGN>(p, f, Cf, ldc)) return;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1438,7 +1510,7 @@ struct TilePlan {
   int slots;
   int wtn;  // columns of one wave's sub-tile
 };
-inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
+inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits, int groups = 1) {
   const int ke = 128 / es;
   const bool dma = (K % ke == 0) && (K2 % ke == 0);
   const int tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
@@ -1453,6 +1525,16 @@ inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits) {
       const int64_t load128 = (t128 + 511) / 512 * (2 * 128 * 128), load192 = (t192 + 255) / 256 * (192 * 192);
       if (load192 < load128) return TilePlan{192, 192, true, 256, 96};
       return TilePlan{128, 128, true, 512, 64};
+    }
+    if (splits <= 1) {
+      // A long-K product whose 256 x 64 tiles (all groups) still fit one round of one
+      // workgroup per CU, i.e. whose 256 x 128 tiles would leave at least half the CUs idle,
+      // takes them: measured 35.4 against 41.7 us alone at 1024 x 3072 x 3072, and the 760M
+      // fuller-block step 87.8 against 91.9 ms. (128 x 192 tiles for the 760M up and dA
+      // products, 256 tiles each, measured faster alone, 44.5 against 47.1 us, but 0.5%
+      // slower over the step.)
+      const int64_t g = groups < 1 ? 1 : groups;
+      if ((int64_t)((M + 255) / 256) * ((N + 63) / 64) * g <= 256) return TilePlan{256, 64, true, 256, 32};
     }
     return TilePlan{256, 128, true, 256, 64};
   }
@@ -1492,7 +1574,7 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
   g.gx2 = s2.K > 0 ? gr.x2 : 0;
   g.gy2 = s2.K > 0 ? gr.y2 : 0;
   g.gtile = gr.tile;
-  const TilePlan plan = gemm_plan(M, N, K, s2.K, (int)sizeof(T), splits);
+  const TilePlan plan = gemm_plan(M, N, K, s2.K, (int)sizeof(T), splits, gr.n);
   if (plan.dma) {
     if constexpr (sizeof(T) == 2) {
       if (plan.bm == 256 && plan.bn == 128) {
@@ -1506,6 +1588,12 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
         g.tiles_n = (N + 191) / 192;
         g.kps = (g.kiters + splits - 1) / splits;
         return launch_dma<T, 192, 192, 2, 2>(st, g, splits, gr.n, epi);
+      }
+      if (plan.bm == 256 && plan.bn == 64) {
+        g.tiles_m = (M + 255) / 256;
+        g.tiles_n = (N + 63) / 64;
+        g.kps = g.kiters;
+        return launch_dma<T, 256, 64, 4, 2>(st, g, 1, gr.n, epi);
       }
     }
     if constexpr (sizeof(T) == 4) {

@@ -103,14 +103,14 @@ int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits) {
   return s < 1 ? 1 : s;
 }
 
-void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n) {
-  const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits);
+void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n, int groups) {
+  const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits, groups);
   *tile_m = t.bm;
   *tile_n = t.bn;
 }
 
-int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits) {
-  const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits);
+int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits, int groups) {
+  const TilePlan t = gemm_plan(M, N, K, K2, prec == PREC_BF16 ? 2 : 4, splits, groups);
   return t.dma ? t.wtn : 64;  // the register-staged kernel: 2 x 2 waves of a 128 x 128 tile
 }
 

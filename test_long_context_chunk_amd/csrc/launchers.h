@@ -180,9 +180,10 @@ hipError_t gemm_store(hipStream_t st, int prec, const void* X, int64_t ldx, cons
 // bf16 operands: C stored twice, Ch = rn_bf16(C) and Cf = rn_f16(C), both [M x ldc].
 hipError_t gemm_store_bf16_f16(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                               int K, void* Ch, void* Cf, int64_t ldc, const GemmSeg2& s2 = GemmSeg2());
-// Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits):
-// per-tile buffers (CE partials, sums of squares, partial dots) are sized from it.
-void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n);
+// Output tile shape the launcher uses for a GEMM of this shape (M, N, K, K2, splits, and the
+// number of products of a grouped launch): per-tile buffers (CE partials, sums of squares,
+// partial dots) are sized from it.
+void gemm_tile_shape(int prec, int M, int N, int K, int K2, int splits, int* tile_m, int* tile_n, int groups = 1);
 // Split-K slabs for a GEMM with a small output and a long K (K + K2): as many as fit in one
 // round of the workgroups the chip runs at once for its tile shape, at least 4 K-iterations
 // per slab, at most max_splits.
@@ -198,4 +199,4 @@ hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx,
                            int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit,
                            int nrec, void* Q, int64_t ldq, const GemmSeg2& s2 = GemmSeg2());
 // Columns of one wave's sub-tile for a GEMM of this shape (the CE record width).
-int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits);
+int gemm_wave_cols(int prec, int M, int N, int K, int K2, int splits, int groups = 1);

@@ -355,7 +355,7 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   c->split = c->prec == PREC_BF16 && L > 0 && c->window > 0;
   const bool res = c->foc || c->split;  // rounding residuals of the forward operands are kept
   int tmm = 0, tnm_w = 0;
-  gemm_tile_shape(c->prec, b, m, d, 0, 1, &tmm, &tnm_w);  // the dA GEMM (M = b, N = m, K = d)
+  gemm_tile_shape(c->prec, b, m, d, 0, 1, &tmm, &tnm_w, nb);  // the dA GEMM (M = b, N = m, K = d, per stream)
   const int tnm = cdiv(m, tnm_w);
   c->dot_tiles = tnm;
   int tns = 0;
