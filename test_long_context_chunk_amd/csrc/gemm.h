@@ -25,6 +25,8 @@
 
 #include "common.h"
 
+#include <type_traits>
+
 // A GEMM may carry a second K-segment: C = X Y^T + X2 Y2^T (same M, N). The kernel walks
 // the concatenated K range, so the two products share accumulators, tiles and splits.
 struct GemmArgs {
@@ -1380,6 +1382,9 @@ __device__ __forceinline__ void ce_combine(float& mx, float& sm, int& ix, float 
 // contribute nothing).
 template <class T>
 struct EpiCEPartial {
+  // 256 x 256 tiles (2 x 4 waves of 128 x 64, the same 64-column records): measured 132.4
+  // against 151.6 us at 1024 x 32000 x 1536 and 469 against 535 us at 512 x 151936 x 2560
+  static constexpr bool kSquareTiles = true;
   const int* tgt;    // [M] target ids
   float* pmax;       // [M x nrec]
   float* psum;
@@ -1468,6 +1473,13 @@ struct EpiCEPartial {
       }
   }
 };
+
+// Epilogues that handle 256 x 256 tiles well (their per-wave work does not depend on the
+// tile fitting an fp32 LDS staging area) declare kSquareTiles = true.
+template <class E, class = void>
+struct SquareTiles : std::false_type {};
+template <class E>
+struct SquareTiles<E, std::void_t<decltype(E::kSquareTiles)>> : std::bool_constant<E::kSquareTiles> {};
 
 // ------------------------------------------------------------------------- launcher
 // Second K-segment of a GEMM (absent when K2 == 0).
@@ -1577,6 +1589,17 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
   const TilePlan plan = gemm_plan(M, N, K, s2.K, (int)sizeof(T), splits, gr.n);
   if (plan.dma) {
     if constexpr (sizeof(T) == 2) {
+      if constexpr (SquareTiles<Epi>::value) {
+        // a long-K product with at least one full round of 256 x 256 tiles: half the operand
+        // bytes per flop of the 256 x 128 tile (2 stages of 64 KB, 16 x 16 MFMA blocks)
+        const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256) * gr.n;
+        if (plan.bm == 256 && plan.bn == 128 && splits <= 1 && t256 >= 256) {
+          g.tiles_m = (M + 255) / 256;
+          g.tiles_n = (N + 255) / 256;
+          g.kps = g.kiters;
+          return launch_dma<T, 256, 256, 2, 4>(st, g, 1, gr.n, epi);
+        }
+      }
       if (plan.bm == 256 && plan.bn == 128) {
         g.tiles_m = (M + 255) / 256;
         g.tiles_n = (N + 127) / 128;
