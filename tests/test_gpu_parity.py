@@ -232,6 +232,21 @@ def test_inplace_swiglu_four_chunks(ttt_lib):
     compare(g, orc, w, "bf16", 4, label="inplace")
 
 
+def test_narrow_tile_products_ragged(ttt_lib):
+    """Long-K products whose 256 x 128 tiles would leave most CUs idle run on 256 x 64 tiles:
+    here d = 1152 (K above 1024), m = 1000 and V = 3000 (ragged against 64 columns) and chunk
+    200 (ragged against 256 rows), so the up product (GELU epilogue), dA (its partial dots
+    through LDS) and the LM head (32-column CE records) all take that plan; three chunks,
+    every gate."""
+    w = W.preset("s125m", vocab=3000, d_model=1152, d_hidden=1000, n_blocks=2, n_tokens=600, chunk=200, lr=0.05)
+    P = W.init_weights(w, 5)
+    x = W.token_stream(w, 6)
+    log("narrow tiles: d=1152 m=1000 V=3000 b=200")
+    g = gpu_run(w, P, x)
+    assert g["status"] == 0
+    compare(g, oracle_run(w, P, x, 3), w, "bf16", 3, label="narrow-tiles")
+
+
 # ---------------------------------------------------------------------- determinism, errors
 def test_runs_are_bitwise_deterministic(ttt_lib):
     w, x, P = inputs("single")
