@@ -74,6 +74,19 @@ def test_lm_head_only_matches_naive_loss(ttt_lib, precision):
     compare(g, orc, w, precision, 4, check_weights=False, label="lm-head")
 
 
+def test_lm_head_square_tiles_ragged(ttt_lib):
+    """The LM head on 256 x 256 tiles (it fills at least one round of them) with ragged rows
+    and columns: n_blocks = 0, chunk 1000, V = 32008 (a last column tile of 8), d = 1536;
+    every loss is the static l_t(W0) of the oracle, every argmax gated."""
+    kw = dict(vocab=32008, d_model=1536, d_hidden=64, n_blocks=0, n_tokens=1000, chunk=1000)
+    w = W.preset("single", **kw)
+    _, x, P = inputs("single", 0, **kw)
+    log("lm head on 256 x 256 tiles: V=32008 d=1536 b=1000")
+    g = gpu_run(w, P, x)
+    assert g["status"] == 0
+    compare(g, oracle_run(w, P, x, 1), w, "bf16", 1, check_weights=False, label="lm-head-square")
+
+
 # ---------------------------------------------------------------------- the five workloads
 def test_toy_fp32_per_token_full(ttt_lib):
     """MLP-only bigram toy: chunk 1 (per-token rule), fp32, all 128 steps."""
