@@ -14,8 +14,8 @@
 // contract over them take them as the B operand in the k-slot order they already have, and
 // read the other operand from LDS in that same order. Each pass can divide its range among
 // several workgroups (k_swa_merge, k_swa_dq_sum and k_swa_dkdv_sum combine the partials in
-// a fixed order). Decoding one row: k_swa_dec_append files its key and value, k_swa_dec and
-// k_swa_dec_merge attend over the window in fp32 (keys and values read in half precision).
+// a fixed order). Decoding one row: k_swa_dec files its key and value and attends over the
+// window in fp32 (keys and values read in half precision), k_swa_dec_merge combines its shares.
 #include "launchers.h"
 #include "common.h"
 
@@ -679,44 +679,52 @@ __global__ void __launch_bounds__(64) k_kv_append(const bf16_t* __restrict__ qkv
 }
 
 // ---------------------------------------------------------------------------- decode
-// One decoded row (position p, its q | k | v in fp32, qkv [3d]): its key and value join the
-// ring first (bf16 and half, as the chunk path stores them), then the attention reads keys
-// max(0, p - window + 1) .. p of the ring (half precision) in fp32 arithmetic. Work: grid (H, nsplit), each
-// workgroup a contiguous share of the keys in blocks of 64, online softmax over the blocks.
+// One decoded row (position p, its q | k | v in fp32, qkv [3d]), grid (H, nsplit): the first
+// share of each head files the head's part of the row's key and value in
+// the ring (bf16 and half, as the chunk path stores them); every share attends over its
+// contiguous run of the keys max(0, p - window + 1) .. p in blocks of 64 (half-precision
+// keys and values, fp32 arithmetic), taking the key and value at p from the row itself (its
+// half-precision values, the ones filed), so that no share reads the slot being written.
 // Per block, four lanes score a key (32 dims each, 16-byte loads, two shuffles), one wave
 // turns the 64 scores into probabilities, and each lane accumulates 8 dims of o over a
 // sixteenth of the keys (16-byte loads of consecutive dims); the sixteenths are summed in
-// LDS at the end. k_swa_dec_merge combines the shares per head.
-constexpr int DEC_KB = 64;  // keys per block of the decode kernel
+// LDS at the end. k_swa_dec_merge combines the shares per head. (Combining them in the
+// share that finishes last, through a per-head counter, needs a device-scope release per
+// share: on this chip that writes the L2 back, and decoding measured 502 against 214 us per
+// token at the 760M fuller block.)
+constexpr int DEC_KB = 64;       // keys per block of the decode kernel
+constexpr int DEC_SPLIT_MAX = 64;
 
-__global__ void __launch_bounds__(NT_A) k_swa_dec_append(const float* __restrict__ qkv, int d, int64_t p, int cr,
-                                                         bf16_t* __restrict__ kc, f16_t* __restrict__ kc16,
-                                                         bf16_t* __restrict__ vc, f16_t* __restrict__ vc16) {
-  const int64_t o = (p % cr) * d;
-  for (int i = threadIdx.x; i < d; i += NT_A) {
-    const float k = qkv[d + i], v = qkv[2 * d + i];
-    kc[o + i] = f2bf(k);
-    kc16[o + i] = f2h(k);
-    vc[o + i] = f2bf(v);
-    vc16[o + i] = f2h(v);
-  }
-}
-
-__global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv, const f16_t* __restrict__ kc,
-                                                  const f16_t* __restrict__ vc, int d, int64_t p, int cr, int window,
+__global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv, bf16_t* __restrict__ kc,
+                                                  f16_t* __restrict__ kc16, bf16_t* __restrict__ vc,
+                                                  f16_t* __restrict__ vc16, int d, int64_t p, int cr, int window,
                                                   float* __restrict__ part) {
   __shared__ float sp[DEC_KB];      // the block's probabilities
   __shared__ float sacc[16][DH];    // per key subset, the partial o
   __shared__ float sml[2];          // the block's (max, sum)
   const int h = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
   const int t = threadIdx.x;
-  // scores: four lanes per key, 32 dims each (16-byte loads)
+  if (split == 0 && t < DH) {
+    const int64_t o = (p % cr) * d + h * DH + t;
+    const float k = qkv[d + h * DH + t], v = qkv[2 * d + h * DH + t];
+    kc[o] = f2bf(k);
+    kc16[o] = f2h(k);
+    vc[o] = f2bf(v);
+    vc16[o] = f2h(v);
+  }
+  // scores: four lanes per key, 32 dims each
   const int kj = t >> 2, kq = (t & 3) * 32;
-  float q[32];
+  float q[32], kown[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) q[i] = qkv[h * DH + kq + i] * 0.08838834764831845f;  // q / sqrt(128)
+  for (int i = 0; i < 32; ++i) {
+    q[i] = qkv[h * DH + kq + i] * 0.08838834764831845f;  // q / sqrt(128)
+    kown[i] = h2f(f2h(qkv[d + h * DH + kq + i]));
+  }
   // values: lane group g of 8 dims, key subset ks (keys ks, ks + 16, ..)
   const int g = (t & 15) * 8, ks = t >> 4;
+  float vown[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) vown[x] = h2f(f2h(qkv[2 * d + h * DH + g + x]));
   int64_t k0 = p - window + 1;
   if (k0 < 0) k0 = 0;
   const int64_t nk = p - k0 + 1;
@@ -732,9 +740,9 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
   auto load = [&](Ops& o, int64_t kb) {
     const int64_t rk = ((kb + kj) % cr) * d + h * DH + kq;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o.k[c] = *(const uint4*)(kc + rk + 8 * c);
+    for (int c = 0; c < 4; ++c) o.k[c] = *(const uint4*)(kc16 + rk + 8 * c);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) o.v[jj] = *(const uint4*)(vc + ((kb + ks + 16 * jj) % cr) * d + h * DH + g);
+    for (int jj = 0; jj < 4; ++jj) o.v[jj] = *(const uint4*)(vc16 + ((kb + ks + 16 * jj) % cr) * d + h * DH + g);
   };
   Ops cur, nxt;
   if (b0 < b1) load(cur, k0 + b0 * DEC_KB);
@@ -744,11 +752,16 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
     {
       const int64_t kp = kb + kj;
       float a = 0.f;
+      if (kp == p) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f16_t* e = (const f16_t*)&cur.k[c];
+        for (int i = 0; i < 32; ++i) a = fmaf(kown[i], q[i], a);
+      } else {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) a = fmaf(h2f(e[x]), q[8 * c + x], a);
+        for (int c = 0; c < 4; ++c) {
+          const f16_t* e = (const f16_t*)&cur.k[c];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) a = fmaf(h2f(e[x]), q[8 * c + x], a);
+        }
       }
       a += __shfl_xor(a, 1, TTT_WAVE);
       a += __shfl_xor(a, 2, TTT_WAVE);
@@ -784,8 +797,13 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
       if (kb + j > p) break;
       const f16_t* e = (const f16_t*)&cur.v[jj];
       const float pj = sp[j];
+      if (kb + j == p) {
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc[x] = fmaf(pj, h2f(e[x]), acc[x]);
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(pj, vown[x], acc[x]);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(pj, h2f(e[x]), acc[x]);
+      }
     }
     __syncthreads();  // sp and sml are rewritten by the next block
     cur = nxt;
@@ -810,7 +828,6 @@ __global__ void __launch_bounds__(NT_A) k_swa_dec(const float* __restrict__ qkv,
 // o [d] = per head, the shares' states combined: grid (H), 128 threads. The shares' maxima
 // and sums go through LDS first (one wave reduces them), so the per-dim sums then issue all
 // their loads independently.
-constexpr int DEC_SPLIT_MAX = 64;
 __global__ void __launch_bounds__(DH) k_swa_dec_merge(const float* __restrict__ part, int nsplit,
                                                       float* __restrict__ o) {
   __shared__ float wts[DEC_SPLIT_MAX];
@@ -969,14 +986,11 @@ int swa_dec_splits(int window) {
 }
 
 hipError_t run_swa_decode(hipStream_t st, const SwaShape& s, const float* qkv, float* part, float* o) {
-  if (!qkv || !part || !o || s.d % DH || s.cr < 1 || s.window < 1 || s.pos < 0 || !s.kc || !s.vc || !s.kc16 ||
-      !s.vc16)
+  if (!qkv || !part || !o || s.d % DH || s.cr < 1 || s.window < 1 || s.pos < 0 || !s.kc || !s.vc || !s.kc16 || !s.vc16)
     return hipErrorInvalidValue;
   const int H = s.d / DH, ns = swa_dec_splits(s.window);
-  hipLaunchKernelGGL(k_swa_dec_append, dim3(1), dim3(NT_A), 0, st, qkv, s.d, s.pos, s.cr, (bf16_t*)s.kc,
-                     (f16_t*)s.kc16, (bf16_t*)s.vc, (f16_t*)s.vc16);
-  hipLaunchKernelGGL(k_swa_dec, dim3(H, ns), dim3(NT_A), 0, st, qkv, (const f16_t*)s.kc16, (const f16_t*)s.vc16, s.d,
-                     s.pos, s.cr, s.window, part);
+  hipLaunchKernelGGL(k_swa_dec, dim3(H, ns), dim3(NT_A), 0, st, qkv, (bf16_t*)s.kc, (f16_t*)s.kc16, (bf16_t*)s.vc,
+                     (f16_t*)s.vc16, s.d, s.pos, s.cr, s.window, part);
   hipLaunchKernelGGL(k_swa_dec_merge, dim3(H), dim3(DH), 0, st, part, ns, o);
   return hipGetLastError();
 }
