@@ -576,6 +576,180 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   epi.template apply<FM, FN, WGM_, WGN_>(pos, acc);
 }
 
+// ---- token-major operands (bf16): C[M x N] = sum over k of X[k][i] Y[k][j], with X [K x M]
+// and Y [K x N] stored row by row (the K index slowest), as the activations and their
+// gradients come out of the chunk's row-major products: the weight gradients read them as
+// they are, with no transposed copy. A K-slice of 64 rows of each operand goes to LDS by
+// direct loads (each 1 KB load fills 64 consecutive 16-byte chunks of the row-major slice
+// tile); the 16-byte chunks of a tile row are XOR-swizzled by km_swz(row), and the MFMA
+// operands come out of LDS through gfx950's transposing read ds_read_b64_tr_b16: within
+// each 16-lane group, lane 4q + w addresses row q, columns 4w .. 4w + 3 of a 4 x 16 block,
+// and lane p receives column p, rows 0 .. 3. Two such reads give a lane the 8 consecutive
+// k of its row that a 32 x 32 x 16 MFMA takes. Needs K a multiple of 64 and M, N multiples
+// of 8.
+// Swizzle of a slice-tile row's 16-byte chunks: the four rows of one transposing read (rows
+// 4a .. 4a + 3) and the two 16-column halves of a 32-row block then fall in distinct bank
+// groups (row pairs 0-1 and 2-3 four chunks apart; the row parity already alternates halves
+// of the bank window when a row is 24 or 16 chunks long... and 8 chunks when it is 32).
+__device__ __forceinline__ int km_swz(int k) { return ((k >> 1) & 1) << 2; }
+
+typedef short km_v4s __attribute__((ext_vector_type(4)));
+// One lane's 8 consecutive k (rows 16 ks + 8 (lane / 32) ..) of tile column c0 + lane % 32,
+// from the slice tile at `tile` (RB bytes per row), as an MFMA operand.
+template <int RB>
+__device__ __forceinline__ uint4 km_operand(const char* tile, int c0, int ks, int lane) {
+  const int g = lane >> 4, rl = lane & 15;
+  const int col = c0 + 16 * (g & 1) + 4 * (rl & 3);
+  const int k = 16 * ks + 8 * (g >> 1) + (rl >> 2);
+  const int jl = col >> 3, within = (col & 7) * 2;
+  const int o0 = k * RB + ((jl ^ km_swz(k)) << 4) + within;
+  const int o1 = (k + 4) * RB + ((jl ^ km_swz(k + 4)) << 4) + within;
+  const km_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) km_v4s*)(tile + o0));
+  const km_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) km_v4s*)(tile + o1));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return make_uint4(ua.x, ua.y, ub.x, ub.y);
+}
+
+// One K-slice of the token-major loop on stage J (as step_slice32): wait until this wave's
+// loads of the stage have landed and its LDS reads are done, barrier, request slice
+// it + S - 1 into the stage read last iteration, multiply stage J.
+template <int RBX, int RBY, int WTM, int WTN, int PW, int S, int J>
+__device__ __forceinline__ void km_step(char* s0, char* s1, char* s2, const char* const (&src)[PW],
+                                        const int64_t (&step)[PW], int it, int n, int dmaoff, int wm, int wn,
+                                        int lane, f32x16_t (&acc)[WTM / 32][WTN / 32]) {
+  constexpr int XB = 64 * RBX;
+  constexpr int NOUT = (S - 2) * PW;
+  __asm__ __volatile__("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NOUT) : "memory");
+  {
+    char* dst = stage_ptr<J + S - 1, S>(s0, s1, s2) + dmaoff;
+    const int64_t kit = min(it + S - 1, n - 1);
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + kit * step[q]),
+                                       (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
+  }
+  const char* tx = stage_ptr<J, S>(s0, s1, s2);
+  const char* ty = tx + XB;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 af[WTM / 32], bfr[WTN / 32];
+#pragma unroll
+    for (int i = 0; i < WTM / 32; ++i) af[i] = km_operand<RBX>(tx, wm * WTM + 32 * i, ks, lane);
+#pragma unroll
+    for (int j = 0; j < WTN / 32; ++j) bfr[j] = km_operand<RBY>(ty, wn * WTN + 32 * j, ks, lane);
+#pragma unroll
+    for (int i = 0; i < WTM / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN / 32; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+  }
+}
+// The K loop: restrict-qualified stage pointers reached through an opaque offset (as in
+// kloop32), so that LDS reads of one stage never wait for the direct loads into another.
+template <int RBX, int RBY, int WTM, int WTN, int PW, int S>
+__device__ __forceinline__ void km_loop(char* __restrict__ s0, char* __restrict__ s1, char* __restrict__ s2,
+                                        const char* const (&src)[PW], const int64_t (&step)[PW], int n, int dmaoff,
+                                        int wm, int wn, int lane, f32x16_t (&acc)[WTM / 32][WTN / 32]) {
+  static_assert(S == 2 || S == 3, "two or three stages");
+#pragma unroll
+  for (int q = 0; q < PW; ++q)
+    __builtin_amdgcn_global_load_lds((const void*)src[q], (__attribute__((address_space(3))) void*)(s0 + dmaoff + q * 1024),
+                                     16, 0, 0);
+  if constexpr (S > 2) {
+    const int64_t k1 = min(1, n - 1);
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + k1 * step[q]),
+                                       (__attribute__((address_space(3))) void*)(s1 + dmaoff + q * 1024), 16, 0, 0);
+  }
+  for (int it = 0; it < n; it += S) {
+    km_step<RBX, RBY, WTM, WTN, PW, S, 0>(s0, s1, s2, src, step, it, n, dmaoff, wm, wn, lane, acc);
+    if (it + 1 < n) km_step<RBX, RBY, WTM, WTN, PW, S, 1>(s0, s1, s2, src, step, it + 1, n, dmaoff, wm, wn, lane, acc);
+    if constexpr (S > 2)
+      if (it + 2 < n) km_step<RBX, RBY, WTM, WTN, PW, S, 2>(s0, s1, s2, src, step, it + 2, n, dmaoff, wm, wn, lane, acc);
+  }
+  __syncthreads();  // every request has landed and every read is done: the LDS is free
+}
+
+template <int BM, int BN, int WGM, int WGN, class Epi>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_km_kernel(GemmArgs g, Epi epi) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM32 = WTM / 32, FN32 = WTN / 32;
+  constexpr int RBX = 2 * BM, RBY = 2 * BN;          // bytes per slice-tile row
+  constexpr int XB = 64 * RBX, YB = 64 * RBY;        // bytes per slice tile
+  constexpr int STAGE = XB + YB;
+  constexpr int S = gemm_stages(BM, BN);  // 128 x 128: two stages, two workgroups per CU
+  constexpr int NL = STAGE / 1024;                   // 1 KB direct loads per slice
+  constexpr int PW = NL / NW;
+  static_assert(XB % 1024 == 0 && YB % 1024 == 0 && NL % NW == 0, "whole 1 KB loads per wave");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BM % 64 == 0 && BN % 64 == 0, "32 x 32 blocks, 8-chunk rows");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const GemmWork w = gemm_work(g);
+  const int tile = w.tile;
+  const int tm = tile % g.tiles_m, tn = tile / g.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const char *gX, *gY, *gX2, *gY2;
+  gemm_group_bases<bf16_t>(g, w.z, gX, gY, gX2, gY2);
+  // this lane's source of each of the wave's loads (slice 0), and the step to the next slice
+  const char* src[PW];
+  int64_t step[PW];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    const int t = wave_s * PW + q;           // load index within the stage
+    const bool xs = t < XB / 1024;
+    const int tl = xs ? t : t - XB / 1024;   // within the operand's tile
+    const int cpr = (xs ? RBX : RBY) / 16;   // chunks per tile row
+    const int c = 64 * tl + lane;
+    const int k = c / cpr, jp = c - k * cpr;
+    const int jl = jp ^ km_swz(k);
+    const int lim = xs ? g.M : g.N, base = xs ? m0 : n0;
+    int col = base + 8 * jl;
+    if (col > lim - 8) col = lim - 8;        // columns past the edge: a valid chunk, masked later
+    const int64_t ld = xs ? g.ldx : g.ldy;
+    src[q] = (xs ? gX : gY) + ((int64_t)k * ld + col) * 2;
+    step[q] = 64 * ld * 2;
+  }
+  f32x16_t acc32[FM32][FN32];
+#pragma unroll
+  for (int i = 0; i < FM32; ++i)
+#pragma unroll
+    for (int j = 0; j < FN32; ++j) acc32[i][j] = f32x16_t{};
+  int zero;
+  __asm__ __volatile__("s_mov_b32 %0, 0" : "=s"(zero));
+  char* const sm = smem + zero;
+  km_loop<RBX, RBY, WTM, WTN, PW, S>(sm, sm + STAGE, S > 2 ? sm + 2 * STAGE : sm + STAGE, src, step, g.kiters,
+                                     (wave_s * PW) * 1024, wm, wn, lane, acc32);
+  f32x4_t acc[WTM / 16][WTN / 16];
+  acc32_to_16<FM32, FN32>(smem, wave, lane, acc32, acc);
+  __syncthreads();
+  EpiPos pos;
+  pos.row0 = w.z * g.M + m0 + wm * WTM;
+  pos.col0 = n0 + wn * WTN;
+  pos.lane = lane;
+  pos.wave = wave;
+  pos.wm = wm;
+  pos.wn = wn;
+  pos.wgm = WGM;
+  pos.wgn = WGN;
+  pos.bm = BM;
+  pos.bn = BN;
+  pos.tid = tid;
+  pos.nthr = NW * 64;
+  pos.smem_bytes = S * STAGE;
+  pos.tm = tm;
+  pos.tn = tn;
+  pos.tile = w.z * g.gtile + tile;
+  pos.split = 0;
+  pos.M = (w.z + 1) * g.M;
+  pos.N = g.N;
+  pos.smem = smem;
+  epi.template apply<WTM / 16, WTN / 16, WGM, WGN>(pos, acc);
+}
+
 // ------------------------------------------------------------------------- epilogues
 // Store 4 vertically adjacent outputs (rows r..r+3 of one column) into a transposed
 // matrix, i.e. 4 consecutive elements of one row of C^T. Packs the store when possible.
@@ -1510,6 +1684,22 @@ inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, int 
     lds_attr = true;
   }
   dim3 grid(g.tiles_m * g.tiles_n, splits, groups);
+  hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, g, epi);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, class Epi>
+inline hipError_t launch_km(hipStream_t st, const GemmArgs& g, int groups, const Epi& epi) {
+  constexpr int STAGE = 64 * 2 * (BM + BN);
+  constexpr size_t lds = (size_t)gemm_stages(BM, BN) * STAGE;
+  auto kern = gemm_km_kernel<BM, BN, WGM, WGN, Epi>;
+  static bool lds_attr = false;  // per instantiation
+  if (!lds_attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_attr = true;
+  }
+  dim3 grid(g.tiles_m * g.tiles_n, 1, groups);
   hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, g, epi);
   return hipGetLastError();
 }

@@ -122,6 +122,38 @@ hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const
   });
 }
 
+hipError_t gemm_grad_km(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N, int K,
+                        void* G, int64_t ldg, float* slot, const GemmGroup& gg) {
+  if (M <= 0 || N <= 0 || gg.n <= 0) return hipSuccess;
+  if (K <= 0 || K % 64 || M % 8 || N % 8 || gg.n > 65535) return hipErrorInvalidValue;
+  EpiGrad<bf16_t> e{(bf16_t*)G, ldg, slot};
+  GemmArgs g{};
+  g.X = X;
+  g.Y = Y;
+  g.ldx = ldx;
+  g.ldy = ldy;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.kit_a = g.kiters = g.kps = K / 64;
+  g.gx = gg.x;
+  g.gy = gg.y;
+  g.gtile = gg.tile;
+  // the same output tiles as the row-major path (per-tile slots are sized from them)
+  const TilePlan t = gemm_plan(M, N, K, 0, 2, 1);
+  if (t.bm == 192 && t.bn == 192) {
+    g.tiles_m = (M + 191) / 192;
+    g.tiles_n = (N + 191) / 192;
+    return launch_km<192, 192, 2, 2>(st, g, gg.n, e);
+  }
+  if (t.bm == 128 && t.bn == 128) {
+    g.tiles_m = (M + 127) / 128;
+    g.tiles_n = (N + 127) / 128;
+    return launch_km<128, 128, 2, 2>(st, g, gg.n, e);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t gemm_ce_partial(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M,
                            int N, int K, const int* tgt, float* pmax, float* psum, int* pidx, float* tgt_logit,
                            int nrec, void* Q, int64_t ldq, const GemmSeg2& s2) {

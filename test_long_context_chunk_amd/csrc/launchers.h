@@ -192,6 +192,12 @@ int gemm_split_k(int prec, int M, int N, int K, int K2, int max_splits);
 // fp32 accumulators per output tile in slot[tile].
 hipError_t gemm_grad(hipStream_t st, int prec, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N,
                      int K, void* G, int64_t ldg, float* slot, const GemmGroup& gg = GemmGroup());
+// The same weight gradient from token-major operands (bf16): G [M x ldg] = sum over k < K
+// of X[k][i] Y[k][j], X [K x ldx], Y [K x ldy] row-major (the activations as the forward
+// and backward products write them); K a multiple of 64, M and N multiples of 8. Same tiles
+// and slots as gemm_grad with K token columns; hipErrorInvalidValue for other shapes.
+hipError_t gemm_grad_km(hipStream_t st, const void* X, int64_t ldx, const void* Y, int64_t ldy, int M, int N, int K,
+                        void* G, int64_t ldg, float* slot, const GemmGroup& gg = GemmGroup());
 // LM head + online-softmax partials over the full vocabulary (N = V): one record per row and
 // per wave column block of gemm_wave_cols() vocabulary entries (records [M x nrec]), and,
 // when Q is non-null, the numerators exp(z - record max) [M x ldq] in the GEMM precision.

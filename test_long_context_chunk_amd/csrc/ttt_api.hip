@@ -46,7 +46,8 @@ struct Block {
   void* Hn = nullptr;       // normed block input [R x d]
   void* HnT = nullptr;      // its transpose [d x Rp]
   float* r = nullptr;       // RMSNorm scale per token [R]
-  void* AT = nullptr;       // activation transpose [m x Rp]
+  void* AT = nullptr;       // activation transpose [m x Rp] (weight gradients from transposed operands)
+  void* A = nullptr;        // activation [R x m] (weight gradients from token-major operands)
   void* GP = nullptr;       // GELU'(U) [R x m]
   void* ResN = nullptr;     // bf16 only: n - rn(n) [R x d]
   void* ResA = nullptr;     // bf16 only: A - rn(A) [R x m]
@@ -99,6 +100,9 @@ struct ttt_ctx {
   // independent token streams advanced together (each with its own fast state, records and
   // clip); a step covers R = nb b token rows, Rp = nb bp columns of the transposed buffers
   int nb = 1, R = 0, Rp = 0;
+  // bf16 training with whole 64-token slices: the weight gradients read the activations and
+  // their gradients token-major (no transposed copies)
+  bool km = false;
   int ms = 0;          // hidden size of the static MLP of every block (0: none)
   int window = 0;      // keys per query of the attention of every block (0: none)
   int cr = 0;          // ring positions per stream and block (window + chunk)
@@ -372,8 +376,10 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
     if (c->cfg.mlp == TTT_MLP_GELU) {
       init_fast(c, B.w1, d, m, w->w1[l]);
       B.GP = dalloc<char>(c, (int64_t)Rr * m * es);
-      B.HnT = dalloc<char>(c, (int64_t)d * Rp * es);
-      check(hipMemsetAsync(B.HnT, 0, (int64_t)d * Rp * es, c->st));
+      if (!c->km) {
+        B.HnT = dalloc<char>(c, (int64_t)d * Rp * es);
+        check(hipMemsetAsync(B.HnT, 0, (int64_t)d * Rp * es, c->st));
+      }
     } else {
       B.WgT = dalloc<char>(c, (int64_t)m * d * es);
       B.WuT = dalloc<char>(c, (int64_t)m * d * es);
@@ -440,8 +446,12 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
     }
     B.Hn = dalloc<char>(c, (int64_t)Rr * d * es);
     B.r = dalloc<float>(c, (int64_t)Rr * 4);
-    B.AT = dalloc<char>(c, (int64_t)m * Rp * es);
-    check(hipMemsetAsync(B.AT, 0, (int64_t)m * Rp * es, c->st));
+    if (c->km) {
+      B.A = dalloc<char>(c, (int64_t)Rr * m * es);
+    } else {
+      B.AT = dalloc<char>(c, (int64_t)m * Rp * es);
+      check(hipMemsetAsync(B.AT, 0, (int64_t)m * Rp * es, c->st));
+    }
     if (res) {
       B.ResN = dalloc<char>(c, (int64_t)Rr * d * es);
       B.ResA = dalloc<char>(c, (int64_t)Rr * m * es);
@@ -485,12 +495,16 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   c->dec_ridx = dalloc<int>(c, (int64_t)cdiv(V, gemv_rec_rows(V)) * 4);
   c->dH = dalloc<float>(c, (int64_t)Rr * d * 4);
   c->dHb = dalloc<char>(c, (int64_t)Rr * d * es);
-  c->dHT = dalloc<char>(c, (int64_t)d * Rp * es);
-  check(hipMemsetAsync(c->dHT, 0, (int64_t)d * Rp * es, c->st));
+  if (!c->km) {
+    c->dHT = dalloc<char>(c, (int64_t)d * Rp * es);
+    check(hipMemsetAsync(c->dHT, 0, (int64_t)d * Rp * es, c->st));
+  }
   c->A = dalloc<char>(c, (int64_t)Rr * mx * es);
   c->dU = dalloc<char>(c, (int64_t)Rr * mx * es);
-  c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
-  check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
+  if (!c->km) {
+    c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
+    check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
+  }
   if (c->cfg.mlp == TTT_MLP_SWIGLU_W2) c->UG = dalloc<float>(c, (int64_t)Rr * m * 4);
   if (c->window > 0 && L > 0) {
     c->dec_qkv = dalloc<float>(c, (int64_t)3 * d * 4);
@@ -625,6 +639,14 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     g.tile = (int)slot_stride;
     return g;
   };
+  auto gradkm = [&](int64_t ldx, int64_t ldy, int64_t slot_stride) {  // the same, token-major: a stream's rows
+    GemmGroup g;
+    g.n = nb;
+    g.x = (int64_t)b * ldx;
+    g.y = (int64_t)b * ldy;
+    g.tile = (int)slot_stride;
+    return g;
+  };
 
   const int ms = c->ms;
   // where a row kernel leaves the pre-norm of the next MLP: block l's static MLP (when the
@@ -695,7 +717,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     }
     if (gelu) {
       // Hn^T is read only by the W1 gradient of the backward pass
-      if (train) check(run_transpose(st, prec, B.Hn, d, Rr, d, B.HnT, Rp));
+      if (train && !c->km) check(run_transpose(st, prec, B.Hn, d, Rr, d, B.HnT, Rp));
       check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
@@ -703,18 +725,19 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       if (split)
         RUN(TTT_K_UP, gemm_f32(st, prec, B.ResN, d, B.w1.W0T, d, b, m, d, 1, c->Ul, m, 0, 0, GemmSeg2(),
                                fw(b, d, n1, true)));
-      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->A, B.AT, B.GP,
+      RUN(TTT_K_UP, gemm_gelu(st, prec, B.Hn, d, bf ? B.w1.W0T : B.w1.WtT, d, b, m, d, c->km ? B.A : c->A, B.AT, B.GP,
                               keep_res ? B.ResA : nullptr, m, Rp, s2, fw(b, d, n1, bf), split ? c->Ul : nullptr));
     } else {
       RUN(TTT_K_UP, gemm_f32(st, prec, B.Hn, d, B.WgT, d, Rr, m, d, 1, c->UG, m, 0, 0));
-      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, Rr, m, d, c->UG, foc ? B.VU : nullptr, c->A, B.AT,
+      RUN(TTT_K_UP, gemm_swiglu(st, prec, B.Hn, d, B.WuT, d, Rr, m, d, c->UG, foc ? B.VU : nullptr, c->km ? B.A : c->A, B.AT,
                                 foc ? B.ResA : nullptr, m, Rp));
     }
     const int S = gemm_split_k(prec, Rr, d, m, bf ? m : 0, SPLIT_MAX);
     check(hipStreamWaitEvent(st, B.w2.ev_upd, 0));  // the previous chunk's step of W2
     GemmSeg2 s2;
-    if (bf) s2 = GemmSeg2{c->A, m, B.w2.WtT, m, m};
-    RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, Rd, 0, s2,
+    void* const Ablk = c->km ? B.A : c->A;  // this block's activation
+    if (bf) s2 = GemmSeg2{Ablk, m, B.w2.WtT, m, m};
+    RUN(TTT_K_DOWN, gemm_f32(st, prec, Ablk, m, bf ? B.w2.W0T : B.w2.WtT, m, b, d, m, S, c->part, d, Rd, 0, s2,
                              fw(b, m, n2, bf)));
     int St = S;  // slabs the residual sums
     if (split) {
@@ -750,7 +773,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, Rd, Rr, d, c->dH, c->dHb, c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
     // dH^T, read by the W2 gradient
-    if (train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+    if (train && !c->km) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
 
     // a7 block backward, top to bottom
     for (int l = L - 1; l >= 0; --l) {
@@ -758,13 +781,20 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       float* cA = foc ? c->cpart + (int64_t)B.cslot * Rr : nullptr;        // tnm slots
       float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * Rr : nullptr;  // one slot
       if (gelu) {
-        RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->dUT,
+        RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->km ? nullptr : c->dUT,
                               foc ? B.ResA : nullptr, cA, m, Rp, Rr, fw(b, d, n2, false)));
         if (train) {
-          RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
-                                  gradg(c->nslots)));
-          RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, Rp, c->dUT, Rp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0,
-                                  gradg(c->nslots)));
+          if (c->km) {
+            RUN(TTT_K_DW, gemm_grad_km(st, B.A, m, c->dHb, d, m, d, b, B.w2.G, d, c->slots + B.w2.slot0,
+                                       gradkm(m, d, c->nslots)));
+            RUN(TTT_K_DW, gemm_grad_km(st, B.Hn, d, c->dU, m, d, m, b, B.w1.G, m, c->slots + B.w1.slot0,
+                                       gradkm(d, m, c->nslots)));
+          } else {
+            RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
+                                    gradg(c->nslots)));
+            RUN(TTT_K_DW, gemm_grad(st, prec, B.HnT, Rp, c->dUT, Rp, d, m, bp, B.w1.G, m, c->slots + B.w1.slot0,
+                                    gradg(c->nslots)));
+          }
         }
         // Which input gradients this block needs, going down (fast MLP, static MLP,
         // attention): a sublayer's input gradient is needed when a fast block lies below, or
@@ -814,10 +844,14 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           }
         }
         // dH^T at this block's input, read by the W2 gradient of the block below
-        if (l > 0 && train) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
+        if (l > 0 && train && !c->km) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
       } else if (train) {
-        RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
-                                gradg(c->nslots)));
+        if (c->km)
+          RUN(TTT_K_DW, gemm_grad_km(st, B.A, m, c->dHb, d, m, d, b, B.w2.G, d, c->slots + B.w2.slot0,
+                                     gradkm(m, d, c->nslots)));
+        else
+          RUN(TTT_K_DW, gemm_grad(st, prec, B.AT, Rp, c->dHT, Rp, m, d, bp, B.w2.G, d, c->slots + B.w2.slot0,
+                                  gradg(c->nslots)));
       }
       if (!gelu && foc) {
         // SwiGLU (one block, W2 only fast): dA, then dn = dG Wg^T + dV Wu^T, only to carry
@@ -1108,6 +1142,7 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   c->nb = streams;
   c->R = streams * c->b;
   c->Rp = streams * c->bp;
+  c->km = c->prec == PREC_BF16 && c->b % 64 == 0 && c->b <= 1024;
   c->ms = ext ? ext->static_hidden : 0;
   c->window = ext ? ext->swa_window : 0;
   // ring positions: the window, plus the b positions a pending decoded chunk writes before
