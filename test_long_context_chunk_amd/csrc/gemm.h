@@ -581,17 +581,21 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
 // gradients come out of the chunk's row-major products: the weight gradients read them as
 // they are, with no transposed copy. A K-slice of 64 rows of each operand goes to LDS by
 // direct loads (each 1 KB load fills 64 consecutive 16-byte chunks of the row-major slice
-// tile); the 16-byte chunks of a tile row are XOR-swizzled by km_swz(row), and the MFMA
+// tile); the 16-byte chunks of a tile row are XOR-swizzled by km_swz, and the MFMA
 // operands come out of LDS through gfx950's transposing read ds_read_b64_tr_b16: within
 // each 16-lane group, lane 4q + w addresses row q, columns 4w .. 4w + 3 of a 4 x 16 block,
 // and lane p receives column p, rows 0 .. 3. Two such reads give a lane the 8 consecutive
 // k of its row that a 32 x 32 x 16 MFMA takes. Needs K a multiple of 64 and M, N multiples
 // of 8.
-// Swizzle of a slice-tile row's 16-byte chunks: the four rows of one transposing read (rows
-// 4a .. 4a + 3) and the two 16-column halves of a 32-row block then fall in distinct bank
-// groups (row pairs 0-1 and 2-3 four chunks apart; the row parity already alternates halves
-// of the bank window when a row is 24 or 16 chunks long... and 8 chunks when it is 32).
-__device__ __forceinline__ int km_swz(int k) { return ((k >> 1) & 1) << 2; }
+// Swizzle of a slice-tile row's 16-byte chunks (cpr chunks per row). Half a wave's
+// transposing read covers 4 consecutive rows x 4 aligned chunks; these 16 chunks take
+// distinct 16-byte slots of the 256-byte bank window when every row's 4 chunks land in a
+// quarter of their own. Rows of a multiple of 16 chunks all start at the same slot: XOR the
+// chunk index with 4 (k mod 4). Rows of 24 chunks (192 columns): odd rows already start
+// half a window away, so 4 ((k / 2) mod 2) suffices (and keeps the XOR within the row).
+__device__ __forceinline__ int km_swz(int k, int cpr) {
+  return (cpr & 15) == 0 ? (k & 3) << 2 : ((k >> 1) & 1) << 2;
+}
 
 typedef short km_v4s __attribute__((ext_vector_type(4)));
 // One lane's 8 consecutive k (rows 16 ks + 8 (lane / 32) ..) of tile column c0 + lane % 32,
@@ -602,8 +606,8 @@ __device__ __forceinline__ uint4 km_operand(const char* tile, int c0, int ks, in
   const int col = c0 + 16 * (g & 1) + 4 * (rl & 3);
   const int k = 16 * ks + 8 * (g >> 1) + (rl >> 2);
   const int jl = col >> 3, within = (col & 7) * 2;
-  const int o0 = k * RB + ((jl ^ km_swz(k)) << 4) + within;
-  const int o1 = (k + 4) * RB + ((jl ^ km_swz(k + 4)) << 4) + within;
+  const int o0 = k * RB + ((jl ^ km_swz(k, RB / 16)) << 4) + within;
+  const int o1 = (k + 4) * RB + ((jl ^ km_swz(k + 4, RB / 16)) << 4) + within;
   const km_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) km_v4s*)(tile + o0));
   const km_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) km_v4s*)(tile + o1));
   const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
@@ -630,17 +634,26 @@ __device__ __forceinline__ void km_step(char* s0, char* s1, char* s2, const char
   }
   const char* tx = stage_ptr<J, S>(s0, s1, s2);
   const char* ty = tx + XB;
+  __builtin_amdgcn_iglp_opt(0);  // let the scheduler interleave the LDS reads with the MFMAs
+  // the operands of k-step ks + 1 are read while the MFMAs of k-step ks run
+  uint4 af[2][WTM / 32], bfr[2][WTN / 32];
+#pragma unroll
+  for (int i = 0; i < WTM / 32; ++i) af[0][i] = km_operand<RBX>(tx, wm * WTM + 32 * i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < WTN / 32; ++j) bfr[0][j] = km_operand<RBY>(ty, wn * WTN + 32 * j, 0, lane);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    uint4 af[WTM / 32], bfr[WTN / 32];
+    const int c = ks & 1;
+    if (ks < 3) {
 #pragma unroll
-    for (int i = 0; i < WTM / 32; ++i) af[i] = km_operand<RBX>(tx, wm * WTM + 32 * i, ks, lane);
+      for (int i = 0; i < WTM / 32; ++i) af[c ^ 1][i] = km_operand<RBX>(tx, wm * WTM + 32 * i, ks + 1, lane);
 #pragma unroll
-    for (int j = 0; j < WTN / 32; ++j) bfr[j] = km_operand<RBY>(ty, wn * WTN + 32 * j, ks, lane);
+      for (int j = 0; j < WTN / 32; ++j) bfr[c ^ 1][j] = km_operand<RBY>(ty, wn * WTN + 32 * j, ks + 1, lane);
+    }
 #pragma unroll
     for (int i = 0; i < WTM / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < WTN / 32; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+      for (int j = 0; j < WTN / 32; ++j) mfma32(acc[i][j], af[c][i], bfr[c][j]);
   }
 }
 // The K loop: restrict-qualified stage pointers reached through an opaque offset (as in
@@ -705,7 +718,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_km_kernel(GemmArgs g, Epi
     const int cpr = (xs ? RBX : RBY) / 16;   // chunks per tile row
     const int c = 64 * tl + lane;
     const int k = c / cpr, jp = c - k * cpr;
-    const int jl = jp ^ km_swz(k);
+    const int jl = jp ^ km_swz(k, cpr);
     const int lim = xs ? g.M : g.N, base = xs ? m0 : n0;
     int col = base + 8 * jl;
     if (col > lim - 8) col = lim - 8;        // columns past the edge: a valid chunk, masked later

@@ -260,6 +260,20 @@ def test_narrow_tile_products_ragged(ttt_lib):
     compare(g, oracle_run(w, P, x, 3), w, "bf16", 3, label="narrow-tiles")
 
 
+def test_token_major_gradients_ragged(ttt_lib):
+    """bf16 weight gradients read the activations token-major when the chunk is a whole
+    number of 64-token slices: here chunk 192 (three slices, an odd count against the
+    two-stage loop) with d = 1000 and m = 1096, neither a multiple of the 128-row tiles, so
+    the edge tiles clamp their columns and mask their outputs; three chunks, every gate."""
+    w = W.preset("s125m", vocab=3000, d_model=1000, d_hidden=1096, n_blocks=2, n_tokens=576, chunk=192, lr=0.05)
+    P = W.init_weights(w, 7)
+    x = W.token_stream(w, 8)
+    log("token-major gradients: d=1000 m=1096 b=192")
+    g = gpu_run(w, P, x)
+    assert g["status"] == 0
+    compare(g, oracle_run(w, P, x, 3), w, "bf16", 3, label="token-major")
+
+
 # ---------------------------------------------------------------------- determinism, errors
 def test_runs_are_bitwise_deterministic(ttt_lib):
     w, x, P = inputs("single")
