@@ -638,8 +638,9 @@ def workload_bench(w, P, x, steps: int, warmup: int, keep_ctx: bool = False, see
     return out
 
 
-# The other workloads of the survey's table, measured beside the headline: name, oracle chunks
-# timed for their CPU baseline (about 2 - 10 s each on 16 host cores).
+# The other preset workloads (one block at d 768, three blocks at d 768, the In-Place shape),
+# measured beside the headline: name, oracle chunks timed for their CPU baseline (about 2 - 10 s
+# each on 16 host cores).
 OTHER_WORKLOADS = [("single", 8), ("s125m", 16), ("inplace", 4)]
 
 
