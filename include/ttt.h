@@ -369,6 +369,21 @@ const char* ttt_status_string(ttt_status s);
 ttt_status ttt_test_gemm(int32_t precision, const void* X, int64_t ldx, const void* Y, int64_t ldy,
                          float* C, int64_t ldc, int32_t M, int32_t N, int32_t K, void* stream);
 
+/* Test hook: the library's weight-gradient GEMM (bf16), G = sum over k < K of X_k^T Y_k
+ * ([E2E] eq. 5: a fast tensor's chunk gradient, summed over the chunk's tokens), stored in
+ * bf16 into G [M x N] (row stride ldg), and each output tile's sum of squared fp32 values
+ * into slots[tile] (the partials of the global gradient norm, [SGF] "how it works").
+ *   token_major = 1: X [K x M], Y [K x N] row-major (row strides ldx, ldy): the activations
+ *     as the chunk's products write them; K a multiple of 64, M and N multiples of 8.
+ *   token_major = 0: X [M x K], Y [N x K] row-major: their transposed copies; K a multiple of
+ *     64.
+ * Both forms run the same output tiles (192 x 192 or 128 x 128, by shape); slots must hold
+ * at least ceil(M / 128) ceil(N / 128) floats. Device pointers, 16-byte aligned rows;
+ * enqueued on `stream`. It exposes the kernels the inner loop uses so that the two operand
+ * layouts can be compared; it is not a second code path. Errors: TTT_EINVAL. */
+ttt_status ttt_test_grad(const void* X, int64_t ldx, const void* Y, int64_t ldy, void* G, int64_t ldg,
+                         float* slots, int32_t M, int32_t N, int32_t K, int32_t token_major, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,8 @@ SIGNATURES = {
     "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "ttt_test_gemm": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                 c_int32, c_int32, c_int32, c_void_p]),
+    "ttt_test_grad": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int32,
+                                c_int32, c_int32, c_int32, c_void_p]),
 }
 
 
@@ -364,6 +366,25 @@ class TTT:
             self.close()
         except Exception:
             pass
+
+
+def grad_test_hook(X, Y, token_major: bool, stream=None):
+    """The weight-gradient GEMM (bf16 G and per-tile sums of squares) through the library's
+    kernels (test hook). token_major: X [K x M], Y [K x N]; else X [M x K], Y [N x K]."""
+    import torch
+    lib = load_library()
+    if token_major:
+        K, M = X.shape
+        N = Y.shape[1]
+    else:
+        M, K = X.shape
+        N = Y.shape[0]
+    G = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    slots = torch.zeros(((M + 127) // 128) * ((N + 127) // 128), dtype=torch.float32, device="cuda")
+    _check(lib.ttt_test_grad(c_void_p(_ptr(X)), X.stride(0), c_void_p(_ptr(Y)), Y.stride(0), c_void_p(_ptr(G)), N,
+                             c_void_p(_ptr(slots)), M, N, K, 1 if token_major else 0,
+                             c_void_p(_stream_handle(stream))), "ttt_test_grad")
+    return G, slots
 
 
 def gemm_test_hook(X, Y, precision: str, stream=None):

@@ -1490,4 +1490,19 @@ ttt_status ttt_test_gemm(int32_t precision, const void* X, int64_t ldx, const vo
   return e == hipSuccess ? TTT_OK : TTT_EDEVICE;
 }
 
+ttt_status ttt_test_grad(const void* X, int64_t ldx, const void* Y, int64_t ldy, void* G, int64_t ldg, float* slots,
+                         int32_t M, int32_t N, int32_t K, int32_t token_major, void* stream) {
+  if (!X || !Y || !G || !slots || M <= 0 || N <= 0 || K <= 0 || K % 64 || ldg < N || ldg % 8) return TTT_EINVAL;
+  if (token_major != 0 && token_major != 1) return TTT_EINVAL;
+  if (token_major) {
+    if (M % 8 || N % 8 || ldx < M || ldy < N || ldx % 8 || ldy % 8) return TTT_EINVAL;
+  } else if (ldx < K || ldy < K || ldx % 8 || ldy % 8) {
+    return TTT_EINVAL;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = token_major ? gemm_grad_km(st, X, ldx, Y, ldy, M, N, K, G, ldg, slots)
+                                   : gemm_grad(st, PREC_BF16, X, ldx, Y, ldy, M, N, K, G, ldg, slots);
+  return e == hipSuccess ? TTT_OK : e == hipErrorInvalidValue ? TTT_EINVAL : TTT_EDEVICE;
+}
+
 }  // extern "C"

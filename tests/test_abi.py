@@ -155,6 +155,12 @@ def test_gemm_hook_validates_shapes(lib):
     assert lib.ttt_test_gemm(1, 1, 8, 1, 8, 1, 8, 4, 4, 6, None) == -1
     assert lib.ttt_test_gemm(0, 1, 8, 1, 8, 1, 8, 4, 4, 6, None) == -1
     assert lib.ttt_test_gemm(7, 1, 8, 1, 8, 1, 8, 4, 4, 8, None) == -1
+    # the gradient hook: K not a multiple of 64, M not a multiple of 8 (token-major), a bad
+    # layout flag, NULL operands
+    assert lib.ttt_test_grad(1, 64, 1, 64, 1, 64, 1, 64, 64, 32, 1, None) == -1
+    assert lib.ttt_test_grad(1, 64, 1, 64, 1, 64, 1, 60, 64, 64, 1, None) == -1
+    assert lib.ttt_test_grad(1, 64, 1, 64, 1, 64, 1, 64, 64, 64, 2, None) == -1
+    assert lib.ttt_test_grad(None, 64, 1, 64, 1, 64, 1, 64, 64, 64, 1, None) == -1
 
 
 def test_kernel_kind_names_match_the_header():

@@ -39,6 +39,48 @@ def test_gemm_tile_engine_ragged(ttt_lib, precision, M, N, K):
     assert np.all(np.abs(C - ref) <= bound), float(np.max(np.abs(C - ref) / bound))
 
 
+# ---------------------------------------------------------------------- weight-gradient GEMM
+# (M, N, K): the 760M W2 and W1 gradients (192 x 192 tiles), the fuller block's (128 x 128),
+# ragged 128-row tiles over three and one 64-token slices, one 8 x 8 tile.
+GRAD_SHAPES = [(6144, 1536, 1024), (1536, 6144, 1024), (3072, 1536, 1024), (1096, 1000, 192), (1000, 1096, 64),
+               (8, 8, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", GRAD_SHAPES)
+def test_grad_token_major_matches_transposed(ttt_lib, M, N, K):
+    """A chunk gradient G = X^T Y over K tokens ([E2E] eq. 5) from the token-major operands
+    (as the chunk's products write them) and from their transposed copies: both within the
+    fp32-accumulation bound of the fp64 product plus one bf16 rounding, and their per-tile
+    sums of squares (the grad-norm partials) within 1e-4 of the fp64 sum. On 192 x 192 tiles
+    both kernels feed the MFMAs the same k order, so G and the partials are bitwise equal."""
+    import torch
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    X = W.round_to_bf16(rng.standard_normal((K, M)).astype(np.float32))
+    Y = W.round_to_bf16(rng.standard_normal((K, N)).astype(np.float32))
+    Xd = torch.from_numpy(X).to(torch.bfloat16).cuda()
+    Yd = torch.from_numpy(Y).to(torch.bfloat16).cuda()
+    log(f"grad M={M} N={N} K={K}")
+    Gk, sk = ttt_lib.grad_test_hook(Xd, Yd, True)
+    Gt, st = ttt_lib.grad_test_hook(Xd.t().contiguous(), Yd.t().contiguous(), False)
+    torch.cuda.synchronize()
+    ref = X.astype(np.float64).T @ Y.astype(np.float64)
+    bound = (K + 2) * 2.0 ** -24 * (np.abs(X).astype(np.float64).T @ np.abs(Y).astype(np.float64))
+    bound += 2.0 ** -8 * np.abs(ref) + 1e-30
+    for G in (Gk, Gt):
+        g = G.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(g - ref) <= bound), float(np.max(np.abs(g - ref) / bound))
+    ss = float(np.sum(ref * ref))
+    for sl in (sk, st):
+        assert abs(float(sl.double().sum().item()) - ss) <= 1e-4 * ss
+    # the planner's choice for short K: 192 x 192 tiles when they leave fewer outputs per CU
+    # over their rounds (256 workgroups a round) than 128 x 128 tiles (512 a round)
+    t192 = ((M + 191) // 192) * ((N + 191) // 192)
+    t128 = ((M + 127) // 128) * ((N + 127) // 128)
+    if (t192 + 255) // 256 * 192 * 192 < (t128 + 511) // 512 * 2 * 128 * 128:
+        assert torch.equal(Gk, Gt)
+        assert torch.equal(sk, st)
+
+
 # ---------------------------------------------------------------------- gather (bit-exact ids)
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
 def test_gather_rows_are_exact(ttt_lib, precision):
