@@ -173,6 +173,14 @@ struct ttt_ctx {
   // main stream, and the main stream waits for its event right before the consumer
   hipStream_t aux = nullptr;
   hipEvent_t ev_to_aux = nullptr, ev_from_aux = nullptr;
+  // GELU blocks without frozen layers, token-major gradients: each block's two weight
+  // gradients run on the aux stream beside the main stream's dHn, norm backward and the next
+  // block's dA. The backward row buffers then alternate by block parity (dHb / dHb2 hold the
+  // gradient at the output of even / odd blocks, dU / dU2 their dU), and ev_grad[l & 1] marks
+  // block l's gradients done.
+  bool agrad = false;
+  void *dHb2 = nullptr, *dU2 = nullptr;
+  hipEvent_t ev_gin = nullptr, ev_grad[2] = {nullptr, nullptr};
 
   // tracing: event pairs around launches of the kinds set in prof_mask
   uint32_t prof_mask = 0;
@@ -501,6 +509,10 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   }
   c->A = dalloc<char>(c, (int64_t)Rr * mx * es);
   c->dU = dalloc<char>(c, (int64_t)Rr * mx * es);
+  if (c->agrad) {
+    c->dHb2 = dalloc<char>(c, (int64_t)Rr * d * es);
+    c->dU2 = dalloc<char>(c, (int64_t)Rr * mx * es);
+  }
   if (!c->km) {
     c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
     check(hipMemsetAsync(c->dUT, 0, (int64_t)m * Rp * es, c->st));
@@ -547,6 +559,8 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   check(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
   check(hipEventCreateWithFlags(&c->ev_to_aux, kSyncEvent));
   check(hipEventCreateWithFlags(&c->ev_from_aux, kSyncEvent));
+  if (c->agrad)
+    for (hipEvent_t* e : {&c->ev_gin, &c->ev_grad[0], &c->ev_grad[1]}) check(hipEventCreateWithFlags(e, kSyncEvent));
 }
 
 // Wait for the aux stream, then release it (before any buffer it may read is freed).
@@ -556,7 +570,7 @@ void release_aux_stream(ttt_ctx* c) {
     (void)hipStreamDestroy(c->aux);
     c->aux = nullptr;
   }
-  for (hipEvent_t* e : {&c->ev_to_aux, &c->ev_from_aux})
+  for (hipEvent_t* e : {&c->ev_to_aux, &c->ev_from_aux, &c->ev_gin, &c->ev_grad[0], &c->ev_grad[1]})
     if (*e) {
       (void)hipEventDestroy(*e);
       *e = nullptr;
@@ -769,8 +783,13 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     RUN(TTT_K_CE_PROB, run_ce_dlogits(st, prec, c->P, Rr, V, c->ce_w, c->pmax, c->ce_nrec, c->lse, c->tok_tgt,
                                       1.0f / (float)b));
     const int S2 = gemm_split_k(prec, Rr, d, V, 0, SPLIT_MAX);
+    // the backward row buffers of block l (alternating by parity with gradients on the aux
+    // stream): the gradient at its output, and its dU
+    const bool ag = c->agrad && train;
+    auto dHbuf = [&](int l) { return ag && (l & 1) ? c->dHb2 : c->dHb; };
+    auto dUbuf = [&](int l) { return ag && (l & 1) ? c->dU2 : c->dU; };
     RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, V, c->E_outT, V, Rr, d, V, S2, c->part, d, Rd, 0));
-    RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, Rd, Rr, d, c->dH, c->dHb, c->H, c->Yb,
+    RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, Rd, Rr, d, c->dH, dHbuf(L - 1), c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
     // dH^T, read by the W2 gradient
     if (train && !c->km) check(run_transpose(st, prec, c->dHb, d, Rr, d, c->dHT, Rp));
@@ -781,10 +800,21 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       float* cA = foc ? c->cpart + (int64_t)B.cslot * Rr : nullptr;        // tnm slots
       float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * Rr : nullptr;  // one slot
       if (gelu) {
-        RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.w2.Wop, d, b, m, d, B.GP, c->dU, c->km ? nullptr : c->dUT,
+        // dU of block l overwrites that of block l + 2, which its gradients on the aux stream read
+        if (ag && l + 2 < L) check(hipStreamWaitEvent(st, c->ev_grad[l & 1], 0));
+        RUN(TTT_K_DU, gemm_du(st, prec, dHbuf(l), d, B.w2.Wop, d, b, m, d, B.GP, dUbuf(l), c->km ? nullptr : c->dUT,
                               foc ? B.ResA : nullptr, cA, m, Rp, Rr, fw(b, d, n2, false)));
         if (train) {
-          if (c->km) {
+          if (ag) {
+            // G2 = A^T dH, G1 = Hn^T dU on the aux stream, once this block's dU is in
+            check(hipEventRecord(c->ev_gin, st));
+            check(hipStreamWaitEvent(c->aux, c->ev_gin, 0));
+            RUN_ON(TTT_K_DW, c->aux, gemm_grad_km(c->aux, B.A, m, dHbuf(l), d, m, d, b, B.w2.G, d,
+                                                  c->slots + B.w2.slot0, gradkm(m, d, c->nslots)));
+            RUN_ON(TTT_K_DW, c->aux, gemm_grad_km(c->aux, B.Hn, d, dUbuf(l), m, d, m, b, B.w1.G, m,
+                                                  c->slots + B.w1.slot0, gradkm(d, m, c->nslots)));
+            check(hipEventRecord(c->ev_grad[l & 1], c->aux));
+          } else if (c->km) {
             RUN(TTT_K_DW, gemm_grad_km(st, B.A, m, c->dHb, d, m, d, b, B.w2.G, d, c->slots + B.w2.slot0,
                                        gradkm(m, d, c->nslots)));
             RUN(TTT_K_DW, gemm_grad_km(st, B.Hn, d, c->dU, m, d, m, b, B.w1.G, m, c->slots + B.w1.slot0,
@@ -806,9 +836,12 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
         const bool first_f = !has_s && !has_a;
         if (below_f || (foc && (rms || !first_f))) {
           const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
-          RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
+          RUN(TTT_K_DHN, gemm_f32(st, prec, dUbuf(l), m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
                                   fw(b, m, n1, false)));
-          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, c->dHb,
+          // the gradient at block l - 1's output overwrites that at block l + 1's, which its
+          // gradients on the aux stream read
+          if (ag && l + 1 < L) check(hipStreamWaitEvent(st, c->ev_grad[(l + 1) & 1], 0));
+          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, dHbuf(l + 1),
                                            foc ? B.ResN : nullptr, cN, below_f));
         }
         const bool below_s = l > 0 || (foc && has_a);
@@ -878,7 +911,8 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
   // the chunk's keys and values join each attention ring once nothing reads the old slots
   for (int l = 0; l < L && c->window > 0; ++l) check(run_kv_append(st, swa_shape(c, c->blocks[l], chunk_pos)));
 
-  // a8 global grad norm and clip scale, one per stream; a9 update
+  // a8 global grad norm and clip scale, one per stream, once every gradient is in; a9 update
+  if (c->agrad && L > 0) check(hipStreamWaitEvent(st, c->ev_grad[0], 0));
   RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx,
                                    2 * c->max_chunks, nb, c->err));
   // The step runs on the aux stream, in the order the next chunk's forward pass needs the
@@ -1145,6 +1179,7 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   c->km = c->prec == PREC_BF16 && c->b % 64 == 0 && c->b <= 1024;
   c->ms = ext ? ext->static_hidden : 0;
   c->window = ext ? ext->swa_window : 0;
+  c->agrad = c->km && cfg->mlp == TTT_MLP_GELU && c->ms == 0 && c->window == 0;
   // ring positions: the window, plus the b positions a pending decoded chunk writes before
   // its step reads the window in front of it
   c->cr = c->window > 0 ? c->window + c->b : 0;
