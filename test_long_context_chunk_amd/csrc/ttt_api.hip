@@ -168,18 +168,19 @@ struct ttt_ctx {
   int64_t pos = 0;
   ttt_status sticky = TTT_OK;
 
-  // off-critical-path work (the transposed copies the weight-gradient GEMMs read, and the
-  // SGD step) runs on a second stream (default priority): it starts after an event on the
+  // off-critical-path work (the weight gradients of GELU blocks on the token-major path, and
+  // the SGD step) runs on a second stream (default priority): it starts after an event on the
   // main stream, and the main stream waits for its event right before the consumer
   hipStream_t aux = nullptr;
   hipEvent_t ev_to_aux = nullptr, ev_from_aux = nullptr;
-  // GELU blocks without frozen layers, token-major gradients: each block's two weight
-  // gradients run on the aux stream beside the main stream's dHn, norm backward and the next
-  // block's dA. The backward row buffers then alternate by block parity (dHb / dHb2 hold the
-  // gradient at the output of even / odd blocks, dU / dU2 their dU), and ev_grad[l & 1] marks
+  // GELU blocks, token-major gradients: each block's two weight gradients run on the aux
+  // stream beside the main stream's dHn, norm backward, frozen layers and the next block's dA.
+  // The backward row buffers then alternate by block parity (dHb / dHb2 hold the gradient at
+  // the output of even / odd blocks, dU / dU2 their fast dU), the gradients between a
+  // block's sublayers go to dHm and the static MLP's dU to dUs, and ev_grad[l & 1] marks
   // block l's gradients done.
   bool agrad = false;
-  void *dHb2 = nullptr, *dU2 = nullptr;
+  void *dHb2 = nullptr, *dU2 = nullptr, *dHm = nullptr, *dUs = nullptr;
   hipEvent_t ev_gin = nullptr, ev_grad[2] = {nullptr, nullptr};
 
   // tracing: event pairs around launches of the kinds set in prof_mask
@@ -512,6 +513,8 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   if (c->agrad) {
     c->dHb2 = dalloc<char>(c, (int64_t)Rr * d * es);
     c->dU2 = dalloc<char>(c, (int64_t)Rr * mx * es);
+    if (c->ms > 0 || c->window > 0) c->dHm = dalloc<char>(c, (int64_t)Rr * d * es);
+    if (c->ms > 0) c->dUs = dalloc<char>(c, (int64_t)Rr * c->ms * es);
   }
   if (!c->km) {
     c->dUT = dalloc<char>(c, (int64_t)m * Rp * es);
@@ -834,28 +837,34 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
         const bool has_s = ms > 0, has_a = c->window > 0;
         const bool below_f = l > 0 || (foc && (has_s || has_a));
         const bool first_f = !has_s && !has_a;
+        // where the gradients between this block's sublayers go, and the buffer of the one at
+        // its input (block l - 1's output): that buffer holds the gradient block l + 1's
+        // gradients on the aux stream read, so they must be done first
+        void* const mid = ag ? c->dHm : c->dHb;
+        auto to_below = [&]() {
+          if (ag && l + 1 < L) check(hipStreamWaitEvent(st, c->ev_grad[(l + 1) & 1], 0));
+          return dHbuf(l + 1);
+        };
         if (below_f || (foc && (rms || !first_f))) {
           const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
           RUN(TTT_K_DHN, gemm_f32(st, prec, dUbuf(l), m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
                                   fw(b, m, n1, false)));
-          // the gradient at block l - 1's output overwrites that at block l + 1's, which its
-          // gradients on the aux stream read
-          if (ag && l + 1 < L) check(hipStreamWaitEvent(st, c->ev_grad[(l + 1) & 1], 0));
-          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH, dHbuf(l + 1),
-                                           foc ? B.ResN : nullptr, cN, below_f));
+          RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH,
+                                           first_f ? to_below() : mid, foc ? B.ResN : nullptr, cN, below_f));
         }
         const bool below_s = l > 0 || (foc && has_a);
         if (has_s && below_f) {
           // back through the static MLP (frozen: no weight gradient), once over all rows
           float* cAs = foc ? c->cpart + (int64_t)B.scslot * Rr : nullptr;
           float* cNs = foc ? c->cpart + (int64_t)(B.scslot + c->dot_tiles_s) * Rr : nullptr;
-          RUN(TTT_K_DU, gemm_du(st, prec, c->dHb, d, B.SW2, d, Rr, ms, d, B.SGP, c->dU, nullptr,
+          void* const dUs = ag ? c->dUs : c->dU;  // the fast dU may still be read on the aux stream
+          RUN(TTT_K_DU, gemm_du(st, prec, mid, d, B.SW2, d, Rr, ms, d, B.SGP, dUs, nullptr,
                                 foc ? B.SResA : nullptr, cAs, ms, 0, Rr));
           if (below_s || (foc && (rms || has_a))) {
             const int Ss = gemm_split_k(prec, Rr, d, ms, 0, SPLIT_MAX);
-            RUN(TTT_K_DHN, gemm_f32(st, prec, c->dU, ms, B.SW1, ms, Rr, d, ms, Ss, c->part, d, Rd, 0));
-            RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Ss, Rd, B.Sn, B.Sr, Rr, d, rms, c->dH, c->dHb,
-                                             foc ? B.SResN : nullptr, cNs, below_s));
+            RUN(TTT_K_DHN, gemm_f32(st, prec, dUs, ms, B.SW1, ms, Rr, d, ms, Ss, c->part, d, Rd, 0));
+            RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Ss, Rd, B.Sn, B.Sr, Rr, d, rms, c->dH,
+                                             has_a ? mid : to_below(), foc ? B.SResN : nullptr, cNs, below_s));
           }
         }
         if (has_a && (has_s ? below_s : below_f)) {
@@ -864,7 +873,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           float* cO = foc ? c->cpart + (int64_t)B.acslot * Rr : nullptr;
           float* cNa = foc ? c->cpart + (int64_t)(B.acslot + 1) * Rr : nullptr;
           const int So = gemm_split_k(prec, Rr, d, d, 0, SPLIT_MAX);
-          RUN(TTT_K_DHN, gemm_f32(st, prec, c->dHb, d, B.Wo, d, Rr, d, d, So, c->part, d, Rd, 0));
+          RUN(TTT_K_DHN, gemm_f32(st, prec, mid, d, B.Wo, d, Rr, d, d, So, c->part, d, Rd, 0));
           RUN(TTT_K_NORM_BWD, run_dy_finish(st, prec, c->part, So, Rd, Rr, d, c->dOf, c->dOb, foc ? B.Of : nullptr,
                                             foc ? B.Ob : nullptr, cO));
           if (l > 0 || (foc && rms)) {
@@ -872,7 +881,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
                                             c->dQKV, c->swa_part));
             const int Sq = gemm_split_k(prec, Rr, d, 3 * d, 0, SPLIT_MAX);
             RUN(TTT_K_DHN, gemm_f32(st, prec, c->dQKV, 3 * d, B.Wqkv, 3 * d, Rr, d, 3 * d, Sq, c->part, d, Rd, 0));
-            RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Sq, Rd, B.Na, B.ra, Rr, d, rms, c->dH, c->dHb,
+            RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Sq, Rd, B.Na, B.ra, Rr, d, rms, c->dH, to_below(),
                                              foc ? B.ResNa : nullptr, cNa, l > 0));
           }
         }
@@ -1179,7 +1188,7 @@ ttt_status ttt_create_ext(const ttt_config* cfg, const ttt_weights* w, const ttt
   c->km = c->prec == PREC_BF16 && c->b % 64 == 0 && c->b <= 1024;
   c->ms = ext ? ext->static_hidden : 0;
   c->window = ext ? ext->swa_window : 0;
-  c->agrad = c->km && cfg->mlp == TTT_MLP_GELU && c->ms == 0 && c->window == 0;
+  c->agrad = c->km && cfg->mlp == TTT_MLP_GELU;
   // ring positions: the window, plus the b positions a pending decoded chunk writes before
   // its step reads the window in front of it
   c->cr = c->window > 0 ? c->window + c->b : 0;
