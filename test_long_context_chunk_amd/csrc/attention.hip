@@ -957,20 +957,34 @@ hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, v
   return hipGetLastError();
 }
 
-hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
-                       const float* lse2, float* Dq, void* dQKV, float* part) {
+hipError_t run_swa_dsum(hipStream_t st, const SwaShape& s, const float* dOf, const float* Of, float* Dq) {
+  if (!shape_ok(s)) return hipErrorInvalidValue;
+  const unsigned R = (unsigned)((int64_t)s.streams * s.b);
+  hipLaunchKernelGGL(k_swa_dsum, dim3(R, s.d / DH), dim3(64), 0, st, dOf, Of, s.d, s.b, Dq);
+  return hipGetLastError();
+}
+
+hipError_t run_swa_bwd_dq(hipStream_t st, const SwaShape& s, const void* dOb, const float* lse2, const float* Dq,
+                          void* dQKV, float* part) {
   if (!shape_ok(s)) return hipErrorInvalidValue;
   const int H = s.d / DH;
   const int ns = swa_dq_splits(s);
   if (ns > 1 && !part) return hipErrorInvalidValue;
   const unsigned R = (unsigned)((int64_t)s.streams * s.b);
-  hipLaunchKernelGGL(k_swa_dsum, dim3(R, H), dim3(64), 0, st, dOf, Of, s.d, s.b, Dq);
   dim3 gq((s.b + BLK - 1) / BLK * ns, H, s.streams);
   hipLaunchKernelGGL(k_swa_bwd_dq, gq, dim3(NT_A), 0, st, geo(s), ns, part, (const bf16_t*)dOb, lse2, Dq,
                      (bf16_t*)dQKV);
   if (ns > 1) hipLaunchKernelGGL(k_swa_dq_sum, dim3(R), dim3(NT_A), 0, st, part, ns, s.d, (bf16_t*)dQKV);
+  return hipGetLastError();
+}
+
+hipError_t run_swa_bwd_dkdv(hipStream_t st, const SwaShape& s, const void* dOb, const float* lse2, const float* Dq,
+                            void* dQKV, float* part) {
+  if (!shape_ok(s)) return hipErrorInvalidValue;
+  const int H = s.d / DH;
   const int nk = swa_dkdv_splits(s);
   if (nk > 1 && !part) return hipErrorInvalidValue;
+  const unsigned R = (unsigned)((int64_t)s.streams * s.b);
   dim3 grid((s.b + BLK - 1) / BLK * nk, H, s.streams);
   hipLaunchKernelGGL(k_swa_bwd_dkdv, grid, dim3(NT_A), 0, st, geo(s), nk, part, (const bf16_t*)dOb, lse2, Dq,
                      (bf16_t*)dQKV);

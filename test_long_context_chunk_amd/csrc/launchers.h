@@ -116,10 +116,16 @@ int swa_dkdv_splits(const SwaShape& s);
 hipError_t run_swa_fwd(hipStream_t st, const SwaShape& s, float* Of, void* Ob, void* Ol, float* lse2, float* part,
                        float* pm, float* pl);
 // From dO (fp32 dOf for the row term D, bf16 dOb for the products): dQ, dK, dV of the
-// chunk's rows (bf16) into dQKV [streams b x 3d]; Dq [streams][d / 128][b] is scratch.
-// part: scratch for the split dQ partials, [swa_dq_splits(s)][streams b x d] fp32.
-hipError_t run_swa_bwd(hipStream_t st, const SwaShape& s, const float* dOf, const void* dOb, const float* Of,
-                       const float* lse2, float* Dq, void* dQKV, float* part);
+// chunk's rows (bf16) into dQKV [streams b x 3d], in three parts: the row term Dq
+// [streams][d / 128][b] from dOf and Of; then dQ (part: its split partials,
+// [swa_dq_splits(s)][streams b x d] fp32) and dK, dV (part: theirs, [2 swa_dkdv_splits(s)]
+// [streams b x d]). The last two read only dOb, lse2, Dq and the forward's q, k, v, write
+// disjoint columns of dQKV, and may run at once (two streams) when their part buffers differ.
+hipError_t run_swa_dsum(hipStream_t st, const SwaShape& s, const float* dOf, const float* Of, float* Dq);
+hipError_t run_swa_bwd_dq(hipStream_t st, const SwaShape& s, const void* dOb, const float* lse2, const float* Dq,
+                          void* dQKV, float* part);
+hipError_t run_swa_bwd_dkdv(hipStream_t st, const SwaShape& s, const void* dOb, const float* lse2, const float* Dq,
+                            void* dQKV, float* part);
 // Decode of one row at position s.pos (single stream): its key and value (fp32 qkv [3d]) join
 // the ring, and o [d] (fp32) = its attention over the window; part is scratch of
 // d / 128 * swa_dec_splits(window) * 130 floats.

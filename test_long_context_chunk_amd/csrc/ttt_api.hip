@@ -109,6 +109,7 @@ struct ttt_ctx {
   bool eval_ring = false;  // the attention reads and fills the passage rings (evaluation)
   float *dOf = nullptr, *Dq = nullptr;  // attention backward scratch: dO fp32, row terms
   float *swa_part = nullptr, *swa_m = nullptr, *swa_l = nullptr;  // forward split partials
+  float* swa_part2 = nullptr;  // the dK, dV pass's split partials (it runs beside the dQ pass)
   void *dOb = nullptr, *dQKV = nullptr;
   int dot_tiles_s = 0;  // column tiles of the static dA GEMM
   std::vector<void*> allocs;
@@ -182,6 +183,8 @@ struct ttt_ctx {
   bool agrad = false;
   void *dHb2 = nullptr, *dU2 = nullptr, *dHm = nullptr, *dUs = nullptr;
   hipEvent_t ev_gin = nullptr, ev_grad[2] = {nullptr, nullptr};
+  // attention backward: the dK, dV pass on the aux stream beside the dQ pass
+  hipEvent_t ev_ain = nullptr, ev_aout = nullptr;
 
   // tracing: event pairs around launches of the kinds set in prof_mask
   uint32_t prof_mask = 0;
@@ -536,6 +539,7 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
       c->swa_m = dalloc<float>(c, (int64_t)ns * Rr * (d / 128) * 4);
       c->swa_l = dalloc<float>(c, (int64_t)ns * Rr * (d / 128) * 4);
     }
+    if (swa_dkdv_splits(sh) > 1) c->swa_part2 = dalloc<float>(c, (int64_t)2 * swa_dkdv_splits(sh) * Rr * d * 4);
   }
   if (c->foc && c->cfg.mlp == TTT_MLP_SWIGLU_W2) {
     c->DG = dalloc<char>(c, (int64_t)Rr * m * es);
@@ -564,6 +568,8 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   check(hipEventCreateWithFlags(&c->ev_from_aux, kSyncEvent));
   if (c->agrad)
     for (hipEvent_t* e : {&c->ev_gin, &c->ev_grad[0], &c->ev_grad[1]}) check(hipEventCreateWithFlags(e, kSyncEvent));
+  if (c->window > 0)
+    for (hipEvent_t* e : {&c->ev_ain, &c->ev_aout}) check(hipEventCreateWithFlags(e, kSyncEvent));
 }
 
 // Wait for the aux stream, then release it (before any buffer it may read is freed).
@@ -573,7 +579,8 @@ void release_aux_stream(ttt_ctx* c) {
     (void)hipStreamDestroy(c->aux);
     c->aux = nullptr;
   }
-  for (hipEvent_t* e : {&c->ev_to_aux, &c->ev_from_aux, &c->ev_gin, &c->ev_grad[0], &c->ev_grad[1]})
+  for (hipEvent_t* e : {&c->ev_to_aux, &c->ev_from_aux, &c->ev_gin, &c->ev_grad[0], &c->ev_grad[1], &c->ev_ain,
+                        &c->ev_aout})
     if (*e) {
       (void)hipEventDestroy(*e);
       *e = nullptr;
@@ -877,8 +884,15 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           RUN(TTT_K_NORM_BWD, run_dy_finish(st, prec, c->part, So, Rd, Rr, d, c->dOf, c->dOb, foc ? B.Of : nullptr,
                                             foc ? B.Ob : nullptr, cO));
           if (l > 0 || (foc && rms)) {
-            RUN(TTT_K_ATTN_BWD, run_swa_bwd(st, swa_shape(c, B, chunk_pos), c->dOf, c->dOb, B.Of, B.lse2, c->Dq,
-                                            c->dQKV, c->swa_part));
+            // dK, dV on the aux stream beside dQ: both read only dO, D and the chunk's q, k, v
+            const SwaShape sh = swa_shape(c, B, chunk_pos);
+            RUN(TTT_K_ATTN_BWD, run_swa_dsum(st, sh, c->dOf, B.Of, c->Dq));
+            check(hipEventRecord(c->ev_ain, st));
+            check(hipStreamWaitEvent(c->aux, c->ev_ain, 0));
+            RUN_ON(TTT_K_ATTN_BWD, c->aux, run_swa_bwd_dkdv(c->aux, sh, c->dOb, B.lse2, c->Dq, c->dQKV, c->swa_part2));
+            check(hipEventRecord(c->ev_aout, c->aux));
+            RUN(TTT_K_ATTN_BWD, run_swa_bwd_dq(st, sh, c->dOb, B.lse2, c->Dq, c->dQKV, c->swa_part));
+            check(hipStreamWaitEvent(st, c->ev_aout, 0));
             const int Sq = gemm_split_k(prec, Rr, d, 3 * d, 0, SPLIT_MAX);
             RUN(TTT_K_DHN, gemm_f32(st, prec, c->dQKV, 3 * d, B.Wqkv, 3 * d, Rr, d, 3 * d, Sq, c->part, d, Rd, 0));
             RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, Sq, Rd, B.Na, B.ra, Rr, d, rms, c->dH, to_below(),
