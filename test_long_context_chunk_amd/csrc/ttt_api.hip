@@ -812,15 +812,20 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       if (gelu) {
         // dU of block l overwrites that of block l + 2, which its gradients on the aux stream read
         if (ag && l + 2 < L) check(hipStreamWaitEvent(st, c->ev_grad[l & 1], 0));
+        if (ag) {
+          // G2 = A^T dH on the aux stream as soon as the gradient at the block's output is in
+          check(hipEventRecord(c->ev_gin, st));
+          check(hipStreamWaitEvent(c->aux, c->ev_gin, 0));
+          RUN_ON(TTT_K_DW, c->aux, gemm_grad_km(c->aux, B.A, m, dHbuf(l), d, m, d, b, B.w2.G, d,
+                                                c->slots + B.w2.slot0, gradkm(m, d, c->nslots)));
+        }
         RUN(TTT_K_DU, gemm_du(st, prec, dHbuf(l), d, B.w2.Wop, d, b, m, d, B.GP, dUbuf(l), c->km ? nullptr : c->dUT,
                               foc ? B.ResA : nullptr, cA, m, Rp, Rr, fw(b, d, n2, false)));
         if (train) {
           if (ag) {
-            // G2 = A^T dH, G1 = Hn^T dU on the aux stream, once this block's dU is in
+            // G1 = Hn^T dU on the aux stream once this block's dU is in
             check(hipEventRecord(c->ev_gin, st));
             check(hipStreamWaitEvent(c->aux, c->ev_gin, 0));
-            RUN_ON(TTT_K_DW, c->aux, gemm_grad_km(c->aux, B.A, m, dHbuf(l), d, m, d, b, B.w2.G, d,
-                                                  c->slots + B.w2.slot0, gradkm(m, d, c->nslots)));
             RUN_ON(TTT_K_DW, c->aux, gemm_grad_km(c->aux, B.Hn, d, dUbuf(l), m, d, m, b, B.w1.G, m,
                                                   c->slots + B.w1.slot0, gradkm(d, m, c->nslots)));
             check(hipEventRecord(c->ev_grad[l & 1], c->aux));
