@@ -939,15 +939,25 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
   // the chunk's keys and values join each attention ring once nothing reads the old slots
   for (int l = 0; l < L && c->window > 0; ++l) check(run_kv_append(st, swa_shape(c, c->blocks[l], chunk_pos)));
 
-  // a8 global grad norm and clip scale, one per stream, once every gradient is in; a9 update
-  if (c->agrad && L > 0) check(hipStreamWaitEvent(st, c->ev_grad[0], 0));
-  RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx,
-                                   2 * c->max_chunks, nb, c->err));
+  // a8 global grad norm and clip scale, one per stream, once every gradient is in; a9 update.
   // The step runs on the aux stream, in the order the next chunk's forward pass needs the
   // tensors; each GEMM that reads a fast tensor waits for that tensor's event. (A context
-  // with no blocks has no fast tensors.)
-  if (!c->fast.empty()) {
+  // with no blocks has no fast tensors.) With the gradients on the aux stream the norm runs
+  // there too, right behind them, so no stream hop separates it from the step; the fork
+  // keeps the step behind this backward's products that read rn(W0 + D) on the main stream.
+  if (c->agrad && !c->fast.empty()) {
     aux_fork(c);
+    RUN_ON(TTT_K_GRADNORM, c->aux, run_gradnorm(c->aux, c->slots, c->nslots, c->cfg.clip, c->sc,
+                                                c->stats + 2 * chunk_idx, 2 * c->max_chunks, nb, c->err));
+    // the next chunk's first rows overwrite the lowest block's normed input, which its W1
+    // gradient reads: the main stream goes on once every gradient is in
+    check(hipStreamWaitEvent(st, c->ev_grad[0], 0));
+  } else {
+    RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx,
+                                     2 * c->max_chunks, nb, c->err));
+    if (!c->fast.empty()) aux_fork(c);
+  }
+  if (!c->fast.empty()) {
     for (FastTensor* f : c->fast) {
       RUN_ON(TTT_K_UPDATE, c->aux, run_update(c->aux, prec, f->G, f->D, f->W0, f->Wop, f->WtT, f->rows, f->cols,
                                               c->cfg.lr, c->sc, bf ? 1 : 0, nb));
@@ -1160,6 +1170,7 @@ int64_t static_settle_bytes(const ttt_ctx* c) {
 
 ttt_status read_sticky(ttt_ctx* c) {
   int e = 0;
+  aux_join(c);  // the grad norm, which may raise the non-finite bit, can run on the aux stream
   check(hipMemcpyAsync(&e, c->err, 4, hipMemcpyDeviceToHost, c->st));
   check(hipStreamSynchronize(c->st));
   if (c->sticky == TTT_OK) {
@@ -1426,6 +1437,7 @@ ttt_status ttt_stream_chunk_stats(ttt_ctx* c, int32_t s, float* dst, int64_t off
   if (offset < 0 || n < 0 || offset + n > c->pos / c->b) return TTT_EINVAL;
   try {
     const float* src = c->stats + (int64_t)s * 2 * c->max_chunks + 2 * offset;
+    aux_join(c);  // the grad norm that writes them can run on the aux stream
     if (n > 0) check(hipMemcpyAsync(dst, src, n * 8, hipMemcpyDeviceToDevice, c->st));
     return read_sticky(c);
   } catch (const HipFail& f) {
