@@ -185,6 +185,9 @@ struct ttt_ctx {
   hipEvent_t ev_gin = nullptr, ev_grad[2] = {nullptr, nullptr};
   // attention backward: the dK, dV pass on the aux stream beside the dQ pass
   hipEvent_t ev_ain = nullptr, ev_aout = nullptr;
+  // recorded on the main stream after the backward's last product that reads rn(W0 + D) (the
+  // lowest block's dHn, else its dA): the SGD steps on the aux stream wait for it
+  hipEvent_t ev_wread = nullptr;
 
   // tracing: event pairs around launches of the kinds set in prof_mask
   uint32_t prof_mask = 0;
@@ -567,7 +570,8 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   check(hipEventCreateWithFlags(&c->ev_to_aux, kSyncEvent));
   check(hipEventCreateWithFlags(&c->ev_from_aux, kSyncEvent));
   if (c->agrad)
-    for (hipEvent_t* e : {&c->ev_gin, &c->ev_grad[0], &c->ev_grad[1]}) check(hipEventCreateWithFlags(e, kSyncEvent));
+    for (hipEvent_t* e : {&c->ev_gin, &c->ev_grad[0], &c->ev_grad[1], &c->ev_wread})
+      check(hipEventCreateWithFlags(e, kSyncEvent));
   if (c->window > 0)
     for (hipEvent_t* e : {&c->ev_ain, &c->ev_aout}) check(hipEventCreateWithFlags(e, kSyncEvent));
 }
@@ -580,7 +584,7 @@ void release_aux_stream(ttt_ctx* c) {
     c->aux = nullptr;
   }
   for (hipEvent_t* e : {&c->ev_to_aux, &c->ev_from_aux, &c->ev_gin, &c->ev_grad[0], &c->ev_grad[1], &c->ev_ain,
-                        &c->ev_aout})
+                        &c->ev_aout, &c->ev_wread})
     if (*e) {
       (void)hipEventDestroy(*e);
       *e = nullptr;
@@ -861,9 +865,11 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
           const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
           RUN(TTT_K_DHN, gemm_f32(st, prec, dUbuf(l), m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
                                   fw(b, m, n1, false)));
+          if (ag && l == 0) check(hipEventRecord(c->ev_wread, st));
           RUN(TTT_K_NORM_BWD, run_norm_bwd(st, prec, c->part, S, Rd, B.Hn, B.r, Rr, d, rms, c->dH,
                                            first_f ? to_below() : mid, foc ? B.ResN : nullptr, cN, below_f));
         }
+        if (ag && l == 0 && !(below_f || (foc && (rms || !first_f)))) check(hipEventRecord(c->ev_wread, st));
         const bool below_s = l > 0 || (foc && has_a);
         if (has_s && below_f) {
           // back through the static MLP (frozen: no weight gradient), once over all rows
@@ -943,12 +949,12 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
   // The step runs on the aux stream, in the order the next chunk's forward pass needs the
   // tensors; each GEMM that reads a fast tensor waits for that tensor's event. (A context
   // with no blocks has no fast tensors.) With the gradients on the aux stream the norm runs
-  // there too, right behind them, so no stream hop separates it from the step; the fork
-  // keeps the step behind this backward's products that read rn(W0 + D) on the main stream.
+  // there too, right behind them, so no stream hop separates it from the step; the step
+  // waits only for the backward's last product on the main stream that reads rn(W0 + D).
   if (c->agrad && !c->fast.empty()) {
-    aux_fork(c);
     RUN_ON(TTT_K_GRADNORM, c->aux, run_gradnorm(c->aux, c->slots, c->nslots, c->cfg.clip, c->sc,
                                                 c->stats + 2 * chunk_idx, 2 * c->max_chunks, nb, c->err));
+    check(hipStreamWaitEvent(c->aux, c->ev_wread, 0));
     // the next chunk's first rows overwrite the lowest block's normed input, which its W1
     // gradient reads: the main stream goes on once every gradient is in
     check(hipStreamWaitEvent(st, c->ev_grad[0], 0));
