@@ -746,7 +746,11 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     if (gelu) {
       // Hn^T is read only by the W1 gradient of the backward pass
       if (train && !c->km) check(run_transpose(st, prec, B.Hn, d, Rr, d, B.HnT, Rp));
-      check(hipStreamWaitEvent(st, B.w1.ev_upd, 0));  // the previous chunk's step of W1
+      // the previous chunk's steps: the lowest block waits for W1's here and for W2's before its
+      // down-projection; a higher block's steps finish long before its forward pass, so one
+      // wait for W2's (queued after W1's on the aux stream) covers both (each wait costs
+      // queue time on the main stream even when it is satisfied)
+      check(hipStreamWaitEvent(st, (l > 0 ? B.w2 : B.w1).ev_upd, 0));
       GemmSeg2 s2;
       if (bf) s2 = GemmSeg2{B.Hn, d, B.w1.WtT, d, d};
       // split: the input's residual term against W0 as its own product, added before the GELU
@@ -761,7 +765,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
                                 foc ? B.ResA : nullptr, m, Rp));
     }
     const int S = gemm_split_k(prec, Rr, d, m, bf ? m : 0, SPLIT_MAX);
-    check(hipStreamWaitEvent(st, B.w2.ev_upd, 0));  // the previous chunk's step of W2
+    if (!gelu || l == 0) check(hipStreamWaitEvent(st, B.w2.ev_upd, 0));  // the previous chunk's step of W2
     GemmSeg2 s2;
     void* const Ablk = c->km ? B.A : c->A;  // this block's activation
     if (bf) s2 = GemmSeg2{Ablk, m, B.w2.WtT, m, m};
