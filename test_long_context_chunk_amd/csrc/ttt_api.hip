@@ -181,6 +181,7 @@ struct ttt_ctx {
   // block's sublayers go to dHm and the static MLP's dU to dUs, and ev_grad[l & 1] marks
   // block l's gradients done.
   bool agrad = false;
+  bool grads_inflight = false;  // the last step's gradients may still read the lowest block's Hn
   void *dHb2 = nullptr, *dU2 = nullptr, *dHm = nullptr, *dUs = nullptr;
   hipEvent_t ev_gin = nullptr, ev_grad[2] = {nullptr, nullptr};
   // attention backward: the dK, dV pass on the aux stream beside the dQ pass
@@ -705,9 +706,19 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     return mlp_norm(B);
   };
 
+  // The previous step's gradients on the aux stream read the lowest block's normed input
+  // Hn: the row kernel that rewrites it waits for them first.
+  auto guard_hn0 = [&](const void* n) {
+    if (c->grads_inflight && L > 0 && n == c->blocks[0].Hn) {
+      check(hipStreamWaitEvent(st, c->ev_grad[0], 0));
+      c->grads_inflight = false;
+    }
+  };
+
   // a1 gather, and a2 the lowest block's pre-norm
   {
     const NormOut o = first_norm(0);
+    guard_hn0(o.n);
     RUN(TTT_K_GATHER, run_row_in(st, prec, tok, srt, V, c->E_in, c->tok_prev, c->tok_tgt, c->err, nullptr, 0, 0, c->H,
                                  Rr, d, L == 0 ? c->Yb : nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res,
                                  L == 0 && split ? c->Yl : nullptr));
@@ -727,6 +738,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       RUN(TTT_K_DOWN, gemm_f32(st, prec, B.Ob, d, B.WoT, d, Rr, d, d, So, c->part, d, Rd, 0,
                                split ? GemmSeg2{B.Obl, d, B.WoT, d, d} : GemmSeg2()));
       const NormOut o = mlp_norm(B);
+      guard_hn0(o.n);
       RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, So, Rd,
                                      c->H, Rr, d, nullptr, c->cfg.rms_eps, rms, o.n, o.r, o.res));
     }
@@ -739,6 +751,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       const int Ss = gemm_split_k(prec, Rr, d, ms, split ? ms : 0, SPLIT_MAX);
       RUN(TTT_K_DOWN, gemm_f32(st, prec, c->A, ms, B.SW2T, ms, Rr, d, ms, Ss, c->part, d, Rd, 0,
                                split ? GemmSeg2{B.SResA, ms, B.SW2T, ms, ms} : GemmSeg2()));
+      guard_hn0(B.Hn);
       RUN(TTT_K_RESIDUAL, run_row_in(st, prec, nullptr, srt, V, nullptr, nullptr, nullptr, nullptr, c->part, Ss, Rd,
                                      c->H, Rr, d, nullptr, c->cfg.rms_eps, rms, B.Hn, B.r,
                                      keep_res ? B.ResN : nullptr));
@@ -959,9 +972,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     RUN_ON(TTT_K_GRADNORM, c->aux, run_gradnorm(c->aux, c->slots, c->nslots, c->cfg.clip, c->sc,
                                                 c->stats + 2 * chunk_idx, 2 * c->max_chunks, nb, c->err));
     check(hipStreamWaitEvent(c->aux, c->ev_wread, 0));
-    // the next chunk's first rows overwrite the lowest block's normed input, which its W1
-    // gradient reads: the main stream goes on once every gradient is in
-    check(hipStreamWaitEvent(st, c->ev_grad[0], 0));
+    // the lowest block's W1 gradient reads its normed input, which the next forward pass
+    // rewrites: that pass waits for the gradients right before (guard_hn0)
+    c->grads_inflight = true;
   } else {
     RUN(TTT_K_GRADNORM, run_gradnorm(st, c->slots, c->nslots, c->cfg.clip, c->sc, c->stats + 2 * chunk_idx,
                                      2 * c->max_chunks, nb, c->err));
