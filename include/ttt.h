@@ -369,6 +369,22 @@ const char* ttt_status_string(ttt_status s);
 ttt_status ttt_test_gemm(int32_t precision, const void* X, int64_t ldx, const void* Y, int64_t ldy,
                          float* C, int64_t ldc, int32_t M, int32_t N, int32_t K, void* stream);
 
+/* Test hook: the forward product of a fast weight in bf16 mode, C = X (Y + Y2)^T in fp32, with
+ * X [M x K], Y and Y2 [N x K] bf16 (row strides ldx, ldy, ldy2 elements): the bf16 path
+ * multiplies the block input by the frozen W0 and by the rounded accumulated update as two
+ * K-segments over the same rows of X ([E2E] section 3, eq. (5): the weights a chunk is scored
+ * with are W0 plus the sum of the earlier steps). The K range is cut into `splits` slabs
+ * (1 .. 8), each written to its own M x ldc fp32 block of C (C holds splits * M * ldc
+ * floats; the caller sums the slabs). `form` picks how the tile engine walks the two
+ * segments: 0 as the inner loop does (its tile plan decides), 1 one segment after the other,
+ * 2 both weights' slices against one staged slice of X wherever the tile plan allows it, so
+ * that tests can hold both forms to the product. K a multiple of 8; 16-byte aligned rows;
+ * enqueued on `stream`. It exposes the kernels the inner loop uses on ragged shapes; it is
+ * not a second code path. Errors: TTT_EINVAL. */
+ttt_status ttt_test_gemm_pair(const void* X, int64_t ldx, const void* Y, int64_t ldy, const void* Y2,
+                              int64_t ldy2, float* C, int64_t ldc, int32_t M, int32_t N, int32_t K,
+                              int32_t splits, int32_t form, void* stream);
+
 /* Test hook: the library's weight-gradient GEMM (bf16), G = sum over k < K of X_k^T Y_k
  * ([E2E] eq. 5: a fast tensor's chunk gradient, summed over the chunk's tokens), stored in
  * bf16 into G [M x N] (row stride ldg), and each output tile's sum of squared fp32 values

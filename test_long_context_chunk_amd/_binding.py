@@ -58,6 +58,8 @@ SIGNATURES = {
     "ttt_profile_read": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "ttt_test_gemm": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                 c_int32, c_int32, c_int32, c_void_p]),
+    "ttt_test_gemm_pair": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                     c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "ttt_test_grad": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int32,
                                 c_int32, c_int32, c_int32, c_void_p]),
 }
@@ -385,6 +387,21 @@ def grad_test_hook(X, Y, token_major: bool, stream=None):
                              c_void_p(_ptr(slots)), M, N, K, 1 if token_major else 0,
                              c_void_p(_stream_handle(stream))), "ttt_test_grad")
     return G, slots
+
+
+def gemm_pair_test_hook(X, Y, Y2, splits: int = 1, form: int = 0, stream=None):
+    """C = X (Y + Y2)^T (bf16 operands, two K-segments over the same X rows) through the
+    library's GEMM tile engine (test hook); returns the fp32 slabs [splits x M x N]. form: 0 the
+    inner loop's choice, 1 the segments one after the other, 2 shared X slices."""
+    import torch
+    lib = load_library()
+    M, K = X.shape
+    N = Y.shape[0]
+    C = torch.empty((splits, M, N), dtype=torch.float32, device="cuda")
+    _check(lib.ttt_test_gemm_pair(c_void_p(_ptr(X)), X.stride(0), c_void_p(_ptr(Y)), Y.stride(0), c_void_p(_ptr(Y2)),
+                                  Y2.stride(0), c_void_p(_ptr(C)), N, M, N, K, splits, form,
+                                  c_void_p(_stream_handle(stream))), "ttt_test_gemm_pair")
+    return C
 
 
 def gemm_test_hook(X, Y, precision: str, stream=None):

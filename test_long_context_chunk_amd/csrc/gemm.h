@@ -229,6 +229,17 @@ __global__ void __launch_bounds__(256) gemm_reg_kernel(GemmArgs g, Epi epi) {
 constexpr int gemm_stages(int BM, int BN) {
   return ((BM + BN) * 128 * 3 <= 160 * 1024 && !(BM == 128 && BN == 128)) ? 3 : 2;
 }
+// Stages of the shared-X form (NB = 2 B regions per stage): two at 256 x 128, three at 256 x 64.
+constexpr int gemm_stages_nb(int BM, int BN, int NB) {
+  return NB == 1 ? gemm_stages(BM, BN) : (((BM + NB * BN) * 128 * 3 <= 160 * 1024) ? 3 : 2);
+}
+// LDS of a launch: its stages, and never less than the one-segment form's, whose size the
+// epilogues' staging areas are planned for (TileGeo).
+constexpr int gemm_lds_bytes(int BM, int BN, int NB) {
+  const int a = gemm_stages_nb(BM, BN, NB) * (BM + NB * BN) * 128;
+  const int b = gemm_stages(BM, BN) * (BM + BN) * 128;
+  return a > b ? a : b;
+}
 
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS tile row (tile-local row index t;
 // the A rows come first, then the B rows, both regions a multiple of 16 rows). 16 x 16
@@ -377,7 +388,11 @@ __device__ __forceinline__ void dma_slice(const char* const (&p1)[PW], const cha
 }
 
 // The four 16-k steps of one 128-byte slice held in `cur`, on 32 x 32 output blocks.
-template <int BM, int BN, int WGM, int WGN>
+// With NB = 2 the stage holds two B regions of BN rows each (the same output columns of two
+// weight operands, Y then Y2): each A fragment read from LDS feeds both, and both products
+// accumulate into the same blocks (independent blocks first, so no MFMA waits on the one
+// just issued).
+template <int BM, int BN, int WGM, int WGN, int NB = 1>
 __device__ __forceinline__ void mma_slice32(const char* cur, int wm, int wn, int lane,
                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
   __builtin_amdgcn_iglp_opt(0);  // let the scheduler interleave the LDS reads with the MFMAs
@@ -388,21 +403,25 @@ __device__ __forceinline__ void mma_slice32(const char* cur, int wm, int wn, int
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int ch = 2 * ks + (lane >> 5);
-    uint4 af[FM], bfr[FN];
+    uint4 af[FM], bfr[NB][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 32 + (lane & 31);
       af[i] = *(const uint4*)(cur + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
     }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = wn * WTN + j * 32 + (lane & 31);
-      bfr[j] = *(const uint4*)(sb + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
-    }
+    for (int s = 0; s < NB; ++s)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 32 + (lane & 31);
+        bfr[s][j] = *(const uint4*)(sb + s * BN * ROWB + r * ROWB + ((ch ^ lds_swz<true>(r)) << 4));
+      }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+    for (int s = 0; s < NB; ++s)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma32(acc[i][j], af[i], bfr[s][j]);
   }
 }
 
@@ -419,7 +438,7 @@ __device__ __forceinline__ char* stage_ptr(char* s0, char* s1, char* s2) {
 // everyone finished reading the stage refilled next), request slice it + S - 1 into the
 // stage read last iteration, multiply stage J. The barrier is written out because a
 // fence-based barrier would also wait for the newer loads.
-template <int BM, int BN, int WGM, int WGN, int PW, int S, int J>
+template <int BM, int BN, int WGM, int WGN, int PW, int S, int J, int NB>
 __device__ __forceinline__ void step_slice32(char* s0, char* s1, char* s2, const char* const (&p1)[PW],
                                              const char* const (&p2)[PW], int kit_a, int kit0, int it, int n, int dmaoff,
                                              int wm, int wn, int lane,
@@ -428,13 +447,13 @@ __device__ __forceinline__ void step_slice32(char* s0, char* s1, char* s2, const
   static_assert(NOUT < 64, "vmcnt holds at most 63");
   __asm__ __volatile__("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NOUT) : "memory");
   dma_slice<PW>(p1, p2, kit_a, kit0 + min(it + S - 1, n - 1), stage_ptr<J + S - 1, S>(s0, s1, s2) + dmaoff);
-  mma_slice32<BM, BN, WGM, WGN>(stage_ptr<J, S>(s0, s1, s2), wm, wn, lane, acc);
+  mma_slice32<BM, BN, WGM, WGN, NB>(stage_ptr<J, S>(s0, s1, s2), wm, wn, lane, acc);
 }
 
 // The K loop. The stage pointers are restrict-qualified (they never overlap) and reach here
 // through an opaque offset, so every LDS read and direct load carries an alias scope: the
 // compiler then never waits for loads into one stage before reading another.
-template <int BM, int BN, int WGM, int WGN, int PW, int S>
+template <int BM, int BN, int WGM, int WGN, int PW, int S, int NB>
 __device__ __forceinline__ void kloop32(char* __restrict__ s0, char* __restrict__ s1, char* __restrict__ s2,
                                         const char* const (&p1)[PW], const char* const (&p2)[PW], int kit_a, int kit0,
                                         int n, int dmaoff, int wm, int wn, int lane,
@@ -443,26 +462,31 @@ __device__ __forceinline__ void kloop32(char* __restrict__ s0, char* __restrict_
   dma_slice<PW>(p1, p2, kit_a, kit0, s0 + dmaoff);
   if constexpr (S > 2) dma_slice<PW>(p1, p2, kit_a, kit0 + min(1, n - 1), s1 + dmaoff);
   for (int it = 0; it < n; it += S) {
-    step_slice32<BM, BN, WGM, WGN, PW, S, 0>(s0, s1, s2, p1, p2, kit_a, kit0, it, n, dmaoff, wm, wn, lane, acc);
+    step_slice32<BM, BN, WGM, WGN, PW, S, 0, NB>(s0, s1, s2, p1, p2, kit_a, kit0, it, n, dmaoff, wm, wn, lane, acc);
     if (it + 1 < n)
-      step_slice32<BM, BN, WGM, WGN, PW, S, 1>(s0, s1, s2, p1, p2, kit_a, kit0, it + 1, n, dmaoff, wm, wn, lane, acc);
+      step_slice32<BM, BN, WGM, WGN, PW, S, 1, NB>(s0, s1, s2, p1, p2, kit_a, kit0, it + 1, n, dmaoff, wm, wn, lane, acc);
     if constexpr (S > 2)
       if (it + 2 < n)
-        step_slice32<BM, BN, WGM, WGN, PW, S, 2>(s0, s1, s2, p1, p2, kit_a, kit0, it + 2, n, dmaoff, wm, wn, lane, acc);
+        step_slice32<BM, BN, WGM, WGN, PW, S, 2, NB>(s0, s1, s2, p1, p2, kit_a, kit0, it + 2, n, dmaoff, wm, wn, lane, acc);
   }
   __syncthreads();  // every request has landed and every read is done: the LDS is free
 }
 
-template <class T, int BM, int BN, int WGM, int WGN, class Epi>
+// NB = 2 (bf16, 32 x 32 blocks only): C = X (Y + Y2)^T for a second K-segment that reads the
+// same X rows (X2 = X): each stage holds the A rows once and the B rows of both weights, so a
+// K-slice moves (BM + 2 BN) rows for the work of two slices of the concatenated walk, which
+// would move 2 (BM + BN). kiters then counts one segment's slices.
+template <class T, int BM, int BN, int WGM, int WGN, class Epi, int NB = 1>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Epi epi) {
   constexpr int WGM_ = WGM, WGN_ = WGN;
   constexpr int NW = WGM * WGN;
   constexpr int ROWB = 128;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int PW = (BM + BN) / 8 / NW;  // 8-row blocks per wave
-  static_assert(((BM + BN) / 8) % NW == 0, "whole 8-row blocks per wave");
+  constexpr int STAGE = (BM + NB * BN) * ROWB;
+  constexpr int PW = (BM + NB * BN) / 8 / NW;  // 8-row blocks per wave
+  static_assert(((BM + NB * BN) / 8) % NW == 0, "whole 8-row blocks per wave");
+  static_assert(NB == 1 || (sizeof(T) == 2 && use_mfma32<T, BM, BN, WGM, WGN>()), "shared-X form: bf16, 32 x 32 blocks");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -489,15 +513,26 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
     const int blk = wave_s * PW + q;
     const bool xs = blk * 8 < BM;  // whole 8-row blocks: BM % 8 == 0
     const int t = blk * 8 + rsub;  // tile-local row
-    const int r = xs ? min(m0 + t, g.M - 1) : min(n0 + t - BM, g.N - 1);
     // lane L writes physical chunk L & 7 of row t; it loads logical chunk (L & 7) ^ swz(t)
     const int cbyte = ((lane & 7) ^ lds_swz<use_mfma32<T, BM, BN, WGM, WGN>()>(t)) << 4;
-    const char* const b1 = xs ? gX : gY;
-    const char* const b2 = xs ? gX2 : gY2;
-    const int64_t l1 = (xs ? g.ldx : g.ldy) * (int64_t)sizeof(T);
-    const int64_t l2 = (xs ? g.ldx2 : g.ldy2) * (int64_t)sizeof(T);
-    p1[q] = b1 + (int64_t)r * l1 + cbyte;
-    p2[q] = has2 ? b2 + (int64_t)r * l2 + cbyte : p1[q];
+    if constexpr (NB == 2) {
+      // A rows, then the B rows of Y, then those of Y2 (regions of 16k rows: the swizzle of
+      // a row is the same counted from its region's start)
+      const bool ys2 = t >= BM + BN;
+      const int r = xs ? min(m0 + t, g.M - 1) : min(n0 + t - BM - (ys2 ? BN : 0), g.N - 1);
+      const char* const b = xs ? gX : (ys2 ? gY2 : gY);
+      const int64_t l = (xs ? g.ldx : (ys2 ? g.ldy2 : g.ldy)) * (int64_t)sizeof(T);
+      p1[q] = b + (int64_t)r * l + cbyte;
+      p2[q] = p1[q];
+    } else {
+      const int r = xs ? min(m0 + t, g.M - 1) : min(n0 + t - BM, g.N - 1);
+      const char* const b1 = xs ? gX : gY;
+      const char* const b2 = xs ? gX2 : gY2;
+      const int64_t l1 = (xs ? g.ldx : g.ldy) * (int64_t)sizeof(T);
+      const int64_t l2 = (xs ? g.ldx2 : g.ldy2) * (int64_t)sizeof(T);
+      p1[q] = b1 + (int64_t)r * l1 + cbyte;
+      p2[q] = has2 ? b2 + (int64_t)r * l2 + cbyte : p1[q];
+    }
   }
   char* const sdst = smem + (wave_s * PW) * 1024;
   const int kit_a = g.kit_a;
@@ -520,7 +555,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
 
   if constexpr (use_mfma32<T, BM, BN, WGM, WGN>()) {
     // 32 x 32 MFMA blocks, S-stage pipeline; re-dealt into the 16 x 16 layout after
-    constexpr int S = gemm_stages(BM, BN);
+    constexpr int S = gemm_stages_nb(BM, BN, NB);
     f32x16_t acc32[WTM / 32][WTN / 32];
 #pragma unroll
     for (int i = 0; i < WTM / 32; ++i)
@@ -530,11 +565,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
     __asm__ __volatile__("s_mov_b32 %0, 0" : "=s"(zero));
     char* const sm = smem + zero;
     if (kit0 < kit1)
-      kloop32<BM, BN, WGM, WGN, PW, S>(sm, sm + STAGE, S > 2 ? sm + 2 * STAGE : sm + STAGE, p1, p2, kit_a, kit0,
-                                       kit1 - kit0, (wave_s * PW) * 1024, wm, wn, lane, acc32);
+      kloop32<BM, BN, WGM, WGN, PW, S, NB>(sm, sm + STAGE, S > 2 ? sm + 2 * STAGE : sm + STAGE, p1, p2, kit_a,
+                                           kit0, kit1 - kit0, (wave_s * PW) * 1024, wm, wn, lane, acc32);
     acc32_to_16<WTM / 32, WTN / 32>(smem, wave, lane, acc32, acc);
     __syncthreads();  // the epilogue may reuse the LDS
-  } else {
+  } else if constexpr (NB == 1) {
     if (kit0 < kit1) issue(kit0, 0);
     for (int it = kit0; it < kit1; ++it) {
       const int cur = (it - kit0) & 1;
@@ -565,7 +600,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_dma_kernel(GemmArgs g, Ep
   pos.bn = BN;
   pos.tid = tid;
   pos.nthr = NW * 64;
-  pos.smem_bytes = gemm_stages(BM, BN) * STAGE;
+  pos.smem_bytes = gemm_lds_bytes(BM, BN, NB);
   pos.tm = tm;
   pos.tn = tn;
   pos.tile = w.z * g.gtile + tile;
@@ -1676,6 +1711,7 @@ struct Seg2 {
   const void* Y = nullptr;
   int64_t ldy = 0;
   int K = 0;
+  int share = -1;  // shared-X form over the same X rows: -1 by the plan's rule, 0 never, 1 where the tile allows
 };
 
 // n products of one shape in one launch (see GemmArgs): per-product operand offsets in
@@ -1686,10 +1722,10 @@ struct Group {
   int tile = 0;
 };
 
-template <class T, int BM, int BN, int WGM, int WGN, class Epi>
+template <class T, int BM, int BN, int WGM, int WGN, class Epi, int NB = 1>
 inline hipError_t launch_dma(hipStream_t st, const GemmArgs& g, int splits, int groups, const Epi& epi) {
-  constexpr size_t lds = (size_t)gemm_stages(BM, BN) * (BM + BN) * 128;
-  auto kern = gemm_dma_kernel<T, BM, BN, WGM, WGN, Epi>;
+  constexpr size_t lds = (size_t)gemm_lds_bytes(BM, BN, NB);
+  auto kern = gemm_dma_kernel<T, BM, BN, WGM, WGN, Epi, NB>;
   static bool lds_attr = false;  // per instantiation
   if (!lds_attr) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1758,6 +1794,12 @@ inline TilePlan gemm_plan(int M, int N, int K, int K2, int es, int splits, int g
   return t;
 }
 
+// A second segment over the same X rows (same pointer, stride, K and per-product offset):
+// the product is X (Y + Y2)^T and the shared-X form applies.
+inline bool shared_x(const void* X, int64_t ldx, int K, const Seg2& s2, const Group& gr) {
+  return s2.share != 0 && s2.K == K && s2.X == X && s2.ldx == ldx && gr.x2 == gr.x && K > 0;
+}
+
 // C = X Y^T (+ X2 Y2^T) with a fused epilogue. K-slices of 128 bytes go through LDS by
 // direct loads when both K extents are whole slices, else through registers. Wide outputs
 // (at least one 256 x 256 tile per CU) use 256 x 256 tiles with 8 waves; the rest 128 x 128.
@@ -1806,6 +1848,15 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
       if (plan.bm == 256 && plan.bn == 128) {
         g.tiles_m = (M + 255) / 256;
         g.tiles_n = (N + 127) / 128;
+        // the shared-X form of this tile has two stages only; measured alone it is slower than the
+        // concatenated walk at every split-K and wide-N product of the workloads (1024 x 6144 x
+        // 1536 x 2: 56.7 against 47.3 us; 1024 x 1536 x 6144 x 2 in 5 slabs: 50.6 against 43.3)
+        // and faster only over a long single slab, so it is used here only when asked for
+        if (s2.share == 1 && shared_x(X, ldx, K, s2, gr)) {
+          g.kiters = g.kit_a;
+          g.kps = (g.kiters + splits - 1) / splits;
+          return launch_dma<T, 256, 128, 4, 2, Epi, 2>(st, g, splits, gr.n, epi);
+        }
         g.kps = (g.kiters + splits - 1) / splits;
         return launch_dma<T, 256, 128, 4, 2>(st, g, splits, gr.n, epi);
       }
@@ -1818,6 +1869,14 @@ inline hipError_t launch_gemm(hipStream_t st, const void* X, int64_t ldx, const 
       if (plan.bm == 256 && plan.bn == 64) {
         g.tiles_m = (M + 255) / 256;
         g.tiles_n = (N + 63) / 64;
+        if (shared_x(X, ldx, K, s2, gr)) {
+          // the second segment reads the same X rows: one X slice per pair of weight slices,
+          // three stages (measured 18.1 against 20.5 us at 1024 x 3072 x 768 x 2, 28.7 against
+          // 34.0 at 1024 x 3072 x 1536 x 2)
+          g.kiters = g.kit_a;
+          g.kps = g.kiters;
+          return launch_dma<T, 256, 64, 4, 2, Epi, 2>(st, g, 1, gr.n, epi);
+        }
         g.kps = g.kiters;
         return launch_dma<T, 256, 64, 4, 2>(st, g, 1, gr.n, epi);
       }

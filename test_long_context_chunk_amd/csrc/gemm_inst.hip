@@ -32,6 +32,7 @@ inline Seg2 seg(const GemmSeg2& s) {
   r.Y = s.Y;
   r.ldy = s.ldy;
   r.K = s.K;
+  r.share = s.share;
   return r;
 }
 }  // namespace

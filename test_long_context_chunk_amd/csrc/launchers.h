@@ -142,6 +142,7 @@ struct GemmSeg2 {
   const void* Y = nullptr;
   int64_t ldy = 0;
   int K = 0;
+  int share = -1;  // over the same X rows: -1 the plan's choice of form, 0 the concatenated walk, 1 shared-X
 };
 
 // n independent products of one shape in one launch. Product z reads X, Y, X2, Y2 at

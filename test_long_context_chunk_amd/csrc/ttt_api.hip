@@ -1588,6 +1588,17 @@ ttt_status ttt_test_gemm(int32_t precision, const void* X, int64_t ldx, const vo
   return e == hipSuccess ? TTT_OK : TTT_EDEVICE;
 }
 
+ttt_status ttt_test_gemm_pair(const void* X, int64_t ldx, const void* Y, int64_t ldy, const void* Y2, int64_t ldy2,
+                              float* C, int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t splits, int32_t form,
+                              void* stream) {
+  if (!X || !Y || !Y2 || !C || M < 0 || N < 0 || K < 0 || splits < 1 || splits > SPLIT_MAX) return TTT_EINVAL;
+  if (K % 8 || ldx % 8 || ldy % 8 || ldy2 % 8 || ldx < K || ldy < K || ldy2 < K || ldc < N) return TTT_EINVAL;
+  if (form < 0 || form > 2) return TTT_EINVAL;
+  const hipError_t e = gemm_f32((hipStream_t)stream, PREC_BF16, X, ldx, Y, ldy, M, N, K, splits, C, ldc,
+                                (int64_t)M * ldc, 0, GemmSeg2{X, ldx, Y2, ldy2, K, form - 1});
+  return e == hipSuccess ? TTT_OK : TTT_EDEVICE;
+}
+
 ttt_status ttt_test_grad(const void* X, int64_t ldx, const void* Y, int64_t ldy, void* G, int64_t ldg, float* slots,
                          int32_t M, int32_t N, int32_t K, int32_t token_major, void* stream) {
   if (!X || !Y || !G || !slots || M <= 0 || N <= 0 || K <= 0 || K % 64 || ldg < N || ldg % 8) return TTT_EINVAL;

@@ -161,6 +161,12 @@ def test_gemm_hook_validates_shapes(lib):
     assert lib.ttt_test_grad(1, 64, 1, 64, 1, 64, 1, 60, 64, 64, 1, None) == -1
     assert lib.ttt_test_grad(1, 64, 1, 64, 1, 64, 1, 64, 64, 64, 2, None) == -1
     assert lib.ttt_test_grad(None, 64, 1, 64, 1, 64, 1, 64, 64, 64, 1, None) == -1
+    # the two-weight hook: K not a multiple of 8, splits out of range, a NULL second weight
+    assert lib.ttt_test_gemm_pair(1, 8, 1, 8, 1, 8, 1, 8, 4, 4, 6, 1, 0, None) == -1
+    assert lib.ttt_test_gemm_pair(1, 8, 1, 8, 1, 8, 1, 8, 4, 4, 8, 0, 0, None) == -1
+    assert lib.ttt_test_gemm_pair(1, 8, 1, 8, 1, 8, 1, 8, 4, 4, 8, 9, 0, None) == -1
+    assert lib.ttt_test_gemm_pair(1, 8, 1, 8, None, 8, 1, 8, 4, 4, 8, 1, 0, None) == -1
+    assert lib.ttt_test_gemm_pair(1, 8, 1, 8, 1, 8, 1, 8, 4, 4, 8, 1, 3, None) == -1
 
 
 def test_kernel_kind_names_match_the_header():

@@ -39,6 +39,39 @@ def test_gemm_tile_engine_ragged(ttt_lib, precision, M, N, K):
     assert np.all(np.abs(C - ref) <= bound), float(np.max(np.abs(C - ref) / bound))
 
 
+# (M, N, K, splits): the 760M up product (one slab) and down product (5 slabs), the In-Place
+# down product (M = 512), ragged rows and columns with an uneven last slab and an empty one;
+# on 256 x 64 tiles the 125M-style up product and a ragged one; a short-K product (its tile
+# plan walks the two segments one after the other).
+PAIR_SHAPES = [(1024, 6144, 1536, 1), (1024, 1536, 6144, 5), (512, 2560, 9728, 4), (300, 200, 576, 3),
+               (257, 130, 1024, 7), (1024, 3072, 768, 1), (300, 200, 576, 1), (1, 8, 64, 1)]
+
+
+@pytest.mark.parametrize("form", [0, 1, 2])
+@pytest.mark.parametrize("M,N,K,splits", PAIR_SHAPES)
+def test_gemm_two_weights_shared_rows(ttt_lib, M, N, K, splits, form):
+    """The bf16 forward product X (W0 + rn(D))^T as two K-segments over the same rows of X,
+    split over K into slabs, in each form of the tile engine (the inner loop's choice, the
+    segments one after the other, shared X slices): the slab sum within the fp32
+    accumulation bound of the fp64 product, on ragged shapes."""
+    import torch
+    rng = np.random.default_rng(M * 7 + N * 13 + K + splits)
+    X = W.round_to_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    Y = W.round_to_bf16(0.02 * rng.standard_normal((N, K)).astype(np.float32))
+    Y2 = W.round_to_bf16(1e-4 * rng.standard_normal((N, K)).astype(np.float32))
+    log(f"gemm pair M={M} N={N} K={K} splits={splits} form={form}")
+    C = ttt_lib.gemm_pair_test_hook(ttt_lib.to_device(X, "bf16"), ttt_lib.to_device(Y, "bf16"),
+                                    ttt_lib.to_device(Y2, "bf16"), splits, form)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy().astype(np.float64).sum(axis=0)
+    X64, Y64, Y264 = (a.astype(np.float64) for a in (X, Y, Y2))
+    ref = X64 @ Y64.T + X64 @ Y264.T
+    bound = (2 * K + splits + 2) * 2.0 ** -24 * (np.abs(X64) @ (np.abs(Y64) + np.abs(Y264)).T) + 1e-30
+    assert np.all(np.abs(C - ref) <= bound), float(np.max(np.abs(C - ref) / bound))
+    # the update's own contribution is resolved (a path that dropped Y2 fails here)
+    assert np.all(np.abs(C - X64 @ Y64.T - X64 @ Y264.T) <= 0.5 * np.abs(X64 @ Y264.T) + bound)
+
+
 # ---------------------------------------------------------------------- weight-gradient GEMM
 # (M, N, K): the 760M W2 and W1 gradients (192 x 192 tiles), the fuller block's (128 x 128),
 # ragged 128-row tiles over three and one 64-token slices, one 8 x 8 tile.
