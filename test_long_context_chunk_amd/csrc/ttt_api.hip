@@ -176,13 +176,16 @@ struct ttt_ctx {
   hipEvent_t ev_to_aux = nullptr, ev_from_aux = nullptr;
   // GELU blocks, token-major gradients: each block's two weight gradients run on the aux
   // stream beside the main stream's dHn, norm backward, frozen layers and the next block's dA.
-  // The backward row buffers then alternate by block parity (dHb / dHb2 hold the gradient at
-  // the output of even / odd blocks, dU / dU2 their fast dU), the gradients between a
-  // block's sublayers go to dHm and the static MLP's dU to dUs, and ev_grad[l & 1] marks
-  // block l's gradients done.
+  // Each block then has backward row buffers of its own (dHl[l] holds the gradient at block
+  // l's output, dUl[l] its fast dU; blocks 0 and 1 use dHb / dU and dHb2 / dU2), so nothing
+  // the main stream writes in a chunk is read by a gradient still running on the aux stream:
+  // a block's buffers are rewritten only in the next chunk, whose forward pass waits for the
+  // SGD steps queued behind every gradient. The gradients between a block's sublayers go to
+  // dHm and the static MLP's dU to dUs; ev_grad[0] marks the lowest block's gradients done.
   bool agrad = false;
   bool grads_inflight = false;  // the last step's gradients may still read the lowest block's Hn
   void *dHb2 = nullptr, *dU2 = nullptr, *dHm = nullptr, *dUs = nullptr;
+  std::vector<void*> dHl, dUl;
   hipEvent_t ev_gin = nullptr, ev_grad[2] = {nullptr, nullptr};
   // attention backward: the dK, dV pass on the aux stream beside the dQ pass
   hipEvent_t ev_ain = nullptr, ev_aout = nullptr;
@@ -520,6 +523,10 @@ void build(ttt_ctx* c, const ttt_weights* w, const ttt_block_ext* ext) {
   if (c->agrad) {
     c->dHb2 = dalloc<char>(c, (int64_t)Rr * d * es);
     c->dU2 = dalloc<char>(c, (int64_t)Rr * mx * es);
+    for (int l = 0; l < L; ++l) {
+      c->dHl.push_back(l == 0 ? c->dHb : l == 1 ? c->dHb2 : dalloc<char>(c, (int64_t)Rr * d * es));
+      c->dUl.push_back(l == 0 ? c->dU : l == 1 ? c->dU2 : dalloc<char>(c, (int64_t)Rr * mx * es));
+    }
     if (c->ms > 0 || c->window > 0) c->dHm = dalloc<char>(c, (int64_t)Rr * d * es);
     if (c->ms > 0) c->dUs = dalloc<char>(c, (int64_t)Rr * c->ms * es);
   }
@@ -814,11 +821,11 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
     RUN(TTT_K_CE_PROB, run_ce_dlogits(st, prec, c->P, Rr, V, c->ce_w, c->pmax, c->ce_nrec, c->lse, c->tok_tgt,
                                       1.0f / (float)b));
     const int S2 = gemm_split_k(prec, Rr, d, V, 0, SPLIT_MAX);
-    // the backward row buffers of block l (alternating by parity with gradients on the aux
+    // the backward row buffers of block l (one pair per block with gradients on the aux
     // stream): the gradient at its output, and its dU
     const bool ag = c->agrad && train;
-    auto dHbuf = [&](int l) { return ag && (l & 1) ? c->dHb2 : c->dHb; };
-    auto dUbuf = [&](int l) { return ag && (l & 1) ? c->dU2 : c->dU; };
+    auto dHbuf = [&](int l) { return ag ? c->dHl[l] : c->dHb; };
+    auto dUbuf = [&](int l) { return ag ? c->dUl[l] : c->dU; };
     RUN(TTT_K_CE_DY, gemm_f32(st, prec, c->P, V, c->E_outT, V, Rr, d, V, S2, c->part, d, Rd, 0));
     RUN(TTT_K_DY_SUM, run_dy_finish(st, prec, c->part, S2, Rd, Rr, d, c->dH, dHbuf(L - 1), c->H, c->Yb,
                                     foc ? c->cpart : nullptr));
@@ -831,8 +838,6 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
       float* cA = foc ? c->cpart + (int64_t)B.cslot * Rr : nullptr;        // tnm slots
       float* cN = foc ? c->cpart + (int64_t)(B.cslot + tnm) * Rr : nullptr;  // one slot
       if (gelu) {
-        // dU of block l overwrites that of block l + 2, which its gradients on the aux stream read
-        if (ag && l + 2 < L) check(hipStreamWaitEvent(st, c->ev_grad[l & 1], 0));
         if (ag) {
           // G2 = A^T dH on the aux stream as soon as the gradient at the block's output is in
           check(hipEventRecord(c->ev_gin, st));
@@ -849,7 +854,7 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
             check(hipStreamWaitEvent(c->aux, c->ev_gin, 0));
             RUN_ON(TTT_K_DW, c->aux, gemm_grad_km(c->aux, B.Hn, d, dUbuf(l), m, d, m, b, B.w1.G, m,
                                                   c->slots + B.w1.slot0, gradkm(d, m, c->nslots)));
-            check(hipEventRecord(c->ev_grad[l & 1], c->aux));
+            if (l == 0) check(hipEventRecord(c->ev_grad[0], c->aux));
           } else if (c->km) {
             RUN(TTT_K_DW, gemm_grad_km(st, B.A, m, c->dHb, d, m, d, b, B.w2.G, d, c->slots + B.w2.slot0,
                                        gradkm(m, d, c->nslots)));
@@ -871,13 +876,9 @@ void run_chunk(ttt_ctx* c, const int32_t* tok, int64_t ldtok, float* loss_out, i
         const bool below_f = l > 0 || (foc && (has_s || has_a));
         const bool first_f = !has_s && !has_a;
         // where the gradients between this block's sublayers go, and the buffer of the one at
-        // its input (block l - 1's output): that buffer holds the gradient block l + 1's
-        // gradients on the aux stream read, so they must be done first
+        // its input (block l - 1's output; the lowest block's is not written)
         void* const mid = ag ? c->dHm : c->dHb;
-        auto to_below = [&]() {
-          if (ag && l + 1 < L) check(hipStreamWaitEvent(st, c->ev_grad[(l + 1) & 1], 0));
-          return dHbuf(l + 1);
-        };
+        auto to_below = [&]() { return dHbuf(l > 0 ? l - 1 : 0); };
         if (below_f || (foc && (rms || !first_f))) {
           const int S = gemm_split_k(prec, Rr, d, m, 0, SPLIT_MAX);
           RUN(TTT_K_DHN, gemm_f32(st, prec, dUbuf(l), m, B.w1.Wop, m, b, d, m, S, c->part, d, Rd, 0, GemmSeg2(),
