@@ -8,7 +8,7 @@ import math
 import numpy as np
 import pytest
 
-from _parity import TOL, compare, device_weights, gpu_run, inputs, log, oracle_run, rel_l2
+from _parity import TOL, argmax_gate_rows, compare, device_weights, gpu_run, inputs, log, oracle_run, rel_l2
 
 import oracle as O
 import ttt_workloads as W
@@ -318,6 +318,78 @@ def test_inplace_swiglu_four_chunks(ttt_lib):
     g = gpu_run(w, P, x, n_tokens=4 * w.chunk)
     assert g["status"] == 0
     compare(g, orc, w, "bf16", 4, label="inplace")
+
+
+@pytest.mark.parametrize("name", ["s125m", "inplace"])
+def test_full_stream_zero_lr_is_static(ttt_lib, name):
+    """eta = 0 over the whole stream in the benchmark's launch configuration (the 125M-style
+    stack's 128K tokens, the In-Place shape's 64K): sampled tokens one by one against the
+    oracle's static l_t(W0) ([E2E] eq. 4), losses and the argmax gate; the fast weights do not
+    move."""
+    w, x, P = inputs(name)
+    log(f"{name}: full stream at lr 0 ({w.n_tokens} tokens)")
+    g = gpu_run(w, P, x, lr=0.0)
+    assert g["status"] == 0
+    rng = np.random.default_rng(11)
+    idx = np.sort(rng.choice(w.n_tokens, 64, replace=False))
+    model = O.Model.from_workload(w)
+    z, h, _ = O.logits(model, O.as_f64(P), x[idx])
+    ref, _, _, _ = O.ce_stats(z, x[idx + 1])
+    err = float(np.max(np.abs(g["losses"][idx] - ref)))
+    log(f"[{name} lr 0, 64 sampled tokens] loss max |d| {err:.3g}")
+    assert err <= TOL["bf16"]["loss"]
+    argmax_gate_rows(g["argmax"][idx], z, h, P["E_out"], "bf16", label=f"{name}-lr0")
+    for k, D in g["D"].items():
+        assert not D.any(), k
+
+
+@pytest.mark.parametrize("name", ["s125m", "inplace"])
+def test_full_stream_properties(ttt_lib, name):
+    """The whole stream (128K tokens of the 125M-style stack, 64K of the In-Place shape): one
+    prefill call leaves every loss finite and every argmax a valid id; every chunk's clip
+    scale is min(1, c / g_i) of its own grad norm ([SGF] "how it works"); the first chunks'
+    steps obey ||W_i - W_{i-1}||_F = lr min(g_i, c); and the same stream as per-chunk calls
+    gives bitwise the same losses and updates."""
+    import torch
+    import test_long_context_chunk_amd as ttt
+    w, x, P = inputs(name)
+    dev = device_weights(P, "bf16")
+    log(f"{name}: full stream ({w.n_tokens} tokens), one call")
+    full = gpu_run(w, P, x, dev=dev)
+    assert full["status"] == 0
+    assert np.all(np.isfinite(full["losses"]))
+    assert full["argmax"].min() >= 0 and full["argmax"].max() < w.vocab
+    g_i, s_i = full["stats"][:, 0], full["stats"][:, 1]
+    assert np.all(np.isfinite(g_i)) and np.all(g_i > 0)
+    assert np.max(np.abs(s_i - np.minimum(1.0, w.clip / g_i))) <= 1e-6
+    log(f"{name}: per-chunk calls ({w.n_chunks})")
+    ctx = ttt.TTT.from_workload(w, dev, max_tokens=w.n_tokens)
+    tok = torch.from_numpy(x.astype(np.int32)).cuda()
+    keys = list(full["D"])
+
+    def delta():
+        return {k: ctx.fast_weight(int(k.split(".")[1]), k.split(".")[0], "delta").cpu().numpy().astype(np.float64)
+                for k in keys}
+
+    prev = {k: np.zeros_like(full["D"][k]) for k in keys}
+    worst = 0.0
+    for i in range(w.n_chunks):
+        ctx.prefill(tok[i * w.chunk:(i + 1) * w.chunk + 1])
+        if i < 3:
+            D = delta()
+            gi, si = ctx.chunk_stats(i, 1).cpu().numpy()[0]
+            step = math.sqrt(sum(float(np.sum((D[k] - prev[k]) ** 2)) for k in keys))
+            expect = w.lr * min(gi, w.clip)
+            worst = max(worst, abs(step - expect) / expect)
+            prev = D
+    losses = ctx.token_losses().cpu().numpy()
+    D = delta()
+    ctx.close()
+    log(f"[{name} full] clip identity worst rel err {worst:.3g}")
+    assert worst <= 1e-3
+    assert np.array_equal(losses, full["losses"].astype(np.float32))
+    for k in keys:
+        assert np.array_equal(D[k], full["D"][k]), k
 
 
 def test_narrow_tile_products_ragged(ttt_lib):
