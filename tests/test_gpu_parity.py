@@ -343,9 +343,10 @@ def test_full_stream_zero_lr_is_static(ttt_lib, name):
         assert not D.any(), k
 
 
-@pytest.mark.parametrize("name", ["s125m", "inplace"])
+@pytest.mark.parametrize("name", ["s125m", "inplace", "e2e760m"])
 def test_full_stream_properties(ttt_lib, name):
-    """The whole stream (128K tokens of the 125M-style stack, 64K of the In-Place shape): one
+    """The whole stream (128K tokens of the 125M-style stack, 64K of the In-Place shape, 32K of
+    the fuller block with window-8192 attention, its rings wrapping three times over): one
     prefill call leaves every loss finite and every argmax a valid id; every chunk's clip
     scale is min(1, c / g_i) of its own grad norm ([SGF] "how it works"); the first chunks'
     steps obey ||W_i - W_{i-1}||_F = lr min(g_i, c); and the same stream as per-chunk calls
