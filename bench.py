@@ -102,6 +102,7 @@ def kind_flops_per_chunk(w, kind: str) -> float:
 KIND_KERNEL = {"up": "EpiGelu", "du": "EpiDU", "dw": "EpiGrad", "ce_fwd": "EpiCEPartial"}
 GEMM_SOURCES = ["test_long_context_chunk_amd/csrc/gemm.h", "test_long_context_chunk_amd/csrc/gemm_inst.hip",
                 "test_long_context_chunk_amd/csrc/common.h"]
+ATTENTION_SOURCES = ["test_long_context_chunk_amd/csrc/attention.hip", "test_long_context_chunk_amd/csrc/common.h"]
 
 
 def split_k(M: int, N: int, K: int, K2: int) -> int:
@@ -141,12 +142,16 @@ def hbm_kernel_bytes(w, kind: str) -> float:
 HBM_KINDS = ["update", "ce_prob", "gather", "residual", "norm_bwd", "dy_sum"]
 
 
-def gemm_sources_sha256() -> str:
+def sources_sha256(sources) -> str:
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def gemm_sources_sha256() -> str:
+    return sources_sha256(GEMM_SOURCES)
 
 
 def measured_traffic(workload: str, kind: str):
@@ -161,8 +166,10 @@ def measured_traffic(workload: str, kind: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"^gemm_sources_sha256:\s*([0-9a-f]{64})", text, re.M)
-    if not m or m.group(1) != gemm_sources_sha256():
+    # the attention kernels live in their own sources, recorded on a line of their own
+    label, sha = ("attention", sources_sha256(ATTENTION_SOURCES)) if kind == "attn" else ("gemm", gemm_sources_sha256())
+    m = re.search(rf"^{label}_sources_sha256:\s*([0-9a-f]{{64}})", text, re.M)
+    if not m or m.group(1) != sha:
         return None
     m = re.search(rf"^traffic {re.escape(kind)} \S+ fetch_kib=\S+ write_kib=\S+ bytes=(\S+)", text, re.M)
     return float(m.group(1)) if m else None
@@ -491,8 +498,8 @@ def e2e_bench(steps: int, warmup: int, seed: int, cpu: bool, cpu_chunks: int = 2
         "alg_flops_per_token": fl["total"] / T,
         "roofline": {
             "bound": "mfma", "kernel": "attn", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-            "frac": achieved * 1e12 / PEAK_BF16, "traffic": None, "alg_flops_per_launch": per_launch,
-            "avg_launch_us": avg_s * 1e6, "launches": a_n, "kernel_name": "k_swa_fwd",
+            "frac": achieved * 1e12 / PEAK_BF16, "traffic": measured_traffic(w.name, "attn"),
+            "alg_flops_per_launch": per_launch, "avg_launch_us": avg_s * 1e6, "launches": a_n, "kernel_name": "k_swa_fwd",
             "note": "half-precision q, k, v and p, one MFMA per product step: executed flops equal the "
                     "algorithmic ones (no recompute)",
         },
@@ -679,7 +686,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     if args.only == "e2e":
-        print(json.dumps(e2e_bench(args.steps, args.warmup, args.seed, cpu=not args.no_cpu_baseline)), flush=True)
+        print(json.dumps(e2e_bench(args.steps, args.warmup, args.seed, cpu=not args.no_cpu_baseline,
+                                   decode=not args.no_decode)), flush=True)
         return
     if args.only == "batch":
         wb = W.preset(args.workload)
