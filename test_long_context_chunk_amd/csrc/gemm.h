@@ -1197,6 +1197,53 @@ struct EpiSwiglu {
   int64_t lda, ldat;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    if constexpr (sizeof(T) == 2 && AccTile<FM, FN, WGM, WGN>::FITS && TileGeo<FM, FN, WGM, WGN>::BN == 128) {
+      // interior tiles: the fp32 tile in LDS, rows of 8 columns per thread with 16-byte
+      // accesses (every gate piece requested before any is used); A written back to LDS for
+      // the transposed pass
+      using G = TileGeo<FM, FN, WGM, WGN>;
+      constexpr int NT = AccTile<FM, FN, WGM, WGN>::NT;
+      constexpr int TPR = G::BN / 8, RPP = NT / TPR, NP = G::BM / RPP;
+      const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+      if (m0 + G::BM <= p.M && n0 + G::BN <= p.N && (lda & 7) == 0 && (NT % TPR) == 0 && (G::BM % RPP) == 0) {
+        acc_to_lds<FM, FN, WGM, WGN>(p, acc);
+        float* U = (float*)p.smem;
+        const int c = (p.tid % TPR) * 8;
+        float4 g0[NP], g1[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const int64_t o = (int64_t)(m0 + k * RPP + p.tid / TPR) * lda + n0 + c;
+          g0[k] = *(const float4*)(UG + o);
+          g1[k] = *(const float4*)(UG + o + 4);
+        }
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const int r = k * RPP + p.tid / TPR;
+          const int64_t o = (int64_t)(m0 + r) * lda + n0 + c;
+          float4* up = (float4*)(U + r * G::BN + c);
+          const float4 v0 = up[0], v1 = up[1];
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          const float g[8] = {g0[k].x, g0[k].y, g0[k].z, g0[k].w, g1[k].x, g1[k].y, g1[k].z, g1[k].w};
+          float a[8], rs[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            a[q] = silu_f(g[q]) * v[q];
+            rs[q] = a[q] - bf2f(f2bf(a[q]));
+          }
+          store_row8_bf16((bf16_t*)A + o, a, 8, true);
+          if (VU) {
+            *(float4*)(VU + o) = v0;
+            *(float4*)(VU + o + 4) = v1;
+          }
+          if (RES) store_row8_bf16((bf16_t*)RES + o, rs, 8, true);
+          up[0] = make_float4(a[0], a[1], a[2], a[3]);
+          up[1] = make_float4(a[4], a[5], a[6], a[7]);
+        }
+        __syncthreads();
+        if (AT) lds_cols_to_global_bf16<FM, FN, WGM, WGN>(p, (bf16_t*)AT, ldat);
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r0 = epi_row(p, i, 0);
@@ -1428,6 +1475,63 @@ struct EpiSwigluBwd {
   int64_t ld, ldc;
   template <int FM, int FN, int WGM, int WGN>
   __device__ __forceinline__ void apply(const EpiPos& p, f32x4_t (&acc)[FM][FN]) const {
+    if constexpr (sizeof(T) == 2 && AccTile<FM, FN, WGM, WGN>::FITS && TileGeo<FM, FN, WGM, WGN>::BN == 128) {
+      // interior tiles: the fp32 tile in LDS, rows of 8 columns per thread with 16-byte
+      // accesses, in two halves of a thread's rows (each half's operand pieces requested
+      // before any is used); each row's partial dot sums its 16 pieces in a fixed order
+      using G = TileGeo<FM, FN, WGM, WGN>;
+      constexpr int NT = AccTile<FM, FN, WGM, WGN>::NT;
+      constexpr int TPR = G::BN / 8, RPP = NT / TPR, NP = G::BM / RPP, NH = NP / 2;
+      const int m0 = p.row0 - p.wm * G::WTM, n0 = p.col0 - p.wn * G::WTN;
+      if (m0 + G::BM <= p.M && n0 + G::BN <= p.N && (ld & 7) == 0 && (NT % TPR) == 0 && (G::BM % RPP) == 0 &&
+          NP % 2 == 0 && TPR == 16) {
+        acc_to_lds<FM, FN, WGM, WGN>(p, acc);
+        const float* U = (const float*)p.smem;
+        const int c = (p.tid % TPR) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float4 g0[NH], g1[NH], v0[NH], v1[NH];
+          uint4 rq[NH];
+#pragma unroll
+          for (int k = 0; k < NH; ++k) {
+            const int64_t o = (int64_t)(m0 + (h * NH + k) * RPP + p.tid / TPR) * ld + n0 + c;
+            g0[k] = *(const float4*)(UG + o);
+            g1[k] = *(const float4*)(UG + o + 4);
+            v0[k] = *(const float4*)(VU + o);
+            v1[k] = *(const float4*)(VU + o + 4);
+            rq[k] = RES ? *(const uint4*)((const bf16_t*)RES + o) : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < NH; ++k) {
+            const int r = (h * NH + k) * RPP + p.tid / TPR;
+            const int64_t o = (int64_t)(m0 + r) * ld + n0 + c;
+            const float4 a0 = *(const float4*)(U + r * G::BN + c), a1 = *(const float4*)(U + r * G::BN + c + 4);
+            const float da[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float g[8] = {g0[k].x, g0[k].y, g0[k].z, g0[k].w, g1[k].x, g1[k].y, g1[k].z, g1[k].w};
+            const float vu[8] = {v0[k].x, v0[k].y, v0[k].z, v0[k].w, v1[k].x, v1[k].y, v1[k].z, v1[k].w};
+            const uint32_t rw[4] = {rq[k].x, rq[k].y, rq[k].z, rq[k].w};
+            float dg[8], dv[8];
+            float dot = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float sg = 1.0f / (1.0f + expf(-g[q]));
+              dg[q] = da[q] * vu[q] * sg * (1.0f + g[q] * (1.0f - sg));
+              dv[q] = da[q] * g[q] * sg;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              dot += da[2 * q] * __uint_as_float(rw[q] << 16);
+              dot += da[2 * q + 1] * __uint_as_float(rw[q] & 0xffff0000u);
+            }
+            store_row8_bf16((bf16_t*)DG + o, dg, 8, true);
+            store_row8_bf16((bf16_t*)DV + o, dv, 8, true);
+            dot = row16_sum(dot);
+            if (cdot && (p.tid % TPR) == 0) cdot[(int64_t)p.tn * ldc + m0 + r] = dot;
+          }
+        }
+        return;
+      }
+    }
     float dots[FM][4];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
