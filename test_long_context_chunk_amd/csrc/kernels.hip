@@ -344,12 +344,13 @@ __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax,
                                                  const int* __restrict__ pidx, int nrec, int b, StreamRows sr,
                                                  const float* __restrict__ tgt_logit, float* __restrict__ lse,
                                                  float* __restrict__ loss, int* __restrict__ amax) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-  if (row >= b) return;
+  // one row per block (a large vocabulary has thousands of records per row): thread t takes
+  // records t, t + NT, ..; then a butterfly within each wave and the waves in order
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
   float mx = -INFINITY, sm = 0.f;
   int ix = 0x7fffffff;
-  for (int j = lane; j < nrec; j += 64) {
+  for (int j = tid; j < nrec; j += NT) {
     const int64_t o = (int64_t)row * nrec + j;
     ce_combine(mx, sm, ix, pmax[o], psum[o], pidx[o]);
   }
@@ -360,7 +361,20 @@ __global__ void __launch_bounds__(NT) k_ce_merge(const float* __restrict__ pmax,
     const int oix = __shfl_xor(ix, off, TTT_WAVE);
     ce_combine(mx, sm, ix, omx, osm, oix);
   }
+  __shared__ float wmx[NT / 64], wsm[NT / 64];
+  __shared__ int wix[NT / 64];
   if (lane == 0) {
+    wmx[wave] = mx;
+    wsm[wave] = sm;
+    wix[wave] = ix;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    mx = wmx[0];
+    sm = wsm[0];
+    ix = wix[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) ce_combine(mx, sm, ix, wmx[w], wsm[w], wix[w]);
     const float l = mx + logf(sm);
     lse[row] = l;
     const int64_t o = sr.ld * (row / sr.bs) + row % sr.bs;
@@ -953,8 +967,8 @@ hipError_t run_loss_correct(hipStream_t st, const float* cpart, int nslot, int b
 hipError_t run_ce_merge(hipStream_t st, const float* pmax, const float* psum, const int* pidx, int nrec, int b,
                         StreamRows sr, const float* tgt_logit, float* lse, float* loss, int* amax) {
   if (sr.bs < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_ce_merge, dim3((b + 3) / 4), dim3(NT), 0, st, pmax, psum, pidx, nrec, b, sr, tgt_logit, lse,
-                     loss, amax);
+  if (b <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_ce_merge, dim3(b), dim3(NT), 0, st, pmax, psum, pidx, nrec, b, sr, tgt_logit, lse, loss, amax);
   return hipGetLastError();
 }
 
