@@ -55,3 +55,25 @@ def test_attention_flops_of_the_timed_steps():
     assert full == 4 * w.d_model * w.chunk * w.swa_window
     first = bench.e2e_flops_per_step(w, 0)["attn_fwd"] / launches
     assert first < full  # the first pass over the stream starts with short windows
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(monkeypatch):
+    """roofline.traffic comes from the committed counter summaries, which record the sha256 of
+    the sources the counters were taken on: a line's dominant kind has a figure while the
+    sources read as recorded, and none once they read differently (the attention forward is
+    checked against its own sources, the GEMM kinds against the GEMM sources)."""
+    import os
+    import re
+    kinds = [("s760m", "up"), ("single", "ce_fwd"), ("s125m", "dw"), ("inplace", "ce_fwd"), ("e2e760m", "attn")]
+    for wl, kind in kinds:
+        text = open(os.path.join(bench.ROOT, "profiles", f"traffic_{wl}.md")).read()
+        rec = {lab: re.search(rf"^{lab}_sources_sha256:\s*([0-9a-f]{{64}})", text, re.M).group(1)
+               for lab in ("gemm", "attention") if re.search(rf"^{lab}_sources_sha256:", text, re.M)}
+        as_recorded = lambda src: rec["attention"] if src == bench.ATTENTION_SOURCES else rec["gemm"]
+        monkeypatch.setattr(bench, "sources_sha256", as_recorded)
+        t = bench.measured_traffic(wl, kind)
+        assert t is not None and t > 0, (wl, kind)
+        assert bench.measured_traffic(wl, "no_such_kind") is None
+        monkeypatch.setattr(bench, "sources_sha256", lambda src: "0" * 64)
+        assert bench.measured_traffic(wl, kind) is None, (wl, kind)
+    assert bench.measured_traffic("no_such_workload", "up") is None
